@@ -1,0 +1,123 @@
+/*
+ * rib.h -- C ABI of the MI355X (gfx950) library for RIB window attention with
+ * the CLA output gate.
+ *
+ * Source of the method: "Rank-Factorized Implicit Neural Bias: Scaling
+ * Super-Resolution Transformer with FlashAttention" (arXiv 2603.06738), as
+ * summarised on gist.science (French and Italian pages, methodology part A
+ * "Rank-factorized Implicit Neural Bias" and part B "Convolutional Local
+ * Attention") and on the omica.com.cn explainer (section 2.2 "RIB core
+ * design", section 2.3 "CLA", section 5.2 "caching the positional factors").
+ *
+ * Conventions shared by every entry point:
+ *   - All pointers are device pointers (memory from hipMalloc or a framework
+ *     allocator on the current device) unless stated otherwise.  The caller
+ *     owns every buffer; the library allocates no device or host memory and
+ *     keeps no state apart from a thread-local error message.
+ *   - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t
+ *     passed as void*, NULL = the null stream) and the call returns.  RIB_OK
+ *     means "validated and enqueued"; a fault inside a kernel surfaces at the
+ *     caller's next synchronisation.
+ *   - Arguments are validated before anything is launched.  On any error no
+ *     work is enqueued, outputs are untouched, and rib_last_error() describes
+ *     the problem.  Validation makes no HIP call, so it also works on a host
+ *     without a GPU.
+ *   - Feature maps are flat NHWC: element (b, y, x, c) of a [B][H][W][C] array
+ *     sits at ((b*H + y)*W + x)*C + c with C = heads*dh; head h owns channels
+ *     [h*dh, (h+1)*dh).
+ */
+#ifndef RIB_H
+#define RIB_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RIB_OK = 0,
+  RIB_ERR_INVALID_ARG = 1, /* null pointer, size < 1, window < 2, misalignment, aliasing */
+  RIB_ERR_UNSUPPORTED = 2, /* valid request outside the compiled variants (never a slow fallback) */
+  RIB_ERR_HIP = 3          /* the HIP runtime refused a launch; see rib_last_error() */
+} rib_status;
+
+typedef enum { RIB_F32 = 0, RIB_BF16 = 1 } rib_dtype;
+
+/*
+ * rib_encode -- positional factors of one window size (explainer section 2.2:
+ * coordinate encoding layer, implicit neural field; gist.science part A,
+ * mechanism steps 1-2).
+ *
+ * For every in-window position n = iy*window + ix (0 <= n < window^2):
+ *   c   = (u(iy), u(ix)),  u(k) = float32((2k - (window-1)) / (window-1)),
+ *         i.e. coordinates in [-1, 1] with both ends included;
+ *   r   = [c_y, c_x, then for i = 0..L-1: sin(2^i c_y), sin(2^i c_x),
+ *          cos(2^i c_y), cos(2^i c_x)]                    (2 + 4L features);
+ *   h   = ReLU(r W_h + b_h)                                (hidden values);
+ *   qp[n] = h Wp_q,  kp[n] = h Wp_k                        (R values each).
+ *
+ * weights : device, float32, packed row-major, y = x W convention:
+ *           W_h[2+4L][hidden] | b_h[hidden] | Wp_q[hidden][R] | Wp_k[hidden][R].
+ * qp, kp  : device, float32, [window*window][R] row-major, written.
+ *           Compute once per window size and reuse them for every window,
+ *           head and image (explainer section 5.2 caches them).
+ * Limits  : 2 <= window <= 128, 0 <= L <= 16, 1 <= hidden <= 256, 1 <= R <= 64;
+ *           all pointers 4-byte aligned; qp and kp must not overlap weights
+ *           or each other.  Arithmetic is float32 (sinf/cosf, fp32 sums).
+ */
+rib_status rib_encode(int window, int L, int hidden, int R, const float* weights, float* qp,
+                      float* kp, void* stream);
+
+/*
+ * rib_window_attn -- RIB window attention with the CLA gate (gist.science
+ * part A mechanism steps 3-4 and part B; explainer section 2.2 "attention
+ * rewrite" and section 2.3):
+ *
+ *   per image b, window (wy, wx) of window x window tokens, head h:
+ *     S = Qc Kc^T / sqrt(dh) + Qp Kp^T / sqrt(R)
+ *       = [Qc/sqrt(dh), Qp/sqrt(R)] [Kc, Kp]^T        (one contraction)
+ *     O = (softmax(S) V) * sigmoid(G)                 (element-wise gate)
+ *
+ * The window grid is anchored at (0,0).  A window holds only the real tokens
+ * (y < H, x < W): when H or W is not a multiple of `window`, the missing
+ * positions are masked out of the softmax and produce no output.  Qp/Kp are
+ * indexed by in-window position n = (y mod window)*window + (x mod window)
+ * and are shared by all heads.
+ *
+ * qc, kc, v, g : device, [B][H][W][heads*dh] of `dtype` (read).
+ * o            : device, same shape and dtype (written); must not overlap any
+ *                input.
+ * qp, kp       : device, float32 [window*window][R] from rib_encode (read).
+ * dtype        : RIB_F32 -- fp32 in, fp32 arithmetic, fp32 out;
+ *                RIB_BF16 -- bf16 in and out, bf16 matrix-core products with
+ *                fp32 accumulation and fp32 softmax.
+ * Limits       : 2 <= window <= 128; B*H*W*heads*dh < 2^31;
+ *                RIB_F32: dh <= 64, R <= 64;
+ *                RIB_BF16: (dh, R) in {(8,8), (16,16), (30,16), (32,16),
+ *                (16,32), (30,32)} (others return RIB_ERR_UNSUPPORTED).
+ *                Base pointers must be 16-byte aligned.
+ */
+rib_status rib_window_attn(const void* qc, const void* kc, const void* v, const void* g,
+                           const float* qp, const float* kp, void* o, int B, int H, int W,
+                           int heads, int dh, int R, int window, rib_dtype dtype, void* stream);
+
+/*
+ * rib_attn_supported -- RIB_OK if rib_window_attn has a compiled variant for
+ * (dh, R, window, dtype), RIB_ERR_UNSUPPORTED if not, RIB_ERR_INVALID_ARG for
+ * nonsensical values.  Launches nothing.
+ */
+rib_status rib_attn_supported(int dh, int R, int window, rib_dtype dtype);
+
+/* Text describing the last non-OK status returned on this thread ("" if none).
+ * The pointer stays valid until the next library call on the same thread. */
+const char* rib_last_error(void);
+
+/* ABI version of this header (incremented on any incompatible change). */
+int rib_abi_version(void);
+
+#define RIB_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RIB_H */

@@ -1,0 +1,195 @@
+"""CPU oracle for RIB window attention with the CLA gate -- TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The GPU library and its Python binding never touch it.
+
+The arithmetic lives in ``rib_oracle.c`` (plain fp64 C, OpenMP over
+image x window x head units); this module only builds it with gcc, loads it
+with ctypes and marshals numpy arrays.  ``brute.py`` is a second, independent
+pure-Python implementation for tiny cases.
+
+Method: "Rank-Factorized Implicit Neural Bias: Scaling Super-Resolution
+Transformer with FlashAttention" (gist.science summaries, methodology part A;
+omica.com.cn explainer, sections 2.2 and 2.3).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rib_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I = ctypes.POINTER(ctypes.c_int)
+
+
+def compile_oracle(src: str, out: str) -> str:
+    """gcc with IEEE semantics: no fast-math, no FMA contraction."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-shared", "-fPIC", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(_LIB):
+        compile_oracle(_SRC, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        _lib = _configure(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _configure(L):
+    L.rib_oracle_threads.restype = ctypes.c_int
+    L.rib_oracle_encode.argtypes = [ctypes.c_int] * 4 + [_D, _D, _D]
+    L.rib_oracle_encode.restype = ctypes.c_int
+    L.rib_oracle_attn_units.argtypes = [_D] * 6 + [ctypes.c_int] * 7 + [ctypes.c_long] * 2 + [_D]
+    L.rib_oracle_attn_units.restype = ctypes.c_int
+    L.rib_oracle_attn_rows.argtypes = [_D] * 6 + [ctypes.c_int] * 8 + [_I] * 3 + [_D]
+    L.rib_oracle_attn_rows.restype = ctypes.c_int
+    L.rib_oracle_window_debug.argtypes = ([_D] * 6 + [ctypes.c_int] * 11 + [_D] * 3 + [_I] * 3)
+    L.rib_oracle_window_debug.restype = ctypes.c_int
+    return L
+
+
+class using:
+    """Context manager: route this module's calls to another build of the oracle
+    (the mutation tests load deliberately broken copies to prove the pins bite)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = _lib
+        _lib = _configure(ctypes.CDLL(self.path))
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def threads() -> int:
+    """OpenMP threads the oracle runs with (all host cores unless OMP_NUM_THREADS says otherwise)."""
+    return int(lib().rib_oracle_threads())
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(_D)
+
+
+def weight_count(L: int, hidden: int, R: int) -> int:
+    """Length of the packed weight vector W_h | b_h | Wp_q | Wp_k."""
+    return (2 + 4 * L) * hidden + hidden + 2 * hidden * R
+
+
+def encode(window: int, L: int, hidden: int, R: int, weights) -> tuple[np.ndarray, np.ndarray]:
+    """Qp, Kp as [window*window, R] float64 (coordinate encoder + implicit field)."""
+    w = _f64(weights).reshape(-1)
+    if w.size != weight_count(L, hidden, R):
+        raise ValueError("packed weight vector has the wrong length")
+    n = window * window
+    qp = np.zeros((n, R), np.float64)
+    kp = np.zeros((n, R), np.float64)
+    if lib().rib_oracle_encode(window, L, hidden, R, _p(w), _p(qp), _p(kp)) != 0:
+        raise ValueError("oracle encode rejected its arguments")
+    return qp, kp
+
+
+def _shape_args(qc, heads, dh):
+    B, H, W, C = qc.shape
+    if C != heads * dh:
+        raise ValueError("channel count must equal heads*dh")
+    return B, H, W
+
+
+def units(B: int, H: int, W: int, heads: int, window: int) -> int:
+    """Number of (image, window, head) units of a problem."""
+    return B * (-(-H // window)) * (-(-W // window)) * heads
+
+
+def window_attn(qc, kc, v, g, qp, kp, heads: int, window: int, unit_range=None) -> np.ndarray:
+    """O = (softmax(Qc Kc^T/sqrt(dh) + Qp Kp^T/sqrt(R)) V) * sigmoid(G), NHWC float64.
+
+    ``unit_range=(begin, end)`` restricts the work to those (image, window,
+    head) units; outputs of the other units are left at zero.
+    """
+    qc, kc, v, g = (_f64(a) for a in (qc, kc, v, g))
+    qp, kp = _f64(qp), _f64(kp)
+    dh = qc.shape[-1] // heads
+    B, H, W = _shape_args(qc, heads, dh)
+    R = qp.shape[-1]
+    o = np.zeros(qc.shape, np.float64)
+    ub, ue = (0, -1) if unit_range is None else unit_range
+    rc = lib().rib_oracle_attn_units(_p(qc), _p(kc), _p(v), _p(g), _p(qp), _p(kp), B, H, W, heads,
+                                     dh, R, window, ub, ue, _p(o))
+    if rc != 0:
+        raise ValueError("oracle attention rejected its arguments")
+    return o
+
+
+def window_attn_rows(qc, kc, v, g, qp, kp, heads: int, window: int, tok_b, tok_y, tok_x) -> np.ndarray:
+    """Output rows [n, heads*dh] for the query tokens (tok_b[k], tok_y[k], tok_x[k])."""
+    qc, kc, v, g = (_f64(a) for a in (qc, kc, v, g))
+    qp, kp = _f64(qp), _f64(kp)
+    dh = qc.shape[-1] // heads
+    B, H, W = _shape_args(qc, heads, dh)
+    R = qp.shape[-1]
+    tb, ty, tx = (np.ascontiguousarray(np.asarray(t, dtype=np.int32)) for t in (tok_b, tok_y, tok_x))
+    nq = tb.size
+    out = np.zeros((nq, heads * dh), np.float64)
+    rc = lib().rib_oracle_attn_rows(_p(qc), _p(kc), _p(v), _p(g), _p(qp), _p(kp), B, H, W, heads, dh,
+                                    R, window, nq, tb.ctypes.data_as(_I), ty.ctypes.data_as(_I),
+                                    tx.ctypes.data_as(_I), _p(out))
+    if rc != 0:
+        raise ValueError("oracle row attention rejected its arguments")
+    return out
+
+
+def window_debug(qc, kc, v, g, qp, kp, heads: int, window: int, b: int, wy: int, wx: int, h: int):
+    """(Sc, Bm, P, tokens) for one (image, window, head): content score, explicit bias, softmax.
+
+    ``tokens`` is an int array [nt, 3] of (y, x, n) in map scan order.
+    """
+    qc, kc, v, g = (_f64(a) for a in (qc, kc, v, g))
+    qp, kp = _f64(qp), _f64(kp)
+    dh = qc.shape[-1] // heads
+    B, H, W = _shape_args(qc, heads, dh)
+    R = qp.shape[-1]
+    cap = window * window
+    Sc = np.zeros(cap * cap, np.float64)
+    Bm = np.zeros(cap * cap, np.float64)
+    P = np.zeros(cap * cap, np.float64)
+    ty = np.zeros(cap, np.int32)
+    tx = np.zeros(cap, np.int32)
+    tn = np.zeros(cap, np.int32)
+    nt = lib().rib_oracle_window_debug(_p(qc), _p(kc), _p(v), _p(g), _p(qp), _p(kp), B, H, W, heads,
+                                       dh, R, window, b, wy, wx, h, _p(Sc), _p(Bm), _p(P),
+                                       ty.ctypes.data_as(_I), tx.ctypes.data_as(_I),
+                                       tn.ctypes.data_as(_I))
+    if nt < 0:
+        raise ValueError("oracle debug view rejected its arguments")
+    m = nt * nt
+    toks = np.stack([ty[:nt], tx[:nt], tn[:nt]], axis=1)
+    return (Sc[:m].reshape(nt, nt), Bm[:m].reshape(nt, nt), P[:m].reshape(nt, nt), toks)

@@ -1,0 +1,317 @@
+/*
+ * rib_oracle.c -- plain, slow, fp64 CPU oracle for RIB window attention with
+ * the CLA output gate.  TEST INFRASTRUCTURE ONLY: the parity tests, the smoke
+ * check and the benchmark's CPU-baseline leg call it; the GPU library never
+ * links, loads or calls it, and it shares no code with that library.
+ *
+ * Method followed ("Rank-Factorized Implicit Neural Bias: Scaling
+ * Super-Resolution Transformer with FlashAttention", as summarised on
+ * gist.science (fr/it, "Methodologie proposee" / "Metodologia proposta",
+ * part A) and on the omica.com.cn explainer, sections 2.2 and 2.3):
+ *
+ *   coordinate encoder   r = [c, sin(2^i c), cos(2^i c)]_{i<L},  c in [-1,1]^2
+ *   implicit field       h = ReLU(r W_h + b_h),  Qp = h Wp_q,  Kp = h Wp_k
+ *   attention            S = Qc Kc^T / sqrt(dh) + Qp Kp^T / sqrt(R)
+ *   CLA gate             O = (softmax(S) V) * sigmoid(G)
+ *
+ * This file computes exactly that definition.  It does NOT use the channel
+ * concatenation trick: the bias B = Qp Kp^T / sqrt(R) is materialised as its
+ * own array (row by row) and added to the content score, then softmax, then
+ * the V product, then the gate.  Everything is double precision; inputs are
+ * the exact values of the caller's fp32 / bf16 tensors, upcast.
+ *
+ * Readings of points the pages leave open (each also listed in the design
+ * notes of the repository):
+ *   - coordinates include both endpoints, u(k) = -1 + 2k/(ws-1), and are
+ *     float32 values (the pseudocode feeds a float tensor): the oracle rounds
+ *     (2k-(ws-1))/(ws-1) to float once, then works in double;
+ *   - coordinate order (y, x) with in-window index n = iy*ws + ix;
+ *   - frequencies exactly 2^i, i = 0..L-1, no pi factor; the raw coordinates
+ *     come first, then sin and cos for each frequency, y before x;
+ *   - the hidden layer has a bias, the two rank heads have none;
+ *   - one (Qp, Kp) pair shared by every head; D in 1/sqrt(D) is the head dim;
+ *   - weights are stored W[in][out] row-major (y = x W);
+ *   - maps that are not a multiple of the window: windows are anchored at
+ *     (0,0), a window holds only the real tokens inside the map, and padded
+ *     positions neither attend nor are attended to;
+ *   - sigmoid(z) = 1 / (1 + exp(-z)), per element, G laid out like O.
+ *
+ * Packed weight layout (fp64 here, the same order the library takes in fp32):
+ *   W_h[2+4L][hidden] | b_h[hidden] | Wp_q[hidden][R] | Wp_k[hidden][R]
+ * Feature maps are NHWC: [B][H][W][heads*dh], head h owning channels
+ * [h*dh, (h+1)*dh).
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int rib_oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* One coordinate value, as a float32, then widened: endpoints -1 and +1. */
+static double coord_value(int k, int ws) {
+  float num = (float)(2 * k - (ws - 1));
+  float den = (float)(ws - 1);
+  float u = num / den;
+  return (double)u;
+}
+
+/* Fourier features of one token: out has 2 + 4L entries. */
+static void fourier_features(double cy, double cx, int L, double* out) {
+  int f = 0;
+  out[f++] = cy;
+  out[f++] = cx;
+  for (int i = 0; i < L; ++i) {
+    double freq = ldexp(1.0, i);
+    out[f++] = sin(freq * cy);
+    out[f++] = sin(freq * cx);
+    out[f++] = cos(freq * cy);
+    out[f++] = cos(freq * cx);
+  }
+}
+
+/*
+ * Encoder (explainer section 2.2, "coordinate encoding layer" and "implicit
+ * neural field"): Qp, Kp are [ws*ws][R] row-major.  Returns 0, or -1 on a bad
+ * argument.
+ */
+int rib_oracle_encode(int ws, int L, int hidden, int R, const double* weights,
+                      double* qp, double* kp) {
+  if (ws < 2 || L < 0 || hidden < 1 || R < 1 || !weights || !qp || !kp) return -1;
+  const int F = 2 + 4 * L;
+  const double* Wh = weights;
+  const double* bh = Wh + (size_t)F * hidden;
+  const double* Wq = bh + hidden;
+  const double* Wk = Wq + (size_t)hidden * R;
+  const int N = ws * ws;
+  double* feat = (double*)malloc(sizeof(double) * F);
+  double* h = (double*)malloc(sizeof(double) * hidden);
+  if (!feat || !h) { free(feat); free(h); return -1; }
+  for (int n = 0; n < N; ++n) {
+    int iy = n / ws, ix = n % ws;
+    fourier_features(coord_value(iy, ws), coord_value(ix, ws), L, feat);
+    for (int j = 0; j < hidden; ++j) {
+      double acc = bh[j];
+      for (int f = 0; f < F; ++f) acc += feat[f] * Wh[(size_t)f * hidden + j];
+      h[j] = acc > 0.0 ? acc : 0.0;
+    }
+    for (int r = 0; r < R; ++r) {
+      double aq = 0.0, ak = 0.0;
+      for (int j = 0; j < hidden; ++j) {
+        aq += h[j] * Wq[(size_t)j * R + r];
+        ak += h[j] * Wk[(size_t)j * R + r];
+      }
+      qp[(size_t)n * R + r] = aq;
+      kp[(size_t)n * R + r] = ak;
+    }
+  }
+  free(feat);
+  free(h);
+  return 0;
+}
+
+typedef struct {
+  const double *qc, *kc, *v, *g, *qp, *kp;
+  int B, H, W, heads, dh, R, ws;
+} problem;
+
+static size_t elem(const problem* p, int b, int y, int x, int h, int d) {
+  return (((size_t)b * p->H + y) * p->W + x) * (size_t)(p->heads * p->dh) + (size_t)h * p->dh + d;
+}
+
+/*
+ * The real tokens of window (wy, wx): every map position whose window is
+ * (floor(y/ws), floor(x/ws)) = (wy, wx), found by scanning the map.  Writes
+ * their coordinates and in-window index n = (y mod ws)*ws + (x mod ws);
+ * returns how many there are.
+ */
+static int window_tokens(const problem* p, int wy, int wx, int* ty, int* tx, int* tn) {
+  int cnt = 0;
+  for (int y = 0; y < p->H; ++y) {
+    if (y / p->ws != wy) continue;
+    for (int x = 0; x < p->W; ++x) {
+      if (x / p->ws != wx) continue;
+      ty[cnt] = y;
+      tx[cnt] = x;
+      tn[cnt] = (y % p->ws) * p->ws + (x % p->ws);
+      ++cnt;
+    }
+  }
+  return cnt;
+}
+
+/*
+ * One query row i of one (image, window, head): content score row Sc, bias
+ * row Bm, softmax row P, then O = (P V) * sigmoid(G) written to out (length
+ * dh).  Sc, Bm, P are caller scratch of length nt.
+ */
+static void attend_row(const problem* p, int b, int h, int i, int nt, const int* ty, const int* tx,
+                       const int* tn, double* Sc, double* Bm, double* P, double* out) {
+  const double inv_sqrt_dh = 1.0 / sqrt((double)p->dh);
+  const double inv_sqrt_r = 1.0 / sqrt((double)p->R);
+  const double* q = p->qc + elem(p, b, ty[i], tx[i], h, 0);
+  const double* qpos = p->qp + (size_t)tn[i] * p->R;
+  for (int j = 0; j < nt; ++j) {
+    const double* k = p->kc + elem(p, b, ty[j], tx[j], h, 0);
+    double s = 0.0;
+    for (int d = 0; d < p->dh; ++d) s += q[d] * k[d];
+    Sc[j] = s * inv_sqrt_dh;
+    const double* kpos = p->kp + (size_t)tn[j] * p->R;
+    double bb = 0.0;
+    for (int r = 0; r < p->R; ++r) bb += qpos[r] * kpos[r];
+    Bm[j] = bb * inv_sqrt_r;
+  }
+  double mx = -INFINITY;
+  for (int j = 0; j < nt; ++j) {
+    double s = Sc[j] + Bm[j];
+    P[j] = s;
+    if (s > mx) mx = s;
+  }
+  double sum = 0.0;
+  for (int j = 0; j < nt; ++j) {
+    P[j] = exp(P[j] - mx);
+    sum += P[j];
+  }
+  for (int j = 0; j < nt; ++j) P[j] /= sum;
+  for (int d = 0; d < p->dh; ++d) {
+    double a = 0.0;
+    for (int j = 0; j < nt; ++j) a += P[j] * p->v[elem(p, b, ty[j], tx[j], h, d)];
+    double gate = 1.0 / (1.0 + exp(-p->g[elem(p, b, ty[i], tx[i], h, d)]));
+    out[d] = a * gate;
+  }
+}
+
+static int check_problem(const problem* p) {
+  if (!p->qc || !p->kc || !p->v || !p->g || !p->qp || !p->kp) return -1;
+  if (p->B < 1 || p->H < 1 || p->W < 1 || p->heads < 1 || p->dh < 1 || p->R < 1 || p->ws < 2) return -1;
+  return 0;
+}
+
+/*
+ * Whole attention over a subset of (image, window, head) units.  Units are
+ * numbered u = ((b*nWy + wy)*nWx + wx)*heads + h; the oracle computes units
+ * [u_begin, u_end) and writes their outputs into o (full NHWC array; other
+ * entries are left as they are).  u_end < 0 means all units.
+ */
+int rib_oracle_attn_units(const double* qc, const double* kc, const double* v, const double* g,
+                          const double* qp, const double* kp, int B, int H, int W, int heads,
+                          int dh, int R, int ws, long u_begin, long u_end, double* o) {
+  problem p = {qc, kc, v, g, qp, kp, B, H, W, heads, dh, R, ws};
+  if (check_problem(&p) || !o) return -1;
+  const int nWy = (H + ws - 1) / ws, nWx = (W + ws - 1) / ws;
+  const long units = (long)B * nWy * nWx * heads;
+  if (u_end < 0 || u_end > units) u_end = units;
+  if (u_begin < 0) u_begin = 0;
+  int fail = 0;
+#pragma omp parallel
+  {
+    const int cap = ws * ws;
+    int* ty = (int*)malloc(sizeof(int) * cap);
+    int* tx = (int*)malloc(sizeof(int) * cap);
+    int* tn = (int*)malloc(sizeof(int) * cap);
+    double* Sc = (double*)malloc(sizeof(double) * cap);
+    double* Bm = (double*)malloc(sizeof(double) * cap);
+    double* P = (double*)malloc(sizeof(double) * cap);
+    double* out = (double*)malloc(sizeof(double) * dh);
+    if (!ty || !tx || !tn || !Sc || !Bm || !P || !out) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (long u = u_begin; u < u_end; ++u) {
+        int h = (int)(u % heads);
+        long t = u / heads;
+        int wx = (int)(t % nWx);
+        t /= nWx;
+        int wy = (int)(t % nWy);
+        int b = (int)(t / nWy);
+        int nt = window_tokens(&p, wy, wx, ty, tx, tn);
+        for (int i = 0; i < nt; ++i) {
+          attend_row(&p, b, h, i, nt, ty, tx, tn, Sc, Bm, P, out);
+          for (int d = 0; d < dh; ++d) o[elem(&p, b, ty[i], tx[i], h, d)] = out[d];
+        }
+      }
+    }
+    free(ty); free(tx); free(tn); free(Sc); free(Bm); free(P); free(out);
+  }
+  return fail ? -1 : 0;
+}
+
+int rib_oracle_attn(const double* qc, const double* kc, const double* v, const double* g,
+                    const double* qp, const double* kp, int B, int H, int W, int heads, int dh,
+                    int R, int ws, double* o) {
+  return rib_oracle_attn_units(qc, kc, v, g, qp, kp, B, H, W, heads, dh, R, ws, 0, -1, o);
+}
+
+/*
+ * Output rows for selected query tokens only (all heads): for each k < nq,
+ * token (qb[k], qy[k], qx[k]) gets out[k][heads*dh].  Used to check full-size
+ * problems at sampled positions.
+ */
+int rib_oracle_attn_rows(const double* qc, const double* kc, const double* v, const double* g,
+                         const double* qp, const double* kp, int B, int H, int W, int heads,
+                         int dh, int R, int ws, int nq, const int* qb, const int* qy,
+                         const int* qx, double* out) {
+  problem p = {qc, kc, v, g, qp, kp, B, H, W, heads, dh, R, ws};
+  if (check_problem(&p) || nq < 0 || (nq > 0 && (!qb || !qy || !qx || !out))) return -1;
+  for (int k = 0; k < nq; ++k)
+    if (qb[k] < 0 || qb[k] >= B || qy[k] < 0 || qy[k] >= H || qx[k] < 0 || qx[k] >= W) return -1;
+  int fail = 0;
+#pragma omp parallel
+  {
+    const int cap = ws * ws;
+    int* ty = (int*)malloc(sizeof(int) * cap);
+    int* tx = (int*)malloc(sizeof(int) * cap);
+    int* tn = (int*)malloc(sizeof(int) * cap);
+    double* Sc = (double*)malloc(sizeof(double) * cap);
+    double* Bm = (double*)malloc(sizeof(double) * cap);
+    double* P = (double*)malloc(sizeof(double) * cap);
+    if (!ty || !tx || !tn || !Sc || !Bm || !P) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (long t = 0; t < (long)nq * heads; ++t) {
+        int k = (int)(t / heads), h = (int)(t % heads);
+        int nt = window_tokens(&p, qy[k] / ws, qx[k] / ws, ty, tx, tn);
+        int i = -1;
+        for (int j = 0; j < nt; ++j)
+          if (ty[j] == qy[k] && tx[j] == qx[k]) i = j;
+        attend_row(&p, qb[k], h, i, nt, ty, tx, tn, Sc, Bm, P, out + ((size_t)k * heads + h) * dh);
+      }
+    }
+    free(ty); free(tx); free(tn); free(Sc); free(Bm); free(P);
+  }
+  return fail ? -1 : 0;
+}
+
+/*
+ * Debug view of one (image b, window (wy,wx), head h): the content score
+ * matrix Sc, the explicit bias matrix Bm and the softmax P, each nt x nt
+ * row-major over the window's real tokens in map scan order; token (y, x)
+ * and in-window index n are returned in ty/tx/tn.  Caller provides arrays of
+ * ws*ws entries (ws^4 for the matrices).  Returns nt, or -1.
+ */
+int rib_oracle_window_debug(const double* qc, const double* kc, const double* v, const double* g,
+                            const double* qp, const double* kp, int B, int H, int W, int heads,
+                            int dh, int R, int ws, int b, int wy, int wx, int h, double* Sc,
+                            double* Bm, double* P, int* ty, int* tx, int* tn) {
+  problem p = {qc, kc, v, g, qp, kp, B, H, W, heads, dh, R, ws};
+  if (check_problem(&p) || b < 0 || b >= B || h < 0 || h >= heads) return -1;
+  int nt = window_tokens(&p, wy, wx, ty, tx, tn);
+  double* out = (double*)malloc(sizeof(double) * dh);
+  if (!out) return -1;
+  for (int i = 0; i < nt; ++i)
+    attend_row(&p, b, h, i, nt, ty, tx, tn, Sc + (size_t)i * nt, Bm + (size_t)i * nt,
+               P + (size_t)i * nt, out);
+  free(out);
+  return nt;
+}

@@ -1,0 +1,158 @@
+"""RIB window attention with the CLA gate on MI355X (gfx950).
+
+A thin ctypes binding over ``librib.so`` (the hand-written HIP kernels behind
+the C ABI in ``include/rib.h``).  The binding only marshals arguments: it
+checks devices, dtypes, shapes and contiguity, allocates outputs with torch and
+passes raw device pointers plus torch's current HIP stream.  Every step of the
+computation runs in the library's kernels; there is no fallback path, and the
+calls raise if the library is missing.
+
+    qp, kp = encode(window, L, hidden, R, weights)          # once per window size
+    o = window_attn(qc, kc, v, g, qp, kp, heads, window)    # per layer call
+
+Method: "Rank-Factorized Implicit Neural Bias: Scaling Super-Resolution
+Transformer with FlashAttention" (gist.science summaries, part A/B;
+omica.com.cn explainer, sections 2.2, 2.3 and 5.2).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librib.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "rib.h")
+
+RIB_OK, RIB_ERR_INVALID_ARG, RIB_ERR_UNSUPPORTED, RIB_ERR_HIP = 0, 1, 2, 3
+RIB_F32, RIB_BF16 = 0, 1
+
+_lib = None
+
+
+class RibError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"rib status {status}: {message}")
+        self.status = status
+
+
+def lib(path: str | None = None):
+    """Load librib.so (built in-tree by ``build.py``); raise if it is not there."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build the HIP library first "
+                           "(python super_resolution_transformer_amd/build.py)")
+    L = ctypes.CDLL(p)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    L.rib_encode.argtypes = [i, i, i, i, vp, vp, vp, vp]
+    L.rib_encode.restype = i
+    L.rib_window_attn.argtypes = [vp] * 7 + [i] * 8 + [vp]
+    L.rib_window_attn.restype = i
+    L.rib_attn_supported.argtypes = [i, i, i, i]
+    L.rib_attn_supported.restype = i
+    L.rib_last_error.argtypes = []
+    L.rib_last_error.restype = ctypes.c_char_p
+    L.rib_abi_version.argtypes = []
+    L.rib_abi_version.restype = i
+    if path is None:
+        _lib = L
+    return L
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/rib.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(rib_\w+)\s*\(", text, flags=re.M)
+
+
+def _check(status: int) -> None:
+    if status != RIB_OK:
+        raise RibError(status, lib().rib_last_error().decode())
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def weight_count(L: int, hidden: int, R: int) -> int:
+    """Length of the packed weight vector W_h | b_h | Wp_q | Wp_k."""
+    return (2 + 4 * L) * hidden + hidden + 2 * hidden * R
+
+
+def encode(window: int, L: int, hidden: int, R: int, weights):
+    """Positional factors (Qp, Kp), each float32 [window*window, R], on the weights' device."""
+    import torch
+    if not (weights.is_cuda and weights.dtype == torch.float32 and weights.is_contiguous()):
+        raise ValueError("weights must be a contiguous float32 GPU tensor")
+    if weights.numel() != weight_count(L, hidden, R):
+        raise ValueError("packed weight vector has the wrong length")
+    qp = torch.empty((window * window, R), dtype=torch.float32, device=weights.device)
+    kp = torch.empty_like(qp)
+    encode_into(window, L, hidden, R, weights, qp, kp)
+    return qp, kp
+
+
+def encode_into(window, L, hidden, R, weights, qp, kp) -> None:
+    _check(lib().rib_encode(window, L, hidden, R, _ptr(weights), _ptr(qp), _ptr(kp), _stream(weights)))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return RIB_F32
+    if t.dtype == torch.bfloat16:
+        return RIB_BF16
+    raise ValueError("feature maps must be float32 or bfloat16")
+
+
+def window_attn(qc, kc, v, g, qp, kp, heads: int, window: int):
+    """O = (softmax([Qc/sqrt(dh), Qp/sqrt(R)] [Kc, Kp]^T) V) * sigmoid(G) per window and head.
+
+    qc, kc, v, g: [B, H, W, heads*dh] contiguous GPU tensors (float32 or bfloat16);
+    qp, kp: float32 [window*window, R] from ``encode``.  Returns O like qc.
+    """
+    import torch
+    o = torch.empty_like(qc)
+    window_attn_into(qc, kc, v, g, qp, kp, heads, window, o)
+    return o
+
+
+def window_attn_into(qc, kc, v, g, qp, kp, heads: int, window: int, o) -> None:
+    import torch
+    ts = (qc, kc, v, g, o)
+    if any(t.dim() != 4 for t in ts) or any(t.shape != qc.shape for t in ts):
+        raise ValueError("qc, kc, v, g, o must all be [B, H, W, C]")
+    if any(t.dtype != qc.dtype for t in ts):
+        raise ValueError("qc, kc, v, g, o must share one dtype")
+    if not all(t.is_cuda and t.is_contiguous() for t in ts + (qp, kp)):
+        raise ValueError("all tensors must be contiguous GPU tensors")
+    if qp.dtype != torch.float32 or kp.dtype != torch.float32 or qp.shape != kp.shape or qp.dim() != 2:
+        raise ValueError("qp, kp must be float32 [window*window, R]")
+    if qp.shape[0] != window * window:
+        raise ValueError("qp, kp must have window*window rows")
+    B, H, W, C = qc.shape
+    if heads < 1 or C % heads:
+        raise ValueError("channel count must be a multiple of heads")
+    dh, R = C // heads, qp.shape[1]
+    _check(lib().rib_window_attn(_ptr(qc), _ptr(kc), _ptr(v), _ptr(g), _ptr(qp), _ptr(kp), _ptr(o),
+                                 B, H, W, heads, dh, R, window, _dtype_code(qc), _stream(qc)))
+
+
+def supported(dh: int, R: int, window: int, dtype) -> bool:
+    """Whether rib_window_attn has a compiled variant for this shape and dtype."""
+    code = _dtype_code_from(dtype)
+    return lib().rib_attn_supported(dh, R, window, code) == RIB_OK
+
+
+def _dtype_code_from(dtype) -> int:
+    import torch
+    return {torch.float32: RIB_F32, torch.bfloat16: RIB_BF16}[dtype]

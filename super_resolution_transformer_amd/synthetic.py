@@ -1,0 +1,128 @@
+"""Seeded synthetic inputs for RIB window attention.
+
+This module holds none of the method's arithmetic: it draws random tensors of
+the shapes the pages describe and rounds them to bf16 when asked.  Both the
+GPU path's tests and the CPU oracle read the arrays it returns, so the two
+always see bit-identical inputs.
+
+Workloads (shapes from the omica.com.cn explainer: width D=180 with 6 heads,
+section 3.1; SST-lite D=48 / 3 heads / R=16, section 5.1; L=10 frequency
+bands, section 2.2; cyclic windows 16/32/64, section 3.2; 96x96 windows and
+training patches, gist.science summaries part 3; 1280x720 and 640x360 inputs,
+explainer sections 2.1 and 5.1):
+
+  tiny-fp32         1 x 64x64,   C=48  (3 x 16), window 16, fp32
+  sst-lite-bf16     1 x 180x320, C=48  (3 x 16), windows 16, 32, 64
+  sst-infer-bf16    1 x 180x320, C=180 (6 x 30), window 64
+  sst-train-bf16   32 x 96x96,   C=180 (6 x 30), window 96
+  large-input-bf16  1 x 360x640, C=180 (6 x 30), window 96
+
+Every config uses R=16, L=10 and a hidden width of 64.  Feature maps are
+N(0,1); the coordinate-MLP weights are N(0, 1/fan_in) with fan_in = 2+4L for
+W_h and b_h and fan_in = hidden for the two rank heads.  Draw order: Qc, Kc,
+V, G, then W_h, b_h, Wp_q, Wp_k, from numpy's PCG64 with the config's seed.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    dtype: str            # "f32" or "bf16"
+    B: int
+    H: int
+    W: int
+    heads: int
+    dh: int
+    windows: tuple
+    R: int = 16
+    L: int = 10
+    hidden: int = 64
+    seed: int = 0
+
+    @property
+    def C(self) -> int:
+        return self.heads * self.dh
+
+
+CONFIGS = {
+    1: Config("tiny-fp32", "f32", 1, 64, 64, 3, 16, (16,), seed=0),
+    2: Config("sst-lite-bf16", "bf16", 1, 180, 320, 3, 16, (16, 32, 64), seed=1),
+    3: Config("sst-infer-bf16", "bf16", 1, 180, 320, 6, 30, (64,), seed=2),
+    4: Config("sst-train-bf16", "bf16", 32, 96, 96, 6, 30, (96,), seed=3),
+    5: Config("large-input-bf16", "bf16", 1, 360, 640, 6, 30, (96,), seed=4),
+}
+
+
+def round_bf16(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Round float32 values to bf16, nearest-even.  Returns (uint16 bits, float32 values)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32)
+    bias = ((b >> 16) & 1) + np.uint32(0x7FFF)
+    r = ((b + bias) & np.uint32(0xFFFF0000)).astype(np.uint32)
+    return (r >> 16).astype(np.uint16), r.view(np.float32)
+
+
+def weight_count(L: int, hidden: int, R: int) -> int:
+    return (2 + 4 * L) * hidden + hidden + 2 * hidden * R
+
+
+@dataclass
+class Problem:
+    """One set of inputs.  ``*_f32`` hold the exact values (bf16-representable
+    when dtype is bf16); ``*_bits`` hold the bf16 bit patterns (bf16 only)."""
+    B: int
+    H: int
+    W: int
+    heads: int
+    dh: int
+    R: int
+    L: int
+    hidden: int
+    dtype: str
+    qc: np.ndarray
+    kc: np.ndarray
+    v: np.ndarray
+    g: np.ndarray
+    weights: np.ndarray          # packed float32: W_h | b_h | Wp_q | Wp_k
+    bits: dict = field(default_factory=dict)
+
+    @property
+    def C(self) -> int:
+        return self.heads * self.dh
+
+
+def draw_weights(rng: np.random.Generator, L: int, hidden: int, R: int) -> np.ndarray:
+    F = 2 + 4 * L
+    wh = rng.standard_normal((F, hidden)) / np.sqrt(F)
+    bh = rng.standard_normal(hidden) / np.sqrt(F)
+    wq = rng.standard_normal((hidden, R)) / np.sqrt(hidden)
+    wk = rng.standard_normal((hidden, R)) / np.sqrt(hidden)
+    return np.concatenate([wh.ravel(), bh, wq.ravel(), wk.ravel()]).astype(np.float32)
+
+
+def make_problem(B: int, H: int, W: int, heads: int, dh: int, R: int = 16, L: int = 10,
+                 hidden: int = 64, dtype: str = "bf16", seed: int = 0) -> Problem:
+    rng = np.random.default_rng(seed)
+    shape = (B, H, W, heads * dh)
+    arrs = [rng.standard_normal(shape, dtype=np.float32) for _ in range(4)]
+    weights = draw_weights(rng, L, hidden, R)
+    bits = {}
+    if dtype == "bf16":
+        names = ("qc", "kc", "v", "g")
+        for i, nm in enumerate(names):
+            bits[nm], arrs[i] = round_bf16(arrs[i])
+    elif dtype != "f32":
+        raise ValueError("dtype must be 'f32' or 'bf16'")
+    return Problem(B, H, W, heads, dh, R, L, hidden, dtype, *arrs, weights=weights, bits=bits)
+
+
+def config_problem(idx: int, batch: int | None = None) -> Problem:
+    """Inputs of one of the five workloads (``batch`` overrides B, e.g. for a CPU sample)."""
+    c = CONFIGS[idx]
+    return make_problem(c.B if batch is None else batch, c.H, c.W, c.heads, c.dh, c.R, c.L,
+                        c.hidden, c.dtype, c.seed)
