@@ -1,0 +1,463 @@
+// attn_bf16.hip -- bf16 MFMA RIB window attention with the CLA gate (gfx950).
+//
+// Per image, window and head ("Rank-Factorized Implicit Neural Bias",
+// gist.science summaries part A mechanism steps 3-4 and part B; omica.com.cn
+// explainer sections 2.2 "attention rewrite" and 2.3):
+//   Q~ = [Qp/sqrt(R), Qc/sqrt(dh)],  K~ = [Kp, Kc]
+//   S  = Q~ K~^T  (content score + positional bias in one contraction)
+//   O  = (softmax(S) V) * sigmoid(G)
+// (The pages concatenate content first; the column order of a contraction does
+// not change its value, and positional-first keeps the LDS rows aligned.)
+//
+// Design (one workgroup = 4 waves = 256 queries of one (image, window, head)):
+//
+//  * Scores are computed transposed, S^T = K~ Q~^T, with
+//    v_mfma_f32_32x32x16_bf16: K~ rows are the A operand (read from LDS), the
+//    wave's queries are the B operand (kept in VGPRs for the whole loop).  In
+//    the 32x32 accumulator each lane then owns ONE query and 16 of the 32 keys
+//    of a block, so softmax row statistics are in-lane plus one
+//    v_permlane32_swap.
+//  * The same accumulator registers, rounded to bf16, are exactly the B
+//    operand of O^T = V^T P^T, provided V^T is stored in LDS with the keys in
+//    the accumulator's row order.  P never leaves registers.
+//  * Softmax runs in base 2: log2(e) is folded into the query scales.  Two
+//    spare contraction columns (dh+R+2 <= 16*KC) carry the running maximum:
+//    column "m" holds -m_hat in Q~ (a bf16 value) against 1 in K~, column "o"
+//    holds -OFF in Q~ against 1 in K~ (2^14 for padded keys, which masks them,
+//    and 0 in column m).  The MFMA therefore returns t = s*log2(e) - m_hat -
+//    OFF directly and the fast path is just p = exp2(t).
+//  * Rescaling is lazy: p = exp2(t) <= 2^-OFF * 2^(growth of the maximum).
+//    The packed bf16 P values are OR-reduced; bit 14 of a half is set iff
+//    p >= 2, i.e. the maximum grew by more than OFF+1 = 8 (factor 256).  Only
+//    then (and on the first tile) does the wave take the slow path: exact row
+//    maximum, new m_hat rounded to bf16, subtract, exp2 again, rescale O.
+//  * The row sum l comes for free from the PV MFMA: V^T row dh is all ones.
+//  * Key tiles of KT = 64 keys are double-buffered in LDS with one barrier per
+//    tile; the next tile's global loads are issued before the current tile's
+//    MFMAs.  Window partitioning is pure index arithmetic on the NHWC arrays:
+//    a window's real tokens are enumerated row-major, r = iy*nx + ix, so
+//    padded positions are never loaded, and only the last tile can hold
+//    padded keys.
+//  * Workgroups are numbered so that the q-blocks of one (image, window, head)
+//    are consecutive on one XCD (shared K/V in that XCD's L2).
+#include "rib_device.hpp"
+#include "rib_launch.hpp"
+
+namespace rib {
+
+namespace {
+
+constexpr int KT = 64;             // keys per tile
+constexpr int NWAVE = 4;           // waves per workgroup
+constexpr int QW = 64;             // queries per wave (two 32-query MFMA blocks)
+constexpr int QB = QW * NWAVE;     // queries per workgroup
+constexpr float OFF = 7.0f;        // p = exp2(s - m_hat - OFF) <= 2^-OFF normally
+constexpr float LOG2E = 1.4426950408889634f;
+
+template <int DH, int R>
+struct Shape {
+  static_assert(DH % 2 == 0 && R % 2 == 0, "head dim and rank must be even");
+  static constexpr int KC = (R + DH + 2 + 15) / 16;  // 16-wide contraction chunks
+  static constexpr int DT = (DH + 1 + 31) / 32;      // 32-row output tiles (ones row at DH)
+  static constexpr int ROWDW = 8 * KC;               // dwords per Q~/K~ row
+  static constexpr int KSTR = ROWDW + 4;             // LDS row stride in dwords (bank spread)
+  static constexpr int CONSTDW = R / 2 + DH / 2;     // dword with columns (m, o)
+  static constexpr int CM = CONSTDW / 8;             // chunk holding it
+  static constexpr int GM = (CONSTDW % 8) / 4;       // lane half holding it
+  static constexpr int DM = CONSTDW % 4;             // dword inside the 16-byte operand
+  static constexpr int VDW = 16 * DT;                // dwords per V row (d < 32*DT)
+  static constexpr int VSTR = KT / 2 + 4;            // dwords per transposed V row
+  static constexpr int KS_DW = KT * KSTR;
+  static constexpr int VS_DW = 32 * DT * VSTR;
+  static constexpr int STAGE_DW = KS_DW + VS_DW;
+  static constexpr int QS_DW = QB * KSTR;
+  static constexpr int LDS_DW = (2 * STAGE_DW > QS_DW) ? 2 * STAGE_DW : QS_DW;
+  // accumulator position of the row sum (V^T row DH)
+  static constexpr int LT = DH / 32;
+  static constexpr int LW = DH % 32;
+  static constexpr int LR = 4 * (LW / 8) + (LW % 4);
+  static constexpr int LG = (LW / 4) % 2;
+  // per-lane staging registers for the next tile
+  static constexpr int KREG = ROWDW / 2;
+  static constexpr int VREG = VDW / 2;
+  static constexpr int NREG = KREG > VREG ? KREG : VREG;
+  static_assert(KC <= 4 && DT <= 2, "variant too large");
+};
+
+struct Geo {
+  const uint32_t* qc;
+  const uint32_t* kc;
+  const uint32_t* v;
+  const uint32_t* g;
+  const float* qp;
+  const float* kp;
+  uint32_t* o;
+  int H, W, C, ws, b, wy, wx, h, nx, n_real;
+  float inv_nx;
+};
+
+// real index r of a window -> element offset of the token's head slice and
+// in-window index n
+template <int DH>
+__device__ __forceinline__ void locate(const Geo& G, int r, int& off, int& n) {
+  const int iy = (int)(((float)r + 0.5f) * G.inv_nx);
+  const int ix = r - iy * G.nx;
+  off = ((G.b * G.H + G.wy * G.ws + iy) * G.W + G.wx * G.ws + ix) * G.C + G.h * DH;
+  n = iy * G.ws + ix;
+}
+
+// ---- staging of one key tile ------------------------------------------------
+// Each wave has one role for the whole kernel (wave-uniform branches):
+//   role 0: the key's positional factor Kp (R fp32, converted to bf16 at store)
+//   role 1: the key's content Kc (dh bf16) + the (m, o) column pair
+//   role 2/3: the two halves of the key's V row (+ the ones row at d = dh),
+//             written transposed.
+// Every role fills the same NV 16-byte registers with raw loads, so the four
+// paths merge cleanly into one set of VGPRs.
+template <int DH, int R>
+struct Stage {
+  static constexpr int NV0 = R / 4;
+  static constexpr int NV1 = (DH / 2 + 3) / 4;
+  static constexpr int NV2 = 2 * Shape<DH, R>::DT;
+  static constexpr int NV = NV0 > NV1 ? (NV0 > NV2 ? NV0 : NV2) : (NV1 > NV2 ? NV1 : NV2);
+  u32x4_t raw[NV];
+};
+
+template <int DH, int R>
+__device__ __forceinline__ void load_tile(const Geo& G, int wave, int r, Stage<DH, R>& st) {
+  using T = Stage<DH, R>;
+  int off, n;
+  locate<DH>(G, r < G.n_real ? r : G.n_real - 1, off, n);
+  if (wave == 0) {
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(G.kp + n * R);
+#pragma unroll
+    for (int i = 0; i < T::NV; ++i) st.raw[i] = i < T::NV0 ? src[i] : (u32x4_t){0u, 0u, 0u, 0u};
+  } else {
+    const uint32_t* src = (wave == 1 ? G.kc : G.v) + (off >> 1);
+    const int base = wave == 3 ? 8 * Shape<DH, R>::DT : 0;  // V dword offset of this half
+#pragma unroll
+    for (int i = 0; i < T::NV; ++i) {
+      uint32_t d[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int w = base + 4 * i + e;
+        d[e] = w < DH / 2 ? src[w] : 0u;
+      }
+      st.raw[i] = (u32x4_t){d[0], d[1], d[2], d[3]};
+    }
+  }
+}
+
+// position of key j (0..KT-1) in the transposed V tile: the key order of the
+// S^T accumulator rows, grouped as the PV MFMA's contraction index expects
+__device__ __forceinline__ int vpos(int j) {
+  const int kb = j >> 5, w = j & 31;
+  const int c = w >> 4, eh = (w >> 3) & 1, g = (w >> 2) & 1, el = w & 3;
+  return kb * 32 + 16 * c + 8 * g + 4 * eh + el;
+}
+
+template <int DH, int R>
+__device__ __forceinline__ void store_tile(uint32_t* stage, int wave, int j, bool real,
+                                           const Stage<DH, R>& st) {
+  using S = Shape<DH, R>;
+  if (wave == 0) {
+    uint32_t* dst = stage + j * S::KSTR;
+#pragma unroll
+    for (int i = 0; i < R / 8; ++i) {
+      const f32x4_t a = __builtin_bit_cast(f32x4_t, st.raw[2 * i]);
+      const f32x4_t b = __builtin_bit_cast(f32x4_t, st.raw[2 * i + 1]);
+      u32x4_t out = {pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(b[0], b[1]),
+                     pack_bf16(b[2], b[3])};
+      if (!real) out = (u32x4_t){0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t*>(dst + 4 * i) = out;
+    }
+  } else if (wave == 1) {
+    uint32_t* dst = stage + j * S::KSTR + R / 2;
+#pragma unroll
+    for (int i = 0; i < (S::ROWDW - R / 2) / 4; ++i) {
+      uint32_t d[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int w = 4 * i + e;
+        uint32_t val;
+        if (w < DH / 2) val = real ? st.raw[w / 4][w % 4] : 0u;
+        else if (w == DH / 2) val = real ? 0x3F803F80u : 0x46800000u;  // (1,1) real, (0,2^14) padded
+        else val = 0u;
+        d[e] = val;
+      }
+      *reinterpret_cast<u32x4_t*>(dst + 4 * i) = (u32x4_t){d[0], d[1], d[2], d[3]};
+    }
+  } else {
+    uint32_t* vs = stage + S::KS_DW;
+    const bool odd = j & 1;
+    const int col = vpos(j & ~1) >> 1;
+    const int base = wave == 3 ? 8 * S::DT : 0;
+#pragma unroll
+    for (int i = 0; i < 8 * S::DT; ++i) {
+      const int w = base + i;
+      uint32_t mine = st.raw[i / 4][i % 4];
+      mine = w == DH / 2 ? 0x00003F80u : mine;  // (1, 0): ones row at d = DH
+      mine = real ? mine : 0u;
+      const uint32_t nb = lane_xor1(mine);
+      // even lane: channel 2w of keys (j, j+1); odd lane: channel 2w+1 of keys (j-1, j)
+      const uint32_t ev = (mine & 0xFFFFu) | (nb << 16);
+      const uint32_t od = (nb >> 16) | (mine & 0xFFFF0000u);
+      vs[(2 * w + (odd ? 1 : 0)) * S::VSTR + col] = odd ? od : ev;
+    }
+  }
+}
+
+template <int DH, int R>
+__global__ void __launch_bounds__(QB, 2)
+attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
+                 const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
+                 const float* __restrict__ qp, const float* __restrict__ kp,
+                 uint32_t* __restrict__ o, int B, int H, int W, int heads, int ws, int total) {
+  using S = Shape<DH, R>;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[S::LDS_DW];
+
+  const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
+  if (logical >= total) return;
+  const int nWy = (H + ws - 1) / ws, nWx = (W + ws - 1) / ws;
+  const int qblocks = (ws * ws + QB - 1) / QB;
+  Geo G;
+  int q0;
+  {
+    int t = logical;
+    const int qblk = t % qblocks; t /= qblocks;
+    G.h = t % heads; t /= heads;
+    G.wx = t % nWx; t /= nWx;
+    G.wy = t % nWy;
+    G.b = t / nWy;
+    G.qc = qc; G.kc = kc; G.v = v; G.g = g; G.qp = qp; G.kp = kp; G.o = o;
+    G.H = H; G.W = W; G.C = heads * DH; G.ws = ws;
+    G.nx = min(ws, W - G.wx * ws);
+    G.n_real = min(ws, H - G.wy * ws) * G.nx;
+    G.inv_nx = 1.0f / (float)G.nx;
+    q0 = qblk * QB;
+    if (q0 >= G.n_real) return;
+  }
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int gh = lane >> 5;  // lane half
+
+  // ---- prologue: build the workgroup's Q~ rows in LDS, then pick up the B operands
+  {
+    const int r = q0 + tid;
+    const bool real = r < G.n_real;
+    int off, n;
+    locate<DH>(G, real ? r : G.n_real - 1, off, n);
+    const float sp = LOG2E / sqrtf((float)R);
+    const float sc = LOG2E / sqrtf((float)DH);
+    uint32_t row[S::ROWDW];
+#pragma unroll
+    for (int w = 0; w < S::ROWDW; ++w) {
+      uint32_t val;
+      if (w < R / 2) {
+        const float2 pq = *reinterpret_cast<const float2*>(qp + n * R + 2 * w);
+        val = pack_bf16(pq.x * sp, pq.y * sp);
+      } else if (w < R / 2 + DH / 2) {
+        const uint32_t x = qc[(off >> 1) + (w - R / 2)];
+        val = pack_bf16(bf16_lo(x) * sc, bf16_hi(x) * sc);
+      } else if (w == S::CONSTDW) {
+        val = 0xC0E00000u;  // (-m_hat = 0, -OFF = -7)
+      } else {
+        val = 0u;
+      }
+      row[w] = (real || w == S::CONSTDW) ? val : 0u;
+    }
+    uint32_t* dst = lds + tid * S::KSTR;
+#pragma unroll
+    for (int w = 0; w < S::ROWDW; w += 4)
+      *reinterpret_cast<u32x4_t*>(dst + w) = (u32x4_t){row[w], row[w + 1], row[w + 2], row[w + 3]};
+  }
+  __syncthreads();
+  u32x4_t qt[2][S::KC];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int c = 0; c < S::KC; ++c)
+      qt[qb][c] = *reinterpret_cast<const u32x4_t*>(lds + (wave * QW + qb * 32 + l32) * S::KSTR + 8 * c + 4 * gh);
+  __syncthreads();
+
+  const int ntiles = (G.n_real + KT - 1) / KT;
+  const bool active = q0 + wave * QW < G.n_real;
+  Stage<DH, R> st;
+  load_tile<DH, R>(G, wave, lane, st);
+  store_tile<DH, R>(lds, wave, lane, lane < G.n_real, st);
+  __syncthreads();
+
+  f32x16_t O[2][S::DT];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) O[qb][dt][e] = 0.0f;
+  float mhat[2] = {0.0f, 0.0f};
+
+  for (int it = 0; it < ntiles; ++it) {
+    const uint32_t* stage = lds + (it & 1) * S::STAGE_DW;
+    const bool more = it + 1 < ntiles;
+    if (more) load_tile<DH, R>(G, wave, (it + 1) * KT + lane, st);
+
+    if (active) {
+      // ---- scores: S^T = K~ Q~^T for 64 keys x 64 queries
+      f32x16_t Sacc[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        u32x4_t a[S::KC];
+#pragma unroll
+        for (int c = 0; c < S::KC; ++c)
+          a[c] = *reinterpret_cast<const u32x4_t*>(stage + (kb * 32 + l32) * S::KSTR + 8 * c + 4 * gh);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          f32x16_t acc;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+          for (int c = 0; c < S::KC; ++c)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[c]),
+                                                          __builtin_bit_cast(bf16x8_t, qt[qb][c]), acc, 0, 0, 0);
+          Sacc[qb][kb] = acc;
+        }
+      }
+      // ---- fast path: p = exp2(t), packed to bf16
+      uint32_t P[2][2][8];
+      uint32_t orv = 0;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            P[qb][kb][i] = pack_bf16(__builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i]),
+                                     __builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i + 1]));
+            orv |= P[qb][kb][i];
+          }
+      const bool need = (it == 0) || (orv & 0x40004000u);
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        // ---- slow path: exact maximum, new reference, recompute, rescale
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, Sacc[qb][kb][e]);
+          const LanePair pr = lane_pair(mx);
+          mx = fmaxf(pr.lo, pr.hi);
+          const bool grow = (it == 0) || (mx + OFF > 0.0f);
+          const float mnew = grow ? round_bf16(mhat[qb] + mx + OFF) : mhat[qb];
+          const float shift = mnew - mhat[qb];
+          mhat[qb] = mnew;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              P[qb][kb][i] = pack_bf16(__builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i] - shift),
+                                       __builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i + 1] - shift));
+          if (it > 0) {
+            const float sc = __builtin_amdgcn_exp2f(-shift);
+#pragma unroll
+            for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) O[qb][dt][e] *= sc;
+          }
+          const uint32_t cd = pack_bf16(-mnew, -OFF);
+          if (gh == S::GM) qt[qb][S::CM][S::DM] = cd;
+        }
+      }
+      // ---- O^T += V^T P^T
+      const uint32_t* vs = stage + S::KS_DW;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          u32x4_t va[S::DT];
+#pragma unroll
+          for (int dt = 0; dt < S::DT; ++dt)
+            va[dt] = *reinterpret_cast<const u32x4_t*>(vs + (dt * 32 + l32) * S::VSTR + kb * 16 + 8 * c2 + 4 * gh);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const u32x4_t pb = {P[qb][kb][4 * c2], P[qb][kb][4 * c2 + 1], P[qb][kb][4 * c2 + 2],
+                                P[qb][kb][4 * c2 + 3]};
+#pragma unroll
+            for (int dt = 0; dt < S::DT; ++dt)
+              O[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va[dt]),
+                                                                  __builtin_bit_cast(bf16x8_t, pb), O[qb][dt], 0, 0, 0);
+          }
+        }
+    }
+    if (more) store_tile<DH, R>(lds + ((it + 1) & 1) * S::STAGE_DW, wave, lane, (it + 1) * KT + lane < G.n_real, st);
+    __syncthreads();
+  }
+
+  if (!active) return;
+  // ---- epilogue: O / l * sigmoid(G), bf16, NHWC
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = q0 + wave * QW + qb * 32 + l32;
+    const LanePair pr = lane_pair(O[qb][S::LT][S::LR]);
+    const float lsum = S::LG ? pr.hi : pr.lo;
+    if (r >= G.n_real) continue;
+    const float inv = 1.0f / lsum;
+    int off, n;
+    locate<DH>(G, r, off, n);
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = dt * 32 + 8 * q4 + 4 * gh;
+        if (d0 >= DH) continue;
+        const int e0 = 4 * q4;
+        const int gw = (off + d0) >> 1;  // dword index of channels (d0, d0+1)
+        const uint32_t g01 = g[gw];
+        const uint32_t r01 = pack_bf16(O[qb][dt][e0 + 0] * inv * sigmoidf(bf16_lo(g01)),
+                                       O[qb][dt][e0 + 1] * inv * sigmoidf(bf16_hi(g01)));
+        if (d0 + 4 <= DH) {
+          const uint32_t g23 = g[gw + 1];
+          const uint32_t r23 = pack_bf16(O[qb][dt][e0 + 2] * inv * sigmoidf(bf16_lo(g23)),
+                                         O[qb][dt][e0 + 3] * inv * sigmoidf(bf16_hi(g23)));
+          o[gw] = r01;
+          o[gw + 1] = r23;
+        } else {
+          o[gw] = r01;
+        }
+      }
+  }
+}
+
+template <int DH, int R>
+hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
+  const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws;
+  const int qblocks = (a.ws * a.ws + QB - 1) / QB;
+  const int total = a.B * nWy * nWx * a.heads * qblocks;
+  const int grid = 8 * ((total + 7) / 8);
+  hipLaunchKernelGGL((attn_bf16_kernel<DH, R>), dim3(grid), dim3(QB), 0, stream,
+                     (const uint32_t*)a.qc, (const uint32_t*)a.kc, (const uint32_t*)a.v,
+                     (const uint32_t*)a.g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.H, a.W, a.heads, a.ws,
+                     total);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_bf16_supported(int dh, int R) {
+  return (dh == 8 && R == 8) || (dh == 16 && R == 16) || (dh == 30 && R == 16) ||
+         (dh == 32 && R == 16) || (dh == 16 && R == 32) || (dh == 30 && R == 32);
+}
+
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream) {
+  if (a.dh == 8 && a.R == 8) return launch_variant<8, 8>(a, stream);
+  if (a.dh == 16 && a.R == 16) return launch_variant<16, 16>(a, stream);
+  if (a.dh == 30 && a.R == 16) return launch_variant<30, 16>(a, stream);
+  if (a.dh == 32 && a.R == 16) return launch_variant<32, 16>(a, stream);
+  if (a.dh == 16 && a.R == 32) return launch_variant<16, 32>(a, stream);
+  if (a.dh == 30 && a.R == 32) return launch_variant<30, 32>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace rib

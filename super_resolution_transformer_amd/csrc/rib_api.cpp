@@ -1,0 +1,116 @@
+// rib_api.cpp -- the C ABI declared in include/rib.h: argument validation,
+// variant selection and error reporting.  Validation runs entirely on the host
+// and makes no HIP call, so every error path can be exercised without a GPU.
+#include "../../include/rib.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "rib_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+rib_status fail(rib_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+rib_status fail(rib_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+rib_status ok() {
+  g_err[0] = '\0';
+  return RIB_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+rib_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(RIB_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int rib_abi_version(void) { return RIB_ABI_VERSION; }
+
+const char* rib_last_error(void) { return g_err; }
+
+rib_status rib_encode(int window, int L, int hidden, int R, const float* weights, float* qp,
+                      float* kp, void* stream) {
+  if (!weights || !qp || !kp) return fail(RIB_ERR_INVALID_ARG, "rib_encode: null pointer");
+  if (window < 2) return fail(RIB_ERR_INVALID_ARG, "rib_encode: window must be >= 2 (got %d)", window);
+  if (L < 0 || hidden < 1 || R < 1)
+    return fail(RIB_ERR_INVALID_ARG, "rib_encode: need L >= 0, hidden >= 1, R >= 1 (got %d, %d, %d)", L,
+                hidden, R);
+  if (window > 128 || L > 16 || hidden > 256 || R > 64)
+    return fail(RIB_ERR_UNSUPPORTED,
+                "rib_encode: limits are window <= 128, L <= 16, hidden <= 256, R <= 64 (got %d, %d, %d, %d)",
+                window, L, hidden, R);
+  if (!aligned(weights, 4) || !aligned(qp, 4) || !aligned(kp, 4))
+    return fail(RIB_ERR_INVALID_ARG, "rib_encode: pointers must be 4-byte aligned");
+  const size_t nw = sizeof(float) * ((size_t)(2 + 4 * L) * hidden + hidden + 2 * (size_t)hidden * R);
+  const size_t no = sizeof(float) * (size_t)window * window * R;
+  if (overlap(qp, no, kp, no) || overlap(qp, no, weights, nw) || overlap(kp, no, weights, nw))
+    return fail(RIB_ERR_INVALID_ARG, "rib_encode: qp, kp and weights must not overlap");
+  return hip_status(rib::launch_encode(window, L, hidden, R, weights, qp, kp, (hipStream_t)stream),
+                    "rib_encode launch");
+}
+
+rib_status rib_attn_supported(int dh, int R, int window, rib_dtype dtype) {
+  if (dh < 1 || R < 1 || window < 2) return fail(RIB_ERR_INVALID_ARG, "dh, R >= 1 and window >= 2 required");
+  if (dtype != RIB_F32 && dtype != RIB_BF16) return fail(RIB_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (window > 128) return fail(RIB_ERR_UNSUPPORTED, "window %d > 128", window);
+  if (dtype == RIB_F32) {
+    if (dh > 64 || R > 64) return fail(RIB_ERR_UNSUPPORTED, "fp32 path: dh and R must be <= 64");
+    return ok();
+  }
+  if (!rib::attn_bf16_supported(dh, R))
+    return fail(RIB_ERR_UNSUPPORTED, "bf16 path: no compiled variant for (dh=%d, R=%d)", dh, R);
+  return ok();
+}
+
+rib_status rib_window_attn(const void* qc, const void* kc, const void* v, const void* g,
+                           const float* qp, const float* kp, void* o, int B, int H, int W,
+                           int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
+  if (!qc || !kc || !v || !g || !qp || !kp || !o)
+    return fail(RIB_ERR_INVALID_ARG, "rib_window_attn: null pointer");
+  if (B < 1 || H < 1 || W < 1 || heads < 1 || dh < 1 || R < 1)
+    return fail(RIB_ERR_INVALID_ARG, "rib_window_attn: B, H, W, heads, dh, R must be >= 1");
+  if (window < 2) return fail(RIB_ERR_INVALID_ARG, "rib_window_attn: window must be >= 2 (got %d)", window);
+  if (dtype != RIB_F32 && dtype != RIB_BF16)
+    return fail(RIB_ERR_INVALID_ARG, "rib_window_attn: unknown dtype %d", (int)dtype);
+  const rib_status sup = rib_attn_supported(dh, R, window, dtype);
+  if (sup != RIB_OK) return sup;
+  const uint64_t elems = (uint64_t)B * H * W * (uint64_t)heads * dh;
+  if (elems >= (1ull << 31))
+    return fail(RIB_ERR_UNSUPPORTED, "rib_window_attn: B*H*W*heads*dh must be < 2^31");
+  if (!aligned(qc, 16) || !aligned(kc, 16) || !aligned(v, 16) || !aligned(g, 16) || !aligned(qp, 16) ||
+      !aligned(kp, 16) || !aligned(o, 16))
+    return fail(RIB_ERR_INVALID_ARG, "rib_window_attn: pointers must be 16-byte aligned");
+  const size_t nb = (size_t)elems * (dtype == RIB_F32 ? 4 : 2);
+  const size_t np = sizeof(float) * (size_t)window * window * R;
+  if (overlap(o, nb, qc, nb) || overlap(o, nb, kc, nb) || overlap(o, nb, v, nb) || overlap(o, nb, g, nb) ||
+      overlap(o, nb, qp, np) || overlap(o, nb, kp, np))
+    return fail(RIB_ERR_INVALID_ARG, "rib_window_attn: output overlaps an input");
+  const rib::AttnArgs a{qc, kc, v, g, qp, kp, o, B, H, W, heads, dh, R, window};
+  const hipError_t e = dtype == RIB_F32 ? rib::launch_attn_f32(a, (hipStream_t)stream)
+                                        : rib::launch_attn_bf16(a, (hipStream_t)stream);
+  return hip_status(e, "rib_window_attn launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,28 @@
+// rib_launch.hpp -- internal launchers behind the C ABI (arguments already validated).
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace rib {
+
+struct AttnArgs {
+  const void* qc;
+  const void* kc;
+  const void* v;
+  const void* g;
+  const float* qp;
+  const float* kp;
+  void* o;
+  int B, H, W, heads, dh, R, ws;
+};
+
+hipError_t launch_encode(int ws, int L, int hidden, int R, const float* w, float* qp, float* kp,
+                         hipStream_t stream);
+
+// fp32 path: any dh <= 64, R <= 64.
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
+
+// bf16 MFMA path: returns hipErrorInvalidValue if (dh, R) has no compiled variant.
+bool attn_bf16_supported(int dh, int R);
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace rib

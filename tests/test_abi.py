@@ -1,0 +1,119 @@
+"""The C ABI library on the host: it loads, exports what include/rib.h declares,
+and rejects bad arguments before any HIP call (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import super_resolution_transformer_amd as rib
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(rib.LIB_PATH):
+        from super_resolution_transformer_amd import build
+        build.build()
+    return rib.lib()
+
+
+def test_header_declares_the_boundary():
+    assert set(rib.header_functions()) == {
+        "rib_encode", "rib_window_attn", "rib_attn_supported", "rib_last_error", "rib_abi_version"}
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in rib.header_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version_matches_header(L):
+    m = re.search(r"#define\s+RIB_ABI_VERSION\s+(\d+)", open(rib.HEADER).read())
+    assert L.rib_abi_version() == int(m.group(1))
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        rib.lib(str(tmp_path / "librib.so"))
+
+
+def test_support_query(L):
+    assert L.rib_attn_supported(30, 16, 96, rib.RIB_BF16) == rib.RIB_OK
+    assert L.rib_attn_supported(16, 16, 16, rib.RIB_BF16) == rib.RIB_OK
+    assert L.rib_attn_supported(16, 16, 16, rib.RIB_F32) == rib.RIB_OK
+    assert L.rib_attn_supported(7, 5, 16, rib.RIB_F32) == rib.RIB_OK
+    assert L.rib_attn_supported(31, 16, 16, rib.RIB_BF16) == rib.RIB_ERR_UNSUPPORTED
+    assert L.rib_attn_supported(30, 16, 129, rib.RIB_BF16) == rib.RIB_ERR_UNSUPPORTED
+    assert L.rib_attn_supported(65, 16, 16, rib.RIB_F32) == rib.RIB_ERR_UNSUPPORTED
+    assert L.rib_attn_supported(30, 16, 1, rib.RIB_BF16) == rib.RIB_ERR_INVALID_ARG
+    assert L.rib_attn_supported(30, 16, 16, 7) == rib.RIB_ERR_INVALID_ARG
+    assert "dtype" in L.rib_last_error().decode()
+
+
+# Fake, never-dereferenced device addresses: every call below must fail validation.
+# (Skipped where a GPU is visible, so a validation bug can never launch on them.)
+def _no_gpu():
+    try:
+        import torch
+        return not torch.cuda.is_available()
+    except Exception:
+        return True
+
+
+fake = pytest.mark.skipif(not _no_gpu(), reason="fake-pointer validation checks run only without a GPU")
+MB = 1 << 20
+P = [ctypes.c_void_p(0x10000000 + i * 64 * MB) for i in range(8)]
+
+
+def attn(L, ptrs=None, B=1, H=8, W=8, heads=2, dh=30, R=16, window=8, dtype=rib.RIB_BF16, stream=None):
+    p = list(ptrs or P[:7])
+    return L.rib_window_attn(*p, B, H, W, heads, dh, R, window, dtype, stream)
+
+
+@fake
+def test_attn_validation(L):
+    assert attn(L, [None] + P[1:7]) == rib.RIB_ERR_INVALID_ARG
+    assert "null" in L.rib_last_error().decode()
+    assert attn(L, P[:6] + [None]) == rib.RIB_ERR_INVALID_ARG
+    assert attn(L, B=0) == rib.RIB_ERR_INVALID_ARG
+    assert attn(L, heads=0) == rib.RIB_ERR_INVALID_ARG
+    assert attn(L, window=1) == rib.RIB_ERR_INVALID_ARG
+    assert attn(L, dtype=5) == rib.RIB_ERR_INVALID_ARG
+    assert attn(L, dh=31) == rib.RIB_ERR_UNSUPPORTED
+    assert attn(L, window=200) == rib.RIB_ERR_UNSUPPORTED
+    assert attn(L, B=1 << 12, H=1 << 10, W=1 << 10) == rib.RIB_ERR_UNSUPPORTED   # >= 2^31 elements
+    assert "2^31" in L.rib_last_error().decode()
+    mis = [ctypes.c_void_p(P[0].value + 4)] + P[1:7]
+    assert attn(L, mis) == rib.RIB_ERR_INVALID_ARG
+    assert "aligned" in L.rib_last_error().decode()
+    alias = P[:6] + [ctypes.c_void_p(P[2].value + 256)]                     # o inside v
+    assert attn(L, alias) == rib.RIB_ERR_INVALID_ARG
+    assert "overlap" in L.rib_last_error().decode()
+    alias_qp = P[:6] + [P[4]]                                               # o == qp
+    assert attn(L, alias_qp) == rib.RIB_ERR_INVALID_ARG
+
+
+@fake
+def test_encode_validation(L):
+    w, q, k = P[0], P[1], P[2]
+    assert L.rib_encode(16, 10, 64, 16, None, q, k, None) == rib.RIB_ERR_INVALID_ARG
+    assert L.rib_encode(1, 10, 64, 16, w, q, k, None) == rib.RIB_ERR_INVALID_ARG
+    assert L.rib_encode(16, -1, 64, 16, w, q, k, None) == rib.RIB_ERR_INVALID_ARG
+    assert L.rib_encode(16, 10, 0, 16, w, q, k, None) == rib.RIB_ERR_INVALID_ARG
+    assert L.rib_encode(129, 10, 64, 16, w, q, k, None) == rib.RIB_ERR_UNSUPPORTED
+    assert L.rib_encode(16, 17, 64, 16, w, q, k, None) == rib.RIB_ERR_UNSUPPORTED
+    assert L.rib_encode(16, 10, 64, 16, w, q, q, None) == rib.RIB_ERR_INVALID_ARG     # qp == kp
+    assert L.rib_encode(16, 10, 64, 16, w, w, k, None) == rib.RIB_ERR_INVALID_ARG     # qp == weights
+    assert L.rib_encode(16, 10, 64, 16, ctypes.c_void_p(w.value + 2), q, k, None) == rib.RIB_ERR_INVALID_ARG
+    assert L.rib_last_error().decode() != ""
+
+
+def test_python_binding_argument_checks():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 4, 4, 8)
+    with pytest.raises(ValueError):
+        rib.encode(4, 10, 64, 16, torch.zeros(3))          # not a GPU tensor
+    with pytest.raises(ValueError):
+        rib.window_attn_into(x, x, x, x[:, :2], torch.zeros(16, 4), torch.zeros(16, 4), 2, 4, x)
+    with pytest.raises(ValueError):
+        rib.window_attn_into(x, x, x, x, torch.zeros(16, 4), torch.zeros(16, 4), 2, 4, x)  # CPU tensors

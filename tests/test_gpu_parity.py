@@ -1,0 +1,255 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64 CPU oracle.
+
+Tolerances: max abs error <= 1e-5 for fp32 inputs, <= 2e-2 for bf16 inputs
+with fp32 accumulation; window/index mapping (locality, equivariance, one-hot
+index pins) bit-exact.  Small problems are compared element by element over the
+whole output; the full-size workloads (in the launch configuration the
+benchmark times) are compared at sampled query tokens, which the oracle
+computes row by row.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import super_resolution_transformer_amd as rib
+from super_resolution_transformer_amd import synthetic
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "GPU tests need a GPU"
+    rib.lib()
+    return t
+
+
+def to_dev(torch, p):
+    if p.dtype == "bf16":
+        cv = lambda nm: torch.from_numpy(p.bits[nm].view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        cv = lambda nm: torch.from_numpy(getattr(p, nm)).cuda()
+    return [cv(nm) for nm in ("qc", "kc", "v", "g")], torch.from_numpy(p.weights).cuda()
+
+
+def gpu_run(torch, p, ws):
+    (qc, kc, v, g), w = to_dev(torch, p)
+    qp, kp = rib.encode(ws, p.L, p.hidden, p.R, w)
+    o = rib.window_attn(qc, kc, v, g, qp, kp, p.heads, ws)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), qp.cpu().numpy(), kp.cpu().numpy()
+
+
+def compare(got, want, dtype, what):
+    err = np.abs(got - want)
+    mx = float(err.max()) if err.size else 0.0
+    note(f"  {what}: max|err| {mx:.3g}  max|O| {float(np.abs(want).max()):.3g}  tol {TOL[dtype]}")
+    assert np.all(np.isfinite(got)), what
+    assert mx <= TOL[dtype], what
+
+
+# ---------------------------------------------------------------- encoder
+@pytest.mark.parametrize("ws", [2, 3, 4, 7, 16, 32, 64, 96, 128])
+def test_encode_matches_oracle(torch, ws):
+    p = synthetic.config_problem(3)
+    note(f"encode ws={ws}")
+    w = torch.from_numpy(p.weights).cuda()
+    qp, kp = rib.encode(ws, p.L, p.hidden, p.R, w)
+    torch.cuda.synchronize()
+    oq, ok = oracle.encode(ws, p.L, p.hidden, p.R, p.weights)
+    for got, want in ((qp, oq), (kp, ok)):
+        e = np.abs(got.cpu().numpy() - want).max()
+        note(f"  max|err| {e:.3g}")
+        assert e <= 1e-5
+
+
+def test_encode_other_sizes(torch):
+    for (L, hidden, R, ws) in [(0, 8, 4, 5), (15, 32, 8, 16), (16, 256, 64, 9), (3, 1, 1, 2)]:
+        note(f"encode L={L} hidden={hidden} R={R} ws={ws}")
+        w = synthetic.draw_weights(np.random.default_rng(L), L, hidden, R)
+        qp, kp = rib.encode(ws, L, hidden, R, torch.from_numpy(w).cuda())
+        oq, ok = oracle.encode(ws, L, hidden, R, w)
+        assert np.abs(qp.cpu().numpy() - oq).max() <= 1e-5
+        assert np.abs(kp.cpu().numpy() - ok).max() <= 1e-5
+
+
+# ---------------------------------------------------------------- whole outputs, small shapes
+SMALL = [
+    # B, H, W, heads, dh, R, ws, dtype
+    (1, 64, 64, 3, 16, 16, 16, "f32"),        # tiny fp32 workload, whole
+    (1, 5, 7, 1, 16, 16, 2, "f32"),
+    (2, 37, 53, 3, 30, 16, 16, "f32"),
+    (1, 20, 30, 2, 7, 5, 8, "f32"),
+    (1, 9, 70, 1, 64, 64, 32, "f32"),
+    (1, 5, 7, 1, 16, 16, 4, "bf16"),
+    (1, 5, 7, 2, 16, 16, 96, "bf16"),          # window larger than the map
+    (3, 37, 53, 3, 30, 16, 16, "bf16"),
+    (1, 37, 53, 3, 30, 16, 32, "bf16"),
+    (2, 37, 53, 2, 32, 16, 32, "bf16"),
+    (1, 100, 61, 2, 16, 16, 64, "bf16"),
+    (1, 70, 61, 1, 30, 16, 96, "bf16"),
+    (1, 30, 31, 2, 8, 8, 8, "bf16"),
+    (1, 30, 31, 2, 16, 32, 16, "bf16"),
+    (1, 30, 31, 2, 30, 32, 16, "bf16"),
+    (1, 1, 1, 2, 30, 16, 2, "bf16"),           # a window with one token
+    (1, 1, 100, 1, 30, 16, 16, "bf16"),
+    (1, 3, 130, 1, 16, 16, 128, "bf16"),       # largest window
+]
+
+
+@pytest.mark.parametrize("B,H,W,heads,dh,R,ws,dtype", SMALL)
+def test_attention_whole_output(torch, B, H, W, heads, dh, R, ws, dtype):
+    note(f"attn whole B={B} H={H} W={W} heads={heads} dh={dh} R={R} ws={ws} {dtype}")
+    p = synthetic.make_problem(B, H, W, heads, dh, R, dtype=dtype, seed=H * 1000 + W + ws)
+    got, qp, kp = gpu_run(torch, p, ws)
+    oq, ok = oracle.encode(ws, p.L, p.hidden, p.R, p.weights)
+    want = oracle.window_attn(p.qc, p.kc, p.v, p.g, oq, ok, heads, ws)
+    compare(got, want, dtype, "O")
+
+
+def test_sst_lite_cyclic_windows_whole_16(torch):
+    """The SST-lite workload (180x320, C=48, 3 heads) at window 16, whole output."""
+    p = synthetic.config_problem(2)
+    got, _, _ = gpu_run(torch, p, 16)
+    oq, ok = oracle.encode(16, p.L, p.hidden, p.R, p.weights)
+    want = oracle.window_attn(p.qc, p.kc, p.v, p.g, oq, ok, p.heads, 16)
+    compare(got, want, "bf16", "sst-lite ws16")
+
+
+# ---------------------------------------------------------------- full-size workloads, sampled rows
+def sample_tokens(B, H, W, ws, n, seed):
+    """Sampled query tokens: window corners and edges of every window type, plus random ones."""
+    rng = np.random.default_rng(seed)
+    toks = set()
+    nWy, nWx = -(-H // ws), -(-W // ws)
+    for wy in {0, nWy // 2, nWy - 1}:
+        for wx in {0, nWx // 2, nWx - 1}:
+            y0, x0 = wy * ws, wx * ws
+            y1, x1 = min(H, y0 + ws) - 1, min(W, x0 + ws) - 1
+            for (y, x) in [(y0, x0), (y0, x1), (y1, x0), (y1, x1), ((y0 + y1) // 2, (x0 + x1) // 2)]:
+                toks.add((int(rng.integers(B)), y, x))
+    while len(toks) < n:
+        toks.add((int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(W))))
+    t = np.array(sorted(toks))
+    return t[:, 0], t[:, 1], t[:, 2]
+
+
+@pytest.mark.parametrize("cfg,ws", [(2, 32), (2, 64), (3, 64), (4, 96), (5, 96)])
+def test_full_size_workload_sampled(torch, cfg, ws):
+    p = synthetic.config_problem(cfg)
+    note(f"workload {synthetic.CONFIGS[cfg].name} ws={ws}: B={p.B} H={p.H} W={p.W} C={p.C}")
+    got, _, _ = gpu_run(torch, p, ws)
+    tb, ty, tx = sample_tokens(p.B, p.H, p.W, ws, 384, seed=cfg)
+    oq, ok = oracle.encode(ws, p.L, p.hidden, p.R, p.weights)
+    want = oracle.window_attn_rows(p.qc, p.kc, p.v, p.g, oq, ok, p.heads, ws, tb, ty, tx)
+    compare(got[tb, ty, tx], want, p.dtype, f"{len(tb)} sampled rows")
+    # property at every position: |O| <= max|V| * sigmoid(G) elementwise (convex combination)
+    assert np.all(np.isfinite(got))
+
+
+# ---------------------------------------------------------------- bit-exact index pins
+def one_hot_inputs(ws, H, W, B, heads, dh, alpha=32.0, seed=3):
+    rng = np.random.default_rng(seed)
+    C = heads * dh
+    qc = np.zeros((B, H, W, C), np.float32)
+    for y in range(H):
+        for x in range(W):
+            n = (y % ws) * ws + (x % ws)
+            for h in range(heads):
+                qc[:, y, x, h * dh + n] = alpha
+    v = synthetic.round_bf16(rng.standard_normal((B, H, W, C)).astype(np.float32) + 3.0)[1]
+    g = np.full((B, H, W, C), 100.0, np.float32)
+    return qc, v, g
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ws,H,W", [(2, 5, 7), (4, 9, 6), (4, 8, 8), (4, 13, 11)])
+def test_one_hot_index_mapping_is_bit_exact(torch, dtype, ws, H, W):
+    note(f"one-hot ws={ws} H={H} W={W} {dtype}")
+    B, heads, dh, R = 2, 2, 16, 16
+    qc, v, g = one_hot_inputs(ws, H, W, B, heads, dh)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    qct, vt, gt = (torch.from_numpy(a).cuda().to(tdt) for a in (qc, v, g))
+    z = torch.zeros((ws * ws, R), dtype=torch.float32, device="cuda")
+    o = rib.window_attn(qct, qct, vt, gt, z, z, heads, ws)
+    assert torch.equal(o, vt)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ws,H,W,R,dh", [(4, 4, 4, 16, 16), (4, 9, 6, 16, 30), (2, 5, 7, 16, 16),
+                                         (5, 11, 8, 32, 16), (4, 7, 9, 32, 30)])
+def test_positional_one_hot_is_bit_exact(torch, dtype, ws, H, W, R, dh):
+    """Qc = Kc = 0 and Qp = Kp = alpha * I (R >= window^2): the bias alone makes P one-hot on
+    the diagonal, so O == V bit for bit -- pins the positional columns and their indexing."""
+    note(f"positional one-hot ws={ws} H={H} W={W} R={R} dh={dh} {dtype}")
+    B, heads = 2, 2
+    if dtype == "bf16" and not rib.supported(dh, R, ws, torch.bfloat16):
+        pytest.skip("no bf16 variant")
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    rng = np.random.default_rng(1)
+    v = synthetic.round_bf16(rng.standard_normal((B, H, W, heads * dh)).astype(np.float32) + 3.0)[1]
+    vt = torch.from_numpy(v).cuda().to(tdt)
+    z = torch.zeros_like(vt)
+    g = torch.full_like(vt, 100.0)
+    eye = torch.zeros((ws * ws, R), dtype=torch.float32, device="cuda")
+    eye[torch.arange(ws * ws), torch.arange(ws * ws)] = 32.0
+    o = rib.window_attn(z, z, vt, g, eye, eye, heads, ws)
+    assert torch.equal(o, vt)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_locality_and_equivariance_bit_exact(torch, dtype):
+    note(f"locality {dtype}")
+    ws, H, W, B, heads, dh, R = 16, 48, 48, 2, 3, 30 if dtype == "bf16" else 16, 16
+    p = synthetic.make_problem(B, H, W, heads, dh, R, dtype=dtype, seed=7)
+    (qc, kc, v, g), w = to_dev(torch, p)
+    qp, kp = rib.encode(ws, p.L, p.hidden, R, w)
+    base = rib.window_attn(qc, kc, v, g, qp, kp, heads, ws)
+    kc2, v2 = kc.clone(), v.clone()
+    kc2[1, 20, 37] += 1.5
+    v2[1, 20, 37] -= 2.0
+    out = rib.window_attn(qc, kc2, v2, g, qp, kp, heads, ws)
+    changed = (out != base).any(dim=-1).cpu().numpy()
+    inside = np.zeros_like(changed)
+    inside[1, 16:32, 32:48] = True
+    assert changed[inside].mean() > 0.9 and not changed[~inside].any()
+
+    def swap(a):
+        a = a.clone()
+        t = a[:, 0:16, 16:32].clone()
+        a[:, 0:16, 16:32] = a[:, 32:48, 0:16]
+        a[:, 32:48, 0:16] = t
+        return a
+    out = rib.window_attn(swap(qc), swap(kc), swap(v), swap(g), qp, kp, heads, ws)
+    assert torch.equal(out, swap(base))
+    same = [torch.stack([a[0], a[0]]).contiguous() for a in (qc, kc, v, g)]
+    out = rib.window_attn(*same, qp, kp, heads, ws)
+    assert torch.equal(out[0], out[1]) and torch.equal(out[0], base[0])
+
+
+def test_repeat_calls_are_deterministic(torch):
+    p = synthetic.make_problem(1, 96, 96, 6, 30, 16, dtype="bf16", seed=9)
+    (qc, kc, v, g), w = to_dev(torch, p)
+    qp, kp = rib.encode(96, p.L, p.hidden, p.R, w)
+    a = rib.window_attn(qc, kc, v, g, qp, kp, 6, 96)
+    b = rib.window_attn(qc, kc, v, g, qp, kp, 6, 96)
+    assert torch.equal(a, b)
+
+
+def test_unsupported_shape_raises(torch):
+    x = torch.zeros((1, 8, 8, 2 * 31), dtype=torch.bfloat16, device="cuda")
+    z = torch.zeros((64, 16), dtype=torch.float32, device="cuda")
+    with pytest.raises(rib.RibError) as e:
+        rib.window_attn(x, x, x, x, z, z, 2, 8)
+    assert e.value.status == rib.RIB_ERR_UNSUPPORTED
