@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark: RIB window attention with the CLA gate on one MI355X.
+
+One step = the whole hot path over one batch of resident synthetic input:
+rib_encode (positional factors for the window size) + rib_window_attn
+(fused window attention, bf16 MFMA).  The headline workload is the SST
+training-patch forward: 32 images of 96x96 tokens, C = 180 (6 heads x 30),
+R = 16, one 96x96 window per image.  Secondary figures for the 64x64 window
+(1x180x320, C = 180), the 640x360 input with 96x96 windows, and the 16x16
+window of the SST-lite map (HBM-bound) are reported in the same JSON line.
+
+Prints ONE JSON line.  Timing: HIP events on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk/CU
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+ATTN_SRC = os.path.join(ROOT, "super_resolution_transformer_amd", "csrc", "attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_train96_traffic.txt")
+
+
+def algorithmic(B, H, W, heads, dh, R, ws, elt):
+    """Score pairs E, flops F and bytes M of one rib_window_attn call (real tokens only)."""
+    nwy, nwx = -(-H // ws), -(-W // ws)
+    pairs = 0
+    for wy in range(nwy):
+        for wx in range(nwx):
+            n = min(ws, H - wy * ws) * min(ws, W - wx * ws)
+            pairs += n * n
+    E = B * heads * pairs
+    F = E * (2 * (dh + R) + 2 * dh)
+    M = B * H * W * heads * dh * 5 * elt + 2 * ws * ws * R * 4
+    return E, F, M
+
+
+def source_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it still
+    describes the current kernel source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != source_sha(ATTN_SRC):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Workload:
+    def __init__(self, torch, rib, synthetic, cfg_idx, ws, copies=1):
+        c = synthetic.CONFIGS[cfg_idx]
+        self.cfg, self.ws = c, ws
+        p = synthetic.config_problem(cfg_idx)
+        self.p = p
+        bf = lambda nm: torch.from_numpy(p.bits[nm].view("int16")).view(torch.bfloat16).cuda()
+        base = [bf(n) for n in ("qc", "kc", "v", "g")]
+        self.sets = [base] + [[t.clone() for t in base] for _ in range(copies - 1)]
+        self.outs = [torch.empty_like(base[0]) for _ in range(copies)]
+        self.w = torch.from_numpy(p.weights).cuda()
+        n = ws * ws
+        self.qp = torch.empty((n, c.R), dtype=torch.float32, device="cuda")
+        self.kp = torch.empty_like(self.qp)
+        self.rib = rib
+        self.k = 0
+        self.E, self.F, self.M = algorithmic(c.B, c.H, c.W, c.heads, c.dh, c.R, ws, 2)
+        self.tokens = c.B * c.H * c.W
+
+    def encode(self):
+        c = self.cfg
+        self.rib.encode_into(self.ws, c.L, c.hidden, c.R, self.w, self.qp, self.kp)
+
+    def attn(self):
+        c = self.cfg
+        i = self.k % len(self.sets)
+        self.k += 1
+        qc, kc, v, g = self.sets[i]
+        self.rib.window_attn_into(qc, kc, v, g, self.qp, self.kp, c.heads, self.ws, self.outs[i])
+
+
+def time_steps(torch, wl, steps, warmup):
+    """Whole-step timing plus per-launch timing of the attention kernel, HIP events on the
+    current stream (the stream the library launches on)."""
+    for _ in range(warmup):
+        wl.encode()
+        wl.attn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for a, b, c in ev:
+        a.record()
+        wl.encode()
+        b.record()
+        wl.attn()
+        c.record()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    enc_ms = sorted(a.elapsed_time(b) for a, b, _ in ev)
+    attn_ms = sorted(b.elapsed_time(c) for _, b, c in ev)
+    return total_ms / steps, sum(enc_ms) / steps, sum(attn_ms) / steps, attn_ms, wall
+
+
+def time_attn_only(torch, wl, reps, warmup):
+    for _ in range(warmup):
+        wl.attn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        wl.attn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def cpu_baseline(synthetic, cfg_idx, ws, units_sample):
+    """The fp64 oracle as it stands, on the host cores, over a bounded sample of
+    (image, window, head) units of the same workload, scaled to tokens/s."""
+    import oracle
+    p = synthetic.config_problem(cfg_idx)
+    c = synthetic.CONFIGS[cfg_idx]
+    qp, kp = oracle.encode(ws, c.L, c.hidden, c.R, p.weights)
+    total_units = oracle.units(c.B, c.H, c.W, c.heads, ws)
+    units_sample = min(units_sample, total_units)
+    t0 = time.perf_counter()
+    oracle.window_attn(p.qc, p.kc, p.v, p.g, qp, kp, c.heads, ws, unit_range=(0, units_sample))
+    dt = time.perf_counter() - t0
+    full = dt * total_units / units_sample           # all units are full 96x96 windows here
+    return {
+        "value": c.B * c.H * c.W / full,
+        "unit": "tokens/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"{units_sample} of {total_units} (image, window, head) units of the same workload "
+                  f"(each a full {ws}x{ws} window, 1 head), {dt:.1f} s, scaled by unit count",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary window sizes")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-units", type=int, default=0,
+                    help="oracle sample size in window-head units (default: 2 per oracle thread)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        msg = ("bench.py measures one GPU: this path needs no inter-GPU exchange and this build "
+               "runs on a single MI355X; --gpus must be 1")
+        print(json.dumps({"error": msg, "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import super_resolution_transformer_amd as rib
+    from super_resolution_transformer_amd import synthetic
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    rib.lib()
+
+    # ---- headline workload: 32 x 96x96 patches, 96x96 window
+    wl = Workload(torch, rib, synthetic, 4, 96)
+    ms_step, ms_enc, ms_attn, attn_list, wall = time_steps(torch, wl, args.steps, args.warmup)
+    tflops = wl.F / (ms_attn * 1e-3) / 1e12
+    traffic = read_traffic()
+    out = {
+        "metric": "RIB window-attn tokens/s + TFLOP/s (% bf16 MFMA peak) at 64x64 and 96x96 windows",
+        "value": wl.tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "sst-train-bf16: 32 x 96x96 map, C=180 (6 heads x dh 30), R=16, "
+                               "L=10, hidden 64, one 96x96 window per image",
+                   "B": 32, "H": 96, "W": 96, "C": 180, "heads": 6, "dh": 30, "R": 16, "window": 96,
+                   "step": "rib_encode + rib_window_attn"},
+        "tflops": tflops,
+        "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "ms_attn": ms_attn,
+        "ms_encode": ms_enc,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "kernel": "attn_bf16_kernel<30,16>", "algorithmic_flop_per_launch": wl.F,
+                     "launch_ms_p10_p50_p90": [attn_list[len(attn_list) // 10], attn_list[len(attn_list) // 2],
+                                               attn_list[(9 * len(attn_list)) // 10]]},
+    }
+    del wl
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        extra = {}
+        for name, cfg_idx, ws, copies in (("64x64 window, 1x180x320, C=180", 3, 64, 1),
+                                          ("96x96 window, 1x360x640 (640x360 input), C=180", 5, 96, 1),
+                                          ("32x32 window, 1x180x320, C=48", 2, 32, 1),
+                                          ("16x16 window, 1x180x320, C=48 (HBM-bound; 40 rotating input sets)",
+                                           2, 16, 40)):
+            w2 = Workload(torch, rib, synthetic, cfg_idx, ws, copies=copies)
+            w2.encode()
+            ms = time_attn_only(torch, w2, reps=max(20, 2 * copies), warmup=max(5, copies))
+            tf = w2.F / (ms * 1e-3) / 1e12
+            extra[name] = {"ms_attn": ms, "tokens_per_s": w2.tokens / (ms * 1e-3), "tflops": tf,
+                           "pct_bf16_peak": 100 * tf / PEAK_BF16_TFLOPS,
+                           "alg_gbs": w2.M / (ms * 1e-3) / 1e9,
+                           "pct_hbm": 100 * w2.M / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            del w2
+            torch.cuda.empty_cache()
+        out["other_windows"] = extra
+
+    if args.copy_calibration:
+        x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = {"read": x.numel() * 4, "write": y.numel() * 4}
+        del x, y
+
+    if not args.no_cpu:
+        import oracle
+        units = args.cpu_units or 2 * oracle.threads()
+        out["cpu_baseline"] = cpu_baseline(synthetic, 4, 96, units)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

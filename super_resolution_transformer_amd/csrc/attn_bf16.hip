@@ -81,7 +81,8 @@ struct Shape {
   static constexpr int KREG = ROWDW / 2;
   static constexpr int VREG = VDW / 2;
   static constexpr int NREG = KREG > VREG ? KREG : VREG;
-  static_assert(KC <= 4 && DT <= 2, "variant too large");
+  static_assert(KC <= 4 && DT <= 2 && DH <= 32 && R <= 32, "variant too large");
+  static_assert(!(R > 16 && DT > 1), "wave 3 stages either Kp[16..32) or the second V tile");
 };
 
 struct Geo {
@@ -107,45 +108,34 @@ __device__ __forceinline__ void locate(const Geo& G, int r, int& off, int& n) {
 }
 
 // ---- staging of one key tile ------------------------------------------------
-// Each wave has one role for the whole kernel (wave-uniform branches):
-//   role 0: the key's positional factor Kp (R fp32, converted to bf16 at store)
-//   role 1: the key's content Kc (dh bf16) + the (m, o) column pair
-//   role 2/3: the two halves of the key's V row (+ the ones row at d = dh),
-//             written transposed.
-// Every role fills the same NV 16-byte registers with raw loads, so the four
-// paths merge cleanly into one set of VGPRs.
-template <int DH, int R>
+// Every wave issues the same four 16-byte buffer loads per lane and tile; only
+// the wave-uniform buffer descriptor and the offset formula differ:
+//   wave 0: the key's positional factor Kp[n][0..16)     (fp32, from kp)
+//   wave 1: the key's content slice Kc (dh bf16)          (from kc)
+//   wave 2: the key's value slice V (dh bf16)             (from v)
+//   wave 3: Kp[n][16..32) when R = 32, otherwise nothing  (zero-length buffer)
+// Buffer loads are bounds-checked by the hardware (reads past the descriptor's
+// size return 0), so the last head slice of the map may over-read its 16-byte
+// chunk safely.  Keeping the load code identical across waves keeps the
+// prefetch free of branches, so its latency stays hidden behind the MFMAs;
+// all role-specific conversion happens at the LDS store after the compute.
+constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
+
 struct Stage {
-  static constexpr int NV0 = R / 4;
-  static constexpr int NV1 = (DH / 2 + 3) / 4;
-  static constexpr int NV2 = 2 * Shape<DH, R>::DT;
-  static constexpr int NV = NV0 > NV1 ? (NV0 > NV2 ? NV0 : NV2) : (NV1 > NV2 ? NV1 : NV2);
-  u32x4_t raw[NV];
+  u32x4_t raw[4];
 };
 
 template <int DH, int R>
-__device__ __forceinline__ void load_tile(const Geo& G, int wave, int r, Stage<DH, R>& st) {
-  using T = Stage<DH, R>;
+__device__ __forceinline__ void load_tile(const Geo& G, __amdgpu_buffer_rsrc_t rsrc, int wave, int r,
+                                          Stage& st) {
   int off, n;
   locate<DH>(G, r < G.n_real ? r : G.n_real - 1, off, n);
-  if (wave == 0) {
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(G.kp + n * R);
+  // byte offset: positional rows for waves 0/3, token head slice for waves 1/2
+  const bool pos = (wave == 0) | (wave == 3);
+  const unsigned voff = pos ? (unsigned)(n * (R * 4) + (wave == 3 ? 64 : 0)) : 2u * (unsigned)off;
 #pragma unroll
-    for (int i = 0; i < T::NV; ++i) st.raw[i] = i < T::NV0 ? src[i] : (u32x4_t){0u, 0u, 0u, 0u};
-  } else {
-    const uint32_t* src = (wave == 1 ? G.kc : G.v) + (off >> 1);
-    const int base = wave == 3 ? 8 * Shape<DH, R>::DT : 0;  // V dword offset of this half
-#pragma unroll
-    for (int i = 0; i < T::NV; ++i) {
-      uint32_t d[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int w = base + 4 * i + e;
-        d[e] = w < DH / 2 ? src[w] : 0u;
-      }
-      st.raw[i] = (u32x4_t){d[0], d[1], d[2], d[3]};
-    }
-  }
+  for (int i = 0; i < 4; ++i)
+    st.raw[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff + 16u * i, 0, 0));
 }
 
 // position of key j (0..KT-1) in the transposed V tile: the key order of the
@@ -156,22 +146,28 @@ __device__ __forceinline__ int vpos(int j) {
   return kb * 32 + 16 * c + 8 * g + 4 * eh + el;
 }
 
+__device__ __forceinline__ uint32_t pick(const Stage& st, int w) { return st.raw[w >> 2][w & 3]; }
+
+// Kp fp32 chunks (8 floats) -> 4 packed bf16 dwords
+__device__ __forceinline__ u32x4_t kp_to_bf16(const u32x4_t& x, const u32x4_t& y, bool real) {
+  const f32x4_t a = __builtin_bit_cast(f32x4_t, x);
+  const f32x4_t b = __builtin_bit_cast(f32x4_t, y);
+  const u32x4_t out = {pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(b[0], b[1]), pack_bf16(b[2], b[3])};
+  return real ? out : (u32x4_t){0u, 0u, 0u, 0u};
+}
+
 template <int DH, int R>
-__device__ __forceinline__ void store_tile(uint32_t* stage, int wave, int j, bool real,
-                                           const Stage<DH, R>& st) {
+__device__ __forceinline__ void store_tile(uint32_t* stage, int wave, int j, bool real, const Stage& st) {
   using S = Shape<DH, R>;
-  if (wave == 0) {
-    uint32_t* dst = stage + j * S::KSTR;
+  if (wave == 0 || (wave == 3 && R > 16)) {
+    // positional columns: dwords [0, R/2) of the K~ row (wave 3: the second half when R = 32)
+    uint32_t* dst = stage + j * S::KSTR + (wave == 3 ? 8 : 0);
+    constexpr int NQ = (R > 16 ? 16 : R) / 8;      // b128 writes per wave
 #pragma unroll
-    for (int i = 0; i < R / 8; ++i) {
-      const f32x4_t a = __builtin_bit_cast(f32x4_t, st.raw[2 * i]);
-      const f32x4_t b = __builtin_bit_cast(f32x4_t, st.raw[2 * i + 1]);
-      u32x4_t out = {pack_bf16(a[0], a[1]), pack_bf16(a[2], a[3]), pack_bf16(b[0], b[1]),
-                     pack_bf16(b[2], b[3])};
-      if (!real) out = (u32x4_t){0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4_t*>(dst + 4 * i) = out;
-    }
+    for (int i = 0; i < NQ; ++i)
+      *reinterpret_cast<u32x4_t*>(dst + 4 * i) = kp_to_bf16(st.raw[2 * i], st.raw[2 * i + 1], real);
   } else if (wave == 1) {
+    // content columns + the (m, o) pair + zero padding: dwords [R/2, ROWDW)
     uint32_t* dst = stage + j * S::KSTR + R / 2;
 #pragma unroll
     for (int i = 0; i < (S::ROWDW - R / 2) / 4; ++i) {
@@ -180,22 +176,24 @@ __device__ __forceinline__ void store_tile(uint32_t* stage, int wave, int j, boo
       for (int e = 0; e < 4; ++e) {
         const int w = 4 * i + e;
         uint32_t val;
-        if (w < DH / 2) val = real ? st.raw[w / 4][w % 4] : 0u;
+        if (w < DH / 2) val = real ? pick(st, w) : 0u;
         else if (w == DH / 2) val = real ? 0x3F803F80u : 0x46800000u;  // (1,1) real, (0,2^14) padded
         else val = 0u;
         d[e] = val;
       }
       *reinterpret_cast<u32x4_t*>(dst + 4 * i) = (u32x4_t){d[0], d[1], d[2], d[3]};
     }
-  } else {
+  }
+  if (wave == 2 || (wave == 3 && S::DT > 1)) {
+    // V^T rows: wave 2 channels [0, 32), wave 3 channels [32, 64) (ones row / zeros only)
     uint32_t* vs = stage + S::KS_DW;
     const bool odd = j & 1;
     const int col = vpos(j & ~1) >> 1;
-    const int base = wave == 3 ? 8 * S::DT : 0;
+    const int base = wave == 3 ? 16 : 0;
 #pragma unroll
-    for (int i = 0; i < 8 * S::DT; ++i) {
+    for (int i = 0; i < 16; ++i) {
       const int w = base + i;
-      uint32_t mine = st.raw[i / 4][i % 4];
+      uint32_t mine = (w < DH / 2 && i < 16) ? pick(st, i) : 0u;
       mine = w == DH / 2 ? 0x00003F80u : mine;  // (1, 0): ones row at d = DH
       mine = real ? mine : 0u;
       const uint32_t nb = lane_xor1(mine);
@@ -284,8 +282,15 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
 
   const int ntiles = (G.n_real + KT - 1) / KT;
   const bool active = q0 + wave * QW < G.n_real;
-  Stage<DH, R> st;
-  load_tile<DH, R>(G, wave, lane, st);
+  // this wave's load source (wave-uniform): see load_tile
+  const unsigned map_bytes = (unsigned)(B * H * W * heads * DH) * 2u;
+  const unsigned pos_bytes = (unsigned)(ws * ws * R) * 4u;
+  const void* src = wave == 1 ? (const void*)kc : wave == 2 ? (const void*)v : (const void*)kp;
+  const unsigned nbytes = wave == 1 || wave == 2 ? map_bytes : (wave == 0 || R > 16 ? pos_bytes : 0u);
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(src), (short)0, (int)nbytes, (int)RSRC_WORD3);
+  Stage st;
+  load_tile<DH, R>(G, rsrc, wave, lane, st);
   store_tile<DH, R>(lds, wave, lane, lane < G.n_real, st);
   __syncthreads();
 
@@ -301,7 +306,7 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
   for (int it = 0; it < ntiles; ++it) {
     const uint32_t* stage = lds + (it & 1) * S::STAGE_DW;
     const bool more = it + 1 < ntiles;
-    if (more) load_tile<DH, R>(G, wave, (it + 1) * KT + lane, st);
+    if (more) load_tile<DH, R>(G, rsrc, wave, (it + 1) * KT + lane, st);
 
     if (active) {
       // ---- scores: S^T = K~ Q~^T for 64 keys x 64 queries
