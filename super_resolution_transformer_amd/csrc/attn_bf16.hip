@@ -13,31 +13,35 @@
 //
 //  * Scores are computed transposed, S^T = K~ Q~^T, with
 //    v_mfma_f32_32x32x16_bf16: K~ rows are the A operand (read from LDS), the
-//    wave's queries are the B operand (kept in VGPRs for the whole loop).  In
-//    the 32x32 accumulator each lane then owns ONE query and 16 of the 32 keys
-//    of a block, so softmax row statistics are in-lane plus one
+//    wave's 64 queries are the B operand (kept in VGPRs for the whole loop).
+//    In the 32x32 accumulator each lane then owns ONE query and 16 of the 32
+//    keys of a block, so softmax row statistics are in-lane plus one
 //    v_permlane32_swap.
 //  * The same accumulator registers, rounded to bf16, are exactly the B
-//    operand of O^T = V^T P^T, provided V^T is stored in LDS with the keys in
-//    the accumulator's row order.  P never leaves registers.
-//  * Softmax runs in base 2: log2(e) is folded into the query scales.  Two
-//    spare contraction columns (dh+R+2 <= 16*KC) carry the running maximum:
-//    column "m" holds -m_hat in Q~ (a bf16 value) against 1 in K~, column "o"
-//    holds -OFF in Q~ against 1 in K~ (2^14 for padded keys, which masks them,
-//    and 0 in column m).  The MFMA therefore returns t = s*log2(e) - m_hat -
-//    OFF directly and the fast path is just p = exp2(t).
-//  * Rescaling is lazy: p = exp2(t) <= 2^-OFF * 2^(growth of the maximum).
-//    The packed bf16 P values are OR-reduced; bit 14 of a half is set iff
-//    p >= 2, i.e. the maximum grew by more than OFF+1 = 8 (factor 256).  Only
-//    then (and on the first tile) does the wave take the slow path: exact row
-//    maximum, new m_hat rounded to bf16, subtract, exp2 again, rescale O.
-//  * The row sum l comes for free from the PV MFMA: V^T row dh is all ones.
-//  * Key tiles of KT = 64 keys are double-buffered in LDS with one barrier per
-//    tile; the next tile's global loads are issued before the current tile's
-//    MFMAs.  Window partitioning is pure index arithmetic on the NHWC arrays:
-//    a window's real tokens are enumerated row-major, r = iy*nx + ix, so
-//    padded positions are never loaded, and only the last tile can hold
-//    padded keys.
+//    operand of O^T = V^T P^T.  V stays token-major in LDS; the A operand
+//    (8 keys of one channel per lane) is assembled with ds_read_b64_tr_b16,
+//    whose 16-lane transpose is addressed so that the keys come out in the
+//    accumulator's row order.  P never leaves registers.
+//  * Softmax runs in base 2 (log2 e folded into the query scales).  Two spare
+//    contraction columns carry the running maximum: column "m" holds -m_hat
+//    in Q~ (a bf16 value) against 1 in K~, column "o" holds -OFF against 1
+//    (2^14 for padded keys, which masks them; those have 0 in column m).  The
+//    MFMA returns t = s*log2(e) - m_hat - OFF and the fast path is p = exp2(t).
+//  * Rescaling is lazy: p <= 2^-OFF * 2^(growth of the maximum).  The packed
+//    bf16 P values are OR-reduced; bit 14 of a half is set iff p >= 2, i.e.
+//    the maximum grew by more than OFF+1 = 8 (a factor 256).  Only then (and on
+//    the first tile) does the wave take the slow path: exact row maximum, new
+//    m_hat rounded to bf16, recompute, rescale O.
+//  * The row sum l comes for free from the PV MFMA: V channel dh is all ones.
+//  * Software pipeline over key tiles of KT = 64: iteration i issues the
+//    global loads of tile i+1, the QK^T MFMAs of tile i and the exp2/convert
+//    work of tile i-1 in one basic block, so the matrix cores, the
+//    transcendental unit and the VALU work side by side; then the PV MFMAs of
+//    tile i-1 and the LDS store of tile i+1.  Three LDS stages, one barrier
+//    per tile.
+//  * Window partitioning is index arithmetic on the NHWC arrays: a window's
+//    real tokens are enumerated row-major, r = iy*nx + ix, so padded positions
+//    are never loaded, and only the last tile can hold padded keys.
 //  * Workgroups are numbered so that the q-blocks of one (image, window, head)
 //    are consecutive on one XCD (shared K/V in that XCD's L2).
 #include "rib_device.hpp"
@@ -51,48 +55,38 @@ constexpr int KT = 64;             // keys per tile
 constexpr int NWAVE = 4;           // waves per workgroup
 constexpr int QW = 64;             // queries per wave (two 32-query MFMA blocks)
 constexpr int QB = QW * NWAVE;     // queries per workgroup
+constexpr int NSTAGE = 3;          // LDS stages of the key-tile pipeline
 constexpr float OFF = 7.0f;        // p = exp2(s - m_hat - OFF) <= 2^-OFF normally
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
 
 template <int DH, int R>
 struct Shape {
-  static_assert(DH % 2 == 0 && R % 2 == 0, "head dim and rank must be even");
+  static_assert(DH % 2 == 0 && R % 8 == 0, "head dim must be even, rank a multiple of 8");
   static constexpr int KC = (R + DH + 2 + 15) / 16;  // 16-wide contraction chunks
-  static constexpr int DT = (DH + 1 + 31) / 32;      // 32-row output tiles (ones row at DH)
+  static constexpr int DT = (DH + 1 + 31) / 32;      // 32-channel output tiles (ones row at DH)
   static constexpr int ROWDW = 8 * KC;               // dwords per Q~/K~ row
   static constexpr int KSTR = ROWDW + 4;             // LDS row stride in dwords (bank spread)
   static constexpr int CONSTDW = R / 2 + DH / 2;     // dword with columns (m, o)
   static constexpr int CM = CONSTDW / 8;             // chunk holding it
   static constexpr int GM = (CONSTDW % 8) / 4;       // lane half holding it
   static constexpr int DM = CONSTDW % 4;             // dword inside the 16-byte operand
-  static constexpr int VDW = 16 * DT;                // dwords per V row (d < 32*DT)
-  static constexpr int VSTR = KT / 2 + 4;            // dwords per transposed V row
+  static constexpr int VSTR = 16 * DT + 4;           // dwords per token-major V row in LDS
   static constexpr int KS_DW = KT * KSTR;
-  static constexpr int VS_DW = 32 * DT * VSTR;
+  static constexpr int VS_DW = KT * VSTR;
   static constexpr int STAGE_DW = KS_DW + VS_DW;
   static constexpr int QS_DW = QB * KSTR;
-  static constexpr int LDS_DW = (2 * STAGE_DW > QS_DW) ? 2 * STAGE_DW : QS_DW;
-  // accumulator position of the row sum (V^T row DH)
+  static constexpr int LDS_DW = (NSTAGE * STAGE_DW > QS_DW) ? NSTAGE * STAGE_DW : QS_DW;
+  // accumulator position of the row sum (V channel DH)
   static constexpr int LT = DH / 32;
   static constexpr int LW = DH % 32;
   static constexpr int LR = 4 * (LW / 8) + (LW % 4);
   static constexpr int LG = (LW / 4) % 2;
-  // per-lane staging registers for the next tile
-  static constexpr int KREG = ROWDW / 2;
-  static constexpr int VREG = VDW / 2;
-  static constexpr int NREG = KREG > VREG ? KREG : VREG;
   static_assert(KC <= 4 && DT <= 2 && DH <= 32 && R <= 32, "variant too large");
   static_assert(!(R > 16 && DT > 1), "wave 3 stages either Kp[16..32) or the second V tile");
 };
 
 struct Geo {
-  const uint32_t* qc;
-  const uint32_t* kc;
-  const uint32_t* v;
-  const uint32_t* g;
-  const float* qp;
-  const float* kp;
-  uint32_t* o;
   int H, W, C, ws, b, wy, wx, h, nx, n_real;
   float inv_nx;
 };
@@ -118,9 +112,7 @@ __device__ __forceinline__ void locate(const Geo& G, int r, int& off, int& n) {
 // size return 0), so the last head slice of the map may over-read its 16-byte
 // chunk safely.  Keeping the load code identical across waves keeps the
 // prefetch free of branches, so its latency stays hidden behind the MFMAs;
-// all role-specific conversion happens at the LDS store after the compute.
-constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
-
+// all role-specific conversion happens at the LDS store.
 struct Stage {
   u32x4_t raw[4];
 };
@@ -130,20 +122,11 @@ __device__ __forceinline__ void load_tile(const Geo& G, __amdgpu_buffer_rsrc_t r
                                           Stage& st) {
   int off, n;
   locate<DH>(G, r < G.n_real ? r : G.n_real - 1, off, n);
-  // byte offset: positional rows for waves 0/3, token head slice for waves 1/2
   const bool pos = (wave == 0) | (wave == 3);
   const unsigned voff = pos ? (unsigned)(n * (R * 4) + (wave == 3 ? 64 : 0)) : 2u * (unsigned)off;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     st.raw[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff + 16u * i, 0, 0));
-}
-
-// position of key j (0..KT-1) in the transposed V tile: the key order of the
-// S^T accumulator rows, grouped as the PV MFMA's contraction index expects
-__device__ __forceinline__ int vpos(int j) {
-  const int kb = j >> 5, w = j & 31;
-  const int c = w >> 4, eh = (w >> 3) & 1, g = (w >> 2) & 1, el = w & 3;
-  return kb * 32 + 16 * c + 8 * g + 4 * eh + el;
 }
 
 __device__ __forceinline__ uint32_t pick(const Stage& st, int w) { return st.raw[w >> 2][w & 3]; }
@@ -162,7 +145,7 @@ __device__ __forceinline__ void store_tile(uint32_t* stage, int wave, int j, boo
   if (wave == 0 || (wave == 3 && R > 16)) {
     // positional columns: dwords [0, R/2) of the K~ row (wave 3: the second half when R = 32)
     uint32_t* dst = stage + j * S::KSTR + (wave == 3 ? 8 : 0);
-    constexpr int NQ = (R > 16 ? 16 : R) / 8;      // b128 writes per wave
+    constexpr int NQ = (R > 16 ? 16 : R) / 8;
 #pragma unroll
     for (int i = 0; i < NQ; ++i)
       *reinterpret_cast<u32x4_t*>(dst + 4 * i) = kp_to_bf16(st.raw[2 * i], st.raw[2 * i + 1], real);
@@ -185,24 +168,175 @@ __device__ __forceinline__ void store_tile(uint32_t* stage, int wave, int j, boo
     }
   }
   if (wave == 2 || (wave == 3 && S::DT > 1)) {
-    // V^T rows: wave 2 channels [0, 32), wave 3 channels [32, 64) (ones row / zeros only)
-    uint32_t* vs = stage + S::KS_DW;
-    const bool odd = j & 1;
-    const int col = vpos(j & ~1) >> 1;
+    // token-major V row: wave 2 channels [0, 32), wave 3 channels [32, 64)
+    uint32_t* dst = stage + S::KS_DW + j * S::VSTR + (wave == 3 ? 16 : 0);
     const int base = wave == 3 ? 16 : 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int w = base + i;
-      uint32_t mine = (w < DH / 2 && i < 16) ? pick(st, i) : 0u;
-      mine = w == DH / 2 ? 0x00003F80u : mine;  // (1, 0): ones row at d = DH
-      mine = real ? mine : 0u;
-      const uint32_t nb = lane_xor1(mine);
-      // even lane: channel 2w of keys (j, j+1); odd lane: channel 2w+1 of keys (j-1, j)
-      const uint32_t ev = (mine & 0xFFFFu) | (nb << 16);
-      const uint32_t od = (nb >> 16) | (mine & 0xFFFF0000u);
-      vs[(2 * w + (odd ? 1 : 0)) * S::VSTR + col] = odd ? od : ev;
+    for (int i = 0; i < 4; ++i) {
+      uint32_t d[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int w = base + 4 * i + e;
+        uint32_t val = (w < DH / 2 && base == 0) ? pick(st, 4 * i + e) : 0u;
+        val = w == DH / 2 ? 0x00003F80u : val;  // (1, 0): ones at channel DH
+        d[e] = real ? val : 0u;
+      }
+      *reinterpret_cast<u32x4_t*>(dst + 4 * i) = (u32x4_t){d[0], d[1], d[2], d[3]};
     }
   }
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// 4 bf16 of the transposing LDS read (16-lane groups: output lane i, element k
+// comes from input lane 4k + i/4, element i%4)
+__device__ __forceinline__ u32x2_t ds_read_tr16(const uint32_t* p) {
+  const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4_t*)(__attribute__((address_space(3))) void*)(const_cast<uint32_t*>(p)));
+  return __builtin_bit_cast(u32x2_t, r);
+}
+
+template <int DH, int R>
+struct Regs {
+  using S = Shape<DH, R>;
+  f32x16_t O[2][S::DT];
+  u32x4_t qt[2][S::KC];
+  float mhat[2];
+};
+
+// S^T = K~ Q~^T for the tile in `stage` (64 keys x the wave's 64 queries)
+template <int DH, int R>
+__device__ __forceinline__ void qk_tile(const uint32_t* stage, int l32, int gh, const Regs<DH, R>& rg,
+                                        f32x16_t (&Sacc)[2][2]) {
+  using S = Shape<DH, R>;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    u32x4_t a[S::KC];
+#pragma unroll
+    for (int c = 0; c < S::KC; ++c)
+      a[c] = *reinterpret_cast<const u32x4_t*>(stage + (kb * 32 + l32) * S::KSTR + 8 * c + 4 * gh);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16_t acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < S::KC; ++c)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[c]),
+                                                      __builtin_bit_cast(bf16x8_t, rg.qt[qb][c]), acc, 0, 0, 0);
+      Sacc[qb][kb] = acc;
+    }
+  }
+}
+
+// p = exp2(t - shift) packed to bf16 pairs; returns the OR of all packed words
+__device__ __forceinline__ uint32_t exp_tile(const f32x16_t (&Sacc)[2][2], uint32_t (&P)[2][2][8], float shift0,
+                                             float shift1) {
+  uint32_t orv = 0;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float sh = qb ? shift1 : shift0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        P[qb][kb][i] = pack_bf16(__builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i] - sh),
+                                 __builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i + 1] - sh));
+        orv |= P[qb][kb][i];
+      }
+  }
+  return orv;
+}
+
+// fast-path exponentials (no shift)
+__device__ __forceinline__ uint32_t exp_tile_fast(const f32x16_t (&Sacc)[2][2], uint32_t (&P)[2][2][8]) {
+  uint32_t orv = 0;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        P[qb][kb][i] = pack_bf16(__builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i]),
+                                 __builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i + 1]));
+        orv |= P[qb][kb][i];
+      }
+  return orv;
+}
+
+// Slow path for the tile whose scores are in Sacc: exact row maximum, new
+// reference m_hat, exponentials again, rescale of O (unless first), and the
+// correction of the already computed next-tile scores Snext by the shift.
+template <int DH, int R, bool NEXT>
+__device__ __forceinline__ void rescale_tile(Regs<DH, R>& rg, const f32x16_t (&Sacc)[2][2], uint32_t (&P)[2][2][8],
+                                             f32x16_t (&Snext)[2][2], bool first, int gh) {
+  using S = Shape<DH, R>;
+  float shift[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, Sacc[qb][kb][e]);
+    const LanePair pr = lane_pair(mx);
+    mx = fmaxf(pr.lo, pr.hi);
+    const bool grow = first || (mx + OFF > 0.0f);
+    const float mnew = grow ? round_bf16(rg.mhat[qb] + mx + OFF) : rg.mhat[qb];
+    shift[qb] = mnew - rg.mhat[qb];
+    rg.mhat[qb] = mnew;
+    if (!first) {
+      const float sc = __builtin_amdgcn_exp2f(-shift[qb]);
+#pragma unroll
+      for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) rg.O[qb][dt][e] *= sc;
+    }
+    const uint32_t cd = pack_bf16(-mnew, -OFF);
+    if (gh == S::GM) rg.qt[qb][S::CM][S::DM] = cd;
+    if constexpr (NEXT) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) Snext[qb][kb][e] -= shift[qb];
+    }
+  }
+  exp_tile(Sacc, P, shift[0], shift[1]);
+}
+
+// O^T += V^T P^T for the tile whose V rows are in `stage`
+template <int DH, int R>
+__device__ __forceinline__ void pv_tile(const uint32_t* stage, int lane, Regs<DH, R>& rg, const uint32_t (&P)[2][2][8]) {
+  using S = Shape<DH, R>;
+  const uint32_t* vs = stage + S::KS_DW;
+  // transposing read: 16-lane group q = lane/16 covers channels 16*(q%2) + i of the
+  // 32-channel tile for keys 4g + k (g = q/2); input lane j = 4k + m addresses
+  // channels 16*(q%2) + 4m .. +3 of key 4g + k (+8 for the second read).
+  const int j = lane & 15, q = lane >> 4;
+  const int key0 = 4 * (q >> 1) + (j >> 2);
+  const int ch0 = 16 * (q & 1) + 4 * (j & 3);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      u32x4_t va[S::DT];
+#pragma unroll
+      for (int dt = 0; dt < S::DT; ++dt) {
+        const uint32_t* p = vs + (kb * 32 + 16 * c2 + key0) * S::VSTR + ((dt * 32 + ch0) >> 1);
+        const u32x2_t lo = ds_read_tr16(p);
+        const u32x2_t hi = ds_read_tr16(p + 8 * S::VSTR);
+        va[dt] = (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
+      }
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const u32x4_t pb = {P[qb][kb][4 * c2], P[qb][kb][4 * c2 + 1], P[qb][kb][4 * c2 + 2], P[qb][kb][4 * c2 + 3]};
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt)
+          rg.O[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va[dt]),
+                                                                 __builtin_bit_cast(bf16x8_t, pb), rg.O[qb][dt], 0, 0, 0);
+      }
+    }
 }
 
 template <int DH, int R>
@@ -227,7 +361,6 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
     G.wx = t % nWx; t /= nWx;
     G.wy = t % nWy;
     G.b = t / nWy;
-    G.qc = qc; G.kc = kc; G.v = v; G.g = g; G.qp = qp; G.kp = kp; G.o = o;
     G.H = H; G.W = W; G.C = heads * DH; G.ws = ws;
     G.nx = min(ws, W - G.wx * ws);
     G.n_real = min(ws, H - G.wy * ws) * G.nx;
@@ -272,12 +405,18 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
       *reinterpret_cast<u32x4_t*>(dst + w) = (u32x4_t){row[w], row[w + 1], row[w + 2], row[w + 3]};
   }
   __syncthreads();
-  u32x4_t qt[2][S::KC];
+  Regs<DH, R> rg;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
     for (int c = 0; c < S::KC; ++c)
-      qt[qb][c] = *reinterpret_cast<const u32x4_t*>(lds + (wave * QW + qb * 32 + l32) * S::KSTR + 8 * c + 4 * gh);
+      rg.qt[qb][c] = *reinterpret_cast<const u32x4_t*>(lds + (wave * QW + qb * 32 + l32) * S::KSTR + 8 * c + 4 * gh);
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) rg.O[qb][dt][e] = 0.0f;
+    rg.mhat[qb] = 0.0f;
+  }
   __syncthreads();
 
   const int ntiles = (G.n_real + KT - 1) / KT;
@@ -289,115 +428,59 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
   const unsigned nbytes = wave == 1 || wave == 2 ? map_bytes : (wave == 0 || R > 16 ? pos_bytes : 0u);
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(src), (short)0, (int)nbytes, (int)RSRC_WORD3);
+
+  // ---- pipeline prologue: tile 0 staged and scored, tile 1 staged
   Stage st;
   load_tile<DH, R>(G, rsrc, wave, lane, st);
   store_tile<DH, R>(lds, wave, lane, lane < G.n_real, st);
   __syncthreads();
+  if (ntiles > 1) load_tile<DH, R>(G, rsrc, wave, KT + lane, st);
+  f32x16_t SA[2][2], SB[2][2];
+  uint32_t P[2][2][8];
+  if (active) qk_tile<DH, R>(lds, l32, gh, rg, SA);
+  if (ntiles > 1) {
+    store_tile<DH, R>(lds + S::STAGE_DW, wave, lane, KT + lane < G.n_real, st);
+    __syncthreads();
+  }
 
-  f32x16_t O[2][S::DT];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int dt = 0; dt < S::DT; ++dt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) O[qb][dt][e] = 0.0f;
-  float mhat[2] = {0.0f, 0.0f};
-
-  for (int it = 0; it < ntiles; ++it) {
-    const uint32_t* stage = lds + (it & 1) * S::STAGE_DW;
+  // One pipeline step: the scores of tile `it` go into Snew while the softmax
+  // and PV of tile it-1 (scores in Sprev) run.  Stages: s_cur holds tile it,
+  // the one before it tile it-1, the one after it receives tile it+1.
+  int s_cur = 1;
+  auto step = [&](int it, f32x16_t (&Sprev)[2][2], f32x16_t (&Snew)[2][2]) {
+    const int s_prev = s_cur == 0 ? NSTAGE - 1 : s_cur - 1;
+    const int s_next = s_cur == NSTAGE - 1 ? 0 : s_cur + 1;
     const bool more = it + 1 < ntiles;
     if (more) load_tile<DH, R>(G, rsrc, wave, (it + 1) * KT + lane, st);
-
     if (active) {
-      // ---- scores: S^T = K~ Q~^T for 64 keys x 64 queries
-      f32x16_t Sacc[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        u32x4_t a[S::KC];
-#pragma unroll
-        for (int c = 0; c < S::KC; ++c)
-          a[c] = *reinterpret_cast<const u32x4_t*>(stage + (kb * 32 + l32) * S::KSTR + 8 * c + 4 * gh);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          f32x16_t acc;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-#pragma unroll
-          for (int c = 0; c < S::KC; ++c)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[c]),
-                                                          __builtin_bit_cast(bf16x8_t, qt[qb][c]), acc, 0, 0, 0);
-          Sacc[qb][kb] = acc;
-        }
-      }
-      // ---- fast path: p = exp2(t), packed to bf16
-      uint32_t P[2][2][8];
-      uint32_t orv = 0;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            P[qb][kb][i] = pack_bf16(__builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i]),
-                                     __builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i + 1]));
-            orv |= P[qb][kb][i];
-          }
-      const bool need = (it == 0) || (orv & 0x40004000u);
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        // ---- slow path: exact maximum, new reference, recompute, rescale
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, Sacc[qb][kb][e]);
-          const LanePair pr = lane_pair(mx);
-          mx = fmaxf(pr.lo, pr.hi);
-          const bool grow = (it == 0) || (mx + OFF > 0.0f);
-          const float mnew = grow ? round_bf16(mhat[qb] + mx + OFF) : mhat[qb];
-          const float shift = mnew - mhat[qb];
-          mhat[qb] = mnew;
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-              P[qb][kb][i] = pack_bf16(__builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i] - shift),
-                                       __builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i + 1] - shift));
-          if (it > 0) {
-            const float sc = __builtin_amdgcn_exp2f(-shift);
-#pragma unroll
-            for (int dt = 0; dt < S::DT; ++dt)
-#pragma unroll
-              for (int e = 0; e < 16; ++e) O[qb][dt][e] *= sc;
-          }
-          const uint32_t cd = pack_bf16(-mnew, -OFF);
-          if (gh == S::GM) qt[qb][S::CM][S::DM] = cd;
-        }
-      }
-      // ---- O^T += V^T P^T
-      const uint32_t* vs = stage + S::KS_DW;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          u32x4_t va[S::DT];
-#pragma unroll
-          for (int dt = 0; dt < S::DT; ++dt)
-            va[dt] = *reinterpret_cast<const u32x4_t*>(vs + (dt * 32 + l32) * S::VSTR + kb * 16 + 8 * c2 + 4 * gh);
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            const u32x4_t pb = {P[qb][kb][4 * c2], P[qb][kb][4 * c2 + 1], P[qb][kb][4 * c2 + 2],
-                                P[qb][kb][4 * c2 + 3]};
-#pragma unroll
-            for (int dt = 0; dt < S::DT; ++dt)
-              O[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va[dt]),
-                                                                  __builtin_bit_cast(bf16x8_t, pb), O[qb][dt], 0, 0, 0);
-          }
-        }
+      qk_tile<DH, R>(lds + s_cur * S::STAGE_DW, l32, gh, rg, Snew);
+      const uint32_t orv = exp_tile_fast(Sprev, P);
+      const bool need = (it == 1) || (orv & 0x40004000u);
+      if (__builtin_amdgcn_ballot_w64(need)) rescale_tile<DH, R, true>(rg, Sprev, P, Snew, it == 1, gh);
+      pv_tile<DH, R>(lds + s_prev * S::STAGE_DW, lane, rg, P);
     }
-    if (more) store_tile<DH, R>(lds + ((it + 1) & 1) * S::STAGE_DW, wave, lane, (it + 1) * KT + lane < G.n_real, st);
+    if (more) store_tile<DH, R>(lds + s_next * S::STAGE_DW, wave, lane, (it + 1) * KT + lane < G.n_real, st);
     __syncthreads();
+    s_cur = s_next;
+  };
+  // the last tile: softmax + PV only (its scores are in Slast, its stage before s_cur)
+  auto finish = [&](f32x16_t (&Slast)[2][2]) {
+    if (!active) return;
+    const uint32_t orv = exp_tile_fast(Slast, P);
+    const bool need = (ntiles == 1) || (orv & 0x40004000u);
+    if (__builtin_amdgcn_ballot_w64(need)) rescale_tile<DH, R, false>(rg, Slast, P, Slast, ntiles == 1, gh);
+    pv_tile<DH, R>(lds + (s_cur == 0 ? NSTAGE - 1 : s_cur - 1) * S::STAGE_DW, lane, rg, P);
+  };
+  int it = 1;
+  for (; it + 1 < ntiles; it += 2) {
+    step(it, SA, SB);
+    step(it + 1, SB, SA);
+  }
+  if (it < ntiles) {
+    step(it, SA, SB);
+    finish(SB);
+  } else {
+    finish(SA);  // also the single-tile case
   }
 
   if (!active) return;
@@ -405,7 +488,7 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int r = q0 + wave * QW + qb * 32 + l32;
-    const LanePair pr = lane_pair(O[qb][S::LT][S::LR]);
+    const LanePair pr = lane_pair(rg.O[qb][S::LT][S::LR]);
     const float lsum = S::LG ? pr.hi : pr.lo;
     if (r >= G.n_real) continue;
     const float inv = 1.0f / lsum;
@@ -420,12 +503,12 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
         const int e0 = 4 * q4;
         const int gw = (off + d0) >> 1;  // dword index of channels (d0, d0+1)
         const uint32_t g01 = g[gw];
-        const uint32_t r01 = pack_bf16(O[qb][dt][e0 + 0] * inv * sigmoidf(bf16_lo(g01)),
-                                       O[qb][dt][e0 + 1] * inv * sigmoidf(bf16_hi(g01)));
+        const uint32_t r01 = pack_bf16(rg.O[qb][dt][e0 + 0] * inv * sigmoidf(bf16_lo(g01)),
+                                       rg.O[qb][dt][e0 + 1] * inv * sigmoidf(bf16_hi(g01)));
         if (d0 + 4 <= DH) {
           const uint32_t g23 = g[gw + 1];
-          const uint32_t r23 = pack_bf16(O[qb][dt][e0 + 2] * inv * sigmoidf(bf16_lo(g23)),
-                                         O[qb][dt][e0 + 3] * inv * sigmoidf(bf16_hi(g23)));
+          const uint32_t r23 = pack_bf16(rg.O[qb][dt][e0 + 2] * inv * sigmoidf(bf16_lo(g23)),
+                                         rg.O[qb][dt][e0 + 3] * inv * sigmoidf(bf16_hi(g23)));
           o[gw] = r01;
           o[gw + 1] = r23;
         } else {
