@@ -9,7 +9,7 @@
 // (The pages concatenate content first; the column order of a contraction does
 // not change its value, and positional-first keeps the LDS rows aligned.)
 //
-// Design (one workgroup = 4 waves = 256 queries of one (image, window, head)):
+// Design (one workgroup = 8 waves = 512 queries of one (image, window, head)):
 //
 //  * Scores are computed transposed, S^T = K~ Q~^T, with
 //    v_mfma_f32_32x32x16_bf16: K~ rows are the A operand (read from LDS), the
@@ -27,18 +27,24 @@
 //    in Q~ (a bf16 value) against 1 in K~, column "o" holds -OFF against 1
 //    (2^14 for padded keys, which masks them; those have 0 in column m).  The
 //    MFMA returns t = s*log2(e) - m_hat - OFF and the fast path is p = exp2(t).
+//  * P is packed to bf16 by truncation with one v_perm_b32 per pair (the
+//    rounding convert costs as much as an exp2 on gfx950); the same P feeds
+//    PV and the row sum, so O = PV / l sees a consistent set of weights.
 //  * Rescaling is lazy: p <= 2^-OFF * 2^(growth of the maximum).  The packed
 //    bf16 P values are OR-reduced; bit 14 of a half is set iff p >= 2, i.e.
 //    the maximum grew by more than OFF+1 = 8 (a factor 256).  Only then (and on
 //    the first tile) does the wave take the slow path: exact row maximum, new
 //    m_hat rounded to bf16, recompute, rescale O.
 //  * The row sum l comes for free from the PV MFMA: V channel dh is all ones.
-//  * Software pipeline over key tiles of KT = 64: iteration i issues the
-//    global loads of tile i+1, the QK^T MFMAs of tile i and the exp2/convert
-//    work of tile i-1 in one basic block, so the matrix cores, the
-//    transcendental unit and the VALU work side by side; then the PV MFMAs of
-//    tile i-1 and the LDS store of tile i+1.  Three LDS stages, one barrier
-//    per tile.
+//  * Ping-pong over key tiles of KT = 64.  A workgroup has 8 waves, two per
+//    SIMD, in two groups (waves 0-3 and 4-7) that run half a step apart and
+//    swap roles at every barrier: while one group runs its MFMA phase
+//    (QK^T of tile t and PV of tile t-1, 20 MFMAs per wave), the wave of the
+//    other group on the same SIMD runs its transcendental phase (exp2,
+//    convert and overflow check of tile t, plus its share of staging the
+//    next tiles into LDS).  The matrix core and the transcendental unit of
+//    every SIMD are thus busy at the same time.  Three LDS stages; tile loads
+//    are issued a full step before they are stored.
 //  * Window partitioning is index arithmetic on the NHWC arrays: a window's
 //    real tokens are enumerated row-major, r = iy*nx + ix, so padded positions
 //    are never loaded, and only the last tile can hold padded keys.
@@ -52,7 +58,7 @@ namespace rib {
 namespace {
 
 constexpr int KT = 64;             // keys per tile
-constexpr int NWAVE = 4;           // waves per workgroup
+constexpr int NWAVE = 8;           // waves per workgroup (two groups of four)
 constexpr int QW = 64;             // queries per wave (two 32-query MFMA blocks)
 constexpr int QB = QW * NWAVE;     // queries per workgroup
 constexpr int NSTAGE = 3;          // LDS stages of the key-tile pipeline
@@ -66,14 +72,15 @@ struct Shape {
   static constexpr int KC = (R + DH + 2 + 15) / 16;  // 16-wide contraction chunks
   static constexpr int DT = (DH + 1 + 31) / 32;      // 32-channel output tiles (ones row at DH)
   static constexpr int ROWDW = 8 * KC;               // dwords per Q~/K~ row
-  static constexpr int KSTR = ROWDW + 4;             // LDS row stride in dwords (bank spread)
+  static constexpr int KCH = 2 * KC;                 // 16-byte chunks per K~ row
+  static constexpr int KSTR = ROWDW + 4;             // row stride of the Q~ staging rows (bank spread)
   static constexpr int CONSTDW = R / 2 + DH / 2;     // dword with columns (m, o)
   static constexpr int CM = CONSTDW / 8;             // chunk holding it
   static constexpr int GM = (CONSTDW % 8) / 4;       // lane half holding it
   static constexpr int DM = CONSTDW % 4;             // dword inside the 16-byte operand
-  static constexpr int VSTR = 16 * DT + 4;           // dwords per token-major V row in LDS
-  static constexpr int KS_DW = KT * KSTR;
-  static constexpr int VS_DW = KT * VSTR;
+  static constexpr int VSTR = 16 * DT;               // dwords of V per key
+  static constexpr int KS_DW = KT * ROWDW;           // K~ tile, chunk-major: [chunk][key][4 dwords]
+  static constexpr int VS_DW = KT * VSTR;            // V tile, swizzled for the transposing reads
   static constexpr int STAGE_DW = KS_DW + VS_DW;
   static constexpr int QS_DW = QB * KSTR;
   static constexpr int LDS_DW = (NSTAGE * STAGE_DW > QS_DW) ? NSTAGE * STAGE_DW : QS_DW;
@@ -101,20 +108,43 @@ __device__ __forceinline__ void locate(const Geo& G, int r, int& off, int& n) {
   n = iy * G.ws + ix;
 }
 
+// ---- LDS layouts of a key tile ----------------------------------------------
+// K~: chunk-major, 16-byte chunk c of key j at dword (c*KT + j)*4.  The A
+// operand of chunk c for 32 keys is then 512 contiguous bytes per lane half,
+// and a staging write of one chunk for 64 keys is 1 KB contiguous.
+__device__ __forceinline__ int kchunk_dw(int c, int j) { return (c * KT + j) * 4; }
+// V: 8-byte pieces (4 channels) of 4 consecutive keys and one 16-channel half
+// form a 128-byte block; piece (key, ch) sits at 8-byte index
+//   ((key/4) * 2DT + ch/16) * 16 + (key%4) * 4 + (ch%16)/4,
+// so each 16-lane group of a transposing read covers one contiguous block.
+template <int DT>
+__device__ __forceinline__ int vpiece_dw(int key, int ch) {
+  return 2 * ((((key >> 2) * (2 * DT) + (ch >> 4)) << 4) + ((key & 3) << 2) + ((ch & 15) >> 2));
+}
+
 // ---- staging of one key tile ------------------------------------------------
-// Every wave issues the same four 16-byte buffer loads per lane and tile; only
-// the wave-uniform buffer descriptor and the offset formula differ:
-//   wave 0: the key's positional factor Kp[n][0..16)     (fp32, from kp)
-//   wave 1: the key's content slice Kc (dh bf16)          (from kc)
-//   wave 2: the key's value slice V (dh bf16)             (from v)
-//   wave 3: Kp[n][16..32) when R = 32, otherwise nothing  (zero-length buffer)
-// Buffer loads are bounds-checked by the hardware (reads past the descriptor's
-// size return 0), so the last head slice of the map may over-read its 16-byte
-// chunk safely.  Keeping the load code identical across waves keeps the
-// prefetch free of branches, so its latency stays hidden behind the MFMAs;
-// all role-specific conversion happens at the LDS store.
+// Each wave loads two 16-byte chunks per lane (lane = key) and tile with the
+// same code; only the wave-uniform buffer descriptor and offset differ:
+//   wave 0 / 1: Kp[n][0..8) / Kp[n][8..16)  (fp32)      waves 6 / 7: Kp[n][16..32) when R = 32
+//   wave 2 / 3: Kc dwords [0, 8) / [8, 16)   (bf16)
+//   wave 4 / 5: V  dwords [0, 8) / [8, 16)   (bf16)
+// A wave without a load role gets a zero-length descriptor (its loads return
+// zeros and touch no memory).  Buffer loads are bounds-checked by the
+// hardware, so the last head slice of the map may over-read its last chunk.
+// At the store each role converts its chunks into its part of the LDS rows:
+// K~ row = [bf16 Kp (R/2 dwords) | Kc (dh/2) | (m, o) column pair | zeros],
+// V row = [V (dh/2 dwords), ones pair (1, 0) at channel dh, zeros].
 struct Stage {
-  u32x4_t raw[4];
+  u32x4_t raw[2];
+};
+
+template <int DH, int R>
+struct Roles {
+  static constexpr bool KP1 = R >= 16;           // wave 1 loads Kp[8..16)
+  static constexpr bool KP67 = R == 32;          // waves 6/7 load Kp[16..32)
+  static constexpr bool KC1 = DH / 2 > 8;        // wave 3 loads Kc dwords [8, 16)
+  static constexpr bool V1 = DH / 2 > 8;         // wave 5 loads V dwords [8, 16)
+  static constexpr int KCREG = Shape<DH, R>::ROWDW - R / 2;  // dwords of the K~ row after Kp
 };
 
 template <int DH, int R>
@@ -122,14 +152,12 @@ __device__ __forceinline__ void load_tile(const Geo& G, __amdgpu_buffer_rsrc_t r
                                           Stage& st) {
   int off, n;
   locate<DH>(G, r < G.n_real ? r : G.n_real - 1, off, n);
-  const bool pos = (wave == 0) | (wave == 3);
-  const unsigned voff = pos ? (unsigned)(n * (R * 4) + (wave == 3 ? 64 : 0)) : 2u * (unsigned)off;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    st.raw[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff + 16u * i, 0, 0));
+  const bool pos = (wave == 0) | (wave == 1) | (wave >= 6);
+  const unsigned sub = wave >= 6 ? (unsigned)(wave - 4) : (unsigned)(wave & 1);  // 32-byte sub-chunk
+  const unsigned voff = (pos ? (unsigned)(n * (R * 4)) : 2u * (unsigned)off) + 32u * sub;
+  st.raw[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, 0, 0));
+  st.raw[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff + 16u, 0, 0));
 }
-
-__device__ __forceinline__ uint32_t pick(const Stage& st, int w) { return st.raw[w >> 2][w & 3]; }
 
 // Kp fp32 chunks (8 floats) -> 4 packed bf16 dwords
 __device__ __forceinline__ u32x4_t kp_to_bf16(const u32x4_t& x, const u32x4_t& y, bool real) {
@@ -139,49 +167,78 @@ __device__ __forceinline__ u32x4_t kp_to_bf16(const u32x4_t& x, const u32x4_t& y
   return real ? out : (u32x4_t){0u, 0u, 0u, 0u};
 }
 
+// dword w of the K~ row region after Kp: content, the (m, o) pair, or zero
+template <int DH>
+__device__ __forceinline__ uint32_t kc_word(int w, uint32_t data, bool real) {
+  if (w < DH / 2) return real ? data : 0u;
+  if (w == DH / 2) return real ? 0x3F803F80u : 0x46800000u;  // (1,1) real, (0,2^14) padded
+  return 0u;
+}
+// dword w of the V row: value, the ones pair at channel DH, or zero
+template <int DH>
+__device__ __forceinline__ uint32_t v_word(int w, uint32_t data, bool real) {
+  uint32_t val = w < DH / 2 ? data : (w == DH / 2 ? 0x00003F80u : 0u);
+  return real ? val : 0u;
+}
+
 template <int DH, int R>
 __device__ __forceinline__ void store_tile(uint32_t* stage, int wave, int j, bool real, const Stage& st) {
   using S = Shape<DH, R>;
-  if (wave == 0 || (wave == 3 && R > 16)) {
-    // positional columns: dwords [0, R/2) of the K~ row (wave 3: the second half when R = 32)
-    uint32_t* dst = stage + j * S::KSTR + (wave == 3 ? 8 : 0);
-    constexpr int NQ = (R > 16 ? 16 : R) / 8;
+  using RL = Roles<DH, R>;
+  uint32_t* vs = stage + S::KS_DW;
+  // dword w (a multiple of 4) of key j's K~ row
+  auto kdst = [&](int w) { return reinterpret_cast<u32x4_t*>(stage + kchunk_dw(w >> 2, j)); };
+  // V channels [ch, ch+8) of key j (ch a multiple of 8)
+  auto vdst = [&](int ch) { return reinterpret_cast<u32x4_t*>(vs + vpiece_dw<S::DT>(j, ch)); };
+  if (wave == 0 || (wave == 1 && RL::KP1) || (wave >= 6 && RL::KP67)) {
+    const int q = wave >= 6 ? wave - 4 : wave;  // which 8-float group of Kp
+    *kdst(4 * q) = kp_to_bf16(st.raw[0], st.raw[1], real);
+  }
+  if (wave == 2 || wave == 3) {
+    const int w0 = wave == 2 ? 0 : 8;
+    if (w0 < RL::KCREG) {
 #pragma unroll
-    for (int i = 0; i < NQ; ++i)
-      *reinterpret_cast<u32x4_t*>(dst + 4 * i) = kp_to_bf16(st.raw[2 * i], st.raw[2 * i + 1], real);
-  } else if (wave == 1) {
-    // content columns + the (m, o) pair + zero padding: dwords [R/2, ROWDW)
-    uint32_t* dst = stage + j * S::KSTR + R / 2;
+      for (int i = 0; i < 2; ++i) {
+        if (w0 + 4 * i >= RL::KCREG) break;
+        uint32_t d[4];
 #pragma unroll
-    for (int i = 0; i < (S::ROWDW - R / 2) / 4; ++i) {
-      uint32_t d[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int w = 4 * i + e;
-        uint32_t val;
-        if (w < DH / 2) val = real ? pick(st, w) : 0u;
-        else if (w == DH / 2) val = real ? 0x3F803F80u : 0x46800000u;  // (1,1) real, (0,2^14) padded
-        else val = 0u;
-        d[e] = val;
+        for (int e = 0; e < 4; ++e) d[e] = kc_word<DH>(w0 + 4 * i + e, st.raw[i][e], real);
+        *kdst(R / 2 + w0 + 4 * i) = (u32x4_t){d[0], d[1], d[2], d[3]};
       }
-      *reinterpret_cast<u32x4_t*>(dst + 4 * i) = (u32x4_t){d[0], d[1], d[2], d[3]};
     }
   }
-  if (wave == 2 || (wave == 3 && S::DT > 1)) {
-    // token-major V row: wave 2 channels [0, 32), wave 3 channels [32, 64)
-    uint32_t* dst = stage + S::KS_DW + j * S::VSTR + (wave == 3 ? 16 : 0);
-    const int base = wave == 3 ? 16 : 0;
+  if constexpr (RL::KCREG > 16) {
+    // the K~ row continues past 16 dwords after Kp: (m, o) pair and zeros only
+    if (wave == 7) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < (RL::KCREG - 16) / 4; ++i) {
+        uint32_t d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = kc_word<DH>(16 + 4 * i + e, 0u, real);
+        *kdst(R / 2 + 16 + 4 * i) = (u32x4_t){d[0], d[1], d[2], d[3]};
+      }
+    }
+  }
+  if (wave == 4 || wave == 5) {
+    const int w0 = wave == 4 ? 0 : 8;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
       uint32_t d[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int w = base + 4 * i + e;
-        uint32_t val = (w < DH / 2 && base == 0) ? pick(st, 4 * i + e) : 0u;
-        val = w == DH / 2 ? 0x00003F80u : val;  // (1, 0): ones at channel DH
-        d[e] = real ? val : 0u;
+      for (int e = 0; e < 4; ++e) d[e] = v_word<DH>(w0 + 4 * i + e, st.raw[i][e], real);
+      *vdst(2 * (w0 + 4 * i)) = (u32x4_t){d[0], d[1], d[2], d[3]};
+    }
+  }
+  if constexpr (S::DT > 1) {
+    // V channels [32, 64): the ones pair (dh = 32) and zeros
+    if (wave == 6) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = v_word<DH>(16 + 4 * i + e, 0u, real);
+        *vdst(32 + 8 * i) = (u32x4_t){d[0], d[1], d[2], d[3]};
       }
-      *reinterpret_cast<u32x4_t*>(dst + 4 * i) = (u32x4_t){d[0], d[1], d[2], d[3]};
     }
   }
 }
@@ -205,17 +262,31 @@ struct Regs {
   float mhat[2];
 };
 
-// S^T = K~ Q~^T for the tile in `stage` (64 keys x the wave's 64 queries)
+// Operands of one MFMA phase, all read from LDS before the first MFMA issues:
+// the K~ rows of the tile being scored (A operand of S^T = K~ Q~^T) and the
+// transposed V of the tile being accumulated (A operand of O^T = V^T P^T).
 template <int DH, int R>
-__device__ __forceinline__ void qk_tile(const uint32_t* stage, int l32, int gh, const Regs<DH, R>& rg,
-                                        f32x16_t (&Sacc)[2][2]) {
+struct PhaseOps {
+  u32x4_t ka[2][Shape<DH, R>::KC];
+  u32x4_t va[2][2][Shape<DH, R>::DT];
+};
+
+template <int DH, int R>
+__device__ __forceinline__ void read_k_ops(const uint32_t* stage, int l32, int gh, PhaseOps<DH, R>& ops) {
   using S = Shape<DH, R>;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    u32x4_t a[S::KC];
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int c = 0; c < S::KC; ++c)
-      a[c] = *reinterpret_cast<const u32x4_t*>(stage + (kb * 32 + l32) * S::KSTR + 8 * c + 4 * gh);
+      ops.ka[kb][c] = *reinterpret_cast<const u32x4_t*>(stage + kchunk_dw(2 * c + gh, kb * 32 + l32));
+}
+
+// S^T = K~ Q~^T for 64 keys x the wave's 64 queries
+template <int DH, int R>
+__device__ __forceinline__ void qk_tile(const PhaseOps<DH, R>& ops, const Regs<DH, R>& rg, f32x16_t (&Sacc)[2][2]) {
+  using S = Shape<DH, R>;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16_t acc;
@@ -223,14 +294,15 @@ __device__ __forceinline__ void qk_tile(const uint32_t* stage, int l32, int gh, 
       for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
 #pragma unroll
       for (int c = 0; c < S::KC; ++c)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[c]),
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ops.ka[kb][c]),
                                                       __builtin_bit_cast(bf16x8_t, rg.qt[qb][c]), acc, 0, 0, 0);
       Sacc[qb][kb] = acc;
     }
-  }
 }
 
-// p = exp2(t - shift) packed to bf16 pairs; returns the OR of all packed words
+// p = exp2(t - shift) packed to bf16 pairs (truncated: P feeds both the PV
+// product and, through the ones channel of V, the row sum, so the rounding of
+// P cancels in O = PV / l); returns the OR of all packed words
 __device__ __forceinline__ uint32_t exp_tile(const f32x16_t (&Sacc)[2][2], uint32_t (&P)[2][2][8], float shift0,
                                              float shift1) {
   uint32_t orv = 0;
@@ -241,8 +313,8 @@ __device__ __forceinline__ uint32_t exp_tile(const f32x16_t (&Sacc)[2][2], uint3
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        P[qb][kb][i] = pack_bf16(__builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i] - sh),
-                                 __builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i + 1] - sh));
+        P[qb][kb][i] = pack_bf16_trunc(__builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i] - sh),
+                                       __builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i + 1] - sh));
         orv |= P[qb][kb][i];
       }
   }
@@ -258,19 +330,19 @@ __device__ __forceinline__ uint32_t exp_tile_fast(const f32x16_t (&Sacc)[2][2], 
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        P[qb][kb][i] = pack_bf16(__builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i]),
-                                 __builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i + 1]));
+        P[qb][kb][i] = pack_bf16_trunc(__builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i]),
+                                       __builtin_amdgcn_exp2f(Sacc[qb][kb][2 * i + 1]));
         orv |= P[qb][kb][i];
       }
   return orv;
 }
 
 // Slow path for the tile whose scores are in Sacc: exact row maximum, new
-// reference m_hat, exponentials again, rescale of O (unless first), and the
-// correction of the already computed next-tile scores Snext by the shift.
-template <int DH, int R, bool NEXT>
+// reference m_hat (rounded to bf16), exponentials again, rescale of O
+// (unless this is the first tile) and the new -m_hat in the Q~ operand.
+template <int DH, int R>
 __device__ __forceinline__ void rescale_tile(Regs<DH, R>& rg, const f32x16_t (&Sacc)[2][2], uint32_t (&P)[2][2][8],
-                                             f32x16_t (&Snext)[2][2], bool first, int gh) {
+                                             bool first, int gh) {
   using S = Shape<DH, R>;
   float shift[2];
 #pragma unroll
@@ -295,19 +367,13 @@ __device__ __forceinline__ void rescale_tile(Regs<DH, R>& rg, const f32x16_t (&S
     }
     const uint32_t cd = pack_bf16(-mnew, -OFF);
     if (gh == S::GM) rg.qt[qb][S::CM][S::DM] = cd;
-    if constexpr (NEXT) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) Snext[qb][kb][e] -= shift[qb];
-    }
   }
   exp_tile(Sacc, P, shift[0], shift[1]);
 }
 
-// O^T += V^T P^T for the tile whose V rows are in `stage`
+// transposed V operands of one tile (see pv_tile)
 template <int DH, int R>
-__device__ __forceinline__ void pv_tile(const uint32_t* stage, int lane, Regs<DH, R>& rg, const uint32_t (&P)[2][2][8]) {
+__device__ __forceinline__ void read_v_ops(const uint32_t* stage, int lane, PhaseOps<DH, R>& ops) {
   using S = Shape<DH, R>;
   const uint32_t* vs = stage + S::KS_DW;
   // transposing read: 16-lane group q = lane/16 covers channels 16*(q%2) + i of the
@@ -319,28 +385,36 @@ __device__ __forceinline__ void pv_tile(const uint32_t* stage, int lane, Regs<DH
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      u32x4_t va[S::DT];
+    for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt) {
-        const uint32_t* p = vs + (kb * 32 + 16 * c2 + key0) * S::VSTR + ((dt * 32 + ch0) >> 1);
-        const u32x2_t lo = ds_read_tr16(p);
-        const u32x2_t hi = ds_read_tr16(p + 8 * S::VSTR);
-        va[dt] = (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
+        const int key = kb * 32 + 16 * c2 + key0;
+        const u32x2_t lo = ds_read_tr16(vs + vpiece_dw<S::DT>(key, dt * 32 + ch0));
+        const u32x2_t hi = ds_read_tr16(vs + vpiece_dw<S::DT>(key + 8, dt * 32 + ch0));
+        ops.va[kb][c2][dt] = (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
       }
+}
+
+// O^T += V^T P^T
+template <int DH, int R>
+__device__ __forceinline__ void pv_tile(const PhaseOps<DH, R>& ops, Regs<DH, R>& rg, const uint32_t (&P)[2][2][8]) {
+  using S = Shape<DH, R>;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const u32x4_t pb = {P[qb][kb][4 * c2], P[qb][kb][4 * c2 + 1], P[qb][kb][4 * c2 + 2], P[qb][kb][4 * c2 + 3]};
 #pragma unroll
         for (int dt = 0; dt < S::DT; ++dt)
-          rg.O[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va[dt]),
+          rg.O[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ops.va[kb][c2][dt]),
                                                                  __builtin_bit_cast(bf16x8_t, pb), rg.O[qb][dt], 0, 0, 0);
       }
-    }
 }
 
 template <int DH, int R>
-__global__ void __launch_bounds__(QB, 2)
+__global__ void __launch_bounds__(QB, 1)
 attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
                  const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                  const float* __restrict__ qp, const float* __restrict__ kp,
@@ -421,67 +495,81 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
 
   const int ntiles = (G.n_real + KT - 1) / KT;
   const bool active = q0 + wave * QW < G.n_real;
+  const int grp = wave >> 2;  // 0: waves 0-3 lead, 1: waves 4-7 follow half a step behind
   // this wave's load source (wave-uniform): see load_tile
+  using RL = Roles<DH, R>;
   const unsigned map_bytes = (unsigned)(B * H * W * heads * DH) * 2u;
   const unsigned pos_bytes = (unsigned)(ws * ws * R) * 4u;
-  const void* src = wave == 1 ? (const void*)kc : wave == 2 ? (const void*)v : (const void*)kp;
-  const unsigned nbytes = wave == 1 || wave == 2 ? map_bytes : (wave == 0 || R > 16 ? pos_bytes : 0u);
+  const void* src = (wave == 2 || wave == 3) ? (const void*)kc
+                  : (wave == 4 || wave == 5) ? (const void*)v : (const void*)kp;
+  const bool loads = wave == 0 || (wave == 1 && RL::KP1) || wave == 2 || (wave == 3 && RL::KC1) ||
+                     wave == 4 || (wave == 5 && RL::V1) || (wave >= 6 && RL::KP67);
+  const unsigned nbytes = !loads ? 0u : (wave >= 2 && wave <= 5) ? map_bytes : pos_bytes;
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(src), (short)0, (int)nbytes, (int)RSRC_WORD3);
 
-  // ---- pipeline prologue: tile 0 staged and scored, tile 1 staged
+  // ---- prologue: tile 0 staged by everyone, tile 1 loaded into registers
   Stage st;
   load_tile<DH, R>(G, rsrc, wave, lane, st);
   store_tile<DH, R>(lds, wave, lane, lane < G.n_real, st);
-  __syncthreads();
   if (ntiles > 1) load_tile<DH, R>(G, rsrc, wave, KT + lane, st);
-  f32x16_t SA[2][2], SB[2][2];
-  uint32_t P[2][2][8];
-  if (active) qk_tile<DH, R>(lds, l32, gh, rg, SA);
-  if (ntiles > 1) {
-    store_tile<DH, R>(lds + S::STAGE_DW, wave, lane, KT + lane < G.n_real, st);
-    __syncthreads();
-  }
+  __syncthreads();
 
-  // One pipeline step: the scores of tile `it` go into Snew while the softmax
-  // and PV of tile it-1 (scores in Sprev) run.  Stages: s_cur holds tile it,
-  // the one before it tile it-1, the one after it receives tile it+1.
-  int s_cur = 1;
-  auto step = [&](int it, f32x16_t (&Sprev)[2][2], f32x16_t (&Snew)[2][2]) {
-    const int s_prev = s_cur == 0 ? NSTAGE - 1 : s_cur - 1;
-    const int s_next = s_cur == NSTAGE - 1 ? 0 : s_cur + 1;
-    const bool more = it + 1 < ntiles;
-    if (more) load_tile<DH, R>(G, rsrc, wave, (it + 1) * KT + lane, st);
-    if (active) {
-      qk_tile<DH, R>(lds + s_cur * S::STAGE_DW, l32, gh, rg, Snew);
-      const uint32_t orv = exp_tile_fast(Sprev, P);
-      const bool need = (it == 1) || (orv & 0x40004000u);
-      if (__builtin_amdgcn_ballot_w64(need)) rescale_tile<DH, R, true>(rg, Sprev, P, Snew, it == 1, gh);
-      pv_tile<DH, R>(lds + s_prev * S::STAGE_DW, lane, rg, P);
+  f32x16_t Sacc[2][2];
+  uint32_t P[2][2][8];
+  // Half-steps: the leading group (waves 0-3) runs MFMA(0), softmax(0),
+  // MFMA(1), ..., softmax(T-1), MFMA(T), idle; the following group (waves
+  // 4-7) runs idle, MFMA(0), ..., softmax(T-1), MFMA(T).  MFMA(t) = QK^T of
+  // tile t (t < T) and PV of tile t-1 (t >= 1); softmax(t) = exp2, convert
+  // and overflow check of tile t plus this wave's share of staging: the
+  // leading group stores tile t+1 and loads t+2, the following group stores
+  // t+2 and loads t+3 (it stages tile 1 in its idle first half-step).  A
+  // stage is rewritten only after both groups' last PV on the tile it held.
+  auto softmax = [&](int t) {
+    const int xs = t + 1 + grp;  // tile staged now
+    if (xs < ntiles) {
+      store_tile<DH, R>(lds + (xs % NSTAGE) * S::STAGE_DW, wave, lane, xs * KT + lane < G.n_real, st);
+      if (xs + 1 < ntiles) load_tile<DH, R>(G, rsrc, wave, (xs + 1) * KT + lane, st);
     }
-    if (more) store_tile<DH, R>(lds + s_next * S::STAGE_DW, wave, lane, (it + 1) * KT + lane < G.n_real, st);
+    if (active) {
+      const uint32_t orv = exp_tile_fast(Sacc, P);
+      const bool first = t == 0;
+      if (__builtin_amdgcn_ballot_w64(first || (orv & 0x40004000u))) rescale_tile<DH, R>(rg, Sacc, P, first, gh);
+    }
+  };
+  if (grp == 1) {
+    if (ntiles > 1) {
+      store_tile<DH, R>(lds + S::STAGE_DW, wave, lane, KT + lane < G.n_real, st);
+      if (ntiles > 2) load_tile<DH, R>(G, rsrc, wave, 2 * KT + lane, st);
+    }
     __syncthreads();
-    s_cur = s_next;
-  };
-  // the last tile: softmax + PV only (its scores are in Slast, its stage before s_cur)
-  auto finish = [&](f32x16_t (&Slast)[2][2]) {
-    if (!active) return;
-    const uint32_t orv = exp_tile_fast(Slast, P);
-    const bool need = (ntiles == 1) || (orv & 0x40004000u);
-    if (__builtin_amdgcn_ballot_w64(need)) rescale_tile<DH, R, false>(rg, Slast, P, Slast, ntiles == 1, gh);
-    pv_tile<DH, R>(lds + (s_cur == 0 ? NSTAGE - 1 : s_cur - 1) * S::STAGE_DW, lane, rg, P);
-  };
-  int it = 1;
-  for (; it + 1 < ntiles; it += 2) {
-    step(it, SA, SB);
-    step(it + 1, SB, SA);
   }
-  if (it < ntiles) {
-    step(it, SA, SB);
-    finish(SB);
-  } else {
-    finish(SA);  // also the single-tile case
+  PhaseOps<DH, R> ops;
+  if (active) {
+    read_k_ops<DH, R>(lds, l32, gh, ops);
+    qk_tile<DH, R>(ops, rg, Sacc);
   }
+  __syncthreads();
+  for (int t = 0; t + 1 < ntiles; ++t) {
+    softmax(t);
+    __syncthreads();
+    if (active) {
+      read_k_ops<DH, R>(lds + ((t + 1) % NSTAGE) * S::STAGE_DW, l32, gh, ops);
+      read_v_ops<DH, R>(lds + (t % NSTAGE) * S::STAGE_DW, lane, ops);
+      __builtin_amdgcn_sched_barrier(0);  // every operand read issues before the first MFMA
+      qk_tile<DH, R>(ops, rg, Sacc);
+      pv_tile<DH, R>(ops, rg, P);
+    }
+    __syncthreads();
+  }
+  softmax(ntiles - 1);
+  __syncthreads();
+  if (active) {
+    read_v_ops<DH, R>(lds + ((ntiles - 1) % NSTAGE) * S::STAGE_DW, lane, ops);
+    pv_tile<DH, R>(ops, rg, P);
+  }
+  __syncthreads();
+  if (grp == 0) __syncthreads();
 
   if (!active) return;
   // ---- epilogue: O / l * sigmoid(G), bf16, NHWC

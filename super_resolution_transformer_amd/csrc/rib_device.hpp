@@ -19,6 +19,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Two floats -> packed bf16 pair by truncation (the high 16 bits of each; low
+// half = a).  One full-rate v_perm_b32, where the rounding convert runs at the
+// transcendental rate.
+__device__ __forceinline__ uint32_t pack_bf16_trunc(float a, float b) {
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a), 0x07060302u);
+}
+
 // float value of one bf16 half of a packed dword
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __builtin_bit_cast(float, x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __builtin_bit_cast(float, x & 0xFFFF0000u); }
