@@ -145,18 +145,38 @@ struct Roles {
   static constexpr bool KC1 = DH / 2 > 8;        // wave 3 loads Kc dwords [8, 16)
   static constexpr bool V1 = DH / 2 > 8;         // wave 5 loads V dwords [8, 16)
   static constexpr int KCREG = Shape<DH, R>::ROWDW - R / 2;  // dwords of the K~ row after Kp
+  // every K~ part is staged by waves 0-3: the K~ operands of the next tile can
+  // then be read during the softmax phase (see the main loop)
+  static constexpr bool KPREF = !KP67 && KCREG <= 16;
 };
 
-template <int DH, int R>
-__device__ __forceinline__ void load_tile(const Geo& G, __amdgpu_buffer_rsrc_t rsrc, int wave, int r,
-                                          Stage& st) {
-  int off, n;
-  locate<DH>(G, r < G.n_real ? r : G.n_real - 1, off, n);
-  const bool pos = (wave == 0) | (wave == 1) | (wave >= 6);
-  const unsigned sub = wave >= 6 ? (unsigned)(wave - 4) : (unsigned)(wave & 1);  // 32-byte sub-chunk
-  const unsigned voff = (pos ? (unsigned)(n * (R * 4)) : 2u * (unsigned)off) + 32u * sub;
-  st.raw[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, 0, 0));
-  st.raw[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff + 16u, 0, 0));
+// Per-lane position of the key this lane loads, advanced by KT keys per tile
+// without divisions: (ix, column of the window) and the byte offset of the
+// lane's chunks in this wave's source buffer.  Offsets of lanes past the last
+// real key run on beyond the window; those keys are masked at the store and
+// reads past the buffer end return zeros (bounds-checked buffer loads).
+struct Cursor {
+  int ix;
+  unsigned voff;
+};
+
+struct CursorStep {
+  unsigned col;   // bytes per window column (uniform)
+  unsigned wrap;  // bytes from the end of one window row to the start of the next (uniform)
+};
+
+__device__ __forceinline__ void cursor_advance(Cursor& c, const CursorStep& cs, int nx) {
+  c.ix += KT;
+  c.voff += KT * cs.col;
+  while (c.ix >= nx) {
+    c.ix -= nx;
+    c.voff += cs.wrap;
+  }
+}
+
+__device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t rsrc, const Cursor& c, Stage& st) {
+  st.raw[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, c.voff, 0, 0));
+  st.raw[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rsrc, c.voff + 16u, 0, 0));
 }
 
 // Kp fp32 chunks (8 floats) -> 4 packed bf16 dwords
@@ -181,10 +201,12 @@ __device__ __forceinline__ uint32_t v_word(int w, uint32_t data, bool real) {
   return real ? val : 0u;
 }
 
-template <int DH, int R>
-__device__ __forceinline__ void store_tile(uint32_t* stage, int wave, int j, bool real, const Stage& st) {
+// MASK: the tile may hold padded keys (only the last tile of a window can)
+template <int DH, int R, bool MASK>
+__device__ __forceinline__ void store_tile(uint32_t* stage, int wave, int j, bool real_key, const Stage& st) {
   using S = Shape<DH, R>;
   using RL = Roles<DH, R>;
+  const bool real = MASK ? real_key : true;
   uint32_t* vs = stage + S::KS_DW;
   // dword w (a multiple of 4) of key j's K~ row
   auto kdst = [&](int w) { return reinterpret_cast<u32x4_t*>(stage + kchunk_dw(w >> 2, j)); };
@@ -271,14 +293,24 @@ struct PhaseOps {
   u32x4_t va[2][2][Shape<DH, R>::DT];
 };
 
+// Keeps an LDS dword index in a register as computed: every read of a phase
+// then addresses base + immediate offset, instead of the compiler hoisting one
+// address register per read out of the loop.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// K~ operands of one tile; kst = dword index of the stage's K~ block
 template <int DH, int R>
-__device__ __forceinline__ void read_k_ops(const uint32_t* stage, int l32, int gh, PhaseOps<DH, R>& ops) {
+__device__ __forceinline__ void read_k_ops(const uint32_t* lds, int kst, int l32, int gh, PhaseOps<DH, R>& ops) {
   using S = Shape<DH, R>;
+  const uint32_t* base = lds + opaque(kst + kchunk_dw(gh, l32));
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int c = 0; c < S::KC; ++c)
-      ops.ka[kb][c] = *reinterpret_cast<const u32x4_t*>(stage + kchunk_dw(2 * c + gh, kb * 32 + l32));
+      ops.ka[kb][c] = *reinterpret_cast<const u32x4_t*>(base + kchunk_dw(2 * c, kb * 32));
 }
 
 // S^T = K~ Q~^T for 64 keys x the wave's 64 queries
@@ -371,26 +403,28 @@ __device__ __forceinline__ void rescale_tile(Regs<DH, R>& rg, const f32x16_t (&S
   exp_tile(Sacc, P, shift[0], shift[1]);
 }
 
-// transposed V operands of one tile (see pv_tile)
+// transposed V operands of one tile (see pv_tile); vst = dword index of the
+// stage's V block
 template <int DH, int R>
-__device__ __forceinline__ void read_v_ops(const uint32_t* stage, int lane, PhaseOps<DH, R>& ops) {
+__device__ __forceinline__ void read_v_ops(const uint32_t* lds, int vst, int lane, PhaseOps<DH, R>& ops) {
   using S = Shape<DH, R>;
-  const uint32_t* vs = stage + S::KS_DW;
   // transposing read: 16-lane group q = lane/16 covers channels 16*(q%2) + i of the
   // 32-channel tile for keys 4g + k (g = q/2); input lane j = 4k + m addresses
   // channels 16*(q%2) + 4m .. +3 of key 4g + k (+8 for the second read).
+  // Keys kb*32 + 16*c2 (+8) and channel tiles dt shift the address by constants.
   const int j = lane & 15, q = lane >> 4;
   const int key0 = 4 * (q >> 1) + (j >> 2);
   const int ch0 = 16 * (q & 1) + 4 * (j & 3);
+  const uint32_t* base = lds + opaque(vst + vpiece_dw<S::DT>(key0, ch0));
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt) {
-        const int key = kb * 32 + 16 * c2 + key0;
-        const u32x2_t lo = ds_read_tr16(vs + vpiece_dw<S::DT>(key, dt * 32 + ch0));
-        const u32x2_t hi = ds_read_tr16(vs + vpiece_dw<S::DT>(key + 8, dt * 32 + ch0));
+        const int kofs = kb * 32 + 16 * c2;
+        const u32x2_t lo = ds_read_tr16(base + vpiece_dw<S::DT>(kofs, dt * 32));
+        const u32x2_t hi = ds_read_tr16(base + vpiece_dw<S::DT>(kofs + 8, dt * 32));
         ops.va[kb][c2][dt] = (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
       }
 }
@@ -496,7 +530,7 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
   const int ntiles = (G.n_real + KT - 1) / KT;
   const bool active = q0 + wave * QW < G.n_real;
   const int grp = wave >> 2;  // 0: waves 0-3 lead, 1: waves 4-7 follow half a step behind
-  // this wave's load source (wave-uniform): see load_tile
+  // this wave's load source (wave-uniform): see the staging notes above
   using RL = Roles<DH, R>;
   const unsigned map_bytes = (unsigned)(B * H * W * heads * DH) * 2u;
   const unsigned pos_bytes = (unsigned)(ws * ws * R) * 4u;
@@ -507,12 +541,31 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
   const unsigned nbytes = !loads ? 0u : (wave >= 2 && wave <= 5) ? map_bytes : pos_bytes;
   const __amdgpu_buffer_rsrc_t rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(src), (short)0, (int)nbytes, (int)RSRC_WORD3);
+  // load cursor of this lane, starting at key r = lane of tile 0
+  const bool pos = (wave == 0) | (wave == 1) | (wave >= 6);
+  const unsigned sub = wave >= 6 ? (unsigned)(wave - 4) : (unsigned)(wave & 1);  // 32-byte sub-chunk
+  CursorStep cs;
+  cs.col = pos ? (unsigned)(R * 4) : (unsigned)(G.C * 2);
+  const unsigned row_bytes = pos ? (unsigned)(ws * R * 4) : (unsigned)(W * G.C * 2);
+  cs.wrap = row_bytes - (unsigned)G.nx * cs.col;
+  Cursor cur;
+  {
+    const int iy = (int)(((float)lane + 0.5f) * G.inv_nx);
+    cur.ix = lane - iy * G.nx;
+    const unsigned base = pos ? 0u : 2u * (unsigned)(((G.b * H + G.wy * ws) * W + G.wx * ws) * G.C + G.h * DH);
+    cur.voff = base + (unsigned)iy * row_bytes + (unsigned)cur.ix * cs.col + 32u * sub;
+  }
 
   // ---- prologue: tile 0 staged by everyone, tile 1 loaded into registers
   Stage st;
-  load_tile<DH, R>(G, rsrc, wave, lane, st);
-  store_tile<DH, R>(lds, wave, lane, lane < G.n_real, st);
-  if (ntiles > 1) load_tile<DH, R>(G, rsrc, wave, KT + lane, st);
+  load_tile(rsrc, cur, st);
+  if (ntiles > 1) {
+    store_tile<DH, R, false>(lds, wave, lane, true, st);
+    cursor_advance(cur, cs, G.nx);
+    load_tile(rsrc, cur, st);
+  } else {
+    store_tile<DH, R, true>(lds, wave, lane, lane < G.n_real, st);
+  }
   __syncthreads();
 
   f32x16_t Sacc[2][2];
@@ -520,52 +573,68 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
   // Half-steps: the leading group (waves 0-3) runs MFMA(0), softmax(0),
   // MFMA(1), ..., softmax(T-1), MFMA(T), idle; the following group (waves
   // 4-7) runs idle, MFMA(0), ..., softmax(T-1), MFMA(T).  MFMA(t) = QK^T of
-  // tile t (t < T) and PV of tile t-1 (t >= 1); softmax(t) = exp2, convert
-  // and overflow check of tile t plus this wave's share of staging: the
-  // leading group stores tile t+1 and loads t+2, the following group stores
-  // t+2 and loads t+3 (it stages tile 1 in its idle first half-step).  A
-  // stage is rewritten only after both groups' last PV on the tile it held.
-  auto softmax = [&](int t) {
-    const int xs = t + 1 + grp;  // tile staged now
-    if (xs < ntiles) {
-      store_tile<DH, R>(lds + (xs % NSTAGE) * S::STAGE_DW, wave, lane, xs * KT + lane < G.n_real, st);
-      if (xs + 1 < ntiles) load_tile<DH, R>(G, rsrc, wave, (xs + 1) * KT + lane, st);
+  // tile t (t < T) and PV of tile t-1 (t >= 1), plus this wave's share of
+  // staging: store tile t+1 (loaded one step earlier) and load tile t+2,
+  // issued while the operand reads are in flight.  softmax(t) = exp2,
+  // convert and overflow check of tile t, no LDS traffic.  Tile x is stored
+  // in half-steps 2x-2 (leading group) and 2x-1 (following group) and read
+  // in half-steps 2x .. 2x+3; its stage is rewritten in half-step 2x+4.
+  PhaseOps<DH, R> ops;
+  auto stage = [&](int x) {  // store tile x, load tile x+1
+    if (x < ntiles) {
+      uint32_t* dst = lds + (x % NSTAGE) * S::STAGE_DW;
+      if (x + 1 < ntiles) {
+        store_tile<DH, R, false>(dst, wave, lane, true, st);
+        cursor_advance(cur, cs, G.nx);
+        load_tile(rsrc, cur, st);
+      } else {
+        store_tile<DH, R, true>(dst, wave, lane, x * KT + lane < G.n_real, st);
+      }
     }
+  };
+  auto softmax = [&](int t) {
     if (active) {
+      if constexpr (RL::KPREF) {
+        if (t + 1 < ntiles) read_k_ops<DH, R>(lds, ((t + 1) % NSTAGE) * S::STAGE_DW, l32, gh, ops);
+      }
       const uint32_t orv = exp_tile_fast(Sacc, P);
       const bool first = t == 0;
       if (__builtin_amdgcn_ballot_w64(first || (orv & 0x40004000u))) rescale_tile<DH, R>(rg, Sacc, P, first, gh);
     }
   };
-  if (grp == 1) {
-    if (ntiles > 1) {
-      store_tile<DH, R>(lds + S::STAGE_DW, wave, lane, KT + lane < G.n_real, st);
-      if (ntiles > 2) load_tile<DH, R>(G, rsrc, wave, 2 * KT + lane, st);
-    }
-    __syncthreads();
-  }
-  PhaseOps<DH, R> ops;
+  if (grp == 1) __syncthreads();
+  if (active) read_k_ops<DH, R>(lds, 0, l32, gh, ops);
+  stage(1);
   if (active) {
-    read_k_ops<DH, R>(lds, l32, gh, ops);
+    __builtin_amdgcn_sched_barrier(0);
     qk_tile<DH, R>(ops, rg, Sacc);
   }
   __syncthreads();
   for (int t = 0; t + 1 < ntiles; ++t) {
     softmax(t);
     __syncthreads();
+    // The MFMA phase (operand reads, staging, MFMAs) takes issue priority over
+    // the other group's softmax on the same SIMD; with equal priority the
+    // older wave wins every tie and the following group's MFMA phase starves.
+    __builtin_amdgcn_s_setprio(2);
     if (active) {
-      read_k_ops<DH, R>(lds + ((t + 1) % NSTAGE) * S::STAGE_DW, l32, gh, ops);
-      read_v_ops<DH, R>(lds + (t % NSTAGE) * S::STAGE_DW, lane, ops);
-      __builtin_amdgcn_sched_barrier(0);  // every operand read issues before the first MFMA
+      if constexpr (!RL::KPREF) read_k_ops<DH, R>(lds, ((t + 1) % NSTAGE) * S::STAGE_DW, l32, gh, ops);
+      read_v_ops<DH, R>(lds, (t % NSTAGE) * S::STAGE_DW + S::KS_DW, lane, ops);
+    }
+    stage(t + 2);
+    if (active) {
+      __builtin_amdgcn_sched_barrier(0);  // operand reads and staging issue before the first MFMA
       qk_tile<DH, R>(ops, rg, Sacc);
+      __builtin_amdgcn_sched_barrier(0);  // QK first: its operands are the earliest ready
       pv_tile<DH, R>(ops, rg, P);
     }
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
   }
   softmax(ntiles - 1);
   __syncthreads();
   if (active) {
-    read_v_ops<DH, R>(lds + ((ntiles - 1) % NSTAGE) * S::STAGE_DW, lane, ops);
+    read_v_ops<DH, R>(lds, ((ntiles - 1) % NSTAGE) * S::STAGE_DW + S::KS_DW, lane, ops);
     pv_tile<DH, R>(ops, rg, P);
   }
   __syncthreads();
