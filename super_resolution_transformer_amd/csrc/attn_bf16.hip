@@ -675,9 +675,195 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
   }
 }
 
+// ---- small windows (window^2 <= 256) ------------------------------------------
+// One workgroup of four waves covers a whole window and head: every thread
+// stages one key (all roles of the staging scheme above) into its 64-key tile,
+// so all key tiles are resident in LDS after a single barrier and the key loop
+// runs without barriers.  Each lane builds its Q~ operands and reads its gate
+// values straight from global memory before that barrier, so the loads of a
+// workgroup are all in flight at once; two workgroups share a CU.  The
+// workload is HBM-bound (16x16 windows: 4 key tiles).
+constexpr int SQ = 256;        // queries (and keys) per workgroup
+constexpr int SNT = SQ / KT;   // key tiles, all resident
+
+// dword w of a Q~ row: [Qp/sqrt(R), Qc/sqrt(dh)] (log2 e folded in), the
+// (-m_hat = 0, -OFF) pair, zeros
+template <int DH, int R>
+__device__ __forceinline__ uint32_t qrow_word(int w, int off, int n, bool real, const float* __restrict__ qp,
+                                              const uint32_t* __restrict__ qc, float sp, float sc) {
+  using S = Shape<DH, R>;
+  uint32_t val = 0u;
+  if (w < R / 2) {
+    const float2 pq = *reinterpret_cast<const float2*>(qp + n * R + 2 * w);
+    val = pack_bf16(pq.x * sp, pq.y * sp);
+  } else if (w < R / 2 + DH / 2) {
+    const uint32_t x = qc[(off >> 1) + (w - R / 2)];
+    val = pack_bf16(bf16_lo(x) * sc, bf16_hi(x) * sc);
+  } else if (w == S::CONSTDW) {
+    val = 0xC0E00000u;  // (-m_hat = 0, -OFF = -7)
+  }
+  return (real || w == S::CONSTDW) ? val : 0u;
+}
+
+template <int DH, int R>
+__global__ void __launch_bounds__(SQ, 2)
+attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
+                       const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
+                       const float* __restrict__ qp, const float* __restrict__ kp,
+                       uint32_t* __restrict__ o, int B, int H, int W, int heads, int ws, int total) {
+  using S = Shape<DH, R>;
+  using RL = Roles<DH, R>;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[SNT * S::STAGE_DW];
+
+  const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
+  if (logical >= total) return;
+  const int nWy = (H + ws - 1) / ws, nWx = (W + ws - 1) / ws;
+  Geo G;
+  {
+    int t = logical;
+    G.h = t % heads; t /= heads;
+    G.wx = t % nWx; t /= nWx;
+    G.wy = t % nWy;
+    G.b = t / nWy;
+    G.H = H; G.W = W; G.C = heads * DH; G.ws = ws;
+    G.nx = min(ws, W - G.wx * ws);
+    G.n_real = min(ws, H - G.wy * ws) * G.nx;
+    G.inv_nx = 1.0f / (float)G.nx;
+  }
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int gh = lane >> 5;
+
+  // ---- key r = tid: every staging role of the key, into tile r / 64 = wave
+  {
+    const bool real = tid < G.n_real;
+    int off, n;
+    locate<DH>(G, real ? tid : G.n_real - 1, off, n);
+    const unsigned map_bytes = (unsigned)(B * H * W * heads * DH) * 2u;
+    const unsigned pos_bytes = (unsigned)(ws * ws * R) * 4u;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(kc), (short)0,
+                                                                        (int)map_bytes, (int)RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(v), (short)0,
+                                                                        (int)map_bytes, (int)RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(kp), (short)0,
+                                                                        (int)pos_bytes, (int)RSRC_WORD3);
+    uint32_t* stage = lds + wave * S::STAGE_DW;
+    Stage st[8];
+#pragma unroll
+    for (int role = 0; role < 8; ++role) {
+      const bool loads = role == 0 || (role == 1 && RL::KP1) || role == 2 || (role == 3 && RL::KC1) ||
+                         role == 4 || (role == 5 && RL::V1) || (role >= 6 && RL::KP67);
+      if (loads) {
+        const bool pos = role == 0 || role == 1 || role >= 6;
+        const unsigned sub = role >= 6 ? (unsigned)(role - 4) : (unsigned)(role & 1);
+        const unsigned voff = (pos ? (unsigned)(n * (R * 4)) : 2u * (unsigned)off) + 32u * sub;
+        const __amdgpu_buffer_rsrc_t rs = (role == 2 || role == 3) ? rk : (role == 4 || role == 5) ? rv : rp;
+        st[role].raw[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+        st[role].raw[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16u, 0, 0));
+      } else {
+        st[role].raw[0] = (u32x4_t){0u, 0u, 0u, 0u};
+        st[role].raw[1] = (u32x4_t){0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int role = 0; role < 8; ++role) store_tile<DH, R, true>(stage, role, lane, real, st[role]);
+  }
+
+  // ---- this lane's Q~ operands and gate values, straight from global memory
+  const float sp = LOG2E / sqrtf((float)R);
+  const float sc = LOG2E / sqrtf((float)DH);
+  Regs<DH, R> rg;
+  uint32_t gv[2][S::DT][4][2];
+  int offq[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = wave * QW + qb * 32 + l32;
+    const bool real = r < G.n_real;
+    int off, n;
+    locate<DH>(G, real ? r : G.n_real - 1, off, n);
+    offq[qb] = off;
+#pragma unroll
+    for (int c = 0; c < S::KC; ++c) {
+      u32x4_t q;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = qrow_word<DH, R>(8 * c + 4 * gh + i, off, n, real, qp, qc, sp, sc);
+      rg.qt[qb][c] = q;
+    }
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = dt * 32 + 8 * q4 + 4 * gh;
+        const int gw = (off + d0) >> 1;
+        gv[qb][dt][q4][0] = d0 < DH ? g[gw] : 0u;
+        gv[qb][dt][q4][1] = d0 + 4 <= DH ? g[gw + 1] : 0u;
+      }
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) rg.O[qb][dt][e] = 0.0f;
+    rg.mhat[qb] = 0.0f;
+  }
+  __syncthreads();
+  if (wave * QW >= G.n_real) return;  // no barrier follows
+
+  const int ntiles = (G.n_real + KT - 1) / KT;
+  PhaseOps<DH, R> ops;
+  f32x16_t Sacc[2][2];
+  uint32_t P[2][2][8];
+  for (int x = 0; x < ntiles; ++x) {
+    read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
+    read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
+    qk_tile<DH, R>(ops, rg, Sacc);
+    const uint32_t orv = exp_tile_fast(Sacc, P);
+    const bool first = x == 0;
+    if (__builtin_amdgcn_ballot_w64(first || (orv & 0x40004000u))) rescale_tile<DH, R>(rg, Sacc, P, first, gh);
+    pv_tile<DH, R>(ops, rg, P);
+  }
+
+  // ---- epilogue: O / l * sigmoid(G), bf16, NHWC
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = wave * QW + qb * 32 + l32;
+    const LanePair pr = lane_pair(rg.O[qb][S::LT][S::LR]);
+    const float lsum = S::LG ? pr.hi : pr.lo;
+    if (r >= G.n_real) continue;
+    const float inv = 1.0f / lsum;
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = dt * 32 + 8 * q4 + 4 * gh;
+        if (d0 >= DH) continue;
+        const int e0 = 4 * q4;
+        const int gw = (offq[qb] + d0) >> 1;
+        const uint32_t g01 = gv[qb][dt][q4][0];
+        const uint32_t r01 = pack_bf16(rg.O[qb][dt][e0 + 0] * inv * sigmoidf(bf16_lo(g01)),
+                                       rg.O[qb][dt][e0 + 1] * inv * sigmoidf(bf16_hi(g01)));
+        o[gw] = r01;
+        if (d0 + 4 <= DH) {
+          const uint32_t g23 = gv[qb][dt][q4][1];
+          o[gw + 1] = pack_bf16(rg.O[qb][dt][e0 + 2] * inv * sigmoidf(bf16_lo(g23)),
+                                rg.O[qb][dt][e0 + 3] * inv * sigmoidf(bf16_hi(g23)));
+        }
+      }
+  }
+}
+
 template <int DH, int R>
 hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
   const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws;
+  if (a.ws * a.ws <= SQ) {
+    const int total = a.B * nWy * nWx * a.heads;
+    const int grid = 8 * ((total + 7) / 8);
+    hipLaunchKernelGGL((attn_bf16_small_kernel<DH, R>), dim3(grid), dim3(SQ), 0, stream,
+                       (const uint32_t*)a.qc, (const uint32_t*)a.kc, (const uint32_t*)a.v,
+                       (const uint32_t*)a.g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.H, a.W, a.heads, a.ws,
+                       total);
+    return hipGetLastError();
+  }
   const int qblocks = (a.ws * a.ws + QB - 1) / QB;
   const int total = a.B * nWy * nWx * a.heads * qblocks;
   const int grid = 8 * ((total + 7) / 8);

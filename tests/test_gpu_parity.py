@@ -105,6 +105,10 @@ SMALL = [
     (1, 1, 1, 2, 30, 16, 2, "bf16"),           # a window with one token
     (1, 1, 100, 1, 30, 16, 16, "bf16"),
     (1, 3, 130, 1, 16, 16, 128, "bf16"),       # largest window
+    (2, 21, 19, 2, 32, 16, 16, "bf16"),        # whole-window kernel, (32, 16) variant
+    (1, 16, 16, 1, 30, 16, 16, "bf16"),        # exactly one full 16x16 window
+    (2, 17, 33, 3, 16, 16, 16, "bf16"),        # one-row bottom windows
+    (1, 40, 41, 1, 16, 16, 17, "bf16"),        # 289 tokens: the tiled kernel just above 256
 ]
 
 
@@ -209,27 +213,30 @@ def test_positional_one_hot_is_bit_exact(torch, dtype, ws, H, W, R, dh):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_locality_and_equivariance_bit_exact(torch, dtype):
-    note(f"locality {dtype}")
-    ws, H, W, B, heads, dh, R = 16, 48, 48, 2, 3, 30 if dtype == "bf16" else 16, 16
+@pytest.mark.parametrize("ws", [16, 32])
+def test_locality_and_equivariance_bit_exact(torch, dtype, ws):
+    """Window 16 runs the whole-window bf16 kernel, window 32 the tiled one."""
+    note(f"locality ws={ws} {dtype}")
+    H, W, B, heads, dh, R = 3 * ws, 3 * ws, 2, 3, 30 if dtype == "bf16" else 16, 16
     p = synthetic.make_problem(B, H, W, heads, dh, R, dtype=dtype, seed=7)
     (qc, kc, v, g), w = to_dev(torch, p)
     qp, kp = rib.encode(ws, p.L, p.hidden, R, w)
     base = rib.window_attn(qc, kc, v, g, qp, kp, heads, ws)
     kc2, v2 = kc.clone(), v.clone()
-    kc2[1, 20, 37] += 1.5
-    v2[1, 20, 37] -= 2.0
+    ty, tx = ws + ws // 4, 2 * ws + ws // 3  # a token of window (1, 2)
+    kc2[1, ty, tx] += 1.5
+    v2[1, ty, tx] -= 2.0
     out = rib.window_attn(qc, kc2, v2, g, qp, kp, heads, ws)
     changed = (out != base).any(dim=-1).cpu().numpy()
     inside = np.zeros_like(changed)
-    inside[1, 16:32, 32:48] = True
+    inside[1, ws:2 * ws, 2 * ws:3 * ws] = True
     assert changed[inside].mean() > 0.9 and not changed[~inside].any()
 
     def swap(a):
         a = a.clone()
-        t = a[:, 0:16, 16:32].clone()
-        a[:, 0:16, 16:32] = a[:, 32:48, 0:16]
-        a[:, 32:48, 0:16] = t
+        t = a[:, 0:ws, ws:2 * ws].clone()
+        a[:, 0:ws, ws:2 * ws] = a[:, 2 * ws:3 * ws, 0:ws]
+        a[:, 2 * ws:3 * ws, 0:ws] = t
         return a
     out = rib.window_attn(swap(qc), swap(kc), swap(v), swap(g), qp, kp, heads, ws)
     assert torch.equal(out, swap(base))
