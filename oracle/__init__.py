@@ -64,6 +64,8 @@ def _configure(L):
     L.rib_oracle_attn_rows.restype = ctypes.c_int
     L.rib_oracle_window_debug.argtypes = ([_D] * 6 + [ctypes.c_int] * 11 + [_D] * 3 + [_I] * 3)
     L.rib_oracle_window_debug.restype = ctypes.c_int
+    L.rib_oracle_cla_gate.argtypes = [_D] * 5 + [ctypes.c_int] * 4 + [_D]
+    L.rib_oracle_cla_gate.restype = ctypes.c_int
     return L
 
 
@@ -193,3 +195,19 @@ def window_debug(qc, kc, v, g, qp, kp, heads: int, window: int, b: int, wy: int,
     m = nt * nt
     toks = np.stack([ty[:nt], tx[:nt], tn[:nt]], axis=1)
     return (Sc[:m].reshape(nt, nt), Bm[:m].reshape(nt, nt), P[:m].reshape(nt, nt), toks)
+
+
+def cla_gate(x, dw_w, dw_b, pw_w, pw_b) -> np.ndarray:
+    """G = PWConv1x1(DWConv3x3(X)) in NHWC float64 (zero padding, stride 1).
+
+    dw_w: [C, 3, 3], dw_b: [C], pw_w: [C_in, C_out] (y = x W), pw_b: [C].
+    """
+    x = _f64(x)
+    B, H, W, C = x.shape
+    dw_w, dw_b, pw_w, pw_b = _f64(dw_w), _f64(dw_b), _f64(pw_w), _f64(pw_b)
+    if dw_w.shape != (C, 3, 3) or dw_b.shape != (C,) or pw_w.shape != (C, C) or pw_b.shape != (C,):
+        raise ValueError("gate weights do not match the channel count")
+    g = np.zeros(x.shape, np.float64)
+    if lib().rib_oracle_cla_gate(_p(x), _p(dw_w), _p(dw_b), _p(pw_w), _p(pw_b), B, H, W, C, _p(g)) != 0:
+        raise ValueError("oracle gate rejected its arguments")
+    return g

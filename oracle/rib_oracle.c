@@ -315,3 +315,53 @@ int rib_oracle_window_debug(const double* qc, const double* kc, const double* v,
   free(out);
   return nt;
 }
+
+/*
+ * CLA gate producer (explainer section 2.3, the convolution path of CLA;
+ * gist.science summaries part B: a depth-wise 3x3 convolution followed by a
+ * point-wise 1x1 convolution produces the gating map):
+ *
+ *   D[b,y,x,c] = dw_b[c] + sum_{dy,dx in {-1,0,1}} X[b,y+dy,x+dx,c] * dw_w[c][dy+1][dx+1]
+ *                (positions outside the map contribute zero: "same" padding, stride 1)
+ *   G[b,y,x,o] = pw_b[o] + sum_c D[b,y,x,c] * pw_w[c][o]
+ *
+ * X and G are NHWC [B][H][W][C]; dw_w is [C][3][3], pw_w is [C_in][C_out]
+ * (y = x W, the orientation used for every weight here).  D is kept per
+ * token in double and never rounded.
+ */
+int rib_oracle_cla_gate(const double* x, const double* dw_w, const double* dw_b, const double* pw_w,
+                        const double* pw_b, int B, int H, int W, int C, double* g) {
+  if (B < 1 || H < 1 || W < 1 || C < 1) return -1;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* d = (double*)malloc(sizeof(double) * C);
+    if (!d) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(static)
+      for (long t = 0; t < (long)B * H * W; ++t) {
+        int b = (int)(t / ((long)H * W)), y = (int)(t / W % H), xx = (int)(t % W);
+        for (int c = 0; c < C; ++c) {
+          double acc = dw_b[c];
+          for (int dy = -1; dy <= 1; ++dy)
+            for (int dx = -1; dx <= 1; ++dx) {
+              int yy = y + dy, xs = xx + dx;
+              if (yy < 0 || yy >= H || xs < 0 || xs >= W) continue;
+              acc += x[(((size_t)b * H + yy) * W + xs) * C + c] * dw_w[(size_t)c * 9 + (dy + 1) * 3 + (dx + 1)];
+            }
+          d[c] = acc;
+        }
+        double* out = g + (size_t)t * C;
+        for (int o = 0; o < C; ++o) {
+          double acc = pw_b[o];
+          for (int c = 0; c < C; ++c) acc += d[c] * pw_w[(size_t)c * C + o];
+          out[o] = acc;
+        }
+      }
+      free(d);
+    }
+  }
+  return fail ? -1 : 0;
+}

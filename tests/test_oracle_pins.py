@@ -10,7 +10,8 @@ mistake fails at least one pin.
 Pages: "Rank-Factorized Implicit Neural Bias" (gist.science summaries part A:
 the concatenation identity; part B: the gate) and the omica.com.cn explainer
 (section 2.2: coordinate encoder, implicit field, attention rewrite; section
-2.3: O = (softmax(S) V) * sigmoid(G)).
+2.3: O = (softmax(S) V) * sigmoid(G), G from a depth-wise 3x3 and a point-wise
+1x1 convolution).
 """
 import json
 import math
@@ -377,6 +378,77 @@ def test_rows_entry_matches_full():
 
 
 # ---------------------------------------------------------------- mutations: the pins bite
+
+# ---------------------------------------------------------------- CLA gate producer
+def gate_weights(C, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((C, 3, 3)) / 3.0, rng.standard_normal(C) * 0.1,
+            rng.standard_normal((C, C)) / math.sqrt(C), rng.standard_normal(C) * 0.1)
+
+
+def torch_gate(x, dw_w, dw_b, pw_w, pw_b):
+    """The same definition through PyTorch's conv2d (CPU, float64): depth-wise 3x3 with zero
+    padding (groups = C), then a 1x1 convolution whose weight is pw_w transposed."""
+    import torch
+    C = x.shape[-1]
+    xt = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64)).permute(0, 3, 1, 2)
+    d = torch.nn.functional.conv2d(xt, torch.from_numpy(dw_w)[:, None], torch.from_numpy(dw_b),
+                                   padding=1, groups=C)
+    g = torch.nn.functional.conv2d(d, torch.from_numpy(pw_w.T.copy())[:, :, None, None],
+                                   torch.from_numpy(pw_b))
+    return g.permute(0, 2, 3, 1).numpy()
+
+
+@pytest.mark.parametrize("B,H,W,C", [(2, 5, 7, 6), (1, 1, 1, 3), (1, 3, 13, 48), (2, 9, 4, 30)])
+def test_cla_gate_matches_torch_conv2d(B, H, W, C):
+    rng = np.random.default_rng(B * 100 + H * 10 + W + C)
+    x = rng.standard_normal((B, H, W, C))
+    w = gate_weights(C, C)
+    got = oracle.cla_gate(x, *w)
+    want = torch_gate(x, *w)
+    assert np.abs(got - want).max() <= 1e-12 * max(1.0, np.abs(want).max())
+
+
+def test_cla_gate_identity_weights_return_x():
+    """Centre tap 1, identity point-wise weights, no biases: G == X exactly."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 6, 5, 7))
+    dw = np.zeros((7, 3, 3))
+    dw[:, 1, 1] = 1.0
+    g = oracle.cla_gate(x, dw, np.zeros(7), np.eye(7), np.zeros(7))
+    assert np.array_equal(g, x)
+
+
+def test_cla_gate_constant_input_counts_taps():
+    """X = a everywhere, point-wise identity: D = a * (sum of the taps that fall inside the map)
+    + b -- 9 taps inside, 6 on an edge, 4 in a corner (zero padding)."""
+    C, a = 3, 1.5
+    x = np.full((1, 4, 5, C), a)
+    dw = np.arange(1.0, 1.0 + 9 * C).reshape(C, 3, 3)
+    db = np.array([0.25, -0.5, 1.0])
+    g = oracle.cla_gate(x, dw, db, np.eye(C), np.zeros(C))
+    inner = a * dw.sum(axis=(1, 2)) + db
+    corner = a * dw[:, 1:, 1:].sum(axis=(1, 2)) + db      # top-left: rows/cols -1 are outside
+    edge = a * dw[:, 1:, :].sum(axis=(1, 2)) + db         # top edge: row -1 outside
+    assert np.allclose(g[0, 2, 2], inner, rtol=0, atol=1e-12)
+    assert np.allclose(g[0, 0, 0], corner, rtol=0, atol=1e-12)
+    assert np.allclose(g[0, 0, 2], edge, rtol=0, atol=1e-12)
+
+
+def test_cla_gate_point_wise_orientation():
+    """Depth-wise identity, one-hot point-wise weight W[c_in=1][c_out=2] = 1: channel 2 of G is
+    channel 1 of X (y = x W orientation), the others are their biases."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((1, 3, 3, 4))
+    dw = np.zeros((4, 3, 3))
+    dw[:, 1, 1] = 1.0
+    pw = np.zeros((4, 4))
+    pw[1, 2] = 1.0
+    pb = np.array([0.5, -1.0, 0.0, 2.0])
+    g = oracle.cla_gate(x, dw, np.zeros(4), pw, pb)
+    assert np.array_equal(g[..., 2], x[..., 1])
+    assert np.all(g[..., 0] == 0.5) and np.all(g[..., 1] == -1.0) and np.all(g[..., 3] == 2.0)
+
 MUTATIONS = {
     "bias dropped": ("Bm[j] = bb * inv_sqrt_r;", "Bm[j] = 0.0 * bb;"),
     "bias unscaled": ("Bm[j] = bb * inv_sqrt_r;", "Bm[j] = bb;"),
@@ -392,6 +464,12 @@ MUTATIONS = {
     "no max subtraction": ("P[j] = exp(P[j] - mx);", "P[j] = exp(P[j]);"),
     "hidden relu dropped": ("h[j] = acc > 0.0 ? acc : 0.0;", "h[j] = acc;"),
     "kp uses Wq": ("ak += h[j] * Wk[(size_t)j * R + r];", "ak += h[j] * Wq[(size_t)j * R + r];"),
+    "gate point-wise transposed": ("acc += d[c] * pw_w[(size_t)c * C + o];", "acc += d[c] * pw_w[(size_t)o * C + c];"),
+    "gate taps transposed": ("dw_w[(size_t)c * 9 + (dy + 1) * 3 + (dx + 1)]", "dw_w[(size_t)c * 9 + (dx + 1) * 3 + (dy + 1)]"),
+    "gate depth-wise bias dropped": ("double acc = dw_b[c];", "double acc = 0.0 * dw_b[c];"),
+    "gate point-wise bias dropped": ("double acc = pw_b[o];", "double acc = 0.0 * pw_b[o];"),
+    "gate padding on the wrong side": ("if (yy < 0 || yy >= H || xs < 0 || xs >= W) continue;",
+                                       "if (yy < 0 || yy >= H || xs < 0 || xs >= W || (dy == 1 && dx == 1 && y == 0)) continue;"),
 }
 
 PINS = [
@@ -408,6 +486,10 @@ PINS = [
     lambda: test_one_hot_index_mapping_returns_v(4, 9, 6),
     test_large_scores_stay_finite,
     test_encoder_matches_brute,
+    lambda: test_cla_gate_matches_torch_conv2d(2, 5, 7, 6),
+    test_cla_gate_identity_weights_return_x,
+    test_cla_gate_constant_input_counts_taps,
+    test_cla_gate_point_wise_orientation,
 ]
 
 
