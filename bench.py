@@ -7,7 +7,8 @@ rib_encode (positional factors for the window size) + rib_window_attn
 training-patch forward: 32 images of 96x96 tokens, C = 180 (6 heads x 30),
 R = 16, one 96x96 window per image.  Secondary figures for the 64x64 window
 (1x180x320, C = 180), the 640x360 input with 96x96 windows, and the 16x16
-window of the SST-lite map (HBM-bound) are reported in the same JSON line.
+window of the SST-lite map (HBM-bound) are reported in the same JSON line, and so is the
+CLA gate producer (rib_cla_gate, HBM-bound) on the same maps.
 
 Prints ONE JSON line.  Timing: HIP events on the stream the kernels run on.
 """
@@ -137,6 +138,40 @@ def time_attn_only(torch, wl, reps, warmup):
     return s.elapsed_time(e) / reps
 
 
+def time_gate(torch, rib, synthetic):
+    """CLA gate producer G = PWConv1x1(DWConv3x3(X)) on the workloads' maps (bf16); HBM roofline.
+    Algorithmic bytes: X read + G written (bf16) + fp32 weights; input sets rotate so that the
+    maps are not served from the 256 MB MALL."""
+    res = {}
+    for name, (B, H, W, C, copies) in (("32x96x96, C=180", (32, 96, 96, 180, 3)),
+                                       ("1x360x640, C=180", (1, 360, 640, 180, 3)),
+                                       ("1x180x320, C=48", (1, 180, 320, 48, 40))):
+        p = synthetic.make_gate_problem(B, H, W, C, "bf16", seed=7)
+        x0 = torch.from_numpy(p.x_bits.view("int16")).view(torch.bfloat16).cuda()
+        xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+        gs = [torch.empty_like(x0) for _ in range(copies)]
+        w = [torch.from_numpy(a).cuda() for a in (p.dw_w, p.dw_b, p.pw_w, p.pw_b)]
+        reps = max(30, 2 * copies)
+        for i in range(copies):
+            rib.cla_gate_into(xs[i], *w, gs[i])
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(reps):
+            rib.cla_gate_into(xs[i % copies], *w, gs[i % copies])
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        nbytes = 2 * B * H * W * C * 2 + 4 * (C * 9 + C + C * C + C)
+        flops = B * H * W * (18 * C + 2 * C * C)
+        res[name] = {"ms": ms, "alg_gbs": nbytes / (ms * 1e-3) / 1e9,
+                     "pct_hbm": 100 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "tflops": flops / (ms * 1e-3) / 1e12, "tokens_per_s": B * H * W / (ms * 1e-3)}
+        del xs, gs
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(synthetic, cfg_idx, ws, units_sample):
     """The fp64 oracle as it stands, on the host cores, over a bounded sample of
     (image, window, head) units of the same workload, scaled to tokens/s."""
@@ -239,6 +274,9 @@ def main():
             del w2
             torch.cuda.empty_cache()
         out["other_windows"] = extra
+
+    if not args.no_extra:
+        out["cla_gate"] = time_gate(torch, rib, synthetic)
 
     if args.copy_calibration:
         x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")

@@ -107,6 +107,30 @@ rib_status rib_window_attn(const void* qc, const void* kc, const void* v, const 
  */
 rib_status rib_attn_supported(int dh, int R, int window, rib_dtype dtype);
 
+/*
+ * rib_cla_gate -- the gating map of Convolutional Local Attention (explainer
+ * section 2.3: G = PWConv(DWConv3x3(X)), a depth-wise separable convolution of
+ * the block input; gist.science summaries part B: depth-wise 3x3, then
+ * point-wise 1x1):
+ *   D[b,y,x,c] = dw_b[c] + sum_{dy,dx in {-1,0,1}} X[b,y+dy,x+dx,c] dw_w[c][dy+1][dx+1]
+ *                (positions outside the map are zero: same-size output)
+ *   G[b,y,x,o] = pw_b[o] + sum_c D[b,y,x,c] pw_w[c][o]
+ * G is the `g` argument of rib_window_attn.
+ *
+ * x      : device, [B][H][W][C] of `dtype` (read).
+ * g      : device, same shape and dtype (written); must not overlap x or the
+ *          weights.
+ * dw_w   : device, float32 [C][3][3]; dw_b: device, float32 [C].
+ * pw_w   : device, float32 [C][C], row = input channel (y = x W); pw_b: [C].
+ * dtype  : RIB_F32 -- fp32 throughout; RIB_BF16 -- bf16 maps, the depth-wise
+ *          stencil in fp32 rounded to bf16, the point-wise product on bf16
+ *          matrix cores (weights rounded to bf16) with fp32 accumulation.
+ * Limits : C even, 2 <= C <= 256; B*H*W*C < 2^31; pointers 4-byte aligned.
+ */
+rib_status rib_cla_gate(const void* x, const float* dw_w, const float* dw_b, const float* pw_w,
+                        const float* pw_b, void* g, int B, int H, int W, int C, rib_dtype dtype,
+                        void* stream);
+
 /* Text describing the last non-OK status returned on this thread ("" if none).
  * The pointer stays valid until the next library call on the same thread. */
 const char* rib_last_error(void);
@@ -114,7 +138,7 @@ const char* rib_last_error(void);
 /* ABI version of this header (incremented on any incompatible change). */
 int rib_abi_version(void);
 
-#define RIB_ABI_VERSION 1
+#define RIB_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

@@ -51,6 +51,8 @@ def lib(path: str | None = None):
     L.rib_encode.restype = i
     L.rib_window_attn.argtypes = [vp] * 7 + [i] * 8 + [vp]
     L.rib_window_attn.restype = i
+    L.rib_cla_gate.argtypes = [vp] * 6 + [i] * 5 + [vp]
+    L.rib_cla_gate.restype = i
     L.rib_attn_supported.argtypes = [i, i, i, i]
     L.rib_attn_supported.restype = i
     L.rib_last_error.argtypes = []
@@ -145,6 +147,30 @@ def window_attn_into(qc, kc, v, g, qp, kp, heads: int, window: int, o) -> None:
     dh, R = C // heads, qp.shape[1]
     _check(lib().rib_window_attn(_ptr(qc), _ptr(kc), _ptr(v), _ptr(g), _ptr(qp), _ptr(kp), _ptr(o),
                                  B, H, W, heads, dh, R, window, _dtype_code(qc), _stream(qc)))
+
+
+def cla_gate(x, dw_w, dw_b, pw_w, pw_b):
+    """G = PWConv1x1(DWConv3x3(X)) (the CLA gating map) for an NHWC map x; returns a new tensor."""
+    import torch
+    g = torch.empty_like(x)
+    cla_gate_into(x, dw_w, dw_b, pw_w, pw_b, g)
+    return g
+
+
+def cla_gate_into(x, dw_w, dw_b, pw_w, pw_b, g) -> None:
+    import torch
+    if x.dim() != 4 or g.shape != x.shape or g.dtype != x.dtype:
+        raise ValueError("x and g must be [B, H, W, C] of one dtype")
+    B, H, W, C = x.shape
+    ws = (dw_w, dw_b, pw_w, pw_b)
+    if any(t.dtype != torch.float32 for t in ws):
+        raise ValueError("gate weights must be float32")
+    if dw_w.shape != (C, 3, 3) or dw_b.shape != (C,) or pw_w.shape != (C, C) or pw_b.shape != (C,):
+        raise ValueError("gate weights must be dw_w [C,3,3], dw_b [C], pw_w [C,C], pw_b [C]")
+    if not all(t.is_cuda and t.is_contiguous() for t in ws + (x, g)):
+        raise ValueError("all tensors must be contiguous GPU tensors")
+    _check(lib().rib_cla_gate(_ptr(x), _ptr(dw_w), _ptr(dw_b), _ptr(pw_w), _ptr(pw_b), _ptr(g), B, H, W, C,
+                              _dtype_code(x), _stream(x)))
 
 
 def supported(dh: int, R: int, window: int, dtype) -> bool:

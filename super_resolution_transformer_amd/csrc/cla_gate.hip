@@ -1,0 +1,333 @@
+// cla_gate.hip -- the gate producer of Convolutional Local Attention (gfx950).
+//
+// The gating map of CLA comes from a depth-wise separable convolution of the
+// block input (omica.com.cn explainer section 2.3: G = PWConv(DWConv3x3(X));
+// gist.science summaries part B: depth-wise 3x3 then point-wise 1x1):
+//   D[b,y,x,c] = dw_b[c] + sum_{dy,dx} X[b,y+dy,x+dx,c] * dw_w[c][dy+1][dx+1]
+//                (zero padding, stride 1: G keeps the map's shape)
+//   G[b,y,x,o] = pw_b[o] + sum_c D[b,y,x,c] * pw_w[c][o]
+// on NHWC maps.  G then gates the attention output element-wise.
+//
+// Design: persistent workgroups (one wave per 32-channel output block, at least
+// four) walk tiles of 32 tokens (one segment of a map row).  The three input row segments around the tile (with
+// a one-token halo on each side) are loaded straight into LDS (buffer loads
+// with the LDS destination, so a whole tile is in flight without registers),
+// one token per 16-byte-aligned LDS slot, tokens outside the map as zeros;
+// the next tile's loads are issued as soon as phase 1 has read the rows.
+// Phase 1 computes the depth-wise stencil in fp32 from LDS
+// (each thread owns one channel pair, keeps its 18 taps in registers and walks
+// a run of 8 consecutive tokens, so every input column is read and unpacked
+// once) and writes D, rounded to bf16, into a second LDS tile.
+// Phase 2 is the point-wise product as G^T = W_pw^T D^T on
+// v_mfma_f32_32x32x16_bf16: each wave keeps its 32-channel output blocks of
+// W_pw^T as A operands in VGPRs for the whole launch and reads the B operands
+// (8 channels of one token per lane) from the D tile; in the accumulator each
+// lane holds one token and 4 groups of 4 consecutive output channels, which
+// are biased, rounded and written into an LDS output tile; the tile's tokens
+// are one contiguous span of G, stored with 16-byte writes.  The fp32 path
+// keeps D in fp32 and does the point-wise sum with FMAs.
+#include "rib_device.hpp"
+#include "rib_launch.hpp"
+
+namespace rib {
+
+namespace {
+
+constexpr int GT = 32;          // tokens per tile
+constexpr int GTHREADS = 256;   // four waves
+constexpr int GCMAX = 256;      // largest channel count
+
+__device__ __forceinline__ void tile_coords(long tile, int nseg, int H, int& b, int& y, int& x0) {
+  const int seg = (int)(tile % nseg);
+  const long t2 = tile / nseg;
+  y = (int)(t2 % H);
+  b = (int)(t2 / H);
+  x0 = seg * GT;
+}
+
+// ---------------------------------------------------------------- fp32
+__global__ void __launch_bounds__(GTHREADS)
+cla_gate_f32_kernel(const float* __restrict__ x, const float* __restrict__ dw_w, const float* __restrict__ dw_b,
+                    const float* __restrict__ pw_w, const float* __restrict__ pw_b, float* __restrict__ g,
+                    int B, int H, int W, int C, int nseg, long ntiles) {
+  __shared__ float d[GT * GCMAX];
+  for (long tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    int b, y, x0;
+    tile_coords(tile, nseg, H, b, y, x0);
+    for (int e = threadIdx.x; e < GT * C; e += GTHREADS) {
+      const int t = e / C, c = e - t * C;
+      const int xx = x0 + t;
+      float acc = 0.0f;
+      if (xx < W) {
+        acc = dw_b[c];
+        for (int dy = -1; dy <= 1; ++dy)
+          for (int dx = -1; dx <= 1; ++dx) {
+            const int yy = y + dy, xs = xx + dx;
+            if (yy < 0 || yy >= H || xs < 0 || xs >= W) continue;
+            acc = fmaf(x[(((long)b * H + yy) * W + xs) * C + c], dw_w[c * 9 + (dy + 1) * 3 + (dx + 1)], acc);
+          }
+      }
+      d[t * GCMAX + c] = acc;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < GT * C; e += GTHREADS) {
+      const int t = e / C, o = e - t * C;
+      const int xx = x0 + t;
+      if (xx >= W) continue;
+      float acc = pw_b[o];
+      for (int c = 0; c < C; ++c) acc = fmaf(d[t * GCMAX + c], pw_w[c * C + o], acc);
+      g[(((long)b * H + y) * W + xx) * C + o] = acc;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- bf16
+// NB = 32-channel output blocks (C <= 32*NB); NW = max(4, NB) waves, wave w owns output
+// block w.  Phase 1 splits the tile into 4 runs of 8 tokens: thread (pair cp, run) with
+// 16*NW >= C/2 threads per run.
+template <int NB>
+struct GateShape {
+  static constexpr int NW = NB > 4 ? 8 : 4;   // waves per workgroup (2 per SIMD for wide maps)
+  static constexpr int NT = 64 * NW;          // threads
+  static constexpr int KCH = 2 * NB;          // 16-channel contraction chunks
+  static constexpr int DSTR = 8 * KCH + 4;    // dwords per token row of the D tile (bank spread)
+  static constexpr int XT = GT + 2;           // tokens of an input row segment (left/right halo)
+  static constexpr int XS_DW = 3 * XT * 16 * NB + 256;  // staged input rows (+ one wave's overrun)
+  static constexpr int OS_DW = GT * 16 * NB;  // output tile, NHWC order
+  static constexpr int TPR = 16 * NW;         // phase-1 threads per run
+  static constexpr int NRUN = GT / 4;         // tokens per run
+};
+
+template <int NB>
+__global__ void __launch_bounds__(GateShape<NB>::NT, 2)
+cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ dw_w,
+                     const float* __restrict__ dw_b, const float* __restrict__ pw_w,
+                     const float* __restrict__ pw_b, uint32_t* __restrict__ g, int B, int H, int W, int C,
+                     int nseg, long ntiles) {
+  using S = GateShape<NB>;
+  constexpr int XT = S::XT, KCH = S::KCH, DSTR = S::DSTR, NRUN = S::NRUN;
+  __shared__ __attribute__((aligned(16))) uint32_t dt[GT * DSTR];
+  __shared__ __attribute__((aligned(16))) uint32_t xs[S::XS_DW];
+  __shared__ __attribute__((aligned(16))) uint32_t ot[S::OS_DW];
+  __shared__ float pbias[GCMAX];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int gh = lane >> 5;
+  const int CP = C >> 1;  // channel pairs
+  const bool has_block = wave < NB && wave * 32 < C;
+
+  // ---- point-wise weights as A operands of this wave's output block: row = output
+  // channel, 8 input channels per lane
+  u32x4_t wa[KCH];
+  {
+    const int o = wave * 32 + l32;
+#pragma unroll
+    for (int kc = 0; kc < KCH; ++kc) {
+      uint32_t w4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * kc + 8 * gh + 2 * i;
+        const float a = (has_block && o < C && c < C) ? pw_w[c * C + o] : 0.0f;
+        const float b2 = (has_block && o < C && c + 1 < C) ? pw_w[(c + 1) * C + o] : 0.0f;
+        w4[i] = pack_bf16(a, b2);
+      }
+      wa[kc] = (u32x4_t){w4[0], w4[1], w4[2], w4[3]};
+    }
+  }
+
+  // ---- depth-wise taps of this thread's channel pair; it computes tokens t0 .. t0+NRUN-1
+  const int cp = tid % S::TPR;
+  const int t0 = (tid / S::TPR) * NRUN;
+  const bool has_pair = cp < CP;
+  float tap[2][9], tb[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = 2 * cp + h;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) tap[h][k] = has_pair ? dw_w[c * 9 + k] : 0.0f;
+    tb[h] = has_pair ? dw_b[c] : 0.0f;
+  }
+  // contraction channels [C, 16*KCH) stay zero in the D tile
+  for (int e = tid; e < GT * (8 * KCH - CP); e += S::NT) {
+    const int t = e / (8 * KCH - CP), p = CP + e % (8 * KCH - CP);
+    dt[t * DSTR + p] = 0u;
+  }
+  for (int o = tid; o < C; o += S::NT) pbias[o] = pw_b[o];
+
+  // Input staging: LDS holds rows y-1, y, y+1 of tokens x0-1 .. x0+GT as a flat array of
+  // 16-byte chunks, chunk f = (row * XT + token) * CH + k at dwords 4f, one token every TS
+  // dwords (C/2 rounded up to 4) so that a chunk never spans two tokens.  The chunks are
+  // loaded straight into LDS (buffer_load ... lds: lane l of a wave writes base + 16 l), so a
+  // whole tile is in flight at once without registers; tokens outside the map get an
+  // out-of-range offset, which the buffer bounds check turns into zeros.
+  const int TS = (CP + 3) & ~3;
+  const int CH = TS >> 2;  // chunks per token
+  const int NCHK = 3 * XT * CH;
+  const float inv_ch = 1.0f / (float)CH;
+  const unsigned map_bytes = (unsigned)((long)B * H * W * C * 2);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(x), (short)0,
+                                                                      (int)map_bytes, 0x00020000);
+  // Per-lane chunk geometry is the same for every tile: for pass j of this wave, chunk
+  // f = wave*64 + j*NT + lane has row r, token p and sub-chunk k; its byte offset relative to
+  // the tile's first token (row y-1, token x0-1) is pre[j].  Packed: r | p << 2.
+  constexpr int NPASS = (3 * XT * 16 * NB / 4 + S::NT - 1) / S::NT;
+  int rp[NPASS];
+  unsigned pre[NPASS];
+#pragma unroll
+  for (int j = 0; j < NPASS; ++j) {
+    const int f = wave * 64 + j * S::NT + lane;
+    const int q = (int)(((float)f + 0.5f) * inv_ch);  // token row (exact: f < 2^16)
+    const int k = f - q * CH;
+    const int r = q / XT, p = q - r * XT;
+    rp[j] = f < NCHK ? (r | (p << 2)) : -1;
+    pre[j] = (unsigned)(((r * W + p) * CP + 4 * k) * 4);
+  }
+  auto issue_tile = [&](long tile) {
+    int b, y, x0;
+    tile_coords(tile, nseg, H, b, y, x0);
+    const long base = ((((long)b * H + (y - 1)) * W + (x0 - 1)) * CP) * 4;  // may be negative
+#pragma unroll
+    for (int j = 0; j < NPASS; ++j) {
+      const int f0 = wave * 64 + j * S::NT;
+      if (f0 >= NCHK) break;  // wave-uniform
+      const int r = rp[j] & 3, p = rp[j] >> 2;
+      const bool valid = rp[j] >= 0 && y + r - 1 >= 0 && y + r - 1 < H && x0 - 1 + p >= 0 && x0 - 1 + p < W;
+      const unsigned off = valid ? (unsigned)(base + (long)pre[j]) : 0xFFFFFFF0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(xs + 4 * f0), 16, off,
+                                               0, 0, 0);
+    }
+  };
+  if (blockIdx.x < ntiles) issue_tile(blockIdx.x);
+  for (long tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    int b, y, x0;
+    tile_coords(tile, nseg, H, b, y, x0);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's input chunks (and last tile's stores) are done
+    __syncthreads();
+    // ---- phase 1: D = depth-wise 3x3 (fp32) over the run, rounded to bf16 into the D tile;
+    // a column of three input values is read and unpacked once and used by three tokens
+    if (has_pair) {
+      float c0[3][2], c1[3][2], c2[3][2];  // input columns x-1, x, x+1 (rows y-1, y, y+1)
+      auto column = [&](int p, float (&c)[3][2]) {
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+          const uint32_t v = xs[(r * XT + p) * TS + cp];
+          c[r][0] = bf16_lo(v);
+          c[r][1] = bf16_hi(v);
+        }
+      };
+      column(t0, c0);
+      column(t0 + 1, c1);
+#pragma unroll
+      for (int i = 0; i < NRUN; ++i) {
+        column(t0 + i + 2, c2);
+        float a0 = tb[0], a1 = tb[1];
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+          a0 = fmaf(c0[r][0], tap[0][3 * r], a0);
+          a1 = fmaf(c0[r][1], tap[1][3 * r], a1);
+          a0 = fmaf(c1[r][0], tap[0][3 * r + 1], a0);
+          a1 = fmaf(c1[r][1], tap[1][3 * r + 1], a1);
+          a0 = fmaf(c2[r][0], tap[0][3 * r + 2], a0);
+          a1 = fmaf(c2[r][1], tap[1][3 * r + 2], a1);
+        }
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            c0[r][h] = c1[r][h];
+            c1[r][h] = c2[r][h];
+          }
+        dt[(t0 + i) * DSTR + cp] = x0 + t0 + i < W ? pack_bf16(a0, a1) : 0u;
+      }
+    }
+    __syncthreads();
+    // the input rows are consumed: the next tile's loads overlap the point-wise product
+    if (tile + gridDim.x < ntiles) issue_tile(tile + gridDim.x);
+    // ---- phase 2: G^T = W_pw^T D^T for this wave's output block, biased and rounded into
+    // the output tile (NHWC order: token row t holds C/2 dwords)
+    if (has_block) {
+      f32x16_t acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+      for (int kc = 0; kc < KCH; ++kc) {
+        const u32x4_t bo = *reinterpret_cast<const u32x4_t*>(dt + l32 * DSTR + 8 * kc + 4 * gh);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, wa[kc]),
+                                                      __builtin_bit_cast(bf16x8_t, bo), acc, 0, 0, 0);
+      }
+      uint32_t* orow = ot + l32 * CP;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int oc = wave * 32 + 8 * q + 4 * gh;
+        if (oc < C) orow[oc >> 1] = pack_bf16(acc[4 * q] + pbias[oc], acc[4 * q + 1] + pbias[oc + 1]);
+        if (oc + 2 < C) orow[(oc >> 1) + 1] = pack_bf16(acc[4 * q + 2] + pbias[oc + 2], acc[4 * q + 3] + pbias[oc + 3]);
+      }
+    }
+    __syncthreads();
+    // ---- the tile's output tokens are one contiguous span of G: 16-byte stores
+    {
+      const int ntok = min(GT, W - x0);
+      const int ndw = ntok * CP;
+      uint32_t* gs = g + (((long)b * H + y) * W + x0) * CP;
+      for (int c4 = tid; 4 * c4 < ndw; c4 += S::NT) {
+        const int d = 4 * c4;
+        if (d + 4 <= ndw) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ot + d);
+          *reinterpret_cast<u32x4_t*>(gs + d) = v;
+        } else {
+          for (int i = d; i < ndw; ++i) gs[i] = ot[i];
+        }
+      }
+    }
+  }
+}
+
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return cus;
+}
+
+template <int NB>
+hipError_t launch_gate_bf16(const GateArgs& a, int nseg, long ntiles, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((cla_gate_bf16_kernel<NB>), dim3(grid), dim3(GateShape<NB>::NT), 0, stream, (const uint32_t*)a.x,
+                     a.dw_w, a.dw_b, a.pw_w, a.pw_b, (uint32_t*)a.g, a.B, a.H, a.W, a.C, nseg, ntiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_cla_gate(const GateArgs& a, bool bf16, hipStream_t stream) {
+  const int nseg = (a.W + GT - 1) / GT;
+  const long ntiles = (long)a.B * a.H * nseg;
+  const long cap = 2L * device_cus();
+  const int grid = (int)(ntiles < cap ? ntiles : cap);
+  if (!bf16) {
+    hipLaunchKernelGGL(cla_gate_f32_kernel, dim3(grid), dim3(GTHREADS), 0, stream, (const float*)a.x, a.dw_w,
+                       a.dw_b, a.pw_w, a.pw_b, (float*)a.g, a.B, a.H, a.W, a.C, nseg, ntiles);
+    return hipGetLastError();
+  }
+  switch ((a.C + 31) / 32) {
+    case 1: return launch_gate_bf16<1>(a, nseg, ntiles, grid, stream);
+    case 2: return launch_gate_bf16<2>(a, nseg, ntiles, grid, stream);
+    case 3: return launch_gate_bf16<3>(a, nseg, ntiles, grid, stream);
+    case 4: return launch_gate_bf16<4>(a, nseg, ntiles, grid, stream);
+    case 5: return launch_gate_bf16<5>(a, nseg, ntiles, grid, stream);
+    case 6: return launch_gate_bf16<6>(a, nseg, ntiles, grid, stream);
+    case 7: return launch_gate_bf16<7>(a, nseg, ntiles, grid, stream);
+    case 8: return launch_gate_bf16<8>(a, nseg, ntiles, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace rib

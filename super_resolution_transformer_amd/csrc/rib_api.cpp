@@ -113,4 +113,27 @@ rib_status rib_window_attn(const void* qc, const void* kc, const void* v, const 
   return hip_status(e, "rib_window_attn launch");
 }
 
+
+rib_status rib_cla_gate(const void* x, const float* dw_w, const float* dw_b, const float* pw_w,
+                        const float* pw_b, void* g, int B, int H, int W, int C, rib_dtype dtype,
+                        void* stream) {
+  if (!x || !dw_w || !dw_b || !pw_w || !pw_b || !g) return fail(RIB_ERR_INVALID_ARG, "rib_cla_gate: null pointer");
+  if (B < 1 || H < 1 || W < 1 || C < 1)
+    return fail(RIB_ERR_INVALID_ARG, "rib_cla_gate: B, H, W, C must be >= 1 (got %d, %d, %d, %d)", B, H, W, C);
+  if (dtype != RIB_F32 && dtype != RIB_BF16) return fail(RIB_ERR_INVALID_ARG, "rib_cla_gate: unknown dtype %d", (int)dtype);
+  if (C % 2 != 0 || C > 256)
+    return fail(RIB_ERR_UNSUPPORTED, "rib_cla_gate: C must be even and <= 256 (got %d)", C);
+  const size_t elems = (size_t)B * H * W * C;
+  if (elems >= ((size_t)1 << 31)) return fail(RIB_ERR_UNSUPPORTED, "rib_cla_gate: B*H*W*C must be < 2^31");
+  if (!aligned(x, 4) || !aligned(g, 4) || !aligned(dw_w, 4) || !aligned(dw_b, 4) || !aligned(pw_w, 4) ||
+      !aligned(pw_b, 4))
+    return fail(RIB_ERR_INVALID_ARG, "rib_cla_gate: pointers must be 4-byte aligned");
+  const size_t es = dtype == RIB_F32 ? 4 : 2;
+  const size_t nmap = elems * es;
+  if (overlap(g, nmap, x, nmap) || overlap(g, nmap, dw_w, 36 * (size_t)C) || overlap(g, nmap, dw_b, 4 * (size_t)C) ||
+      overlap(g, nmap, pw_w, 4 * (size_t)C * C) || overlap(g, nmap, pw_b, 4 * (size_t)C))
+    return fail(RIB_ERR_INVALID_ARG, "rib_cla_gate: g must not overlap x or the weights");
+  rib::GateArgs a{x, dw_w, dw_b, pw_w, pw_b, g, B, H, W, C};
+  return hip_status(rib::launch_cla_gate(a, dtype == RIB_BF16, (hipStream_t)stream), "rib_cla_gate launch");
+}
 }  // extern "C"

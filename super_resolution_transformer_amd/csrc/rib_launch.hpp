@@ -25,4 +25,17 @@ hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 bool attn_bf16_supported(int dh, int R);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
 
+struct GateArgs {
+  const void* x;
+  const float* dw_w;
+  const float* dw_b;
+  const float* pw_w;
+  const float* pw_b;
+  void* g;
+  int B, H, W, C;
+};
+
+// CLA gate producer; bf16 = false: fp32 maps.  C even, C <= 256.
+hipError_t launch_cla_gate(const GateArgs& a, bool bf16, hipStream_t stream);
+
 }  // namespace rib

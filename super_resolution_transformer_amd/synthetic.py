@@ -126,3 +126,31 @@ def config_problem(idx: int, batch: int | None = None) -> Problem:
     c = CONFIGS[idx]
     return make_problem(c.B if batch is None else batch, c.H, c.W, c.heads, c.dh, c.R, c.L,
                         c.hidden, c.dtype, c.seed)
+
+
+@dataclass
+class GateProblem:
+    """Input map X [B,H,W,C] and the CLA gate producer's weights (float32)."""
+    x: np.ndarray                 # exact values (bf16-representable when dtype is bf16)
+    dw_w: np.ndarray              # [C, 3, 3]
+    dw_b: np.ndarray              # [C]
+    pw_w: np.ndarray              # [C_in, C_out]
+    pw_b: np.ndarray              # [C]
+    dtype: str
+    x_bits: np.ndarray | None = None
+
+
+def make_gate_problem(B: int, H: int, W: int, C: int, dtype: str = "bf16", seed: int = 0) -> GateProblem:
+    """X ~ N(0,1); depth-wise weights and bias ~ N(0, 1/9), point-wise ~ N(0, 1/C) (fan-in)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, H, W, C), dtype=np.float32)
+    dw_w = (rng.standard_normal((C, 3, 3)) / 3.0).astype(np.float32)
+    dw_b = (rng.standard_normal(C) / 3.0).astype(np.float32)
+    pw_w = (rng.standard_normal((C, C)) / np.sqrt(C)).astype(np.float32)
+    pw_b = (rng.standard_normal(C) / np.sqrt(C)).astype(np.float32)
+    bits = None
+    if dtype == "bf16":
+        bits, x = round_bf16(x)
+    elif dtype != "f32":
+        raise ValueError("dtype must be 'f32' or 'bf16'")
+    return GateProblem(x, dw_w, dw_b, pw_w, pw_b, dtype, bits)

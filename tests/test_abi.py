@@ -19,7 +19,8 @@ def L():
 
 def test_header_declares_the_boundary():
     assert set(rib.header_functions()) == {
-        "rib_encode", "rib_window_attn", "rib_attn_supported", "rib_last_error", "rib_abi_version"}
+        "rib_encode", "rib_window_attn", "rib_attn_supported", "rib_last_error", "rib_abi_version",
+        "rib_cla_gate"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -108,6 +109,27 @@ def test_encode_validation(L):
     assert L.rib_last_error().decode() != ""
 
 
+def gate(L, ptrs=None, B=1, H=8, W=8, C=180, dtype=rib.RIB_BF16, stream=None):
+    p = list(ptrs or P[:6])
+    return L.rib_cla_gate(*p, B, H, W, C, dtype, stream)
+
+
+@fake
+def test_gate_validation(L):
+    assert gate(L, [None] + P[1:6]) == rib.RIB_ERR_INVALID_ARG
+    assert gate(L, P[:5] + [None]) == rib.RIB_ERR_INVALID_ARG
+    assert gate(L, B=0) == rib.RIB_ERR_INVALID_ARG
+    assert gate(L, dtype=3) == rib.RIB_ERR_INVALID_ARG
+    assert gate(L, C=181) == rib.RIB_ERR_UNSUPPORTED
+    assert gate(L, C=258) == rib.RIB_ERR_UNSUPPORTED
+    assert gate(L, B=1 << 12, H=1 << 10, W=1 << 10, C=2) == rib.RIB_ERR_UNSUPPORTED
+    assert gate(L, [ctypes.c_void_p(P[0].value + 2)] + P[1:6]) == rib.RIB_ERR_INVALID_ARG
+    assert "aligned" in L.rib_last_error().decode()
+    assert gate(L, P[:5] + [ctypes.c_void_p(P[0].value + 64)]) == rib.RIB_ERR_INVALID_ARG  # g inside x
+    assert "overlap" in L.rib_last_error().decode()
+    assert gate(L, P[:5] + [P[3]]) == rib.RIB_ERR_INVALID_ARG                             # g == pw_w
+
+
 def test_python_binding_argument_checks():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 4, 4, 8)
@@ -117,3 +139,7 @@ def test_python_binding_argument_checks():
         rib.window_attn_into(x, x, x, x[:, :2], torch.zeros(16, 4), torch.zeros(16, 4), 2, 4, x)
     with pytest.raises(ValueError):
         rib.window_attn_into(x, x, x, x, torch.zeros(16, 4), torch.zeros(16, 4), 2, 4, x)  # CPU tensors
+    with pytest.raises(ValueError):
+        rib.cla_gate_into(x, torch.zeros(8, 3, 3), torch.zeros(8), torch.zeros(8, 8), torch.zeros(8), x)
+    with pytest.raises(ValueError):
+        rib.cla_gate_into(x, torch.zeros(8, 9), torch.zeros(8), torch.zeros(8, 8), torch.zeros(8), x)
