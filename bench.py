@@ -151,7 +151,7 @@ def time_gate(torch, rib, synthetic):
         xs = [x0] + [x0.clone() for _ in range(copies - 1)]
         gs = [torch.empty_like(x0) for _ in range(copies)]
         w = [torch.from_numpy(a).cuda() for a in (p.dw_w, p.dw_b, p.pw_w, p.pw_b)]
-        reps = max(30, 2 * copies)
+        reps = max(100, 2 * copies)
         for i in range(copies):
             rib.cla_gate_into(xs[i], *w, gs[i])
         torch.cuda.synchronize()
@@ -265,7 +265,7 @@ def main():
                                            2, 16, 40)):
             w2 = Workload(torch, rib, synthetic, cfg_idx, ws, copies=copies)
             w2.encode()
-            ms = time_attn_only(torch, w2, reps=max(20, 2 * copies), warmup=max(5, copies))
+            ms = time_attn_only(torch, w2, reps=max(100, 2 * copies), warmup=max(10, copies))
             tf = w2.F / (ms * 1e-3) / 1e12
             extra[name] = {"ms_attn": ms, "tokens_per_s": w2.tokens / (ms * 1e-3), "tflops": tf,
                            "pct_bf16_peak": 100 * tf / PEAK_BF16_TFLOPS,
