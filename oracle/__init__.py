@@ -60,6 +60,8 @@ def _configure(L):
     L.rib_oracle_encode.restype = ctypes.c_int
     L.rib_oracle_attn_units.argtypes = [_D] * 6 + [ctypes.c_int] * 7 + [ctypes.c_long] * 2 + [_D]
     L.rib_oracle_attn_units.restype = ctypes.c_int
+    L.rib_oracle_attn_units_heads.argtypes = [_D] * 6 + [ctypes.c_int] * 7 + [ctypes.c_long] * 2 + [_D]
+    L.rib_oracle_attn_units_heads.restype = ctypes.c_int
     L.rib_oracle_attn_rows.argtypes = [_D] * 6 + [ctypes.c_int] * 8 + [_I] * 3 + [_D]
     L.rib_oracle_attn_rows.restype = ctypes.c_int
     L.rib_oracle_window_debug.argtypes = ([_D] * 6 + [ctypes.c_int] * 11 + [_D] * 3 + [_I] * 3)
@@ -134,18 +136,23 @@ def units(B: int, H: int, W: int, heads: int, window: int) -> int:
 def window_attn(qc, kc, v, g, qp, kp, heads: int, window: int, unit_range=None) -> np.ndarray:
     """O = (softmax(Qc Kc^T/sqrt(dh) + Qp Kp^T/sqrt(R)) V) * sigmoid(G), NHWC float64.
 
-    ``unit_range=(begin, end)`` restricts the work to those (image, window,
-    head) units; outputs of the other units are left at zero.
+    ``qp``/``kp`` are one shared [window*window, R] pair, or per-head tables
+    [heads, window*window, R].  ``unit_range=(begin, end)`` restricts the work
+    to those (image, window, head) units; outputs of the other units are left
+    at zero.
     """
     qc, kc, v, g = (_f64(a) for a in (qc, kc, v, g))
     qp, kp = _f64(qp), _f64(kp)
     dh = qc.shape[-1] // heads
     B, H, W = _shape_args(qc, heads, dh)
     R = qp.shape[-1]
+    per_head = qp.ndim == 3
+    if per_head and (qp.shape[0] != heads or kp.shape != qp.shape):
+        raise ValueError("per-head tables must be [heads, window*window, R]")
     o = np.zeros(qc.shape, np.float64)
     ub, ue = (0, -1) if unit_range is None else unit_range
-    rc = lib().rib_oracle_attn_units(_p(qc), _p(kc), _p(v), _p(g), _p(qp), _p(kp), B, H, W, heads,
-                                     dh, R, window, ub, ue, _p(o))
+    fn = lib().rib_oracle_attn_units_heads if per_head else lib().rib_oracle_attn_units
+    rc = fn(_p(qc), _p(kc), _p(v), _p(g), _p(qp), _p(kp), B, H, W, heads, dh, R, window, ub, ue, _p(o))
     if rc != 0:
         raise ValueError("oracle attention rejected its arguments")
     return o

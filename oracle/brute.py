@@ -59,10 +59,12 @@ def encode(window: int, L: int, hidden: int, R: int, weights) -> tuple[list, lis
 
 
 def window_attn(qc, kc, v, g, qp, kp, heads: int, window: int) -> np.ndarray:
+    """qp/kp: one shared list of rows, or a list of per-head lists (tables[h][n][r])."""
     qc, kc, v, g = (np.asarray(a, dtype=np.float64) for a in (qc, kc, v, g))
     B, H, W, C = qc.shape
     dh = C // heads
-    R = len(qp[0])
+    per_head = np.asarray(qp).ndim == 3
+    R = np.asarray(qp).shape[-1]
     groups: dict[tuple, list] = {}
     for b in range(B):
         for y in range(H):
@@ -72,6 +74,8 @@ def window_attn(qc, kc, v, g, qp, kp, heads: int, window: int) -> np.ndarray:
     for (b, _, _), toks in groups.items():
         for h in range(heads):
             lo = h * dh
+            tq = qp[h] if per_head else qp
+            tk = kp[h] if per_head else kp
             for (yi, xi) in toks:
                 ni = (yi % window) * window + (xi % window)
                 scores = []
@@ -82,7 +86,7 @@ def window_attn(qc, kc, v, g, qp, kp, heads: int, window: int) -> np.ndarray:
                         content += qc[b, yi, xi, lo + d] * kc[b, yj, xj, lo + d]
                     bias = 0.0
                     for r in range(R):
-                        bias += qp[ni][r] * kp[nj][r]
+                        bias += tq[ni][r] * tk[nj][r]
                     scores.append(content / math.sqrt(dh) + bias / math.sqrt(R))
                 top = max(scores)
                 e = [math.exp(s - top) for s in scores]

@@ -121,6 +121,7 @@ int rib_oracle_encode(int ws, int L, int hidden, int R, const double* weights,
 typedef struct {
   const double *qc, *kc, *v, *g, *qp, *kp;
   int B, H, W, heads, dh, R, ws;
+  long tstride;  /* elements between the (Qp, Kp) tables of consecutive heads; 0 = one shared pair */
 } problem;
 
 static size_t elem(const problem* p, int b, int y, int x, int h, int d) {
@@ -158,13 +159,13 @@ static void attend_row(const problem* p, int b, int h, int i, int nt, const int*
   const double inv_sqrt_dh = 1.0 / sqrt((double)p->dh);
   const double inv_sqrt_r = 1.0 / sqrt((double)p->R);
   const double* q = p->qc + elem(p, b, ty[i], tx[i], h, 0);
-  const double* qpos = p->qp + (size_t)tn[i] * p->R;
+  const double* qpos = p->qp + (size_t)h * p->tstride + (size_t)tn[i] * p->R;
   for (int j = 0; j < nt; ++j) {
     const double* k = p->kc + elem(p, b, ty[j], tx[j], h, 0);
     double s = 0.0;
     for (int d = 0; d < p->dh; ++d) s += q[d] * k[d];
     Sc[j] = s * inv_sqrt_dh;
-    const double* kpos = p->kp + (size_t)tn[j] * p->R;
+    const double* kpos = p->kp + (size_t)h * p->tstride + (size_t)tn[j] * p->R;
     double bb = 0.0;
     for (int r = 0; r < p->R; ++r) bb += qpos[r] * kpos[r];
     Bm[j] = bb * inv_sqrt_r;
@@ -201,10 +202,10 @@ static int check_problem(const problem* p) {
  * [u_begin, u_end) and writes their outputs into o (full NHWC array; other
  * entries are left as they are).  u_end < 0 means all units.
  */
-int rib_oracle_attn_units(const double* qc, const double* kc, const double* v, const double* g,
-                          const double* qp, const double* kp, int B, int H, int W, int heads,
-                          int dh, int R, int ws, long u_begin, long u_end, double* o) {
-  problem p = {qc, kc, v, g, qp, kp, B, H, W, heads, dh, R, ws};
+static int attn_units(const double* qc, const double* kc, const double* v, const double* g,
+                      const double* qp, const double* kp, int B, int H, int W, int heads, int dh,
+                      int R, int ws, long tstride, long u_begin, long u_end, double* o) {
+  problem p = {qc, kc, v, g, qp, kp, B, H, W, heads, dh, R, ws, tstride};
   if (check_problem(&p) || !o) return -1;
   const int nWy = (H + ws - 1) / ws, nWx = (W + ws - 1) / ws;
   const long units = (long)B * nWy * nWx * heads;
@@ -245,6 +246,23 @@ int rib_oracle_attn_units(const double* qc, const double* kc, const double* v, c
   return fail ? -1 : 0;
 }
 
+int rib_oracle_attn_units(const double* qc, const double* kc, const double* v, const double* g,
+                          const double* qp, const double* kp, int B, int H, int W, int heads,
+                          int dh, int R, int ws, long u_begin, long u_end, double* o) {
+  return attn_units(qc, kc, v, g, qp, kp, B, H, W, heads, dh, R, ws, 0, u_begin, u_end, o);
+}
+
+/*
+ * Per-head positional tables (the alternative to one shared pair): head h
+ * uses Qp, Kp rows at qp + h*ws*ws*R, kp + h*ws*ws*R, i.e. tables laid out
+ * [heads][ws*ws][R].  Everything else as rib_oracle_attn_units.
+ */
+int rib_oracle_attn_units_heads(const double* qc, const double* kc, const double* v, const double* g,
+                                const double* qp, const double* kp, int B, int H, int W, int heads,
+                                int dh, int R, int ws, long u_begin, long u_end, double* o) {
+  return attn_units(qc, kc, v, g, qp, kp, B, H, W, heads, dh, R, ws, (long)ws * ws * R, u_begin, u_end, o);
+}
+
 int rib_oracle_attn(const double* qc, const double* kc, const double* v, const double* g,
                     const double* qp, const double* kp, int B, int H, int W, int heads, int dh,
                     int R, int ws, double* o) {
@@ -260,7 +278,7 @@ int rib_oracle_attn_rows(const double* qc, const double* kc, const double* v, co
                          const double* qp, const double* kp, int B, int H, int W, int heads,
                          int dh, int R, int ws, int nq, const int* qb, const int* qy,
                          const int* qx, double* out) {
-  problem p = {qc, kc, v, g, qp, kp, B, H, W, heads, dh, R, ws};
+  problem p = {qc, kc, v, g, qp, kp, B, H, W, heads, dh, R, ws, 0};
   if (check_problem(&p) || nq < 0 || (nq > 0 && (!qb || !qy || !qx || !out))) return -1;
   for (int k = 0; k < nq; ++k)
     if (qb[k] < 0 || qb[k] >= B || qy[k] < 0 || qy[k] >= H || qx[k] < 0 || qx[k] >= W) return -1;
@@ -304,7 +322,7 @@ int rib_oracle_window_debug(const double* qc, const double* kc, const double* v,
                             const double* qp, const double* kp, int B, int H, int W, int heads,
                             int dh, int R, int ws, int b, int wy, int wx, int h, double* Sc,
                             double* Bm, double* P, int* ty, int* tx, int* tn) {
-  problem p = {qc, kc, v, g, qp, kp, B, H, W, heads, dh, R, ws};
+  problem p = {qc, kc, v, g, qp, kp, B, H, W, heads, dh, R, ws, 0};
   if (check_problem(&p) || b < 0 || b >= B || h < 0 || h >= heads) return -1;
   int nt = window_tokens(&p, wy, wx, ty, tx, tn);
   double* out = (double*)malloc(sizeof(double) * dh);

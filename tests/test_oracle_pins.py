@@ -379,6 +379,36 @@ def test_rows_entry_matches_full():
 
 # ---------------------------------------------------------------- mutations: the pins bite
 
+# ---------------------------------------------------------------- per-head positional tables
+def test_per_head_tables_match_brute_force():
+    """Tables [heads, N, R] (one pair per head): the C oracle against the pure-Python brute force."""
+    p = small_problem(B=2, H=5, W=7, heads=2, dh=3, R=4, seed=31)
+    ws = 4
+    rng = np.random.default_rng(32)
+    qp = rng.standard_normal((2, ws * ws, 4))
+    kp = rng.standard_normal((2, ws * ws, 4))
+    got = oracle.window_attn(p.qc, p.kc, p.v, p.g, qp, kp, 2, ws)
+    want = brute.window_attn(p.qc, p.kc, p.v, p.g, qp.tolist(), kp.tolist(), 2, ws)
+    assert np.abs(got - want).max() <= 1e-12
+
+
+def test_per_head_tables_reduce_to_shared_and_separate():
+    """Equal per-head tables give the shared-table result; each head of a per-head run equals a
+    shared-table run with that head's tables (head h reads table h, not another one)."""
+    p = small_problem(B=1, H=9, W=6, heads=3, dh=2, R=4, seed=33)
+    ws = 4
+    rng = np.random.default_rng(34)
+    q1, k1 = rng.standard_normal((ws * ws, 4)), rng.standard_normal((ws * ws, 4))
+    shared = oracle.window_attn(p.qc, p.kc, p.v, p.g, q1, k1, 3, ws)
+    same = oracle.window_attn(p.qc, p.kc, p.v, p.g, np.stack([q1] * 3), np.stack([k1] * 3), 3, ws)
+    assert np.array_equal(shared, same)
+    qh, kh = rng.standard_normal((3, ws * ws, 4)), rng.standard_normal((3, ws * ws, 4))
+    per = oracle.window_attn(p.qc, p.kc, p.v, p.g, qh, kh, 3, ws)
+    for h in range(3):
+        one = oracle.window_attn(p.qc, p.kc, p.v, p.g, qh[h], kh[h], 3, ws)
+        assert np.array_equal(per[..., 2 * h:2 * h + 2], one[..., 2 * h:2 * h + 2])
+
+
 # ---------------------------------------------------------------- CLA gate producer
 def gate_weights(C, seed):
     rng = np.random.default_rng(seed)
@@ -455,8 +485,8 @@ MUTATIONS = {
     "content scale 1/dh": ("1.0 / sqrt((double)p->dh)", "1.0 / (double)p->dh"),
     "gate sign": ("exp(-p->g[", "exp(p->g["),
     "gate missing": ("out[d] = a * gate;", "out[d] = a + 0.0 * gate;"),
-    "key positional index": ("const double* kpos = p->kp + (size_t)tn[j] * p->R;",
-                             "const double* kpos = p->kp + (size_t)tn[i] * p->R;"),
+    "key positional index": ("const double* kpos = p->kp + (size_t)h * p->tstride + (size_t)tn[j] * p->R;",
+                             "const double* kpos = p->kp + (size_t)h * p->tstride + (size_t)tn[i] * p->R;"),
     "sin/cos swapped": ("out[f++] = sin(freq * cy);", "out[f++] = cos(freq * cy);"),
     "frequency off by one": ("double freq = ldexp(1.0, i);", "double freq = ldexp(1.0, i + 1);"),
     "coordinate endpoints": ("float num = (float)(2 * k - (ws - 1));", "float num = (float)(2 * k - ws);"),
@@ -468,6 +498,7 @@ MUTATIONS = {
     "gate taps transposed": ("dw_w[(size_t)c * 9 + (dy + 1) * 3 + (dx + 1)]", "dw_w[(size_t)c * 9 + (dx + 1) * 3 + (dy + 1)]"),
     "gate depth-wise bias dropped": ("double acc = dw_b[c];", "double acc = 0.0 * dw_b[c];"),
     "gate point-wise bias dropped": ("double acc = pw_b[o];", "double acc = 0.0 * pw_b[o];"),
+    "per-head table of head 0": ("p->qp + (size_t)h * p->tstride", "p->qp + (size_t)0 * p->tstride"),
     "gate padding on the wrong side": ("if (yy < 0 || yy >= H || xs < 0 || xs >= W) continue;",
                                        "if (yy < 0 || yy >= H || xs < 0 || xs >= W || (dy == 1 && dx == 1 && y == 0)) continue;"),
 }
@@ -486,6 +517,7 @@ PINS = [
     lambda: test_one_hot_index_mapping_returns_v(4, 9, 6),
     test_large_scores_stay_finite,
     test_encoder_matches_brute,
+    test_per_head_tables_match_brute_force,
     lambda: test_cla_gate_matches_torch_conv2d(2, 5, 7, 6),
     test_cla_gate_identity_weights_return_x,
     test_cla_gate_constant_input_counts_taps,
