@@ -101,6 +101,19 @@ rib_status rib_window_attn(const void* qc, const void* kc, const void* v, const 
                            int heads, int dh, int R, int window, rib_dtype dtype, void* stream);
 
 /*
+ * rib_window_attn_heads -- rib_window_attn with one positional pair per head
+ * instead of one shared pair: qp and kp are float32 [heads][window*window][R]
+ * (for example, rib_encode run once per head with that head's weights).  The
+ * pages give Qp, Kp without a head index (explainer section 2.2 attention
+ * rewrite), which rib_window_attn reads as one shared pair; this entry point
+ * is the per-head alternative.  Everything else (layouts, dtypes, limits,
+ * errors) is as for rib_window_attn.
+ */
+rib_status rib_window_attn_heads(const void* qc, const void* kc, const void* v, const void* g,
+                                 const float* qp, const float* kp, void* o, int B, int H, int W,
+                                 int heads, int dh, int R, int window, rib_dtype dtype, void* stream);
+
+/*
  * rib_attn_supported -- RIB_OK if rib_window_attn has a compiled variant for
  * (dh, R, window, dtype), RIB_ERR_UNSUPPORTED if not, RIB_ERR_INVALID_ARG for
  * nonsensical values.  Launches nothing.
@@ -138,7 +151,7 @@ const char* rib_last_error(void);
 /* ABI version of this header (incremented on any incompatible change). */
 int rib_abi_version(void);
 
-#define RIB_ABI_VERSION 2
+#define RIB_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

@@ -51,6 +51,8 @@ def lib(path: str | None = None):
     L.rib_encode.restype = i
     L.rib_window_attn.argtypes = [vp] * 7 + [i] * 8 + [vp]
     L.rib_window_attn.restype = i
+    L.rib_window_attn_heads.argtypes = [vp] * 7 + [i] * 8 + [vp]
+    L.rib_window_attn_heads.restype = i
     L.rib_cla_gate.argtypes = [vp] * 6 + [i] * 5 + [vp]
     L.rib_cla_gate.restype = i
     L.rib_attn_supported.argtypes = [i, i, i, i]
@@ -137,16 +139,18 @@ def window_attn_into(qc, kc, v, g, qp, kp, heads: int, window: int, o) -> None:
         raise ValueError("qc, kc, v, g, o must share one dtype")
     if not all(t.is_cuda and t.is_contiguous() for t in ts + (qp, kp)):
         raise ValueError("all tensors must be contiguous GPU tensors")
-    if qp.dtype != torch.float32 or kp.dtype != torch.float32 or qp.shape != kp.shape or qp.dim() != 2:
-        raise ValueError("qp, kp must be float32 [window*window, R]")
-    if qp.shape[0] != window * window:
-        raise ValueError("qp, kp must have window*window rows")
+    if qp.dtype != torch.float32 or kp.dtype != torch.float32 or qp.shape != kp.shape or qp.dim() not in (2, 3):
+        raise ValueError("qp, kp must be float32 [window*window, R] or per-head [heads, window*window, R]")
+    per_head = qp.dim() == 3
+    if qp.shape[-2] != window * window or (per_head and qp.shape[0] != heads):
+        raise ValueError("qp, kp must have window*window rows (and one table per head)")
     B, H, W, C = qc.shape
     if heads < 1 or C % heads:
         raise ValueError("channel count must be a multiple of heads")
-    dh, R = C // heads, qp.shape[1]
-    _check(lib().rib_window_attn(_ptr(qc), _ptr(kc), _ptr(v), _ptr(g), _ptr(qp), _ptr(kp), _ptr(o),
-                                 B, H, W, heads, dh, R, window, _dtype_code(qc), _stream(qc)))
+    dh, R = C // heads, qp.shape[-1]
+    fn = lib().rib_window_attn_heads if per_head else lib().rib_window_attn
+    _check(fn(_ptr(qc), _ptr(kc), _ptr(v), _ptr(g), _ptr(qp), _ptr(kp), _ptr(o),
+              B, H, W, heads, dh, R, window, _dtype_code(qc), _stream(qc)))
 
 
 def cla_gate(x, dw_w, dw_b, pw_w, pw_b):

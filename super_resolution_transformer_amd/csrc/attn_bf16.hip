@@ -452,7 +452,8 @@ __global__ void __launch_bounds__(QB, 1)
 attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
                  const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                  const float* __restrict__ qp, const float* __restrict__ kp,
-                 uint32_t* __restrict__ o, int B, int H, int W, int heads, int ws, int total) {
+                 uint32_t* __restrict__ o, int B, int H, int W, int heads, int ws, int total,
+                 long tstride) {
   using S = Shape<DH, R>;
   __shared__ __attribute__((aligned(16))) uint32_t lds[S::LDS_DW];
 
@@ -476,6 +477,8 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
     q0 = qblk * QB;
     if (q0 >= G.n_real) return;
   }
+  qp += (long)G.h * tstride;  // per-head positional tables (tstride 0: one shared pair)
+  kp += (long)G.h * tstride;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int lane = tid & 63;
@@ -710,7 +713,8 @@ __global__ void __launch_bounds__(SQ, 2)
 attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
                        const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                        const float* __restrict__ qp, const float* __restrict__ kp,
-                       uint32_t* __restrict__ o, int B, int H, int W, int heads, int ws, int total) {
+                       uint32_t* __restrict__ o, int B, int H, int W, int heads, int ws, int total,
+                 long tstride) {
   using S = Shape<DH, R>;
   using RL = Roles<DH, R>;
   __shared__ __attribute__((aligned(16))) uint32_t lds[SNT * S::STAGE_DW];
@@ -730,6 +734,8 @@ attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
     G.n_real = min(ws, H - G.wy * ws) * G.nx;
     G.inv_nx = 1.0f / (float)G.nx;
   }
+  qp += (long)G.h * tstride;  // per-head positional tables (tstride 0: one shared pair)
+  kp += (long)G.h * tstride;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -861,7 +867,7 @@ hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((attn_bf16_small_kernel<DH, R>), dim3(grid), dim3(SQ), 0, stream,
                        (const uint32_t*)a.qc, (const uint32_t*)a.kc, (const uint32_t*)a.v,
                        (const uint32_t*)a.g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.H, a.W, a.heads, a.ws,
-                       total);
+                       total, a.tstride);
     return hipGetLastError();
   }
   const int qblocks = (a.ws * a.ws + QB - 1) / QB;
@@ -870,7 +876,7 @@ hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((attn_bf16_kernel<DH, R>), dim3(grid), dim3(QB), 0, stream,
                      (const uint32_t*)a.qc, (const uint32_t*)a.kc, (const uint32_t*)a.v,
                      (const uint32_t*)a.g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.H, a.W, a.heads, a.ws,
-                     total);
+                     total, a.tstride);
   return hipGetLastError();
 }
 

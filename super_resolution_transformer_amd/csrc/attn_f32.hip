@@ -30,7 +30,7 @@ __global__ void __launch_bounds__(F32_QB)
 attn_f32_kernel(const float* __restrict__ qc, const float* __restrict__ kc,
                 const float* __restrict__ v, const float* __restrict__ g,
                 const float* __restrict__ qp, const float* __restrict__ kp, float* __restrict__ o,
-                int B, int H, int W, int heads, int dh, int R, int ws, int total) {
+                int B, int H, int W, int heads, int dh, int R, int ws, int total, long tstride) {
   __shared__ float sk[F32_KT][DHM];
   __shared__ float sv[F32_KT][DHM];
   __shared__ float skp[F32_KT][RM];
@@ -45,6 +45,8 @@ attn_f32_kernel(const float* __restrict__ qc, const float* __restrict__ kc,
   const int wx = t % nWx; t /= nWx;
   const int wy = t % nWy;
   const int b = t / nWy;
+  qp += (long)h * tstride;  // per-head positional tables (tstride 0: one shared pair)
+  kp += (long)h * tstride;
   const int ny = min(ws, H - wy * ws), nx = min(ws, W - wx * ws);
   const int n_real = ny * nx;
   const int q0 = qblk * F32_QB;
@@ -138,7 +140,7 @@ hipError_t launch_f32(const AttnArgs& a, hipStream_t stream) {
   const int grid = 8 * ((total + 7) / 8);
   hipLaunchKernelGGL((attn_f32_kernel<DHM, RM>), dim3(grid), dim3(F32_QB), 0, stream,
                      (const float*)a.qc, (const float*)a.kc, (const float*)a.v, (const float*)a.g,
-                     a.qp, a.kp, (float*)a.o, a.B, a.H, a.W, a.heads, a.dh, a.R, a.ws, total);
+                     a.qp, a.kp, (float*)a.o, a.B, a.H, a.W, a.heads, a.dh, a.R, a.ws, total, a.tstride);
   return hipGetLastError();
 }
 

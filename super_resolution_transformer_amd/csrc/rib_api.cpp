@@ -84,33 +84,55 @@ rib_status rib_attn_supported(int dh, int R, int window, rib_dtype dtype) {
   return ok();
 }
 
-rib_status rib_window_attn(const void* qc, const void* kc, const void* v, const void* g,
-                           const float* qp, const float* kp, void* o, int B, int H, int W,
-                           int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+// shared by rib_window_attn (one (qp, kp) pair) and rib_window_attn_heads (a pair per head)
+rib_status window_attn(const char* fn, bool per_head, const void* qc, const void* kc, const void* v,
+                       const void* g, const float* qp, const float* kp, void* o, int B, int H, int W,
+                       int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
   if (!qc || !kc || !v || !g || !qp || !kp || !o)
-    return fail(RIB_ERR_INVALID_ARG, "rib_window_attn: null pointer");
+    return fail(RIB_ERR_INVALID_ARG, "%s: null pointer", fn);
   if (B < 1 || H < 1 || W < 1 || heads < 1 || dh < 1 || R < 1)
-    return fail(RIB_ERR_INVALID_ARG, "rib_window_attn: B, H, W, heads, dh, R must be >= 1");
-  if (window < 2) return fail(RIB_ERR_INVALID_ARG, "rib_window_attn: window must be >= 2 (got %d)", window);
+    return fail(RIB_ERR_INVALID_ARG, "%s: B, H, W, heads, dh, R must be >= 1", fn);
+  if (window < 2) return fail(RIB_ERR_INVALID_ARG, "%s: window must be >= 2 (got %d)", fn, window);
   if (dtype != RIB_F32 && dtype != RIB_BF16)
-    return fail(RIB_ERR_INVALID_ARG, "rib_window_attn: unknown dtype %d", (int)dtype);
+    return fail(RIB_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
   const rib_status sup = rib_attn_supported(dh, R, window, dtype);
   if (sup != RIB_OK) return sup;
   const uint64_t elems = (uint64_t)B * H * W * (uint64_t)heads * dh;
   if (elems >= (1ull << 31))
-    return fail(RIB_ERR_UNSUPPORTED, "rib_window_attn: B*H*W*heads*dh must be < 2^31");
+    return fail(RIB_ERR_UNSUPPORTED, "%s: B*H*W*heads*dh must be < 2^31", fn);
   if (!aligned(qc, 16) || !aligned(kc, 16) || !aligned(v, 16) || !aligned(g, 16) || !aligned(qp, 16) ||
       !aligned(kp, 16) || !aligned(o, 16))
-    return fail(RIB_ERR_INVALID_ARG, "rib_window_attn: pointers must be 16-byte aligned");
+    return fail(RIB_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
   const size_t nb = (size_t)elems * (dtype == RIB_F32 ? 4 : 2);
-  const size_t np = sizeof(float) * (size_t)window * window * R;
+  const size_t np = sizeof(float) * (size_t)window * window * R * (per_head ? heads : 1);
   if (overlap(o, nb, qc, nb) || overlap(o, nb, kc, nb) || overlap(o, nb, v, nb) || overlap(o, nb, g, nb) ||
       overlap(o, nb, qp, np) || overlap(o, nb, kp, np))
-    return fail(RIB_ERR_INVALID_ARG, "rib_window_attn: output overlaps an input");
-  const rib::AttnArgs a{qc, kc, v, g, qp, kp, o, B, H, W, heads, dh, R, window};
+    return fail(RIB_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
+  const long tstride = per_head ? (long)window * window * R : 0;
+  const rib::AttnArgs a{qc, kc, v, g, qp, kp, o, B, H, W, heads, dh, R, window, tstride};
   const hipError_t e = dtype == RIB_F32 ? rib::launch_attn_f32(a, (hipStream_t)stream)
                                         : rib::launch_attn_bf16(a, (hipStream_t)stream);
-  return hip_status(e, "rib_window_attn launch");
+  return hip_status(e, per_head ? "rib_window_attn_heads launch" : "rib_window_attn launch");
+}
+}  // namespace
+
+extern "C" {
+
+rib_status rib_window_attn(const void* qc, const void* kc, const void* v, const void* g,
+                           const float* qp, const float* kp, void* o, int B, int H, int W,
+                           int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
+  return window_attn("rib_window_attn", false, qc, kc, v, g, qp, kp, o, B, H, W, heads, dh, R, window,
+                     dtype, stream);
+}
+
+rib_status rib_window_attn_heads(const void* qc, const void* kc, const void* v, const void* g,
+                                 const float* qp, const float* kp, void* o, int B, int H, int W,
+                                 int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
+  return window_attn("rib_window_attn_heads", true, qc, kc, v, g, qp, kp, o, B, H, W, heads, dh, R,
+                     window, dtype, stream);
 }
 
 

@@ -13,6 +13,7 @@ struct AttnArgs {
   const float* kp;
   void* o;
   int B, H, W, heads, dh, R, ws;
+  long tstride;  // floats between the (qp, kp) tables of consecutive heads; 0 = one shared pair
 };
 
 hipError_t launch_encode(int ws, int L, int hidden, int R, const float* w, float* qp, float* kp,

@@ -20,7 +20,7 @@ def L():
 def test_header_declares_the_boundary():
     assert set(rib.header_functions()) == {
         "rib_encode", "rib_window_attn", "rib_attn_supported", "rib_last_error", "rib_abi_version",
-        "rib_cla_gate"}
+        "rib_cla_gate", "rib_window_attn_heads"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -92,6 +92,22 @@ def test_attn_validation(L):
     assert "overlap" in L.rib_last_error().decode()
     alias_qp = P[:6] + [P[4]]                                               # o == qp
     assert attn(L, alias_qp) == rib.RIB_ERR_INVALID_ARG
+
+
+@fake
+def test_attn_heads_validation(L):
+    def heads_call(ptrs, **kw):
+        a = dict(B=1, H=8, W=8, heads=2, dh=30, R=16, window=8, dtype=rib.RIB_BF16)
+        a.update(kw)
+        return L.rib_window_attn_heads(*ptrs, a["B"], a["H"], a["W"], a["heads"], a["dh"], a["R"], a["window"],
+                                       a["dtype"], None)
+    assert heads_call([None] + P[1:7]) == rib.RIB_ERR_INVALID_ARG
+    assert "rib_window_attn_heads" in L.rib_last_error().decode()
+    assert heads_call(P[:7], dh=31) == rib.RIB_ERR_UNSUPPORTED
+    # the per-head tables are heads times larger: o just past one table still overlaps the second
+    tail = P[:6] + [ctypes.c_void_p(P[4].value + 64 * 16 * 4 + 256)]
+    assert heads_call(tail) == rib.RIB_ERR_INVALID_ARG
+    assert "overlap" in L.rib_last_error().decode()
 
 
 @fake

@@ -260,3 +260,61 @@ def test_unsupported_shape_raises(torch):
     with pytest.raises(rib.RibError) as e:
         rib.window_attn(x, x, x, x, z, z, 2, 8)
     assert e.value.status == rib.RIB_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- per-head positional tables
+@pytest.mark.parametrize("B,H,W,heads,dh,R,ws,dtype", [
+    (1, 20, 30, 3, 16, 16, 8, "f32"),
+    (2, 37, 53, 3, 30, 16, 16, "bf16"),     # whole-window kernel
+    (1, 37, 53, 2, 30, 16, 32, "bf16"),     # tiled kernel
+    (1, 30, 31, 2, 16, 32, 16, "bf16"),
+    (1, 70, 61, 2, 30, 32, 64, "bf16"),
+])
+def test_per_head_tables_whole_output(torch, B, H, W, heads, dh, R, ws, dtype):
+    """rib_window_attn_heads: one (Qp, Kp) pair per head, each from rib_encode with its own weights."""
+    note(f"per-head tables B={B} H={H} W={W} heads={heads} dh={dh} R={R} ws={ws} {dtype}")
+    p = synthetic.make_problem(B, H, W, heads, dh, R, dtype=dtype, seed=H * 7 + W + ws)
+    (qc, kc, v, g), _ = to_dev(torch, p)
+    ws_h = [synthetic.draw_weights(np.random.default_rng(100 + h), p.L, p.hidden, R) for h in range(heads)]
+    tabs = [rib.encode(ws, p.L, p.hidden, R, torch.from_numpy(w).cuda()) for w in ws_h]
+    qp = torch.stack([t[0] for t in tabs]).contiguous()
+    kp = torch.stack([t[1] for t in tabs]).contiguous()
+    o = rib.window_attn(qc, kc, v, g, qp, kp, heads, ws)
+    torch.cuda.synchronize()
+    oq = np.stack([oracle.encode(ws, p.L, p.hidden, R, w)[0] for w in ws_h])
+    ok = np.stack([oracle.encode(ws, p.L, p.hidden, R, w)[1] for w in ws_h])
+    want = oracle.window_attn(p.qc, p.kc, p.v, p.g, oq, ok, heads, ws)
+    compare(o.float().cpu().numpy().astype(np.float64), want, dtype, "O")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ws,dh", [(4, 16), (4, 30)])
+def test_per_head_positional_permutation_is_bit_exact(torch, dtype, ws, dh):
+    """Qc = Kc = 0; head h's tables are Qp[n] = a e_n, Kp[m] = a e_{(m + h + 1) mod N}, so query n
+    of head h attends only to key m = (n - h - 1) mod N of its window: O == V moved by a per-head
+    in-window shift, bit for bit (also pins that head h reads table h)."""
+    B, H, W, heads, R = 2, 2 * ws, 3 * ws, 3, 16
+    N = ws * ws
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    rng = np.random.default_rng(2)
+    v = synthetic.round_bf16(rng.standard_normal((B, H, W, heads * dh)).astype(np.float32) + 3.0)[1]
+    vt = torch.from_numpy(v).cuda().to(tdt)
+    z = torch.zeros_like(vt)
+    g = torch.full_like(vt, 100.0)
+    qp = torch.zeros((heads, N, R), dtype=torch.float32, device="cuda")
+    kp = torch.zeros_like(qp)
+    for h in range(heads):
+        qp[h, torch.arange(N), torch.arange(N)] = 32.0
+        kp[h, torch.arange(N), (torch.arange(N) + h + 1) % N] = 32.0
+    o = rib.window_attn(z, z, vt, g, qp, kp, heads, ws).cpu()
+    want = torch.empty_like(o)
+    vc = vt.cpu()
+    for h in range(heads):
+        sl = slice(h * dh, (h + 1) * dh)
+        for y in range(H):
+            for x in range(W):
+                n = (y % ws) * ws + (x % ws)
+                m = (n - h - 1) % N
+                ky, kx = (y // ws) * ws + m // ws, (x // ws) * ws + m % ws
+                want[:, y, x, sl] = vc[:, ky, kx, sl]
+    assert torch.equal(o, want)
