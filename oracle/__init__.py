@@ -68,6 +68,10 @@ def _configure(L):
     L.rib_oracle_window_debug.restype = ctypes.c_int
     L.rib_oracle_cla_gate.argtypes = [_D] * 5 + [ctypes.c_int] * 4 + [_D]
     L.rib_oracle_cla_gate.restype = ctypes.c_int
+    L.rib_oracle_attn_backward.argtypes = [_D] * 7 + [ctypes.c_int] * 7 + [_D] * 6
+    L.rib_oracle_attn_backward.restype = ctypes.c_int
+    L.rib_oracle_encode_backward.argtypes = [ctypes.c_int] * 4 + [_D] * 4
+    L.rib_oracle_encode_backward.restype = ctypes.c_int
     return L
 
 
@@ -218,3 +222,34 @@ def cla_gate(x, dw_w, dw_b, pw_w, pw_b) -> np.ndarray:
     if lib().rib_oracle_cla_gate(_p(x), _p(dw_w), _p(dw_b), _p(pw_w), _p(pw_b), B, H, W, C, _p(g)) != 0:
         raise ValueError("oracle gate rejected its arguments")
     return g
+
+
+def window_attn_backward(qc, kc, v, g, qp, kp, dout, heads: int, window: int):
+    """Gradients (dqc, dkc, dv, dg, dqp, dkp) of O = (softmax(S) V) * sigmoid(G) for the
+    upstream gradient dout (NHWC float64; dqp/dkp [window*window, R], summed over all windows,
+    heads and images)."""
+    qc, kc, v, g, dout = (_f64(a) for a in (qc, kc, v, g, dout))
+    qp, kp = _f64(qp), _f64(kp)
+    dh = qc.shape[-1] // heads
+    B, H, W = _shape_args(qc, heads, dh)
+    R = qp.shape[-1]
+    outs = [np.zeros(qc.shape, np.float64) for _ in range(4)]
+    dqp = np.zeros(qp.shape, np.float64)
+    dkp = np.zeros(kp.shape, np.float64)
+    rc = lib().rib_oracle_attn_backward(_p(qc), _p(kc), _p(v), _p(g), _p(qp), _p(kp), _p(dout), B, H, W, heads,
+                                        dh, R, window, *[_p(a) for a in outs], _p(dqp), _p(dkp))
+    if rc != 0:
+        raise ValueError("oracle backward rejected its arguments")
+    return (*outs, dqp, dkp)
+
+
+def encode_backward(window: int, L: int, hidden: int, R: int, weights, dqp, dkp) -> np.ndarray:
+    """Gradient of the packed weights W_h | b_h | Wp_q | Wp_k for upstream dqp, dkp."""
+    w = _f64(weights).reshape(-1)
+    if w.size != weight_count(L, hidden, R):
+        raise ValueError("packed weight vector has the wrong length")
+    dqp, dkp = _f64(dqp), _f64(dkp)
+    dw = np.zeros_like(w)
+    if lib().rib_oracle_encode_backward(window, L, hidden, R, _p(w), _p(dqp), _p(dkp), _p(dw)) != 0:
+        raise ValueError("oracle encode backward rejected its arguments")
+    return dw

@@ -383,3 +383,205 @@ int rib_oracle_cla_gate(const double* x, const double* dw_w, const double* dw_b,
   }
   return fail ? -1 : 0;
 }
+
+/*
+ * Backward of RIB window attention with the gate (the training path the
+ * pages time: explainer section 4.1, training time per iteration; the
+ * forward as above).  Given dO, the gradient of a loss with respect to O,
+ * per (image, window, head) and real tokens i, j of the window:
+ *   s_ij  = qc_i.kc_j / sqrt(dh) + qp[n_i].kp[n_j] / sqrt(R),  P = softmax over j
+ *   A_i   = sum_j P_ij v_j,   sg_i = sigmoid(g_i),   O_i = A_i * sg_i
+ *   dA_i  = dO_i * sg_i
+ *   dg_i  = dO_i * A_i * sg_i * (1 - sg_i)
+ *   dP_ij = dA_i . v_j,   D_i = sum_j P_ij dP_ij,   dS_ij = P_ij (dP_ij - D_i)
+ *   dqc_i = sum_j dS_ij kc_j / sqrt(dh),   dkc_j = sum_i dS_ij qc_i / sqrt(dh)
+ *   dv_j  = sum_i P_ij dA_i
+ *   dqp[n] = sum over every (image, window, head, i) with n_i = n of sum_j dS_ij kp[n_j] / sqrt(R)
+ *   dkp[n] = sum over every (image, window, head, j) with n_j = n of sum_i dS_ij qp[n_i] / sqrt(R)
+ * Row by row: each row of P, dP and dS is built in full before it is used.
+ * dqp and dkp ([ws*ws][R]) are overwritten.
+ */
+static int attn_backward_unit(const problem* p, const double* dout, int b, int h, int nt, const int* ty,
+                              const int* tx, const int* tn, double* prow, double* dprow, double* akv,
+                              double* dkc_acc, double* dv_acc, double* dkp_acc, double* dqp_acc,
+                              double* dqc, double* dkc, double* dv, double* dg) {
+  const int dh = p->dh, R = p->R;
+  const double inv_sqrt_dh = 1.0 / sqrt((double)dh);
+  const double inv_sqrt_r = 1.0 / sqrt((double)R);
+  memset(dkc_acc, 0, sizeof(double) * (size_t)nt * dh);
+  memset(dv_acc, 0, sizeof(double) * (size_t)nt * dh);
+  for (int i = 0; i < nt; ++i) {
+    const double* q = p->qc + elem(p, b, ty[i], tx[i], h, 0);
+    const double* qpos = p->qp + (size_t)tn[i] * R;
+    /* P row */
+    double mx = -INFINITY;
+    for (int j = 0; j < nt; ++j) {
+      const double* k = p->kc + elem(p, b, ty[j], tx[j], h, 0);
+      const double* kpos = p->kp + (size_t)tn[j] * R;
+      double sc = 0.0, bb = 0.0;
+      for (int d = 0; d < dh; ++d) sc += q[d] * k[d];
+      for (int r = 0; r < R; ++r) bb += qpos[r] * kpos[r];
+      prow[j] = sc * inv_sqrt_dh + bb * inv_sqrt_r;
+      if (prow[j] > mx) mx = prow[j];
+    }
+    double sum = 0.0;
+    for (int j = 0; j < nt; ++j) {
+      prow[j] = exp(prow[j] - mx);
+      sum += prow[j];
+    }
+    for (int j = 0; j < nt; ++j) prow[j] /= sum;
+    /* A_i, gate, dA_i, dg_i */
+    double* dA = akv;  /* length dh */
+    for (int d = 0; d < dh; ++d) {
+      double a = 0.0;
+      for (int j = 0; j < nt; ++j) a += prow[j] * p->v[elem(p, b, ty[j], tx[j], h, d)];
+      const size_t e = elem(p, b, ty[i], tx[i], h, d);
+      const double sg = 1.0 / (1.0 + exp(-p->g[e]));
+      dA[d] = dout[e] * sg;
+      dg[e] = dout[e] * a * sg * (1.0 - sg);
+    }
+    /* dP row, D_i */
+    double D = 0.0;
+    for (int j = 0; j < nt; ++j) {
+      const double* vj = p->v + elem(p, b, ty[j], tx[j], h, 0);
+      double dp = 0.0;
+      for (int d = 0; d < dh; ++d) dp += dA[d] * vj[d];
+      dprow[j] = dp;
+      D += prow[j] * dp;
+    }
+    /* dS row and its contractions */
+    double* dqi = dqc + elem(p, b, ty[i], tx[i], h, 0);
+    for (int d = 0; d < dh; ++d) dqi[d] = 0.0;
+    for (int j = 0; j < nt; ++j) {
+      const double ds = prow[j] * (dprow[j] - D);
+      const double* k = p->kc + elem(p, b, ty[j], tx[j], h, 0);
+      const double* kpos = p->kp + (size_t)tn[j] * R;
+      for (int d = 0; d < dh; ++d) {
+        dqi[d] += ds * k[d] * inv_sqrt_dh;
+        dkc_acc[(size_t)j * dh + d] += ds * q[d] * inv_sqrt_dh;
+        dv_acc[(size_t)j * dh + d] += prow[j] * dA[d];
+      }
+      for (int r = 0; r < R; ++r) {
+        dqp_acc[(size_t)tn[i] * R + r] += ds * kpos[r] * inv_sqrt_r;
+        dkp_acc[(size_t)tn[j] * R + r] += ds * qpos[r] * inv_sqrt_r;
+      }
+    }
+  }
+  for (int j = 0; j < nt; ++j)
+    for (int d = 0; d < dh; ++d) {
+      dkc[elem(p, b, ty[j], tx[j], h, d)] = dkc_acc[(size_t)j * dh + d];
+      dv[elem(p, b, ty[j], tx[j], h, d)] = dv_acc[(size_t)j * dh + d];
+    }
+  return 0;
+}
+
+int rib_oracle_attn_backward(const double* qc, const double* kc, const double* v, const double* g,
+                             const double* qp, const double* kp, const double* dout, int B, int H, int W,
+                             int heads, int dh, int R, int ws, double* dqc, double* dkc, double* dv,
+                             double* dg, double* dqp, double* dkp) {
+  problem p = {qc, kc, v, g, qp, kp, B, H, W, heads, dh, R, ws, 0};
+  if (check_problem(&p) || !dout || !dqc || !dkc || !dv || !dg || !dqp || !dkp) return -1;
+  const int nWy = (H + ws - 1) / ws, nWx = (W + ws - 1) / ws;
+  const long units = (long)B * nWy * nWx * heads;
+  const size_t N = (size_t)ws * ws;
+  memset(dqp, 0, sizeof(double) * N * R);
+  memset(dkp, 0, sizeof(double) * N * R);
+  int fail = 0;
+#pragma omp parallel
+  {
+    const int cap = ws * ws;
+    int* ty = (int*)malloc(sizeof(int) * cap);
+    int* tx = (int*)malloc(sizeof(int) * cap);
+    int* tn = (int*)malloc(sizeof(int) * cap);
+    double* prow = (double*)malloc(sizeof(double) * cap);
+    double* dprow = (double*)malloc(sizeof(double) * cap);
+    double* akv = (double*)malloc(sizeof(double) * dh);
+    double* dkc_acc = (double*)malloc(sizeof(double) * (size_t)cap * dh);
+    double* dv_acc = (double*)malloc(sizeof(double) * (size_t)cap * dh);
+    double* dqp_t = (double*)calloc(N * R, sizeof(double));
+    double* dkp_t = (double*)calloc(N * R, sizeof(double));
+    if (!ty || !tx || !tn || !prow || !dprow || !akv || !dkc_acc || !dv_acc || !dqp_t || !dkp_t) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (long u = 0; u < units; ++u) {
+        int h = (int)(u % heads);
+        long t = u / heads;
+        int wx = (int)(t % nWx);
+        t /= nWx;
+        int wy = (int)(t % nWy);
+        int b = (int)(t / nWy);
+        int nt = window_tokens(&p, wy, wx, ty, tx, tn);
+        attn_backward_unit(&p, dout, b, h, nt, ty, tx, tn, prow, dprow, akv, dkc_acc, dv_acc, dkp_t, dqp_t,
+                           dqc, dkc, dv, dg);
+      }
+#pragma omp critical
+      {
+        for (size_t k = 0; k < N * (size_t)R; ++k) {
+          dqp[k] += dqp_t[k];
+          dkp[k] += dkp_t[k];
+        }
+      }
+    }
+    free(ty); free(tx); free(tn); free(prow); free(dprow); free(akv); free(dkc_acc); free(dv_acc);
+    free(dqp_t); free(dkp_t);
+  }
+  return fail ? -1 : 0;
+}
+
+/*
+ * Backward of the coordinate encoder (explainer section 2.2): given dQp, dKp
+ * ([ws*ws][R]), the gradient of the packed weights W_h | b_h | Wp_q | Wp_k:
+ *   pre = r W_h + b_h,  h = ReLU(pre),  Qp = h Wp_q,  Kp = h Wp_k
+ *   dWp_q = sum_n h_n (x) dQp_n,  dWp_k = sum_n h_n (x) dKp_n
+ *   dh_n = dQp_n Wp_q^T + dKp_n Wp_k^T,  dpre_n = dh_n * [pre_n > 0]
+ *   dW_h = sum_n r_n (x) dpre_n,  db_h = sum_n dpre_n
+ * (the derivative of ReLU at exactly 0 is taken as 0).  dweights is overwritten.
+ */
+int rib_oracle_encode_backward(int ws, int L, int hidden, int R, const double* weights, const double* dqp,
+                               const double* dkp, double* dweights) {
+  if (ws < 2 || L < 0 || hidden < 1 || R < 1) return -1;
+  const int F = 2 + 4 * L;
+  const double* Wh = weights;
+  const double* bh = Wh + (size_t)F * hidden;
+  const double* Wq = bh + hidden;
+  const double* Wk = Wq + (size_t)hidden * R;
+  double* dWh = dweights;
+  double* dbh = dWh + (size_t)F * hidden;
+  double* dWq = dbh + hidden;
+  double* dWk = dWq + (size_t)hidden * R;
+  memset(dweights, 0, sizeof(double) * ((size_t)F * hidden + hidden + 2 * (size_t)hidden * R));
+  double* feat = (double*)malloc(sizeof(double) * F);
+  double* pre = (double*)malloc(sizeof(double) * hidden);
+  if (!feat || !pre) {
+    free(feat); free(pre);
+    return -1;
+  }
+  for (int n = 0; n < ws * ws; ++n) {
+    const int iy = n / ws, ix = n % ws;
+    fourier_features(coord_value(iy, ws), coord_value(ix, ws), L, feat);
+    for (int j = 0; j < hidden; ++j) {
+      double acc = bh[j];
+      for (int f = 0; f < F; ++f) acc += feat[f] * Wh[(size_t)f * hidden + j];
+      pre[j] = acc;
+    }
+    const double* gq = dqp + (size_t)n * R;
+    const double* gk = dkp + (size_t)n * R;
+    for (int j = 0; j < hidden; ++j) {
+      const double hj = pre[j] > 0.0 ? pre[j] : 0.0;
+      double dhj = 0.0;
+      for (int r = 0; r < R; ++r) {
+        dWq[(size_t)j * R + r] += hj * gq[r];
+        dWk[(size_t)j * R + r] += hj * gk[r];
+        dhj += gq[r] * Wq[(size_t)j * R + r] + gk[r] * Wk[(size_t)j * R + r];
+      }
+      const double dpre = pre[j] > 0.0 ? dhj : 0.0;
+      dbh[j] += dpre;
+      for (int f = 0; f < F; ++f) dWh[(size_t)f * hidden + j] += feat[f] * dpre;
+    }
+  }
+  free(feat);
+  free(pre);
+  return 0;
+}
