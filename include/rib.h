@@ -29,6 +29,8 @@
 #ifndef RIB_H
 #define RIB_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -144,6 +146,58 @@ rib_status rib_cla_gate(const void* x, const float* dw_w, const float* dw_b, con
                         const float* pw_b, void* g, int B, int H, int W, int C, rib_dtype dtype,
                         void* stream);
 
+/*
+ * rib_window_attn_backward -- gradients of rib_window_attn for an upstream
+ * gradient dO: the backward half of the training iteration the explainer
+ * times (section 4.1), by the chain rule of the forward above (explainer
+ * sections 2.2 and 2.3).  With sg = sigmoid(G), A = softmax(S) V, O = A * sg:
+ *   dG = dO * O * (1 - sg)            dA = dO * sg
+ *   D_i = dO_i . O_i                  dS_ij = P_ij (dA_i . V_j - D_i)
+ *   dQc = dS Kc / sqrt(dh)            dKc = dS^T Qc / sqrt(dh)
+ *   dV  = P^T dA
+ *   dqp[n] = sum over images, windows, heads of the row of dS Kp / sqrt(R)
+ *            at in-window index n; dkp[n] likewise from dS^T Qp / sqrt(R).
+ * P is recomputed from the inputs (no forward statistics are needed); O is
+ * the forward's output, used only for D and dG.
+ *
+ * qc, kc, v, g, o, dout : device, [B][H][W][heads*dh] of `dtype` (read);
+ *                         o = rib_window_attn(qc, kc, v, g, qp, kp).
+ * qp, kp                : device, float32 [window*window][R] (one shared pair).
+ * dqc, dkc, dv, dg      : device, like qc (written).
+ * dqp, dkp              : device, float32 [window*window][R] (written, not
+ *                         accumulated into).
+ * workspace             : device, at least
+ *                         rib_window_attn_backward_workspace(...) bytes,
+ *                         16-byte aligned; the library keeps nothing in it
+ *                         between calls.
+ * dtype                 : RIB_F32 or RIB_BF16 (bf16 storage, fp32 arithmetic).
+ * Every output and the workspace must be disjoint from every other buffer.
+ * Limits : window <= 128, dh <= 64, R <= 64; B*H*W*heads*max(dh, R) < 2^31;
+ *          pointers 16-byte aligned.
+ */
+size_t rib_window_attn_backward_workspace(int B, int H, int W, int heads, int dh, int R, rib_dtype dtype);
+rib_status rib_window_attn_backward(const void* qc, const void* kc, const void* v, const void* g,
+                                    const float* qp, const float* kp, const void* o, const void* dout,
+                                    void* dqc, void* dkc, void* dv, void* dg, float* dqp, float* dkp,
+                                    void* workspace, size_t workspace_bytes, int B, int H, int W, int heads,
+                                    int dh, int R, int window, rib_dtype dtype, void* stream);
+
+/*
+ * rib_encode_backward -- gradient of the packed encoder weights (layout of
+ * rib_encode) for upstream dqp, dkp (explainer section 2.2, the coordinate
+ * encoder and the two rank heads; the ReLU derivative at 0 is 0):
+ *   dWp_q = sum_n h_n (x) dqp_n     dWp_k = sum_n h_n (x) dkp_n
+ *   dpre_n = (dqp_n Wp_q^T + dkp_n Wp_k^T) * [pre_n > 0]
+ *   dW_h = sum_n r_n (x) dpre_n     db_h = sum_n dpre_n
+ * weights, dqp, dkp : device float32 (read); dweights: device float32, same
+ * length as weights (written).  workspace: device, at least
+ * rib_encode_backward_workspace(...) bytes.  Limits as rib_encode.
+ */
+size_t rib_encode_backward_workspace(int window, int L, int hidden, int R);
+rib_status rib_encode_backward(int window, int L, int hidden, int R, const float* weights, const float* dqp,
+                               const float* dkp, float* dweights, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* Text describing the last non-OK status returned on this thread ("" if none).
  * The pointer stays valid until the next library call on the same thread. */
 const char* rib_last_error(void);
@@ -151,7 +205,7 @@ const char* rib_last_error(void);
 /* ABI version of this header (incremented on any incompatible change). */
 int rib_abi_version(void);
 
-#define RIB_ABI_VERSION 3
+#define RIB_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,8 @@ calls raise if the library is missing.
 
     qp, kp = encode(window, L, hidden, R, weights)          # once per window size
     o = window_attn(qc, kc, v, g, qp, kp, heads, window)    # per layer call
+    grads = window_attn_backward(qc, kc, v, g, qp, kp, o, dout, heads, window)
+    dweights = encode_backward(window, L, hidden, R, weights, grads[4], grads[5])
 
 Method: "Rank-Factorized Implicit Neural Bias: Scaling Super-Resolution
 Transformer with FlashAttention" (gist.science summaries, part A/B;
@@ -55,6 +57,15 @@ def lib(path: str | None = None):
     L.rib_window_attn_heads.restype = i
     L.rib_cla_gate.argtypes = [vp] * 6 + [i] * 5 + [vp]
     L.rib_cla_gate.restype = i
+    sz = ctypes.c_size_t
+    L.rib_window_attn_backward_workspace.argtypes = [i] * 7
+    L.rib_window_attn_backward_workspace.restype = sz
+    L.rib_window_attn_backward.argtypes = [vp] * 15 + [sz] + [i] * 8 + [vp]
+    L.rib_window_attn_backward.restype = i
+    L.rib_encode_backward_workspace.argtypes = [i] * 4
+    L.rib_encode_backward_workspace.restype = sz
+    L.rib_encode_backward.argtypes = [i] * 4 + [vp] * 5 + [sz, vp]
+    L.rib_encode_backward.restype = i
     L.rib_attn_supported.argtypes = [i, i, i, i]
     L.rib_attn_supported.restype = i
     L.rib_last_error.argtypes = []
@@ -175,6 +186,55 @@ def cla_gate_into(x, dw_w, dw_b, pw_w, pw_b, g) -> None:
         raise ValueError("all tensors must be contiguous GPU tensors")
     _check(lib().rib_cla_gate(_ptr(x), _ptr(dw_w), _ptr(dw_b), _ptr(pw_w), _ptr(pw_b), _ptr(g), B, H, W, C,
                               _dtype_code(x), _stream(x)))
+
+
+def window_attn_backward(qc, kc, v, g, qp, kp, o, dout, heads: int, window: int):
+    """Gradients (dqc, dkc, dv, dg, dqp, dkp) of window_attn for the upstream gradient dout.
+
+    o is window_attn's output for the same inputs; dqp, dkp are float32 [window*window, R],
+    summed over every image, window and head.  The workspace is a temporary torch buffer.
+    """
+    import torch
+    ts = (qc, kc, v, g, o, dout)
+    if any(t.dim() != 4 or t.shape != qc.shape or t.dtype != qc.dtype for t in ts):
+        raise ValueError("qc, kc, v, g, o, dout must all be [B, H, W, C] of one dtype")
+    if not all(t.is_cuda and t.is_contiguous() for t in ts + (qp, kp)):
+        raise ValueError("all tensors must be contiguous GPU tensors")
+    if qp.dtype != torch.float32 or kp.dtype != torch.float32 or qp.shape != kp.shape or qp.dim() != 2:
+        raise ValueError("qp, kp must be float32 [window*window, R]")
+    if qp.shape[0] != window * window:
+        raise ValueError("qp, kp must have window*window rows")
+    B, H, W, C = qc.shape
+    if heads < 1 or C % heads:
+        raise ValueError("channel count must be a multiple of heads")
+    dh, R = C // heads, qp.shape[1]
+    code = _dtype_code(qc)
+    outs = [torch.empty_like(qc) for _ in range(4)]
+    dqp, dkp = torch.empty_like(qp), torch.empty_like(kp)
+    nbytes = lib().rib_window_attn_backward_workspace(B, H, W, heads, dh, R, code)
+    work = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=qc.device)
+    _check(lib().rib_window_attn_backward(*[_ptr(t) for t in ts[:4]], _ptr(qp), _ptr(kp), _ptr(o), _ptr(dout),
+                                          *[_ptr(t) for t in outs], _ptr(dqp), _ptr(dkp), _ptr(work), nbytes,
+                                          B, H, W, heads, dh, R, window, code, _stream(qc)))
+    return (*outs, dqp, dkp)
+
+
+def encode_backward(window: int, L: int, hidden: int, R: int, weights, dqp, dkp):
+    """Gradient of the packed encoder weights for upstream (dqp, dkp); float32 like weights."""
+    import torch
+    ts = (weights, dqp, dkp)
+    if not all(t.is_cuda and t.is_contiguous() and t.dtype == torch.float32 for t in ts):
+        raise ValueError("weights, dqp, dkp must be contiguous float32 GPU tensors")
+    if weights.numel() != weight_count(L, hidden, R):
+        raise ValueError("packed weight vector has the wrong length")
+    if dqp.shape != (window * window, R) or dkp.shape != (window * window, R):
+        raise ValueError("dqp, dkp must be [window*window, R]")
+    dw = torch.empty_like(weights)
+    nbytes = lib().rib_encode_backward_workspace(window, L, hidden, R)
+    work = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=weights.device)
+    _check(lib().rib_encode_backward(window, L, hidden, R, _ptr(weights), _ptr(dqp), _ptr(dkp), _ptr(dw),
+                                     _ptr(work), nbytes, _stream(weights)))
+    return dw
 
 
 def supported(dh: int, R: int, window: int, dtype) -> bool:

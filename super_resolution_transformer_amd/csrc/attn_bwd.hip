@@ -1,0 +1,410 @@
+// attn_bwd.hip -- backward of RIB window attention with the CLA gate.
+//
+// Forward, per image, window and head ("Rank-Factorized Implicit Neural
+// Bias", omica.com.cn explainer sections 2.2 "attention rewrite" and 2.3;
+// gist.science summaries part A, the concatenation identity):
+//   s_ij = Qt_i . Kt_j,  Qt = [Qc/sqrt(dh), Qp/sqrt(R)],  Kt = [Kc, Kp]
+//   P = softmax_j(s),  A = P V,  O = A * sigmoid(G)
+// Given dO, the chain rule gives (sg = sigmoid(G)):
+//   dA = dO * sg,   dG = dO * A * sg * (1 - sg) = dO * O * (1 - sg)
+//   D_i = sum_j P_ij (dA_i . V_j) = dA_i . A_i = dO_i . O_i
+//   dS_ij = P_ij (dA_i . V_j - D_i)
+//   dQt = dS Kt  -> dQc = dQt_c / sqrt(dh),  dQp rows = dQt_p / sqrt(R)
+//   dKt = dS^T Qt -> dKc = dKt_c,            dKp rows = dKt_p
+//   dV  = P^T dA
+// and the shared positional tables collect dQp[n], dKp[n] from every window,
+// head and image at in-window index n.  The explainer times a training
+// iteration (section 4.1); this is the backward half of it.
+//
+// Passes (all on one stream):
+//   prep   per token and head: dA, D and dG from dO, O, G
+//   dq     query-major: recomputes the scores with an online softmax (no saved
+//          statistics needed), accumulates dQt, writes dQc, the per-row dQp and
+//          the row log-sum-exp
+//   dkv    key-major: P from the log-sum-exp, accumulates dV and dKt, writes
+//          dKc, dV and the per-row dKp
+//   reduce per (n, r): sums the per-row dQp / dKp over images, windows, heads
+// The dq and dkv kernels here keep one row per thread in fp32 registers and
+// stage the other side through LDS; they serve every (dh, R) and both storage
+// types.  The bf16 MFMA kernels in attn_bwd_bf16.hip replace them for the
+// head shapes they are compiled for.
+#include "rib_bwd.hpp"
+#include "rib_device.hpp"
+
+namespace rib {
+
+namespace {
+
+constexpr int BW_QB = 256;  // rows (threads) per workgroup
+constexpr int BW_KT = 64;   // rows of the other side per LDS tile
+
+template <typename T>
+__device__ __forceinline__ float ldf(const T* p, long i);
+template <>
+__device__ __forceinline__ float ldf<float>(const float* p, long i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ldf<uint16_t>(const uint16_t* p, long i) {
+  return __builtin_bit_cast(float, (uint32_t)p[i] << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ void stf(T* p, long i, float v);
+template <>
+__device__ __forceinline__ void stf<float>(float* p, long i, float v) { p[i] = v; }
+template <>
+__device__ __forceinline__ void stf<uint16_t>(uint16_t* p, long i, float v) {
+  p[i] = (uint16_t)(pack_bf16(v, 0.0f) & 0xFFFFu);
+}
+
+// prep: one thread per (token, head).
+template <typename T>
+__global__ void __launch_bounds__(256)
+bwd_prep_kernel(const T* __restrict__ dout, const T* __restrict__ o, const T* __restrict__ g,
+                T* __restrict__ da, T* __restrict__ dg, float* __restrict__ dsum, long rows, int heads, int dh) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows) return;
+  const long tok = idx / heads;
+  const int h = (int)(idx - tok * heads);
+  const long base = tok * (long)heads * dh + (long)h * dh;
+  float D = 0.0f;
+  for (int d = 0; d < dh; ++d) {
+    const float dov = ldf(dout, base + d), ov = ldf(o, base + d);
+    const float s = 1.0f / (1.0f + expf(-ldf(g, base + d)));
+    D = fmaf(dov, ov, D);
+    stf(da, base + d, dov * s);
+    stf(dg, base + d, dov * ov * (1.0f - s));
+  }
+  dsum[idx] = D;
+}
+
+// Decode of a workgroup's logical index into (b, wy, wx, h, row block) and the
+// real-token enumeration of a window: real index r -> (iy, ix) = (r / nx, r % nx).
+struct Unit {
+  int b, wy, wx, h, blk, nx, n_real;
+};
+
+__device__ __forceinline__ bool decode_unit(int logical, const BwdArgs& a, int rblocks, Unit& u) {
+  const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws;
+  int t = logical;
+  u.blk = t % rblocks; t /= rblocks;
+  u.h = t % a.heads; t /= a.heads;
+  u.wx = t % nWx; t /= nWx;
+  u.wy = t % nWy;
+  u.b = t / nWy;
+  const int ny = min(a.ws, a.H - u.wy * a.ws);
+  u.nx = min(a.ws, a.W - u.wx * a.ws);
+  u.n_real = ny * u.nx;
+  return u.blk * BW_QB < u.n_real;
+}
+
+// token index (b, y, x) and in-window index n of real token r of the unit
+__device__ __forceinline__ void locate(const Unit& u, const BwdArgs& a, int r, long& tok, int& n) {
+  const int iy = r / u.nx, ix = r - iy * u.nx;
+  tok = ((long)u.b * a.H + u.wy * a.ws + iy) * a.W + u.wx * a.ws + ix;
+  n = iy * a.ws + ix;
+}
+
+// dq pass: one thread per query row.
+template <typename T, int DHM, int RM>
+__global__ void __launch_bounds__(BW_QB)
+bwd_dq_kernel(BwdArgs a, int total) {
+  __shared__ float sk[BW_KT][DHM];
+  __shared__ float sv[BW_KT][DHM];
+  __shared__ float skp[BW_KT][RM];
+  const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
+  if (logical >= total) return;
+  const int rblocks = (a.ws * a.ws + BW_QB - 1) / BW_QB;
+  Unit u;
+  if (!decode_unit(logical, a, rblocks, u)) return;
+  const T* qc = (const T*)a.qc;
+  const T* kc = (const T*)a.kc;
+  const T* v = (const T*)a.v;
+  const T* da = (const T*)a.da;
+  const int dh = a.dh, R = a.R, C = a.heads * a.dh;
+  const float sc = 1.0f / sqrtf((float)dh), sp = 1.0f / sqrtf((float)R);
+
+  const int r = u.blk * BW_QB + (int)threadIdx.x;
+  const bool valid = r < u.n_real;
+  long qtok;
+  int qn;
+  locate(u, a, min(r, u.n_real - 1), qtok, qn);
+  const long qoff = qtok * C + (long)u.h * dh;
+  const long qrow = qtok * a.heads + u.h;
+  float q[DHM], qpos[RM], dav[DHM], accc[DHM], accp[RM];
+#pragma unroll
+  for (int d = 0; d < DHM; ++d) {
+    q[d] = d < dh ? ldf(qc, qoff + d) * sc : 0.0f;
+    dav[d] = d < dh ? ldf(da, qoff + d) : 0.0f;
+    accc[d] = 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < RM; ++k) {
+    qpos[k] = k < R ? a.qp[qn * R + k] * sp : 0.0f;
+    accp[k] = 0.0f;
+  }
+  const float D = a.dsum[qrow];
+
+  float m = -INFINITY, l = 0.0f;
+  for (int k0 = 0; k0 < u.n_real; k0 += BW_KT) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < BW_KT * DHM; idx += BW_QB) {
+      const int j = idx / DHM, d = idx % DHM;
+      float kv = 0.0f, vv = 0.0f;
+      if (k0 + j < u.n_real && d < dh) {
+        long tok;
+        int n;
+        locate(u, a, k0 + j, tok, n);
+        kv = ldf(kc, tok * C + (long)u.h * dh + d);
+        vv = ldf(v, tok * C + (long)u.h * dh + d);
+      }
+      sk[j][d] = kv;
+      sv[j][d] = vv;
+    }
+    for (int idx = threadIdx.x; idx < BW_KT * RM; idx += BW_QB) {
+      const int j = idx / RM, k = idx % RM;
+      float pv = 0.0f;
+      if (k0 + j < u.n_real && k < R) {
+        long tok;
+        int n;
+        locate(u, a, k0 + j, tok, n);
+        pv = a.kp[n * R + k];
+      }
+      skp[j][k] = pv;
+    }
+    __syncthreads();
+    const int kend = min(BW_KT, u.n_real - k0);
+    for (int j = 0; j < kend; ++j) {
+      float s = 0.0f, bias = 0.0f, dp = 0.0f;
+#pragma unroll
+      for (int d = 0; d < DHM; ++d) {
+        s = fmaf(q[d], sk[j][d], s);
+        dp = fmaf(dav[d], sv[j][d], dp);
+      }
+#pragma unroll
+      for (int k = 0; k < RM; ++k) bias = fmaf(qpos[k], skp[j][k], bias);
+      s += bias;
+      if (s > m) {
+        const float c = expf(m - s);
+        l *= c;
+#pragma unroll
+        for (int d = 0; d < DHM; ++d) accc[d] *= c;
+#pragma unroll
+        for (int k = 0; k < RM; ++k) accp[k] *= c;
+        m = s;
+      }
+      const float p = expf(s - m);
+      l += p;
+      const float ds = p * (dp - D);
+#pragma unroll
+      for (int d = 0; d < DHM; ++d) accc[d] = fmaf(ds, sk[j][d], accc[d]);
+#pragma unroll
+      for (int k = 0; k < RM; ++k) accp[k] = fmaf(ds, skp[j][k], accp[k]);
+    }
+  }
+  if (!valid) return;
+  const float il = 1.0f / l;
+  T* dqc = (T*)a.dqc;
+#pragma unroll
+  for (int d = 0; d < DHM; ++d)
+    if (d < dh) stf(dqc, qoff + d, accc[d] * il * sc);
+  float* qrows = a.qrows + (((long)u.h * a.B + u.b) * a.H * a.W + (qtok - (long)u.b * a.H * a.W)) * R;
+#pragma unroll
+  for (int k = 0; k < RM; ++k)
+    if (k < R) qrows[k] = accp[k] * il * sp;
+  a.lse[qrow] = m + logf(l);
+}
+
+// dkv pass: one thread per key row.
+template <typename T, int DHM, int RM>
+__global__ void __launch_bounds__(BW_QB)
+bwd_dkv_kernel(BwdArgs a, int total) {
+  __shared__ float sq[BW_KT][DHM];
+  __shared__ float sa[BW_KT][DHM];
+  __shared__ float sqp[BW_KT][RM];
+  __shared__ float slse[BW_KT];
+  __shared__ float sd[BW_KT];
+  const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
+  if (logical >= total) return;
+  const int rblocks = (a.ws * a.ws + BW_QB - 1) / BW_QB;
+  Unit u;
+  if (!decode_unit(logical, a, rblocks, u)) return;
+  const T* qc = (const T*)a.qc;
+  const T* kc = (const T*)a.kc;
+  const T* v = (const T*)a.v;
+  const T* da = (const T*)a.da;
+  const int dh = a.dh, R = a.R, C = a.heads * a.dh;
+  const float sc = 1.0f / sqrtf((float)dh), sp = 1.0f / sqrtf((float)R);
+
+  const int r = u.blk * BW_QB + (int)threadIdx.x;
+  const bool valid = r < u.n_real;
+  long ktok;
+  int kn;
+  locate(u, a, min(r, u.n_real - 1), ktok, kn);
+  const long koff = ktok * C + (long)u.h * dh;
+  float k[DHM], kpos[RM], vv[DHM], dk[DHM], dkp[RM], dv[DHM];
+#pragma unroll
+  for (int d = 0; d < DHM; ++d) {
+    k[d] = d < dh ? ldf(kc, koff + d) : 0.0f;
+    vv[d] = d < dh ? ldf(v, koff + d) : 0.0f;
+    dk[d] = 0.0f;
+    dv[d] = 0.0f;
+  }
+#pragma unroll
+  for (int x = 0; x < RM; ++x) {
+    kpos[x] = x < R ? a.kp[kn * R + x] : 0.0f;
+    dkp[x] = 0.0f;
+  }
+
+  for (int q0 = 0; q0 < u.n_real; q0 += BW_KT) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < BW_KT * DHM; idx += BW_QB) {
+      const int i = idx / DHM, d = idx % DHM;
+      float qv = 0.0f, av = 0.0f;
+      if (q0 + i < u.n_real && d < dh) {
+        long tok;
+        int n;
+        locate(u, a, q0 + i, tok, n);
+        qv = ldf(qc, tok * C + (long)u.h * dh + d) * sc;
+        av = ldf(da, tok * C + (long)u.h * dh + d);
+      }
+      sq[i][d] = qv;
+      sa[i][d] = av;
+    }
+    for (int idx = threadIdx.x; idx < BW_KT * RM; idx += BW_QB) {
+      const int i = idx / RM, x = idx % RM;
+      float pv = 0.0f;
+      if (q0 + i < u.n_real && x < R) {
+        long tok;
+        int n;
+        locate(u, a, q0 + i, tok, n);
+        pv = a.qp[n * R + x] * sp;
+      }
+      sqp[i][x] = pv;
+    }
+    for (int i = threadIdx.x; i < BW_KT; i += BW_QB) {
+      float lv = 0.0f, dv0 = 0.0f;
+      if (q0 + i < u.n_real) {
+        long tok;
+        int n;
+        locate(u, a, q0 + i, tok, n);
+        lv = a.lse[tok * a.heads + u.h];
+        dv0 = a.dsum[tok * a.heads + u.h];
+      }
+      slse[i] = lv;
+      sd[i] = dv0;
+    }
+    __syncthreads();
+    const int qend = min(BW_KT, u.n_real - q0);
+    for (int i = 0; i < qend; ++i) {
+      float s = 0.0f, bias = 0.0f, dp = 0.0f;
+#pragma unroll
+      for (int d = 0; d < DHM; ++d) {
+        s = fmaf(sq[i][d], k[d], s);
+        dp = fmaf(sa[i][d], vv[d], dp);
+      }
+#pragma unroll
+      for (int x = 0; x < RM; ++x) bias = fmaf(sqp[i][x], kpos[x], bias);
+      const float p = expf(s + bias - slse[i]);
+      const float ds = p * (dp - sd[i]);
+#pragma unroll
+      for (int d = 0; d < DHM; ++d) {
+        dv[d] = fmaf(p, sa[i][d], dv[d]);
+        dk[d] = fmaf(ds, sq[i][d], dk[d]);
+      }
+#pragma unroll
+      for (int x = 0; x < RM; ++x) dkp[x] = fmaf(ds, sqp[i][x], dkp[x]);
+    }
+  }
+  if (!valid) return;
+  T* dkc = (T*)a.dkc;
+  T* dvo = (T*)a.dv;
+#pragma unroll
+  for (int d = 0; d < DHM; ++d)
+    if (d < dh) {
+      stf(dkc, koff + d, dk[d]);
+      stf(dvo, koff + d, dv[d]);
+    }
+  float* krows = a.krows + (((long)u.h * a.B + u.b) * a.H * a.W + (ktok - (long)u.b * a.H * a.W)) * R;
+#pragma unroll
+  for (int x = 0; x < RM; ++x)
+    if (x < R) krows[x] = dkp[x];
+}
+
+// reduce: thread per (table, n, r); sums the per-row gradients of every real
+// token at in-window index n over heads, images and windows.
+__global__ void __launch_bounds__(256)
+bwd_table_reduce_kernel(BwdArgs a) {
+  const int N = a.ws * a.ws;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= 2 * N * a.R) return;
+  const int tab = idx / (N * a.R);
+  const int rem = idx - tab * N * a.R;
+  const int n = rem / a.R, r = rem - (rem / a.R) * a.R;
+  const int iy = n / a.ws, ix = n - (n / a.ws) * a.ws;
+  const float* rows = tab ? a.krows : a.qrows;
+  const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws;
+  float acc = 0.0f;
+  for (int hb = 0; hb < a.heads * a.B; ++hb)
+    for (int wy = 0; wy < nWy; ++wy) {
+      const int y = wy * a.ws + iy;
+      if (y >= a.H) break;
+      for (int wx = 0; wx < nWx; ++wx) {
+        const int x = wx * a.ws + ix;
+        if (x >= a.W) break;
+        acc += rows[(((long)hb * a.H + y) * a.W + x) * a.R + r];
+      }
+    }
+  (tab ? a.dkp : a.dqp)[n * a.R + r] = acc;
+}
+
+template <typename T, int DHM, int RM>
+hipError_t launch_rows(const BwdArgs& a, hipStream_t stream) {
+  const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws;
+  const int rblocks = (a.ws * a.ws + BW_QB - 1) / BW_QB;
+  const int total = a.B * nWy * nWx * a.heads * rblocks;
+  const int grid = 8 * ((total + 7) / 8);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, DHM, RM>), dim3(grid), dim3(BW_QB), 0, stream, a, total);
+  hipLaunchKernelGGL((bwd_dkv_kernel<T, DHM, RM>), dim3(grid), dim3(BW_QB), 0, stream, a, total);
+  return hipGetLastError();
+}
+
+template <typename T, int DHM>
+hipError_t launch_rows_r(const BwdArgs& a, hipStream_t stream) {
+  if (a.R <= 16) return launch_rows<T, DHM, 16>(a, stream);
+  if (a.R <= 32) return launch_rows<T, DHM, 32>(a, stream);
+  return launch_rows<T, DHM, 64>(a, stream);
+}
+
+template <typename T>
+hipError_t launch_rows_dh(const BwdArgs& a, hipStream_t stream) {
+  if (a.dh <= 16) return launch_rows_r<T, 16>(a, stream);
+  if (a.dh <= 32) return launch_rows_r<T, 32>(a, stream);
+  return launch_rows_r<T, 64>(a, stream);
+}
+
+template <typename T>
+hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
+  const long rows = (long)a.B * a.H * a.W * a.heads;
+  const int grid = (int)((rows + 255) / 256);
+  hipLaunchKernelGGL((bwd_prep_kernel<T>), dim3(grid), dim3(256), 0, stream, (const T*)a.dout, (const T*)a.o,
+                     (const T*)a.g, (T*)a.da, (T*)a.dg, a.dsum, rows, a.heads, a.dh);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_prep(const BwdArgs& a, bool bf16, hipStream_t stream) {
+  return bf16 ? launch_prep<uint16_t>(a, stream) : launch_prep<float>(a, stream);
+}
+
+hipError_t launch_attn_bwd_rows(const BwdArgs& a, bool bf16, hipStream_t stream) {
+  return bf16 ? launch_rows_dh<uint16_t>(a, stream) : launch_rows_dh<float>(a, stream);
+}
+
+hipError_t launch_attn_bwd_reduce(const BwdArgs& a, hipStream_t stream) {
+  const int n = 2 * a.ws * a.ws * a.R;
+  hipLaunchKernelGGL(bwd_table_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace rib

@@ -11,6 +11,7 @@
 // and exact fp32 semantics (correctly rounded coordinate division, precise
 // sinf/cosf), not for speed.
 #include "rib_device.hpp"
+#include "rib_bwd.hpp"
 #include "rib_launch.hpp"
 
 namespace rib {
@@ -18,20 +19,13 @@ namespace rib {
 constexpr int ENC_TOK = 32;
 constexpr int ENC_THREADS = 256;
 
-__global__ void __launch_bounds__(ENC_THREADS)
-encode_kernel(int ws, int L, int hidden, int R, const float* __restrict__ w,
-              float* __restrict__ qp, float* __restrict__ kp) {
-  extern __shared__ float sm[];
-  const int F = 2 + 4 * L;
-  float* feat = sm;                     // [ENC_TOK][F]
-  float* hid = sm + ENC_TOK * F;        // [ENC_TOK][hidden]
-  const int N = ws * ws;
-  const int n0 = blockIdx.x * ENC_TOK;
+// Fourier features of TOK consecutive positions starting at n0 (clamped to N-1):
+// item (t, i) writes the raw coordinates (i == 0) or the sin/cos pair of
+// frequency 2^(i-1) for both axes.  Coordinates are the correctly rounded fp32
+// value of -1 + 2k/(ws-1).
+static __device__ void fourier_features(int n0, int N, int ws, int L, int TOK, int F, float* feat) {
   const float den = (float)(ws - 1);
-
-  // Fourier features: item (t, i) writes the raw coordinates (i == 0) or the
-  // sin/cos pair of frequency 2^(i-1) for both axes.
-  for (int item = threadIdx.x; item < ENC_TOK * (L + 1); item += ENC_THREADS) {
+  for (int item = threadIdx.x; item < TOK * (L + 1); item += blockDim.x) {
     const int t = item / (L + 1), i = item % (L + 1);
     const int n = min(n0 + t, N - 1);
     const int iy = n / ws, ix = n - (n / ws) * ws;
@@ -50,6 +44,19 @@ encode_kernel(int ws, int L, int hidden, int R, const float* __restrict__ w,
       g[3] = cosf(fr * cx);
     }
   }
+}
+
+__global__ void __launch_bounds__(ENC_THREADS)
+encode_kernel(int ws, int L, int hidden, int R, const float* __restrict__ w,
+              float* __restrict__ qp, float* __restrict__ kp) {
+  extern __shared__ float sm[];
+  const int F = 2 + 4 * L;
+  float* feat = sm;                     // [ENC_TOK][F]
+  float* hid = sm + ENC_TOK * F;        // [ENC_TOK][hidden]
+  const int N = ws * ws;
+  const int n0 = blockIdx.x * ENC_TOK;
+
+  fourier_features(n0, N, ws, L, ENC_TOK, F, feat);
   __syncthreads();
 
   // Hidden layer h = ReLU(r W_h + b_h).
@@ -88,6 +95,101 @@ hipError_t launch_encode(int ws, int L, int hidden, int R, const float* w, float
   const size_t lds = sizeof(float) * ENC_TOK * (size_t)(2 + 4 * L + hidden);
   hipLaunchKernelGGL(encode_kernel, dim3(blocks), dim3(ENC_THREADS), lds, stream, ws, L, hidden, R,
                      w, qp, kp);
+  return hipGetLastError();
+}
+
+// Backward of the encoder (explainer section 2.2, the same three layers): for
+// upstream dQp, dKp ([ws*ws][R]),
+//   dWp_q = sum_n h_n (x) dQp_n,   dWp_k = sum_n h_n (x) dKp_n
+//   dpre_n = (dQp_n Wp_q^T + dKp_n Wp_k^T) * [pre_n > 0]
+//   dW_h = sum_n r_n (x) dpre_n,   db_h = sum_n dpre_n
+// One workgroup handles EB_TOK positions and writes its partial gradient of
+// the whole packed weight vector; a second kernel sums the partials in block
+// order (deterministic, no atomics).  pre_n is recomputed with the forward's
+// exact arithmetic so the ReLU mask matches the forward's.
+constexpr int EB_TOK = 16;
+
+int encode_bwd_blocks(int ws) { return (ws * ws + EB_TOK - 1) / EB_TOK; }
+
+__global__ void __launch_bounds__(ENC_THREADS)
+encode_bwd_kernel(int ws, int L, int hidden, int R, const float* __restrict__ w, const float* __restrict__ dqp,
+                  const float* __restrict__ dkp, float* __restrict__ work) {
+  extern __shared__ float sm[];
+  const int F = 2 + 4 * L;
+  float* feat = sm;                        // [EB_TOK][F]
+  float* hid = feat + EB_TOK * F;          // [EB_TOK][hidden]  ReLU output
+  float* dpre = hid + EB_TOK * hidden;     // [EB_TOK][hidden]
+  float* gq = dpre + EB_TOK * hidden;      // [EB_TOK][R]
+  float* gk = gq + EB_TOK * R;             // [EB_TOK][R]
+  const int N = ws * ws;
+  const int n0 = blockIdx.x * EB_TOK;
+
+  fourier_features(n0, N, ws, L, EB_TOK, F, feat);
+  for (int item = threadIdx.x; item < EB_TOK * R; item += ENC_THREADS) {
+    const int t = item / R, r = item % R;
+    const bool in = n0 + t < N;
+    gq[item] = in ? dqp[(n0 + t) * R + r] : 0.0f;
+    gk[item] = in ? dkp[(n0 + t) * R + r] : 0.0f;
+  }
+  __syncthreads();
+
+  const float* Wh = w;
+  const float* bh = w + F * hidden;
+  const float* Wq = bh + hidden;
+  const float* Wk = Wq + hidden * R;
+  for (int item = threadIdx.x; item < EB_TOK * hidden; item += ENC_THREADS) {
+    const int t = item / hidden, j = item % hidden;
+    const float* f = feat + t * F;
+    float acc = bh[j];
+    for (int k = 0; k < F; ++k) acc = fmaf(f[k], Wh[k * hidden + j], acc);
+    float dh = 0.0f;
+    for (int r = 0; r < R; ++r) dh = fmaf(gq[t * R + r], Wq[j * R + r], fmaf(gk[t * R + r], Wk[j * R + r], dh));
+    hid[item] = fmaxf(acc, 0.0f);
+    dpre[item] = acc > 0.0f ? dh : 0.0f;
+  }
+  __syncthreads();
+
+  const int nw = F * hidden + hidden + 2 * hidden * R;
+  float* out = work + (long)blockIdx.x * nw;
+  for (int item = threadIdx.x; item < nw; item += ENC_THREADS) {
+    float acc = 0.0f;
+    if (item < F * hidden) {
+      const int f = item / hidden, j = item % hidden;
+      for (int t = 0; t < EB_TOK; ++t) acc = fmaf(feat[t * F + f], dpre[t * hidden + j], acc);
+    } else if (item < F * hidden + hidden) {
+      const int j = item - F * hidden;
+      for (int t = 0; t < EB_TOK; ++t) acc += dpre[t * hidden + j];
+    } else {
+      const int k = item - F * hidden - hidden;
+      const bool is_k = k >= hidden * R;
+      const int jr = is_k ? k - hidden * R : k;
+      const int j = jr / R, r = jr % R;
+      const float* gg = is_k ? gk : gq;
+      for (int t = 0; t < EB_TOK; ++t) acc = fmaf(hid[t * hidden + j], gg[t * R + r], acc);
+    }
+    out[item] = acc;
+  }
+}
+
+__global__ void __launch_bounds__(256)
+encode_bwd_reduce_kernel(int nw, int blocks, const float* __restrict__ work, float* __restrict__ dw) {
+  const int item = blockIdx.x * 256 + threadIdx.x;
+  if (item >= nw) return;
+  float acc = 0.0f;
+  for (int b = 0; b < blocks; ++b) acc += work[(long)b * nw + item];
+  dw[item] = acc;
+}
+
+hipError_t launch_encode_backward(int ws, int L, int hidden, int R, const float* w, const float* dqp,
+                                  const float* dkp, float* dw, float* work, hipStream_t stream) {
+  const int blocks = encode_bwd_blocks(ws);
+  const int F = 2 + 4 * L;
+  const int nw = F * hidden + hidden + 2 * hidden * R;
+  const size_t lds = sizeof(float) * EB_TOK * (size_t)(F + 2 * hidden + 2 * R);
+  hipLaunchKernelGGL(encode_bwd_kernel, dim3(blocks), dim3(ENC_THREADS), lds, stream, ws, L, hidden, R, w,
+                     dqp, dkp, work);
+  hipLaunchKernelGGL(encode_bwd_reduce_kernel, dim3((nw + 255) / 256), dim3(256), 0, stream, nw, blocks, work,
+                     dw);
   return hipGetLastError();
 }
 

@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "rib_bwd.hpp"
 #include "rib_launch.hpp"
 
 namespace {
@@ -158,4 +159,116 @@ rib_status rib_cla_gate(const void* x, const float* dw_w, const float* dw_b, con
   rib::GateArgs a{x, dw_w, dw_b, pw_w, pw_b, g, B, H, W, C};
   return hip_status(rib::launch_cla_gate(a, dtype == RIB_BF16, (hipStream_t)stream), "rib_cla_gate launch");
 }
+}  // extern "C"
+
+namespace {
+// Workspace of rib_window_attn_backward: dA (storage type), D, lse, then the
+// per-row dQp and dKp (fp32), each region 256-byte aligned.
+struct BwdLayout {
+  size_t da, dsum, lse, qrows, krows, total;
+};
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+BwdLayout bwd_layout(int B, int H, int W, int heads, int dh, int R, rib_dtype dtype) {
+  const size_t rows = (size_t)B * H * W * heads;
+  const size_t es = dtype == RIB_F32 ? 4 : 2;
+  BwdLayout l;
+  l.da = 0;
+  l.dsum = up256(rows * dh * es);
+  l.lse = l.dsum + up256(rows * 4);
+  l.qrows = l.lse + up256(rows * 4);
+  l.krows = l.qrows + up256(rows * R * 4);
+  l.total = l.krows + up256(rows * R * 4);
+  return l;
+}
+}  // namespace
+
+extern "C" {
+
+size_t rib_window_attn_backward_workspace(int B, int H, int W, int heads, int dh, int R, rib_dtype dtype) {
+  if (B < 1 || H < 1 || W < 1 || heads < 1 || dh < 1 || R < 1 || (dtype != RIB_F32 && dtype != RIB_BF16))
+    return 0;
+  return bwd_layout(B, H, W, heads, dh, R, dtype).total;
+}
+
+rib_status rib_window_attn_backward(const void* qc, const void* kc, const void* v, const void* g,
+                                    const float* qp, const float* kp, const void* o, const void* dout,
+                                    void* dqc, void* dkc, void* dv, void* dg, float* dqp, float* dkp,
+                                    void* workspace, size_t workspace_bytes, int B, int H, int W, int heads,
+                                    int dh, int R, int window, rib_dtype dtype, void* stream) {
+  const char* fn = "rib_window_attn_backward";
+  if (!qc || !kc || !v || !g || !qp || !kp || !o || !dout || !dqc || !dkc || !dv || !dg || !dqp || !dkp ||
+      !workspace)
+    return fail(RIB_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (B < 1 || H < 1 || W < 1 || heads < 1 || dh < 1 || R < 1)
+    return fail(RIB_ERR_INVALID_ARG, "%s: B, H, W, heads, dh, R must be >= 1", fn);
+  if (window < 2) return fail(RIB_ERR_INVALID_ARG, "%s: window must be >= 2 (got %d)", fn, window);
+  if (dtype != RIB_F32 && dtype != RIB_BF16) return fail(RIB_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (window > 128 || dh > 64 || R > 64)
+    return fail(RIB_ERR_UNSUPPORTED, "%s: limits are window <= 128, dh <= 64, R <= 64 (got %d, %d, %d)", fn,
+                window, dh, R);
+  const uint64_t elems = (uint64_t)B * H * W * (uint64_t)heads * dh;
+  if (elems >= (1ull << 31) || (uint64_t)B * H * W * heads * (uint64_t)R >= (1ull << 31))
+    return fail(RIB_ERR_UNSUPPORTED, "%s: B*H*W*heads*max(dh, R) must be < 2^31", fn);
+  const void* all[] = {qc, kc, v, g, qp, kp, o, dout, dqc, dkc, dv, dg, dqp, dkp, workspace};
+  for (const void* p : all)
+    if (!aligned(p, 16)) return fail(RIB_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+  const BwdLayout lay = bwd_layout(B, H, W, heads, dh, R, dtype);
+  if (workspace_bytes < lay.total)
+    return fail(RIB_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, lay.total);
+  const size_t nb = (size_t)elems * (dtype == RIB_F32 ? 4 : 2);
+  const size_t np = sizeof(float) * (size_t)window * window * R;
+  const size_t sizes[] = {nb, nb, nb, nb, np, np, nb, nb, nb, nb, nb, nb, np, np, lay.total};
+  // every output (indices 8..14, the workspace included) is disjoint from every other buffer
+  for (int i = 8; i < 15; ++i)
+    for (int j = 0; j < 15; ++j)
+      if (j != i && overlap(all[i], sizes[i], all[j], sizes[j]))
+        return fail(RIB_ERR_INVALID_ARG, "%s: an output or the workspace overlaps another buffer", fn);
+  char* w = (char*)workspace;
+  rib::BwdArgs a{qc, kc, v, g, qp, kp, o, dout, dqc, dkc, dv, dg, dqp, dkp,
+                 w + lay.da, (float*)(w + lay.dsum), (float*)(w + lay.lse), (float*)(w + lay.qrows),
+                 (float*)(w + lay.krows), B, H, W, heads, dh, R, window};
+  const hipStream_t st = (hipStream_t)stream;
+  const bool bf16 = dtype == RIB_BF16;
+  hipError_t e = rib::launch_attn_bwd_prep(a, bf16, st);
+  if (e == hipSuccess) e = rib::launch_attn_bwd_rows(a, bf16, st);
+  if (e == hipSuccess) e = rib::launch_attn_bwd_reduce(a, st);
+  return hip_status(e, "rib_window_attn_backward launch");
+}
+
+size_t rib_encode_backward_workspace(int window, int L, int hidden, int R) {
+  if (window < 2 || window > 128 || L < 0 || L > 16 || hidden < 1 || hidden > 256 || R < 1 || R > 64) return 0;
+  return sizeof(float) * (size_t)rib::encode_bwd_blocks(window) *
+         ((size_t)(2 + 4 * L) * hidden + hidden + 2 * (size_t)hidden * R);
+}
+
+rib_status rib_encode_backward(int window, int L, int hidden, int R, const float* weights, const float* dqp,
+                               const float* dkp, float* dweights, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  const char* fn = "rib_encode_backward";
+  if (!weights || !dqp || !dkp || !dweights || !workspace) return fail(RIB_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (window < 2) return fail(RIB_ERR_INVALID_ARG, "%s: window must be >= 2 (got %d)", fn, window);
+  if (L < 0 || hidden < 1 || R < 1)
+    return fail(RIB_ERR_INVALID_ARG, "%s: need L >= 0, hidden >= 1, R >= 1 (got %d, %d, %d)", fn, L, hidden, R);
+  if (window > 128 || L > 16 || hidden > 256 || R > 64)
+    return fail(RIB_ERR_UNSUPPORTED, "%s: limits are window <= 128, L <= 16, hidden <= 256, R <= 64", fn);
+  const void* all[] = {weights, dqp, dkp, dweights, workspace};
+  for (const void* p : all)
+    if (!aligned(p, 4)) return fail(RIB_ERR_INVALID_ARG, "%s: pointers must be 4-byte aligned", fn);
+  const size_t need = rib_encode_backward_workspace(window, L, hidden, R);
+  if (workspace_bytes < need)
+    return fail(RIB_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, need);
+  const size_t nw = sizeof(float) * ((size_t)(2 + 4 * L) * hidden + hidden + 2 * (size_t)hidden * R);
+  const size_t no = sizeof(float) * (size_t)window * window * R;
+  const size_t sizes[] = {nw, no, no, nw, need};
+  for (int i = 3; i < 5; ++i)
+    for (int j = 0; j < 5; ++j)
+      if (j != i && overlap(all[i], sizes[i], all[j], sizes[j]))
+        return fail(RIB_ERR_INVALID_ARG, "%s: dweights or the workspace overlaps another buffer", fn);
+  return hip_status(rib::launch_encode_backward(window, L, hidden, R, weights, dqp, dkp, dweights,
+                                                (float*)workspace, (hipStream_t)stream),
+                    "rib_encode_backward launch");
+}
+
 }  // extern "C"

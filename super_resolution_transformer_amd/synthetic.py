@@ -154,3 +154,13 @@ def make_gate_problem(B: int, H: int, W: int, C: int, dtype: str = "bf16", seed:
     elif dtype != "f32":
         raise ValueError("dtype must be 'f32' or 'bf16'")
     return GateProblem(x, dw_w, dw_b, pw_w, pw_b, dtype, bits)
+
+
+def make_upstream_grad(shape, dtype: str = "bf16", seed: int = 0) -> tuple[np.ndarray, np.ndarray | None]:
+    """Upstream gradient dO for the backward: N(0, 1) entries (scale is immaterial, the backward is
+    linear in dO).  Returns (exact float32 values, bf16 bits or None)."""
+    x = np.random.default_rng(seed).standard_normal(shape, dtype=np.float32)
+    if dtype == "bf16":
+        bits, x = round_bf16(x)
+        return x, bits
+    return x, None

@@ -20,7 +20,8 @@ def L():
 def test_header_declares_the_boundary():
     assert set(rib.header_functions()) == {
         "rib_encode", "rib_window_attn", "rib_attn_supported", "rib_last_error", "rib_abi_version",
-        "rib_cla_gate", "rib_window_attn_heads"}
+        "rib_cla_gate", "rib_window_attn_heads", "rib_window_attn_backward", "rib_window_attn_backward_workspace",
+        "rib_encode_backward", "rib_encode_backward_workspace"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -146,6 +147,63 @@ def test_gate_validation(L):
     assert gate(L, P[:5] + [P[3]]) == rib.RIB_ERR_INVALID_ARG                             # g == pw_w
 
 
+PB = [ctypes.c_void_p(0x10000000 + i * 64 * MB) for i in range(15)]
+
+
+def bwd(L, ptrs=None, nbytes=None, B=1, H=8, W=8, heads=2, dh=30, R=16, window=8, dtype=rib.RIB_BF16):
+    p = list(ptrs or PB)
+    if nbytes is None:
+        nbytes = L.rib_window_attn_backward_workspace(B, H, W, heads, dh, R, dtype)
+    return L.rib_window_attn_backward(*p, nbytes, B, H, W, heads, dh, R, window, dtype, None)
+
+
+@fake
+def test_backward_validation(L):
+    need = L.rib_window_attn_backward_workspace(1, 8, 8, 2, 30, 16, rib.RIB_BF16)
+    # dA (bf16) + D + lse + two per-row tables, each region 256-byte aligned
+    rows = 64 * 2
+    up = lambda x: (x + 255) // 256 * 256
+    assert need == up(rows * 30 * 2) + 2 * up(rows * 4) + 2 * up(rows * 16 * 4)
+    assert L.rib_window_attn_backward_workspace(0, 8, 8, 2, 30, 16, rib.RIB_BF16) == 0
+    assert bwd(L, [None] + PB[1:]) == rib.RIB_ERR_INVALID_ARG
+    assert "null" in L.rib_last_error().decode()
+    assert bwd(L, PB[:14] + [None]) == rib.RIB_ERR_INVALID_ARG
+    assert bwd(L, B=0) == rib.RIB_ERR_INVALID_ARG
+    assert bwd(L, window=1) == rib.RIB_ERR_INVALID_ARG
+    assert bwd(L, dtype=4) == rib.RIB_ERR_INVALID_ARG
+    assert bwd(L, dh=65) == rib.RIB_ERR_UNSUPPORTED
+    assert bwd(L, R=65) == rib.RIB_ERR_UNSUPPORTED
+    assert bwd(L, window=129) == rib.RIB_ERR_UNSUPPORTED
+    assert bwd(L, nbytes=need - 1) == rib.RIB_ERR_INVALID_ARG
+    assert "workspace" in L.rib_last_error().decode()
+    assert bwd(L, [ctypes.c_void_p(PB[0].value + 4)] + PB[1:]) == rib.RIB_ERR_INVALID_ARG
+    assert "aligned" in L.rib_last_error().decode()
+    alias = PB[:9] + [PB[2]] + PB[10:]                                    # dkc == v
+    assert bwd(L, alias) == rib.RIB_ERR_INVALID_ARG
+    assert "overlap" in L.rib_last_error().decode()
+    alias = PB[:14] + [ctypes.c_void_p(PB[8].value + 256)]                # workspace inside dqc
+    assert bwd(L, alias) == rib.RIB_ERR_INVALID_ARG
+    alias = PB[:12] + [PB[13], PB[13], PB[14]]                            # dqp == dkp
+    assert bwd(L, alias) == rib.RIB_ERR_INVALID_ARG
+    assert bwd(L, PB[:12] + [PB[4]] + PB[13:]) == rib.RIB_ERR_INVALID_ARG  # dqp == qp (an input)
+
+
+@fake
+def test_encode_backward_validation(L):
+    need = L.rib_encode_backward_workspace(16, 10, 64, 16)
+    nw = 42 * 64 + 64 + 2 * 64 * 16
+    assert need == 4 * nw * 16                                             # 256 positions / 16 per block
+    assert L.rib_encode_backward_workspace(1, 10, 64, 16) == 0
+    w, q, k, d, ws = PB[:5]
+    assert L.rib_encode_backward(16, 10, 64, 16, None, q, k, d, ws, need, None) == rib.RIB_ERR_INVALID_ARG
+    assert L.rib_encode_backward(1, 10, 64, 16, w, q, k, d, ws, need, None) == rib.RIB_ERR_INVALID_ARG
+    assert L.rib_encode_backward(16, 17, 64, 16, w, q, k, d, ws, need, None) == rib.RIB_ERR_UNSUPPORTED
+    assert L.rib_encode_backward(16, 10, 64, 16, w, q, k, d, ws, need - 4, None) == rib.RIB_ERR_INVALID_ARG
+    assert L.rib_encode_backward(16, 10, 64, 16, w, q, k, w, ws, need, None) == rib.RIB_ERR_INVALID_ARG
+    assert L.rib_encode_backward(16, 10, 64, 16, w, q, k, d, d, need, None) == rib.RIB_ERR_INVALID_ARG
+    assert "overlap" in L.rib_last_error().decode()
+
+
 def test_python_binding_argument_checks():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 4, 4, 8)
@@ -157,5 +215,11 @@ def test_python_binding_argument_checks():
         rib.window_attn_into(x, x, x, x, torch.zeros(16, 4), torch.zeros(16, 4), 2, 4, x)  # CPU tensors
     with pytest.raises(ValueError):
         rib.cla_gate_into(x, torch.zeros(8, 3, 3), torch.zeros(8), torch.zeros(8, 8), torch.zeros(8), x)
+    with pytest.raises(ValueError):
+        rib.window_attn_backward(x, x, x, x, torch.zeros(16, 4), torch.zeros(16, 4), x, x[:, :2], 2, 4)
+    with pytest.raises(ValueError):
+        rib.window_attn_backward(x, x, x, x, torch.zeros(16, 4), torch.zeros(16, 4), x, x, 2, 4)  # CPU tensors
+    with pytest.raises(ValueError):
+        rib.encode_backward(4, 10, 64, 16, torch.zeros(3), torch.zeros(16, 16), torch.zeros(16, 16))
     with pytest.raises(ValueError):
         rib.cla_gate_into(x, torch.zeros(8, 9), torch.zeros(8), torch.zeros(8, 8), torch.zeros(8), x)
