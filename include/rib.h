@@ -116,6 +116,20 @@ rib_status rib_window_attn_heads(const void* qc, const void* kc, const void* v, 
                                  int heads, int dh, int R, int window, rib_dtype dtype, void* stream);
 
 /*
+ * rib_window_attn_train -- rib_window_attn that also writes the row
+ * log-sum-exp the backward needs (the training iteration of explainer
+ * section 4.1: forward, then rib_window_attn_backward):
+ *   lse[b][y][x][h] = log sum_j exp(s_ij)   (natural log, over the real keys j
+ *                                           of the query's window, head h)
+ * lse : device, float32 [B][H][W][heads] (written); must not overlap any other
+ *       argument.  Every other argument, limit and error as rib_window_attn
+ *       (one shared (qp, kp) pair).
+ */
+rib_status rib_window_attn_train(const void* qc, const void* kc, const void* v, const void* g,
+                                 const float* qp, const float* kp, void* o, float* lse, int B, int H, int W,
+                                 int heads, int dh, int R, int window, rib_dtype dtype, void* stream);
+
+/*
  * rib_attn_supported -- RIB_OK if rib_window_attn has a compiled variant for
  * (dh, R, window, dtype), RIB_ERR_UNSUPPORTED if not, RIB_ERR_INVALID_ARG for
  * nonsensical values.  Launches nothing.
@@ -157,11 +171,13 @@ rib_status rib_cla_gate(const void* x, const float* dw_w, const float* dw_b, con
  *   dV  = P^T dA
  *   dqp[n] = sum over images, windows, heads of the row of dS Kp / sqrt(R)
  *            at in-window index n; dkp[n] likewise from dS^T Qp / sqrt(R).
- * P is recomputed from the inputs (no forward statistics are needed); O is
- * the forward's output, used only for D and dG.
+ * P = exp(S - lse) is recomputed from the inputs and the forward's row
+ * log-sum-exp; O is the forward's output, used only for D and dG.
  *
  * qc, kc, v, g, o, dout : device, [B][H][W][heads*dh] of `dtype` (read);
- *                         o = rib_window_attn(qc, kc, v, g, qp, kp).
+ *                         o and lse from rib_window_attn_train on the same
+ *                         inputs.
+ * lse                   : device, float32 [B][H][W][heads] (read).
  * qp, kp                : device, float32 [window*window][R] (one shared pair).
  * dqc, dkc, dv, dg      : device, like qc (written).
  * dqp, dkp              : device, float32 [window*window][R] (written, not
@@ -177,10 +193,10 @@ rib_status rib_cla_gate(const void* x, const float* dw_w, const float* dw_b, con
  */
 size_t rib_window_attn_backward_workspace(int B, int H, int W, int heads, int dh, int R, rib_dtype dtype);
 rib_status rib_window_attn_backward(const void* qc, const void* kc, const void* v, const void* g,
-                                    const float* qp, const float* kp, const void* o, const void* dout,
-                                    void* dqc, void* dkc, void* dv, void* dg, float* dqp, float* dkp,
-                                    void* workspace, size_t workspace_bytes, int B, int H, int W, int heads,
-                                    int dh, int R, int window, rib_dtype dtype, void* stream);
+                                    const float* qp, const float* kp, const void* o, const float* lse,
+                                    const void* dout, void* dqc, void* dkc, void* dv, void* dg, float* dqp,
+                                    float* dkp, void* workspace, size_t workspace_bytes, int B, int H, int W,
+                                    int heads, int dh, int R, int window, rib_dtype dtype, void* stream);
 
 /*
  * rib_encode_backward -- gradient of the packed encoder weights (layout of

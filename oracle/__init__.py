@@ -68,6 +68,8 @@ def _configure(L):
     L.rib_oracle_window_debug.restype = ctypes.c_int
     L.rib_oracle_cla_gate.argtypes = [_D] * 5 + [ctypes.c_int] * 4 + [_D]
     L.rib_oracle_cla_gate.restype = ctypes.c_int
+    L.rib_oracle_attn_lse.argtypes = [_D] * 4 + [ctypes.c_int] * 7 + [_D]
+    L.rib_oracle_attn_lse.restype = ctypes.c_int
     L.rib_oracle_attn_backward.argtypes = [_D] * 7 + [ctypes.c_int] * 7 + [_D] * 6
     L.rib_oracle_attn_backward.restype = ctypes.c_int
     L.rib_oracle_encode_backward.argtypes = [ctypes.c_int] * 4 + [_D] * 4
@@ -222,6 +224,18 @@ def cla_gate(x, dw_w, dw_b, pw_w, pw_b) -> np.ndarray:
     if lib().rib_oracle_cla_gate(_p(x), _p(dw_w), _p(dw_b), _p(pw_w), _p(pw_b), B, H, W, C, _p(g)) != 0:
         raise ValueError("oracle gate rejected its arguments")
     return g
+
+
+def window_lse(qc, kc, qp, kp, heads: int, window: int) -> np.ndarray:
+    """Row log-sum-exp of the scores, [B, H, W, heads] float64 (one shared positional pair)."""
+    qc, kc, qp, kp = _f64(qc), _f64(kc), _f64(qp), _f64(kp)
+    dh = qc.shape[-1] // heads
+    B, H, W = _shape_args(qc, heads, dh)
+    out = np.zeros((B, H, W, heads), np.float64)
+    if lib().rib_oracle_attn_lse(_p(qc), _p(kc), _p(qp), _p(kp), B, H, W, heads, dh, qp.shape[-1], window,
+                                 _p(out)) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out
 
 
 def window_attn_backward(qc, kc, v, g, qp, kp, dout, heads: int, window: int):

@@ -312,6 +312,65 @@ int rib_oracle_attn_rows(const double* qc, const double* kc, const double* v, co
 }
 
 /*
+ * Row log-sum-exp of the scores (the normaliser of the softmax above):
+ * lse[b][y][x][h] = log sum_j exp(Sc_ij + Bm_ij) over the real keys j of the
+ * token's window.  This is what a training forward keeps for the backward
+ * (explainer section 4.1 trains with the same attention).  One shared pair.
+ */
+int rib_oracle_attn_lse(const double* qc, const double* kc, const double* qp, const double* kp, int B, int H,
+                        int W, int heads, int dh, int R, int ws, double* lse) {
+  problem p = {qc, kc, qc, qc, qp, kp, B, H, W, heads, dh, R, ws, 0};
+  if (check_problem(&p) || !lse) return -1;
+  const int nWy = (H + ws - 1) / ws, nWx = (W + ws - 1) / ws;
+  const long units = (long)B * nWy * nWx * heads;
+  const double inv_sqrt_dh = 1.0 / sqrt((double)dh);
+  const double inv_sqrt_r = 1.0 / sqrt((double)R);
+  int fail = 0;
+#pragma omp parallel
+  {
+    const int cap = ws * ws;
+    int* ty = (int*)malloc(sizeof(int) * cap);
+    int* tx = (int*)malloc(sizeof(int) * cap);
+    int* tn = (int*)malloc(sizeof(int) * cap);
+    double* S = (double*)malloc(sizeof(double) * cap);
+    if (!ty || !tx || !tn || !S) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (long u = 0; u < units; ++u) {
+        int h = (int)(u % heads);
+        long t = u / heads;
+        int wx = (int)(t % nWx);
+        t /= nWx;
+        int wy = (int)(t % nWy);
+        int b = (int)(t / nWy);
+        int nt = window_tokens(&p, wy, wx, ty, tx, tn);
+        for (int i = 0; i < nt; ++i) {
+          const double* q = qc + elem(&p, b, ty[i], tx[i], h, 0);
+          const double* qpos = qp + (size_t)tn[i] * R;
+          double mx = -INFINITY;
+          for (int j = 0; j < nt; ++j) {
+            const double* k = kc + elem(&p, b, ty[j], tx[j], h, 0);
+            const double* kpos = kp + (size_t)tn[j] * R;
+            double sc = 0.0, bb = 0.0;
+            for (int d = 0; d < dh; ++d) sc += q[d] * k[d];
+            for (int r = 0; r < R; ++r) bb += qpos[r] * kpos[r];
+            S[j] = sc * inv_sqrt_dh + bb * inv_sqrt_r;
+            if (S[j] > mx) mx = S[j];
+          }
+          double sum = 0.0;
+          for (int j = 0; j < nt; ++j) sum += exp(S[j] - mx);
+          lse[(((size_t)b * H + ty[i]) * W + tx[i]) * heads + h] = mx + log(sum);
+        }
+      }
+    }
+    free(ty); free(tx); free(tn); free(S);
+  }
+  return fail ? -1 : 0;
+}
+
+/*
  * Debug view of one (image b, window (wy,wx), head h): the content score
  * matrix Sc, the explicit bias matrix Bm and the softmax P, each nt x nt
  * row-major over the window's real tokens in map scan order; token (y, x)

@@ -9,7 +9,8 @@ calls raise if the library is missing.
 
     qp, kp = encode(window, L, hidden, R, weights)          # once per window size
     o = window_attn(qc, kc, v, g, qp, kp, heads, window)    # per layer call
-    grads = window_attn_backward(qc, kc, v, g, qp, kp, o, dout, heads, window)
+    o, lse = window_attn_train(qc, kc, v, g, qp, kp, heads, window)   # training forward
+    grads = window_attn_backward(qc, kc, v, g, qp, kp, o, lse, dout, heads, window)
     dweights = encode_backward(window, L, hidden, R, weights, grads[4], grads[5])
 
 Method: "Rank-Factorized Implicit Neural Bias: Scaling Super-Resolution
@@ -60,7 +61,9 @@ def lib(path: str | None = None):
     sz = ctypes.c_size_t
     L.rib_window_attn_backward_workspace.argtypes = [i] * 7
     L.rib_window_attn_backward_workspace.restype = sz
-    L.rib_window_attn_backward.argtypes = [vp] * 15 + [sz] + [i] * 8 + [vp]
+    L.rib_window_attn_train.argtypes = [vp] * 8 + [i] * 8 + [vp]
+    L.rib_window_attn_train.restype = i
+    L.rib_window_attn_backward.argtypes = [vp] * 16 + [sz] + [i] * 8 + [vp]
     L.rib_window_attn_backward.restype = i
     L.rib_encode_backward_workspace.argtypes = [i] * 4
     L.rib_encode_backward_workspace.restype = sz
@@ -164,6 +167,30 @@ def window_attn_into(qc, kc, v, g, qp, kp, heads: int, window: int, o) -> None:
               B, H, W, heads, dh, R, window, _dtype_code(qc), _stream(qc)))
 
 
+def window_attn_train(qc, kc, v, g, qp, kp, heads: int, window: int):
+    """window_attn plus the row log-sum-exp the backward needs: returns (o, lse), lse float32
+    [B, H, W, heads] (natural log)."""
+    import torch
+    ts = (qc, kc, v, g)
+    if any(t.dim() != 4 or t.shape != qc.shape or t.dtype != qc.dtype for t in ts):
+        raise ValueError("qc, kc, v, g must all be [B, H, W, C] of one dtype")
+    if not all(t.is_cuda and t.is_contiguous() for t in ts + (qp, kp)):
+        raise ValueError("all tensors must be contiguous GPU tensors")
+    if qp.dtype != torch.float32 or kp.dtype != torch.float32 or qp.shape != kp.shape or qp.dim() != 2:
+        raise ValueError("qp, kp must be float32 [window*window, R]")
+    if qp.shape[0] != window * window:
+        raise ValueError("qp, kp must have window*window rows")
+    B, H, W, C = qc.shape
+    if heads < 1 or C % heads:
+        raise ValueError("channel count must be a multiple of heads")
+    o = torch.empty_like(qc)
+    lse = torch.empty((B, H, W, heads), dtype=torch.float32, device=qc.device)
+    _check(lib().rib_window_attn_train(_ptr(qc), _ptr(kc), _ptr(v), _ptr(g), _ptr(qp), _ptr(kp), _ptr(o), _ptr(lse),
+                                       B, H, W, heads, C // heads, qp.shape[1], window, _dtype_code(qc),
+                                       _stream(qc)))
+    return o, lse
+
+
 def cla_gate(x, dw_w, dw_b, pw_w, pw_b):
     """G = PWConv1x1(DWConv3x3(X)) (the CLA gating map) for an NHWC map x; returns a new tensor."""
     import torch
@@ -188,11 +215,12 @@ def cla_gate_into(x, dw_w, dw_b, pw_w, pw_b, g) -> None:
                               _dtype_code(x), _stream(x)))
 
 
-def window_attn_backward(qc, kc, v, g, qp, kp, o, dout, heads: int, window: int):
+def window_attn_backward(qc, kc, v, g, qp, kp, o, lse, dout, heads: int, window: int):
     """Gradients (dqc, dkc, dv, dg, dqp, dkp) of window_attn for the upstream gradient dout.
 
-    o is window_attn's output for the same inputs; dqp, dkp are float32 [window*window, R],
-    summed over every image, window and head.  The workspace is a temporary torch buffer.
+    (o, lse) come from window_attn_train on the same inputs; dqp, dkp are float32
+    [window*window, R], summed over every image, window and head.  The workspace is a
+    temporary torch buffer.
     """
     import torch
     ts = (qc, kc, v, g, o, dout)
@@ -207,13 +235,16 @@ def window_attn_backward(qc, kc, v, g, qp, kp, o, dout, heads: int, window: int)
     B, H, W, C = qc.shape
     if heads < 1 or C % heads:
         raise ValueError("channel count must be a multiple of heads")
+    if lse.shape != (B, H, W, heads) or lse.dtype != torch.float32 or not (lse.is_cuda and lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 GPU tensor [B, H, W, heads]")
     dh, R = C // heads, qp.shape[1]
     code = _dtype_code(qc)
     outs = [torch.empty_like(qc) for _ in range(4)]
     dqp, dkp = torch.empty_like(qp), torch.empty_like(kp)
     nbytes = lib().rib_window_attn_backward_workspace(B, H, W, heads, dh, R, code)
     work = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=qc.device)
-    _check(lib().rib_window_attn_backward(*[_ptr(t) for t in ts[:4]], _ptr(qp), _ptr(kp), _ptr(o), _ptr(dout),
+    _check(lib().rib_window_attn_backward(*[_ptr(t) for t in ts[:4]], _ptr(qp), _ptr(kp), _ptr(o), _ptr(lse),
+                                          _ptr(dout),
                                           *[_ptr(t) for t in outs], _ptr(dqp), _ptr(dkp), _ptr(work), nbytes,
                                           B, H, W, heads, dh, R, window, code, _stream(qc)))
     return (*outs, dqp, dkp)

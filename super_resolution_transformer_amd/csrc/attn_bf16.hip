@@ -64,6 +64,7 @@ constexpr int QB = QW * NWAVE;     // queries per workgroup
 constexpr int NSTAGE = 3;          // LDS stages of the key-tile pipeline
 constexpr float OFF = 7.0f;        // p = exp2(s - m_hat - OFF) <= 2^-OFF normally
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
 
 template <int DH, int R>
@@ -453,7 +454,7 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
                  const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                  const float* __restrict__ qp, const float* __restrict__ kp,
                  uint32_t* __restrict__ o, int B, int H, int W, int heads, int ws, int total,
-                 long tstride) {
+                 long tstride, float* __restrict__ lse) {
   using S = Shape<DH, R>;
   __shared__ __attribute__((aligned(16))) uint32_t lds[S::LDS_DW];
 
@@ -654,6 +655,7 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
     const float inv = 1.0f / lsum;
     int off, n;
     locate<DH>(G, r, off, n);
+    if (lse) lse[(off - G.h * DH) / G.C * heads + G.h] = (rg.mhat[qb] + OFF + __log2f(lsum)) * LN2;
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
@@ -714,7 +716,7 @@ attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
                        const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                        const float* __restrict__ qp, const float* __restrict__ kp,
                        uint32_t* __restrict__ o, int B, int H, int W, int heads, int ws, int total,
-                 long tstride) {
+                       long tstride, float* __restrict__ lse) {
   using S = Shape<DH, R>;
   using RL = Roles<DH, R>;
   __shared__ __attribute__((aligned(16))) uint32_t lds[SNT * S::STAGE_DW];
@@ -837,6 +839,7 @@ attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
     const float lsum = S::LG ? pr.hi : pr.lo;
     if (r >= G.n_real) continue;
     const float inv = 1.0f / lsum;
+    if (lse) lse[(offq[qb] - G.h * DH) / G.C * heads + G.h] = (rg.mhat[qb] + OFF + __log2f(lsum)) * LN2;
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
@@ -867,7 +870,7 @@ hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((attn_bf16_small_kernel<DH, R>), dim3(grid), dim3(SQ), 0, stream,
                        (const uint32_t*)a.qc, (const uint32_t*)a.kc, (const uint32_t*)a.v,
                        (const uint32_t*)a.g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.H, a.W, a.heads, a.ws,
-                       total, a.tstride);
+                       total, a.tstride, a.lse);
     return hipGetLastError();
   }
   const int qblocks = (a.ws * a.ws + QB - 1) / QB;
@@ -876,7 +879,7 @@ hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((attn_bf16_kernel<DH, R>), dim3(grid), dim3(QB), 0, stream,
                      (const uint32_t*)a.qc, (const uint32_t*)a.kc, (const uint32_t*)a.v,
                      (const uint32_t*)a.g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.H, a.W, a.heads, a.ws,
-                     total, a.tstride);
+                     total, a.tstride, a.lse);
   return hipGetLastError();
 }
 

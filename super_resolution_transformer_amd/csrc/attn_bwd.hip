@@ -18,11 +18,10 @@
 //
 // Passes (all on one stream):
 //   prep   per token and head: dA, D and dG from dO, O, G
-//   dq     query-major: recomputes the scores with an online softmax (no saved
-//          statistics needed), accumulates dQt, writes dQc, the per-row dQp and
-//          the row log-sum-exp
-//   dkv    key-major: P from the log-sum-exp, accumulates dV and dKt, writes
-//          dKc, dV and the per-row dKp
+//   dq     query-major: P = exp(s - lse) from the forward's row log-sum-exp,
+//          accumulates dQt, writes dQc and the per-row dQp
+//   dkv    key-major: the same P, accumulates dV and dKt, writes dKc, dV and
+//          the per-row dKp
 //   reduce per (n, r): sums the per-row dQp / dKp over images, windows, heads
 // The dq and dkv kernels here keep one row per thread in fp32 registers and
 // stage the other side through LDS; they serve every (dh, R) and both storage
@@ -77,34 +76,8 @@ bwd_prep_kernel(const T* __restrict__ dout, const T* __restrict__ o, const T* __
   dsum[idx] = D;
 }
 
-// Decode of a workgroup's logical index into (b, wy, wx, h, row block) and the
-// real-token enumeration of a window: real index r -> (iy, ix) = (r / nx, r % nx).
-struct Unit {
-  int b, wy, wx, h, blk, nx, n_real;
-};
-
-__device__ __forceinline__ bool decode_unit(int logical, const BwdArgs& a, int rblocks, Unit& u) {
-  const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws;
-  int t = logical;
-  u.blk = t % rblocks; t /= rblocks;
-  u.h = t % a.heads; t /= a.heads;
-  u.wx = t % nWx; t /= nWx;
-  u.wy = t % nWy;
-  u.b = t / nWy;
-  const int ny = min(a.ws, a.H - u.wy * a.ws);
-  u.nx = min(a.ws, a.W - u.wx * a.ws);
-  u.n_real = ny * u.nx;
-  return u.blk * BW_QB < u.n_real;
-}
-
-// token index (b, y, x) and in-window index n of real token r of the unit
-__device__ __forceinline__ void locate(const Unit& u, const BwdArgs& a, int r, long& tok, int& n) {
-  const int iy = r / u.nx, ix = r - iy * u.nx;
-  tok = ((long)u.b * a.H + u.wy * a.ws + iy) * a.W + u.wx * a.ws + ix;
-  n = iy * a.ws + ix;
-}
-
-// dq pass: one thread per query row.
+// dq pass: one thread per query row.  (Padded queries of the last row block
+// compute on a copy of the last real row and store nothing.)
 template <typename T, int DHM, int RM>
 __global__ void __launch_bounds__(BW_QB)
 bwd_dq_kernel(BwdArgs a, int total) {
@@ -113,9 +86,8 @@ bwd_dq_kernel(BwdArgs a, int total) {
   __shared__ float skp[BW_KT][RM];
   const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
   if (logical >= total) return;
-  const int rblocks = (a.ws * a.ws + BW_QB - 1) / BW_QB;
   Unit u;
-  if (!decode_unit(logical, a, rblocks, u)) return;
+  if (!decode_unit(logical, a, BW_QB, u)) return;
   const T* qc = (const T*)a.qc;
   const T* kc = (const T*)a.kc;
   const T* v = (const T*)a.v;
@@ -144,7 +116,7 @@ bwd_dq_kernel(BwdArgs a, int total) {
   }
   const float D = a.dsum[qrow];
 
-  float m = -INFINITY, l = 0.0f;
+  const float lrow = a.lse[qrow];
   for (int k0 = 0; k0 < u.n_real; k0 += BW_KT) {
     __syncthreads();
     for (int idx = threadIdx.x; idx < BW_KT * DHM; idx += BW_QB) {
@@ -182,18 +154,7 @@ bwd_dq_kernel(BwdArgs a, int total) {
       }
 #pragma unroll
       for (int k = 0; k < RM; ++k) bias = fmaf(qpos[k], skp[j][k], bias);
-      s += bias;
-      if (s > m) {
-        const float c = expf(m - s);
-        l *= c;
-#pragma unroll
-        for (int d = 0; d < DHM; ++d) accc[d] *= c;
-#pragma unroll
-        for (int k = 0; k < RM; ++k) accp[k] *= c;
-        m = s;
-      }
-      const float p = expf(s - m);
-      l += p;
+      const float p = expf(s + bias - lrow);
       const float ds = p * (dp - D);
 #pragma unroll
       for (int d = 0; d < DHM; ++d) accc[d] = fmaf(ds, sk[j][d], accc[d]);
@@ -202,16 +163,14 @@ bwd_dq_kernel(BwdArgs a, int total) {
     }
   }
   if (!valid) return;
-  const float il = 1.0f / l;
   T* dqc = (T*)a.dqc;
 #pragma unroll
   for (int d = 0; d < DHM; ++d)
-    if (d < dh) stf(dqc, qoff + d, accc[d] * il * sc);
+    if (d < dh) stf(dqc, qoff + d, accc[d] * sc);
   float* qrows = a.qrows + (((long)u.h * a.B + u.b) * a.H * a.W + (qtok - (long)u.b * a.H * a.W)) * R;
 #pragma unroll
   for (int k = 0; k < RM; ++k)
-    if (k < R) qrows[k] = accp[k] * il * sp;
-  a.lse[qrow] = m + logf(l);
+    if (k < R) qrows[k] = accp[k] * sp;
 }
 
 // dkv pass: one thread per key row.
@@ -225,9 +184,8 @@ bwd_dkv_kernel(BwdArgs a, int total) {
   __shared__ float sd[BW_KT];
   const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
   if (logical >= total) return;
-  const int rblocks = (a.ws * a.ws + BW_QB - 1) / BW_QB;
   Unit u;
-  if (!decode_unit(logical, a, rblocks, u)) return;
+  if (!decode_unit(logical, a, BW_QB, u)) return;
   const T* qc = (const T*)a.qc;
   const T* kc = (const T*)a.kc;
   const T* v = (const T*)a.v;
@@ -359,9 +317,7 @@ bwd_table_reduce_kernel(BwdArgs a) {
 
 template <typename T, int DHM, int RM>
 hipError_t launch_rows(const BwdArgs& a, hipStream_t stream) {
-  const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws;
-  const int rblocks = (a.ws * a.ws + BW_QB - 1) / BW_QB;
-  const int total = a.B * nWy * nWx * a.heads * rblocks;
+  const int total = bwd_units(a, BW_QB);
   const int grid = 8 * ((total + 7) / 8);
   hipLaunchKernelGGL((bwd_dq_kernel<T, DHM, RM>), dim3(grid), dim3(BW_QB), 0, stream, a, total);
   hipLaunchKernelGGL((bwd_dkv_kernel<T, DHM, RM>), dim3(grid), dim3(BW_QB), 0, stream, a, total);

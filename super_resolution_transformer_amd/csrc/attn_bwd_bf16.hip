@@ -1,0 +1,579 @@
+// attn_bwd_bf16.hip -- backward of RIB window attention on bf16 matrix cores
+// (gfx950, v_mfma_f32_32x32x16_bf16).
+//
+// The gradients of O = (softmax(S) V) * sigmoid(G), S = Qt Kt^T with the
+// augmented rows Qt = [Qp/sqrt(R), Qc/sqrt(dh)], Kt = [Kp, Kc] ("Rank-
+// Factorized Implicit Neural Bias", gist.science summaries part A, the
+// concatenation identity; omica.com.cn explainer sections 2.2, 2.3 and the
+// training iteration of 4.1), given dA = dO * sigmoid(G) and D = dO . O from
+// the prep pass and the forward's row log-sum-exp:
+//   P = exp(S - lse),  dS = P * (dA V^T - D)
+//   dQt = dS Kt,  dKt = dS^T Qt,  dV = P^T dA
+//
+// Both passes put every per-row constant into the contractions, so an
+// element of the score tile costs one exp2, one multiply and one convert:
+//  * the score rows carry log2(e) (base-2 softmax) and two extra columns: the
+//    query side holds -lse*log2(e) split into a bf16 high part and a bf16
+//    remainder, the key side holds (1, 1).  The MFMA returns t = s*log2(e) -
+//    lse*log2(e) and P = exp2(t);
+//  * the value rows V' = [V | 1 1 | 0] and gradient rows dA' = [dA | -D_hi
+//    -D_lo | 0] (the head dimension padded to 32 has the room) make the MFMA
+//    return dP - D directly.
+//  * padded rows (past the window's real tokens) are all zero on every side:
+//    their P is exp2(0) = 1 but their dP - D is 0 (padded keys, dq pass) or
+//    their dA' row is 0 (padded queries, dkv pass), so they add nothing; no
+//    masking instructions are needed.
+//
+// dq pass (query-major): a workgroup of 8 waves owns 512 queries of one
+// (image, window, head); each wave keeps the B operands of its 64 queries
+// (augmented query rows and dA' rows) in VGPRs and streams the window's keys
+// through LDS in tiles of 64.  S^T = Kt Qt^T and (dP - D)^T = V' dA'^T come
+// out with lane = query, 16 keys per lane; dS^T, rounded to bf16, is then the
+// B operand of dQt^T += Kt^T dS^T, whose A operand is read from the same LDS
+// rows with the transposing ds_read_b64_tr_b16 (the forward kernel's PV
+// trick).  dkv pass (key-major): the mirror image, lane = key: S = Qt Kt^T,
+// dP - D = dA' V'^T, then dV'^T += dA'^T P and dKt^T += Qt^T dS.
+//
+// LDS row layout (both passes): an operand row of 16*NH bf16 columns is cut
+// into 8-byte pieces of 4 columns; piece (row, ch) sits at 8-byte index
+//   ((row/4) * NH + ch/16) * 16 + (row%4) * 4 + (ch%16)/4.
+// Eight consecutive columns of one row are 16 contiguous bytes (the row read
+// of a score A operand), and every 16-lane group of a transposing read covers
+// one 128-byte block.
+#include "rib_bwd.hpp"
+#include "rib_device.hpp"
+
+namespace rib {
+
+namespace {
+
+constexpr int NWV = 8;         // waves per workgroup
+constexpr int RW = 64;         // own rows per wave (two 32-row MFMA blocks)
+constexpr int RB = NWV * RW;   // own rows per workgroup
+constexpr int TT = 64;         // streamed rows per LDS tile
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+template <int DH, int R>
+struct BS {
+  static_assert(DH % 2 == 0 && R % 2 == 0, "even head dim and rank");
+  static constexpr int C0 = R + DH;                  // first of the two constant columns
+  static constexpr int KC = (R + DH + 2 + 15) / 16;  // 16-column chunks of an augmented row
+  static constexpr int DC = (DH + 2 + 15) / 16;      // 16-column chunks of a value / gradient row
+  static constexpr int MT = (R + DH + 31) / 32;      // 32-column tiles of an augmented gradient
+  static constexpr int AP = 2 * KC;                  // 8-column pieces of an augmented row
+  static constexpr int NP = AP + 2 * DC;             // pieces staged per streamed row
+  static constexpr int A_DW = TT * KC * 8;           // dwords of the augmented tile
+  static constexpr int V_DW = TT * DC * 8;           // dwords of the value / gradient tile
+  static constexpr int ST_DW = A_DW + V_DW;
+  static_assert(DC == 2, "value rows are one 32-column tile");
+  static_assert(NP <= 2 * NWV, "at most two staging pieces per thread");
+};
+
+template <int NH>
+__device__ __forceinline__ int piece_dw(int row, int ch) {
+  return 2 * ((((row >> 2) * NH + (ch >> 4)) << 4) + ((row & 3) << 2) + ((ch & 15) >> 2));
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+__device__ __forceinline__ u32x2_t ds_read_tr16(const uint32_t* p) {
+  const s16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4_t*)(__attribute__((address_space(3))) void*)(const_cast<uint32_t*>(p)));
+  return __builtin_bit_cast(u32x2_t, r);
+}
+
+// A operand of X^T B for the 32 columns [c32, c32+32) of a tile in the piece
+// layout and its rows [kofs, kofs+16): lane (column, 8 rows) in the row order
+// of a 32x32 accumulator's registers (see the forward kernel's V^T reads).
+// tbase = dword index of the tile, lbase = piece_dw(row0, ch0) of this lane.
+template <int NH>
+__device__ __forceinline__ u32x4_t tr_operand(const uint32_t* lds, int tbase, int lbase, int kofs, int c32) {
+  const u32x2_t lo = ds_read_tr16(lds + tbase + lbase + piece_dw<NH>(kofs, c32));
+  const u32x2_t hi = ds_read_tr16(lds + tbase + lbase + piece_dw<NH>(kofs + 8, c32));
+  return (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
+}
+
+__device__ __forceinline__ int tr_lane_base_row(int lane) { return 4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2); }
+__device__ __forceinline__ int tr_lane_base_ch(int lane) { return 16 * ((lane >> 4) & 1) + 4 * (lane & 3); }
+
+__device__ __forceinline__ float f32(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+// ---- operand rows ------------------------------------------------------------
+// Raw loads of one 8-column piece (4 column pairs) of a row, converted later:
+// pair k of the piece sits in raw[2k] (and raw[2k+1] for fp32 sources).
+struct Raw {
+  uint32_t w[8];
+};
+
+// Sources of the four row kinds; `tok` = token index, `n` = in-window index.
+struct RowSrc {
+  const uint32_t* map;   // bf16 pairs of the NHWC map of the content part (dword index = element / 2)
+  const float* pos;      // positional table [ws*ws][R]
+  const uint32_t* val;   // bf16 pairs of the value / gradient map
+  const float* rowc;     // per (token, head) constant: lse (query rows) or D (gradient rows)
+};
+
+// augmented row [P | content | const pair | 0]: P = positional factor (fp32),
+// content = bf16 map slice.  kind 0: key row (const pair 1, 1);
+// kind 1: query row (P * sp, content * sc, const pair = -lse*log2e split).
+template <int DH, int R, int P, int KIND>
+__device__ __forceinline__ void load_aug(const RowSrc& s, long tok, int n, long cofs, long crow, Raw& raw) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int col = 8 * P + 2 * k;
+    if (col < R) {
+      const float2 f = *reinterpret_cast<const float2*>(s.pos + (long)n * R + col);
+      raw.w[2 * k] = __builtin_bit_cast(uint32_t, f.x);
+      raw.w[2 * k + 1] = __builtin_bit_cast(uint32_t, f.y);
+    } else if (col < R + DH) {
+      raw.w[2 * k] = s.map[(cofs + col - R) >> 1];
+    } else if (col == R + DH && KIND == 1) {
+      raw.w[2 * k] = __builtin_bit_cast(uint32_t, s.rowc[crow]);
+    }
+  }
+}
+
+// -x split into a bf16 high part and a bf16 remainder, packed (low half = high part)
+__device__ __forceinline__ uint32_t neg_split(float x) {
+  const float hi = round_bf16(x);
+  return pack_bf16(-hi, -(x - hi));
+}
+
+template <int DH, int R, int P, int KIND>
+__device__ __forceinline__ u32x4_t cvt_aug(const Raw& raw, bool real, float sp, float sc) {
+  uint32_t d[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int col = 8 * P + 2 * k;
+    uint32_t x = 0u;
+    if (col < R) {
+      x = KIND == 1 ? pack_bf16(f32(raw.w[2 * k]) * sp, f32(raw.w[2 * k + 1]) * sp)
+                    : pack_bf16(f32(raw.w[2 * k]), f32(raw.w[2 * k + 1]));
+    } else if (col < R + DH) {
+      x = KIND == 1 ? pack_bf16(bf16_lo(raw.w[2 * k]) * sc, bf16_hi(raw.w[2 * k]) * sc) : raw.w[2 * k];
+    } else if (col == R + DH) {
+      x = KIND == 1 ? neg_split(f32(raw.w[2 * k]) * LOG2E) : 0x3F803F80u;
+    }
+    d[k] = real ? x : 0u;
+  }
+  return (u32x4_t){d[0], d[1], d[2], d[3]};
+}
+
+// value-like row [x | const pair | 0] over 32 columns: kind 0: V with (1, 1);
+// kind 1: dA with (-D_hi, -D_lo).  P = piece 0..3.
+template <int DH, int P, int KIND>
+__device__ __forceinline__ void load_val(const RowSrc& s, long vofs, long crow, Raw& raw) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int col = 8 * P + 2 * k;
+    if (col < DH) raw.w[2 * k] = s.val[(vofs + col) >> 1];
+    else if (col == DH && KIND == 1) raw.w[2 * k] = __builtin_bit_cast(uint32_t, s.rowc[crow]);
+  }
+}
+
+template <int DH, int P, int KIND>
+__device__ __forceinline__ u32x4_t cvt_val(const Raw& raw, bool real) {
+  uint32_t d[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int col = 8 * P + 2 * k;
+    uint32_t x = 0u;
+    if (col < DH) x = raw.w[2 * k];
+    else if (col == DH) x = KIND == 1 ? neg_split(f32(raw.w[2 * k])) : 0x3F803F80u;
+    d[k] = real ? x : 0u;
+  }
+  return (u32x4_t){d[0], d[1], d[2], d[3]};
+}
+
+// Piece p of a streamed row (p < AP: augmented row, else value-like row).
+// KIND 0: key rows (dq pass streams keys), KIND 1: query rows (dkv pass).
+template <int DH, int R, int P, int KIND>
+__device__ __forceinline__ void load_piece(const RowSrc& aug, const RowSrc& val, long tok, int n, long cofs,
+                                           long crow, Raw& raw) {
+  using S = BS<DH, R>;
+  if constexpr (P < S::AP) load_aug<DH, R, P, KIND>(aug, tok, n, cofs, crow, raw);
+  else load_val<DH, P - S::AP, KIND>(val, cofs, crow, raw);
+}
+
+template <int DH, int R, int P, int KIND>
+__device__ __forceinline__ void store_piece(uint32_t* tile, int row, const Raw& raw, bool real, float sp, float sc) {
+  using S = BS<DH, R>;
+  if constexpr (P < S::AP) {
+    *reinterpret_cast<u32x4_t*>(tile + piece_dw<S::KC>(row, 8 * P)) = cvt_aug<DH, R, P, KIND>(raw, real, sp, sc);
+  } else {
+    *reinterpret_cast<u32x4_t*>(tile + S::A_DW + piece_dw<S::DC>(row, 8 * (P - S::AP))) =
+        cvt_val<DH, P - S::AP, KIND>(raw, real);
+  }
+}
+
+// B operands of one own row: the augmented row chunks (lane half hh holds
+// columns 16c + 8hh .. +7) and the value-like row chunks.
+template <int DH, int R, int KIND, int C = 0>
+__device__ __forceinline__ void own_aug(const RowSrc& aug, long tok, int n, long cofs, long crow, bool real, int hh,
+                                        float sp, float sc, u32x4_t* at) {
+  if constexpr (C < BS<DH, R>::KC) {
+    Raw r0 = {}, r1 = {};
+    load_aug<DH, R, 2 * C, KIND>(aug, tok, n, cofs, crow, r0);
+    load_aug<DH, R, 2 * C + 1, KIND>(aug, tok, n, cofs, crow, r1);
+    const u32x4_t x0 = cvt_aug<DH, R, 2 * C, KIND>(r0, real, sp, sc);
+    const u32x4_t x1 = cvt_aug<DH, R, 2 * C + 1, KIND>(r1, real, sp, sc);
+    at[C] = hh ? x1 : x0;
+    own_aug<DH, R, KIND, C + 1>(aug, tok, n, cofs, crow, real, hh, sp, sc, at);
+  }
+}
+
+template <int DH, int KIND, int C = 0>
+__device__ __forceinline__ void own_val(const RowSrc& val, long cofs, long crow, bool real, int hh, u32x4_t* vt) {
+  if constexpr (C < 2) {
+    Raw r0 = {}, r1 = {};
+    load_val<DH, 2 * C, KIND>(val, cofs, crow, r0);
+    load_val<DH, 2 * C + 1, KIND>(val, cofs, crow, r1);
+    const u32x4_t x0 = cvt_val<DH, 2 * C, KIND>(r0, real);
+    const u32x4_t x1 = cvt_val<DH, 2 * C + 1, KIND>(r1, real);
+    vt[C] = hh ? x1 : x0;
+    own_val<DH, KIND, C + 1>(val, cofs, crow, real, hh, vt);
+  }
+}
+
+template <int DH, int R, int KIND>
+__device__ __forceinline__ void own_row(const RowSrc& aug, const RowSrc& val, long tok, int n, long cofs, long crow,
+                                        bool real, int hh, float sp, float sc, u32x4_t (&at)[BS<DH, R>::KC],
+                                        u32x4_t (&vt)[2]) {
+  own_aug<DH, R, KIND>(aug, tok, n, cofs, crow, real, hh, sp, sc, at);
+  own_val<DH, KIND>(val, cofs, crow, real, hh, vt);
+}
+
+// Streams the other side of the unit through LDS: every thread stages pieces
+// `wave` and `wave + 8` of row `lane` of a tile.
+template <int DH, int R, int KIND>
+struct Stager {
+  using S = BS<DH, R>;
+  Raw raw[2];
+  bool real;
+  int wave, lane;
+
+  __device__ __forceinline__ void load(const BwdArgs& a, const Unit& u, const RowSrc& aug, const RowSrc& val,
+                                       int t) {
+    const int r = t * TT + lane;
+    real = r < u.n_real;
+    long tok;
+    int n;
+    locate(u, a, real ? r : 0, tok, n);
+    const long cofs = tok * (long)(a.heads * DH) + (long)u.h * DH;
+    const long crow = tok * a.heads + u.h;
+    load_all<0>(aug, val, tok, n, cofs, crow);
+  }
+
+  template <int P>
+  __device__ __forceinline__ void load_all(const RowSrc& aug, const RowSrc& val, long tok, int n, long cofs,
+                                           long crow) {
+    if constexpr (P < S::NP) {
+      if (P % NWV == wave) load_piece<DH, R, P, KIND>(aug, val, tok, n, cofs, crow, raw[P / NWV]);
+      load_all<P + 1>(aug, val, tok, n, cofs, crow);
+    }
+  }
+
+  template <int P = 0>
+  __device__ __forceinline__ void store(uint32_t* tile, float sp, float sc) {
+    if constexpr (P < S::NP) {
+      if (P % NWV == wave) store_piece<DH, R, P, KIND>(tile, lane, raw[P / NWV], real, sp, sc);
+      store<P + 1>(tile, sp, sc);
+    }
+  }
+};
+
+__device__ __forceinline__ f32x16_t mfma(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) z[e] = 0.0f;
+  return z;
+}
+
+// ---- dq pass -------------------------------------------------------------------
+template <int DH, int R>
+__global__ void __launch_bounds__(RB, 1)
+bwd_dq_bf16_kernel(BwdArgs a, int total) {
+  using S = BS<DH, R>;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[2 * S::ST_DW];
+  const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
+  if (logical >= total) return;
+  Unit u;
+  if (!decode_unit(logical, a, RB, u)) return;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int q0 = u.blk * RB;
+  const bool active = q0 + wave * RW < u.n_real;
+  const int C = a.heads * DH;
+  const float sp = LOG2E / sqrtf((float)R), sc = LOG2E / sqrtf((float)DH);
+
+  // query side (own rows): Qt with -lse, dA' with -D
+  const RowSrc qsrc{(const uint32_t*)a.qc, a.qp, nullptr, a.lse};
+  const RowSrc gsrc{nullptr, nullptr, (const uint32_t*)a.da, a.dsum};
+  // key side (streamed): Kt with (1, 1), V' with (1, 1)
+  const RowSrc ksrc{(const uint32_t*)a.kc, a.kp, nullptr, nullptr};
+  const RowSrc vsrc{nullptr, nullptr, (const uint32_t*)a.v, nullptr};
+
+  u32x4_t qt[2][S::KC], dat[2][2];
+  f32x16_t acc[2][S::MT];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = q0 + wave * RW + qb * 32 + l32;
+    const bool real = r < u.n_real;
+    long tok;
+    int n;
+    locate(u, a, real ? r : 0, tok, n);
+    own_row<DH, R, 1>(qsrc, gsrc, tok, n, tok * C + (long)u.h * DH, tok * a.heads + u.h, real, hh, sp, sc, qt[qb],
+                      dat[qb]);
+#pragma unroll
+    for (int mt = 0; mt < S::MT; ++mt) acc[qb][mt] = zero16();
+  }
+
+  Stager<DH, R, 0> stg;
+  stg.wave = wave;
+  stg.lane = lane;
+  const int ntiles = (u.n_real + TT - 1) / TT;
+  stg.load(a, u, ksrc, vsrc, 0);
+  stg.store(lds, sp, sc);
+  __syncthreads();
+  const int trow = tr_lane_base_row(lane), tch = tr_lane_base_ch(lane);
+  const int lb_a = piece_dw<S::KC>(trow, tch);
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = (t & 1) * S::ST_DW;
+    if (t + 1 < ntiles) stg.load(a, u, ksrc, vsrc, t + 1);
+    if (active) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        u32x4_t ka[S::KC], va[2], kt[S::MT][2];
+#pragma unroll
+        for (int c = 0; c < S::KC; ++c)
+          ka[c] = *reinterpret_cast<const u32x4_t*>(lds + buf + piece_dw<S::KC>(kb * 32 + l32, 16 * c + 8 * hh));
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          va[c] = *reinterpret_cast<const u32x4_t*>(lds + buf + S::A_DW +
+                                                    piece_dw<2>(kb * 32 + l32, 16 * c + 8 * hh));
+#pragma unroll
+        for (int mt = 0; mt < S::MT; ++mt)
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) kt[mt][c2] = tr_operand<S::KC>(lds, buf, lb_a, kb * 32 + 16 * c2, 32 * mt);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          f32x16_t s = zero16(), d = zero16();
+#pragma unroll
+          for (int c = 0; c < S::KC; ++c) s = mfma(ka[c], qt[qb][c], s);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) d = mfma(va[c], dat[qb][c], d);
+          uint32_t ds[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            ds[i] = pack_bf16(__builtin_amdgcn_exp2f(s[2 * i]) * d[2 * i],
+                              __builtin_amdgcn_exp2f(s[2 * i + 1]) * d[2 * i + 1]);
+#pragma unroll
+          for (int mt = 0; mt < S::MT; ++mt)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2)
+              acc[qb][mt] = mfma(kt[mt][c2], (u32x4_t){ds[4 * c2], ds[4 * c2 + 1], ds[4 * c2 + 2], ds[4 * c2 + 3]},
+                                 acc[qb][mt]);
+        }
+      }
+    }
+    if (t + 1 < ntiles) stg.store(lds + ((t + 1) & 1) * S::ST_DW, sp, sc);
+    __syncthreads();
+  }
+  if (!active) return;
+
+  // ---- epilogue: register e of acc[qb][mt] is column 32mt + 8(e/4) + 4hh + e%4
+  const float gq = 1.0f / sqrtf((float)R), gc = 1.0f / sqrtf((float)DH);
+  uint32_t* dqc = (uint32_t*)a.dqc;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = q0 + wave * RW + qb * 32 + l32;
+    if (r >= u.n_real) continue;
+    long tok;
+    int n;
+    locate(u, a, r, tok, n);
+    const long cofs = tok * C + (long)u.h * DH;
+    float* qrow = a.qrows + (((long)u.h * a.B + u.b) * a.H * a.W + (tok - (long)u.b * a.H * a.W)) * R;
+#pragma unroll
+    for (int mt = 0; mt < S::MT; ++mt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int c0 = 32 * mt + 8 * g4 + 4 * hh;  // first of 4 consecutive columns
+        const f32x16_t& x = acc[qb][mt];
+        if (c0 + 4 <= R) {
+          *reinterpret_cast<float4*>(qrow + c0) =
+              make_float4(x[4 * g4] * gq, x[4 * g4 + 1] * gq, x[4 * g4 + 2] * gq, x[4 * g4 + 3] * gq);
+        } else if (c0 >= R && c0 < R + DH) {
+          const long e = (cofs + c0 - R) >> 1;
+          dqc[e] = pack_bf16(x[4 * g4] * gc, x[4 * g4 + 1] * gc);
+          if (c0 + 2 < R + DH) dqc[e + 1] = pack_bf16(x[4 * g4 + 2] * gc, x[4 * g4 + 3] * gc);
+        }
+      }
+  }
+}
+
+// ---- dkv pass ------------------------------------------------------------------
+template <int DH, int R>
+__global__ void __launch_bounds__(RB, 1)
+bwd_dkv_bf16_kernel(BwdArgs a, int total) {
+  using S = BS<DH, R>;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[2 * S::ST_DW];
+  const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
+  if (logical >= total) return;
+  Unit u;
+  if (!decode_unit(logical, a, RB, u)) return;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int k0 = u.blk * RB;
+  const bool active = k0 + wave * RW < u.n_real;
+  const int C = a.heads * DH;
+  const float sp = LOG2E / sqrtf((float)R), sc = LOG2E / sqrtf((float)DH);
+
+  const RowSrc qsrc{(const uint32_t*)a.qc, a.qp, nullptr, a.lse};
+  const RowSrc gsrc{nullptr, nullptr, (const uint32_t*)a.da, a.dsum};
+  const RowSrc ksrc{(const uint32_t*)a.kc, a.kp, nullptr, nullptr};
+  const RowSrc vsrc{nullptr, nullptr, (const uint32_t*)a.v, nullptr};
+
+  u32x4_t kt[2][S::KC], vt[2][2];
+  f32x16_t accv[2], acck[2][S::MT];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int r = k0 + wave * RW + kb * 32 + l32;
+    const bool real = r < u.n_real;
+    long tok;
+    int n;
+    locate(u, a, real ? r : 0, tok, n);
+    own_row<DH, R, 0>(ksrc, vsrc, tok, n, tok * C + (long)u.h * DH, 0, real, hh, sp, sc, kt[kb], vt[kb]);
+    accv[kb] = zero16();
+#pragma unroll
+    for (int mt = 0; mt < S::MT; ++mt) acck[kb][mt] = zero16();
+  }
+
+  Stager<DH, R, 1> stg;
+  stg.wave = wave;
+  stg.lane = lane;
+  const int ntiles = (u.n_real + TT - 1) / TT;
+  stg.load(a, u, qsrc, gsrc, 0);
+  stg.store(lds, sp, sc);
+  __syncthreads();
+  const int trow = tr_lane_base_row(lane), tch = tr_lane_base_ch(lane);
+  const int lb_a = piece_dw<S::KC>(trow, tch);
+  const int lb_g = piece_dw<2>(trow, tch);
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = (t & 1) * S::ST_DW;
+    if (t + 1 < ntiles) stg.load(a, u, qsrc, gsrc, t + 1);
+    if (active) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        u32x4_t qa[S::KC], ga[2], gT[2], qT[S::MT][2];
+#pragma unroll
+        for (int c = 0; c < S::KC; ++c)
+          qa[c] = *reinterpret_cast<const u32x4_t*>(lds + buf + piece_dw<S::KC>(qb * 32 + l32, 16 * c + 8 * hh));
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          ga[c] = *reinterpret_cast<const u32x4_t*>(lds + buf + S::A_DW +
+                                                    piece_dw<2>(qb * 32 + l32, 16 * c + 8 * hh));
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) gT[c2] = tr_operand<2>(lds, buf + S::A_DW, lb_g, qb * 32 + 16 * c2, 0);
+#pragma unroll
+        for (int mt = 0; mt < S::MT; ++mt)
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) qT[mt][c2] = tr_operand<S::KC>(lds, buf, lb_a, qb * 32 + 16 * c2, 32 * mt);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          f32x16_t s = zero16(), d = zero16();
+#pragma unroll
+          for (int c = 0; c < S::KC; ++c) s = mfma(qa[c], kt[kb][c], s);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) d = mfma(ga[c], vt[kb][c], d);
+          uint32_t pp[8], ds[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float p0 = __builtin_amdgcn_exp2f(s[2 * i]), p1 = __builtin_amdgcn_exp2f(s[2 * i + 1]);
+            pp[i] = pack_bf16(p0, p1);
+            ds[i] = pack_bf16(p0 * d[2 * i], p1 * d[2 * i + 1]);
+          }
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            const u32x4_t pb = {pp[4 * c2], pp[4 * c2 + 1], pp[4 * c2 + 2], pp[4 * c2 + 3]};
+            const u32x4_t db = {ds[4 * c2], ds[4 * c2 + 1], ds[4 * c2 + 2], ds[4 * c2 + 3]};
+            accv[kb] = mfma(gT[c2], pb, accv[kb]);
+#pragma unroll
+            for (int mt = 0; mt < S::MT; ++mt) acck[kb][mt] = mfma(qT[mt][c2], db, acck[kb][mt]);
+          }
+        }
+      }
+    }
+    if (t + 1 < ntiles) stg.store(lds + ((t + 1) & 1) * S::ST_DW, sp, sc);
+    __syncthreads();
+  }
+  if (!active) return;
+
+  // ---- epilogue: register e is row/column 32mt + 8(e/4) + 4hh + e%4 of the key's gradient
+  uint32_t* dkc = (uint32_t*)a.dkc;
+  uint32_t* dvo = (uint32_t*)a.dv;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int r = k0 + wave * RW + kb * 32 + l32;
+    if (r >= u.n_real) continue;
+    long tok;
+    int n;
+    locate(u, a, r, tok, n);
+    const long cofs = tok * C + (long)u.h * DH;
+    float* krow = a.krows + (((long)u.h * a.B + u.b) * a.H * a.W + (tok - (long)u.b * a.H * a.W)) * R;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int c0 = 8 * g4 + 4 * hh;
+      const f32x16_t& x = accv[kb];
+      if (c0 < DH) {
+        const long e = (cofs + c0) >> 1;
+        dvo[e] = pack_bf16(x[4 * g4], x[4 * g4 + 1]);
+        if (c0 + 2 < DH) dvo[e + 1] = pack_bf16(x[4 * g4 + 2], x[4 * g4 + 3]);
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < S::MT; ++mt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int c0 = 32 * mt + 8 * g4 + 4 * hh;
+        const f32x16_t& x = acck[kb][mt];
+        if (c0 + 4 <= R) {
+          *reinterpret_cast<float4*>(krow + c0) =
+              make_float4(x[4 * g4] * LN2, x[4 * g4 + 1] * LN2, x[4 * g4 + 2] * LN2, x[4 * g4 + 3] * LN2);
+        } else if (c0 >= R && c0 < R + DH) {
+          const long e = (cofs + c0 - R) >> 1;
+          dkc[e] = pack_bf16(x[4 * g4] * LN2, x[4 * g4 + 1] * LN2);
+          if (c0 + 2 < R + DH) dkc[e + 1] = pack_bf16(x[4 * g4 + 2] * LN2, x[4 * g4 + 3] * LN2);
+        }
+      }
+  }
+}
+
+template <int DH, int R>
+hipError_t launch_variant(const BwdArgs& a, hipStream_t stream) {
+  const int total = bwd_units(a, RB);
+  const int grid = 8 * ((total + 7) / 8);
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<DH, R>), dim3(grid), dim3(RB), 0, stream, a, total);
+  hipLaunchKernelGGL((bwd_dkv_bf16_kernel<DH, R>), dim3(grid), dim3(RB), 0, stream, a, total);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attn_bwd_bf16_supported(int dh, int R) { return (dh == 30 && R == 16) || (dh == 16 && R == 16); }
+
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+  if (a.dh == 30 && a.R == 16) return launch_variant<30, 16>(a, stream);
+  if (a.dh == 16 && a.R == 16) return launch_variant<16, 16>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace rib

@@ -30,7 +30,8 @@ __global__ void __launch_bounds__(F32_QB)
 attn_f32_kernel(const float* __restrict__ qc, const float* __restrict__ kc,
                 const float* __restrict__ v, const float* __restrict__ g,
                 const float* __restrict__ qp, const float* __restrict__ kp, float* __restrict__ o,
-                int B, int H, int W, int heads, int dh, int R, int ws, int total, long tstride) {
+                int B, int H, int W, int heads, int dh, int R, int ws, int total, long tstride,
+                float* __restrict__ lse) {
   __shared__ float sk[F32_KT][DHM];
   __shared__ float sv[F32_KT][DHM];
   __shared__ float skp[F32_KT][RM];
@@ -127,6 +128,7 @@ attn_f32_kernel(const float* __restrict__ qc, const float* __restrict__ kc,
     }
   }
   if (!valid) return;
+  if (lse) lse[(qoff - h * dh) / C * heads + h] = m + logf(l);
 #pragma unroll
   for (int d = 0; d < DHM; ++d)
     if (d < dh) o[qoff + d] = acc[d] / l * (1.0f / (1.0f + expf(-g[qoff + d])));
@@ -140,7 +142,8 @@ hipError_t launch_f32(const AttnArgs& a, hipStream_t stream) {
   const int grid = 8 * ((total + 7) / 8);
   hipLaunchKernelGGL((attn_f32_kernel<DHM, RM>), dim3(grid), dim3(F32_QB), 0, stream,
                      (const float*)a.qc, (const float*)a.kc, (const float*)a.v, (const float*)a.g,
-                     a.qp, a.kp, (float*)a.o, a.B, a.H, a.W, a.heads, a.dh, a.R, a.ws, total, a.tstride);
+                     a.qp, a.kp, (float*)a.o, a.B, a.H, a.W, a.heads, a.dh, a.R, a.ws, total, a.tstride,
+                     a.lse);
   return hipGetLastError();
 }
 

@@ -90,8 +90,8 @@ rib_status rib_attn_supported(int dh, int R, int window, rib_dtype dtype) {
 namespace {
 // shared by rib_window_attn (one (qp, kp) pair) and rib_window_attn_heads (a pair per head)
 rib_status window_attn(const char* fn, bool per_head, const void* qc, const void* kc, const void* v,
-                       const void* g, const float* qp, const float* kp, void* o, int B, int H, int W,
-                       int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
+                       const void* g, const float* qp, const float* kp, void* o, float* lse, int B, int H,
+                       int W, int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
   if (!qc || !kc || !v || !g || !qp || !kp || !o)
     return fail(RIB_ERR_INVALID_ARG, "%s: null pointer", fn);
   if (B < 1 || H < 1 || W < 1 || heads < 1 || dh < 1 || R < 1)
@@ -112,8 +112,16 @@ rib_status window_attn(const char* fn, bool per_head, const void* qc, const void
   if (overlap(o, nb, qc, nb) || overlap(o, nb, kc, nb) || overlap(o, nb, v, nb) || overlap(o, nb, g, nb) ||
       overlap(o, nb, qp, np) || overlap(o, nb, kp, np))
     return fail(RIB_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
+  if (lse) {
+    const size_t nl = sizeof(float) * (size_t)B * H * W * heads;
+    const void* ins[] = {qc, kc, v, g, o};
+    for (const void* p : ins)
+      if (overlap(lse, nl, p, nb)) return fail(RIB_ERR_INVALID_ARG, "%s: lse overlaps a map", fn);
+    if (overlap(lse, nl, qp, np) || overlap(lse, nl, kp, np))
+      return fail(RIB_ERR_INVALID_ARG, "%s: lse overlaps a positional table", fn);
+  }
   const long tstride = per_head ? (long)window * window * R : 0;
-  const rib::AttnArgs a{qc, kc, v, g, qp, kp, o, B, H, W, heads, dh, R, window, tstride};
+  const rib::AttnArgs a{qc, kc, v, g, qp, kp, o, B, H, W, heads, dh, R, window, tstride, lse};
   const hipError_t e = dtype == RIB_F32 ? rib::launch_attn_f32(a, (hipStream_t)stream)
                                         : rib::launch_attn_bf16(a, (hipStream_t)stream);
   return hip_status(e, per_head ? "rib_window_attn_heads launch" : "rib_window_attn launch");
@@ -125,15 +133,23 @@ extern "C" {
 rib_status rib_window_attn(const void* qc, const void* kc, const void* v, const void* g,
                            const float* qp, const float* kp, void* o, int B, int H, int W,
                            int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
-  return window_attn("rib_window_attn", false, qc, kc, v, g, qp, kp, o, B, H, W, heads, dh, R, window,
-                     dtype, stream);
+  return window_attn("rib_window_attn", false, qc, kc, v, g, qp, kp, o, nullptr, B, H, W, heads, dh, R,
+                     window, dtype, stream);
+}
+
+rib_status rib_window_attn_train(const void* qc, const void* kc, const void* v, const void* g,
+                                 const float* qp, const float* kp, void* o, float* lse, int B, int H, int W,
+                                 int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
+  if (!lse) return fail(RIB_ERR_INVALID_ARG, "rib_window_attn_train: null pointer");
+  return window_attn("rib_window_attn_train", false, qc, kc, v, g, qp, kp, o, lse, B, H, W, heads, dh, R,
+                     window, dtype, stream);
 }
 
 rib_status rib_window_attn_heads(const void* qc, const void* kc, const void* v, const void* g,
                                  const float* qp, const float* kp, void* o, int B, int H, int W,
                                  int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
-  return window_attn("rib_window_attn_heads", true, qc, kc, v, g, qp, kp, o, B, H, W, heads, dh, R,
-                     window, dtype, stream);
+  return window_attn("rib_window_attn_heads", true, qc, kc, v, g, qp, kp, o, nullptr, B, H, W, heads, dh,
+                     R, window, dtype, stream);
 }
 
 
@@ -162,10 +178,10 @@ rib_status rib_cla_gate(const void* x, const float* dw_w, const float* dw_b, con
 }  // extern "C"
 
 namespace {
-// Workspace of rib_window_attn_backward: dA (storage type), D, lse, then the
+// Workspace of rib_window_attn_backward: dA (storage type), D, then the
 // per-row dQp and dKp (fp32), each region 256-byte aligned.
 struct BwdLayout {
-  size_t da, dsum, lse, qrows, krows, total;
+  size_t da, dsum, qrows, krows, total;
 };
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -176,8 +192,7 @@ BwdLayout bwd_layout(int B, int H, int W, int heads, int dh, int R, rib_dtype dt
   BwdLayout l;
   l.da = 0;
   l.dsum = up256(rows * dh * es);
-  l.lse = l.dsum + up256(rows * 4);
-  l.qrows = l.lse + up256(rows * 4);
+  l.qrows = l.dsum + up256(rows * 4);
   l.krows = l.qrows + up256(rows * R * 4);
   l.total = l.krows + up256(rows * R * 4);
   return l;
@@ -193,13 +208,13 @@ size_t rib_window_attn_backward_workspace(int B, int H, int W, int heads, int dh
 }
 
 rib_status rib_window_attn_backward(const void* qc, const void* kc, const void* v, const void* g,
-                                    const float* qp, const float* kp, const void* o, const void* dout,
-                                    void* dqc, void* dkc, void* dv, void* dg, float* dqp, float* dkp,
-                                    void* workspace, size_t workspace_bytes, int B, int H, int W, int heads,
-                                    int dh, int R, int window, rib_dtype dtype, void* stream) {
+                                    const float* qp, const float* kp, const void* o, const float* lse,
+                                    const void* dout, void* dqc, void* dkc, void* dv, void* dg, float* dqp,
+                                    float* dkp, void* workspace, size_t workspace_bytes, int B, int H, int W,
+                                    int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
   const char* fn = "rib_window_attn_backward";
-  if (!qc || !kc || !v || !g || !qp || !kp || !o || !dout || !dqc || !dkc || !dv || !dg || !dqp || !dkp ||
-      !workspace)
+  if (!qc || !kc || !v || !g || !qp || !kp || !o || !lse || !dout || !dqc || !dkc || !dv || !dg || !dqp ||
+      !dkp || !workspace)
     return fail(RIB_ERR_INVALID_ARG, "%s: null pointer", fn);
   if (B < 1 || H < 1 || W < 1 || heads < 1 || dh < 1 || R < 1)
     return fail(RIB_ERR_INVALID_ARG, "%s: B, H, W, heads, dh, R must be >= 1", fn);
@@ -211,7 +226,7 @@ rib_status rib_window_attn_backward(const void* qc, const void* kc, const void* 
   const uint64_t elems = (uint64_t)B * H * W * (uint64_t)heads * dh;
   if (elems >= (1ull << 31) || (uint64_t)B * H * W * heads * (uint64_t)R >= (1ull << 31))
     return fail(RIB_ERR_UNSUPPORTED, "%s: B*H*W*heads*max(dh, R) must be < 2^31", fn);
-  const void* all[] = {qc, kc, v, g, qp, kp, o, dout, dqc, dkc, dv, dg, dqp, dkp, workspace};
+  const void* all[] = {qc, kc, v, g, qp, kp, o, lse, dout, dqc, dkc, dv, dg, dqp, dkp, workspace};
   for (const void* p : all)
     if (!aligned(p, 16)) return fail(RIB_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
   const BwdLayout lay = bwd_layout(B, H, W, heads, dh, R, dtype);
@@ -219,20 +234,23 @@ rib_status rib_window_attn_backward(const void* qc, const void* kc, const void* 
     return fail(RIB_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, lay.total);
   const size_t nb = (size_t)elems * (dtype == RIB_F32 ? 4 : 2);
   const size_t np = sizeof(float) * (size_t)window * window * R;
-  const size_t sizes[] = {nb, nb, nb, nb, np, np, nb, nb, nb, nb, nb, nb, np, np, lay.total};
-  // every output (indices 8..14, the workspace included) is disjoint from every other buffer
-  for (int i = 8; i < 15; ++i)
-    for (int j = 0; j < 15; ++j)
+  const size_t nl = sizeof(float) * (size_t)B * H * W * heads;
+  const size_t sizes[] = {nb, nb, nb, nb, np, np, nb, nl, nb, nb, nb, nb, nb, np, np, lay.total};
+  // every output (indices 9..15, the workspace included) is disjoint from every other buffer
+  for (int i = 9; i < 16; ++i)
+    for (int j = 0; j < 16; ++j)
       if (j != i && overlap(all[i], sizes[i], all[j], sizes[j]))
         return fail(RIB_ERR_INVALID_ARG, "%s: an output or the workspace overlaps another buffer", fn);
   char* w = (char*)workspace;
-  rib::BwdArgs a{qc, kc, v, g, qp, kp, o, dout, dqc, dkc, dv, dg, dqp, dkp,
-                 w + lay.da, (float*)(w + lay.dsum), (float*)(w + lay.lse), (float*)(w + lay.qrows),
-                 (float*)(w + lay.krows), B, H, W, heads, dh, R, window};
+  rib::BwdArgs a{qc, kc, v, g, qp, kp, o, lse, dout, dqc, dkc, dv, dg, dqp, dkp,
+                 w + lay.da, (float*)(w + lay.dsum), (float*)(w + lay.qrows), (float*)(w + lay.krows),
+                 B, H, W, heads, dh, R, window};
   const hipStream_t st = (hipStream_t)stream;
   const bool bf16 = dtype == RIB_BF16;
   hipError_t e = rib::launch_attn_bwd_prep(a, bf16, st);
-  if (e == hipSuccess) e = rib::launch_attn_bwd_rows(a, bf16, st);
+  if (e == hipSuccess)
+    e = bf16 && rib::attn_bwd_bf16_supported(dh, R) ? rib::launch_attn_bwd_bf16(a, st)
+                                                    : rib::launch_attn_bwd_rows(a, bf16, st);
   if (e == hipSuccess) e = rib::launch_attn_bwd_reduce(a, st);
   return hip_status(e, "rib_window_attn_backward launch");
 }

@@ -14,6 +14,7 @@ struct BwdArgs {
   const float* qp;  // [ws*ws][R] shared positional pair
   const float* kp;
   const void* o;
+  const float* lse;  // row log-sum-exp per (token, head), natural log, from the forward
   const void* dout;
   // gradients
   void* dqc;
@@ -25,16 +26,51 @@ struct BwdArgs {
   // workspace
   void* da;      // dO * sigmoid(G), NHWC, storage type
   float* dsum;   // D = dO . O per (token, head)
-  float* lse;    // row log-sum-exp per (token, head)
   float* qrows;  // per-row dQp, [heads][B][H][W][R]
   float* krows;  // per-row dKp, same layout
   int B, H, W, heads, dh, R, ws;
 };
 
+// Decode of a workgroup's logical index into (b, wy, wx, h, row block) and the
+// real-token enumeration of a window: real index r -> (iy, ix) = (r / nx, r % nx).
+struct Unit {
+  int b, wy, wx, h, blk, nx, n_real;
+};
+
+__device__ __forceinline__ bool decode_unit(int logical, const BwdArgs& a, int rows_per_block, Unit& u) {
+  const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws;
+  const int rblocks = (a.ws * a.ws + rows_per_block - 1) / rows_per_block;
+  int t = logical;
+  u.blk = t % rblocks; t /= rblocks;
+  u.h = t % a.heads; t /= a.heads;
+  u.wx = t % nWx; t /= nWx;
+  u.wy = t % nWy;
+  u.b = t / nWy;
+  const int ny = min(a.ws, a.H - u.wy * a.ws);
+  u.nx = min(a.ws, a.W - u.wx * a.ws);
+  u.n_real = ny * u.nx;
+  return u.blk * rows_per_block < u.n_real;
+}
+
+// token index (b, y, x) and in-window index n of real token r of the unit
+__device__ __forceinline__ void locate(const Unit& u, const BwdArgs& a, int r, long& tok, int& n) {
+  const int iy = r / u.nx, ix = r - iy * u.nx;
+  tok = ((long)u.b * a.H + u.wy * a.ws + iy) * a.W + u.wx * a.ws + ix;
+  n = iy * a.ws + ix;
+}
+
+inline int bwd_units(const BwdArgs& a, int rows_per_block) {
+  const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws;
+  return a.B * nWy * nWx * a.heads * ((a.ws * a.ws + rows_per_block - 1) / rows_per_block);
+}
+
 hipError_t launch_attn_bwd_prep(const BwdArgs& a, bool bf16, hipStream_t stream);
 // dq then dkv, fp32-register kernels for any dh <= 64, R <= 64
 hipError_t launch_attn_bwd_rows(const BwdArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_attn_bwd_reduce(const BwdArgs& a, hipStream_t stream);
+// dq then dkv on bf16 matrix cores; false if (dh, R) has no compiled variant
+bool attn_bwd_bf16_supported(int dh, int R);
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 
 // encoder backward: workspace of encode_bwd_blocks(ws) * weight count floats
 int encode_bwd_blocks(int ws);

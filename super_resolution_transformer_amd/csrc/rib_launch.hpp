@@ -14,6 +14,7 @@ struct AttnArgs {
   void* o;
   int B, H, W, heads, dh, R, ws;
   long tstride;  // floats between the (qp, kp) tables of consecutive heads; 0 = one shared pair
+  float* lse;    // optional: row log-sum-exp per (token, head), natural log
 };
 
 hipError_t launch_encode(int ws, int L, int hidden, int R, const float* w, float* qp, float* kp,

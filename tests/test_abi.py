@@ -20,7 +20,7 @@ def L():
 def test_header_declares_the_boundary():
     assert set(rib.header_functions()) == {
         "rib_encode", "rib_window_attn", "rib_attn_supported", "rib_last_error", "rib_abi_version",
-        "rib_cla_gate", "rib_window_attn_heads", "rib_window_attn_backward", "rib_window_attn_backward_workspace",
+        "rib_cla_gate", "rib_window_attn_heads", "rib_window_attn_train", "rib_window_attn_backward", "rib_window_attn_backward_workspace",
         "rib_encode_backward", "rib_encode_backward_workspace"}
 
 
@@ -96,6 +96,21 @@ def test_attn_validation(L):
 
 
 @fake
+def test_attn_train_validation(L):
+    def train(ptrs, **kw):
+        a = dict(B=1, H=8, W=8, heads=2, dh=30, R=16, window=8, dtype=rib.RIB_BF16)
+        a.update(kw)
+        return L.rib_window_attn_train(*ptrs, a["B"], a["H"], a["W"], a["heads"], a["dh"], a["R"], a["window"],
+                                       a["dtype"], None)
+    assert train(P[:7] + [None]) == rib.RIB_ERR_INVALID_ARG
+    assert "rib_window_attn_train" in L.rib_last_error().decode()
+    assert train(P[:7] + [ctypes.c_void_p(P[6].value + 64)]) == rib.RIB_ERR_INVALID_ARG     # lse inside o
+    assert "overlap" in L.rib_last_error().decode()
+    assert train(P[:7] + [P[4]]) == rib.RIB_ERR_INVALID_ARG                                # lse == qp
+    assert train(P[:8], dh=31) == rib.RIB_ERR_UNSUPPORTED
+
+
+@fake
 def test_attn_heads_validation(L):
     def heads_call(ptrs, **kw):
         a = dict(B=1, H=8, W=8, heads=2, dh=30, R=16, window=8, dtype=rib.RIB_BF16)
@@ -147,7 +162,7 @@ def test_gate_validation(L):
     assert gate(L, P[:5] + [P[3]]) == rib.RIB_ERR_INVALID_ARG                             # g == pw_w
 
 
-PB = [ctypes.c_void_p(0x10000000 + i * 64 * MB) for i in range(15)]
+PB = [ctypes.c_void_p(0x10000000 + i * 64 * MB) for i in range(16)]
 
 
 def bwd(L, ptrs=None, nbytes=None, B=1, H=8, W=8, heads=2, dh=30, R=16, window=8, dtype=rib.RIB_BF16):
@@ -160,14 +175,15 @@ def bwd(L, ptrs=None, nbytes=None, B=1, H=8, W=8, heads=2, dh=30, R=16, window=8
 @fake
 def test_backward_validation(L):
     need = L.rib_window_attn_backward_workspace(1, 8, 8, 2, 30, 16, rib.RIB_BF16)
-    # dA (bf16) + D + lse + two per-row tables, each region 256-byte aligned
+    # dA (bf16) + D + two per-row tables, each region 256-byte aligned
     rows = 64 * 2
     up = lambda x: (x + 255) // 256 * 256
-    assert need == up(rows * 30 * 2) + 2 * up(rows * 4) + 2 * up(rows * 16 * 4)
+    assert need == up(rows * 30 * 2) + up(rows * 4) + 2 * up(rows * 16 * 4)
     assert L.rib_window_attn_backward_workspace(0, 8, 8, 2, 30, 16, rib.RIB_BF16) == 0
     assert bwd(L, [None] + PB[1:]) == rib.RIB_ERR_INVALID_ARG
     assert "null" in L.rib_last_error().decode()
-    assert bwd(L, PB[:14] + [None]) == rib.RIB_ERR_INVALID_ARG
+    assert bwd(L, PB[:15] + [None]) == rib.RIB_ERR_INVALID_ARG
+    assert bwd(L, PB[:7] + [None] + PB[8:]) == rib.RIB_ERR_INVALID_ARG          # lse
     assert bwd(L, B=0) == rib.RIB_ERR_INVALID_ARG
     assert bwd(L, window=1) == rib.RIB_ERR_INVALID_ARG
     assert bwd(L, dtype=4) == rib.RIB_ERR_INVALID_ARG
@@ -178,14 +194,15 @@ def test_backward_validation(L):
     assert "workspace" in L.rib_last_error().decode()
     assert bwd(L, [ctypes.c_void_p(PB[0].value + 4)] + PB[1:]) == rib.RIB_ERR_INVALID_ARG
     assert "aligned" in L.rib_last_error().decode()
-    alias = PB[:9] + [PB[2]] + PB[10:]                                    # dkc == v
+    alias = PB[:10] + [PB[2]] + PB[11:]                                   # dkc == v
     assert bwd(L, alias) == rib.RIB_ERR_INVALID_ARG
     assert "overlap" in L.rib_last_error().decode()
-    alias = PB[:14] + [ctypes.c_void_p(PB[8].value + 256)]                # workspace inside dqc
+    alias = PB[:15] + [ctypes.c_void_p(PB[9].value + 256)]                # workspace inside dqc
     assert bwd(L, alias) == rib.RIB_ERR_INVALID_ARG
-    alias = PB[:12] + [PB[13], PB[13], PB[14]]                            # dqp == dkp
+    alias = PB[:13] + [PB[14], PB[14], PB[15]]                            # dqp == dkp
     assert bwd(L, alias) == rib.RIB_ERR_INVALID_ARG
-    assert bwd(L, PB[:12] + [PB[4]] + PB[13:]) == rib.RIB_ERR_INVALID_ARG  # dqp == qp (an input)
+    assert bwd(L, PB[:13] + [PB[4]] + PB[14:]) == rib.RIB_ERR_INVALID_ARG  # dqp == qp (an input)
+    assert bwd(L, PB[:12] + [PB[7]] + PB[13:]) == rib.RIB_ERR_INVALID_ARG  # dg == lse (an input)
 
 
 @fake
@@ -216,9 +233,13 @@ def test_python_binding_argument_checks():
     with pytest.raises(ValueError):
         rib.cla_gate_into(x, torch.zeros(8, 3, 3), torch.zeros(8), torch.zeros(8, 8), torch.zeros(8), x)
     with pytest.raises(ValueError):
-        rib.window_attn_backward(x, x, x, x, torch.zeros(16, 4), torch.zeros(16, 4), x, x[:, :2], 2, 4)
+        rib.window_attn_backward(x, x, x, x, torch.zeros(16, 4), torch.zeros(16, 4), x, torch.zeros(1, 4, 4, 2),
+                                 x[:, :2], 2, 4)
     with pytest.raises(ValueError):
-        rib.window_attn_backward(x, x, x, x, torch.zeros(16, 4), torch.zeros(16, 4), x, x, 2, 4)  # CPU tensors
+        rib.window_attn_backward(x, x, x, x, torch.zeros(16, 4), torch.zeros(16, 4), x, torch.zeros(1, 4, 4, 2),
+                                 x, 2, 4)  # CPU tensors
+    with pytest.raises(ValueError):
+        rib.window_attn_train(x, x, x, x, torch.zeros(16, 4), torch.zeros(16, 4), 2, 4)       # CPU tensors
     with pytest.raises(ValueError):
         rib.encode_backward(4, 10, 64, 16, torch.zeros(3), torch.zeros(16, 16), torch.zeros(16, 16))
     with pytest.raises(ValueError):

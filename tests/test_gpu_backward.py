@@ -1,7 +1,7 @@
 """GPU parity of the backward pass, called through the C ABI, against the fp64 oracle.
 
-The GPU side runs its own forward (rib_window_attn) for O, then
-rib_window_attn_backward; the oracle differentiates its exact forward.  Every
+The GPU side runs its own training forward (rib_window_attn_train) for O and
+the row log-sum-exp, then rib_window_attn_backward; the oracle differentiates its exact forward.  Every
 gradient is compared over its whole extent with
 
     max |got - ref| <= tol * max |ref|      (tol 1e-5 fp32, 2e-2 bf16)
@@ -51,9 +51,9 @@ def gpu_backward(torch, p, ws, dout_vals, dout_bits):
     maps = [dev(torch, getattr(p, nm), p.bits.get(nm), p.dtype) for nm in ("qc", "kc", "v", "g")]
     w = torch.from_numpy(p.weights).cuda()
     qp, kp = rib.encode(ws, p.L, p.hidden, p.R, w)
-    o = rib.window_attn(*maps, qp, kp, p.heads, ws)
+    o, lse = rib.window_attn_train(*maps, qp, kp, p.heads, ws)
     dout = dev(torch, dout_vals, dout_bits, p.dtype)
-    grads = rib.window_attn_backward(*maps, qp, kp, o, dout, p.heads, ws)
+    grads = rib.window_attn_backward(*maps, qp, kp, o, lse, dout, p.heads, ws)
     dw = rib.encode_backward(ws, p.L, p.hidden, p.R, w, grads[4], grads[5])
     torch.cuda.synchronize()
     out = [t.float().cpu().numpy().astype(np.float64) for t in grads]
@@ -84,6 +84,9 @@ CASES = [
     (2, 40, 24, 6, 30, 16, 10, 64, 16, "bf16"),    # the SST head shape, bf16 storage
     (1, 40, 33, 6, 30, 16, 10, 64, 32, "bf16"),    # ws 32 with a ragged right column
     (1, 20, 20, 2, 16, 16, 10, 64, 16, "bf16"),    # dh 16, partial windows
+    (1, 20, 20, 2, 8, 8, 4, 16, 16, "bf16"),       # a head shape without matrix-core kernels (fp32 rows)
+    (1, 96, 100, 1, 30, 16, 10, 64, 96, "bf16"),   # 96x96 window and a 4-column window: 18 row blocks
+    (1, 70, 64, 2, 16, 16, 10, 64, 64, "bf16"),    # 64x64 windows, ragged bottom row of windows
 ]
 
 
@@ -134,3 +137,35 @@ def test_backward_is_linear_in_images(torch):
         tabs[1] += one[5]
     for k in range(2):
         compare(full[4 + k], tabs[k], 1e-5, NAMES[4 + k] + " sum over images")
+
+
+LSE_CASES = [
+    (1, 64, 64, 3, 16, 16, 16, "f32"),
+    (1, 21, 13, 2, 30, 16, 8, "f32"),
+    (1, 40, 24, 6, 30, 16, 16, "bf16"),     # small-window kernel
+    (1, 70, 33, 6, 30, 16, 32, "bf16"),     # tiled kernel, ragged windows
+    (1, 64, 64, 3, 16, 16, 64, "bf16"),
+    (1, 100, 96, 2, 30, 16, 96, "bf16"),    # 96x96 windows, one 4-row window below
+]
+
+
+@pytest.mark.parametrize("case", LSE_CASES, ids=lambda c: "B{}H{}W{}h{}d{}R{}ws{}-{}".format(*c))
+def test_train_forward_lse(torch, case):
+    """rib_window_attn_train: O bit-identical to rib_window_attn, lse against the oracle's
+    (max abs error 1e-5 fp32, 2e-2 bf16: the forward's bars, on values of order log n)."""
+    B, H, W, heads, dh, R, ws, dtype = case
+    note(f"train forward {case}")
+    p = synthetic.make_problem(B, H, W, heads, dh, R, 10, 64, dtype=dtype, seed=ws + H)
+    maps = [dev(torch, getattr(p, nm), p.bits.get(nm), p.dtype) for nm in ("qc", "kc", "v", "g")]
+    w = torch.from_numpy(p.weights).cuda()
+    qp, kp = rib.encode(ws, p.L, p.hidden, p.R, w)
+    o_plain = rib.window_attn(*maps, qp, kp, heads, ws)
+    o, lse = rib.window_attn_train(*maps, qp, kp, heads, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16) if dtype == "bf16" else o, o_plain.view(torch.int16) if dtype == "bf16"
+                       else o_plain)
+    oq, ok = oracle.encode(ws, p.L, p.hidden, p.R, p.weights)
+    ref = oracle.window_lse(p.qc, p.kc, oq, ok, heads, ws)
+    err = float(np.abs(lse.cpu().numpy() - ref).max())
+    note(f"  lse max|err| {err:.3g}  max|lse| {float(np.abs(ref).max()):.3g}")
+    assert err <= TOL[dtype]

@@ -160,6 +160,36 @@ def test_backward_of_uniform_attention():
         assert np.abs(a).max() < 1e-14
 
 
+@pytest.mark.parametrize("case", CASES[:3], ids=lambda c: "B{B}H{H}W{W}h{heads}d{dh}R{R}ws{ws}".format(**c))
+def test_lse_matches_logsumexp_of_debug_scores(case):
+    """lse equals scipy's logsumexp over the rows of Sc + Bm exposed by the debug entry point, and
+    exp(S - lse) sums to one on every row."""
+    from scipy.special import logsumexp
+    ws = case["ws"]
+    p, qp, kp, _ = attn_case(**case)
+    got = oracle.window_lse(p.qc, p.kc, qp, kp, p.heads, ws)
+    nWy, nWx = -(-p.H // ws), -(-p.W // ws)
+    for b in range(p.B):
+        for wy in range(nWy):
+            for wx in range(nWx):
+                for h in range(p.heads):
+                    Sc, Bm, P, toks = oracle.window_debug(p.qc, p.kc, p.v, p.g, qp, kp, p.heads, ws, b, wy, wx, h)
+                    want = logsumexp(Sc + Bm, axis=1)
+                    np.testing.assert_allclose(got[b, toks[:, 0], toks[:, 1], h], want, rtol=1e-13, atol=1e-13)
+                    np.testing.assert_allclose(np.exp(Sc + Bm - want[:, None]).sum(axis=1), 1.0, rtol=1e-12)
+
+
+def test_lse_of_zero_scores_is_log_window_size():
+    ws = 4
+    p, _, _, _ = attn_case(B=1, H=6, W=7, heads=2, dh=3, R=2, ws=ws, seed=4)
+    z = np.zeros(p.qc.shape)
+    got = oracle.window_lse(z, z, np.zeros((16, 2)), np.zeros((16, 2)), 2, ws)
+    for y in range(6):
+        for x in range(7):
+            n = (min(6, (y // ws + 1) * ws) - y // ws * ws) * (min(7, (x // ws + 1) * ws) - x // ws * ws)
+            np.testing.assert_allclose(got[0, y, x], math.log(n), rtol=1e-15)
+
+
 ENC_CASES = [(4, 2, 5, 3), (8, 3, 7, 4), (2, 0, 3, 2)]
 
 
@@ -218,9 +248,13 @@ BW_MUTATIONS = {
     "encoder relu derivative dropped": ("const double dpre = pre[j] > 0.0 ? dhj : 0.0;", "const double dpre = dhj;"),
     "encoder dWk from dQp": ("dWk[(size_t)j * R + r] += hj * gk[r];", "dWk[(size_t)j * R + r] += hj * gq[r];"),
     "encoder dh misses Wk": ("gk[r] * Wk[(size_t)j * R + r]", "0.0 * Wk[(size_t)j * R + r]"),
+    "lse without the maximum": ("* heads + h] = mx + log(sum);", "* heads + h] = log(sum);"),
+    "lse bias unscaled": ("S[j] = sc * inv_sqrt_dh + bb * inv_sqrt_r;", "S[j] = sc * inv_sqrt_dh + bb;"),
 }
 
 BW_PINS = [
+    lambda: test_lse_matches_logsumexp_of_debug_scores(CASES[0]),
+    test_lse_of_zero_scores_is_log_window_size,
     lambda: test_attention_backward_matches_autograd(CASES[0]),
     lambda: test_attention_backward_matches_autograd(CASES[2]),
     test_attention_backward_matches_finite_differences,
