@@ -191,7 +191,8 @@ rib_status rib_cla_gate(const void* x, const float* dw_w, const float* dw_b, con
  * Limits : window <= 128, dh <= 64, R <= 64; B*H*W*heads*max(dh, R) < 2^31;
  *          pointers 16-byte aligned.
  */
-size_t rib_window_attn_backward_workspace(int B, int H, int W, int heads, int dh, int R, rib_dtype dtype);
+size_t rib_window_attn_backward_workspace(int B, int H, int W, int heads, int dh, int R, int window,
+                                          rib_dtype dtype);
 rib_status rib_window_attn_backward(const void* qc, const void* kc, const void* v, const void* g,
                                     const float* qp, const float* kp, const void* o, const float* lse,
                                     const void* dout, void* dqc, void* dkc, void* dv, void* dg, float* dqp,
@@ -221,7 +222,7 @@ const char* rib_last_error(void);
 /* ABI version of this header (incremented on any incompatible change). */
 int rib_abi_version(void);
 
-#define RIB_ABI_VERSION 4
+#define RIB_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

@@ -59,7 +59,7 @@ def lib(path: str | None = None):
     L.rib_cla_gate.argtypes = [vp] * 6 + [i] * 5 + [vp]
     L.rib_cla_gate.restype = i
     sz = ctypes.c_size_t
-    L.rib_window_attn_backward_workspace.argtypes = [i] * 7
+    L.rib_window_attn_backward_workspace.argtypes = [i] * 8
     L.rib_window_attn_backward_workspace.restype = sz
     L.rib_window_attn_train.argtypes = [vp] * 8 + [i] * 8 + [vp]
     L.rib_window_attn_train.restype = i
@@ -241,7 +241,7 @@ def window_attn_backward(qc, kc, v, g, qp, kp, o, lse, dout, heads: int, window:
     code = _dtype_code(qc)
     outs = [torch.empty_like(qc) for _ in range(4)]
     dqp, dkp = torch.empty_like(qp), torch.empty_like(kp)
-    nbytes = lib().rib_window_attn_backward_workspace(B, H, W, heads, dh, R, code)
+    nbytes = lib().rib_window_attn_backward_workspace(B, H, W, heads, dh, R, window, code)
     work = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=qc.device)
     _check(lib().rib_window_attn_backward(*[_ptr(t) for t in ts[:4]], _ptr(qp), _ptr(kp), _ptr(o), _ptr(lse),
                                           _ptr(dout),

@@ -55,7 +55,59 @@ __device__ __forceinline__ void stf<uint16_t>(uint16_t* p, long i, float v) {
   p[i] = (uint16_t)(pack_bf16(v, 0.0f) & 0xFFFFu);
 }
 
-// prep: one thread per (token, head).
+// prep, staged: a workgroup takes NT whole tokens (NT*C contiguous elements of
+// each map), copies dO, O, G into LDS with coalesced dword loads, computes one
+// (token, head) row per thread, writes dA and dG over the staged dO and O and
+// stores them back coalesced.  LDS: 3 * NT * C elements.
+template <typename T>
+__global__ void __launch_bounds__(256)
+bwd_prep_staged_kernel(const T* __restrict__ dout, const T* __restrict__ o, const T* __restrict__ g,
+                       T* __restrict__ da, T* __restrict__ dg, float* __restrict__ dsum, long ntok, int heads,
+                       int dh, int NT) {
+  extern __shared__ uint32_t sm[];
+  const int C = heads * dh;
+  const long tok0 = (long)blockIdx.x * NT;
+  const int nt = (int)min((long)NT, ntok - tok0);
+  const int ndw = nt * C * (int)sizeof(T) / 4;   // C * sizeof(T) is a multiple of 4
+  const int cap = NT * C * (int)sizeof(T) / 4;
+  uint32_t* s_do = sm;
+  uint32_t* s_o = sm + cap;
+  uint32_t* s_g = sm + 2 * cap;
+  const long base = tok0 * C * (long)sizeof(T) / 4;
+  const uint32_t* gdo = reinterpret_cast<const uint32_t*>(dout) + base;
+  const uint32_t* go = reinterpret_cast<const uint32_t*>(o) + base;
+  const uint32_t* gg = reinterpret_cast<const uint32_t*>(g) + base;
+  for (int i = threadIdx.x; i < ndw; i += 256) {
+    s_do[i] = gdo[i];
+    s_o[i] = go[i];
+    s_g[i] = gg[i];
+  }
+  __syncthreads();
+  T* e_do = reinterpret_cast<T*>(s_do);
+  T* e_o = reinterpret_cast<T*>(s_o);
+  const T* e_g = reinterpret_cast<const T*>(s_g);
+  for (int row = threadIdx.x; row < nt * heads; row += 256) {
+    const int e0 = (row / heads) * C + (row % heads) * dh;
+    float D = 0.0f;
+    for (int d = 0; d < dh; ++d) {
+      const float dov = ldf(e_do, e0 + d), ov = ldf(e_o, e0 + d);
+      const float s = 1.0f / (1.0f + expf(-ldf(e_g, e0 + d)));
+      D = fmaf(dov, ov, D);
+      stf(e_do, e0 + d, dov * s);
+      stf(e_o, e0 + d, dov * ov * (1.0f - s));
+    }
+    dsum[tok0 * heads + row] = D;
+  }
+  __syncthreads();
+  uint32_t* gda = reinterpret_cast<uint32_t*>(da) + base;
+  uint32_t* gdg = reinterpret_cast<uint32_t*>(dg) + base;
+  for (int i = threadIdx.x; i < ndw; i += 256) {
+    gda[i] = s_do[i];
+    gdg[i] = s_o[i];
+  }
+}
+
+// prep for rows too wide to stage (C * sizeof(T) > 16 KB): one thread per (token, head).
 template <typename T>
 __global__ void __launch_bounds__(256)
 bwd_prep_kernel(const T* __restrict__ dout, const T* __restrict__ o, const T* __restrict__ g,
@@ -340,7 +392,18 @@ hipError_t launch_rows_dh(const BwdArgs& a, hipStream_t stream) {
 
 template <typename T>
 hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
-  const long rows = (long)a.B * a.H * a.W * a.heads;
+  const long ntok = (long)a.B * a.H * a.W;
+  const int C = a.heads * a.dh;
+  const int row_bytes = C * (int)sizeof(T);
+  if (row_bytes % 4 == 0 && row_bytes <= 16384) {
+    const int NT = max(1, 16384 / row_bytes);  // <= 48 KB of LDS for the three maps
+    const int grid = (int)((ntok + NT - 1) / NT);
+    const size_t lds = 3 * (size_t)NT * row_bytes;
+    hipLaunchKernelGGL((bwd_prep_staged_kernel<T>), dim3(grid), dim3(256), lds, stream, (const T*)a.dout,
+                       (const T*)a.o, (const T*)a.g, (T*)a.da, (T*)a.dg, a.dsum, ntok, a.heads, a.dh, NT);
+    return hipGetLastError();
+  }
+  const long rows = ntok * a.heads;
   const int grid = (int)((rows + 255) / 256);
   hipLaunchKernelGGL((bwd_prep_kernel<T>), dim3(grid), dim3(256), 0, stream, (const T*)a.dout, (const T*)a.o,
                      (const T*)a.g, (T*)a.da, (T*)a.dg, a.dsum, rows, a.heads, a.dh);

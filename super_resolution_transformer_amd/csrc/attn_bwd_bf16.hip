@@ -34,12 +34,13 @@
 // trick).  dkv pass (key-major): the mirror image, lane = key: S = Qt Kt^T,
 // dP - D = dA' V'^T, then dV'^T += dA'^T P and dKt^T += Qt^T dS.
 //
-// LDS row layout (both passes): an operand row of 16*NH bf16 columns is cut
-// into 8-byte pieces of 4 columns; piece (row, ch) sits at 8-byte index
-//   ((row/4) * NH + ch/16) * 16 + (row%4) * 4 + (ch%16)/4.
-// Eight consecutive columns of one row are 16 contiguous bytes (the row read
-// of a score A operand), and every 16-lane group of a transposing read covers
-// one 128-byte block.
+// LDS layout (both passes): a tile of TT rows is stored chunk-major, one
+// 16-byte chunk = 8 consecutive bf16 columns of a row, chunk c of row j at
+// dword c*CS + 4j with the chunk stride CS = 4*TT + 16.  A row read of a
+// score A operand (16 lanes = 16 rows of one chunk) and a staging write are
+// 256 contiguous bytes; a 16-lane group of a transposing read takes 4 rows x
+// 16 bytes from two neighbouring chunks, which the 16-dword pad puts on
+// disjoint banks.  All three access kinds are free of bank conflicts.
 #include "rib_bwd.hpp"
 #include "rib_device.hpp"
 
@@ -53,6 +54,7 @@ constexpr int RB = NWV * RW;   // own rows per workgroup
 constexpr int TT = 64;         // streamed rows per LDS tile
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+constexpr int CS = 4 * TT + 16;  // dwords between consecutive 8-column chunks of a tile
 
 template <int DH, int R>
 struct BS {
@@ -63,17 +65,16 @@ struct BS {
   static constexpr int MT = (R + DH + 31) / 32;      // 32-column tiles of an augmented gradient
   static constexpr int AP = 2 * KC;                  // 8-column pieces of an augmented row
   static constexpr int NP = AP + 2 * DC;             // pieces staged per streamed row
-  static constexpr int A_DW = TT * KC * 8;           // dwords of the augmented tile
-  static constexpr int V_DW = TT * DC * 8;           // dwords of the value / gradient tile
+  static constexpr int A_DW = 2 * KC * CS;           // dwords of the augmented tile
+  static constexpr int V_DW = 2 * DC * CS;           // dwords of the value / gradient tile
   static constexpr int ST_DW = A_DW + V_DW;
   static_assert(DC == 2, "value rows are one 32-column tile");
+  static_assert(NP == 10, "packed rows of 160 bytes");
   static_assert(NP <= 2 * NWV, "at most two staging pieces per thread");
 };
 
-template <int NH>
-__device__ __forceinline__ int piece_dw(int row, int ch) {
-  return 2 * ((((row >> 2) * NH + (ch >> 4)) << 4) + ((row & 3) << 2) + ((ch & 15) >> 2));
-}
+// dword of chunk c (columns 8c .. 8c+7) of row j of a tile
+__device__ __forceinline__ int chunk_dw(int c, int j) { return c * CS + 4 * j; }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
@@ -84,19 +85,25 @@ __device__ __forceinline__ u32x2_t ds_read_tr16(const uint32_t* p) {
   return __builtin_bit_cast(u32x2_t, r);
 }
 
-// A operand of X^T B for the 32 columns [c32, c32+32) of a tile in the piece
-// layout and its rows [kofs, kofs+16): lane (column, 8 rows) in the row order
-// of a 32x32 accumulator's registers (see the forward kernel's V^T reads).
-// tbase = dword index of the tile, lbase = piece_dw(row0, ch0) of this lane.
-template <int NH>
+// A operand of X^T B for the 32 columns [c32, c32+32) of a tile and its rows
+// [kofs, kofs+16): lane (column, 8 rows) in the row order of a 32x32
+// accumulator's registers (the forward kernel's V^T reads).  In a 16-lane
+// group q of the transposing read, input lane j = 4k + m supplies columns
+// 16(q%2) + 4m .. +3 of row 4(q/2) + k (and of row +8 for the second read).
+// tbase = dword index of the tile, lbase = tr_lane_base(lane).
 __device__ __forceinline__ u32x4_t tr_operand(const uint32_t* lds, int tbase, int lbase, int kofs, int c32) {
-  const u32x2_t lo = ds_read_tr16(lds + tbase + lbase + piece_dw<NH>(kofs, c32));
-  const u32x2_t hi = ds_read_tr16(lds + tbase + lbase + piece_dw<NH>(kofs + 8, c32));
+  const int off = (c32 >> 3) * CS + 4 * kofs;
+  const u32x2_t lo = ds_read_tr16(lds + tbase + lbase + off);
+  const u32x2_t hi = ds_read_tr16(lds + tbase + lbase + off + 32);
   return (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
 }
 
-__device__ __forceinline__ int tr_lane_base_row(int lane) { return 4 * ((lane >> 4) >> 1) + ((lane & 15) >> 2); }
-__device__ __forceinline__ int tr_lane_base_ch(int lane) { return 16 * ((lane >> 4) & 1) + 4 * (lane & 3); }
+__device__ __forceinline__ int tr_lane_base(int lane) {
+  const int q = lane >> 4, j = lane & 15;
+  const int row = 4 * (q >> 1) + (j >> 2);
+  const int col = 16 * (q & 1) + 4 * (j & 3);
+  return chunk_dw(col >> 3, row) + 2 * ((col >> 2) & 1);
+}
 
 __device__ __forceinline__ float f32(uint32_t x) { return __builtin_bit_cast(float, x); }
 
@@ -187,8 +194,8 @@ __device__ __forceinline__ u32x4_t cvt_val(const Raw& raw, bool real) {
   return (u32x4_t){d[0], d[1], d[2], d[3]};
 }
 
-// Piece p of a streamed row (p < AP: augmented row, else value-like row).
-// KIND 0: key rows (dq pass streams keys), KIND 1: query rows (dkv pass).
+// Piece p of a row (p < AP: augmented row, else value-like row).
+// KIND 0: key-side rows (Kt, V'), KIND 1: query-side rows (Qt, dA').
 template <int DH, int R, int P, int KIND>
 __device__ __forceinline__ void load_piece(const RowSrc& aug, const RowSrc& val, long tok, int n, long cofs,
                                            long crow, Raw& raw) {
@@ -197,92 +204,63 @@ __device__ __forceinline__ void load_piece(const RowSrc& aug, const RowSrc& val,
   else load_val<DH, P - S::AP, KIND>(val, cofs, crow, raw);
 }
 
-template <int DH, int R, int P, int KIND>
-__device__ __forceinline__ void store_piece(uint32_t* tile, int row, const Raw& raw, bool real, float sp, float sc) {
+template <int DH, int R, int KIND, int P = 0>
+__device__ __forceinline__ u32x4_t make_chunk(int c, const RowSrc& aug, const RowSrc& val, long tok, int n, long cofs,
+                                              long crow, bool real, float sp, float sc) {
   using S = BS<DH, R>;
-  if constexpr (P < S::AP) {
-    *reinterpret_cast<u32x4_t*>(tile + piece_dw<S::KC>(row, 8 * P)) = cvt_aug<DH, R, P, KIND>(raw, real, sp, sc);
+  if constexpr (P < S::NP) {
+    if (c == P) {
+      Raw raw = {};
+      if (real) load_piece<DH, R, P, KIND>(aug, val, tok, n, cofs, crow, raw);
+      if constexpr (P < S::AP) return cvt_aug<DH, R, P, KIND>(raw, real, sp, sc);
+      else return cvt_val<DH, P - S::AP, KIND>(raw, real);
+    }
+    return make_chunk<DH, R, KIND, P + 1>(c, aug, val, tok, n, cofs, crow, real, sp, sc);
   } else {
-    *reinterpret_cast<u32x4_t*>(tile + S::A_DW + piece_dw<S::DC>(row, 8 * (P - S::AP))) =
-        cvt_val<DH, P - S::AP, KIND>(raw, real);
+    return (u32x4_t){0u, 0u, 0u, 0u};
   }
 }
 
-// B operands of one own row: the augmented row chunks (lane half hh holds
-// columns 16c + 8hh .. +7) and the value-like row chunks.
-template <int DH, int R, int KIND, int C = 0>
-__device__ __forceinline__ void own_aug(const RowSrc& aug, long tok, int n, long cofs, long crow, bool real, int hh,
-                                        float sp, float sc, u32x4_t* at) {
-  if constexpr (C < BS<DH, R>::KC) {
-    Raw r0 = {}, r1 = {};
-    load_aug<DH, R, 2 * C, KIND>(aug, tok, n, cofs, crow, r0);
-    load_aug<DH, R, 2 * C + 1, KIND>(aug, tok, n, cofs, crow, r1);
-    const u32x4_t x0 = cvt_aug<DH, R, 2 * C, KIND>(r0, real, sp, sc);
-    const u32x4_t x1 = cvt_aug<DH, R, 2 * C + 1, KIND>(r1, real, sp, sc);
-    at[C] = hh ? x1 : x0;
-    own_aug<DH, R, KIND, C + 1>(aug, tok, n, cofs, crow, real, hh, sp, sc, at);
-  }
-}
-
-template <int DH, int KIND, int C = 0>
-__device__ __forceinline__ void own_val(const RowSrc& val, long cofs, long crow, bool real, int hh, u32x4_t* vt) {
-  if constexpr (C < 2) {
-    Raw r0 = {}, r1 = {};
-    load_val<DH, 2 * C, KIND>(val, cofs, crow, r0);
-    load_val<DH, 2 * C + 1, KIND>(val, cofs, crow, r1);
-    const u32x4_t x0 = cvt_val<DH, 2 * C, KIND>(r0, real);
-    const u32x4_t x1 = cvt_val<DH, 2 * C + 1, KIND>(r1, real);
-    vt[C] = hh ? x1 : x0;
-    own_val<DH, KIND, C + 1>(val, cofs, crow, real, hh, vt);
-  }
-}
-
+// ---- pack pass -----------------------------------------------------------------
+// Writes the operand rows of one side of every unit in the LDS tile image:
+// [unit][tile][chunk][row][16 bytes] (1 KB per chunk of 64 rows); rows past
+// the window's real tokens are zero.  One thread per (unit, tile, chunk, row),
+// one wave per chunk.  KIND 0: key side (Kt with (1, 1), V' with (1, 1));
+// KIND 1: query side (Qt with -lse*log2e, dA' with -D).
 template <int DH, int R, int KIND>
-__device__ __forceinline__ void own_row(const RowSrc& aug, const RowSrc& val, long tok, int n, long cofs, long crow,
-                                        bool real, int hh, float sp, float sc, u32x4_t (&at)[BS<DH, R>::KC],
-                                        u32x4_t (&vt)[2]) {
-  own_aug<DH, R, KIND>(aug, tok, n, cofs, crow, real, hh, sp, sc, at);
-  own_val<DH, KIND>(val, cofs, crow, real, hh, vt);
-}
-
-// Streams the other side of the unit through LDS: every thread stages pieces
-// `wave` and `wave + 8` of row `lane` of a tile.
-template <int DH, int R, int KIND>
-struct Stager {
+__global__ void __launch_bounds__(256)
+bwd_pack_kernel(BwdArgs a, long total) {
   using S = BS<DH, R>;
-  Raw raw[2];
-  bool real;
-  int wave, lane;
-
-  __device__ __forceinline__ void load(const BwdArgs& a, const Unit& u, const RowSrc& aug, const RowSrc& val,
-                                       int t) {
-    const int r = t * TT + lane;
-    real = r < u.n_real;
-    long tok;
-    int n;
-    locate(u, a, real ? r : 0, tok, n);
-    const long cofs = tok * (long)(a.heads * DH) + (long)u.h * DH;
-    const long crow = tok * a.heads + u.h;
-    load_all<0>(aug, val, tok, n, cofs, crow);
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int row = (int)(idx & 63);
+  long t = idx >> 6;
+  const int c = (int)(t % S::NP);
+  t /= S::NP;
+  const int tile = (int)(t % a.tu);
+  const int unit = (int)(t / a.tu);
+  Unit u;
+  decode_unit(unit, a, a.ws * a.ws, u);
+  const int r = tile * TT + row;
+  const bool real = r < u.n_real;
+  long tok;
+  int n;
+  locate(u, a, real ? r : 0, tok, n);
+  const long cofs = tok * (long)(a.heads * DH) + (long)u.h * DH;
+  const long crow = tok * a.heads + u.h;
+  const float sp = LOG2E / sqrtf((float)R), sc = LOG2E / sqrtf((float)DH);
+  u32x4_t out;
+  if constexpr (KIND == 0) {
+    const RowSrc aug{(const uint32_t*)a.kc, a.kp, nullptr, nullptr};
+    const RowSrc val{nullptr, nullptr, (const uint32_t*)a.v, nullptr};
+    out = make_chunk<DH, R, 0>(c, aug, val, tok, n, cofs, crow, real, sp, sc);
+  } else {
+    const RowSrc aug{(const uint32_t*)a.qc, a.qp, nullptr, a.lse};
+    const RowSrc val{nullptr, nullptr, (const uint32_t*)a.da, a.dsum};
+    out = make_chunk<DH, R, 1>(c, aug, val, tok, n, cofs, crow, real, sp, sc);
   }
-
-  template <int P>
-  __device__ __forceinline__ void load_all(const RowSrc& aug, const RowSrc& val, long tok, int n, long cofs,
-                                           long crow) {
-    if constexpr (P < S::NP) {
-      if (P % NWV == wave) load_piece<DH, R, P, KIND>(aug, val, tok, n, cofs, crow, raw[P / NWV]);
-      load_all<P + 1>(aug, val, tok, n, cofs, crow);
-    }
-  }
-
-  template <int P = 0>
-  __device__ __forceinline__ void store(uint32_t* tile, float sp, float sc) {
-    if constexpr (P < S::NP) {
-      if (P % NWV == wave) store_piece<DH, R, P, KIND>(tile, lane, raw[P / NWV], real, sp, sc);
-      store<P + 1>(tile, sp, sc);
-    }
-  }
-};
+  reinterpret_cast<u32x4_t*>(KIND == 0 ? a.pk : a.pq)[idx] = out;
+}
 
 __device__ __forceinline__ f32x16_t mfma(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -296,73 +274,105 @@ __device__ __forceinline__ f32x16_t zero16() {
   return z;
 }
 
+// Shared frame of both passes: the unit, this wave's own rows and the
+// streamed side's packed image.
+template <int DH, int R>
+struct Frame {
+  using S = BS<DH, R>;
+  Unit u;
+  int unit, r0, wave, lane, l32, hh, ntiles;
+  bool active;
+  const uint32_t* own;     // packed image of the own side of this unit
+  __amdgpu_buffer_rsrc_t other;  // packed image of the streamed side of this unit
+
+  __device__ __forceinline__ bool init(const BwdArgs& a, int total, const uint32_t* own_img,
+                                       const uint32_t* other_img) {
+    const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
+    if (logical >= total) return false;
+    if (!decode_unit(logical, a, RB, u)) return false;
+    unit = logical / ((a.ws * a.ws + RB - 1) / RB);
+    const int tid = threadIdx.x;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    lane = tid & 63;
+    l32 = lane & 31;
+    hh = lane >> 5;
+    r0 = u.blk * RB + wave * RW;
+    active = r0 < u.n_real;
+    ntiles = (u.n_real + TT - 1) / TT;
+    const long img = (long)unit * a.tu * S::NP * 256;  // dwords per unit image
+    own = own_img + img;
+    other = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(other_img + img), (short)0,
+                                              a.tu * S::NP * 1024, (int)0x00020000u);
+    return true;
+  }
+
+  // B operands of own row r: augmented chunks 2c + hh and value-like chunks
+  __device__ __forceinline__ void own_row(int r, u32x4_t (&at)[S::KC], u32x4_t (&vt)[2]) const {
+    const bool real = r < u.n_real;
+    const uint32_t* base = own + ((r >> 6) * S::NP) * 256 + (r & 63) * 4;
+#pragma unroll
+    for (int c = 0; c < S::KC; ++c)
+      at[c] = real ? *reinterpret_cast<const u32x4_t*>(base + (2 * c + hh) * 256) : (u32x4_t){0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      vt[c] = real ? *reinterpret_cast<const u32x4_t*>(base + (S::AP + 2 * c + hh) * 256) : (u32x4_t){0u, 0u, 0u, 0u};
+  }
+
+  // LDS-direct copy of streamed tile t into the stage at dword `buf`: wave w
+  // copies chunks w and w + 8; lane l writes row l of the chunk.
+  __device__ __forceinline__ void issue(uint32_t* lds, int buf, int t) const {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int cc = wave + NWV * k;
+      if (cc < S::NP) {
+        const unsigned off = (unsigned)(((t * S::NP + cc) * 256 + lane * 4) * 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(other, (__attribute__((address_space(3))) void*)(lds + buf + cc * CS),
+                                                 16, off, 0, 0, 0);
+      }
+    }
+  }
+};
+
 // ---- dq pass -------------------------------------------------------------------
 template <int DH, int R>
 __global__ void __launch_bounds__(RB, 1)
 bwd_dq_bf16_kernel(BwdArgs a, int total) {
   using S = BS<DH, R>;
   __shared__ __attribute__((aligned(16))) uint32_t lds[2 * S::ST_DW];
-  const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
-  if (logical >= total) return;
-  Unit u;
-  if (!decode_unit(logical, a, RB, u)) return;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
-  const int q0 = u.blk * RB;
-  const bool active = q0 + wave * RW < u.n_real;
-  const int C = a.heads * DH;
-  const float sp = LOG2E / sqrtf((float)R), sc = LOG2E / sqrtf((float)DH);
-
-  // query side (own rows): Qt with -lse, dA' with -D
-  const RowSrc qsrc{(const uint32_t*)a.qc, a.qp, nullptr, a.lse};
-  const RowSrc gsrc{nullptr, nullptr, (const uint32_t*)a.da, a.dsum};
-  // key side (streamed): Kt with (1, 1), V' with (1, 1)
-  const RowSrc ksrc{(const uint32_t*)a.kc, a.kp, nullptr, nullptr};
-  const RowSrc vsrc{nullptr, nullptr, (const uint32_t*)a.v, nullptr};
+  Frame<DH, R> f;
+  if (!f.init(a, total, a.pq, a.pk)) return;
+  const int l32 = f.l32, hh = f.hh;
 
   u32x4_t qt[2][S::KC], dat[2][2];
   f32x16_t acc[2][S::MT];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int r = q0 + wave * RW + qb * 32 + l32;
-    const bool real = r < u.n_real;
-    long tok;
-    int n;
-    locate(u, a, real ? r : 0, tok, n);
-    own_row<DH, R, 1>(qsrc, gsrc, tok, n, tok * C + (long)u.h * DH, tok * a.heads + u.h, real, hh, sp, sc, qt[qb],
-                      dat[qb]);
+    f.own_row(f.r0 + qb * 32 + l32, qt[qb], dat[qb]);
 #pragma unroll
     for (int mt = 0; mt < S::MT; ++mt) acc[qb][mt] = zero16();
   }
 
-  Stager<DH, R, 0> stg;
-  stg.wave = wave;
-  stg.lane = lane;
-  const int ntiles = (u.n_real + TT - 1) / TT;
-  stg.load(a, u, ksrc, vsrc, 0);
-  stg.store(lds, sp, sc);
+  f.issue(lds, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  const int trow = tr_lane_base_row(lane), tch = tr_lane_base_ch(lane);
-  const int lb_a = piece_dw<S::KC>(trow, tch);
-  for (int t = 0; t < ntiles; ++t) {
+  const int lb = tr_lane_base(f.lane);
+  for (int t = 0; t < f.ntiles; ++t) {
     const int buf = (t & 1) * S::ST_DW;
-    if (t + 1 < ntiles) stg.load(a, u, ksrc, vsrc, t + 1);
-    if (active) {
+    if (t + 1 < f.ntiles) f.issue(lds, ((t + 1) & 1) * S::ST_DW, t + 1);
+    if (f.active) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         u32x4_t ka[S::KC], va[2], kt[S::MT][2];
 #pragma unroll
         for (int c = 0; c < S::KC; ++c)
-          ka[c] = *reinterpret_cast<const u32x4_t*>(lds + buf + piece_dw<S::KC>(kb * 32 + l32, 16 * c + 8 * hh));
+          ka[c] = *reinterpret_cast<const u32x4_t*>(lds + buf + chunk_dw(2 * c + hh, kb * 32 + l32));
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          va[c] = *reinterpret_cast<const u32x4_t*>(lds + buf + S::A_DW +
-                                                    piece_dw<2>(kb * 32 + l32, 16 * c + 8 * hh));
+          va[c] = *reinterpret_cast<const u32x4_t*>(lds + buf + S::A_DW + chunk_dw(2 * c + hh, kb * 32 + l32));
 #pragma unroll
         for (int mt = 0; mt < S::MT; ++mt)
 #pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) kt[mt][c2] = tr_operand<S::KC>(lds, buf, lb_a, kb * 32 + 16 * c2, 32 * mt);
+          for (int c2 = 0; c2 < 2; ++c2) kt[mt][c2] = tr_operand(lds, buf, lb, kb * 32 + 16 * c2, 32 * mt);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           f32x16_t s = zero16(), d = zero16();
@@ -384,17 +394,19 @@ bwd_dq_bf16_kernel(BwdArgs a, int total) {
         }
       }
     }
-    if (t + 1 < ntiles) stg.store(lds + ((t + 1) & 1) * S::ST_DW, sp, sc);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile have landed
     __syncthreads();
   }
-  if (!active) return;
+  if (!f.active) return;
 
   // ---- epilogue: register e of acc[qb][mt] is column 32mt + 8(e/4) + 4hh + e%4
+  const Unit& u = f.u;
+  const int C = a.heads * DH;
   const float gq = 1.0f / sqrtf((float)R), gc = 1.0f / sqrtf((float)DH);
   uint32_t* dqc = (uint32_t*)a.dqc;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int r = q0 + wave * RW + qb * 32 + l32;
+    const int r = f.r0 + qb * 32 + l32;
     if (r >= u.n_real) continue;
     long tok;
     int n;
@@ -425,68 +437,43 @@ __global__ void __launch_bounds__(RB, 1)
 bwd_dkv_bf16_kernel(BwdArgs a, int total) {
   using S = BS<DH, R>;
   __shared__ __attribute__((aligned(16))) uint32_t lds[2 * S::ST_DW];
-  const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
-  if (logical >= total) return;
-  Unit u;
-  if (!decode_unit(logical, a, RB, u)) return;
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
-  const int k0 = u.blk * RB;
-  const bool active = k0 + wave * RW < u.n_real;
-  const int C = a.heads * DH;
-  const float sp = LOG2E / sqrtf((float)R), sc = LOG2E / sqrtf((float)DH);
-
-  const RowSrc qsrc{(const uint32_t*)a.qc, a.qp, nullptr, a.lse};
-  const RowSrc gsrc{nullptr, nullptr, (const uint32_t*)a.da, a.dsum};
-  const RowSrc ksrc{(const uint32_t*)a.kc, a.kp, nullptr, nullptr};
-  const RowSrc vsrc{nullptr, nullptr, (const uint32_t*)a.v, nullptr};
+  Frame<DH, R> f;
+  if (!f.init(a, total, a.pk, a.pq)) return;
+  const int l32 = f.l32, hh = f.hh;
 
   u32x4_t kt[2][S::KC], vt[2][2];
   f32x16_t accv[2], acck[2][S::MT];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const int r = k0 + wave * RW + kb * 32 + l32;
-    const bool real = r < u.n_real;
-    long tok;
-    int n;
-    locate(u, a, real ? r : 0, tok, n);
-    own_row<DH, R, 0>(ksrc, vsrc, tok, n, tok * C + (long)u.h * DH, 0, real, hh, sp, sc, kt[kb], vt[kb]);
+    f.own_row(f.r0 + kb * 32 + l32, kt[kb], vt[kb]);
     accv[kb] = zero16();
 #pragma unroll
     for (int mt = 0; mt < S::MT; ++mt) acck[kb][mt] = zero16();
   }
 
-  Stager<DH, R, 1> stg;
-  stg.wave = wave;
-  stg.lane = lane;
-  const int ntiles = (u.n_real + TT - 1) / TT;
-  stg.load(a, u, qsrc, gsrc, 0);
-  stg.store(lds, sp, sc);
+  f.issue(lds, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  const int trow = tr_lane_base_row(lane), tch = tr_lane_base_ch(lane);
-  const int lb_a = piece_dw<S::KC>(trow, tch);
-  const int lb_g = piece_dw<2>(trow, tch);
-  for (int t = 0; t < ntiles; ++t) {
+  const int lb = tr_lane_base(f.lane);
+  for (int t = 0; t < f.ntiles; ++t) {
     const int buf = (t & 1) * S::ST_DW;
-    if (t + 1 < ntiles) stg.load(a, u, qsrc, gsrc, t + 1);
-    if (active) {
+    if (t + 1 < f.ntiles) f.issue(lds, ((t + 1) & 1) * S::ST_DW, t + 1);
+    if (f.active) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         u32x4_t qa[S::KC], ga[2], gT[2], qT[S::MT][2];
 #pragma unroll
         for (int c = 0; c < S::KC; ++c)
-          qa[c] = *reinterpret_cast<const u32x4_t*>(lds + buf + piece_dw<S::KC>(qb * 32 + l32, 16 * c + 8 * hh));
+          qa[c] = *reinterpret_cast<const u32x4_t*>(lds + buf + chunk_dw(2 * c + hh, qb * 32 + l32));
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          ga[c] = *reinterpret_cast<const u32x4_t*>(lds + buf + S::A_DW +
-                                                    piece_dw<2>(qb * 32 + l32, 16 * c + 8 * hh));
+          ga[c] = *reinterpret_cast<const u32x4_t*>(lds + buf + S::A_DW + chunk_dw(2 * c + hh, qb * 32 + l32));
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) gT[c2] = tr_operand<2>(lds, buf + S::A_DW, lb_g, qb * 32 + 16 * c2, 0);
+        for (int c2 = 0; c2 < 2; ++c2) gT[c2] = tr_operand(lds, buf + S::A_DW, lb, qb * 32 + 16 * c2, 0);
 #pragma unroll
         for (int mt = 0; mt < S::MT; ++mt)
 #pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) qT[mt][c2] = tr_operand<S::KC>(lds, buf, lb_a, qb * 32 + 16 * c2, 32 * mt);
+          for (int c2 = 0; c2 < 2; ++c2) qT[mt][c2] = tr_operand(lds, buf, lb, qb * 32 + 16 * c2, 32 * mt);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           f32x16_t s = zero16(), d = zero16();
@@ -512,17 +499,19 @@ bwd_dkv_bf16_kernel(BwdArgs a, int total) {
         }
       }
     }
-    if (t + 1 < ntiles) stg.store(lds + ((t + 1) & 1) * S::ST_DW, sp, sc);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  if (!active) return;
+  if (!f.active) return;
 
   // ---- epilogue: register e is row/column 32mt + 8(e/4) + 4hh + e%4 of the key's gradient
+  const Unit& u = f.u;
+  const int C = a.heads * DH;
   uint32_t* dkc = (uint32_t*)a.dkc;
   uint32_t* dvo = (uint32_t*)a.dv;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const int r = k0 + wave * RW + kb * 32 + l32;
+    const int r = f.r0 + kb * 32 + l32;
     if (r >= u.n_real) continue;
     long tok;
     int n;
@@ -559,6 +548,12 @@ bwd_dkv_bf16_kernel(BwdArgs a, int total) {
 
 template <int DH, int R>
 hipError_t launch_variant(const BwdArgs& a, hipStream_t stream) {
+  using S = BS<DH, R>;
+  const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws;
+  const long pack_total = (long)a.B * nWy * nWx * a.heads * a.tu * S::NP * TT;
+  const int pgrid = (int)((pack_total + 255) / 256);
+  hipLaunchKernelGGL((bwd_pack_kernel<DH, R, 0>), dim3(pgrid), dim3(256), 0, stream, a, pack_total);
+  hipLaunchKernelGGL((bwd_pack_kernel<DH, R, 1>), dim3(pgrid), dim3(256), 0, stream, a, pack_total);
   const int total = bwd_units(a, RB);
   const int grid = 8 * ((total + 7) / 8);
   hipLaunchKernelGGL((bwd_dq_bf16_kernel<DH, R>), dim3(grid), dim3(RB), 0, stream, a, total);
@@ -569,6 +564,11 @@ hipError_t launch_variant(const BwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 bool attn_bwd_bf16_supported(int dh, int R) { return (dh == 30 && R == 16) || (dh == 16 && R == 16); }
+
+size_t attn_bwd_bf16_image_bytes(int B, int H, int W, int heads, int ws) {
+  const size_t units = (size_t)B * ((H + ws - 1) / ws) * ((W + ws - 1) / ws) * heads;
+  return units * (size_t)bwd_tiles_per_unit(ws) * 10 * 1024;
+}
 
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
   if (a.dh == 30 && a.R == 16) return launch_variant<30, 16>(a, stream);

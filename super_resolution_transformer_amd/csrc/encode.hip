@@ -103,10 +103,11 @@ hipError_t launch_encode(int ws, int L, int hidden, int R, const float* w, float
 //   dWp_q = sum_n h_n (x) dQp_n,   dWp_k = sum_n h_n (x) dKp_n
 //   dpre_n = (dQp_n Wp_q^T + dKp_n Wp_k^T) * [pre_n > 0]
 //   dW_h = sum_n r_n (x) dpre_n,   db_h = sum_n dpre_n
-// One workgroup handles EB_TOK positions and writes its partial gradient of
-// the whole packed weight vector; a second kernel sums the partials in block
-// order (deterministic, no atomics).  pre_n is recomputed with the forward's
-// exact arithmetic so the ReLU mask matches the forward's.
+// Workgroup g handles the EB_TOK positions of chunk g and writes its partial
+// gradient of the whole packed weight vector to its own row of the workspace;
+// a second kernel sums the rows in a fixed order (deterministic, no atomics).
+// pre_n is recomputed with the forward's exact arithmetic so the ReLU mask
+// matches the forward's.
 constexpr int EB_TOK = 16;
 
 int encode_bwd_blocks(int ws) { return (ws * ws + EB_TOK - 1) / EB_TOK; }
@@ -122,62 +123,72 @@ encode_bwd_kernel(int ws, int L, int hidden, int R, const float* __restrict__ w,
   float* gq = dpre + EB_TOK * hidden;      // [EB_TOK][R]
   float* gk = gq + EB_TOK * R;             // [EB_TOK][R]
   const int N = ws * ws;
-  const int n0 = blockIdx.x * EB_TOK;
-
-  fourier_features(n0, N, ws, L, EB_TOK, F, feat);
-  for (int item = threadIdx.x; item < EB_TOK * R; item += ENC_THREADS) {
-    const int t = item / R, r = item % R;
-    const bool in = n0 + t < N;
-    gq[item] = in ? dqp[(n0 + t) * R + r] : 0.0f;
-    gk[item] = in ? dkp[(n0 + t) * R + r] : 0.0f;
-  }
-  __syncthreads();
-
   const float* Wh = w;
   const float* bh = w + F * hidden;
   const float* Wq = bh + hidden;
   const float* Wk = Wq + hidden * R;
-  for (int item = threadIdx.x; item < EB_TOK * hidden; item += ENC_THREADS) {
-    const int t = item / hidden, j = item % hidden;
-    const float* f = feat + t * F;
-    float acc = bh[j];
-    for (int k = 0; k < F; ++k) acc = fmaf(f[k], Wh[k * hidden + j], acc);
-    float dh = 0.0f;
-    for (int r = 0; r < R; ++r) dh = fmaf(gq[t * R + r], Wq[j * R + r], fmaf(gk[t * R + r], Wk[j * R + r], dh));
-    hid[item] = fmaxf(acc, 0.0f);
-    dpre[item] = acc > 0.0f ? dh : 0.0f;
-  }
-  __syncthreads();
-
   const int nw = F * hidden + hidden + 2 * hidden * R;
   float* out = work + (long)blockIdx.x * nw;
-  for (int item = threadIdx.x; item < nw; item += ENC_THREADS) {
-    float acc = 0.0f;
-    if (item < F * hidden) {
-      const int f = item / hidden, j = item % hidden;
-      for (int t = 0; t < EB_TOK; ++t) acc = fmaf(feat[t * F + f], dpre[t * hidden + j], acc);
-    } else if (item < F * hidden + hidden) {
-      const int j = item - F * hidden;
-      for (int t = 0; t < EB_TOK; ++t) acc += dpre[t * hidden + j];
-    } else {
-      const int k = item - F * hidden - hidden;
-      const bool is_k = k >= hidden * R;
-      const int jr = is_k ? k - hidden * R : k;
-      const int j = jr / R, r = jr % R;
-      const float* gg = is_k ? gk : gq;
-      for (int t = 0; t < EB_TOK; ++t) acc = fmaf(hid[t * hidden + j], gg[t * R + r], acc);
+  {
+    const int chunk = blockIdx.x;
+    const int n0 = chunk * EB_TOK;
+    fourier_features(n0, N, ws, L, EB_TOK, F, feat);
+    for (int item = threadIdx.x; item < EB_TOK * R; item += ENC_THREADS) {
+      const int t = item / R, r = item % R;
+      const bool in = n0 + t < N;
+      gq[item] = in ? dqp[(n0 + t) * R + r] : 0.0f;
+      gk[item] = in ? dkp[(n0 + t) * R + r] : 0.0f;
     }
-    out[item] = acc;
+    __syncthreads();
+    for (int item = threadIdx.x; item < EB_TOK * hidden; item += ENC_THREADS) {
+      const int t = item / hidden, j = item % hidden;
+      const float* f = feat + t * F;
+      float acc = bh[j];
+      for (int k = 0; k < F; ++k) acc = fmaf(f[k], Wh[k * hidden + j], acc);
+      float dh = 0.0f;
+      for (int r = 0; r < R; ++r) dh = fmaf(gq[t * R + r], Wq[j * R + r], fmaf(gk[t * R + r], Wk[j * R + r], dh));
+      hid[item] = fmaxf(acc, 0.0f);
+      dpre[item] = acc > 0.0f ? dh : 0.0f;
+    }
+    __syncthreads();
+    for (int item = threadIdx.x; item < nw; item += ENC_THREADS) {
+      float acc = 0.0f;
+      if (item < F * hidden) {
+        const int f = item / hidden, j = item % hidden;
+        for (int t = 0; t < EB_TOK; ++t) acc = fmaf(feat[t * F + f], dpre[t * hidden + j], acc);
+      } else if (item < F * hidden + hidden) {
+        const int j = item - F * hidden;
+        for (int t = 0; t < EB_TOK; ++t) acc += dpre[t * hidden + j];
+      } else {
+        const int k = item - F * hidden - hidden;
+        const bool is_k = k >= hidden * R;
+        const int jr = is_k ? k - hidden * R : k;
+        const int j = jr / R, r = jr % R;
+        const float* gg = is_k ? gk : gq;
+        for (int t = 0; t < EB_TOK; ++t) acc = fmaf(hid[t * hidden + j], gg[t * R + r], acc);
+      }
+      out[item] = acc;
+    }
   }
 }
 
+// Sum of the workgroup rows: a workgroup takes 16 weights; thread (g, w)
+// adds rows g, g+16, ... of weight w, then group sums are added in order g.
 __global__ void __launch_bounds__(256)
 encode_bwd_reduce_kernel(int nw, int blocks, const float* __restrict__ work, float* __restrict__ dw) {
-  const int item = blockIdx.x * 256 + threadIdx.x;
-  if (item >= nw) return;
+  __shared__ float part[16][17];
+  const int w = threadIdx.x & 15, g = threadIdx.x >> 4;
+  const int item = blockIdx.x * 16 + w;
   float acc = 0.0f;
-  for (int b = 0; b < blocks; ++b) acc += work[(long)b * nw + item];
-  dw[item] = acc;
+  if (item < nw)
+    for (int b = g; b < blocks; b += 16) acc += work[(long)b * nw + item];
+  part[g][w] = acc;
+  __syncthreads();
+  if (g == 0 && item < nw) {
+    float sum = 0.0f;
+    for (int k = 0; k < 16; ++k) sum += part[k][w];
+    dw[item] = sum;
+  }
 }
 
 hipError_t launch_encode_backward(int ws, int L, int hidden, int R, const float* w, const float* dqp,
@@ -188,8 +199,7 @@ hipError_t launch_encode_backward(int ws, int L, int hidden, int R, const float*
   const size_t lds = sizeof(float) * EB_TOK * (size_t)(F + 2 * hidden + 2 * R);
   hipLaunchKernelGGL(encode_bwd_kernel, dim3(blocks), dim3(ENC_THREADS), lds, stream, ws, L, hidden, R, w,
                      dqp, dkp, work);
-  hipLaunchKernelGGL(encode_bwd_reduce_kernel, dim3((nw + 255) / 256), dim3(256), 0, stream, nw, blocks, work,
-                     dw);
+  hipLaunchKernelGGL(encode_bwd_reduce_kernel, dim3((nw + 15) / 16), dim3(256), 0, stream, nw, blocks, work, dw);
   return hipGetLastError();
 }
 

@@ -178,15 +178,16 @@ rib_status rib_cla_gate(const void* x, const float* dw_w, const float* dw_b, con
 }  // extern "C"
 
 namespace {
-// Workspace of rib_window_attn_backward: dA (storage type), D, then the
-// per-row dQp and dKp (fp32), each region 256-byte aligned.
+// Workspace of rib_window_attn_backward: dA (storage type), D, the per-row
+// dQp and dKp (fp32), and on the matrix-core path the two packed operand
+// images; each region 256-byte aligned.
 struct BwdLayout {
-  size_t da, dsum, qrows, krows, total;
+  size_t da, dsum, qrows, krows, pk, pq, total;
 };
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-BwdLayout bwd_layout(int B, int H, int W, int heads, int dh, int R, rib_dtype dtype) {
+BwdLayout bwd_layout(int B, int H, int W, int heads, int dh, int R, int window, rib_dtype dtype) {
   const size_t rows = (size_t)B * H * W * heads;
   const size_t es = dtype == RIB_F32 ? 4 : 2;
   BwdLayout l;
@@ -194,17 +195,23 @@ BwdLayout bwd_layout(int B, int H, int W, int heads, int dh, int R, rib_dtype dt
   l.dsum = up256(rows * dh * es);
   l.qrows = l.dsum + up256(rows * 4);
   l.krows = l.qrows + up256(rows * R * 4);
-  l.total = l.krows + up256(rows * R * 4);
+  l.pk = l.krows + up256(rows * R * 4);
+  const bool mfma = dtype == RIB_BF16 && rib::attn_bwd_bf16_supported(dh, R);
+  const size_t img = mfma ? rib::attn_bwd_bf16_image_bytes(B, H, W, heads, window) : 0;
+  l.pq = l.pk + up256(img);
+  l.total = l.pq + up256(img);
   return l;
 }
 }  // namespace
 
 extern "C" {
 
-size_t rib_window_attn_backward_workspace(int B, int H, int W, int heads, int dh, int R, rib_dtype dtype) {
-  if (B < 1 || H < 1 || W < 1 || heads < 1 || dh < 1 || R < 1 || (dtype != RIB_F32 && dtype != RIB_BF16))
+size_t rib_window_attn_backward_workspace(int B, int H, int W, int heads, int dh, int R, int window,
+                                          rib_dtype dtype) {
+  if (B < 1 || H < 1 || W < 1 || heads < 1 || dh < 1 || R < 1 || window < 2 ||
+      (dtype != RIB_F32 && dtype != RIB_BF16))
     return 0;
-  return bwd_layout(B, H, W, heads, dh, R, dtype).total;
+  return bwd_layout(B, H, W, heads, dh, R, window, dtype).total;
 }
 
 rib_status rib_window_attn_backward(const void* qc, const void* kc, const void* v, const void* g,
@@ -229,7 +236,7 @@ rib_status rib_window_attn_backward(const void* qc, const void* kc, const void* 
   const void* all[] = {qc, kc, v, g, qp, kp, o, lse, dout, dqc, dkc, dv, dg, dqp, dkp, workspace};
   for (const void* p : all)
     if (!aligned(p, 16)) return fail(RIB_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
-  const BwdLayout lay = bwd_layout(B, H, W, heads, dh, R, dtype);
+  const BwdLayout lay = bwd_layout(B, H, W, heads, dh, R, window, dtype);
   if (workspace_bytes < lay.total)
     return fail(RIB_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, lay.total);
   const size_t nb = (size_t)elems * (dtype == RIB_F32 ? 4 : 2);
@@ -244,7 +251,8 @@ rib_status rib_window_attn_backward(const void* qc, const void* kc, const void* 
   char* w = (char*)workspace;
   rib::BwdArgs a{qc, kc, v, g, qp, kp, o, lse, dout, dqc, dkc, dv, dg, dqp, dkp,
                  w + lay.da, (float*)(w + lay.dsum), (float*)(w + lay.qrows), (float*)(w + lay.krows),
-                 B, H, W, heads, dh, R, window};
+                 (uint32_t*)(w + lay.pk), (uint32_t*)(w + lay.pq), B, H, W, heads, dh, R, window,
+                 rib::bwd_tiles_per_unit(window)};
   const hipStream_t st = (hipStream_t)stream;
   const bool bf16 = dtype == RIB_BF16;
   hipError_t e = rib::launch_attn_bwd_prep(a, bf16, st);

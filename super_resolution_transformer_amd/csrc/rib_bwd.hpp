@@ -28,8 +28,13 @@ struct BwdArgs {
   float* dsum;   // D = dO . O per (token, head)
   float* qrows;  // per-row dQp, [heads][B][H][W][R]
   float* krows;  // per-row dKp, same layout
+  uint32_t* pk;  // matrix-core path: packed key-side operand rows (tile images)
+  uint32_t* pq;  // matrix-core path: packed query-side operand rows
   int B, H, W, heads, dh, R, ws;
+  int tu;        // 64-row tiles per unit in the packed images
 };
+
+inline int bwd_tiles_per_unit(int ws) { return (ws * ws + 63) / 64; }
 
 // Decode of a workgroup's logical index into (b, wy, wx, h, row block) and the
 // real-token enumeration of a window: real index r -> (iy, ix) = (r / nx, r % nx).
@@ -70,6 +75,8 @@ hipError_t launch_attn_bwd_rows(const BwdArgs& a, bool bf16, hipStream_t stream)
 hipError_t launch_attn_bwd_reduce(const BwdArgs& a, hipStream_t stream);
 // dq then dkv on bf16 matrix cores; false if (dh, R) has no compiled variant
 bool attn_bwd_bf16_supported(int dh, int R);
+// bytes of one packed operand image (pk or pq) for this problem
+size_t attn_bwd_bf16_image_bytes(int B, int H, int W, int heads, int ws);
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 
 // encoder backward: workspace of encode_bwd_blocks(ws) * weight count floats

@@ -168,18 +168,22 @@ PB = [ctypes.c_void_p(0x10000000 + i * 64 * MB) for i in range(16)]
 def bwd(L, ptrs=None, nbytes=None, B=1, H=8, W=8, heads=2, dh=30, R=16, window=8, dtype=rib.RIB_BF16):
     p = list(ptrs or PB)
     if nbytes is None:
-        nbytes = L.rib_window_attn_backward_workspace(B, H, W, heads, dh, R, dtype)
+        nbytes = L.rib_window_attn_backward_workspace(B, H, W, heads, dh, R, window, dtype)
     return L.rib_window_attn_backward(*p, nbytes, B, H, W, heads, dh, R, window, dtype, None)
 
 
 @fake
 def test_backward_validation(L):
-    need = L.rib_window_attn_backward_workspace(1, 8, 8, 2, 30, 16, rib.RIB_BF16)
-    # dA (bf16) + D + two per-row tables, each region 256-byte aligned
+    need = L.rib_window_attn_backward_workspace(1, 8, 8, 2, 30, 16, 8, rib.RIB_BF16)
+    # dA (bf16) + D + two per-row tables + two packed operand images (matrix-core path:
+    # 2 units x one 64-row tile x 10 chunks x 1 KB), each region 256-byte aligned
     rows = 64 * 2
     up = lambda x: (x + 255) // 256 * 256
-    assert need == up(rows * 30 * 2) + up(rows * 4) + 2 * up(rows * 16 * 4)
-    assert L.rib_window_attn_backward_workspace(0, 8, 8, 2, 30, 16, rib.RIB_BF16) == 0
+    assert need == up(rows * 30 * 2) + up(rows * 4) + 2 * up(rows * 16 * 4) + 2 * 2 * 10 * 1024
+    f32 = L.rib_window_attn_backward_workspace(1, 8, 8, 2, 30, 16, 8, rib.RIB_F32)
+    assert f32 == up(rows * 30 * 4) + up(rows * 4) + 2 * up(rows * 16 * 4)      # no images on the fp32 path
+    assert L.rib_window_attn_backward_workspace(0, 8, 8, 2, 30, 16, 8, rib.RIB_BF16) == 0
+    assert L.rib_window_attn_backward_workspace(1, 8, 8, 2, 30, 16, 1, rib.RIB_BF16) == 0
     assert bwd(L, [None] + PB[1:]) == rib.RIB_ERR_INVALID_ARG
     assert "null" in L.rib_last_error().decode()
     assert bwd(L, PB[:15] + [None]) == rib.RIB_ERR_INVALID_ARG
