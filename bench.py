@@ -8,7 +8,9 @@ training-patch forward: 32 images of 96x96 tokens, C = 180 (6 heads x 30),
 R = 16, one 96x96 window per image.  Secondary figures for the 64x64 window
 (1x180x320, C = 180), the 640x360 input with 96x96 windows, and the 16x16
 window of the SST-lite map (HBM-bound) are reported in the same JSON line, and so is the
-CLA gate producer (rib_cla_gate, HBM-bound) on the same maps.
+CLA gate producer (rib_cla_gate, HBM-bound) on the same maps, and the
+training iteration of the attention (rib_window_attn_train + rib_window_attn_backward +
+rib_encode_backward) on the 96x96 and 64x64 workloads.
 
 Prints ONE JSON line.  Timing: HIP events on the stream the kernels run on.
 """
@@ -172,6 +174,65 @@ def time_gate(torch, rib, synthetic):
     return res
 
 
+def time_backward(torch, rib, synthetic, cfg_idx, ws, reps):
+    """Training iteration of the attention on one workload: rib_window_attn_train (O and the row
+    log-sum-exp), rib_window_attn_backward (dQc, dKc, dV, dG, dQp, dKp) and rib_encode_backward
+    (the encoder's weight gradient).  Inputs, outputs and workspaces are allocated before timing.
+    Algorithmic flops of the backward per score pair: recomputed scores 2(dh+R), dP = dA V^T 2dh,
+    dV = P^T dA 2dh, dQt = dS Kt 2(dh+R), dKt = dS^T Qt 2(dh+R)."""
+    c = synthetic.CONFIGS[cfg_idx]
+    p = synthetic.config_problem(cfg_idx)
+    bf = lambda bits: torch.from_numpy(bits.view("int16")).view(torch.bfloat16).cuda()
+    maps = [bf(p.bits[n]) for n in ("qc", "kc", "v", "g")]
+    w = torch.from_numpy(p.weights).cuda()
+    qp, kp = rib.encode(ws, c.L, c.hidden, c.R, w)
+    _, dbits = synthetic.make_upstream_grad(p.qc.shape, "bf16", seed=1)
+    dout = bf(dbits)
+    o, lse = rib.window_attn_train(*maps, qp, kp, c.heads, ws)
+    grads = [torch.empty_like(maps[0]) for _ in range(4)] + [torch.empty_like(qp), torch.empty_like(kp)]
+    work = torch.empty(rib.backward_workspace_bytes(maps[0], qp, c.heads, ws), dtype=torch.uint8, device="cuda")
+    dw = torch.empty_like(w)
+    ework = torch.empty(max(16, rib.lib().rib_encode_backward_workspace(ws, c.L, c.hidden, c.R)),
+                        dtype=torch.uint8, device="cuda")
+
+    def fwd():
+        rib.window_attn_train_into(*maps, qp, kp, c.heads, ws, o, lse)
+
+    def bwd():
+        rib.window_attn_backward_into(*maps, qp, kp, o, lse, dout, c.heads, ws, *grads, work)
+
+    def ebwd():
+        rib.encode_backward_into(ws, c.L, c.hidden, c.R, w, grads[4], grads[5], dw, ework)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    ms_f, ms_b, ms_e = timed(fwd), timed(bwd), timed(ebwd)
+    E, F, _ = algorithmic(c.B, c.H, c.W, c.heads, c.dh, c.R, ws, 2)
+    Fb = E * (6 * (c.dh + c.R) + 4 * c.dh)
+    tf_b = Fb / (ms_b * 1e-3) / 1e12
+    tokens = c.B * c.H * c.W
+    ms_step = ms_f + ms_b + ms_e
+    return {"workload": f"{c.name}: {c.B} x {c.H}x{c.W}, C={c.C} ({c.heads} heads x dh {c.dh}), R={c.R}, "
+                        f"{ws}x{ws} windows",
+            "ms_train_forward": ms_f, "ms_backward": ms_b, "ms_encode_backward": ms_e,
+            "ms_train_step": ms_step, "train_tokens_per_s": tokens / (ms_step * 1e-3),
+            "backward_tflops": tf_b, "backward_pct_bf16_peak": 100 * tf_b / PEAK_BF16_TFLOPS,
+            "backward_algorithmic_flop": Fb,
+            "roofline": {"bound": "mfma", "achieved": tf_b, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf_b / PEAK_BF16_TFLOPS, "traffic": None,
+                         "kernel": "rib_window_attn_backward (prep, two packs, dq, dkv, table reduce)"}}
+
+
 def cpu_baseline(synthetic, cfg_idx, ws, units_sample):
     """The fp64 oracle as it stands, on the host cores, over a bounded sample of
     (image, window, head) units of the same workload, scaled to tokens/s."""
@@ -206,6 +267,9 @@ def main():
                     help="oracle sample size in window-head units (default: 2 per oracle thread)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the training iteration (train forward + backward) on the 96x96 workload")
+    ap.add_argument("--backward-reps", type=int, default=10, help="timed repetitions per backward call")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -220,6 +284,11 @@ def main():
     from super_resolution_transformer_amd import synthetic
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rib.lib()
+
+    if args.backward_only:
+        print(json.dumps({"backward": {"96x96 window, 32x96x96": time_backward(torch, rib, synthetic, 4, 96,
+                                                                                args.backward_reps)}}), flush=True)
+        return
 
     # ---- headline workload: 32 x 96x96 patches, 96x96 window
     wl = Workload(torch, rib, synthetic, 4, 96)
@@ -277,6 +346,10 @@ def main():
 
     if not args.no_extra:
         out["cla_gate"] = time_gate(torch, rib, synthetic)
+        out["backward"] = {"96x96 window, 32x96x96": time_backward(torch, rib, synthetic, 4, 96, args.backward_reps),
+                           "64x64 window, 1x180x320": time_backward(torch, rib, synthetic, 3, 64,
+                                                                    3 * args.backward_reps)}
+        torch.cuda.empty_cache()
 
     if args.copy_calibration:
         x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")

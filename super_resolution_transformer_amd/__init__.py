@@ -171,10 +171,19 @@ def window_attn_train(qc, kc, v, g, qp, kp, heads: int, window: int):
     """window_attn plus the row log-sum-exp the backward needs: returns (o, lse), lse float32
     [B, H, W, heads] (natural log)."""
     import torch
-    ts = (qc, kc, v, g)
+    B, H, W, C = qc.shape
+    o = torch.empty_like(qc)
+    lse = torch.empty((B, H, W, max(heads, 1)), dtype=torch.float32, device=qc.device)
+    window_attn_train_into(qc, kc, v, g, qp, kp, heads, window, o, lse)
+    return o, lse
+
+
+def window_attn_train_into(qc, kc, v, g, qp, kp, heads: int, window: int, o, lse) -> None:
+    import torch
+    ts = (qc, kc, v, g, o)
     if any(t.dim() != 4 or t.shape != qc.shape or t.dtype != qc.dtype for t in ts):
-        raise ValueError("qc, kc, v, g must all be [B, H, W, C] of one dtype")
-    if not all(t.is_cuda and t.is_contiguous() for t in ts + (qp, kp)):
+        raise ValueError("qc, kc, v, g, o must all be [B, H, W, C] of one dtype")
+    if not all(t.is_cuda and t.is_contiguous() for t in ts + (qp, kp, lse)):
         raise ValueError("all tensors must be contiguous GPU tensors")
     if qp.dtype != torch.float32 or kp.dtype != torch.float32 or qp.shape != kp.shape or qp.dim() != 2:
         raise ValueError("qp, kp must be float32 [window*window, R]")
@@ -183,12 +192,11 @@ def window_attn_train(qc, kc, v, g, qp, kp, heads: int, window: int):
     B, H, W, C = qc.shape
     if heads < 1 or C % heads:
         raise ValueError("channel count must be a multiple of heads")
-    o = torch.empty_like(qc)
-    lse = torch.empty((B, H, W, heads), dtype=torch.float32, device=qc.device)
+    if lse.shape != (B, H, W, heads) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, W, heads]")
     _check(lib().rib_window_attn_train(_ptr(qc), _ptr(kc), _ptr(v), _ptr(g), _ptr(qp), _ptr(kp), _ptr(o), _ptr(lse),
                                        B, H, W, heads, C // heads, qp.shape[1], window, _dtype_code(qc),
                                        _stream(qc)))
-    return o, lse
 
 
 def cla_gate(x, dw_w, dw_b, pw_w, pw_b):
@@ -223,15 +231,35 @@ def window_attn_backward(qc, kc, v, g, qp, kp, o, lse, dout, heads: int, window:
     temporary torch buffer.
     """
     import torch
-    ts = (qc, kc, v, g, o, dout)
+    outs = [torch.empty_like(qc) for _ in range(4)]
+    dqp, dkp = torch.empty_like(qp), torch.empty_like(kp)
+    work = torch.empty(max(backward_workspace_bytes(qc, qp, heads, window), 16), dtype=torch.uint8,
+                       device=qc.device)
+    window_attn_backward_into(qc, kc, v, g, qp, kp, o, lse, dout, heads, window, *outs, dqp, dkp, work)
+    return (*outs, dqp, dkp)
+
+
+def backward_workspace_bytes(qc, qp, heads: int, window: int) -> int:
+    """Bytes of device workspace window_attn_backward_into needs for maps like qc."""
+    B, H, W, C = qc.shape
+    return lib().rib_window_attn_backward_workspace(B, H, W, heads, C // heads, qp.shape[-1], window,
+                                                    _dtype_code(qc))
+
+
+def window_attn_backward_into(qc, kc, v, g, qp, kp, o, lse, dout, heads: int, window: int,
+                              dqc, dkc, dv, dg, dqp, dkp, work) -> None:
+    """window_attn_backward into caller buffers; work is a uint8 device buffer of at least
+    backward_workspace_bytes() bytes."""
+    import torch
+    ts = (qc, kc, v, g, o, dout, dqc, dkc, dv, dg)
     if any(t.dim() != 4 or t.shape != qc.shape or t.dtype != qc.dtype for t in ts):
-        raise ValueError("qc, kc, v, g, o, dout must all be [B, H, W, C] of one dtype")
-    if not all(t.is_cuda and t.is_contiguous() for t in ts + (qp, kp)):
+        raise ValueError("qc, kc, v, g, o, dout and the map gradients must all be [B, H, W, C] of one dtype")
+    if not all(t.is_cuda and t.is_contiguous() for t in ts + (qp, kp, dqp, dkp, work)):
         raise ValueError("all tensors must be contiguous GPU tensors")
     if qp.dtype != torch.float32 or kp.dtype != torch.float32 or qp.shape != kp.shape or qp.dim() != 2:
         raise ValueError("qp, kp must be float32 [window*window, R]")
-    if qp.shape[0] != window * window:
-        raise ValueError("qp, kp must have window*window rows")
+    if qp.shape[0] != window * window or dqp.shape != qp.shape or dkp.shape != qp.shape:
+        raise ValueError("qp, kp, dqp, dkp must have window*window rows of R")
     B, H, W, C = qc.shape
     if heads < 1 or C % heads:
         raise ValueError("channel count must be a multiple of heads")
@@ -239,33 +267,36 @@ def window_attn_backward(qc, kc, v, g, qp, kp, o, lse, dout, heads: int, window:
         raise ValueError("lse must be a contiguous float32 GPU tensor [B, H, W, heads]")
     dh, R = C // heads, qp.shape[1]
     code = _dtype_code(qc)
-    outs = [torch.empty_like(qc) for _ in range(4)]
-    dqp, dkp = torch.empty_like(qp), torch.empty_like(kp)
-    nbytes = lib().rib_window_attn_backward_workspace(B, H, W, heads, dh, R, window, code)
-    work = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=qc.device)
+    nbytes = work.numel() * work.element_size()
     _check(lib().rib_window_attn_backward(*[_ptr(t) for t in ts[:4]], _ptr(qp), _ptr(kp), _ptr(o), _ptr(lse),
-                                          _ptr(dout),
-                                          *[_ptr(t) for t in outs], _ptr(dqp), _ptr(dkp), _ptr(work), nbytes,
-                                          B, H, W, heads, dh, R, window, code, _stream(qc)))
-    return (*outs, dqp, dkp)
+                                          _ptr(dout), _ptr(dqc), _ptr(dkc), _ptr(dv), _ptr(dg), _ptr(dqp),
+                                          _ptr(dkp), _ptr(work), nbytes, B, H, W, heads, dh, R, window, code,
+                                          _stream(qc)))
 
 
 def encode_backward(window: int, L: int, hidden: int, R: int, weights, dqp, dkp):
     """Gradient of the packed encoder weights for upstream (dqp, dkp); float32 like weights."""
     import torch
-    ts = (weights, dqp, dkp)
+    dw = torch.empty_like(weights)
+    work = torch.empty(max(lib().rib_encode_backward_workspace(window, L, hidden, R), 16), dtype=torch.uint8,
+                       device=weights.device)
+    encode_backward_into(window, L, hidden, R, weights, dqp, dkp, dw, work)
+    return dw
+
+
+def encode_backward_into(window: int, L: int, hidden: int, R: int, weights, dqp, dkp, dw, work) -> None:
+    import torch
+    ts = (weights, dqp, dkp, dw)
     if not all(t.is_cuda and t.is_contiguous() and t.dtype == torch.float32 for t in ts):
-        raise ValueError("weights, dqp, dkp must be contiguous float32 GPU tensors")
-    if weights.numel() != weight_count(L, hidden, R):
+        raise ValueError("weights, dqp, dkp, dw must be contiguous float32 GPU tensors")
+    if weights.numel() != weight_count(L, hidden, R) or dw.numel() != weights.numel():
         raise ValueError("packed weight vector has the wrong length")
     if dqp.shape != (window * window, R) or dkp.shape != (window * window, R):
         raise ValueError("dqp, dkp must be [window*window, R]")
-    dw = torch.empty_like(weights)
-    nbytes = lib().rib_encode_backward_workspace(window, L, hidden, R)
-    work = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=weights.device)
+    if not (work.is_cuda and work.is_contiguous()):
+        raise ValueError("work must be a contiguous GPU buffer")
     _check(lib().rib_encode_backward(window, L, hidden, R, _ptr(weights), _ptr(dqp), _ptr(dkp), _ptr(dw),
-                                     _ptr(work), nbytes, _stream(weights)))
-    return dw
+                                     _ptr(work), work.numel() * work.element_size(), _stream(weights)))
 
 
 def supported(dh: int, R: int, window: int, dtype) -> bool:
