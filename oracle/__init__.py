@@ -68,6 +68,8 @@ def _configure(L):
     L.rib_oracle_window_debug.restype = ctypes.c_int
     L.rib_oracle_cla_gate.argtypes = [_D] * 5 + [ctypes.c_int] * 4 + [_D]
     L.rib_oracle_cla_gate.restype = ctypes.c_int
+    L.rib_oracle_ln_qkv.argtypes = [_D] * 5 + [ctypes.c_int] * 4 + [ctypes.c_double] + [_D] * 4
+    L.rib_oracle_ln_qkv.restype = ctypes.c_int
     L.rib_oracle_attn_lse.argtypes = [_D] * 4 + [ctypes.c_int] * 7 + [_D]
     L.rib_oracle_attn_lse.restype = ctypes.c_int
     L.rib_oracle_attn_backward.argtypes = [_D] * 7 + [ctypes.c_int] * 7 + [_D] * 6
@@ -267,3 +269,20 @@ def encode_backward(window: int, L: int, hidden: int, R: int, weights, dqp, dkp)
     if lib().rib_oracle_encode_backward(window, L, hidden, R, _p(w), _p(dqp), _p(dkp), _p(dw)) != 0:
         raise ValueError("oracle encode backward rejected its arguments")
     return dw
+
+
+def ln_qkv(x, gamma, beta, w, bias, eps: float = 1e-5, with_xn: bool = False):
+    """(q, k, v[, xn]) of the block's input projection: LayerNorm over channels, then x W + bias
+    with w [C][3C] (columns Q | K | V); NHWC float64."""
+    x = _f64(x)
+    B, H, W, C = x.shape
+    gamma, beta, w, bias = (_f64(a) for a in (gamma, beta, w, bias))
+    if gamma.shape != (C,) or beta.shape != (C,) or w.shape != (C, 3 * C) or bias.shape != (3 * C,):
+        raise ValueError("gamma, beta [C], w [C, 3C], bias [3C] expected")
+    q, k, v = (np.zeros(x.shape, np.float64) for _ in range(3))
+    xn = np.zeros(x.shape, np.float64) if with_xn else None
+    rc = lib().rib_oracle_ln_qkv(_p(x), _p(gamma), _p(beta), _p(w), _p(bias), B, H, W, C, float(eps),
+                                 _p(q), _p(k), _p(v), _p(xn) if with_xn else None)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return (q, k, v, xn) if with_xn else (q, k, v)

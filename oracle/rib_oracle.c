@@ -644,3 +644,53 @@ int rib_oracle_encode_backward(int ws, int L, int hidden, int R, const double* w
   free(pre);
   return 0;
 }
+
+/*
+ * The attention's input projection in an SST block (explainer section 3.1:
+ * each block applies LayerNorm, then RIB attention): per token (b, y, x) with
+ * channels x_c, c < C,
+ *   mu = (1/C) sum_c x_c,  var = (1/C) sum_c (x_c - mu)^2        (biased variance)
+ *   xn_c = (x_c - mu) / sqrt(var + eps) * gamma_c + beta_c
+ *   [q | k | v]_o = bias_o + sum_c xn_c * w[c][o],  o < 3C       (y = x W)
+ * q, k, v are NHWC [B][H][W][C]; xn (if not NULL) receives LN(X), the input
+ * the gate producer reads.
+ */
+int rib_oracle_ln_qkv(const double* x, const double* gamma, const double* beta, const double* w,
+                      const double* bias, int B, int H, int W, int C, double eps, double* q, double* k,
+                      double* v, double* xn) {
+  if (!x || !gamma || !beta || !w || !bias || !q || !k || !v || B < 1 || H < 1 || W < 1 || C < 1 || !(eps >= 0.0))
+    return -1;
+  const long ntok = (long)B * H * W;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double* row = (double*)malloc(sizeof(double) * C);
+    if (!row) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(static)
+      for (long t = 0; t < ntok; ++t) {
+        const double* xt = x + t * C;
+        double mu = 0.0;
+        for (int c = 0; c < C; ++c) mu += xt[c];
+        mu /= C;
+        double var = 0.0;
+        for (int c = 0; c < C; ++c) var += (xt[c] - mu) * (xt[c] - mu);
+        var /= C;
+        const double inv = 1.0 / sqrt(var + eps);
+        for (int c = 0; c < C; ++c) row[c] = (xt[c] - mu) * inv * gamma[c] + beta[c];
+        if (xn)
+          for (int c = 0; c < C; ++c) xn[t * C + c] = row[c];
+        for (int o = 0; o < 3 * C; ++o) {
+          double acc = bias[o];
+          for (int c = 0; c < C; ++c) acc += row[c] * w[(size_t)c * 3 * C + o];
+          double* dst = o < C ? q : (o < 2 * C ? k : v);
+          dst[t * C + o % C] = acc;
+        }
+      }
+    }
+    free(row);
+  }
+  return fail ? -1 : 0;
+}

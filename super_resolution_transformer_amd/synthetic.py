@@ -164,3 +164,35 @@ def make_upstream_grad(shape, dtype: str = "bf16", seed: int = 0) -> tuple[np.nd
         bits, x = round_bf16(x)
         return x, bits
     return x, None
+
+
+@dataclass
+class LnQkvProblem:
+    """Inputs of the block's input projection (LayerNorm, then X W + b into Q | K | V)."""
+    x: np.ndarray                 # [B, H, W, C] exact values (bf16-representable when dtype is bf16)
+    gamma: np.ndarray             # [C]
+    beta: np.ndarray              # [C]
+    w: np.ndarray                 # [C, 3C]  (y = x W; columns Q | K | V)
+    bias: np.ndarray              # [3C]
+    dtype: str
+    x_bits: np.ndarray | None = None
+
+
+def make_ln_qkv_problem(B: int, H: int, W: int, C: int, dtype: str = "bf16", seed: int = 0) -> LnQkvProblem:
+    """Block input with a per-token offset and scale (so the normalisation has work to do):
+    x = a_t + s_t * z, a_t ~ N(0, 1), s_t = exp(N(0, 0.5^2)), z ~ N(0, 1); LayerNorm affine
+    gamma = 1 + N(0, 0.1^2), beta ~ N(0, 0.1^2); projection W ~ N(0, 1/C), bias ~ N(0, 0.1^2)."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((B, H, W, 1))
+    s = np.exp(0.5 * rng.standard_normal((B, H, W, 1)))
+    x = (a + s * rng.standard_normal((B, H, W, C))).astype(np.float32)
+    gamma = (1.0 + 0.1 * rng.standard_normal(C)).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(C)).astype(np.float32)
+    w = (rng.standard_normal((C, 3 * C)) / np.sqrt(C)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(3 * C)).astype(np.float32)
+    bits = None
+    if dtype == "bf16":
+        bits, x = round_bf16(x)
+    elif dtype != "f32":
+        raise ValueError("dtype must be 'f32' or 'bf16'")
+    return LnQkvProblem(x, gamma, beta, w, bias, dtype, bits)
