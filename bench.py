@@ -8,7 +8,8 @@ training-patch forward: 32 images of 96x96 tokens, C = 180 (6 heads x 30),
 R = 16, one 96x96 window per image.  Secondary figures for the 64x64 window
 (1x180x320, C = 180), the 640x360 input with 96x96 windows, and the 16x16
 window of the SST-lite map (HBM-bound) are reported in the same JSON line, and so is the
-CLA gate producer (rib_cla_gate, HBM-bound) on the same maps, and the
+CLA gate producer (rib_cla_gate, HBM-bound) and the LayerNorm + Q/K/V projection
+(rib_ln_qkv, HBM-bound) on the same maps, and the
 training iteration of the attention (rib_window_attn_train + rib_window_attn_backward +
 rib_encode_backward) on the 96x96 and 64x64 workloads.
 
@@ -170,6 +171,40 @@ def time_gate(torch, rib, synthetic):
                      "pct_hbm": 100 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "tflops": flops / (ms * 1e-3) / 1e12, "tokens_per_s": B * H * W / (ms * 1e-3)}
         del xs, gs
+        torch.cuda.empty_cache()
+    return res
+
+
+def time_ln_qkv(torch, rib, synthetic):
+    """Block input projection (rib_ln_qkv: LayerNorm, then x W + b into Q | K | V, plus LN(X) for the
+    gate) on the workloads' maps, bf16; HBM roofline.  Algorithmic bytes: X read, Q, K, V and LN(X)
+    written (bf16) + fp32 parameters; input sets rotate."""
+    res = {}
+    for name, (B, H, W, C, copies) in (("32x96x96, C=180", (32, 96, 96, 180, 2)),
+                                       ("1x360x640, C=180", (1, 360, 640, 180, 3)),
+                                       ("1x180x320, C=48", (1, 180, 320, 48, 40))):
+        p = synthetic.make_ln_qkv_problem(B, H, W, C, "bf16", seed=3)
+        x0 = torch.from_numpy(p.x_bits.view("int16")).view(torch.bfloat16).cuda()
+        xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+        outs = [[torch.empty_like(x0) for _ in range(4)] for _ in range(copies)]
+        w = [torch.from_numpy(a).cuda() for a in (p.gamma, p.beta, p.w, p.bias)]
+        reps = max(100, 2 * copies)
+        for i in range(copies):
+            rib.ln_qkv_into(xs[i], *w, *outs[i])
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(reps):
+            rib.ln_qkv_into(xs[i % copies], *w, *outs[i % copies])
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        nbytes = 5 * B * H * W * C * 2 + 4 * (2 * C + 3 * C * C + 3 * C)
+        flops = B * H * W * 2 * C * 3 * C
+        res[name] = {"ms": ms, "alg_gbs": nbytes / (ms * 1e-3) / 1e9,
+                     "pct_hbm": 100 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "tflops": flops / (ms * 1e-3) / 1e12, "tokens_per_s": B * H * W / (ms * 1e-3)}
+        del xs, outs
         torch.cuda.empty_cache()
     return res
 
@@ -346,6 +381,7 @@ def main():
 
     if not args.no_extra:
         out["cla_gate"] = time_gate(torch, rib, synthetic)
+        out["ln_qkv"] = time_ln_qkv(torch, rib, synthetic)
         out["backward"] = {"96x96 window, 32x96x96": time_backward(torch, rib, synthetic, 4, 96, args.backward_reps),
                            "64x64 window, 1x180x320": time_backward(torch, rib, synthetic, 3, 64,
                                                                     3 * args.backward_reps)}

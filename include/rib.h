@@ -215,6 +215,29 @@ rib_status rib_encode_backward(int window, int L, int hidden, int R, const float
                                const float* dkp, float* dweights, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/*
+ * rib_ln_qkv -- the attention's input projection in an SST block (explainer
+ * section 3.1: each block runs LayerNorm, then the RIB attention), per token:
+ *   mu = mean_c x_c,  var = mean_c (x_c - mu)^2         (biased variance)
+ *   xn_c = (x_c - mu) / sqrt(var + eps) * gamma_c + beta_c
+ *   [q | k | v] = xn W + bias                           (y = x W, W [C][3C])
+ * x, q, k, v : device, [B][H][W][C] of `dtype` (x read; q, k, v written) --
+ *              q, k, v are the qc, kc, v arguments of rib_window_attn.
+ * xn         : device, like x, or NULL; receives LN(X) (the gate producer's
+ *              input in this reading of the block).
+ * gamma, beta: device float32 [C]; w: device float32 [C][3C], columns Q | K | V;
+ *              bias: device float32 [3C].
+ * dtype      : RIB_F32 -- fp32 throughout.  RIB_BF16 -- LayerNorm in fp32,
+ *              xn and W rounded to bf16, the product on bf16 matrix cores
+ *              with fp32 accumulation, outputs rounded to bf16.
+ * Outputs must not overlap each other or any input.
+ * Limits : C <= 256 (even for bf16); B*H*W*C < 2^30; pointers 16-byte
+ *          aligned; 0 <= eps <= 1.
+ */
+rib_status rib_ln_qkv(const void* x, const float* gamma, const float* beta, const float* w, const float* bias,
+                      void* q, void* k, void* v, void* xn, int B, int H, int W, int C, float eps, rib_dtype dtype,
+                      void* stream);
+
 /* Text describing the last non-OK status returned on this thread ("" if none).
  * The pointer stays valid until the next library call on the same thread. */
 const char* rib_last_error(void);
@@ -222,7 +245,7 @@ const char* rib_last_error(void);
 /* ABI version of this header (incremented on any incompatible change). */
 int rib_abi_version(void);
 
-#define RIB_ABI_VERSION 5
+#define RIB_ABI_VERSION 6
 
 #ifdef __cplusplus
 }

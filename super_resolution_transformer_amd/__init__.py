@@ -69,6 +69,8 @@ def lib(path: str | None = None):
     L.rib_encode_backward_workspace.restype = sz
     L.rib_encode_backward.argtypes = [i] * 4 + [vp] * 5 + [sz, vp]
     L.rib_encode_backward.restype = i
+    L.rib_ln_qkv.argtypes = [vp] * 9 + [i] * 4 + [ctypes.c_float, i, vp]
+    L.rib_ln_qkv.restype = i
     L.rib_attn_supported.argtypes = [i, i, i, i]
     L.rib_attn_supported.restype = i
     L.rib_last_error.argtypes = []
@@ -297,6 +299,34 @@ def encode_backward_into(window: int, L: int, hidden: int, R: int, weights, dqp,
         raise ValueError("work must be a contiguous GPU buffer")
     _check(lib().rib_encode_backward(window, L, hidden, R, _ptr(weights), _ptr(dqp), _ptr(dkp), _ptr(dw),
                                      _ptr(work), work.numel() * work.element_size(), _stream(weights)))
+
+
+def ln_qkv(x, gamma, beta, w, bias, eps: float = 1e-5, with_xn: bool = False):
+    """(q, k, v[, xn]) = LayerNorm(x) W + bias split into Q | K | V, for an NHWC map x
+    (w float32 [C, 3C], gamma/beta [C], bias [3C])."""
+    import torch
+    outs = [torch.empty_like(x) for _ in range(4 if with_xn else 3)]
+    ln_qkv_into(x, gamma, beta, w, bias, *outs[:3], outs[3] if with_xn else None, eps)
+    return tuple(outs)
+
+
+def ln_qkv_into(x, gamma, beta, w, bias, q, k, v, xn=None, eps: float = 1e-5) -> None:
+    import torch
+    if x.dim() != 4:
+        raise ValueError("x must be [B, H, W, C]")
+    B, H, W, C = x.shape
+    maps = [t for t in (q, k, v, xn) if t is not None]
+    if any(t.shape != x.shape or t.dtype != x.dtype for t in maps):
+        raise ValueError("q, k, v (and xn) must match x in shape and dtype")
+    ws = (gamma, beta, w, bias)
+    if any(t.dtype != torch.float32 for t in ws):
+        raise ValueError("gamma, beta, w, bias must be float32")
+    if gamma.shape != (C,) or beta.shape != (C,) or w.shape != (C, 3 * C) or bias.shape != (3 * C,):
+        raise ValueError("gamma, beta [C], w [C, 3C], bias [3C] expected")
+    if not all(t.is_cuda and t.is_contiguous() for t in ws + (x, *maps)):
+        raise ValueError("all tensors must be contiguous GPU tensors")
+    _check(lib().rib_ln_qkv(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(w), _ptr(bias), _ptr(q), _ptr(k), _ptr(v),
+                            _ptr(xn) if xn is not None else None, B, H, W, C, float(eps), _dtype_code(x), _stream(x)))
 
 
 def supported(dh: int, R: int, window: int, dtype) -> bool:

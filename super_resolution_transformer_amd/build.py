@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librib.so")
-SOURCES = ["rib_api.cpp", "encode.hip", "attn_f32.hip", "attn_bf16.hip", "cla_gate.hip", "attn_bwd.hip", "attn_bwd_bf16.hip"]
+SOURCES = ["rib_api.cpp", "encode.hip", "attn_f32.hip", "attn_bf16.hip", "cla_gate.hip", "ln_qkv.hip", "attn_bwd.hip", "attn_bwd_bf16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

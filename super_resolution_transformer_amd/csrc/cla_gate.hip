@@ -286,6 +286,16 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
   }
 }
 
+
+template <int NB>
+hipError_t launch_gate_bf16(const GateArgs& a, int nseg, long ntiles, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((cla_gate_bf16_kernel<NB>), dim3(grid), dim3(GateShape<NB>::NT), 0, stream, (const uint32_t*)a.x,
+                     a.dw_w, a.dw_b, a.pw_w, a.pw_b, (uint32_t*)a.g, a.B, a.H, a.W, a.C, nseg, ntiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 int device_cus() {
   static int cus = 0;
   if (cus == 0) {
@@ -297,15 +307,6 @@ int device_cus() {
   }
   return cus;
 }
-
-template <int NB>
-hipError_t launch_gate_bf16(const GateArgs& a, int nseg, long ntiles, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((cla_gate_bf16_kernel<NB>), dim3(grid), dim3(GateShape<NB>::NT), 0, stream, (const uint32_t*)a.x,
-                     a.dw_w, a.dw_b, a.pw_w, a.pw_b, (uint32_t*)a.g, a.B, a.H, a.W, a.C, nseg, ntiles);
-  return hipGetLastError();
-}
-
-}  // namespace
 
 hipError_t launch_cla_gate(const GateArgs& a, bool bf16, hipStream_t stream) {
   const int nseg = (a.W + GT - 1) / GT;

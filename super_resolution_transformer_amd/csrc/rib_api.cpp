@@ -298,3 +298,36 @@ rib_status rib_encode_backward(int window, int L, int hidden, int R, const float
 }
 
 }  // extern "C"
+
+extern "C" {
+
+rib_status rib_ln_qkv(const void* x, const float* gamma, const float* beta, const float* w, const float* bias,
+                      void* q, void* k, void* v, void* xn, int B, int H, int W, int C, float eps, rib_dtype dtype,
+                      void* stream) {
+  const char* fn = "rib_ln_qkv";
+  if (!x || !gamma || !beta || !w || !bias || !q || !k || !v) return fail(RIB_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (B < 1 || H < 1 || W < 1 || C < 1)
+    return fail(RIB_ERR_INVALID_ARG, "%s: B, H, W, C must be >= 1 (got %d, %d, %d, %d)", fn, B, H, W, C);
+  if (dtype != RIB_F32 && dtype != RIB_BF16) return fail(RIB_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (!(eps >= 0.0f) || eps > 1.0f) return fail(RIB_ERR_INVALID_ARG, "%s: eps must be in [0, 1]", fn);
+  if (C > 256 || (dtype == RIB_BF16 && C % 2 != 0))
+    return fail(RIB_ERR_UNSUPPORTED, "%s: C must be <= 256 (and even for bf16), got %d", fn, C);
+  const size_t elems = (size_t)B * H * W * C;
+  if (elems >= ((size_t)1 << 30)) return fail(RIB_ERR_UNSUPPORTED, "%s: B*H*W*C must be < 2^30", fn);
+  const void* all[] = {x, q, k, v, xn, gamma, beta, w, bias};
+  for (const void* p : all)
+    if (p && !aligned(p, 16)) return fail(RIB_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+  const size_t nm = elems * (dtype == RIB_F32 ? 4 : 2);
+  const size_t sizes[] = {nm, nm, nm, nm, nm, 4 * (size_t)C, 4 * (size_t)C, 12 * (size_t)C * C, 12 * (size_t)C};
+  // outputs (1..4) are disjoint from every other buffer
+  for (int i = 1; i < 5; ++i) {
+    if (!all[i]) continue;
+    for (int j = 0; j < 9; ++j)
+      if (j != i && all[j] && overlap(all[i], sizes[i], all[j], sizes[j]))
+        return fail(RIB_ERR_INVALID_ARG, "%s: an output overlaps another buffer", fn);
+  }
+  const rib::LnQkvArgs a{x, gamma, beta, w, bias, q, k, v, xn, B, H, W, C, eps};
+  return hip_status(rib::launch_ln_qkv(a, dtype == RIB_BF16, (hipStream_t)stream), "rib_ln_qkv launch");
+}
+
+}  // extern "C"

@@ -40,4 +40,25 @@ struct GateArgs {
 // CLA gate producer; bf16 = false: fp32 maps.  C even, C <= 256.
 hipError_t launch_cla_gate(const GateArgs& a, bool bf16, hipStream_t stream);
 
+// compute units of the device current at the first call (cached)
+int device_cus();
+
+struct LnQkvArgs {
+  const void* x;
+  const float* gamma;
+  const float* beta;
+  const float* w;     // [C][3C]
+  const float* bias;  // [3C]
+  void* q;
+  void* k;
+  void* v;
+  void* xn;           // optional (nullptr)
+  int B, H, W, C;
+  float eps;
+};
+
+// LayerNorm + Q/K/V projection; bf16 = false: fp32 maps.  C <= 256.
+bool ln_qkv_mfma(int C);
+hipError_t launch_ln_qkv(const LnQkvArgs& a, bool bf16, hipStream_t stream);
+
 }  // namespace rib

@@ -21,7 +21,7 @@ def test_header_declares_the_boundary():
     assert set(rib.header_functions()) == {
         "rib_encode", "rib_window_attn", "rib_attn_supported", "rib_last_error", "rib_abi_version",
         "rib_cla_gate", "rib_window_attn_heads", "rib_window_attn_train", "rib_window_attn_backward", "rib_window_attn_backward_workspace",
-        "rib_encode_backward", "rib_encode_backward_workspace"}
+        "rib_encode_backward", "rib_encode_backward_workspace", "rib_ln_qkv"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -223,6 +223,29 @@ def test_encode_backward_validation(L):
     assert L.rib_encode_backward(16, 10, 64, 16, w, q, k, w, ws, need, None) == rib.RIB_ERR_INVALID_ARG
     assert L.rib_encode_backward(16, 10, 64, 16, w, q, k, d, d, need, None) == rib.RIB_ERR_INVALID_ARG
     assert "overlap" in L.rib_last_error().decode()
+
+
+def lnq(L, ptrs=None, B=1, H=8, W=8, C=180, eps=1e-5, dtype=rib.RIB_BF16):
+    p = list(ptrs or P[:5] + [P[5], P[6], P[7], None])
+    return L.rib_ln_qkv(*p, B, H, W, C, ctypes.c_float(eps), dtype, None)
+
+
+@fake
+def test_ln_qkv_validation(L):
+    assert lnq(L, [None] + P[1:8] + [None]) == rib.RIB_ERR_INVALID_ARG
+    assert "rib_ln_qkv" in L.rib_last_error().decode()
+    assert lnq(L, P[:7] + [None, None]) == rib.RIB_ERR_INVALID_ARG          # v missing
+    assert lnq(L, B=0) == rib.RIB_ERR_INVALID_ARG
+    assert lnq(L, dtype=2) == rib.RIB_ERR_INVALID_ARG
+    assert lnq(L, eps=-1.0) == rib.RIB_ERR_INVALID_ARG
+    assert lnq(L, C=257) == rib.RIB_ERR_UNSUPPORTED
+    assert lnq(L, C=181) == rib.RIB_ERR_UNSUPPORTED                          # odd C, bf16
+    assert lnq(L, [ctypes.c_void_p(P[0].value + 4)] + P[1:8] + [None]) == rib.RIB_ERR_INVALID_ARG
+    assert "aligned" in L.rib_last_error().decode()
+    assert lnq(L, P[:5] + [P[0], P[6], P[7], None]) == rib.RIB_ERR_INVALID_ARG  # q == x
+    assert "overlap" in L.rib_last_error().decode()
+    assert lnq(L, P[:5] + [P[5], P[5], P[7], None]) == rib.RIB_ERR_INVALID_ARG  # q == k
+    assert lnq(L, P[:8] + [P[3]]) == rib.RIB_ERR_INVALID_ARG                     # xn == w
 
 
 def test_python_binding_argument_checks():

@@ -1,11 +1,13 @@
 """GPU parity of the CLA gate producer G = PWConv1x1(DWConv3x3(X)) (rib_cla_gate, through the
 C ABI) against the fp64 CPU oracle.
 
-Tolerances: fp32 maps, max abs error <= 1e-5.  bf16 maps, derived from the arithmetic: D and the
-point-wise weights are each rounded to bf16 (relative error <= 2^-9 apiece) before an fp32-accumulated
-product, and G itself is rounded to bf16 (<= 2^-9 relative), so per element
-    |err| <= 2^-8 * S + 2^-8 * |G| + 1e-5,   S = sum_c |D_c| |W_co| + |b_o|,
-where S is bounded from above by the oracle run on the absolute values of every input.
+Tolerances: fp32 maps, max abs error <= 1e-5.  bf16 maps, derived from the arithmetic.  bf16 keeps an
+8-bit significand, so rounding to nearest has relative error <= u = 2^-8.  D and the point-wise
+weights are each rounded before an fp32-accumulated product, so each term carries at most
+(2u + u^2) |D_c| |W_co| < 2^-7 |D_c W_co|; G itself is then rounded (<= u relative).  Per element
+    |err| <= 2^-7 * S + 2^-8 * |G| + 1e-5,   S = sum_c |D_c| |W_co| + |b_o|,
+where S is bounded from above by the oracle run on the absolute values of every input (the fp32
+accumulation error, <= C 2^-24 S, and the fp32 stencil's are inside the 1e-5 and the slack of u^2).
 Identity weights and locality are checked bit for bit.
 """
 import sys
@@ -55,7 +57,7 @@ def compare(got, want, dtype, what, S=None):
     if dtype == "f32":
         tol = np.full_like(want, TOL["f32"])
     else:
-        tol = 2.0 ** -8 * S + 2.0 ** -8 * np.abs(want) + 1e-5
+        tol = 2.0 ** -7 * S + 2.0 ** -8 * np.abs(want) + 1e-5
     worst = float((err / tol).max()) if err.size else 0.0
     note(f"  {what}: max|err| {float(err.max()) if err.size else 0.0:.3g}  max|G| {float(np.abs(want).max()):.3g}"
          f"  max err/tol {worst:.3f}")
