@@ -70,6 +70,10 @@ def _configure(L):
     L.rib_oracle_cla_gate.restype = ctypes.c_int
     L.rib_oracle_ln_qkv.argtypes = [_D] * 5 + [ctypes.c_int] * 4 + [ctypes.c_double] + [_D] * 4
     L.rib_oracle_ln_qkv.restype = ctypes.c_int
+    L.rib_oracle_encode3d.argtypes = [ctypes.c_int] * 5 + [_D] * 3
+    L.rib_oracle_encode3d.restype = ctypes.c_int
+    L.rib_oracle_attn3d.argtypes = [_D] * 6 + [ctypes.c_int] * 9 + [_D]
+    L.rib_oracle_attn3d.restype = ctypes.c_int
     L.rib_oracle_attn_lse.argtypes = [_D] * 4 + [ctypes.c_int] * 7 + [_D]
     L.rib_oracle_attn_lse.restype = ctypes.c_int
     L.rib_oracle_attn_backward.argtypes = [_D] * 7 + [ctypes.c_int] * 7 + [_D] * 6
@@ -286,3 +290,36 @@ def ln_qkv(x, gamma, beta, w, bias, eps: float = 1e-5, with_xn: bool = False):
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return (q, k, v, xn) if with_xn else (q, k, v)
+
+
+def weight_count3d(L: int, hidden: int, R: int) -> int:
+    """Packed weights of the space-time encoder: W_h [3+6L][hidden] | b_h | Wp_q | Wp_k."""
+    return (3 + 6 * L) * hidden + hidden + 2 * hidden * R
+
+
+def encode3d(wt: int, ws: int, L: int, hidden: int, R: int, weights) -> tuple[np.ndarray, np.ndarray]:
+    """Qp, Kp as [wt*ws*ws, R] float64 for wt x ws x ws space-time windows."""
+    w = _f64(weights).reshape(-1)
+    if w.size != weight_count3d(L, hidden, R):
+        raise ValueError("packed weight vector has the wrong length")
+    n = wt * ws * ws
+    qp = np.zeros((n, R), np.float64)
+    kp = np.zeros((n, R), np.float64)
+    if lib().rib_oracle_encode3d(wt, ws, L, hidden, R, _p(w), _p(qp), _p(kp)) != 0:
+        raise ValueError("oracle encode3d rejected its arguments")
+    return qp, kp
+
+
+def window_attn3d(qc, kc, v, g, qp, kp, heads: int, wt: int, ws: int) -> np.ndarray:
+    """Attention over wt x ws x ws windows of [B, T, H, W, C] video maps (float64)."""
+    qc, kc, v, g = (_f64(a) for a in (qc, kc, v, g))
+    qp, kp = _f64(qp), _f64(kp)
+    B, T, H, W, C = qc.shape
+    if C % heads:
+        raise ValueError("channel count must be a multiple of heads")
+    o = np.zeros(qc.shape, np.float64)
+    rc = lib().rib_oracle_attn3d(_p(qc), _p(kc), _p(v), _p(g), _p(qp), _p(kp), B, T, H, W, heads, C // heads,
+                                 qp.shape[-1], wt, ws, _p(o))
+    if rc != 0:
+        raise ValueError("oracle attn3d rejected its arguments")
+    return o

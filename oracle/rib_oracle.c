@@ -694,3 +694,146 @@ int rib_oracle_ln_qkv(const double* x, const double* gamma, const double* beta, 
   }
   return fail ? -1 : 0;
 }
+
+/*
+ * Space-time windows (explainer section 6: for video, the coordinate MLP takes
+ * spatio-temporal coordinates and the attention windows become 3-D).
+ * A video map is [B][T][H][W][C]; a window spans wt frames x ws rows x ws
+ * columns, anchored at (0, 0, 0); in-window index n = (it*ws + iy)*ws + ix.
+ */
+
+/* temporal coordinate: the same float32 grid over wt points; 0 for a single frame */
+static double coord_value_t(int k, int wt) { return wt == 1 ? 0.0 : coord_value(k, wt); }
+
+/* [c_t, c_y, c_x], then for each frequency 2^i: sin t, sin y, sin x, cos t, cos y, cos x */
+static void fourier_features3(double ct, double cy, double cx, int L, double* out) {
+  int f = 0;
+  out[f++] = ct;
+  out[f++] = cy;
+  out[f++] = cx;
+  for (int i = 0; i < L; ++i) {
+    const double freq = ldexp(1.0, i);
+    out[f++] = sin(freq * ct);
+    out[f++] = sin(freq * cy);
+    out[f++] = sin(freq * cx);
+    out[f++] = cos(freq * ct);
+    out[f++] = cos(freq * cy);
+    out[f++] = cos(freq * cx);
+  }
+}
+
+/* Encoder over a wt x ws x ws window: Qp, Kp [wt*ws*ws][R]; weights W_h[(3+6L)][hidden] | b_h | Wp_q | Wp_k. */
+int rib_oracle_encode3d(int wt, int ws, int L, int hidden, int R, const double* weights, double* qp, double* kp) {
+  if (wt < 1 || ws < 2 || L < 0 || hidden < 1 || R < 1 || !weights || !qp || !kp) return -1;
+  const int F = 3 + 6 * L;
+  const double* Wh = weights;
+  const double* bh = Wh + (size_t)F * hidden;
+  const double* Wq = bh + hidden;
+  const double* Wk = Wq + (size_t)hidden * R;
+  double* feat = (double*)malloc(sizeof(double) * F);
+  double* h = (double*)malloc(sizeof(double) * hidden);
+  if (!feat || !h) {
+    free(feat); free(h);
+    return -1;
+  }
+  for (int it = 0; it < wt; ++it)
+    for (int iy = 0; iy < ws; ++iy)
+      for (int ix = 0; ix < ws; ++ix) {
+        const int n = (it * ws + iy) * ws + ix;
+        fourier_features3(coord_value_t(it, wt), coord_value(iy, ws), coord_value(ix, ws), L, feat);
+        for (int j = 0; j < hidden; ++j) {
+          double acc = bh[j];
+          for (int f = 0; f < F; ++f) acc += feat[f] * Wh[(size_t)f * hidden + j];
+          h[j] = acc > 0.0 ? acc : 0.0;
+        }
+        for (int r = 0; r < R; ++r) {
+          double aq = 0.0, ak = 0.0;
+          for (int j = 0; j < hidden; ++j) {
+            aq += h[j] * Wq[(size_t)j * R + r];
+            ak += h[j] * Wk[(size_t)j * R + r];
+          }
+          qp[(size_t)n * R + r] = aq;
+          kp[(size_t)n * R + r] = ak;
+        }
+      }
+  free(feat);
+  free(h);
+  return 0;
+}
+
+/*
+ * Attention over space-time windows, the 2-D definition with 3-D windows: per
+ * (image, window, head) and real query i, S = Qc Kc^T / sqrt(dh) + Qp[n_i] Kp[n_j]^T / sqrt(R)
+ * over the window's real tokens j, softmax, times V, gated by sigmoid(G).
+ * The window's tokens are found by scanning the whole video.
+ */
+int rib_oracle_attn3d(const double* qc, const double* kc, const double* v, const double* g, const double* qp,
+                      const double* kp, int B, int T, int H, int W, int heads, int dh, int R, int wt, int ws,
+                      double* o) {
+  if (!qc || !kc || !v || !g || !qp || !kp || !o || B < 1 || T < 1 || H < 1 || W < 1 || heads < 1 || dh < 1 ||
+      R < 1 || wt < 1 || ws < 2)
+    return -1;
+  const int C = heads * dh;
+  const int nWt = (T + wt - 1) / wt, nWy = (H + ws - 1) / ws, nWx = (W + ws - 1) / ws;
+  const long units = (long)B * nWt * nWy * nWx * heads;
+  const double inv_sqrt_dh = 1.0 / sqrt((double)dh), inv_sqrt_r = 1.0 / sqrt((double)R);
+  int fail = 0;
+#pragma omp parallel
+  {
+    const int cap = wt * ws * ws;
+    long* off = (long*)malloc(sizeof(long) * cap);
+    int* tn = (int*)malloc(sizeof(int) * cap);
+    double* P = (double*)malloc(sizeof(double) * cap);
+    if (!off || !tn || !P) {
+#pragma omp atomic write
+      fail = 1;
+    } else {
+#pragma omp for schedule(dynamic, 1)
+      for (long u = 0; u < units; ++u) {
+        const int h = (int)(u % heads);
+        long r = u / heads;
+        const int wx = (int)(r % nWx);
+        r /= nWx;
+        const int wy = (int)(r % nWy);
+        r /= nWy;
+        const int wtw = (int)(r % nWt);
+        const int b = (int)(r / nWt);
+        int nt = 0;
+        for (int t = 0; t < T; ++t) {
+          if (t / wt != wtw) continue;
+          for (int y = 0; y < H; ++y) {
+            if (y / ws != wy) continue;
+            for (int x = 0; x < W; ++x) {
+              if (x / ws != wx) continue;
+              off[nt] = ((((long)b * T + t) * H + y) * W + x) * C + (long)h * dh;
+              tn[nt] = ((t % wt) * ws + y % ws) * ws + x % ws;
+              ++nt;
+            }
+          }
+        }
+        for (int i = 0; i < nt; ++i) {
+          double mx = -INFINITY;
+          for (int j = 0; j < nt; ++j) {
+            double sc = 0.0, bb = 0.0;
+            for (int d = 0; d < dh; ++d) sc += qc[off[i] + d] * kc[off[j] + d];
+            for (int k = 0; k < R; ++k) bb += qp[(size_t)tn[i] * R + k] * kp[(size_t)tn[j] * R + k];
+            P[j] = sc * inv_sqrt_dh + bb * inv_sqrt_r;
+            if (P[j] > mx) mx = P[j];
+          }
+          double sum = 0.0;
+          for (int j = 0; j < nt; ++j) {
+            P[j] = exp(P[j] - mx);
+            sum += P[j];
+          }
+          for (int d = 0; d < dh; ++d) {
+            double a = 0.0;
+            for (int j = 0; j < nt; ++j) a += P[j] * v[off[j] + d];
+            o[off[i] + d] = a / sum / (1.0 + exp(-g[off[i] + d]));
+          }
+        }
+      }
+    }
+    free(off); free(tn); free(P);
+  }
+  return fail ? -1 : 0;
+}
