@@ -9,7 +9,8 @@ R = 16, one 96x96 window per image.  Secondary figures for the 64x64 window
 (1x180x320, C = 180), the 640x360 input with 96x96 windows, and the 16x16
 window of the SST-lite map (HBM-bound) are reported in the same JSON line, and so is the
 CLA gate producer (rib_cla_gate, HBM-bound) and the LayerNorm + Q/K/V projection
-(rib_ln_qkv, HBM-bound) on the same maps, and the
+(rib_ln_qkv, HBM-bound) on the same maps, space-time windows on an 8-frame video map
+(rib_window_attn3d), and the
 training iteration of the attention (rib_window_attn_train + rib_window_attn_backward +
 rib_encode_backward) on the 96x96 and 64x64 workloads.
 
@@ -172,6 +173,46 @@ def time_gate(torch, rib, synthetic):
                      "tflops": flops / (ms * 1e-3) / 1e12, "tokens_per_s": B * H * W / (ms * 1e-3)}
         del xs, gs
         torch.cuda.empty_cache()
+    return res
+
+
+def time_space_time(torch, rib, synthetic):
+    """Space-time windows on a video map (rib_encode3d once, then rib_window_attn3d timed): 8 frames of the
+    SST inference map 180x320, C=180 (6 heads x dh 30), R=16, bf16; windows 2x32x32 and 4x16x16."""
+    res = {}
+    B, T, H, W, heads, dh, R, L, hidden = 1, 8, 180, 320, 6, 30, 16, 10, 64
+    p = synthetic.make_problem(B * T, H, W, heads, dh, R, dtype="bf16", seed=12)
+    maps = [torch.from_numpy(p.bits[n].view("int16")).view(torch.bfloat16).cuda().view(B, T, H, W, heads * dh)
+            for n in ("qc", "kc", "v", "g")]
+    rng = __import__("numpy").random.default_rng(13)
+    F = 3 + 6 * L
+    w = torch.tensor(rng.standard_normal(F * hidden + hidden + 2 * hidden * R), dtype=torch.float32).cuda() * 0.1
+    for wt, ws in ((2, 32), (4, 16)):
+        qp, kp = rib.encode3d(wt, ws, L, hidden, R, w)
+        for _ in range(5):
+            rib.window_attn3d(*maps, qp, kp, heads, wt, ws)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 50
+        s.record()
+        for _ in range(reps):
+            rib.window_attn3d(*maps, qp, kp, heads, wt, ws)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        pairs = 0
+        for t0 in range(0, T, wt):
+            for y0 in range(0, H, ws):
+                for x0 in range(0, W, ws):
+                    n = (min(T, t0 + wt) - t0) * (min(H, y0 + ws) - y0) * (min(W, x0 + ws) - x0)
+                    pairs += n * n
+        flops = B * heads * pairs * (2 * (dh + R) + 2 * dh)
+        tf = flops / (ms * 1e-3) / 1e12
+        res[f"{wt}x{ws}x{ws} windows, 8 x 180x320, C=180"] = {
+            "ms_attn": ms, "tokens_per_s": B * T * H * W / (ms * 1e-3), "tflops": tf,
+            "pct_bf16_peak": 100 * tf / PEAK_BF16_TFLOPS}
+    del maps
+    torch.cuda.empty_cache()
     return res
 
 
@@ -382,6 +423,7 @@ def main():
     if not args.no_extra:
         out["cla_gate"] = time_gate(torch, rib, synthetic)
         out["ln_qkv"] = time_ln_qkv(torch, rib, synthetic)
+        out["space_time"] = time_space_time(torch, rib, synthetic)
         out["backward"] = {"96x96 window, 32x96x96": time_backward(torch, rib, synthetic, 4, 96, args.backward_reps),
                            "64x64 window, 1x180x320": time_backward(torch, rib, synthetic, 3, 64,
                                                                     3 * args.backward_reps)}

@@ -238,6 +238,31 @@ rib_status rib_ln_qkv(const void* x, const float* gamma, const float* beta, cons
                       void* q, void* k, void* v, void* xn, int B, int H, int W, int C, float eps, rib_dtype dtype,
                       void* stream);
 
+/*
+ * Space-time windows for video (explainer section 6: the coordinate MLP takes
+ * spatio-temporal coordinates and the attention windows become 3-D).
+ *
+ * rib_encode3d -- Qp, Kp float32 [frames*window*window][R] for windows of
+ * `frames` frames x window x window.  Position n = (it*window + iy)*window + ix
+ * has coordinates (c_t, c_y, c_x) on the float32 grid -1 + 2k/(n-1) of each
+ * axis (c_t = 0 when frames == 1); features [c_t, c_y, c_x], then for each
+ * frequency 2^i, i < L: sin t, sin y, sin x, cos t, cos y, cos x (3 + 6L).
+ * weights: W_h[(3+6L)][hidden] | b_h | Wp_q[hidden][R] | Wp_k[hidden][R].
+ * Limits: frames*window^2 <= 16384, window <= 128, L <= 16, hidden <= 256,
+ * R <= 64.
+ *
+ * rib_window_attn3d -- rib_window_attn over [B][T][H][W][heads*dh] video maps
+ * with windows of `frames` frames x window x window anchored at (0, 0, 0);
+ * edge windows hold only their real tokens.  qp, kp from rib_encode3d.
+ * Limits as rib_window_attn, with frames*window^2 <= 16384 and
+ * B*T*H*W*heads*dh < 2^31.
+ */
+rib_status rib_encode3d(int frames, int window, int L, int hidden, int R, const float* weights, float* qp,
+                        float* kp, void* stream);
+rib_status rib_window_attn3d(const void* qc, const void* kc, const void* v, const void* g, const float* qp,
+                             const float* kp, void* o, int B, int T, int H, int W, int heads, int dh, int R,
+                             int frames, int window, rib_dtype dtype, void* stream);
+
 /* Text describing the last non-OK status returned on this thread ("" if none).
  * The pointer stays valid until the next library call on the same thread. */
 const char* rib_last_error(void);
@@ -245,7 +270,7 @@ const char* rib_last_error(void);
 /* ABI version of this header (incremented on any incompatible change). */
 int rib_abi_version(void);
 
-#define RIB_ABI_VERSION 6
+#define RIB_ABI_VERSION 7
 
 #ifdef __cplusplus
 }

@@ -71,6 +71,10 @@ def lib(path: str | None = None):
     L.rib_encode_backward.restype = i
     L.rib_ln_qkv.argtypes = [vp] * 9 + [i] * 4 + [ctypes.c_float, i, vp]
     L.rib_ln_qkv.restype = i
+    L.rib_encode3d.argtypes = [i] * 5 + [vp] * 4
+    L.rib_encode3d.restype = i
+    L.rib_window_attn3d.argtypes = [vp] * 7 + [i] * 10 + [vp]
+    L.rib_window_attn3d.restype = i
     L.rib_attn_supported.argtypes = [i, i, i, i]
     L.rib_attn_supported.restype = i
     L.rib_last_error.argtypes = []
@@ -327,6 +331,43 @@ def ln_qkv_into(x, gamma, beta, w, bias, q, k, v, xn=None, eps: float = 1e-5) ->
         raise ValueError("all tensors must be contiguous GPU tensors")
     _check(lib().rib_ln_qkv(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(w), _ptr(bias), _ptr(q), _ptr(k), _ptr(v),
                             _ptr(xn) if xn is not None else None, B, H, W, C, float(eps), _dtype_code(x), _stream(x)))
+
+
+def weight_count3d(L: int, hidden: int, R: int) -> int:
+    """Length of the packed space-time encoder weights W_h [3+6L][hidden] | b_h | Wp_q | Wp_k."""
+    return (3 + 6 * L) * hidden + hidden + 2 * hidden * R
+
+
+def encode3d(frames: int, window: int, L: int, hidden: int, R: int, weights):
+    """Positional factors of frames x window x window space-time windows: float32 [frames*window^2, R] each."""
+    import torch
+    if not (weights.is_cuda and weights.dtype == torch.float32 and weights.is_contiguous()):
+        raise ValueError("weights must be a contiguous float32 GPU tensor")
+    if weights.numel() != weight_count3d(L, hidden, R):
+        raise ValueError("packed weight vector has the wrong length")
+    qp = torch.empty((frames * window * window, R), dtype=torch.float32, device=weights.device)
+    kp = torch.empty_like(qp)
+    _check(lib().rib_encode3d(frames, window, L, hidden, R, _ptr(weights), _ptr(qp), _ptr(kp), _stream(weights)))
+    return qp, kp
+
+
+def window_attn3d(qc, kc, v, g, qp, kp, heads: int, frames: int, window: int):
+    """Window attention over [B, T, H, W, heads*dh] video maps with frames x window x window windows."""
+    import torch
+    ts = (qc, kc, v, g)
+    if any(t.dim() != 5 or t.shape != qc.shape or t.dtype != qc.dtype for t in ts):
+        raise ValueError("qc, kc, v, g must all be [B, T, H, W, C] of one dtype")
+    if not all(t.is_cuda and t.is_contiguous() for t in ts + (qp, kp)):
+        raise ValueError("all tensors must be contiguous GPU tensors")
+    if qp.dtype != torch.float32 or kp.shape != qp.shape or qp.dim() != 2 or qp.shape[0] != frames * window * window:
+        raise ValueError("qp, kp must be float32 [frames*window*window, R]")
+    B, T, H, W, C = qc.shape
+    if heads < 1 or C % heads:
+        raise ValueError("channel count must be a multiple of heads")
+    o = torch.empty_like(qc)
+    _check(lib().rib_window_attn3d(_ptr(qc), _ptr(kc), _ptr(v), _ptr(g), _ptr(qp), _ptr(kp), _ptr(o), B, T, H, W,
+                                   heads, C // heads, qp.shape[1], frames, window, _dtype_code(qc), _stream(qc)))
+    return o
 
 
 def supported(dh: int, R: int, window: int, dtype) -> bool:

@@ -94,19 +94,42 @@ struct Shape {
   static_assert(!(R > 16 && DT > 1), "wave 3 stages either Kp[16..32) or the second V tile");
 };
 
+// A window spans wt frames x ws rows x ws columns of a [B][T][H][W][C] map
+// (T = wt = 1 for images); its real tokens are enumerated frame-major, then
+// row-major: r = (it*ny + iy)*nx + ix with ny, nx the window's real rows and
+// columns.  In-window index n = (it*ws + iy)*ws + ix.
 struct Geo {
-  int H, W, C, ws, b, wy, wx, h, nx, n_real;
-  float inv_nx;
+  int T, H, W, C, wt, ws, b, tw, wy, wx, h, ny, nx, n_real;
+  float inv_nx, inv_ny;
 };
 
 // real index r of a window -> element offset of the token's head slice and
 // in-window index n
 template <int DH>
 __device__ __forceinline__ void locate(const Geo& G, int r, int& off, int& n) {
-  const int iy = (int)(((float)r + 0.5f) * G.inv_nx);
-  const int ix = r - iy * G.nx;
-  off = ((G.b * G.H + G.wy * G.ws + iy) * G.W + G.wx * G.ws + ix) * G.C + G.h * DH;
-  n = iy * G.ws + ix;
+  const int rr = (int)(((float)r + 0.5f) * G.inv_nx);  // real row, frame-major
+  const int ix = r - rr * G.nx;
+  const int it = (int)(((float)rr + 0.5f) * G.inv_ny);
+  const int iy = rr - it * G.ny;
+  off = (((G.b * G.T + G.tw * G.wt + it) * G.H + G.wy * G.ws + iy) * G.W + G.wx * G.ws + ix) * G.C + G.h * DH;
+  n = (it * G.ws + iy) * G.ws + ix;
+}
+
+// window decode of a logical unit u = (((b*nWt + tw)*nWy + wy)*nWx + wx)*heads + h
+template <int DH>
+__device__ __forceinline__ void decode_window(Geo& G, int u, int T, int H, int W, int heads, int wt, int ws) {
+  const int nWy = (H + ws - 1) / ws, nWx = (W + ws - 1) / ws, nWt = (T + wt - 1) / wt;
+  G.h = u % heads; u /= heads;
+  G.wx = u % nWx; u /= nWx;
+  G.wy = u % nWy; u /= nWy;
+  G.tw = u % nWt;
+  G.b = u / nWt;
+  G.T = T; G.H = H; G.W = W; G.C = heads * DH; G.wt = wt; G.ws = ws;
+  G.nx = min(ws, W - G.wx * ws);
+  G.ny = min(ws, H - G.wy * ws);
+  G.n_real = min(wt, T - G.tw * wt) * G.ny * G.nx;
+  G.inv_nx = 1.0f / (float)G.nx;
+  G.inv_ny = 1.0f / (float)G.ny;
 }
 
 // ---- LDS layouts of a key tile ----------------------------------------------
@@ -157,21 +180,26 @@ struct Roles {
 // real key run on beyond the window; those keys are masked at the store and
 // reads past the buffer end return zeros (bounds-checked buffer loads).
 struct Cursor {
-  int ix;
+  int ix, iy;  // column, and row within the frame, of the lane's key
   unsigned voff;
 };
 
 struct CursorStep {
-  unsigned col;   // bytes per window column (uniform)
-  unsigned wrap;  // bytes from the end of one window row to the start of the next (uniform)
+  unsigned col;    // bytes per window column (uniform)
+  unsigned wrap;   // bytes from the end of one window row to the start of the next (uniform)
+  unsigned fskip;  // bytes from past the window's last row of a frame to its first row of the next
 };
 
-__device__ __forceinline__ void cursor_advance(Cursor& c, const CursorStep& cs, int nx) {
+__device__ __forceinline__ void cursor_advance(Cursor& c, const CursorStep& cs, int nx, int ny) {
   c.ix += KT;
   c.voff += KT * cs.col;
   while (c.ix >= nx) {
     c.ix -= nx;
     c.voff += cs.wrap;
+    if (++c.iy == ny) {
+      c.iy = 0;
+      c.voff += cs.fskip;
+    }
   }
 }
 
@@ -453,29 +481,20 @@ __global__ void __launch_bounds__(QB, 1)
 attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
                  const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                  const float* __restrict__ qp, const float* __restrict__ kp,
-                 uint32_t* __restrict__ o, int B, int H, int W, int heads, int ws, int total,
+                 uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws, int total,
                  long tstride, float* __restrict__ lse) {
   using S = Shape<DH, R>;
   __shared__ __attribute__((aligned(16))) uint32_t lds[S::LDS_DW];
 
   const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
   if (logical >= total) return;
-  const int nWy = (H + ws - 1) / ws, nWx = (W + ws - 1) / ws;
-  const int qblocks = (ws * ws + QB - 1) / QB;
+  const int NW = wt * ws * ws;  // tokens of a full window
+  const int qblocks = (NW + QB - 1) / QB;
   Geo G;
   int q0;
   {
-    int t = logical;
-    const int qblk = t % qblocks; t /= qblocks;
-    G.h = t % heads; t /= heads;
-    G.wx = t % nWx; t /= nWx;
-    G.wy = t % nWy;
-    G.b = t / nWy;
-    G.H = H; G.W = W; G.C = heads * DH; G.ws = ws;
-    G.nx = min(ws, W - G.wx * ws);
-    G.n_real = min(ws, H - G.wy * ws) * G.nx;
-    G.inv_nx = 1.0f / (float)G.nx;
-    q0 = qblk * QB;
+    decode_window<DH>(G, logical / qblocks, T, H, W, heads, wt, ws);
+    q0 = (logical % qblocks) * QB;
     if (q0 >= G.n_real) return;
   }
   qp += (long)G.h * tstride;  // per-head positional tables (tstride 0: one shared pair)
@@ -536,8 +555,8 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
   const int grp = wave >> 2;  // 0: waves 0-3 lead, 1: waves 4-7 follow half a step behind
   // this wave's load source (wave-uniform): see the staging notes above
   using RL = Roles<DH, R>;
-  const unsigned map_bytes = (unsigned)(B * H * W * heads * DH) * 2u;
-  const unsigned pos_bytes = (unsigned)(ws * ws * R) * 4u;
+  const unsigned map_bytes = (unsigned)(B * T * H * W * heads * DH) * 2u;
+  const unsigned pos_bytes = (unsigned)(NW * R) * 4u;
   const void* src = (wave == 2 || wave == 3) ? (const void*)kc
                   : (wave == 4 || wave == 5) ? (const void*)v : (const void*)kp;
   const bool loads = wave == 0 || (wave == 1 && RL::KP1) || wave == 2 || (wave == 3 && RL::KC1) ||
@@ -551,13 +570,19 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
   CursorStep cs;
   cs.col = pos ? (unsigned)(R * 4) : (unsigned)(G.C * 2);
   const unsigned row_bytes = pos ? (unsigned)(ws * R * 4) : (unsigned)(W * G.C * 2);
+  const unsigned frame_bytes = pos ? (unsigned)(ws * ws * R * 4) : (unsigned)(H * W * G.C * 2);
   cs.wrap = row_bytes - (unsigned)G.nx * cs.col;
+  cs.fskip = (unsigned)((pos ? ws : H) - G.ny) * row_bytes;
   Cursor cur;
   {
-    const int iy = (int)(((float)lane + 0.5f) * G.inv_nx);
-    cur.ix = lane - iy * G.nx;
-    const unsigned base = pos ? 0u : 2u * (unsigned)(((G.b * H + G.wy * ws) * W + G.wx * ws) * G.C + G.h * DH);
-    cur.voff = base + (unsigned)iy * row_bytes + (unsigned)cur.ix * cs.col + 32u * sub;
+    const int rr = (int)(((float)lane + 0.5f) * G.inv_nx);
+    cur.ix = lane - rr * G.nx;
+    const int it = (int)(((float)rr + 0.5f) * G.inv_ny);
+    cur.iy = rr - it * G.ny;
+    const unsigned base =
+        pos ? 0u
+            : 2u * (unsigned)((((G.b * T + G.tw * wt) * H + G.wy * ws) * W + G.wx * ws) * G.C + G.h * DH);
+    cur.voff = base + (unsigned)it * frame_bytes + (unsigned)cur.iy * row_bytes + (unsigned)cur.ix * cs.col + 32u * sub;
   }
 
   // ---- prologue: tile 0 staged by everyone, tile 1 loaded into registers
@@ -565,7 +590,7 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
   load_tile(rsrc, cur, st);
   if (ntiles > 1) {
     store_tile<DH, R, false>(lds, wave, lane, true, st);
-    cursor_advance(cur, cs, G.nx);
+    cursor_advance(cur, cs, G.nx, G.ny);
     load_tile(rsrc, cur, st);
   } else {
     store_tile<DH, R, true>(lds, wave, lane, lane < G.n_real, st);
@@ -589,7 +614,7 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
       uint32_t* dst = lds + (x % NSTAGE) * S::STAGE_DW;
       if (x + 1 < ntiles) {
         store_tile<DH, R, false>(dst, wave, lane, true, st);
-        cursor_advance(cur, cs, G.nx);
+        cursor_advance(cur, cs, G.nx, G.ny);
         load_tile(rsrc, cur, st);
       } else {
         store_tile<DH, R, true>(dst, wave, lane, x * KT + lane < G.n_real, st);
@@ -715,27 +740,16 @@ __global__ void __launch_bounds__(SQ, 2)
 attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
                        const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                        const float* __restrict__ qp, const float* __restrict__ kp,
-                       uint32_t* __restrict__ o, int B, int H, int W, int heads, int ws, int total,
-                       long tstride, float* __restrict__ lse) {
+                       uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws,
+                       int total, long tstride, float* __restrict__ lse) {
   using S = Shape<DH, R>;
   using RL = Roles<DH, R>;
   __shared__ __attribute__((aligned(16))) uint32_t lds[SNT * S::STAGE_DW];
 
   const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
   if (logical >= total) return;
-  const int nWy = (H + ws - 1) / ws, nWx = (W + ws - 1) / ws;
   Geo G;
-  {
-    int t = logical;
-    G.h = t % heads; t /= heads;
-    G.wx = t % nWx; t /= nWx;
-    G.wy = t % nWy;
-    G.b = t / nWy;
-    G.H = H; G.W = W; G.C = heads * DH; G.ws = ws;
-    G.nx = min(ws, W - G.wx * ws);
-    G.n_real = min(ws, H - G.wy * ws) * G.nx;
-    G.inv_nx = 1.0f / (float)G.nx;
-  }
+  decode_window<DH>(G, logical, T, H, W, heads, wt, ws);
   qp += (long)G.h * tstride;  // per-head positional tables (tstride 0: one shared pair)
   kp += (long)G.h * tstride;
   const int tid = threadIdx.x;
@@ -749,8 +763,8 @@ attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
     const bool real = tid < G.n_real;
     int off, n;
     locate<DH>(G, real ? tid : G.n_real - 1, off, n);
-    const unsigned map_bytes = (unsigned)(B * H * W * heads * DH) * 2u;
-    const unsigned pos_bytes = (unsigned)(ws * ws * R) * 4u;
+    const unsigned map_bytes = (unsigned)(B * T * H * W * heads * DH) * 2u;
+    const unsigned pos_bytes = (unsigned)(wt * ws * ws * R) * 4u;
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(kc), (short)0,
                                                                         (int)map_bytes, (int)RSRC_WORD3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(v), (short)0,
@@ -863,23 +877,24 @@ attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
 
 template <int DH, int R>
 hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
-  const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws;
-  if (a.ws * a.ws <= SQ) {
-    const int total = a.B * nWy * nWx * a.heads;
+  const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws, nWt = (a.T + a.wt - 1) / a.wt;
+  const int NW = a.wt * a.ws * a.ws;
+  if (NW <= SQ) {
+    const int total = a.B * nWt * nWy * nWx * a.heads;
     const int grid = 8 * ((total + 7) / 8);
     hipLaunchKernelGGL((attn_bf16_small_kernel<DH, R>), dim3(grid), dim3(SQ), 0, stream,
                        (const uint32_t*)a.qc, (const uint32_t*)a.kc, (const uint32_t*)a.v,
-                       (const uint32_t*)a.g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.H, a.W, a.heads, a.ws,
-                       total, a.tstride, a.lse);
+                       (const uint32_t*)a.g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt,
+                       a.ws, total, a.tstride, a.lse);
     return hipGetLastError();
   }
-  const int qblocks = (a.ws * a.ws + QB - 1) / QB;
-  const int total = a.B * nWy * nWx * a.heads * qblocks;
+  const int qblocks = (NW + QB - 1) / QB;
+  const int total = a.B * nWt * nWy * nWx * a.heads * qblocks;
   const int grid = 8 * ((total + 7) / 8);
   hipLaunchKernelGGL((attn_bf16_kernel<DH, R>), dim3(grid), dim3(QB), 0, stream,
                      (const uint32_t*)a.qc, (const uint32_t*)a.kc, (const uint32_t*)a.v,
-                     (const uint32_t*)a.g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.H, a.W, a.heads, a.ws,
-                     total, a.tstride, a.lse);
+                     (const uint32_t*)a.g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt,
+                     a.ws, total, a.tstride, a.lse);
   return hipGetLastError();
 }
 

@@ -30,7 +30,7 @@ __global__ void __launch_bounds__(F32_QB)
 attn_f32_kernel(const float* __restrict__ qc, const float* __restrict__ kc,
                 const float* __restrict__ v, const float* __restrict__ g,
                 const float* __restrict__ qp, const float* __restrict__ kp, float* __restrict__ o,
-                int B, int H, int W, int heads, int dh, int R, int ws, int total, long tstride,
+                int B, int T, int H, int W, int heads, int dh, int R, int wt, int ws, int total, long tstride,
                 float* __restrict__ lse) {
   __shared__ float sk[F32_KT][DHM];
   __shared__ float sv[F32_KT][DHM];
@@ -38,29 +38,29 @@ attn_f32_kernel(const float* __restrict__ qc, const float* __restrict__ kc,
 
   const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
   if (logical >= total) return;
-  const int nWy = (H + ws - 1) / ws, nWx = (W + ws - 1) / ws;
-  const int qblocks = (ws * ws + F32_QB - 1) / F32_QB;
+  const int nWy = (H + ws - 1) / ws, nWx = (W + ws - 1) / ws, nWt = (T + wt - 1) / wt;
+  const int qblocks = (wt * ws * ws + F32_QB - 1) / F32_QB;
   int t = logical;
   const int qblk = t % qblocks; t /= qblocks;
   const int h = t % heads; t /= heads;
   const int wx = t % nWx; t /= nWx;
-  const int wy = t % nWy;
-  const int b = t / nWy;
+  const int wy = t % nWy; t /= nWy;
+  const int tw = t % nWt;
+  const int b = t / nWt;
   qp += (long)h * tstride;  // per-head positional tables (tstride 0: one shared pair)
   kp += (long)h * tstride;
   const int ny = min(ws, H - wy * ws), nx = min(ws, W - wx * ws);
-  const int n_real = ny * nx;
+  const int n_real = min(wt, T - tw * wt) * ny * nx;
   const int q0 = qblk * F32_QB;
   if (q0 >= n_real) return;
   const int C = heads * dh;
-  const float inv_nx = 1.0f / (float)nx;
-
-  // real index r -> (element offset of the token's head slice, in-window index n)
+  // real index r (frame-major, then row-major over the window's real tokens) ->
+  // (element offset of the token's head slice, in-window index n = (it*ws + iy)*ws + ix)
   auto locate = [&](int r, int& off, int& n) {
-    const int iy = (int)(((float)r + 0.5f) * inv_nx);
-    const int ix = r - iy * nx;
-    off = ((b * H + wy * ws + iy) * W + wx * ws + ix) * C + h * dh;
-    n = iy * ws + ix;
+    const int rr = r / nx, ix = r - rr * nx;
+    const int it = rr / ny, iy = rr - it * ny;
+    off = (((b * T + tw * wt + it) * H + wy * ws + iy) * W + wx * ws + ix) * C + h * dh;
+    n = (it * ws + iy) * ws + ix;
   };
 
   const int r = q0 + (int)threadIdx.x;
@@ -136,14 +136,14 @@ attn_f32_kernel(const float* __restrict__ qc, const float* __restrict__ kc,
 
 template <int DHM, int RM>
 hipError_t launch_f32(const AttnArgs& a, hipStream_t stream) {
-  const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws;
-  const int qblocks = (a.ws * a.ws + F32_QB - 1) / F32_QB;
-  const int total = a.B * nWy * nWx * a.heads * qblocks;
+  const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws, nWt = (a.T + a.wt - 1) / a.wt;
+  const int qblocks = (a.wt * a.ws * a.ws + F32_QB - 1) / F32_QB;
+  const int total = a.B * nWt * nWy * nWx * a.heads * qblocks;
   const int grid = 8 * ((total + 7) / 8);
   hipLaunchKernelGGL((attn_f32_kernel<DHM, RM>), dim3(grid), dim3(F32_QB), 0, stream,
                      (const float*)a.qc, (const float*)a.kc, (const float*)a.v, (const float*)a.g,
-                     a.qp, a.kp, (float*)a.o, a.B, a.H, a.W, a.heads, a.dh, a.R, a.ws, total, a.tstride,
-                     a.lse);
+                     a.qp, a.kp, (float*)a.o, a.B, a.T, a.H, a.W, a.heads, a.dh, a.R, a.wt, a.ws, total,
+                     a.tstride, a.lse);
   return hipGetLastError();
 }
 

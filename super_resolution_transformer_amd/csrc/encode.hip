@@ -46,17 +46,47 @@ static __device__ void fourier_features(int n0, int N, int ws, int L, int TOK, i
   }
 }
 
+// Space-time windows (explainer section 6, video): position n = (it*ws + iy)*ws + ix
+// of a wt x ws x ws window has coordinates (c_t, c_y, c_x), c_t = 0 for wt = 1;
+// features [c_t, c_y, c_x], then for each frequency 2^(i-1): sin t, sin y,
+// sin x, cos t, cos y, cos x.
+static __device__ void fourier_features3(int n0, int N, int wt, int ws, int L, int TOK, int F, float* feat) {
+  for (int item = threadIdx.x; item < TOK * (L + 1); item += blockDim.x) {
+    const int t = item / (L + 1), i = item % (L + 1);
+    const int n = min(n0 + t, N - 1);
+    const int it = n / (ws * ws), r2 = n - it * ws * ws;
+    const int iy = r2 / ws, ix = r2 - (r2 / ws) * ws;
+    const float c[3] = {wt == 1 ? 0.0f : (float)(2 * it - (wt - 1)) / (float)(wt - 1),
+                        (float)(2 * iy - (ws - 1)) / (float)(ws - 1), (float)(2 * ix - (ws - 1)) / (float)(ws - 1)};
+    float* f = feat + t * F;
+    if (i == 0) {
+      f[0] = c[0];
+      f[1] = c[1];
+      f[2] = c[2];
+    } else {
+      const float fr = ldexpf(1.0f, i - 1);
+      float* g = f + 3 + 6 * (i - 1);
+      for (int a = 0; a < 3; ++a) {
+        g[a] = sinf(fr * c[a]);
+        g[3 + a] = cosf(fr * c[a]);
+      }
+    }
+  }
+}
+
+// wt = 0: image windows (2 coordinates); wt >= 1: space-time windows of wt frames
 __global__ void __launch_bounds__(ENC_THREADS)
-encode_kernel(int ws, int L, int hidden, int R, const float* __restrict__ w,
+encode_kernel(int wt, int ws, int L, int hidden, int R, const float* __restrict__ w,
               float* __restrict__ qp, float* __restrict__ kp) {
   extern __shared__ float sm[];
-  const int F = 2 + 4 * L;
+  const int F = wt ? 3 + 6 * L : 2 + 4 * L;
   float* feat = sm;                     // [ENC_TOK][F]
   float* hid = sm + ENC_TOK * F;        // [ENC_TOK][hidden]
-  const int N = ws * ws;
+  const int N = (wt ? wt : 1) * ws * ws;
   const int n0 = blockIdx.x * ENC_TOK;
 
-  fourier_features(n0, N, ws, L, ENC_TOK, F, feat);
+  if (wt) fourier_features3(n0, N, wt, ws, L, ENC_TOK, F, feat);
+  else fourier_features(n0, N, ws, L, ENC_TOK, F, feat);
   __syncthreads();
 
   // Hidden layer h = ReLU(r W_h + b_h).
@@ -93,7 +123,17 @@ hipError_t launch_encode(int ws, int L, int hidden, int R, const float* w, float
   const int N = ws * ws;
   const int blocks = (N + ENC_TOK - 1) / ENC_TOK;
   const size_t lds = sizeof(float) * ENC_TOK * (size_t)(2 + 4 * L + hidden);
-  hipLaunchKernelGGL(encode_kernel, dim3(blocks), dim3(ENC_THREADS), lds, stream, ws, L, hidden, R,
+  hipLaunchKernelGGL(encode_kernel, dim3(blocks), dim3(ENC_THREADS), lds, stream, 0, ws, L, hidden, R,
+                     w, qp, kp);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode3d(int wt, int ws, int L, int hidden, int R, const float* w, float* qp, float* kp,
+                           hipStream_t stream) {
+  const int N = wt * ws * ws;
+  const int blocks = (N + ENC_TOK - 1) / ENC_TOK;
+  const size_t lds = sizeof(float) * ENC_TOK * (size_t)(3 + 6 * L + hidden);
+  hipLaunchKernelGGL(encode_kernel, dim3(blocks), dim3(ENC_THREADS), lds, stream, wt, ws, L, hidden, R,
                      w, qp, kp);
   return hipGetLastError();
 }

@@ -89,42 +89,46 @@ rib_status rib_attn_supported(int dh, int R, int window, rib_dtype dtype) {
 
 namespace {
 // shared by rib_window_attn (one (qp, kp) pair) and rib_window_attn_heads (a pair per head)
+// T, wt: frames of the map and of a window (1, 1 for images)
 rib_status window_attn(const char* fn, bool per_head, const void* qc, const void* kc, const void* v,
-                       const void* g, const float* qp, const float* kp, void* o, float* lse, int B, int H,
-                       int W, int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
+                       const void* g, const float* qp, const float* kp, void* o, float* lse, int B, int T, int H,
+                       int W, int heads, int dh, int R, int wt, int window, rib_dtype dtype, void* stream) {
   if (!qc || !kc || !v || !g || !qp || !kp || !o)
     return fail(RIB_ERR_INVALID_ARG, "%s: null pointer", fn);
-  if (B < 1 || H < 1 || W < 1 || heads < 1 || dh < 1 || R < 1)
-    return fail(RIB_ERR_INVALID_ARG, "%s: B, H, W, heads, dh, R must be >= 1", fn);
+  if (B < 1 || T < 1 || H < 1 || W < 1 || heads < 1 || dh < 1 || R < 1 || wt < 1)
+    return fail(RIB_ERR_INVALID_ARG, "%s: B, T, H, W, heads, dh, R, frames per window must be >= 1", fn);
   if (window < 2) return fail(RIB_ERR_INVALID_ARG, "%s: window must be >= 2 (got %d)", fn, window);
+  if (wt > 64 || (long)wt * window * window > 16384)
+    return fail(RIB_ERR_UNSUPPORTED, "%s: a window holds at most 16384 tokens (got %d x %d x %d)", fn, wt, window,
+                window);
   if (dtype != RIB_F32 && dtype != RIB_BF16)
     return fail(RIB_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
   const rib_status sup = rib_attn_supported(dh, R, window, dtype);
   if (sup != RIB_OK) return sup;
-  const uint64_t elems = (uint64_t)B * H * W * (uint64_t)heads * dh;
+  const uint64_t elems = (uint64_t)B * T * H * W * (uint64_t)heads * dh;
   if (elems >= (1ull << 31))
-    return fail(RIB_ERR_UNSUPPORTED, "%s: B*H*W*heads*dh must be < 2^31", fn);
+    return fail(RIB_ERR_UNSUPPORTED, "%s: B*T*H*W*heads*dh must be < 2^31", fn);
   if (!aligned(qc, 16) || !aligned(kc, 16) || !aligned(v, 16) || !aligned(g, 16) || !aligned(qp, 16) ||
       !aligned(kp, 16) || !aligned(o, 16))
     return fail(RIB_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
   const size_t nb = (size_t)elems * (dtype == RIB_F32 ? 4 : 2);
-  const size_t np = sizeof(float) * (size_t)window * window * R * (per_head ? heads : 1);
+  const size_t np = sizeof(float) * (size_t)wt * window * window * R * (per_head ? heads : 1);
   if (overlap(o, nb, qc, nb) || overlap(o, nb, kc, nb) || overlap(o, nb, v, nb) || overlap(o, nb, g, nb) ||
       overlap(o, nb, qp, np) || overlap(o, nb, kp, np))
     return fail(RIB_ERR_INVALID_ARG, "%s: output overlaps an input", fn);
   if (lse) {
-    const size_t nl = sizeof(float) * (size_t)B * H * W * heads;
+    const size_t nl = sizeof(float) * (size_t)B * T * H * W * heads;
     const void* ins[] = {qc, kc, v, g, o};
     for (const void* p : ins)
       if (overlap(lse, nl, p, nb)) return fail(RIB_ERR_INVALID_ARG, "%s: lse overlaps a map", fn);
     if (overlap(lse, nl, qp, np) || overlap(lse, nl, kp, np))
       return fail(RIB_ERR_INVALID_ARG, "%s: lse overlaps a positional table", fn);
   }
-  const long tstride = per_head ? (long)window * window * R : 0;
-  const rib::AttnArgs a{qc, kc, v, g, qp, kp, o, B, H, W, heads, dh, R, window, tstride, lse};
+  const long tstride = per_head ? (long)wt * window * window * R : 0;
+  const rib::AttnArgs a{qc, kc, v, g, qp, kp, o, B, H, W, heads, dh, R, window, tstride, lse, T, wt};
   const hipError_t e = dtype == RIB_F32 ? rib::launch_attn_f32(a, (hipStream_t)stream)
                                         : rib::launch_attn_bf16(a, (hipStream_t)stream);
-  return hip_status(e, per_head ? "rib_window_attn_heads launch" : "rib_window_attn launch");
+  return hip_status(e, fn);
 }
 }  // namespace
 
@@ -133,7 +137,7 @@ extern "C" {
 rib_status rib_window_attn(const void* qc, const void* kc, const void* v, const void* g,
                            const float* qp, const float* kp, void* o, int B, int H, int W,
                            int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
-  return window_attn("rib_window_attn", false, qc, kc, v, g, qp, kp, o, nullptr, B, H, W, heads, dh, R,
+  return window_attn("rib_window_attn", false, qc, kc, v, g, qp, kp, o, nullptr, B, 1, H, W, heads, dh, R, 1,
                      window, dtype, stream);
 }
 
@@ -141,15 +145,15 @@ rib_status rib_window_attn_train(const void* qc, const void* kc, const void* v, 
                                  const float* qp, const float* kp, void* o, float* lse, int B, int H, int W,
                                  int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
   if (!lse) return fail(RIB_ERR_INVALID_ARG, "rib_window_attn_train: null pointer");
-  return window_attn("rib_window_attn_train", false, qc, kc, v, g, qp, kp, o, lse, B, H, W, heads, dh, R,
-                     window, dtype, stream);
+  return window_attn("rib_window_attn_train", false, qc, kc, v, g, qp, kp, o, lse, B, 1, H, W, heads, dh, R,
+                     1, window, dtype, stream);
 }
 
 rib_status rib_window_attn_heads(const void* qc, const void* kc, const void* v, const void* g,
                                  const float* qp, const float* kp, void* o, int B, int H, int W,
                                  int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
-  return window_attn("rib_window_attn_heads", true, qc, kc, v, g, qp, kp, o, nullptr, B, H, W, heads, dh,
-                     R, window, dtype, stream);
+  return window_attn("rib_window_attn_heads", true, qc, kc, v, g, qp, kp, o, nullptr, B, 1, H, W, heads, dh,
+                     R, 1, window, dtype, stream);
 }
 
 
@@ -328,6 +332,38 @@ rib_status rib_ln_qkv(const void* x, const float* gamma, const float* beta, cons
   }
   const rib::LnQkvArgs a{x, gamma, beta, w, bias, q, k, v, xn, B, H, W, C, eps};
   return hip_status(rib::launch_ln_qkv(a, dtype == RIB_BF16, (hipStream_t)stream), "rib_ln_qkv launch");
+}
+
+}  // extern "C"
+
+extern "C" {
+
+rib_status rib_encode3d(int frames, int window, int L, int hidden, int R, const float* weights, float* qp,
+                        float* kp, void* stream) {
+  const char* fn = "rib_encode3d";
+  if (!weights || !qp || !kp) return fail(RIB_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (frames < 1 || window < 2)
+    return fail(RIB_ERR_INVALID_ARG, "%s: need frames >= 1, window >= 2 (got %d, %d)", fn, frames, window);
+  if (L < 0 || hidden < 1 || R < 1)
+    return fail(RIB_ERR_INVALID_ARG, "%s: need L >= 0, hidden >= 1, R >= 1 (got %d, %d, %d)", fn, L, hidden, R);
+  if (window > 128 || frames > 64 || (long)frames * window * window > 16384 || L > 16 || hidden > 256 || R > 64)
+    return fail(RIB_ERR_UNSUPPORTED,
+                "%s: limits are frames*window^2 <= 16384, window <= 128, L <= 16, hidden <= 256, R <= 64", fn);
+  if (!aligned(weights, 4) || !aligned(qp, 4) || !aligned(kp, 4))
+    return fail(RIB_ERR_INVALID_ARG, "%s: pointers must be 4-byte aligned", fn);
+  const size_t nw = sizeof(float) * ((size_t)(3 + 6 * L) * hidden + hidden + 2 * (size_t)hidden * R);
+  const size_t no = sizeof(float) * (size_t)frames * window * window * R;
+  if (overlap(qp, no, kp, no) || overlap(qp, no, weights, nw) || overlap(kp, no, weights, nw))
+    return fail(RIB_ERR_INVALID_ARG, "%s: qp, kp and weights must not overlap", fn);
+  return hip_status(rib::launch_encode3d(frames, window, L, hidden, R, weights, qp, kp, (hipStream_t)stream),
+                    "rib_encode3d launch");
+}
+
+rib_status rib_window_attn3d(const void* qc, const void* kc, const void* v, const void* g, const float* qp,
+                             const float* kp, void* o, int B, int T, int H, int W, int heads, int dh, int R,
+                             int frames, int window, rib_dtype dtype, void* stream) {
+  return window_attn("rib_window_attn3d", false, qc, kc, v, g, qp, kp, o, nullptr, B, T, H, W, heads, dh, R, frames,
+                     window, dtype, stream);
 }
 
 }  // extern "C"

@@ -15,10 +15,15 @@ struct AttnArgs {
   int B, H, W, heads, dh, R, ws;
   long tstride;  // floats between the (qp, kp) tables of consecutive heads; 0 = one shared pair
   float* lse;    // optional: row log-sum-exp per (token, head), natural log
+  int T = 1;     // frames of a [B][T][H][W][C] video map (1: images)
+  int wt = 1;    // frames per space-time window (1: 2-D windows)
 };
 
 hipError_t launch_encode(int ws, int L, int hidden, int R, const float* w, float* qp, float* kp,
                          hipStream_t stream);
+// space-time encoder over wt x ws x ws windows (3 coordinates, 3 + 6L features)
+hipError_t launch_encode3d(int wt, int ws, int L, int hidden, int R, const float* w, float* qp, float* kp,
+                           hipStream_t stream);
 
 // fp32 path: any dh <= 64, R <= 64.
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);

@@ -21,7 +21,8 @@ def test_header_declares_the_boundary():
     assert set(rib.header_functions()) == {
         "rib_encode", "rib_window_attn", "rib_attn_supported", "rib_last_error", "rib_abi_version",
         "rib_cla_gate", "rib_window_attn_heads", "rib_window_attn_train", "rib_window_attn_backward", "rib_window_attn_backward_workspace",
-        "rib_encode_backward", "rib_encode_backward_workspace", "rib_ln_qkv"}
+        "rib_encode_backward", "rib_encode_backward_workspace", "rib_ln_qkv", "rib_encode3d",
+        "rib_window_attn3d"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -246,6 +247,31 @@ def test_ln_qkv_validation(L):
     assert "overlap" in L.rib_last_error().decode()
     assert lnq(L, P[:5] + [P[5], P[5], P[7], None]) == rib.RIB_ERR_INVALID_ARG  # q == k
     assert lnq(L, P[:8] + [P[3]]) == rib.RIB_ERR_INVALID_ARG                     # xn == w
+
+
+@fake
+def test_space_time_validation(L):
+    def a3(ptrs=None, **kw):
+        a = dict(B=1, T=4, H=8, W=8, heads=2, dh=30, R=16, frames=2, window=8, dtype=rib.RIB_BF16)
+        a.update(kw)
+        return L.rib_window_attn3d(*(ptrs or P[:7]), a["B"], a["T"], a["H"], a["W"], a["heads"], a["dh"], a["R"],
+                                   a["frames"], a["window"], a["dtype"], None)
+    assert a3([None] + P[1:7]) == rib.RIB_ERR_INVALID_ARG
+    assert "rib_window_attn3d" in L.rib_last_error().decode()
+    assert a3(T=0) == rib.RIB_ERR_INVALID_ARG
+    assert a3(frames=0) == rib.RIB_ERR_INVALID_ARG
+    assert a3(frames=2, window=96) == rib.RIB_ERR_UNSUPPORTED                    # 18432 tokens per window
+    assert "16384" in L.rib_last_error().decode()
+    assert a3(dh=31) == rib.RIB_ERR_UNSUPPORTED
+    assert a3(B=1 << 10, T=1 << 10, H=64, W=64, dh=30) == rib.RIB_ERR_UNSUPPORTED  # >= 2^31 elements
+    # the tables are frames times longer: o just past one 2-D table still overlaps
+    assert a3(P[:6] + [ctypes.c_void_p(P[4].value + 64 * 16 * 4 + 256)]) == rib.RIB_ERR_INVALID_ARG
+    w, q, k = P[0], P[1], P[2]
+    assert L.rib_encode3d(2, 8, 10, 64, 16, None, q, k, None) == rib.RIB_ERR_INVALID_ARG
+    assert L.rib_encode3d(0, 8, 10, 64, 16, w, q, k, None) == rib.RIB_ERR_INVALID_ARG
+    assert L.rib_encode3d(2, 1, 10, 64, 16, w, q, k, None) == rib.RIB_ERR_INVALID_ARG
+    assert L.rib_encode3d(2, 96, 10, 64, 16, w, q, k, None) == rib.RIB_ERR_UNSUPPORTED
+    assert L.rib_encode3d(2, 8, 10, 64, 16, w, q, q, None) == rib.RIB_ERR_INVALID_ARG
 
 
 def test_python_binding_argument_checks():
