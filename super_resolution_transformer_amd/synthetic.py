@@ -121,6 +121,37 @@ def make_problem(B: int, H: int, W: int, heads: int, dh: int, R: int = 16, L: in
     return Problem(B, H, W, heads, dh, R, L, hidden, dtype, *arrs, weights=weights, bits=bits)
 
 
+def make_spike_problem(B: int, H: int, W: int, heads: int, dh: int, R: int, ws: int, a: float, b: float,
+                       dtype: str = "bf16", seed: int = 0) -> Problem:
+    """A problem whose scores jump far above the first key tile's maximum.
+
+    Every head slice of the queries with (y + x) even is replaced by a * e_0; in
+    every window two keys at in-window (row, column) positions (ws // 3, 7) and
+    (2 * ws // 3, ws // 2 + 1), where they exist, get b * e_0.  For those
+    queries the two keys score a * b / sqrt(dh) (plus the positional bias),
+    far above every other key, so the softmax is dominated by keys that are
+    not in the first tile.  a and b should be exact in bf16."""
+    p = make_problem(B, H, W, heads, dh, R, dtype=dtype, seed=seed)
+    qc, kc = p.qc.copy(), p.kc.copy()
+    yy, xx = np.meshgrid(np.arange(H), np.arange(W), indexing="ij")
+    even = (yy + xx) % 2 == 0
+    spike = np.zeros((H, W), bool)
+    for (iy, ix) in ((ws // 3, 7), (2 * ws // 3, ws // 2 + 1)):
+        if iy < ws and ix < ws:
+            spike |= ((yy % ws) == iy) & ((xx % ws) == ix)
+    e0 = np.zeros(dh, np.float32)
+    e0[0] = 1.0
+    for h in range(heads):
+        sl = slice(h * dh, (h + 1) * dh)
+        qc[:, even, sl] = a * e0
+        kc[:, spike, sl] = b * e0
+    p.qc, p.kc = qc, kc
+    if dtype == "bf16":
+        p.bits["qc"], p.qc = round_bf16(qc)
+        p.bits["kc"], p.kc = round_bf16(kc)
+    return p
+
+
 def config_problem(idx: int, batch: int | None = None) -> Problem:
     """Inputs of one of the five workloads (``batch`` overrides B, e.g. for a CPU sample)."""
     c = CONFIGS[idx]
