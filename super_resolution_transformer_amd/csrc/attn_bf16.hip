@@ -35,7 +35,8 @@
 //    the maximum grew by more than OFF+1 = 8 (a factor 256).  Only then (and on
 //    the first tile) does the wave take the slow path: exact row maximum, new
 //    m_hat rounded to bf16, recompute, rescale O.
-//  * The row sum l comes for free from the PV MFMA: V channel dh is all ones.
+//  * The row sum l comes for free from the PV MFMA: V channel dh is all ones
+//    (a head of 32 channels, which has no spare channel, sums P with v_dot2).
 //  * Ping-pong over key tiles of KT = 64.  A workgroup has 8 waves, two per
 //    SIMD, in two groups (waves 0-3 and 4-7) that run half a step apart and
 //    swap roles at every barrier: while one group runs its MFMA phase
@@ -71,7 +72,11 @@ template <int DH, int R>
 struct Shape {
   static_assert(DH % 2 == 0 && R % 8 == 0, "head dim must be even, rank a multiple of 8");
   static constexpr int KC = (R + DH + 2 + 15) / 16;  // 16-wide contraction chunks
-  static constexpr int DT = (DH + 1 + 31) / 32;      // 32-channel output tiles (ones row at DH)
+  // The row sum l rides along the PV product as V channel DH (all ones) when the
+  // last 32-channel output tile has room for it; a head of 32 channels would
+  // need a whole second tile for it, so there l is summed from P with v_dot2.
+  static constexpr bool ONES = DH % 32 != 0;
+  static constexpr int DT = (DH + (ONES ? 1 : 0) + 31) / 32;  // 32-channel output tiles
   static constexpr int ROWDW = 8 * KC;               // dwords per Q~/K~ row
   static constexpr int KCH = 2 * KC;                 // 16-byte chunks per K~ row
   static constexpr int KSTR = ROWDW + 4;             // row stride of the Q~ staging rows (bank spread)
@@ -223,10 +228,11 @@ __device__ __forceinline__ uint32_t kc_word(int w, uint32_t data, bool real) {
   if (w == DH / 2) return real ? 0x3F803F80u : 0x46800000u;  // (1,1) real, (0,2^14) padded
   return 0u;
 }
-// dword w of the V row: value, the ones pair at channel DH, or zero
+// dword w of the V row: value, the ones pair at channel DH (when the tile has
+// room for it), or zero
 template <int DH>
 __device__ __forceinline__ uint32_t v_word(int w, uint32_t data, bool real) {
-  uint32_t val = w < DH / 2 ? data : (w == DH / 2 ? 0x00003F80u : 0u);
+  uint32_t val = w < DH / 2 ? data : (w == DH / 2 && DH % 32 != 0 ? 0x00003F80u : 0u);
   return real ? val : 0u;
 }
 
@@ -311,7 +317,22 @@ struct Regs {
   f32x16_t O[2][S::DT];
   u32x4_t qt[2][S::KC];
   float mhat[2];
+  float lpart[2];  // this lane's share of l (only when l is not a V channel)
 };
+
+// l of the lane's query of block qb: the ones channel of the PV product, or
+// the two lane halves' partial sums
+template <int DH, int R>
+__device__ __forceinline__ float row_sum(const Regs<DH, R>& rg, int qb) {
+  using S = Shape<DH, R>;
+  if constexpr (S::ONES) {
+    const LanePair pr = lane_pair(rg.O[qb][S::LT][S::LR]);
+    return S::LG ? pr.hi : pr.lo;
+  } else {
+    const LanePair pr = lane_pair(rg.lpart[qb]);
+    return pr.lo + pr.hi;
+  }
+}
 
 // Operands of one MFMA phase, all read from LDS before the first MFMA issues:
 // the K~ rows of the tile being scored (A operand of S^T = K~ Q~^T) and the
@@ -425,6 +446,7 @@ __device__ __forceinline__ void rescale_tile(Regs<DH, R>& rg, const f32x16_t (&S
       for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) rg.O[qb][dt][e] *= sc;
+      if constexpr (!S::ONES) rg.lpart[qb] *= sc;
     }
     const uint32_t cd = pack_bf16(-mnew, -OFF);
     if (gh == S::GM) rg.qt[qb][S::CM][S::DM] = cd;
@@ -458,10 +480,20 @@ __device__ __forceinline__ void read_v_ops(const uint32_t* lds, int vst, int lan
       }
 }
 
-// O^T += V^T P^T
+// O^T += V^T P^T (and, without a ones channel, l += the lane's p values)
 template <int DH, int R>
 __device__ __forceinline__ void pv_tile(const PhaseOps<DH, R>& ops, Regs<DH, R>& rg, const uint32_t (&P)[2][2][8]) {
   using S = Shape<DH, R>;
+  if constexpr (!S::ONES) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          rg.lpart[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, P[qb][kb][i]),
+                                                         __builtin_bit_cast(bf16x2_t, 0x3F803F80u), rg.lpart[qb], false);
+  }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -547,6 +579,7 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
 #pragma unroll
       for (int e = 0; e < 16; ++e) rg.O[qb][dt][e] = 0.0f;
     rg.mhat[qb] = 0.0f;
+    rg.lpart[qb] = 0.0f;
   }
   __syncthreads();
 
@@ -674,8 +707,7 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int r = q0 + wave * QW + qb * 32 + l32;
-    const LanePair pr = lane_pair(rg.O[qb][S::LT][S::LR]);
-    const float lsum = S::LG ? pr.hi : pr.lo;
+    const float lsum = row_sum(rg, qb);
     if (r >= G.n_real) continue;
     const float inv = 1.0f / lsum;
     int off, n;
@@ -827,6 +859,7 @@ attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
 #pragma unroll
       for (int e = 0; e < 16; ++e) rg.O[qb][dt][e] = 0.0f;
     rg.mhat[qb] = 0.0f;
+    rg.lpart[qb] = 0.0f;
   }
   __syncthreads();
   if (wave * QW >= G.n_real) return;  // no barrier follows
@@ -849,8 +882,7 @@ attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int r = wave * QW + qb * 32 + l32;
-    const LanePair pr = lane_pair(rg.O[qb][S::LT][S::LR]);
-    const float lsum = S::LG ? pr.hi : pr.lo;
+    const float lsum = row_sum(rg, qb);
     if (r >= G.n_real) continue;
     const float inv = 1.0f / lsum;
     if (lse) lse[(offq[qb] - G.h * DH) / G.C * heads + G.h] = (rg.mhat[qb] + OFF + __log2f(lsum)) * LN2;
