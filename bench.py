@@ -216,6 +216,48 @@ def time_space_time(torch, rib, synthetic):
     return res
 
 
+def time_cyclic(torch, rib, synthetic):
+    """The cyclic window schedule (16, 32, 64) on the SST-lite shape (1 x 180x320, C=48, 3 heads x dh 16, R=16,
+    bf16) and on the inference shape (C=180, 6 heads x dh 30): three independent rib_window_attn calls one
+    after another, and the same three calls in one rib_window_attn_multi."""
+    res = {}
+    for label, heads, dh in (("1x180x320, C=48", 3, 16), ("1x180x320, C=180", 6, 30)):
+        calls = []
+        pairs = 0
+        for k, ws in enumerate((16, 32, 64)):
+            p = synthetic.make_problem(1, 180, 320, heads, dh, 16, dtype="bf16", seed=40 + k)
+            maps = [torch.from_numpy(p.bits[n].view("int16")).view(torch.bfloat16).cuda() for n in ("qc", "kc", "v", "g")]
+            qp, kp = rib.encode(ws, p.L, p.hidden, p.R, torch.from_numpy(p.weights).cuda())
+            calls.append((*maps, qp, kp, heads, ws))
+            for y0 in range(0, 180, ws):
+                for x0 in range(0, 320, ws):
+                    n = (min(180, y0 + ws) - y0) * (min(320, x0 + ws) - x0)
+                    pairs += n * n
+        outs = [torch.empty_like(c[0]) for c in calls]
+
+        def timed(fn, reps=50):
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            return s.elapsed_time(e) / reps
+        ms_sep = timed(lambda: [rib.window_attn_into(*c, o) for c, o in zip(calls, outs)])
+        ms_multi = timed(lambda: rib.window_attn_multi_into(calls, outs))
+        flops = heads * pairs * (2 * (dh + 16) + 2 * dh)
+        res[f"windows 16+32+64, {label}"] = {
+            "ms_three_calls": ms_sep, "ms_one_multi_call": ms_multi,
+            "tflops_multi": flops / (ms_multi * 1e-3) / 1e12,
+            "pct_bf16_peak_multi": 100 * flops / (ms_multi * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        del calls, outs
+        torch.cuda.empty_cache()
+    return res
+
+
 def time_ln_qkv(torch, rib, synthetic):
     """Block input projection (rib_ln_qkv: LayerNorm, then x W + b into Q | K | V, plus LN(X) for the
     gate) on the workloads' maps, bf16; HBM roofline.  Algorithmic bytes: X read, Q, K, V and LN(X)
@@ -424,6 +466,7 @@ def main():
         out["cla_gate"] = time_gate(torch, rib, synthetic)
         out["ln_qkv"] = time_ln_qkv(torch, rib, synthetic)
         out["space_time"] = time_space_time(torch, rib, synthetic)
+        out["cyclic_schedule"] = time_cyclic(torch, rib, synthetic)
         out["backward"] = {"96x96 window, 32x96x96": time_backward(torch, rib, synthetic, 4, 96, args.backward_reps),
                            "64x64 window, 1x180x320": time_backward(torch, rib, synthetic, 3, 64,
                                                                     3 * args.backward_reps)}

@@ -116,6 +116,39 @@ rib_status rib_window_attn_heads(const void* qc, const void* kc, const void* v, 
                                  int heads, int dh, int R, int window, rib_dtype dtype, void* stream);
 
 /*
+ * rib_window_attn_multi -- several independent rib_window_attn calls in as
+ * few kernel launches as possible.  The window size of the SST blocks cycles
+ * through 16, 32 and 64 (explainer section 3.2 "cyclic window strategy"); a
+ * caller holding independent work at several points of that cycle (other
+ * images, other streams of a batch, or the three window sizes of one shape)
+ * passes the calls together, and the library runs them side by side:
+ * RIB_BF16 calls that share (dh, R) take one launch per kernel kind (windows
+ * of <= 256 tokens, larger windows) and per 8 calls, largest windows first;
+ * RIB_F32 calls run one after another.  Each call's output is bit-identical to
+ * that of rib_window_attn with the same arguments.
+ *
+ * calls : host array of n call descriptions (read; not kept after return);
+ *         each field as the argument of the same name of rib_window_attn
+ *         (one shared (qp, kp) pair per call, window sizes may differ).
+ * n     : 1 <= n <= RIB_MAX_CALLS.
+ * Errors: every call is validated as rib_window_attn validates its arguments,
+ *         and no call's output may overlap an argument of another call;
+ *         on any error nothing is launched.
+ */
+#define RIB_MAX_CALLS 16
+typedef struct {
+  const void* qc;
+  const void* kc;
+  const void* v;
+  const void* g;
+  const float* qp;
+  const float* kp;
+  void* o;
+  int B, H, W, heads, dh, R, window;
+} rib_attn_call;
+rib_status rib_window_attn_multi(int n, const rib_attn_call* calls, rib_dtype dtype, void* stream);
+
+/*
  * rib_window_attn_train -- rib_window_attn that also writes the row
  * log-sum-exp the backward needs (the training iteration of explainer
  * section 4.1: forward, then rib_window_attn_backward):
@@ -270,7 +303,7 @@ const char* rib_last_error(void);
 /* ABI version of this header (incremented on any incompatible change). */
 int rib_abi_version(void);
 
-#define RIB_ABI_VERSION 7
+#define RIB_ABI_VERSION 8
 
 #ifdef __cplusplus
 }

@@ -39,6 +39,14 @@ class RibError(RuntimeError):
         self.status = status
 
 
+class AttnCall(ctypes.Structure):
+    """rib_attn_call: one call of rib_window_attn_multi."""
+    _fields_ = [("qc", ctypes.c_void_p), ("kc", ctypes.c_void_p), ("v", ctypes.c_void_p), ("g", ctypes.c_void_p),
+                ("qp", ctypes.c_void_p), ("kp", ctypes.c_void_p), ("o", ctypes.c_void_p),
+                ("B", ctypes.c_int), ("H", ctypes.c_int), ("W", ctypes.c_int), ("heads", ctypes.c_int),
+                ("dh", ctypes.c_int), ("R", ctypes.c_int), ("window", ctypes.c_int)]
+
+
 def lib(path: str | None = None):
     """Load librib.so (built in-tree by ``build.py``); raise if it is not there."""
     global _lib
@@ -75,6 +83,8 @@ def lib(path: str | None = None):
     L.rib_encode3d.restype = i
     L.rib_window_attn3d.argtypes = [vp] * 7 + [i] * 10 + [vp]
     L.rib_window_attn3d.restype = i
+    L.rib_window_attn_multi.argtypes = [i, ctypes.POINTER(AttnCall), i, vp]
+    L.rib_window_attn_multi.restype = i
     L.rib_attn_supported.argtypes = [i, i, i, i]
     L.rib_attn_supported.restype = i
     L.rib_last_error.argtypes = []
@@ -171,6 +181,41 @@ def window_attn_into(qc, kc, v, g, qp, kp, heads: int, window: int, o) -> None:
     fn = lib().rib_window_attn_heads if per_head else lib().rib_window_attn
     _check(fn(_ptr(qc), _ptr(kc), _ptr(v), _ptr(g), _ptr(qp), _ptr(kp), _ptr(o),
               B, H, W, heads, dh, R, window, _dtype_code(qc), _stream(qc)))
+
+
+def window_attn_multi(calls):
+    """Several independent window_attn calls in as few launches as possible.
+
+    calls: list of (qc, kc, v, g, qp, kp, heads, window), all of one dtype; window sizes and
+    shapes may differ.  Returns the list of outputs, each equal to window_attn's."""
+    import torch
+    outs = [torch.empty_like(c[0]) for c in calls]
+    window_attn_multi_into(calls, outs)
+    return outs
+
+
+def window_attn_multi_into(calls, outs) -> None:
+    import torch
+    if len(calls) != len(outs) or not calls:
+        raise ValueError("need one output per call and at least one call")
+    arr = (AttnCall * len(calls))()
+    dtype = calls[0][0].dtype
+    for k, ((qc, kc, v, g, qp, kp, heads, window), o) in enumerate(zip(calls, outs)):
+        ts = (qc, kc, v, g, o)
+        if any(t.dim() != 4 or t.shape != qc.shape or t.dtype != dtype for t in ts):
+            raise ValueError("each call's qc, kc, v, g, o must be [B, H, W, C] of the batch's dtype")
+        if not all(t.is_cuda and t.is_contiguous() for t in ts + (qp, kp)):
+            raise ValueError("all tensors must be contiguous GPU tensors")
+        if qp.dtype != torch.float32 or kp.dtype != torch.float32 or qp.shape != kp.shape or qp.dim() != 2:
+            raise ValueError("qp, kp must be float32 [window*window, R]")
+        if qp.shape[0] != window * window:
+            raise ValueError("qp, kp must have window*window rows")
+        B, H, W, C = qc.shape
+        if heads < 1 or C % heads:
+            raise ValueError("channel count must be a multiple of heads")
+        arr[k] = AttnCall(_ptr(qc), _ptr(kc), _ptr(v), _ptr(g), _ptr(qp), _ptr(kp), _ptr(o),
+                          B, H, W, heads, C // heads, qp.shape[1], window)
+    _check(lib().rib_window_attn_multi(len(calls), arr, _dtype_code(calls[0][0]), _stream(calls[0][0])))
 
 
 def window_attn_train(qc, kc, v, g, qp, kp, heads: int, window: int):

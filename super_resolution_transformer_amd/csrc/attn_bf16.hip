@@ -508,17 +508,16 @@ __device__ __forceinline__ void pv_tile(const PhaseOps<DH, R>& ops, Regs<DH, R>&
       }
 }
 
+// One workgroup of the tiled kernel: logical = (window unit) * qblocks + query block.
 template <int DH, int R>
-__global__ void __launch_bounds__(QB, 1)
-attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
+__device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
                  const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                  const float* __restrict__ qp, const float* __restrict__ kp,
                  uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws, int total,
-                 long tstride, float* __restrict__ lse) {
+                 long tstride, float* __restrict__ lse, int logical) {
   using S = Shape<DH, R>;
   __shared__ __attribute__((aligned(16))) uint32_t lds[S::LDS_DW];
 
-  const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
   if (logical >= total) return;
   const int NW = wt * ws * ws;  // tokens of a full window
   const int qblocks = (NW + QB - 1) / QB;
@@ -767,18 +766,17 @@ __device__ __forceinline__ uint32_t qrow_word(int w, int off, int n, bool real, 
   return (real || w == S::CONSTDW) ? val : 0u;
 }
 
+// One workgroup of the whole-window kernel: logical = window unit.
 template <int DH, int R>
-__global__ void __launch_bounds__(SQ, 2)
-attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
+__device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
                        const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                        const float* __restrict__ qp, const float* __restrict__ kp,
                        uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws,
-                       int total, long tstride, float* __restrict__ lse) {
+                       int total, long tstride, float* __restrict__ lse, int logical) {
   using S = Shape<DH, R>;
   using RL = Roles<DH, R>;
   __shared__ __attribute__((aligned(16))) uint32_t lds[SNT * S::STAGE_DW];
 
-  const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
   if (logical >= total) return;
   Geo G;
   decode_window<DH>(G, logical, T, H, W, heads, wt, ws);
@@ -908,6 +906,90 @@ attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
 }
 
 template <int DH, int R>
+__global__ void __launch_bounds__(QB, 1)
+attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
+                 const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
+                 const float* __restrict__ qp, const float* __restrict__ kp,
+                 uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws, int total,
+                 long tstride, float* __restrict__ lse) {
+  attn_tiled_body<DH, R>(qc, kc, v, g, qp, kp, o, B, T, H, W, heads, wt, ws, total, tstride, lse,
+                         xcd_swizzle(blockIdx.x, gridDim.x));
+}
+
+template <int DH, int R>
+__global__ void __launch_bounds__(SQ, 2)
+attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
+                       const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
+                       const float* __restrict__ qp, const float* __restrict__ kp,
+                       uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws,
+                       int total, long tstride, float* __restrict__ lse) {
+  attn_small_body<DH, R>(qc, kc, v, g, qp, kp, o, B, T, H, W, heads, wt, ws, total, tstride, lse,
+                         xcd_swizzle(blockIdx.x, gridDim.x));
+}
+
+// ---- several independent calls in one launch ---------------------------------
+// The calls of a group share the kernel variant (dh, R, whole-window or tiled)
+// and otherwise differ freely (maps, window sizes, tables).  Each call owns a
+// contiguous range of the grid, a multiple of 8 workgroups long, so that the
+// dispatcher's round-robin over the 8 XCDs gives every XCD the same share of
+// every call; inside a call, window unit 8k + x takes workgroups whose index is
+// x mod 8, i.e. all query blocks of one (window, head) run on one XCD and share
+// its L2.  The host orders the calls longest first.
+constexpr int GROUP_MAX = 8;
+
+struct CallDesc {
+  const uint32_t* qc;
+  const uint32_t* kc;
+  const uint32_t* v;
+  const uint32_t* g;
+  const float* qp;
+  const float* kp;
+  uint32_t* o;
+  float* lse;
+  long tstride;
+  int B, T, H, W, heads, wt, ws, units, qblocks;
+};
+
+struct CallGroup {
+  int n;
+  int first[GROUP_MAX + 1];  // first workgroup of each call; first[n] = grid size
+  CallDesc c[GROUP_MAX];
+};
+
+// this workgroup's call (every index static: the selection stays in SGPRs)
+__device__ __forceinline__ int group_call(const CallGroup& grp, int bid, CallDesc& c) {
+  int i = 0;
+  c = grp.c[0];
+#pragma unroll
+  for (int k = 1; k < GROUP_MAX; ++k)
+    if (k < grp.n && bid >= grp.first[k]) {
+      c = grp.c[k];
+      i = k;
+    }
+  return bid - grp.first[i];
+}
+
+template <int DH, int R>
+__global__ void __launch_bounds__(QB, 1) attn_bf16_group_kernel(const CallGroup grp) {
+  CallDesc c;
+  const int lb = group_call(grp, blockIdx.x, c);
+  const int per = 8 * c.qblocks;
+  const int unit = (lb / per) * 8 + lb % 8;
+  if (unit >= c.units) return;
+  attn_tiled_body<DH, R>(c.qc, c.kc, c.v, c.g, c.qp, c.kp, c.o, c.B, c.T, c.H, c.W, c.heads, c.wt, c.ws,
+                         c.units * c.qblocks, c.tstride, c.lse, unit * c.qblocks + (lb % per) / 8);
+}
+
+template <int DH, int R>
+__global__ void __launch_bounds__(SQ, 2) attn_bf16_small_group_kernel(const CallGroup grp) {
+  CallDesc c;
+  const int lb = group_call(grp, blockIdx.x, c);
+  if (lb >= c.units) return;
+  attn_small_body<DH, R>(c.qc, c.kc, c.v, c.g, c.qp, c.kp, c.o, c.B, c.T, c.H, c.W, c.heads, c.wt, c.ws,
+                         c.units, c.tstride, c.lse, lb);
+}
+
+template <int DH, int R>
 hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
   const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws, nWt = (a.T + a.wt - 1) / a.wt;
   const int NW = a.wt * a.ws * a.ws;
@@ -930,11 +1012,92 @@ hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// window units of a call and whether it takes the whole-window kernel
+inline int call_units(const AttnArgs& a) {
+  const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws, nWt = (a.T + a.wt - 1) / a.wt;
+  return a.B * nWt * nWy * nWx * a.heads;
+}
+inline bool call_small(const AttnArgs& a) { return a.wt * a.ws * a.ws <= SQ; }
+inline int call_qblocks(const AttnArgs& a) { return (a.wt * a.ws * a.ws + QB - 1) / QB; }
+
+template <int DH, int R>
+hipError_t launch_group(const AttnArgs* const* calls, int n, bool small, hipStream_t stream) {
+  CallGroup grp{};
+  grp.n = n;
+  int first = 0;
+  for (int i = 0; i < n; ++i) {
+    const AttnArgs& a = *calls[i];
+    CallDesc& c = grp.c[i];
+    c.qc = (const uint32_t*)a.qc;
+    c.kc = (const uint32_t*)a.kc;
+    c.v = (const uint32_t*)a.v;
+    c.g = (const uint32_t*)a.g;
+    c.qp = a.qp;
+    c.kp = a.kp;
+    c.o = (uint32_t*)a.o;
+    c.lse = a.lse;
+    c.tstride = a.tstride;
+    c.B = a.B; c.T = a.T; c.H = a.H; c.W = a.W; c.heads = a.heads; c.wt = a.wt; c.ws = a.ws;
+    c.units = call_units(a);
+    c.qblocks = small ? 1 : call_qblocks(a);
+    grp.first[i] = first;
+    first += 8 * ((c.units + 7) / 8) * c.qblocks;
+  }
+  grp.first[n] = first;
+  if (small)
+    hipLaunchKernelGGL((attn_bf16_small_group_kernel<DH, R>), dim3(first), dim3(SQ), 0, stream, grp);
+  else
+    hipLaunchKernelGGL((attn_bf16_group_kernel<DH, R>), dim3(first), dim3(QB), 0, stream, grp);
+  return hipGetLastError();
+}
+
+// all calls share (dh, R): whole-window calls in groups of the whole-window
+// kernel, the others in groups of the tiled kernel, longest windows first
+template <int DH, int R>
+hipError_t launch_multi_variant(const AttnArgs* calls, int n, hipStream_t stream) {
+  for (int small = 1; small >= 0; --small) {
+    const AttnArgs* sel[64];
+    int m = 0;
+    for (int i = 0; i < n && m < 64; ++i)
+      if (call_small(calls[i]) == (small != 0)) sel[m++] = &calls[i];
+    // longest first: key tiles per window (stable insertion sort)
+    for (int i = 1; i < m; ++i) {
+      const AttnArgs* x = sel[i];
+      const int kx = x->wt * x->ws * x->ws;
+      int j = i - 1;
+      while (j >= 0 && sel[j]->wt * sel[j]->ws * sel[j]->ws < kx) {
+        sel[j + 1] = sel[j];
+        --j;
+      }
+      sel[j + 1] = x;
+    }
+    for (int i = 0; i < m; i += GROUP_MAX) {
+      const hipError_t e = launch_group<DH, R>(sel + i, m - i < GROUP_MAX ? m - i : GROUP_MAX, small != 0, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
 }  // namespace
 
 bool attn_bf16_supported(int dh, int R) {
   return (dh == 8 && R == 8) || (dh == 16 && R == 16) || (dh == 30 && R == 16) ||
          (dh == 32 && R == 16) || (dh == 16 && R == 32) || (dh == 30 && R == 32);
+}
+
+hipError_t launch_attn_bf16_multi(const AttnArgs* calls, int n, hipStream_t stream) {
+  if (n < 1 || n > 64) return hipErrorInvalidValue;
+  const int dh = calls[0].dh, R = calls[0].R;
+  for (int i = 1; i < n; ++i)
+    if (calls[i].dh != dh || calls[i].R != R) return hipErrorInvalidValue;
+  if (dh == 8 && R == 8) return launch_multi_variant<8, 8>(calls, n, stream);
+  if (dh == 16 && R == 16) return launch_multi_variant<16, 16>(calls, n, stream);
+  if (dh == 30 && R == 16) return launch_multi_variant<30, 16>(calls, n, stream);
+  if (dh == 32 && R == 16) return launch_multi_variant<32, 16>(calls, n, stream);
+  if (dh == 16 && R == 32) return launch_multi_variant<16, 32>(calls, n, stream);
+  if (dh == 30 && R == 32) return launch_multi_variant<30, 32>(calls, n, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream) {

@@ -90,9 +90,9 @@ rib_status rib_attn_supported(int dh, int R, int window, rib_dtype dtype) {
 namespace {
 // shared by rib_window_attn (one (qp, kp) pair) and rib_window_attn_heads (a pair per head)
 // T, wt: frames of the map and of a window (1, 1 for images)
-rib_status window_attn(const char* fn, bool per_head, const void* qc, const void* kc, const void* v,
-                       const void* g, const float* qp, const float* kp, void* o, float* lse, int B, int T, int H,
-                       int W, int heads, int dh, int R, int wt, int window, rib_dtype dtype, void* stream) {
+rib_status check_attn(const char* fn, bool per_head, const void* qc, const void* kc, const void* v,
+                      const void* g, const float* qp, const float* kp, void* o, float* lse, int B, int T, int H,
+                      int W, int heads, int dh, int R, int wt, int window, rib_dtype dtype, rib::AttnArgs& a) {
   if (!qc || !kc || !v || !g || !qp || !kp || !o)
     return fail(RIB_ERR_INVALID_ARG, "%s: null pointer", fn);
   if (B < 1 || T < 1 || H < 1 || W < 1 || heads < 1 || dh < 1 || R < 1 || wt < 1)
@@ -125,7 +125,17 @@ rib_status window_attn(const char* fn, bool per_head, const void* qc, const void
       return fail(RIB_ERR_INVALID_ARG, "%s: lse overlaps a positional table", fn);
   }
   const long tstride = per_head ? (long)wt * window * window * R : 0;
-  const rib::AttnArgs a{qc, kc, v, g, qp, kp, o, B, H, W, heads, dh, R, window, tstride, lse, T, wt};
+  a = rib::AttnArgs{qc, kc, v, g, qp, kp, o, B, H, W, heads, dh, R, window, tstride, lse, T, wt};
+  return RIB_OK;
+}
+
+rib_status window_attn(const char* fn, bool per_head, const void* qc, const void* kc, const void* v,
+                       const void* g, const float* qp, const float* kp, void* o, float* lse, int B, int T, int H,
+                       int W, int heads, int dh, int R, int wt, int window, rib_dtype dtype, void* stream) {
+  rib::AttnArgs a{};
+  const rib_status st = check_attn(fn, per_head, qc, kc, v, g, qp, kp, o, lse, B, T, H, W, heads, dh, R, wt,
+                                   window, dtype, a);
+  if (st != RIB_OK) return st;
   const hipError_t e = dtype == RIB_F32 ? rib::launch_attn_f32(a, (hipStream_t)stream)
                                         : rib::launch_attn_bf16(a, (hipStream_t)stream);
   return hip_status(e, fn);
@@ -154,6 +164,54 @@ rib_status rib_window_attn_heads(const void* qc, const void* kc, const void* v, 
                                  int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
   return window_attn("rib_window_attn_heads", true, qc, kc, v, g, qp, kp, o, nullptr, B, 1, H, W, heads, dh,
                      R, 1, window, dtype, stream);
+}
+
+rib_status rib_window_attn_multi(int n, const rib_attn_call* calls, rib_dtype dtype, void* stream) {
+  const char* fn = "rib_window_attn_multi";
+  if (!calls) return fail(RIB_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (n < 1 || n > RIB_MAX_CALLS)
+    return fail(RIB_ERR_INVALID_ARG, "%s: n must be in [1, %d] (got %d)", fn, RIB_MAX_CALLS, n);
+  rib::AttnArgs args[RIB_MAX_CALLS];
+  size_t bytes[RIB_MAX_CALLS];
+  for (int i = 0; i < n; ++i) {
+    const rib_attn_call& c = calls[i];
+    const rib_status st = check_attn(fn, false, c.qc, c.kc, c.v, c.g, c.qp, c.kp, c.o, nullptr, c.B, 1, c.H, c.W,
+                                     c.heads, c.dh, c.R, 1, c.window, dtype, args[i]);
+    if (st != RIB_OK) return st;
+    bytes[i] = (size_t)c.B * c.H * c.W * (size_t)c.heads * c.dh * (dtype == RIB_F32 ? 4 : 2);
+  }
+  // no call may write what another call reads or writes
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j) {
+      if (i == j) continue;
+      const rib_attn_call& a = calls[i];
+      const rib_attn_call& b = calls[j];
+      const size_t np = sizeof(float) * (size_t)b.window * b.window * b.R;
+      if (overlap(a.o, bytes[i], b.qc, bytes[j]) || overlap(a.o, bytes[i], b.kc, bytes[j]) ||
+          overlap(a.o, bytes[i], b.v, bytes[j]) || overlap(a.o, bytes[i], b.g, bytes[j]) ||
+          overlap(a.o, bytes[i], b.o, bytes[j]) || overlap(a.o, bytes[i], b.qp, np) ||
+          overlap(a.o, bytes[i], b.kp, np))
+        return fail(RIB_ERR_INVALID_ARG, "%s: the output of call %d overlaps an argument of call %d", fn, i, j);
+    }
+  hipError_t e = hipSuccess;
+  if (dtype == RIB_F32) {
+    for (int i = 0; i < n && e == hipSuccess; ++i) e = rib::launch_attn_f32(args[i], (hipStream_t)stream);
+  } else {
+    // one multi launch per (dh, R) variant present, in order of first appearance
+    bool done[RIB_MAX_CALLS] = {};
+    for (int i = 0; i < n && e == hipSuccess; ++i) {
+      if (done[i]) continue;
+      rib::AttnArgs sel[RIB_MAX_CALLS];
+      int m = 0;
+      for (int j = i; j < n; ++j)
+        if (!done[j] && args[j].dh == args[i].dh && args[j].R == args[i].R) {
+          sel[m++] = args[j];
+          done[j] = true;
+        }
+      e = rib::launch_attn_bf16_multi(sel, m, (hipStream_t)stream);
+    }
+  }
+  return hip_status(e, fn);
 }
 
 

@@ -31,6 +31,9 @@ hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 // bf16 MFMA path: returns hipErrorInvalidValue if (dh, R) has no compiled variant.
 bool attn_bf16_supported(int dh, int R);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
+// several independent bf16 calls sharing (dh, R) in as few launches as possible
+// (one per kernel kind and per 8 calls); n <= 64
+hipError_t launch_attn_bf16_multi(const AttnArgs* calls, int n, hipStream_t stream);
 
 struct GateArgs {
   const void* x;

@@ -22,7 +22,7 @@ def test_header_declares_the_boundary():
         "rib_encode", "rib_window_attn", "rib_attn_supported", "rib_last_error", "rib_abi_version",
         "rib_cla_gate", "rib_window_attn_heads", "rib_window_attn_train", "rib_window_attn_backward", "rib_window_attn_backward_workspace",
         "rib_encode_backward", "rib_encode_backward_workspace", "rib_ln_qkv", "rib_encode3d",
-        "rib_window_attn3d"}
+        "rib_window_attn3d", "rib_window_attn_multi"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -274,6 +274,35 @@ def test_space_time_validation(L):
     assert L.rib_encode3d(2, 8, 10, 64, 16, w, q, q, None) == rib.RIB_ERR_INVALID_ARG
 
 
+@fake
+def test_multi_validation(L):
+    def call(base=0, **kw):
+        a = dict(B=1, H=8, W=8, heads=2, dh=30, R=16, window=8)
+        a.update(kw)
+        ptrs = [ctypes.c_void_p(p.value + base) for p in P[:7]]
+        return rib.AttnCall(*[p.value for p in ptrs], a["B"], a["H"], a["W"], a["heads"], a["dh"], a["R"],
+                            a["window"])
+
+    def multi(calls, n=None, dtype=rib.RIB_BF16):
+        arr = (rib.AttnCall * max(len(calls), 1))(*calls)
+        return L.rib_window_attn_multi(len(calls) if n is None else n, arr, dtype, None)
+
+    assert L.rib_window_attn_multi(1, None, rib.RIB_BF16, None) == rib.RIB_ERR_INVALID_ARG
+    assert "rib_window_attn_multi" in L.rib_last_error().decode()
+    assert multi([call()], n=0) == rib.RIB_ERR_INVALID_ARG
+    assert multi([call()] * 17) == rib.RIB_ERR_INVALID_ARG                     # more than RIB_MAX_CALLS
+    assert multi([call(), call(MB, window=1)]) == rib.RIB_ERR_INVALID_ARG      # one bad call fails the batch
+    assert multi([call(), call(MB, dh=31)]) == rib.RIB_ERR_UNSUPPORTED
+    bad = call(MB)
+    bad.o = P[2].value + 256                                                  # output of call 1 inside v of call 0
+    assert multi([call(), bad]) == rib.RIB_ERR_INVALID_ARG
+    assert "overlap" in L.rib_last_error().decode()
+    same_out = call(MB)
+    same_out.o = P[6].value                                                   # both calls write one buffer
+    assert multi([call(), same_out]) == rib.RIB_ERR_INVALID_ARG
+    assert multi([call()], dtype=9) == rib.RIB_ERR_INVALID_ARG
+
+
 def test_python_binding_argument_checks():
     torch = pytest.importorskip("torch")
     x = torch.zeros(1, 4, 4, 8)
@@ -297,3 +326,7 @@ def test_python_binding_argument_checks():
         rib.encode_backward(4, 10, 64, 16, torch.zeros(3), torch.zeros(16, 16), torch.zeros(16, 16))
     with pytest.raises(ValueError):
         rib.cla_gate_into(x, torch.zeros(8, 9), torch.zeros(8), torch.zeros(8, 8), torch.zeros(8), x)
+    with pytest.raises(ValueError):
+        rib.window_attn_multi([(x, x, x, x, torch.zeros(16, 4), torch.zeros(16, 4), 2, 4)])          # CPU tensors
+    with pytest.raises(ValueError):
+        rib.window_attn_multi_into([], [])
