@@ -50,7 +50,8 @@
 //    real tokens are enumerated row-major, r = iy*nx + ix, so padded positions
 //    are never loaded, and only the last tile can hold padded keys.
 //  * Workgroups are numbered so that the q-blocks of one (image, window, head)
-//    are consecutive on one XCD (shared K/V in that XCD's L2).
+//    run on one XCD (shared K/V in that XCD's L2) and the window units are
+//    dealt round-robin over the XCDs (edge windows spread evenly).
 #include "rib_device.hpp"
 #include "rib_launch.hpp"
 
@@ -905,6 +906,18 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
   }
 }
 
+// Workgroup -> logical index (window unit * qblocks + query block) for a grid
+// of 8 * ceil(units / 8) * qblocks workgroups.  Window unit 8k + x takes the
+// workgroups whose index is x mod 8, which the dispatcher's round-robin sends
+// to one XCD: the query blocks of a (window, head) share that XCD's L2, and
+// every XCD gets every eighth window unit, so the smaller edge windows of a
+// map spread evenly over the XCDs.  Logical indices past the last unit are
+// padding and return at once.
+__device__ __forceinline__ int interleave_logical(int bid, int qblocks) {
+  const int per = 8 * qblocks;
+  return ((bid / per) * 8 + bid % 8) * qblocks + (bid % per) / 8;
+}
+
 template <int DH, int R>
 __global__ void __launch_bounds__(QB, 1)
 attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
@@ -913,7 +926,7 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
                  uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws, int total,
                  long tstride, float* __restrict__ lse) {
   attn_tiled_body<DH, R>(qc, kc, v, g, qp, kp, o, B, T, H, W, heads, wt, ws, total, tstride, lse,
-                         xcd_swizzle(blockIdx.x, gridDim.x));
+                         interleave_logical(blockIdx.x, (wt * ws * ws + QB - 1) / QB));
 }
 
 template <int DH, int R>
@@ -924,7 +937,7 @@ attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
                        uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws,
                        int total, long tstride, float* __restrict__ lse) {
   attn_small_body<DH, R>(qc, kc, v, g, qp, kp, o, B, T, H, W, heads, wt, ws, total, tstride, lse,
-                         xcd_swizzle(blockIdx.x, gridDim.x));
+                         interleave_logical(blockIdx.x, 1));
 }
 
 // ---- several independent calls in one launch ---------------------------------
@@ -932,9 +945,8 @@ attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
 // and otherwise differ freely (maps, window sizes, tables).  Each call owns a
 // contiguous range of the grid, a multiple of 8 workgroups long, so that the
 // dispatcher's round-robin over the 8 XCDs gives every XCD the same share of
-// every call; inside a call, window unit 8k + x takes workgroups whose index is
-// x mod 8, i.e. all query blocks of one (window, head) run on one XCD and share
-// its L2.  The host orders the calls longest first.
+// every call; inside a call, workgroups map to (window unit, query block) as in
+// a single call (interleave_logical).  The host orders the calls longest first.
 constexpr int GROUP_MAX = 8;
 
 struct CallDesc {
@@ -973,20 +985,16 @@ template <int DH, int R>
 __global__ void __launch_bounds__(QB, 1) attn_bf16_group_kernel(const CallGroup grp) {
   CallDesc c;
   const int lb = group_call(grp, blockIdx.x, c);
-  const int per = 8 * c.qblocks;
-  const int unit = (lb / per) * 8 + lb % 8;
-  if (unit >= c.units) return;
   attn_tiled_body<DH, R>(c.qc, c.kc, c.v, c.g, c.qp, c.kp, c.o, c.B, c.T, c.H, c.W, c.heads, c.wt, c.ws,
-                         c.units * c.qblocks, c.tstride, c.lse, unit * c.qblocks + (lb % per) / 8);
+                         c.units * c.qblocks, c.tstride, c.lse, interleave_logical(lb, c.qblocks));
 }
 
 template <int DH, int R>
 __global__ void __launch_bounds__(SQ, 2) attn_bf16_small_group_kernel(const CallGroup grp) {
   CallDesc c;
   const int lb = group_call(grp, blockIdx.x, c);
-  if (lb >= c.units) return;
   attn_small_body<DH, R>(c.qc, c.kc, c.v, c.g, c.qp, c.kp, c.o, c.B, c.T, c.H, c.W, c.heads, c.wt, c.ws,
-                         c.units, c.tstride, c.lse, lb);
+                         c.units, c.tstride, c.lse, interleave_logical(lb, 1));
 }
 
 template <int DH, int R>
@@ -995,7 +1003,7 @@ hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
   const int NW = a.wt * a.ws * a.ws;
   if (NW <= SQ) {
     const int total = a.B * nWt * nWy * nWx * a.heads;
-    const int grid = 8 * ((total + 7) / 8);
+    const int grid = 8 * ((total + 7) / 8);  // interleave_logical with one query block
     hipLaunchKernelGGL((attn_bf16_small_kernel<DH, R>), dim3(grid), dim3(SQ), 0, stream,
                        (const uint32_t*)a.qc, (const uint32_t*)a.kc, (const uint32_t*)a.v,
                        (const uint32_t*)a.g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt,
@@ -1003,8 +1011,9 @@ hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const int qblocks = (NW + QB - 1) / QB;
-  const int total = a.B * nWt * nWy * nWx * a.heads * qblocks;
-  const int grid = 8 * ((total + 7) / 8);
+  const int units = a.B * nWt * nWy * nWx * a.heads;
+  const int total = units * qblocks;
+  const int grid = 8 * ((units + 7) / 8) * qblocks;  // see interleave_logical
   hipLaunchKernelGGL((attn_bf16_kernel<DH, R>), dim3(grid), dim3(QB), 0, stream,
                      (const uint32_t*)a.qc, (const uint32_t*)a.kc, (const uint32_t*)a.v,
                      (const uint32_t*)a.g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt,
