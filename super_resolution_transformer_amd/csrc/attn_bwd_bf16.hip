@@ -318,15 +318,15 @@ struct Frame {
       vt[c] = real ? *reinterpret_cast<const u32x4_t*>(base + (S::AP + 2 * c + hh) * 256) : (u32x4_t){0u, 0u, 0u, 0u};
   }
 
-  // LDS-direct copy of streamed tile t into the stage at dword `buf`: wave w
-  // copies chunks w and w + 8; lane l writes row l of the chunk.
-  __device__ __forceinline__ void issue(uint32_t* lds, int buf, int t) const {
+  // LDS-direct copy of streamed tile t into the stage `dst`: wave w copies
+  // chunks w and w + 8; lane l writes row l of the chunk.
+  __device__ __forceinline__ void issue(uint32_t* dst, int t) const {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int cc = wave + NWV * k;
       if (cc < S::NP) {
         const unsigned off = (unsigned)(((t * S::NP + cc) * 256 + lane * 4) * 4);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(other, (__attribute__((address_space(3))) void*)(lds + buf + cc * CS),
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(other, (__attribute__((address_space(3))) void*)(dst + cc * CS),
                                                  16, off, 0, 0, 0);
       }
     }
@@ -338,7 +338,11 @@ template <int DH, int R>
 __global__ void __launch_bounds__(RB, 1)
 bwd_dq_bf16_kernel(BwdArgs a, int total) {
   using S = BS<DH, R>;
-  __shared__ __attribute__((aligned(16))) uint32_t lds[2 * S::ST_DW];
+  // two stages as two arrays (not one double buffer): the compiler then sees
+  // that reads of one stage do not depend on the copies landing in the other
+  // and does not wait for those copies before every read
+  __shared__ __attribute__((aligned(16))) uint32_t lds0[S::ST_DW];
+  __shared__ __attribute__((aligned(16))) uint32_t lds1[S::ST_DW];
   Frame<DH, R> f;
   if (!f.init(a, total, a.pq, a.pk)) return;
   const int l32 = f.l32, hh = f.hh;
@@ -352,27 +356,27 @@ bwd_dq_bf16_kernel(BwdArgs a, int total) {
     for (int mt = 0; mt < S::MT; ++mt) acc[qb][mt] = zero16();
   }
 
-  f.issue(lds, 0, 0);
+  f.issue(lds0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int lb = tr_lane_base(f.lane);
-  for (int t = 0; t < f.ntiles; ++t) {
-    const int buf = (t & 1) * S::ST_DW;
-    if (t + 1 < f.ntiles) f.issue(lds, ((t + 1) & 1) * S::ST_DW, t + 1);
+  // tile t from stage `cur` while tile t + 1 lands in `nxt`
+  auto tile = [&](const uint32_t* cur, uint32_t* nxt, int t) {
+    if (t + 1 < f.ntiles) f.issue(nxt, t + 1);
     if (f.active) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         u32x4_t ka[S::KC], va[2], kt[S::MT][2];
 #pragma unroll
         for (int c = 0; c < S::KC; ++c)
-          ka[c] = *reinterpret_cast<const u32x4_t*>(lds + buf + chunk_dw(2 * c + hh, kb * 32 + l32));
+          ka[c] = *reinterpret_cast<const u32x4_t*>(cur + chunk_dw(2 * c + hh, kb * 32 + l32));
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          va[c] = *reinterpret_cast<const u32x4_t*>(lds + buf + S::A_DW + chunk_dw(2 * c + hh, kb * 32 + l32));
+          va[c] = *reinterpret_cast<const u32x4_t*>(cur + S::A_DW + chunk_dw(2 * c + hh, kb * 32 + l32));
 #pragma unroll
         for (int mt = 0; mt < S::MT; ++mt)
 #pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) kt[mt][c2] = tr_operand(lds, buf, lb, kb * 32 + 16 * c2, 32 * mt);
+          for (int c2 = 0; c2 < 2; ++c2) kt[mt][c2] = tr_operand(cur, 0, lb, kb * 32 + 16 * c2, 32 * mt);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           f32x16_t s = zero16(), d = zero16();
@@ -396,6 +400,10 @@ bwd_dq_bf16_kernel(BwdArgs a, int total) {
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of the next tile have landed
     __syncthreads();
+  };
+  for (int t = 0; t < f.ntiles; t += 2) {
+    tile(lds0, lds1, t);
+    if (t + 1 < f.ntiles) tile(lds1, lds0, t + 1);
   }
   if (!f.active) return;
 
@@ -436,7 +444,9 @@ template <int DH, int R>
 __global__ void __launch_bounds__(RB, 1)
 bwd_dkv_bf16_kernel(BwdArgs a, int total) {
   using S = BS<DH, R>;
-  __shared__ __attribute__((aligned(16))) uint32_t lds[2 * S::ST_DW];
+  // two stages as two arrays, as in the dq pass
+  __shared__ __attribute__((aligned(16))) uint32_t lds0[S::ST_DW];
+  __shared__ __attribute__((aligned(16))) uint32_t lds1[S::ST_DW];
   Frame<DH, R> f;
   if (!f.init(a, total, a.pk, a.pq)) return;
   const int l32 = f.l32, hh = f.hh;
@@ -451,29 +461,29 @@ bwd_dkv_bf16_kernel(BwdArgs a, int total) {
     for (int mt = 0; mt < S::MT; ++mt) acck[kb][mt] = zero16();
   }
 
-  f.issue(lds, 0, 0);
+  f.issue(lds0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   const int lb = tr_lane_base(f.lane);
-  for (int t = 0; t < f.ntiles; ++t) {
-    const int buf = (t & 1) * S::ST_DW;
-    if (t + 1 < f.ntiles) f.issue(lds, ((t + 1) & 1) * S::ST_DW, t + 1);
+  // tile t from stage `cur` while tile t + 1 lands in `nxt`
+  auto tile = [&](const uint32_t* cur, uint32_t* nxt, int t) {
+    if (t + 1 < f.ntiles) f.issue(nxt, t + 1);
     if (f.active) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         u32x4_t qa[S::KC], ga[2], gT[2], qT[S::MT][2];
 #pragma unroll
         for (int c = 0; c < S::KC; ++c)
-          qa[c] = *reinterpret_cast<const u32x4_t*>(lds + buf + chunk_dw(2 * c + hh, qb * 32 + l32));
+          qa[c] = *reinterpret_cast<const u32x4_t*>(cur + chunk_dw(2 * c + hh, qb * 32 + l32));
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          ga[c] = *reinterpret_cast<const u32x4_t*>(lds + buf + S::A_DW + chunk_dw(2 * c + hh, qb * 32 + l32));
+          ga[c] = *reinterpret_cast<const u32x4_t*>(cur + S::A_DW + chunk_dw(2 * c + hh, qb * 32 + l32));
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) gT[c2] = tr_operand(lds, buf + S::A_DW, lb, qb * 32 + 16 * c2, 0);
+        for (int c2 = 0; c2 < 2; ++c2) gT[c2] = tr_operand(cur, S::A_DW, lb, qb * 32 + 16 * c2, 0);
 #pragma unroll
         for (int mt = 0; mt < S::MT; ++mt)
 #pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) qT[mt][c2] = tr_operand(lds, buf, lb, qb * 32 + 16 * c2, 32 * mt);
+          for (int c2 = 0; c2 < 2; ++c2) qT[mt][c2] = tr_operand(cur, 0, lb, qb * 32 + 16 * c2, 32 * mt);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           f32x16_t s = zero16(), d = zero16();
@@ -501,6 +511,10 @@ bwd_dkv_bf16_kernel(BwdArgs a, int total) {
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  for (int t = 0; t < f.ntiles; t += 2) {
+    tile(lds0, lds1, t);
+    if (t + 1 < f.ntiles) tile(lds1, lds0, t + 1);
   }
   if (!f.active) return;
 
