@@ -312,19 +312,20 @@ __device__ __forceinline__ u32x2_t ds_read_tr16(const uint32_t* p) {
   return __builtin_bit_cast(u32x2_t, r);
 }
 
-template <int DH, int R>
+// per-wave state of NQ 32-query blocks
+template <int DH, int R, int NQ = 2>
 struct Regs {
   using S = Shape<DH, R>;
-  f32x16_t O[2][S::DT];
-  u32x4_t qt[2][S::KC];
-  float mhat[2];
-  float lpart[2];  // this lane's share of l (only when l is not a V channel)
+  f32x16_t O[NQ][S::DT];
+  u32x4_t qt[NQ][S::KC];
+  float mhat[NQ];
+  float lpart[NQ];  // this lane's share of l (only when l is not a V channel)
 };
 
 // l of the lane's query of block qb: the ones channel of the PV product, or
 // the two lane halves' partial sums
-template <int DH, int R>
-__device__ __forceinline__ float row_sum(const Regs<DH, R>& rg, int qb) {
+template <int DH, int R, int NQ>
+__device__ __forceinline__ float row_sum(const Regs<DH, R, NQ>& rg, int qb) {
   using S = Shape<DH, R>;
   if constexpr (S::ONES) {
     const LanePair pr = lane_pair(rg.O[qb][S::LT][S::LR]);
@@ -364,14 +365,15 @@ __device__ __forceinline__ void read_k_ops(const uint32_t* lds, int kst, int l32
       ops.ka[kb][c] = *reinterpret_cast<const u32x4_t*>(base + kchunk_dw(2 * c, kb * 32));
 }
 
-// S^T = K~ Q~^T for 64 keys x the wave's 64 queries
-template <int DH, int R>
-__device__ __forceinline__ void qk_tile(const PhaseOps<DH, R>& ops, const Regs<DH, R>& rg, f32x16_t (&Sacc)[2][2]) {
+// S^T = K~ Q~^T for 64 keys x the wave's 32 NQ queries
+template <int DH, int R, int NQ>
+__device__ __forceinline__ void qk_tile(const PhaseOps<DH, R>& ops, const Regs<DH, R, NQ>& rg,
+                                        f32x16_t (&Sacc)[NQ][2]) {
   using S = Shape<DH, R>;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < NQ; ++qb) {
       f32x16_t acc;
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
@@ -386,12 +388,13 @@ __device__ __forceinline__ void qk_tile(const PhaseOps<DH, R>& ops, const Regs<D
 // p = exp2(t - shift) packed to bf16 pairs (truncated: P feeds both the PV
 // product and, through the ones channel of V, the row sum, so the rounding of
 // P cancels in O = PV / l); returns the OR of all packed words
-__device__ __forceinline__ uint32_t exp_tile(const f32x16_t (&Sacc)[2][2], uint32_t (&P)[2][2][8], float shift0,
-                                             float shift1) {
+template <int NQ>
+__device__ __forceinline__ uint32_t exp_tile(const f32x16_t (&Sacc)[NQ][2], uint32_t (&P)[NQ][2][8],
+                                             const float (&shift)[NQ]) {
   uint32_t orv = 0;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float sh = qb ? shift1 : shift0;
+  for (int qb = 0; qb < NQ; ++qb) {
+    const float sh = shift[qb];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -405,10 +408,11 @@ __device__ __forceinline__ uint32_t exp_tile(const f32x16_t (&Sacc)[2][2], uint3
 }
 
 // fast-path exponentials (no shift)
-__device__ __forceinline__ uint32_t exp_tile_fast(const f32x16_t (&Sacc)[2][2], uint32_t (&P)[2][2][8]) {
+template <int NQ>
+__device__ __forceinline__ uint32_t exp_tile_fast(const f32x16_t (&Sacc)[NQ][2], uint32_t (&P)[NQ][2][8]) {
   uint32_t orv = 0;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < NQ; ++qb)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -423,13 +427,13 @@ __device__ __forceinline__ uint32_t exp_tile_fast(const f32x16_t (&Sacc)[2][2], 
 // Slow path for the tile whose scores are in Sacc: exact row maximum, new
 // reference m_hat (rounded to bf16), exponentials again, rescale of O
 // (unless this is the first tile) and the new -m_hat in the Q~ operand.
-template <int DH, int R>
-__device__ __forceinline__ void rescale_tile(Regs<DH, R>& rg, const f32x16_t (&Sacc)[2][2], uint32_t (&P)[2][2][8],
-                                             bool first, int gh) {
+template <int DH, int R, int NQ>
+__device__ __forceinline__ void rescale_tile(Regs<DH, R, NQ>& rg, const f32x16_t (&Sacc)[NQ][2],
+                                             uint32_t (&P)[NQ][2][8], bool first, int gh) {
   using S = Shape<DH, R>;
-  float shift[2];
+  float shift[NQ];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < NQ; ++qb) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -452,7 +456,7 @@ __device__ __forceinline__ void rescale_tile(Regs<DH, R>& rg, const f32x16_t (&S
     const uint32_t cd = pack_bf16(-mnew, -OFF);
     if (gh == S::GM) rg.qt[qb][S::CM][S::DM] = cd;
   }
-  exp_tile(Sacc, P, shift[0], shift[1]);
+  exp_tile(Sacc, P, shift);
 }
 
 // transposed V operands of one tile (see pv_tile); vst = dword index of the
@@ -482,12 +486,12 @@ __device__ __forceinline__ void read_v_ops(const uint32_t* lds, int vst, int lan
 }
 
 // O^T += V^T P^T (and, without a ones channel, l += the lane's p values)
-template <int DH, int R>
-__device__ __forceinline__ void pv_tile(const PhaseOps<DH, R>& ops, Regs<DH, R>& rg, const uint32_t (&P)[2][2][8]) {
+template <int DH, int R, int NQ>
+__device__ __forceinline__ void pv_tile(const PhaseOps<DH, R>& ops, Regs<DH, R, NQ>& rg, const uint32_t (&P)[NQ][2][8]) {
   using S = Shape<DH, R>;
   if constexpr (!S::ONES) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < NQ; ++qb)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -500,7 +504,7 @@ __device__ __forceinline__ void pv_tile(const PhaseOps<DH, R>& ops, Regs<DH, R>&
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < NQ; ++qb) {
         const u32x4_t pb = {P[qb][kb][4 * c2], P[qb][kb][4 * c2 + 1], P[qb][kb][4 * c2 + 2], P[qb][kb][4 * c2 + 3]};
 #pragma unroll
         for (int dt = 0; dt < S::DT; ++dt)
@@ -741,10 +745,12 @@ __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc,
 // One workgroup of four waves covers a whole window and head: every thread
 // stages one key (all roles of the staging scheme above) into its 64-key tile,
 // so all key tiles are resident in LDS after a single barrier and the key loop
-// runs without barriers.  Each lane builds its Q~ operands and reads its gate
-// values straight from global memory before that barrier, so the loads of a
-// workgroup are all in flight at once; two workgroups share a CU.  The
-// workload is HBM-bound (16x16 windows: 4 key tiles).
+// runs without barriers.  Each wave takes its 64 queries as two blocks of 32,
+// one after the other, which keeps it under 168 registers: three workgroups
+// (four below 128 registers) share a CU, so the grid of a small map is
+// resident at once.  The first block's Q~ operands and gate values come
+// straight from global memory before that barrier, so the loads of a
+// workgroup are all in flight together.  16x16 windows hold 4 key tiles.
 constexpr int SQ = 256;        // queries (and keys) per workgroup
 constexpr int SNT = SQ / KT;   // key tiles, all resident
 
@@ -824,25 +830,27 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
     for (int role = 0; role < 8; ++role) store_tile<DH, R, true>(stage, role, lane, real, st[role]);
   }
 
-  // ---- this lane's Q~ operands and gate values, straight from global memory
+  // ---- the wave's 64 queries run as two passes of 32 (NQ = 1): fewer live
+  // registers, so three workgroups fit on a CU.  A pass picks up its Q~
+  // operands and gate values straight from global memory; the first pass
+  // issues those loads before the staging barrier.
   const float sp = LOG2E / sqrtf((float)R);
   const float sc = LOG2E / sqrtf((float)DH);
-  Regs<DH, R> rg;
-  uint32_t gv[2][S::DT][4][2];
-  int offq[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  Regs<DH, R, 1> rg;
+  uint32_t gv[S::DT][4][2];
+  int offq = 0;
+  auto load_block = [&](int qb) {
     const int r = wave * QW + qb * 32 + l32;
     const bool real = r < G.n_real;
     int off, n;
     locate<DH>(G, real ? r : G.n_real - 1, off, n);
-    offq[qb] = off;
+    offq = off;
 #pragma unroll
     for (int c = 0; c < S::KC; ++c) {
       u32x4_t q;
 #pragma unroll
       for (int i = 0; i < 4; ++i) q[i] = qrow_word<DH, R>(8 * c + 4 * gh + i, off, n, real, qp, qc, sp, sc);
-      rg.qt[qb][c] = q;
+      rg.qt[0][c] = q;
     }
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
@@ -850,59 +858,60 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = dt * 32 + 8 * q4 + 4 * gh;
         const int gw = (off + d0) >> 1;
-        gv[qb][dt][q4][0] = d0 < DH ? g[gw] : 0u;
-        gv[qb][dt][q4][1] = d0 + 4 <= DH ? g[gw + 1] : 0u;
+        gv[dt][q4][0] = d0 < DH ? g[gw] : 0u;
+        gv[dt][q4][1] = d0 + 4 <= DH ? g[gw + 1] : 0u;
       }
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) rg.O[qb][dt][e] = 0.0f;
-    rg.mhat[qb] = 0.0f;
-    rg.lpart[qb] = 0.0f;
-  }
+      for (int e = 0; e < 16; ++e) rg.O[0][dt][e] = 0.0f;
+    rg.mhat[0] = 0.0f;
+    rg.lpart[0] = 0.0f;
+  };
+  load_block(0);
   __syncthreads();
-  if (wave * QW >= G.n_real) return;  // no barrier follows
 
   const int ntiles = (G.n_real + KT - 1) / KT;
-  PhaseOps<DH, R> ops;
-  f32x16_t Sacc[2][2];
-  uint32_t P[2][2][8];
-  for (int x = 0; x < ntiles; ++x) {
-    read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
-    read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
-    qk_tile<DH, R>(ops, rg, Sacc);
-    const uint32_t orv = exp_tile_fast(Sacc, P);
-    const bool first = x == 0;
-    if (__builtin_amdgcn_ballot_w64(first || (orv & 0x40004000u))) rescale_tile<DH, R>(rg, Sacc, P, first, gh);
-    pv_tile<DH, R>(ops, rg, P);
-  }
-
-  // ---- epilogue: O / l * sigmoid(G), bf16, NHWC
-#pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
+    if (wave * QW + qb * 32 >= G.n_real) return;  // no real query left in this wave; no barrier follows
+    if (qb > 0) load_block(qb);
+    PhaseOps<DH, R> ops;
+    f32x16_t Sacc[1][2];
+    uint32_t P[1][2][8];
+    for (int x = 0; x < ntiles; ++x) {
+      read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
+      read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
+      qk_tile<DH, R>(ops, rg, Sacc);
+      const uint32_t orv = exp_tile_fast(Sacc, P);
+      const bool first = x == 0;
+      if (__builtin_amdgcn_ballot_w64(first || (orv & 0x40004000u))) rescale_tile<DH, R>(rg, Sacc, P, first, gh);
+      pv_tile<DH, R>(ops, rg, P);
+    }
+
+    // ---- epilogue of the block: O / l * sigmoid(G), bf16, NHWC
     const int r = wave * QW + qb * 32 + l32;
-    const float lsum = row_sum(rg, qb);
-    if (r >= G.n_real) continue;
-    const float inv = 1.0f / lsum;
-    if (lse) lse[(offq[qb] - G.h * DH) / G.C * heads + G.h] = (rg.mhat[qb] + OFF + __log2f(lsum)) * LN2;
+    const float lsum = row_sum(rg, 0);
+    if (r < G.n_real) {
+      const float inv = 1.0f / lsum;
+      if (lse) lse[(offq - G.h * DH) / G.C * heads + G.h] = (rg.mhat[0] + OFF + __log2f(lsum)) * LN2;
 #pragma unroll
-    for (int dt = 0; dt < S::DT; ++dt)
+      for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = dt * 32 + 8 * q4 + 4 * gh;
-        if (d0 >= DH) continue;
-        const int e0 = 4 * q4;
-        const int gw = (offq[qb] + d0) >> 1;
-        const uint32_t g01 = gv[qb][dt][q4][0];
-        const uint32_t r01 = pack_bf16(rg.O[qb][dt][e0 + 0] * inv * sigmoidf(bf16_lo(g01)),
-                                       rg.O[qb][dt][e0 + 1] * inv * sigmoidf(bf16_hi(g01)));
-        o[gw] = r01;
-        if (d0 + 4 <= DH) {
-          const uint32_t g23 = gv[qb][dt][q4][1];
-          o[gw + 1] = pack_bf16(rg.O[qb][dt][e0 + 2] * inv * sigmoidf(bf16_lo(g23)),
-                                rg.O[qb][dt][e0 + 3] * inv * sigmoidf(bf16_hi(g23)));
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = dt * 32 + 8 * q4 + 4 * gh;
+          if (d0 >= DH) continue;
+          const int e0 = 4 * q4;
+          const int gw = (offq + d0) >> 1;
+          const uint32_t g01 = gv[dt][q4][0];
+          o[gw] = pack_bf16(rg.O[0][dt][e0 + 0] * inv * sigmoidf(bf16_lo(g01)),
+                            rg.O[0][dt][e0 + 1] * inv * sigmoidf(bf16_hi(g01)));
+          if (d0 + 4 <= DH) {
+            const uint32_t g23 = gv[dt][q4][1];
+            o[gw + 1] = pack_bf16(rg.O[0][dt][e0 + 2] * inv * sigmoidf(bf16_lo(g23)),
+                                  rg.O[0][dt][e0 + 3] * inv * sigmoidf(bf16_hi(g23)));
+          }
         }
-      }
+    }
   }
 }
 
@@ -930,7 +939,7 @@ attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ k
 }
 
 template <int DH, int R>
-__global__ void __launch_bounds__(SQ, 2)
+__global__ void __launch_bounds__(SQ, 3)
 attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
                        const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                        const float* __restrict__ qp, const float* __restrict__ kp,
@@ -990,7 +999,7 @@ __global__ void __launch_bounds__(QB, 1) attn_bf16_group_kernel(const CallGroup 
 }
 
 template <int DH, int R>
-__global__ void __launch_bounds__(SQ, 2) attn_bf16_small_group_kernel(const CallGroup grp) {
+__global__ void __launch_bounds__(SQ, 3) attn_bf16_small_group_kernel(const CallGroup grp) {
   CallDesc c;
   const int lb = group_call(grp, blockIdx.x, c);
   attn_small_body<DH, R>(c.qc, c.kc, c.v, c.g, c.qp, c.kp, c.o, c.B, c.T, c.H, c.W, c.heads, c.wt, c.ws,
