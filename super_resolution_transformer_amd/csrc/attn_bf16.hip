@@ -27,9 +27,10 @@
 //    in Q~ (a bf16 value) against 1 in K~, column "o" holds -OFF against 1
 //    (2^14 for padded keys, which masks them; those have 0 in column m).  The
 //    MFMA returns t = s*log2(e) - m_hat - OFF and the fast path is p = exp2(t).
-//  * P is packed to bf16 by truncation with one v_perm_b32 per pair (the
-//    rounding convert costs as much as an exp2 on gfx950); the same P feeds
-//    PV and the row sum, so O = PV / l sees a consistent set of weights.
+//  * P is packed to bf16 by truncation with one v_perm_b32 per pair; the same
+//    P feeds PV and the row sum, so O = PV / l sees a consistent set of
+//    weights and the truncation's bias cancels (its spread is that of
+//    rounding; the rounding convert costs the same).
 //  * Rescaling is lazy: p <= 2^-OFF * 2^(growth of the maximum).  The packed
 //    bf16 P values are OR-reduced; bit 14 of a half is set iff p >= 2, i.e.
 //    the maximum grew by more than OFF+1 = 8 (a factor 256).  Only then (and on
@@ -40,12 +41,13 @@
 //  * Ping-pong over key tiles of KT = 64.  A workgroup has 8 waves, two per
 //    SIMD, in two groups (waves 0-3 and 4-7) that run half a step apart and
 //    swap roles at every barrier: while one group runs its MFMA phase
-//    (QK^T of tile t and PV of tile t-1, 20 MFMAs per wave), the wave of the
-//    other group on the same SIMD runs its transcendental phase (exp2,
-//    convert and overflow check of tile t, plus its share of staging the
-//    next tiles into LDS).  The matrix core and the transcendental unit of
-//    every SIMD are thus busy at the same time.  Three LDS stages; tile loads
-//    are issued a full step before they are stored.
+//    (operand reads, its share of staging the next tiles into LDS, QK^T of
+//    tile t and PV of tile t-1: 20 MFMAs per wave), the wave of the other
+//    group on the same SIMD runs its softmax phase (exp2, packing and
+//    overflow check of tile t, and the next tile's K~ operand reads).  The
+//    matrix core thus runs while the other wave's exponentials, which hold
+//    the SIMD's vector issue for about 8 cycles each, go through.  Three LDS
+//    stages; tile loads are issued a full step before they are stored.
 //  * Window partitioning is index arithmetic on the NHWC arrays: a window's
 //    real tokens are enumerated row-major, r = iy*nx + ix, so padded positions
 //    are never loaded, and only the last tile can hold padded keys.

@@ -20,8 +20,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 }
 
 // Two floats -> packed bf16 pair by truncation (the high 16 bits of each; low
-// half = a).  One full-rate v_perm_b32, where the rounding convert runs at the
-// transcendental rate.
+// half = a): one v_perm_b32.
 __device__ __forceinline__ uint32_t pack_bf16_trunc(float a, float b) {
   return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, b), __builtin_bit_cast(uint32_t, a), 0x07060302u);
 }
