@@ -78,6 +78,10 @@ def _configure(L):
     L.rib_oracle_attn_lse.restype = ctypes.c_int
     L.rib_oracle_attn_backward.argtypes = [_D] * 7 + [ctypes.c_int] * 7 + [_D] * 6
     L.rib_oracle_attn_backward.restype = ctypes.c_int
+    L.rib_oracle_attn_backward_heads.argtypes = [_D] * 7 + [ctypes.c_int] * 7 + [_D] * 6
+    L.rib_oracle_attn_backward_heads.restype = ctypes.c_int
+    L.rib_oracle_attn_lse_heads.argtypes = [_D] * 4 + [ctypes.c_int] * 7 + [_D]
+    L.rib_oracle_attn_lse_heads.restype = ctypes.c_int
     L.rib_oracle_encode_backward.argtypes = [ctypes.c_int] * 4 + [_D] * 4
     L.rib_oracle_encode_backward.restype = ctypes.c_int
     return L
@@ -233,31 +237,38 @@ def cla_gate(x, dw_w, dw_b, pw_w, pw_b) -> np.ndarray:
 
 
 def window_lse(qc, kc, qp, kp, heads: int, window: int) -> np.ndarray:
-    """Row log-sum-exp of the scores, [B, H, W, heads] float64 (one shared positional pair)."""
+    """Row log-sum-exp of the scores, [B, H, W, heads] float64.  qp, kp: one shared pair
+    [window*window, R] or one pair per head [heads, window*window, R]."""
     qc, kc, qp, kp = _f64(qc), _f64(kc), _f64(qp), _f64(kp)
     dh = qc.shape[-1] // heads
     B, H, W = _shape_args(qc, heads, dh)
     out = np.zeros((B, H, W, heads), np.float64)
-    if lib().rib_oracle_attn_lse(_p(qc), _p(kc), _p(qp), _p(kp), B, H, W, heads, dh, qp.shape[-1], window,
-                                 _p(out)) != 0:
+    fn = lib().rib_oracle_attn_lse_heads if qp.ndim == 3 else lib().rib_oracle_attn_lse
+    if qp.ndim == 3 and qp.shape[0] != heads:
+        raise ValueError("per-head tables need one pair per head")
+    if fn(_p(qc), _p(kc), _p(qp), _p(kp), B, H, W, heads, dh, qp.shape[-1], window, _p(out)) != 0:
         raise ValueError("oracle rejected its arguments")
     return out
 
 
 def window_attn_backward(qc, kc, v, g, qp, kp, dout, heads: int, window: int):
     """Gradients (dqc, dkc, dv, dg, dqp, dkp) of O = (softmax(S) V) * sigmoid(G) for the
-    upstream gradient dout (NHWC float64; dqp/dkp [window*window, R], summed over all windows,
-    heads and images)."""
+    upstream gradient dout (NHWC float64).  With one shared pair qp, kp [window*window, R],
+    dqp/dkp have that shape and sum over all windows, heads and images; with one pair per
+    head [heads, window*window, R], dqp[h]/dkp[h] sum over the windows and images of head h."""
     qc, kc, v, g, dout = (_f64(a) for a in (qc, kc, v, g, dout))
     qp, kp = _f64(qp), _f64(kp)
     dh = qc.shape[-1] // heads
     B, H, W = _shape_args(qc, heads, dh)
     R = qp.shape[-1]
+    if qp.ndim == 3 and qp.shape[0] != heads:
+        raise ValueError("per-head tables need one pair per head")
     outs = [np.zeros(qc.shape, np.float64) for _ in range(4)]
     dqp = np.zeros(qp.shape, np.float64)
     dkp = np.zeros(kp.shape, np.float64)
-    rc = lib().rib_oracle_attn_backward(_p(qc), _p(kc), _p(v), _p(g), _p(qp), _p(kp), _p(dout), B, H, W, heads,
-                                        dh, R, window, *[_p(a) for a in outs], _p(dqp), _p(dkp))
+    fn = lib().rib_oracle_attn_backward_heads if qp.ndim == 3 else lib().rib_oracle_attn_backward
+    rc = fn(_p(qc), _p(kc), _p(v), _p(g), _p(qp), _p(kp), _p(dout), B, H, W, heads,
+            dh, R, window, *[_p(a) for a in outs], _p(dqp), _p(dkp))
     if rc != 0:
         raise ValueError("oracle backward rejected its arguments")
     return (*outs, dqp, dkp)

@@ -317,9 +317,9 @@ int rib_oracle_attn_rows(const double* qc, const double* kc, const double* v, co
  * token's window.  This is what a training forward keeps for the backward
  * (explainer section 4.1 trains with the same attention).  One shared pair.
  */
-int rib_oracle_attn_lse(const double* qc, const double* kc, const double* qp, const double* kp, int B, int H,
-                        int W, int heads, int dh, int R, int ws, double* lse) {
-  problem p = {qc, kc, qc, qc, qp, kp, B, H, W, heads, dh, R, ws, 0};
+static int attn_lse(const double* qc, const double* kc, const double* qp, const double* kp, int B, int H, int W,
+                    int heads, int dh, int R, int ws, long tstride, double* lse) {
+  problem p = {qc, kc, qc, qc, qp, kp, B, H, W, heads, dh, R, ws, tstride};
   if (check_problem(&p) || !lse) return -1;
   const int nWy = (H + ws - 1) / ws, nWx = (W + ws - 1) / ws;
   const long units = (long)B * nWy * nWx * heads;
@@ -348,11 +348,11 @@ int rib_oracle_attn_lse(const double* qc, const double* kc, const double* qp, co
         int nt = window_tokens(&p, wy, wx, ty, tx, tn);
         for (int i = 0; i < nt; ++i) {
           const double* q = qc + elem(&p, b, ty[i], tx[i], h, 0);
-          const double* qpos = qp + (size_t)tn[i] * R;
+          const double* qpos = qp + h * tstride + (size_t)tn[i] * R;
           double mx = -INFINITY;
           for (int j = 0; j < nt; ++j) {
             const double* k = kc + elem(&p, b, ty[j], tx[j], h, 0);
-            const double* kpos = kp + (size_t)tn[j] * R;
+            const double* kpos = kp + h * tstride + (size_t)tn[j] * R;
             double sc = 0.0, bb = 0.0;
             for (int d = 0; d < dh; ++d) sc += q[d] * k[d];
             for (int r = 0; r < R; ++r) bb += qpos[r] * kpos[r];
@@ -368,6 +368,17 @@ int rib_oracle_attn_lse(const double* qc, const double* kc, const double* qp, co
     free(ty); free(tx); free(tn); free(S);
   }
   return fail ? -1 : 0;
+}
+
+int rib_oracle_attn_lse(const double* qc, const double* kc, const double* qp, const double* kp, int B, int H,
+                        int W, int heads, int dh, int R, int ws, double* lse) {
+  return attn_lse(qc, kc, qp, kp, B, H, W, heads, dh, R, ws, 0, lse);
+}
+
+/* The same with one (Qp, Kp) pair per head: qp, kp are [heads][ws*ws][R]. */
+int rib_oracle_attn_lse_heads(const double* qc, const double* kc, const double* qp, const double* kp, int B,
+                              int H, int W, int heads, int dh, int R, int ws, double* lse) {
+  return attn_lse(qc, kc, qp, kp, B, H, W, heads, dh, R, ws, (long)ws * ws * R, lse);
 }
 
 /*
@@ -469,14 +480,16 @@ static int attn_backward_unit(const problem* p, const double* dout, int b, int h
   const double inv_sqrt_r = 1.0 / sqrt((double)R);
   memset(dkc_acc, 0, sizeof(double) * (size_t)nt * dh);
   memset(dv_acc, 0, sizeof(double) * (size_t)nt * dh);
+  const double* qtab = p->qp + h * p->tstride;  /* this head's pair (the shared one when tstride = 0) */
+  const double* ktab = p->kp + h * p->tstride;
   for (int i = 0; i < nt; ++i) {
     const double* q = p->qc + elem(p, b, ty[i], tx[i], h, 0);
-    const double* qpos = p->qp + (size_t)tn[i] * R;
+    const double* qpos = qtab + (size_t)tn[i] * R;
     /* P row */
     double mx = -INFINITY;
     for (int j = 0; j < nt; ++j) {
       const double* k = p->kc + elem(p, b, ty[j], tx[j], h, 0);
-      const double* kpos = p->kp + (size_t)tn[j] * R;
+      const double* kpos = ktab + (size_t)tn[j] * R;
       double sc = 0.0, bb = 0.0;
       for (int d = 0; d < dh; ++d) sc += q[d] * k[d];
       for (int r = 0; r < R; ++r) bb += qpos[r] * kpos[r];
@@ -514,7 +527,7 @@ static int attn_backward_unit(const problem* p, const double* dout, int b, int h
     for (int j = 0; j < nt; ++j) {
       const double ds = prow[j] * (dprow[j] - D);
       const double* k = p->kc + elem(p, b, ty[j], tx[j], h, 0);
-      const double* kpos = p->kp + (size_t)tn[j] * R;
+      const double* kpos = ktab + (size_t)tn[j] * R;
       for (int d = 0; d < dh; ++d) {
         dqi[d] += ds * k[d] * inv_sqrt_dh;
         dkc_acc[(size_t)j * dh + d] += ds * q[d] * inv_sqrt_dh;
@@ -534,17 +547,21 @@ static int attn_backward_unit(const problem* p, const double* dout, int b, int h
   return 0;
 }
 
-int rib_oracle_attn_backward(const double* qc, const double* kc, const double* v, const double* g,
-                             const double* qp, const double* kp, const double* dout, int B, int H, int W,
-                             int heads, int dh, int R, int ws, double* dqc, double* dkc, double* dv,
-                             double* dg, double* dqp, double* dkp) {
-  problem p = {qc, kc, v, g, qp, kp, B, H, W, heads, dh, R, ws, 0};
+/* per_head = 0: one shared (Qp, Kp) pair, dqp and dkp [ws*ws][R] summed over
+ * heads too; per_head = 1: qp, kp, dqp, dkp are [heads][ws*ws][R] and head h's
+ * table gradient sums over images and windows only. */
+static int attn_backward(const double* qc, const double* kc, const double* v, const double* g,
+                         const double* qp, const double* kp, const double* dout, int B, int H, int W,
+                         int heads, int dh, int R, int ws, int per_head, double* dqc, double* dkc, double* dv,
+                         double* dg, double* dqp, double* dkp) {
+  const size_t N = (size_t)ws * ws;
+  problem p = {qc, kc, v, g, qp, kp, B, H, W, heads, dh, R, ws, per_head ? (long)(N * R) : 0};
   if (check_problem(&p) || !dout || !dqc || !dkc || !dv || !dg || !dqp || !dkp) return -1;
   const int nWy = (H + ws - 1) / ws, nWx = (W + ws - 1) / ws;
   const long units = (long)B * nWy * nWx * heads;
-  const size_t N = (size_t)ws * ws;
-  memset(dqp, 0, sizeof(double) * N * R);
-  memset(dkp, 0, sizeof(double) * N * R);
+  const size_t NT = N * (size_t)R * (per_head ? (size_t)heads : 1);  /* table gradient entries */
+  memset(dqp, 0, sizeof(double) * NT);
+  memset(dkp, 0, sizeof(double) * NT);
   int fail = 0;
 #pragma omp parallel
   {
@@ -557,8 +574,8 @@ int rib_oracle_attn_backward(const double* qc, const double* kc, const double* v
     double* akv = (double*)malloc(sizeof(double) * dh);
     double* dkc_acc = (double*)malloc(sizeof(double) * (size_t)cap * dh);
     double* dv_acc = (double*)malloc(sizeof(double) * (size_t)cap * dh);
-    double* dqp_t = (double*)calloc(N * R, sizeof(double));
-    double* dkp_t = (double*)calloc(N * R, sizeof(double));
+    double* dqp_t = (double*)calloc(NT, sizeof(double));
+    double* dkp_t = (double*)calloc(NT, sizeof(double));
     if (!ty || !tx || !tn || !prow || !dprow || !akv || !dkc_acc || !dv_acc || !dqp_t || !dkp_t) {
 #pragma omp atomic write
       fail = 1;
@@ -572,12 +589,13 @@ int rib_oracle_attn_backward(const double* qc, const double* kc, const double* v
         int wy = (int)(t % nWy);
         int b = (int)(t / nWy);
         int nt = window_tokens(&p, wy, wx, ty, tx, tn);
-        attn_backward_unit(&p, dout, b, h, nt, ty, tx, tn, prow, dprow, akv, dkc_acc, dv_acc, dkp_t, dqp_t,
-                           dqc, dkc, dv, dg);
+        const size_t toff = per_head ? (size_t)h * N * R : 0;
+        attn_backward_unit(&p, dout, b, h, nt, ty, tx, tn, prow, dprow, akv, dkc_acc, dv_acc, dkp_t + toff,
+                           dqp_t + toff, dqc, dkc, dv, dg);
       }
 #pragma omp critical
       {
-        for (size_t k = 0; k < N * (size_t)R; ++k) {
+        for (size_t k = 0; k < NT; ++k) {
           dqp[k] += dqp_t[k];
           dkp[k] += dkp_t[k];
         }
@@ -587,6 +605,23 @@ int rib_oracle_attn_backward(const double* qc, const double* kc, const double* v
     free(dqp_t); free(dkp_t);
   }
   return fail ? -1 : 0;
+}
+
+int rib_oracle_attn_backward(const double* qc, const double* kc, const double* v, const double* g,
+                             const double* qp, const double* kp, const double* dout, int B, int H, int W,
+                             int heads, int dh, int R, int ws, double* dqc, double* dkc, double* dv,
+                             double* dg, double* dqp, double* dkp) {
+  return attn_backward(qc, kc, v, g, qp, kp, dout, B, H, W, heads, dh, R, ws, 0, dqc, dkc, dv, dg, dqp, dkp);
+}
+
+/* The backward with one (Qp, Kp) pair per head (the per-head reading of the
+ * explainer's section 2.2 attention rewrite): qp, kp, dqp, dkp are
+ * [heads][ws*ws][R]; dqp[h], dkp[h] sum over every image and window of head h. */
+int rib_oracle_attn_backward_heads(const double* qc, const double* kc, const double* v, const double* g,
+                                   const double* qp, const double* kp, const double* dout, int B, int H, int W,
+                                   int heads, int dh, int R, int ws, double* dqc, double* dkc, double* dv,
+                                   double* dg, double* dqp, double* dkp) {
+  return attn_backward(qc, kc, v, g, qp, kp, dout, B, H, W, heads, dh, R, ws, 1, dqc, dkc, dv, dg, dqp, dkp);
 }
 
 /*
