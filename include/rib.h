@@ -233,6 +233,27 @@ rib_status rib_window_attn_backward(const void* qc, const void* kc, const void* 
                                     int heads, int dh, int R, int window, rib_dtype dtype, void* stream);
 
 /*
+ * rib_window_attn_heads_train / rib_window_attn_heads_backward -- the training
+ * forward and the backward with one positional pair per head (the per-head
+ * reading of the explainer's section 2.2 attention rewrite, as in
+ * rib_window_attn_heads): qp and kp are float32 [heads][window*window][R], and
+ * so are dqp and dkp, whose head h sums over the images and windows of that
+ * head only.  Every other argument, layout, limit, workspace size
+ * (rib_window_attn_backward_workspace) and error as rib_window_attn_train and
+ * rib_window_attn_backward.  The encoder gradient of head h's tables is
+ * rib_encode_backward on dqp[h], dkp[h] with that head's weights.
+ */
+rib_status rib_window_attn_heads_train(const void* qc, const void* kc, const void* v, const void* g,
+                                       const float* qp, const float* kp, void* o, float* lse, int B, int H, int W,
+                                       int heads, int dh, int R, int window, rib_dtype dtype, void* stream);
+rib_status rib_window_attn_heads_backward(const void* qc, const void* kc, const void* v, const void* g,
+                                          const float* qp, const float* kp, const void* o, const float* lse,
+                                          const void* dout, void* dqc, void* dkc, void* dv, void* dg,
+                                          float* dqp, float* dkp, void* workspace, size_t workspace_bytes, int B,
+                                          int H, int W, int heads, int dh, int R, int window, rib_dtype dtype,
+                                          void* stream);
+
+/*
  * rib_encode_backward -- gradient of the packed encoder weights (layout of
  * rib_encode) for upstream dqp, dkp (explainer section 2.2, the coordinate
  * encoder and the two rank heads; the ReLU derivative at 0 is 0):
@@ -303,7 +324,7 @@ const char* rib_last_error(void);
 /* ABI version of this header (incremented on any incompatible change). */
 int rib_abi_version(void);
 
-#define RIB_ABI_VERSION 8
+#define RIB_ABI_VERSION 9
 
 #ifdef __cplusplus
 }

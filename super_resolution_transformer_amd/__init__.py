@@ -73,6 +73,10 @@ def lib(path: str | None = None):
     L.rib_window_attn_train.restype = i
     L.rib_window_attn_backward.argtypes = [vp] * 16 + [sz] + [i] * 8 + [vp]
     L.rib_window_attn_backward.restype = i
+    L.rib_window_attn_heads_backward.argtypes = [vp] * 16 + [sz] + [i] * 8 + [vp]
+    L.rib_window_attn_heads_backward.restype = i
+    L.rib_window_attn_heads_train.argtypes = [vp] * 8 + [i] * 8 + [vp]
+    L.rib_window_attn_heads_train.restype = i
     L.rib_encode_backward_workspace.argtypes = [i] * 4
     L.rib_encode_backward_workspace.restype = sz
     L.rib_encode_backward.argtypes = [i] * 4 + [vp] * 5 + [sz, vp]
@@ -236,18 +240,19 @@ def window_attn_train_into(qc, kc, v, g, qp, kp, heads: int, window: int, o, lse
         raise ValueError("qc, kc, v, g, o must all be [B, H, W, C] of one dtype")
     if not all(t.is_cuda and t.is_contiguous() for t in ts + (qp, kp, lse)):
         raise ValueError("all tensors must be contiguous GPU tensors")
-    if qp.dtype != torch.float32 or kp.dtype != torch.float32 or qp.shape != kp.shape or qp.dim() != 2:
-        raise ValueError("qp, kp must be float32 [window*window, R]")
-    if qp.shape[0] != window * window:
-        raise ValueError("qp, kp must have window*window rows")
+    if qp.dtype != torch.float32 or kp.dtype != torch.float32 or qp.shape != kp.shape or qp.dim() not in (2, 3):
+        raise ValueError("qp, kp must be float32 [window*window, R] or per-head [heads, window*window, R]")
+    per_head = qp.dim() == 3
+    if qp.shape[-2] != window * window or (per_head and qp.shape[0] != heads):
+        raise ValueError("qp, kp must have window*window rows (and one table per head)")
     B, H, W, C = qc.shape
     if heads < 1 or C % heads:
         raise ValueError("channel count must be a multiple of heads")
     if lse.shape != (B, H, W, heads) or lse.dtype != torch.float32:
         raise ValueError("lse must be float32 [B, H, W, heads]")
-    _check(lib().rib_window_attn_train(_ptr(qc), _ptr(kc), _ptr(v), _ptr(g), _ptr(qp), _ptr(kp), _ptr(o), _ptr(lse),
-                                       B, H, W, heads, C // heads, qp.shape[1], window, _dtype_code(qc),
-                                       _stream(qc)))
+    fn = lib().rib_window_attn_heads_train if per_head else lib().rib_window_attn_train
+    _check(fn(_ptr(qc), _ptr(kc), _ptr(v), _ptr(g), _ptr(qp), _ptr(kp), _ptr(o), _ptr(lse),
+              B, H, W, heads, C // heads, qp.shape[-1], window, _dtype_code(qc), _stream(qc)))
 
 
 def cla_gate(x, dw_w, dw_b, pw_w, pw_b):
@@ -277,9 +282,10 @@ def cla_gate_into(x, dw_w, dw_b, pw_w, pw_b, g) -> None:
 def window_attn_backward(qc, kc, v, g, qp, kp, o, lse, dout, heads: int, window: int):
     """Gradients (dqc, dkc, dv, dg, dqp, dkp) of window_attn for the upstream gradient dout.
 
-    (o, lse) come from window_attn_train on the same inputs; dqp, dkp are float32
-    [window*window, R], summed over every image, window and head.  The workspace is a
-    temporary torch buffer.
+    (o, lse) come from window_attn_train on the same inputs.  With one shared pair qp, kp
+    [window*window, R], dqp and dkp have that shape and sum over every image, window and
+    head; with one pair per head [heads, window*window, R], dqp[h], dkp[h] sum over head h's
+    images and windows.  The workspace is a temporary torch buffer.
     """
     import torch
     outs = [torch.empty_like(qc) for _ in range(4)]
@@ -307,22 +313,23 @@ def window_attn_backward_into(qc, kc, v, g, qp, kp, o, lse, dout, heads: int, wi
         raise ValueError("qc, kc, v, g, o, dout and the map gradients must all be [B, H, W, C] of one dtype")
     if not all(t.is_cuda and t.is_contiguous() for t in ts + (qp, kp, dqp, dkp, work)):
         raise ValueError("all tensors must be contiguous GPU tensors")
-    if qp.dtype != torch.float32 or kp.dtype != torch.float32 or qp.shape != kp.shape or qp.dim() != 2:
-        raise ValueError("qp, kp must be float32 [window*window, R]")
-    if qp.shape[0] != window * window or dqp.shape != qp.shape or dkp.shape != qp.shape:
-        raise ValueError("qp, kp, dqp, dkp must have window*window rows of R")
+    if qp.dtype != torch.float32 or kp.dtype != torch.float32 or qp.shape != kp.shape or qp.dim() not in (2, 3):
+        raise ValueError("qp, kp must be float32 [window*window, R] or per-head [heads, window*window, R]")
+    per_head = qp.dim() == 3
+    if qp.shape[-2] != window * window or dqp.shape != qp.shape or dkp.shape != qp.shape:
+        raise ValueError("qp, kp, dqp, dkp must have window*window rows of R, and one shape")
     B, H, W, C = qc.shape
-    if heads < 1 or C % heads:
-        raise ValueError("channel count must be a multiple of heads")
+    if heads < 1 or C % heads or (per_head and qp.shape[0] != heads):
+        raise ValueError("channel count must be a multiple of heads (and per-head tables one per head)")
     if lse.shape != (B, H, W, heads) or lse.dtype != torch.float32 or not (lse.is_cuda and lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 GPU tensor [B, H, W, heads]")
-    dh, R = C // heads, qp.shape[1]
+    dh, R = C // heads, qp.shape[-1]
     code = _dtype_code(qc)
     nbytes = work.numel() * work.element_size()
-    _check(lib().rib_window_attn_backward(*[_ptr(t) for t in ts[:4]], _ptr(qp), _ptr(kp), _ptr(o), _ptr(lse),
-                                          _ptr(dout), _ptr(dqc), _ptr(dkc), _ptr(dv), _ptr(dg), _ptr(dqp),
-                                          _ptr(dkp), _ptr(work), nbytes, B, H, W, heads, dh, R, window, code,
-                                          _stream(qc)))
+    fn = lib().rib_window_attn_heads_backward if per_head else lib().rib_window_attn_backward
+    _check(fn(*[_ptr(t) for t in ts[:4]], _ptr(qp), _ptr(kp), _ptr(o), _ptr(lse),
+              _ptr(dout), _ptr(dqc), _ptr(dkc), _ptr(dv), _ptr(dg), _ptr(dqp),
+              _ptr(dkp), _ptr(work), nbytes, B, H, W, heads, dh, R, window, code, _stream(qc)))
 
 
 def encode_backward(window: int, L: int, hidden: int, R: int, weights, dqp, dkp):

@@ -163,7 +163,7 @@ bwd_dq_kernel(BwdArgs a, int total) {
   }
 #pragma unroll
   for (int k = 0; k < RM; ++k) {
-    qpos[k] = k < R ? a.qp[qn * R + k] * sp : 0.0f;
+    qpos[k] = k < R ? a.qp[u.h * a.tstride + qn * R + k] * sp : 0.0f;
     accp[k] = 0.0f;
   }
   const float D = a.dsum[qrow];
@@ -191,7 +191,7 @@ bwd_dq_kernel(BwdArgs a, int total) {
         long tok;
         int n;
         locate(u, a, k0 + j, tok, n);
-        pv = a.kp[n * R + k];
+        pv = a.kp[u.h * a.tstride + n * R + k];
       }
       skp[j][k] = pv;
     }
@@ -261,7 +261,7 @@ bwd_dkv_kernel(BwdArgs a, int total) {
   }
 #pragma unroll
   for (int x = 0; x < RM; ++x) {
-    kpos[x] = x < R ? a.kp[kn * R + x] : 0.0f;
+    kpos[x] = x < R ? a.kp[u.h * a.tstride + kn * R + x] : 0.0f;
     dkp[x] = 0.0f;
   }
 
@@ -287,7 +287,7 @@ bwd_dkv_kernel(BwdArgs a, int total) {
         long tok;
         int n;
         locate(u, a, q0 + i, tok, n);
-        pv = a.qp[n * R + x] * sp;
+        pv = a.qp[u.h * a.tstride + n * R + x] * sp;
       }
       sqp[i][x] = pv;
     }
@@ -340,21 +340,26 @@ bwd_dkv_kernel(BwdArgs a, int total) {
     if (x < R) krows[x] = dkp[x];
 }
 
-// reduce: thread per (table, n, r); sums the per-row gradients of every real
-// token at in-window index n over heads, images and windows.
+// reduce: thread per (table head, table, n, r); sums the per-row gradients of
+// every real token at in-window index n over images and windows, and over the
+// heads too unless each head has its own table (tab_heads = heads).
 __global__ void __launch_bounds__(256)
 bwd_table_reduce_kernel(BwdArgs a) {
   const int N = a.ws * a.ws;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  if (idx >= 2 * N * a.R) return;
+  int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= a.tab_heads * 2 * N * a.R) return;
+  const int th = idx / (2 * N * a.R);  // table head (0 when the heads share one table)
+  idx -= th * 2 * N * a.R;
   const int tab = idx / (N * a.R);
   const int rem = idx - tab * N * a.R;
   const int n = rem / a.R, r = rem - (rem / a.R) * a.R;
   const int iy = n / a.ws, ix = n - (n / a.ws) * a.ws;
   const float* rows = tab ? a.krows : a.qrows;
   const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws;
+  const int hb0 = a.tab_heads > 1 ? th * a.B : 0;                 // rows are [heads][B][H][W][R]
+  const int hb1 = a.tab_heads > 1 ? (th + 1) * a.B : a.heads * a.B;
   float acc = 0.0f;
-  for (int hb = 0; hb < a.heads * a.B; ++hb)
+  for (int hb = hb0; hb < hb1; ++hb)
     for (int wy = 0; wy < nWy; ++wy) {
       const int y = wy * a.ws + iy;
       if (y >= a.H) break;
@@ -364,7 +369,7 @@ bwd_table_reduce_kernel(BwdArgs a) {
         acc += rows[(((long)hb * a.H + y) * a.W + x) * a.R + r];
       }
     }
-  (tab ? a.dkp : a.dqp)[n * a.R + r] = acc;
+  (tab ? a.dkp : a.dqp)[(long)th * N * a.R + n * a.R + r] = acc;
 }
 
 template <typename T, int DHM, int RM>
@@ -421,7 +426,7 @@ hipError_t launch_attn_bwd_rows(const BwdArgs& a, bool bf16, hipStream_t stream)
 }
 
 hipError_t launch_attn_bwd_reduce(const BwdArgs& a, hipStream_t stream) {
-  const int n = 2 * a.ws * a.ws * a.R;
+  const int n = a.tab_heads * 2 * a.ws * a.ws * a.R;
   hipLaunchKernelGGL(bwd_table_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

@@ -251,11 +251,11 @@ bwd_pack_kernel(BwdArgs a, long total) {
   const float sp = LOG2E / sqrtf((float)R), sc = LOG2E / sqrtf((float)DH);
   u32x4_t out;
   if constexpr (KIND == 0) {
-    const RowSrc aug{(const uint32_t*)a.kc, a.kp, nullptr, nullptr};
+    const RowSrc aug{(const uint32_t*)a.kc, a.kp + u.h * a.tstride, nullptr, nullptr};
     const RowSrc val{nullptr, nullptr, (const uint32_t*)a.v, nullptr};
     out = make_chunk<DH, R, 0>(c, aug, val, tok, n, cofs, crow, real, sp, sc);
   } else {
-    const RowSrc aug{(const uint32_t*)a.qc, a.qp, nullptr, a.lse};
+    const RowSrc aug{(const uint32_t*)a.qc, a.qp + u.h * a.tstride, nullptr, a.lse};
     const RowSrc val{nullptr, nullptr, (const uint32_t*)a.da, a.dsum};
     out = make_chunk<DH, R, 1>(c, aug, val, tok, n, cofs, crow, real, sp, sc);
   }

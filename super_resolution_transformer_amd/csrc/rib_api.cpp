@@ -166,6 +166,14 @@ rib_status rib_window_attn_heads(const void* qc, const void* kc, const void* v, 
                      R, 1, window, dtype, stream);
 }
 
+rib_status rib_window_attn_heads_train(const void* qc, const void* kc, const void* v, const void* g,
+                                       const float* qp, const float* kp, void* o, float* lse, int B, int H, int W,
+                                       int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
+  if (!lse) return fail(RIB_ERR_INVALID_ARG, "rib_window_attn_heads_train: null pointer");
+  return window_attn("rib_window_attn_heads_train", true, qc, kc, v, g, qp, kp, o, lse, B, 1, H, W, heads, dh,
+                     R, 1, window, dtype, stream);
+}
+
 rib_status rib_window_attn_multi(int n, const rib_attn_call* calls, rib_dtype dtype, void* stream) {
   const char* fn = "rib_window_attn_multi";
   if (!calls) return fail(RIB_ERR_INVALID_ARG, "%s: null pointer", fn);
@@ -276,12 +284,16 @@ size_t rib_window_attn_backward_workspace(int B, int H, int W, int heads, int dh
   return bwd_layout(B, H, W, heads, dh, R, window, dtype).total;
 }
 
-rib_status rib_window_attn_backward(const void* qc, const void* kc, const void* v, const void* g,
-                                    const float* qp, const float* kp, const void* o, const float* lse,
-                                    const void* dout, void* dqc, void* dkc, void* dv, void* dg, float* dqp,
-                                    float* dkp, void* workspace, size_t workspace_bytes, int B, int H, int W,
-                                    int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
-  const char* fn = "rib_window_attn_backward";
+}  // extern "C"
+
+namespace {
+// shared by rib_window_attn_backward (one (qp, kp) pair; table gradients summed
+// over heads) and rib_window_attn_heads_backward (a pair and a gradient per head)
+rib_status window_attn_backward(const char* fn, bool per_head, const void* qc, const void* kc, const void* v,
+                                const void* g, const float* qp, const float* kp, const void* o, const float* lse,
+                                const void* dout, void* dqc, void* dkc, void* dv, void* dg, float* dqp,
+                                float* dkp, void* workspace, size_t workspace_bytes, int B, int H, int W,
+                                int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
   if (!qc || !kc || !v || !g || !qp || !kp || !o || !lse || !dout || !dqc || !dkc || !dv || !dg || !dqp ||
       !dkp || !workspace)
     return fail(RIB_ERR_INVALID_ARG, "%s: null pointer", fn);
@@ -302,7 +314,7 @@ rib_status rib_window_attn_backward(const void* qc, const void* kc, const void* 
   if (workspace_bytes < lay.total)
     return fail(RIB_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, lay.total);
   const size_t nb = (size_t)elems * (dtype == RIB_F32 ? 4 : 2);
-  const size_t np = sizeof(float) * (size_t)window * window * R;
+  const size_t np = sizeof(float) * (size_t)window * window * R * (per_head ? heads : 1);
   const size_t nl = sizeof(float) * (size_t)B * H * W * heads;
   const size_t sizes[] = {nb, nb, nb, nb, np, np, nb, nl, nb, nb, nb, nb, nb, np, np, lay.total};
   // every output (indices 9..15, the workspace included) is disjoint from every other buffer
@@ -315,6 +327,8 @@ rib_status rib_window_attn_backward(const void* qc, const void* kc, const void* 
                  w + lay.da, (float*)(w + lay.dsum), (float*)(w + lay.qrows), (float*)(w + lay.krows),
                  (uint32_t*)(w + lay.pk), (uint32_t*)(w + lay.pq), B, H, W, heads, dh, R, window,
                  rib::bwd_tiles_per_unit(window)};
+  a.tstride = per_head ? (long)window * window * R : 0;
+  a.tab_heads = per_head ? heads : 1;
   const hipStream_t st = (hipStream_t)stream;
   const bool bf16 = dtype == RIB_BF16;
   hipError_t e = rib::launch_attn_bwd_prep(a, bf16, st);
@@ -322,7 +336,31 @@ rib_status rib_window_attn_backward(const void* qc, const void* kc, const void* 
     e = bf16 && rib::attn_bwd_bf16_supported(dh, R) ? rib::launch_attn_bwd_bf16(a, st)
                                                     : rib::launch_attn_bwd_rows(a, bf16, st);
   if (e == hipSuccess) e = rib::launch_attn_bwd_reduce(a, st);
-  return hip_status(e, "rib_window_attn_backward launch");
+  return hip_status(e, fn);
+}
+}  // namespace
+
+extern "C" {
+
+rib_status rib_window_attn_backward(const void* qc, const void* kc, const void* v, const void* g,
+                                    const float* qp, const float* kp, const void* o, const float* lse,
+                                    const void* dout, void* dqc, void* dkc, void* dv, void* dg, float* dqp,
+                                    float* dkp, void* workspace, size_t workspace_bytes, int B, int H, int W,
+                                    int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
+  return window_attn_backward("rib_window_attn_backward", false, qc, kc, v, g, qp, kp, o, lse, dout, dqc, dkc,
+                              dv, dg, dqp, dkp, workspace, workspace_bytes, B, H, W, heads, dh, R, window, dtype,
+                              stream);
+}
+
+rib_status rib_window_attn_heads_backward(const void* qc, const void* kc, const void* v, const void* g,
+                                          const float* qp, const float* kp, const void* o, const float* lse,
+                                          const void* dout, void* dqc, void* dkc, void* dv, void* dg,
+                                          float* dqp, float* dkp, void* workspace, size_t workspace_bytes, int B,
+                                          int H, int W, int heads, int dh, int R, int window, rib_dtype dtype,
+                                          void* stream) {
+  return window_attn_backward("rib_window_attn_heads_backward", true, qc, kc, v, g, qp, kp, o, lse, dout, dqc,
+                              dkc, dv, dg, dqp, dkp, workspace, workspace_bytes, B, H, W, heads, dh, R, window,
+                              dtype, stream);
 }
 
 size_t rib_encode_backward_workspace(int window, int L, int hidden, int R) {

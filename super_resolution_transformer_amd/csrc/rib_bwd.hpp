@@ -11,7 +11,7 @@ struct BwdArgs {
   const void* kc;
   const void* v;
   const void* g;
-  const float* qp;  // [ws*ws][R] shared positional pair
+  const float* qp;  // [ws*ws][R] shared positional pair, or [heads][ws*ws][R] (tstride > 0)
   const float* kp;
   const void* o;
   const float* lse;  // row log-sum-exp per (token, head), natural log, from the forward
@@ -21,7 +21,7 @@ struct BwdArgs {
   void* dkc;
   void* dv;
   void* dg;
-  float* dqp;  // [ws*ws][R]
+  float* dqp;  // [ws*ws][R] summed over heads, or [heads][ws*ws][R] (tab_heads = heads)
   float* dkp;
   // workspace
   void* da;      // dO * sigmoid(G), NHWC, storage type
@@ -32,6 +32,8 @@ struct BwdArgs {
   uint32_t* pq;  // matrix-core path: packed query-side operand rows
   int B, H, W, heads, dh, R, ws;
   int tu;        // 64-row tiles per unit in the packed images
+  long tstride = 0;   // floats between the positional pairs of consecutive heads (0: one shared pair)
+  int tab_heads = 1;  // table gradients per head (heads) or summed over heads (1)
 };
 
 inline int bwd_tiles_per_unit(int ws) { return (ws * ws + 63) / 64; }

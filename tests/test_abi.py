@@ -22,7 +22,8 @@ def test_header_declares_the_boundary():
         "rib_encode", "rib_window_attn", "rib_attn_supported", "rib_last_error", "rib_abi_version",
         "rib_cla_gate", "rib_window_attn_heads", "rib_window_attn_train", "rib_window_attn_backward", "rib_window_attn_backward_workspace",
         "rib_encode_backward", "rib_encode_backward_workspace", "rib_ln_qkv", "rib_encode3d",
-        "rib_window_attn3d", "rib_window_attn_multi"}
+        "rib_window_attn3d", "rib_window_attn_multi", "rib_window_attn_heads_train",
+        "rib_window_attn_heads_backward"}
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -208,6 +209,37 @@ def test_backward_validation(L):
     assert bwd(L, alias) == rib.RIB_ERR_INVALID_ARG
     assert bwd(L, PB[:13] + [PB[4]] + PB[14:]) == rib.RIB_ERR_INVALID_ARG  # dqp == qp (an input)
     assert bwd(L, PB[:12] + [PB[7]] + PB[13:]) == rib.RIB_ERR_INVALID_ARG  # dg == lse (an input)
+
+
+@fake
+def test_heads_training_validation(L):
+    def hb(ptrs=None, nbytes=None, **kw):
+        a = dict(B=1, H=8, W=8, heads=2, dh=30, R=16, window=8, dtype=rib.RIB_BF16)
+        a.update(kw)
+        p = list(ptrs or PB)
+        if nbytes is None:
+            nbytes = L.rib_window_attn_backward_workspace(a["B"], a["H"], a["W"], a["heads"], a["dh"], a["R"],
+                                                          a["window"], a["dtype"])
+        return L.rib_window_attn_heads_backward(*p, nbytes, a["B"], a["H"], a["W"], a["heads"], a["dh"], a["R"],
+                                                a["window"], a["dtype"], None)
+    assert hb([None] + PB[1:]) == rib.RIB_ERR_INVALID_ARG
+    assert "rib_window_attn_heads_backward" in L.rib_last_error().decode()
+    assert hb(dh=65) == rib.RIB_ERR_UNSUPPORTED
+    assert hb(nbytes=16) == rib.RIB_ERR_INVALID_ARG
+    # the per-head tables are heads times larger: dqp just past one table still overlaps qp's second
+    tab = 8 * 8 * 16 * 4
+    assert hb(PB[:13] + [ctypes.c_void_p(PB[4].value + tab + 256)] + PB[14:]) == rib.RIB_ERR_INVALID_ARG
+    assert "overlap" in L.rib_last_error().decode()
+
+    def ht(ptrs, **kw):
+        a = dict(B=1, H=8, W=8, heads=2, dh=30, R=16, window=8, dtype=rib.RIB_BF16)
+        a.update(kw)
+        return L.rib_window_attn_heads_train(*ptrs, a["B"], a["H"], a["W"], a["heads"], a["dh"], a["R"],
+                                             a["window"], a["dtype"], None)
+    assert ht(P[:7] + [None]) == rib.RIB_ERR_INVALID_ARG
+    assert "rib_window_attn_heads_train" in L.rib_last_error().decode()
+    assert ht(P[:8], dh=31) == rib.RIB_ERR_UNSUPPORTED
+    assert ht(P[:6] + [ctypes.c_void_p(P[4].value + tab + 256), P[7]]) == rib.RIB_ERR_INVALID_ARG   # o in qp's 2nd table
 
 
 @fake

@@ -169,3 +169,71 @@ def test_train_forward_lse(torch, case):
     err = float(np.abs(lse.cpu().numpy() - ref).max())
     note(f"  lse max|err| {err:.3g}  max|lse| {float(np.abs(ref).max()):.3g}")
     assert err <= TOL[dtype]
+
+
+# ---------------------------------------------------------------- one positional pair per head
+HEAD_CASES = [
+    # (B, H, W, heads, dh, R, ws, dtype)
+    (2, 40, 24, 6, 30, 16, 16, "bf16"),     # matrix-core path, the SST head shape
+    (1, 40, 33, 3, 16, 16, 32, "bf16"),     # matrix-core path, dh 16, ragged windows
+    (1, 20, 20, 2, 8, 8, 16, "bf16"),       # no matrix-core variant: fp32-register rows on bf16 maps
+    (2, 21, 13, 3, 16, 16, 8, "f32"),       # fp32, ragged edge windows
+]
+
+
+@pytest.mark.parametrize("case", HEAD_CASES, ids=lambda c: "B{}H{}W{}h{}d{}R{}ws{}-{}".format(*c))
+def test_per_head_backward_whole_output(torch, case):
+    """rib_window_attn_heads_train + rib_window_attn_heads_backward against the oracle with one
+    (Qp, Kp) pair per head (each from its own encoder weights): every gradient, dQp and dKp per
+    head, at the bars of the shared-pair tests; the lse against the oracle's per-head lse."""
+    B, H, W, heads, dh, R, ws, dtype = case
+    L, hidden = 10, 64
+    note(f"per-head backward {case}")
+    p = synthetic.make_problem(B, H, W, heads, dh, R, L, hidden, dtype=dtype, seed=B * 11 + ws)
+    rng = np.random.default_rng(ws + heads)
+    ws_list = [synthetic.draw_weights(rng, L, hidden, R) for _ in range(heads)]
+    tabs = [oracle.encode(ws, L, hidden, R, w) for w in ws_list]
+    oqp, okp = np.stack([t[0] for t in tabs]), np.stack([t[1] for t in tabs])
+    dvals, dbits = synthetic.make_upstream_grad(p.qc.shape, dtype, seed=ws + 7)
+    maps = [dev(torch, getattr(p, nm), p.bits.get(nm), dtype) for nm in ("qc", "kc", "v", "g")]
+    gt = [rib.encode(ws, L, hidden, R, torch.from_numpy(w).cuda()) for w in ws_list]
+    qp = torch.stack([t[0] for t in gt]).contiguous()
+    kp = torch.stack([t[1] for t in gt]).contiguous()
+    o, lse = rib.window_attn_train(*maps, qp, kp, heads, ws)
+    o_plain = rib.window_attn(*maps, qp, kp, heads, ws)
+    grads = rib.window_attn_backward(*maps, qp, kp, o, lse, dev(torch, dvals, dbits, dtype), heads, ws)
+    torch.cuda.synchronize()
+    same = torch.equal(o.view(torch.int16), o_plain.view(torch.int16)) if dtype == "bf16" else torch.equal(o, o_plain)
+    assert same, "per-head train forward differs from the per-head forward"
+    lref = oracle.window_lse(p.qc, p.kc, oqp, okp, heads, ws)
+    lerr = float(np.abs(lse.cpu().numpy() - lref).max())
+    note(f"  lse max|err| {lerr:.3g}")
+    assert lerr <= TOL[dtype]
+    ref = oracle.window_attn_backward(p.qc, p.kc, p.v, p.g, oqp, okp, dvals, heads, ws)
+    got = [t.float().cpu().numpy().astype(np.float64) for t in grads]
+    assert got[4].shape == (heads, ws * ws, R) and got[5].shape == (heads, ws * ws, R)
+    for nm, a, b in zip(NAMES, got, ref):
+        compare(a, b, TOL[dtype], nm)
+
+
+def test_per_head_backward_with_equal_tables_matches_the_shared_pair(torch):
+    """All heads holding one pair: map gradients bit-identical to rib_window_attn_backward's, and the
+    per-head table gradients sum over heads to the shared ones (within fp32 summation order)."""
+    ws = 16
+    p = synthetic.make_problem(2, 40, 24, 6, 30, 16, 10, 64, dtype="bf16", seed=3)
+    dvals, dbits = synthetic.make_upstream_grad(p.qc.shape, "bf16", seed=4)
+    maps = [dev(torch, getattr(p, nm), p.bits.get(nm), "bf16") for nm in ("qc", "kc", "v", "g")]
+    qp, kp = rib.encode(ws, p.L, p.hidden, p.R, torch.from_numpy(p.weights).cuda())
+    qh, kh = qp.expand(6, -1, -1).contiguous(), kp.expand(6, -1, -1).contiguous()
+    dout = dev(torch, dvals, dbits, "bf16")
+    o, lse = rib.window_attn_train(*maps, qp, kp, 6, ws)
+    oh, lseh = rib.window_attn_train(*maps, qh, kh, 6, ws)
+    shared = rib.window_attn_backward(*maps, qp, kp, o, lse, dout, 6, ws)
+    per = rib.window_attn_backward(*maps, qh, kh, oh, lseh, dout, 6, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), oh.view(torch.int16)) and torch.equal(lse, lseh)
+    for k in range(4):
+        assert torch.equal(shared[k].view(torch.int16), per[k].view(torch.int16)), NAMES[k]
+    for k in (4, 5):
+        compare(per[k].sum(0).cpu().numpy().astype(np.float64), shared[k].cpu().numpy().astype(np.float64), 1e-5,
+                NAMES[k] + " summed over heads")
