@@ -9,11 +9,16 @@
 // on NHWC maps.  G then gates the attention output element-wise.
 //
 // Design: persistent workgroups (one wave per 32-channel output block, at least
-// four) walk tiles of 32 tokens (one segment of a map row).  The three input row segments around the tile (with
-// a one-token halo on each side) are loaded straight into LDS (buffer loads
-// with the LDS destination, so a whole tile is in flight without registers),
-// one token per 16-byte-aligned LDS slot, tokens outside the map as zeros;
-// the next tile's loads are issued as soon as phase 1 has read the rows.
+// four), as many as fit on the chip at once, each take one contiguous range of
+// tiles of 32 tokens (one segment of a map row), numbered so that a range walks
+// down 32-token columns of the map.  The input row segments (with a one-token
+// halo on each side) live in a ring of four LDS row buffers, loaded straight
+// into LDS (buffer loads with the LDS destination, so a whole row is in flight
+// without registers), one token per 16-byte-aligned LDS slot, tokens outside
+// the map as zeros.  A tile reads rows y-1, y, y+1 from three of the buffers
+// while the row y+2 of the next tile lands in the fourth: every input row is
+// loaded once per column range instead of once for each of the three tiles
+// that read it, and its latency hides behind a whole tile.
 // Phase 1 computes the depth-wise stencil in fp32 from LDS
 // (each thread owns one channel pair, keeps its 18 taps in registers and walks
 // a run of 8 consecutive tokens, so every input column is read and unpacked
@@ -22,8 +27,9 @@
 // v_mfma_f32_32x32x16_bf16: each wave keeps its 32-channel output blocks of
 // W_pw^T as A operands in VGPRs for the whole launch and reads the B operands
 // (8 channels of one token per lane) from the D tile; in the accumulator each
-// lane holds one token and 4 groups of 4 consecutive output channels, which
-// are biased, rounded and written into an LDS output tile; the tile's tokens
+// lane holds one token and 4 groups of 4 consecutive output channels (the
+// accumulator starts from their biases), which are rounded and written into an
+// LDS output tile; the tile's tokens
 // are one contiguous span of G, stored with 16-byte writes.  The fp32 path
 // keeps D in fp32 and does the point-wise sum with FMAs.
 #include "rib_device.hpp"
@@ -36,6 +42,18 @@ namespace {
 constexpr int GT = 32;          // tokens per tile
 constexpr int GTHREADS = 256;   // four waves
 constexpr int GCMAX = 256;      // largest channel count
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also releases global memory,
+// which makes every wave wait for its LDS-bound buffer loads first; here the next tile's
+// loads must stay in flight across the barriers of the current tile.
+// (s_waitcnt lgkmcnt(0) with the other counters left at their maximum: 0xC07F on gfx9;
+// the signal fences keep the compiler from moving memory accesses across the barrier.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 __device__ __forceinline__ void tile_coords(long tile, int nseg, int H, int& b, int& y, int& x0) {
   const int seg = (int)(tile % nseg);
@@ -93,11 +111,19 @@ struct GateShape {
   static constexpr int KCH = 2 * NB;          // 16-channel contraction chunks
   static constexpr int DSTR = 8 * KCH + 4;    // dwords per token row of the D tile (bank spread)
   static constexpr int XT = GT + 2;           // tokens of an input row segment (left/right halo)
-  static constexpr int XS_DW = 3 * XT * 16 * NB + 256;  // staged input rows (+ one wave's overrun)
+  // one input row segment as 16-byte chunks (at most XT tokens of 16*NB dwords), loaded in
+  // NPASS passes of NT lanes; the buffer holds the last pass's overrun too
+  static constexpr int NPASS = (XT * 4 * NB + NT - 1) / NT;
+  static constexpr int ROW_DW = NPASS * NT * 4;
   static constexpr int OS_DW = GT * 16 * NB;  // output tile, NHWC order
   static constexpr int TPR = 16 * NW;         // phase-1 threads per run
   static constexpr int NRUN = GT / 4;         // tokens per run
 };
+
+// Row ring: the input rows y-1, y, y+1 of the current tile and the prefetched row y+2 live
+// in four LDS arrays.  Separate arrays (not one indexed array) let the compiler see that
+// reading three of them never waits for the copies into the fourth.
+#define GATE_RING(I) ((I) == 0 ? rb0 : (I) == 1 ? rb1 : (I) == 2 ? rb2 : rb3)
 
 template <int NB>
 __global__ void __launch_bounds__(GateShape<NB>::NT, 2)
@@ -106,11 +132,14 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
                      const float* __restrict__ pw_b, uint32_t* __restrict__ g, int B, int H, int W, int C,
                      int nseg, long ntiles) {
   using S = GateShape<NB>;
-  constexpr int XT = S::XT, KCH = S::KCH, DSTR = S::DSTR, NRUN = S::NRUN;
+  constexpr int XT = S::XT, KCH = S::KCH, DSTR = S::DSTR, NRUN = S::NRUN, NPASS = S::NPASS;
   __shared__ __attribute__((aligned(16))) uint32_t dt[GT * DSTR];
-  __shared__ __attribute__((aligned(16))) uint32_t xs[S::XS_DW];
+  __shared__ __attribute__((aligned(16))) uint32_t rb0[S::ROW_DW];
+  __shared__ __attribute__((aligned(16))) uint32_t rb1[S::ROW_DW];
+  __shared__ __attribute__((aligned(16))) uint32_t rb2[S::ROW_DW];
+  __shared__ __attribute__((aligned(16))) uint32_t rb3[S::ROW_DW];
   __shared__ __attribute__((aligned(16))) uint32_t ot[S::OS_DW];
-  __shared__ float pbias[GCMAX];
+  __shared__ __attribute__((aligned(16))) float pbias[GCMAX];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -156,68 +185,68 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
     const int t = e / (8 * KCH - CP), p = CP + e % (8 * KCH - CP);
     dt[t * DSTR + p] = 0u;
   }
-  for (int o = tid; o < C; o += S::NT) pbias[o] = pw_b[o];
+  for (int o = tid; o < GCMAX; o += S::NT) pbias[o] = o < C ? pw_b[o] : 0.0f;
 
-  // Input staging: LDS holds rows y-1, y, y+1 of tokens x0-1 .. x0+GT as a flat array of
-  // 16-byte chunks, chunk f = (row * XT + token) * CH + k at dwords 4f, one token every TS
-  // dwords (C/2 rounded up to 4) so that a chunk never spans two tokens.  The chunks are
-  // loaded straight into LDS (buffer_load ... lds: lane l of a wave writes base + 16 l), so a
-  // whole tile is in flight at once without registers; tokens outside the map get an
-  // out-of-range offset, which the buffer bounds check turns into zeros.
+  // Input staging: an LDS row buffer holds tokens x0-1 .. x0+GT of one map row as 16-byte
+  // chunks, chunk f = token * CH + k at dwords 4f, one token every TS dwords (C/2 rounded up
+  // to 4) so that a chunk never spans two tokens.  The chunks are loaded straight into LDS
+  // (buffer_load ... lds: lane l of a wave writes base + 16 l), so a whole row is in flight
+  // without registers; rows and tokens outside the map get an out-of-range offset, which the
+  // buffer bounds check turns into zeros.
   const int TS = (CP + 3) & ~3;
   const int CH = TS >> 2;  // chunks per token
-  const int NCHK = 3 * XT * CH;
+  const int NCHK = XT * CH;
   const float inv_ch = 1.0f / (float)CH;
   const unsigned map_bytes = (unsigned)((long)B * H * W * C * 2);
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(x), (short)0,
                                                                       (int)map_bytes, 0x00020000);
-  // Per-lane chunk geometry is the same for every tile: for pass j of this wave, chunk
-  // f = wave*64 + j*NT + lane has row r, token p and sub-chunk k; its byte offset relative to
-  // the tile's first token (row y-1, token x0-1) is pre[j].  Packed: r | p << 2.
-  constexpr int NPASS = (3 * XT * 16 * NB / 4 + S::NT - 1) / S::NT;
-  int rp[NPASS];
+  // Per-lane chunk geometry is the same for every row: for pass j of this wave, chunk
+  // f = wave*64 + j*NT + lane is sub-chunk k of token p (-1: past the row), at byte offset
+  // pre[j] from the row's first token.
+  int ptok[NPASS];
   unsigned pre[NPASS];
 #pragma unroll
   for (int j = 0; j < NPASS; ++j) {
     const int f = wave * 64 + j * S::NT + lane;
-    const int q = (int)(((float)f + 0.5f) * inv_ch);  // token row (exact: f < 2^16)
+    const int q = (int)(((float)f + 0.5f) * inv_ch);  // token (exact: f < 2^16)
     const int k = f - q * CH;
-    const int r = q / XT, p = q - r * XT;
-    rp[j] = f < NCHK ? (r | (p << 2)) : -1;
-    pre[j] = (unsigned)(((r * W + p) * CP + 4 * k) * 4);
+    ptok[j] = f < NCHK ? q : -1;
+    pre[j] = (unsigned)((q * CP + 4 * k) * 4);
   }
-  auto issue_tile = [&](long tile) {
-    int b, y, x0;
-    tile_coords(tile, nseg, H, b, y, x0);
-    const long base = ((((long)b * H + (y - 1)) * W + (x0 - 1)) * CP) * 4;  // may be negative
+  auto issue_row = [&](uint32_t* dst, int b, int yrow, int x0) {
+    const bool row_ok = yrow >= 0 && yrow < H;
+    const long base = ((((long)b * H + yrow) * W + (x0 - 1)) * CP) * 4;  // may be negative
 #pragma unroll
     for (int j = 0; j < NPASS; ++j) {
-      const int f0 = wave * 64 + j * S::NT;
-      if (f0 >= NCHK) break;  // wave-uniform
-      const int r = rp[j] & 3, p = rp[j] >> 2;
-      const bool valid = rp[j] >= 0 && y + r - 1 >= 0 && y + r - 1 < H && x0 - 1 + p >= 0 && x0 - 1 + p < W;
+      const int xt = x0 - 1 + ptok[j];
+      const bool valid = row_ok && ptok[j] >= 0 && xt >= 0 && xt < W;
       const unsigned off = valid ? (unsigned)(base + (long)pre[j]) : 0xFFFFFFF0u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(xs + 4 * f0), 16, off,
-                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void*)(dst + 4 * (wave * 64 + j * S::NT)),
+                                               16, off, 0, 0, 0);
     }
   };
-  if (blockIdx.x < ntiles) issue_tile(blockIdx.x);
-  for (long tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    int b, y, x0;
-    tile_coords(tile, nseg, H, b, y, x0);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's input chunks (and last tile's stores) are done
-    __syncthreads();
+
+
+  // One tile: output row y, tokens x0 .. x0+GT-1.  Rows y-1, y, y+1 have landed; the row
+  // y+2 of the next tile (if this workgroup computes it) is loaded meanwhile.
+  auto step = [&](auto kc, int b, int y, int x0, bool more) {
+    constexpr int K = decltype(kc)::value;
+    const uint32_t* up = GATE_RING((K + 3) & 3);
+    const uint32_t* mid = GATE_RING(K);
+    const uint32_t* dn = GATE_RING((K + 1) & 3);
+    if (more) issue_row(GATE_RING((K + 2) & 3), b, y + 2, x0);  // that array held row y-2
     // ---- phase 1: D = depth-wise 3x3 (fp32) over the run, rounded to bf16 into the D tile;
     // a column of three input values is read and unpacked once and used by three tokens
     if (has_pair) {
       float c0[3][2], c1[3][2], c2[3][2];  // input columns x-1, x, x+1 (rows y-1, y, y+1)
       auto column = [&](int p, float (&c)[3][2]) {
-#pragma unroll
-        for (int r = 0; r < 3; ++r) {
-          const uint32_t v = xs[(r * XT + p) * TS + cp];
-          c[r][0] = bf16_lo(v);
-          c[r][1] = bf16_hi(v);
-        }
+        const uint32_t v0 = up[p * TS + cp], v1 = mid[p * TS + cp], v2 = dn[p * TS + cp];
+        c[0][0] = bf16_lo(v0);
+        c[0][1] = bf16_hi(v0);
+        c[1][0] = bf16_lo(v1);
+        c[1][1] = bf16_hi(v1);
+        c[2][0] = bf16_lo(v2);
+        c[2][1] = bf16_hi(v2);
       };
       column(t0, c0);
       column(t0 + 1, c1);
@@ -244,30 +273,33 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
         dt[(t0 + i) * DSTR + cp] = x0 + t0 + i < W ? pack_bf16(a0, a1) : 0u;
       }
     }
-    __syncthreads();
-    // the input rows are consumed: the next tile's loads overlap the point-wise product
-    if (tile + gridDim.x < ntiles) issue_tile(tile + gridDim.x);
-    // ---- phase 2: G^T = W_pw^T D^T for this wave's output block, biased and rounded into
-    // the output tile (NHWC order: token row t holds C/2 dwords)
+    lds_barrier();
+    // ---- phase 2: G^T = W_pw^T D^T for this wave's output block, started from the bias and
+    // rounded into the output tile (NHWC order: token row t holds C/2 dwords)
     if (has_block) {
       f32x16_t acc;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t bq = *reinterpret_cast<const f32x4_t*>(pbias + wave * 32 + 8 * q + 4 * gh);
 #pragma unroll
-      for (int kc = 0; kc < KCH; ++kc) {
-        const u32x4_t bo = *reinterpret_cast<const u32x4_t*>(dt + l32 * DSTR + 8 * kc + 4 * gh);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, wa[kc]),
-                                                      __builtin_bit_cast(bf16x8_t, bo), acc, 0, 0, 0);
+        for (int e = 0; e < 4; ++e) acc[4 * q + e] = bq[e];
       }
+      u32x4_t bo[KCH];
+#pragma unroll
+      for (int kc = 0; kc < KCH; ++kc) bo[kc] = *reinterpret_cast<const u32x4_t*>(dt + l32 * DSTR + 8 * kc + 4 * gh);
+#pragma unroll
+      for (int kc = 0; kc < KCH; ++kc)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, wa[kc]),
+                                                      __builtin_bit_cast(bf16x8_t, bo[kc]), acc, 0, 0, 0);
       uint32_t* orow = ot + l32 * CP;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int oc = wave * 32 + 8 * q + 4 * gh;
-        if (oc < C) orow[oc >> 1] = pack_bf16(acc[4 * q] + pbias[oc], acc[4 * q + 1] + pbias[oc + 1]);
-        if (oc + 2 < C) orow[(oc >> 1) + 1] = pack_bf16(acc[4 * q + 2] + pbias[oc + 2], acc[4 * q + 3] + pbias[oc + 3]);
+        if (oc < C) orow[oc >> 1] = pack_bf16(acc[4 * q], acc[4 * q + 1]);
+        if (oc + 2 < C) orow[(oc >> 1) + 1] = pack_bf16(acc[4 * q + 2], acc[4 * q + 3]);
       }
     }
-    __syncthreads();
+    lds_barrier();
     // ---- the tile's output tokens are one contiguous span of G: 16-byte stores
     {
       const int ntok = min(GT, W - x0);
@@ -283,8 +315,52 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
         }
       }
     }
+  };
+
+  // Tiles are numbered column by column: tile t is row t mod H of column t / H, a column
+  // being one 32-token segment of one image.  Each workgroup takes one contiguous range of
+  // tiles and walks down its columns, so every input row is loaded once per column range
+  // (plus one halo row above and below), not once per tile that reads it.
+  const long t_begin = (long)blockIdx.x * ntiles / gridDim.x;
+  const long t_end = (long)(blockIdx.x + 1) * ntiles / gridDim.x;
+  long t = t_begin;
+  while (t < t_end) {
+    const long col = t / H;
+    int y = (int)(t - col * H);
+    const int b = (int)(col / nseg);
+    const int x0 = (int)(col - (long)b * nseg) * GT;
+    const int yend = (int)min((long)H, y + (t_end - t));
+    // all waves are past the previous column's last tile, whose phase 1 ended the row reads;
+    // row r sits in ring array (r - y + 1) mod 4 for this column range, so the steps take the
+    // arrays in a fixed rotation (straight-line code: each step's arrays are known statically)
+    issue_row(rb0, b, y - 1, x0);
+    issue_row(rb1, b, y, x0);
+    issue_row(rb2, b, y + 1, x0);
+    for (;;) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed (and its last stores)
+      __syncthreads();
+      step(std::integral_constant<int, 1>{}, b, y, x0, y + 1 < yend);
+      if (++y >= yend) break;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      step(std::integral_constant<int, 2>{}, b, y, x0, y + 1 < yend);
+      if (++y >= yend) break;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      step(std::integral_constant<int, 3>{}, b, y, x0, y + 1 < yend);
+      if (++y >= yend) break;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      step(std::integral_constant<int, 0>{}, b, y, x0, y + 1 < yend);
+      if (++y >= yend) break;
+    }
+    t = (long)col * H + y;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 }
+
+#undef GATE_RING
 
 
 template <int NB>
@@ -311,14 +387,19 @@ int device_cus() {
 hipError_t launch_cla_gate(const GateArgs& a, bool bf16, hipStream_t stream) {
   const int nseg = (a.W + GT - 1) / GT;
   const long ntiles = (long)a.B * a.H * nseg;
-  const long cap = 2L * device_cus();
-  const int grid = (int)(ntiles < cap ? ntiles : cap);
   if (!bf16) {
+    const long cap = 2L * device_cus();
+    const int grid = (int)(ntiles < cap ? ntiles : cap);
     hipLaunchKernelGGL(cla_gate_f32_kernel, dim3(grid), dim3(GTHREADS), 0, stream, (const float*)a.x, a.dw_w,
                        a.dw_b, a.pw_w, a.pw_b, (float*)a.g, a.B, a.H, a.W, a.C, nseg, ntiles);
     return hipGetLastError();
   }
-  switch ((a.C + 31) / 32) {
+  // bf16: persistent workgroups, as many as are resident at once (two per CU up to 128
+  // channels, one beyond: LDS and registers), each walking a contiguous range of tiles
+  const int nb = (a.C + 31) / 32;
+  const long cap = (nb > 4 ? 1L : 2L) * device_cus();
+  const int grid = (int)(ntiles < cap ? ntiles : cap);
+  switch (nb) {
     case 1: return launch_gate_bf16<1>(a, nseg, ntiles, grid, stream);
     case 2: return launch_gate_bf16<2>(a, nseg, ntiles, grid, stream);
     case 3: return launch_gate_bf16<3>(a, nseg, ntiles, grid, stream);
