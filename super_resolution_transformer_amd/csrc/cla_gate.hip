@@ -19,19 +19,22 @@
 // while the row y+2 of the next tile lands in the fourth: every input row is
 // loaded once per column range instead of once for each of the three tiles
 // that read it, and its latency hides behind a whole tile.
-// Phase 1 computes the depth-wise stencil in fp32 from LDS
-// (each thread owns one channel pair, keeps its 18 taps in registers and walks
-// a run of 8 consecutive tokens, so every input column is read and unpacked
-// once) and writes D, rounded to bf16, into a second LDS tile.
+// Phase 1 computes the depth-wise stencil from LDS with v_dot2_f32_bf16 (bf16
+// taps and inputs, exact products, fp32 sums): each thread owns one channel
+// pair, keeps its taps in registers and walks a run of 8 consecutive tokens,
+// so every input column is read and permuted once; it writes D, rounded to
+// bf16, into a D tile.
 // Phase 2 is the point-wise product as G^T = W_pw^T D^T on
 // v_mfma_f32_32x32x16_bf16: each wave keeps its 32-channel output blocks of
 // W_pw^T as A operands in VGPRs for the whole launch and reads the B operands
 // (8 channels of one token per lane) from the D tile; in the accumulator each
 // lane holds one token and 4 groups of 4 consecutive output channels (the
 // accumulator starts from their biases), which are rounded and written into an
-// LDS output tile; the tile's tokens
-// are one contiguous span of G, stored with 16-byte writes.  The fp32 path
-// keeps D in fp32 and does the point-wise sum with FMAs.
+// LDS output tile; the tile's tokens are one contiguous span of G, stored with
+// 16-byte writes.  The two phases are software-pipelined: a step computes the
+// stencil of one tile while the matrix core runs the point-wise product of the
+// previous one, and stores the tile before that.  The fp32 path keeps the
+// weights and D in fp32 and does the point-wise sum with FMAs.
 #include "rib_device.hpp"
 #include "rib_launch.hpp"
 
@@ -112,9 +115,10 @@ struct GateShape {
   static constexpr int DSTR = 8 * KCH + 4;    // dwords per token row of the D tile (bank spread)
   static constexpr int XT = GT + 2;           // tokens of an input row segment (left/right halo)
   // one input row segment as 16-byte chunks (at most XT tokens of 16*NB dwords), loaded in
-  // NPASS passes of NT lanes; the buffer holds the last pass's overrun too
+  // NPASS passes of NT lanes; a wave's 64 chunks of a pass are loaded only if the first is
+  // in the row, so a buffer holds the row's chunks rounded up to 64
   static constexpr int NPASS = (XT * 4 * NB + NT - 1) / NT;
-  static constexpr int ROW_DW = NPASS * NT * 4;
+  static constexpr int ROW_DW = (XT * 4 * NB + 63) / 64 * 64 * 4;
   static constexpr int OS_DW = GT * 16 * NB;  // output tile, NHWC order
   static constexpr int TPR = 16 * NW;         // phase-1 threads per run
   static constexpr int NRUN = GT / 4;         // tokens per run
@@ -133,12 +137,14 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
                      int nseg, long ntiles) {
   using S = GateShape<NB>;
   constexpr int XT = S::XT, KCH = S::KCH, DSTR = S::DSTR, NRUN = S::NRUN, NPASS = S::NPASS;
-  __shared__ __attribute__((aligned(16))) uint32_t dt[GT * DSTR];
+  __shared__ __attribute__((aligned(16))) uint32_t dt0[GT * DSTR];  // D tiles, by tile parity
+  __shared__ __attribute__((aligned(16))) uint32_t dt1[GT * DSTR];
   __shared__ __attribute__((aligned(16))) uint32_t rb0[S::ROW_DW];
   __shared__ __attribute__((aligned(16))) uint32_t rb1[S::ROW_DW];
   __shared__ __attribute__((aligned(16))) uint32_t rb2[S::ROW_DW];
   __shared__ __attribute__((aligned(16))) uint32_t rb3[S::ROW_DW];
-  __shared__ __attribute__((aligned(16))) uint32_t ot[S::OS_DW];
+  __shared__ __attribute__((aligned(16))) uint32_t ot0[S::OS_DW];  // output tiles, by tile parity
+  __shared__ __attribute__((aligned(16))) uint32_t ot1[S::OS_DW];
   __shared__ __attribute__((aligned(16))) float pbias[GCMAX];
 
   const int tid = threadIdx.x;
@@ -168,22 +174,34 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
     }
   }
 
-  // ---- depth-wise taps of this thread's channel pair; it computes tokens t0 .. t0+NRUN-1
+  // ---- depth-wise taps of this thread's channel pair (channel 2cp + h); it computes tokens
+  // t0 .. t0+NRUN-1.  The taps are bf16 operands of v_dot2_f32_bf16: w01[h][j] holds the
+  // taps of rows y-1 and y in input column j (x-1, x, x+1), w2[h][j] the row y+1 tap in
+  // half h and zero in the other half, so that it can be dotted with the input word of the
+  // channel pair as read
   const int cp = tid % S::TPR;
   const int t0 = (tid / S::TPR) * NRUN;
   const bool has_pair = cp < CP;
-  float tap[2][9], tb[2];
+  uint32_t w01[2][3], w2[2][3];
+  float tb[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int c = 2 * cp + h;
+    float tap[9];
 #pragma unroll
-    for (int k = 0; k < 9; ++k) tap[h][k] = has_pair ? dw_w[c * 9 + k] : 0.0f;
+    for (int k = 0; k < 9; ++k) tap[k] = has_pair ? dw_w[c * 9 + k] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      w01[h][j] = pack_bf16(tap[j], tap[3 + j]);
+      w2[h][j] = h == 0 ? pack_bf16(tap[6 + j], 0.0f) : pack_bf16(0.0f, tap[6 + j]);
+    }
     tb[h] = has_pair ? dw_b[c] : 0.0f;
   }
   // contraction channels [C, 16*KCH) stay zero in the D tile
   for (int e = tid; e < GT * (8 * KCH - CP); e += S::NT) {
     const int t = e / (8 * KCH - CP), p = CP + e % (8 * KCH - CP);
-    dt[t * DSTR + p] = 0u;
+    dt0[t * DSTR + p] = 0u;
+    dt1[t * DSTR + p] = 0u;
   }
   for (int o = tid; o < GCMAX; o += S::NT) pbias[o] = o < C ? pw_b[o] : 0.0f;
 
@@ -218,6 +236,7 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
     const long base = ((((long)b * H + yrow) * W + (x0 - 1)) * CP) * 4;  // may be negative
 #pragma unroll
     for (int j = 0; j < NPASS; ++j) {
+      if (wave * 64 + j * S::NT >= NCHK) break;  // wave-uniform
       const int xt = x0 - 1 + ptok[j];
       const bool valid = row_ok && ptok[j] >= 0 && xt >= 0 && xt < W;
       const unsigned off = valid ? (unsigned)(base + (long)pre[j]) : 0xFFFFFFF0u;
@@ -227,93 +246,146 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
   };
 
 
-  // One tile: output row y, tokens x0 .. x0+GT-1.  Rows y-1, y, y+1 have landed; the row
-  // y+2 of the next tile (if this workgroup computes it) is loaded meanwhile.
-  auto step = [&](auto kc, int b, int y, int x0, bool more) {
-    constexpr int K = decltype(kc)::value;
-    const uint32_t* up = GATE_RING((K + 3) & 3);
-    const uint32_t* mid = GATE_RING(K);
-    const uint32_t* dn = GATE_RING((K + 1) & 3);
-    if (more) issue_row(GATE_RING((K + 2) & 3), b, y + 2, x0);  // that array held row y-2
-    // ---- phase 1: D = depth-wise 3x3 (fp32) over the run, rounded to bf16 into the D tile;
-    // a column of three input values is read and unpacked once and used by three tokens
-    if (has_pair) {
-      float c0[3][2], c1[3][2], c2[3][2];  // input columns x-1, x, x+1 (rows y-1, y, y+1)
-      auto column = [&](int p, float (&c)[3][2]) {
-        const uint32_t v0 = up[p * TS + cp], v1 = mid[p * TS + cp], v2 = dn[p * TS + cp];
-        c[0][0] = bf16_lo(v0);
-        c[0][1] = bf16_hi(v0);
-        c[1][0] = bf16_lo(v1);
-        c[1][1] = bf16_hi(v1);
-        c[2][0] = bf16_lo(v2);
-        c[2][1] = bf16_hi(v2);
-      };
-      column(t0, c0);
-      column(t0 + 1, c1);
+  // ---- one tile's stencil, with the point-wise product of the previous tile spread over it.
+  // Phase 1: D = depth-wise 3x3 of the tile over this thread's run (bf16 products with fp32
+  // accumulation, six v_dot2_f32_bf16 per channel and token), rounded to bf16 into a D tile;
+  // a column of three input words is read and permuted once and used by three tokens.  Phase 2 (MMA): G^T = W_pw^T D^T of the previous tile for this wave's
+  // output block, started from the bias, its KCH matrix-core products issued one or two per
+  // token of the run so that they execute while the wave's vector work goes on.  Threads
+  // without a channel pair read pair 0 (one broadcast address) and store nothing.  The
+  // token loop has no branches.
+  auto work = [&](auto mma_c, const uint32_t* up, const uint32_t* mid, const uint32_t* dn, uint32_t* dtw,
+                  const uint32_t* dtr, f32x16_t& acc) {
+    constexpr bool MMA = decltype(mma_c)::value;
+    // the run's NRUN + 2 input columns, all read up front so that no token waits for LDS
+    const int cpr = has_pair ? cp : 0;
+    uint32_t raw[NRUN + 2][3];
 #pragma unroll
-      for (int i = 0; i < NRUN; ++i) {
-        column(t0 + i + 2, c2);
-        float a0 = tb[0], a1 = tb[1];
-#pragma unroll
-        for (int r = 0; r < 3; ++r) {
-          a0 = fmaf(c0[r][0], tap[0][3 * r], a0);
-          a1 = fmaf(c0[r][1], tap[1][3 * r], a1);
-          a0 = fmaf(c1[r][0], tap[0][3 * r + 1], a0);
-          a1 = fmaf(c1[r][1], tap[1][3 * r + 1], a1);
-          a0 = fmaf(c2[r][0], tap[0][3 * r + 2], a0);
-          a1 = fmaf(c2[r][1], tap[1][3 * r + 2], a1);
-        }
-#pragma unroll
-        for (int r = 0; r < 3; ++r)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            c0[r][h] = c1[r][h];
-            c1[r][h] = c2[r][h];
-          }
-        dt[(t0 + i) * DSTR + cp] = x0 + t0 + i < W ? pack_bf16(a0, a1) : 0u;
-      }
+    for (int p = 0; p < NRUN + 2; ++p) {
+      raw[p][0] = up[(t0 + p) * TS + cpr];
+      raw[p][1] = mid[(t0 + p) * TS + cpr];
+      raw[p][2] = dn[(t0 + p) * TS + cpr];
     }
-    lds_barrier();
-    // ---- phase 2: G^T = W_pw^T D^T for this wave's output block, started from the bias and
-    // rounded into the output tile (NHWC order: token row t holds C/2 dwords)
-    if (has_block) {
-      f32x16_t acc;
+    if constexpr (MMA) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const f32x4_t bq = *reinterpret_cast<const f32x4_t*>(pbias + wave * 32 + 8 * q + 4 * gh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[4 * q + e] = bq[e];
       }
-      u32x4_t bo[KCH];
+    }
+    auto operand = [&](int kc) { return *reinterpret_cast<const u32x4_t*>(dtr + l32 * DSTR + 8 * kc + 4 * gh); };
+    // an input column as dot-product operands: lo = (row y-1, row y) of channel 2cp, hi = the
+    // same of channel 2cp+1 (one byte permute each), r2 = the row y+1 word as read
+    struct Col { uint32_t lo, hi, r2; };
+    auto column = [&](int p) {
+      return Col{__builtin_amdgcn_perm(raw[p][1], raw[p][0], 0x05040100u),
+                 __builtin_amdgcn_perm(raw[p][1], raw[p][0], 0x07060302u), raw[p][2]};
+    };
+    auto dot2 = [](uint32_t a, uint32_t b, float c) {
+      return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                             false);
+    };
+    Col c0 = column(0), c1 = column(1);
+    uint32_t dv[NRUN];
 #pragma unroll
-      for (int kc = 0; kc < KCH; ++kc) bo[kc] = *reinterpret_cast<const u32x4_t*>(dt + l32 * DSTR + 8 * kc + 4 * gh);
+    for (int i = 0; i < NRUN; ++i) {
+      if constexpr (MMA) {
 #pragma unroll
-      for (int kc = 0; kc < KCH; ++kc)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, wa[kc]),
-                                                      __builtin_bit_cast(bf16x8_t, bo[kc]), acc, 0, 0, 0);
-      uint32_t* orow = ot + l32 * CP;
+        for (int kc = i; kc < KCH; kc += NRUN)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, wa[kc]),
+                                                        __builtin_bit_cast(bf16x8_t, operand(kc)), acc, 0, 0, 0);
+      }
+      const Col c2 = column(i + 2);
+      float a0 = tb[0], a1 = tb[1];
+      a0 = dot2(c0.lo, w01[0][0], a0);
+      a1 = dot2(c0.hi, w01[1][0], a1);
+      a0 = dot2(c1.lo, w01[0][1], a0);
+      a1 = dot2(c1.hi, w01[1][1], a1);
+      a0 = dot2(c2.lo, w01[0][2], a0);
+      a1 = dot2(c2.hi, w01[1][2], a1);
+      a0 = dot2(c0.r2, w2[0][0], a0);
+      a1 = dot2(c0.r2, w2[1][0], a1);
+      a0 = dot2(c1.r2, w2[0][1], a0);
+      a1 = dot2(c1.r2, w2[1][1], a1);
+      a0 = dot2(c2.r2, w2[0][2], a0);
+      a1 = dot2(c2.r2, w2[1][2], a1);
+      c0 = c1;
+      c1 = c2;
+      dv[i] = pack_bf16(a0, a1);
+    }
+    // tokens past the map's right edge get a value too: their G rows are never stored
+    if (has_pair) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int oc = wave * 32 + 8 * q + 4 * gh;
-        if (oc < C) orow[oc >> 1] = pack_bf16(acc[4 * q], acc[4 * q + 1]);
-        if (oc + 2 < C) orow[(oc >> 1) + 1] = pack_bf16(acc[4 * q + 2], acc[4 * q + 3]);
+      for (int i = 0; i < NRUN; ++i) dtw[(t0 + i) * DSTR + cp] = dv[i];
+    }
+  };
+  // phase 2 alone (the last tile of a column range): products from the bias start
+  auto pointwise = [&](const uint32_t* dt, f32x16_t& acc) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4_t bq = *reinterpret_cast<const f32x4_t*>(pbias + wave * 32 + 8 * q + 4 * gh);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[4 * q + e] = bq[e];
+    }
+#pragma unroll
+    for (int kc = 0; kc < KCH; ++kc) {
+      const u32x4_t bo = *reinterpret_cast<const u32x4_t*>(dt + l32 * DSTR + 8 * kc + 4 * gh);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, wa[kc]),
+                                                    __builtin_bit_cast(bf16x8_t, bo), acc, 0, 0, 0);
+    }
+  };
+  // the accumulator rounded into an output tile (NHWC order: token row t holds C/2 dwords)
+  auto put = [&](const f32x16_t& acc, uint32_t* ot) {
+    uint32_t* orow = ot + l32 * CP;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int oc = wave * 32 + 8 * q + 4 * gh;
+      if (oc < C) orow[oc >> 1] = pack_bf16(acc[4 * q], acc[4 * q + 1]);
+      if (oc + 2 < C) orow[(oc >> 1) + 1] = pack_bf16(acc[4 * q + 2], acc[4 * q + 3]);
+    }
+  };
+  // an output tile's tokens are one contiguous span of G: 16-byte stores
+  auto store = [&](const uint32_t* ot, int b, int y, int x0) {
+    const int ntok = min(GT, W - x0);
+    const int ndw = ntok * CP;
+    uint32_t* gs = g + (((long)b * H + y) * W + x0) * CP;
+    for (int c4 = tid; 4 * c4 < ndw; c4 += S::NT) {
+      const int d = 4 * c4;
+      if (d + 4 <= ndw) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ot + d);
+        *reinterpret_cast<u32x4_t*>(gs + d) = v;
+      } else {
+        for (int i = d; i < ndw; ++i) gs[i] = ot[i];
       }
     }
-    lds_barrier();
-    // ---- the tile's output tokens are one contiguous span of G: 16-byte stores
-    {
-      const int ntok = min(GT, W - x0);
-      const int ndw = ntok * CP;
-      uint32_t* gs = g + (((long)b * H + y) * W + x0) * CP;
-      for (int c4 = tid; 4 * c4 < ndw; c4 += S::NT) {
-        const int d = 4 * c4;
-        if (d + 4 <= ndw) {
-          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ot + d);
-          *reinterpret_cast<u32x4_t*>(gs + d) = v;
-        } else {
-          for (int i = d; i < ndw; ++i) gs[i] = ot[i];
-        }
-      }
+  };
+
+  // One step of the pipeline, for tile i (output row y) of a column range: the stencil of
+  // tile i, the point-wise product of tile i-1 and the stores of tile i-2.  The product's
+  // matrix-core work is issued first and runs while the same waves compute the stencil on
+  // the vector units.  Rows y-1, y, y+1 have landed; the row y+2 of tile i+1 (if this
+  // workgroup computes it) is loaded meanwhile.  Tile i's D and output tiles are dt and ot
+  // of parity (i+1) & 1 = K & 1 with K = (i+1) mod 4, the ring rotation.  One barrier per
+  // step (before it) orders everything: every LDS array written in a step is read only in
+  // a later step, and every array read in a step is rewritten only in a later one.
+  auto step = [&](auto kc, int b, int y, int x0, bool more, bool prev, bool prev2) {
+    constexpr int K = decltype(kc)::value;
+    uint32_t* dtw = (K & 1) ? dt1 : dt0;
+    const uint32_t* dtr = (K & 1) ? dt0 : dt1;
+    uint32_t* otw = (K & 1) ? ot0 : ot1;
+    const uint32_t* otr = (K & 1) ? ot1 : ot0;
+    if (more) issue_row(GATE_RING((K + 2) & 3), b, y + 2, x0);  // that array held row y-2
+    if (prev2) store(otr, b, y - 2, x0);
+    const uint32_t* up = GATE_RING((K + 3) & 3);
+    const uint32_t* mid = GATE_RING(K);
+    const uint32_t* dn = GATE_RING((K + 1) & 3);
+    f32x16_t acc;
+    if (prev && has_block) {  // wave-uniform
+      work(std::true_type{}, up, mid, dn, dtw, dtr, acc);
+      put(acc, otw);
+    } else {
+      work(std::false_type{}, up, mid, dn, dtw, dtr, acc);
     }
   };
 
@@ -326,35 +398,51 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
   long t = t_begin;
   while (t < t_end) {
     const long col = t / H;
-    int y = (int)(t - col * H);
+    const int y0 = (int)(t - col * H);
     const int b = (int)(col / nseg);
     const int x0 = (int)(col - (long)b * nseg) * GT;
-    const int yend = (int)min((long)H, y + (t_end - t));
-    // all waves are past the previous column's last tile, whose phase 1 ended the row reads;
-    // row r sits in ring array (r - y + 1) mod 4 for this column range, so the steps take the
-    // arrays in a fixed rotation (straight-line code: each step's arrays are known statically)
-    issue_row(rb0, b, y - 1, x0);
-    issue_row(rb1, b, y, x0);
-    issue_row(rb2, b, y + 1, x0);
+    const int yend = (int)min((long)H, y0 + (t_end - t));
+    // all waves are past the previous column's last step, whose stencil ended the row reads;
+    // row r sits in ring array (r - y0 + 1) mod 4 for this column range, so the steps take
+    // the arrays in a fixed rotation (straight-line code: each step's arrays are known
+    // statically)
+    issue_row(rb0, b, y0 - 1, x0);
+    issue_row(rb1, b, y0, x0);
+    issue_row(rb2, b, y0 + 1, x0);
+    int y = y0;
     for (;;) {
       __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed (and its last stores)
       __syncthreads();
-      step(std::integral_constant<int, 1>{}, b, y, x0, y + 1 < yend);
+      step(std::integral_constant<int, 1>{}, b, y, x0, y + 1 < yend, y > y0, y > y0 + 1);
       if (++y >= yend) break;
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      step(std::integral_constant<int, 2>{}, b, y, x0, y + 1 < yend);
+      step(std::integral_constant<int, 2>{}, b, y, x0, y + 1 < yend, y > y0, y > y0 + 1);
       if (++y >= yend) break;
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      step(std::integral_constant<int, 3>{}, b, y, x0, y + 1 < yend);
+      step(std::integral_constant<int, 3>{}, b, y, x0, y + 1 < yend, y > y0, y > y0 + 1);
       if (++y >= yend) break;
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      step(std::integral_constant<int, 0>{}, b, y, x0, y + 1 < yend);
+      step(std::integral_constant<int, 0>{}, b, y, x0, y + 1 < yend, y > y0, y > y0 + 1);
       if (++y >= yend) break;
     }
-    t = (long)col * H + y;
+    // drain: with n = yend - y0 tiles, the last (n-1) still needs its point-wise product and
+    // both the last two their stores; tile i's arrays have parity (i+1) & 1
+    const int n = yend - y0;
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (n >= 2) store((n & 1) ? ot0 : ot1, b, yend - 2, x0);
+    if (has_block) {
+      f32x16_t acc;
+      pointwise((n & 1) ? dt1 : dt0, acc);
+      put(acc, (n & 1) ? ot1 : ot0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    store((n & 1) ? ot1 : ot0, b, yend - 1, x0);
+    t = (long)col * H + yend;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }

@@ -2,12 +2,14 @@
 C ABI) against the fp64 CPU oracle.
 
 Tolerances: fp32 maps, max abs error <= 1e-5.  bf16 maps, derived from the arithmetic.  bf16 keeps an
-8-bit significand, so rounding to nearest has relative error <= u = 2^-8.  D and the point-wise
-weights are each rounded before an fp32-accumulated product, so each term carries at most
-(2u + u^2) |D_c| |W_co| < 2^-7 |D_c W_co|; G itself is then rounded (<= u relative).  Per element
-    |err| <= 2^-7 * S + 2^-8 * |G| + 1e-5,   S = sum_c |D_c| |W_co| + |b_o|,
-where S is bounded from above by the oracle run on the absolute values of every input (the fp32
-accumulation error, <= C 2^-24 S, and the fp32 stencil's are inside the 1e-5 and the slack of u^2).
+8-bit significand, so rounding to nearest has relative error <= u = 2^-8.  The depth-wise taps, D
+and the point-wise weights are each rounded to bf16 before fp32-accumulated products (the bf16
+kernel computes the stencil with bf16 dot products), so each term of the point-wise sum carries at
+most (1 + u)^3 - 1 < 3u + 3u^2 + u^3 < 2^-6 of |D_c|_abs |W_co|, |D_c|_abs being the stencil on
+absolute values; G itself is then rounded (<= u relative).  Per element
+    |err| <= 2^-6 * S + 2^-8 * |G| + 1e-5,   S = sum_c |D_c|_abs |W_co| + |b_o|,
+where S is the oracle run on the absolute values of every input (the fp32 accumulation errors,
+<= C 2^-24 S, are inside the 1e-5 and the slack of 2^-6 over 3u + 3u^2 + u^3).
 Identity weights and locality are checked bit for bit.
 """
 import sys
@@ -57,7 +59,7 @@ def compare(got, want, dtype, what, S=None):
     if dtype == "f32":
         tol = np.full_like(want, TOL["f32"])
     else:
-        tol = 2.0 ** -7 * S + 2.0 ** -8 * np.abs(want) + 1e-5
+        tol = 2.0 ** -6 * S + 2.0 ** -8 * np.abs(want) + 1e-5
     worst = float((err / tol).max()) if err.size else 0.0
     note(f"  {what}: max|err| {float(err.max()) if err.size else 0.0:.3g}  max|G| {float(np.abs(want).max()):.3g}"
          f"  max err/tol {worst:.3f}")
