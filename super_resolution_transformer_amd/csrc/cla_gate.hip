@@ -46,18 +46,6 @@ constexpr int GT = 32;          // tokens per tile
 constexpr int GTHREADS = 256;   // four waves
 constexpr int GCMAX = 256;      // largest channel count
 
-// Workgroup barrier that orders LDS only.  __syncthreads() also releases global memory,
-// which makes every wave wait for its LDS-bound buffer loads first; here the next tile's
-// loads must stay in flight across the barriers of the current tile.
-// (s_waitcnt lgkmcnt(0) with the other counters left at their maximum: 0xC07F on gfx9;
-// the signal fences keep the compiler from moving memory accesses across the barrier.)
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 __device__ __forceinline__ void tile_coords(long tile, int nseg, int H, int& b, int& y, int& x0) {
   const int seg = (int)(tile % nseg);
   const long t2 = tile / nseg;
