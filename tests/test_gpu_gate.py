@@ -94,6 +94,20 @@ def test_gate_whole_output(torch, B, H, W, C, dtype):
     compare(g.float().cpu().numpy().astype(np.float64), want, dtype, "G", abs_bound(p) if dtype == "bf16" else None)
 
 
+@pytest.mark.parametrize("B,H,W,C", [(2, 203, 90, 180), (3, 150, 70, 48)])
+def test_gate_whole_output_long_ranges(torch, B, H, W, C):
+    """Maps with several times more 32-token tiles than workgroups (1218 tiles at C = 180, 1350 at
+    C = 48), ragged in W and H: every workgroup walks a range of tiles down the map's columns, the
+    ranges start and end mid-column and cross column and image boundaries.  Whole output."""
+    note(f"gate long ranges B={B} H={H} W={W} C={C}")
+    p = synthetic.make_gate_problem(B, H, W, C, "bf16", seed=B + H + W + C)
+    x, w = to_dev(torch, p)
+    g = rib.cla_gate(x, *w)
+    torch.cuda.synchronize()
+    want = oracle.cla_gate(p.x, p.dw_w, p.dw_b, p.pw_w, p.pw_b)
+    compare(g.float().cpu().numpy().astype(np.float64), want, "bf16", "G", abs_bound(p))
+
+
 @pytest.mark.parametrize("shape", [(32, 96, 96, 180), (1, 180, 320, 48), (1, 360, 640, 180)])
 def test_gate_full_size_bands(torch, shape):
     """Full-size maps of the workloads; row bands (top, middle, bottom) of the first and last
