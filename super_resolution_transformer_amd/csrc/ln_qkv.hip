@@ -49,6 +49,21 @@ __device__ __forceinline__ f32x4_t lq_mfma(const u32x4_t& a, const u32x4_t& b, c
                                                  0, 0, 0);
 }
 
+// Sum over the 16 lanes of a DPP row (lanes 16k .. 16k+15), result in every lane of the row:
+// swap within pairs, then within quads, then mirror the half-row (quad 0 <-> quad 1) and the
+// row (half 0 <-> half 1).  Four DPP-modified adds, no LDS round trip.
+__device__ __forceinline__ float row16_sum(float v) {
+  auto dpp = [](float x, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  v += dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  v += dpp(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  v += dpp(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  v += dpp(v, std::integral_constant<int, 0x140>{});  // row_mirror
+  return v;
+}
+
 // Wait until at most n of this wave's vector memory operations are in flight
 // (they complete in issue order): the next tile's copies are issued before the
 // current tile's output stores, so waiting for the copies leaves the stores
@@ -85,8 +100,8 @@ ln_qkv_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ gam
   __shared__ __attribute__((aligned(16))) uint32_t s_xb[S::XT_DW];
   __shared__ __attribute__((aligned(16))) uint32_t s_b[S::B_DW];
   __shared__ __attribute__((aligned(16))) uint32_t s_o[S::O_DW];
-  __shared__ float s_gb[2][S::KP];
-  __shared__ float s_bias[3 * S::KP];
+  __shared__ __attribute__((aligned(16))) float s_gb[2][S::KP];
+  __shared__ __attribute__((aligned(16))) float s_bias[3 * S::KP];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -167,8 +182,7 @@ ln_qkv_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ gam
       float sum = 0.0f;
 #pragma unroll
       for (int i = 0; i < CPT; ++i) sum += xv[i];  // channels past C hold 0
-#pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 16);
+      sum = row16_sum(sum);
       const float mu = sum * (1.0f / (float)C);
       float sq = 0.0f;
 #pragma unroll
@@ -176,17 +190,18 @@ ln_qkv_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ gam
         const float d = c0 + i < C ? xv[i] - mu : 0.0f;
         sq = fmaf(d, d, sq);
       }
-#pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) sq += __shfl_xor(sq, m, 16);
+      sq = row16_sum(sq);
       const float inv = 1.0f / sqrtf(sq / (float)C + eps);
       uint32_t* xo = xcur + t * (C / 2);
 #pragma unroll
       for (int g4 = 0; g4 < CPT / 4; ++g4) {
         const int c = c0 + 4 * g4;
         if (c < C) {
+          const f32x4_t gm = *reinterpret_cast<const f32x4_t*>(&s_gb[0][c]);
+          const f32x4_t bt = *reinterpret_cast<const f32x4_t*>(&s_gb[1][c]);
           float y[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = t < nt ? (xv[4 * g4 + e] - mu) * inv * s_gb[0][c + e] + s_gb[1][c + e] : 0.0f;
+          for (int e = 0; e < 4; ++e) y[e] = t < nt ? (xv[4 * g4 + e] - mu) * inv * gm[e] + bt[e] : 0.0f;
           const u32x2_t pk = {pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
           *reinterpret_cast<u32x2_t*>(s_b + (c >> 3) * S::BCS + 4 * t + ((c & 7) >> 1)) = pk;  // chunk c/8, token t
           if (xn) *reinterpret_cast<u32x2_t*>(xo + c / 2) = pk;  // the tile's own copy becomes LN(X)
@@ -196,11 +211,17 @@ ln_qkv_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ gam
     __syncthreads();
 
     // ---- y^T = W^T xn^T per 16 tokens (tg), then + bias, bf16, into the output tile [part][token][C]
+    // accumulators start from the bias of the lane's 4 outputs (blocks past 3C compute nothing;
+    // for the others ob + 15 < 3C rounded up to 16 <= 3 KP, inside s_bias)
     f32x4_t acc[NBW][2];
 #pragma unroll
-    for (int i = 0; i < NBW; ++i)
+    for (int i = 0; i < NBW; ++i) {
+      const int ob = 16 * (wave + LQ_NW * i);
+      const f32x4_t b4 = ob < C3 ? *reinterpret_cast<const f32x4_t*>(s_bias + ob + 4 * g)
+                                 : (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int tg = 0; tg < 2; ++tg) acc[i][tg] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+      for (int tg = 0; tg < 2; ++tg) acc[i][tg] = b4;
+    }
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       // B operand: lane = (token 16 tg + l16, channels 32kc + 8g .. +7) = chunk 4kc + g
@@ -222,8 +243,8 @@ ln_qkv_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ gam
         const int part = o0 / C, ch = o0 - part * C;
 #pragma unroll
         for (int tg = 0; tg < 2; ++tg) {
-          const uint32_t lo = pack_bf16(acc[i][tg][0] + s_bias[o0], acc[i][tg][1] + s_bias[o0 + 1]);
-          const uint32_t hi = pack_bf16(acc[i][tg][2] + s_bias[o0 + 2], acc[i][tg][3] + s_bias[o0 + 3]);
+          const uint32_t lo = pack_bf16(acc[i][tg][0], acc[i][tg][1]);
+          const uint32_t hi = pack_bf16(acc[i][tg][2], acc[i][tg][3]);
           *reinterpret_cast<u32x2_t*>(ot + (part * LQ_TT + 16 * tg + l16) * C + ch) = (u32x2_t){lo, hi};
         }
       }
