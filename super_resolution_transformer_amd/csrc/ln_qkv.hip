@@ -314,16 +314,14 @@ ln_qkv_plain_kernel(const T* __restrict__ x, const float* __restrict__ gamma, co
     const T* xt = x + (t0 + t) * C;
     float sum = 0.0f;
     for (int c = sub; c < C; c += 16) sum += lq_ld(xt, c);
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) sum += __shfl_xor(sum, m, 16);
+    sum = row16_sum(sum);  // the 16 threads of token t are one DPP row, active together
     const float mu = sum / (float)C;
     float sq = 0.0f;
     for (int c = sub; c < C; c += 16) {
       const float d = lq_ld(xt, c) - mu;
       sq = fmaf(d, d, sq);
     }
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) sq += __shfl_xor(sq, m, 16);
+    sq = row16_sum(sq);
     const float inv = 1.0f / sqrtf(sq / (float)C + eps);
     for (int c = sub; c < C; c += 16) {
       const float y = (lq_ld(xt, c) - mu) * inv * gamma[c] + beta[c];
