@@ -358,17 +358,27 @@ bwd_table_reduce_kernel(BwdArgs a) {
   const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws;
   const int hb0 = a.tab_heads > 1 ? th * a.B : 0;                 // rows are [heads][B][H][W][R]
   const int hb1 = a.tab_heads > 1 ? (th + 1) * a.B : a.heads * a.B;
+  // every (window, image-head) term of this table entry; eight independent partial sums keep
+  // eight loads of the image-head loop in flight
+  const long hstride = (long)a.H * a.W * a.R;
   float acc = 0.0f;
-  for (int hb = hb0; hb < hb1; ++hb)
-    for (int wy = 0; wy < nWy; ++wy) {
-      const int y = wy * a.ws + iy;
-      if (y >= a.H) break;
-      for (int wx = 0; wx < nWx; ++wx) {
-        const int x = wx * a.ws + ix;
-        if (x >= a.W) break;
-        acc += rows[(((long)hb * a.H + y) * a.W + x) * a.R + r];
+  for (int wy = 0; wy < nWy; ++wy) {
+    const int y = wy * a.ws + iy;
+    if (y >= a.H) break;
+    for (int wx = 0; wx < nWx; ++wx) {
+      const int x = wx * a.ws + ix;
+      if (x >= a.W) break;
+      const float* p = rows + (((long)hb0 * a.H + y) * a.W + x) * a.R + r;
+      float s[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+      int hb = hb0;
+      for (; hb + 8 <= hb1; hb += 8, p += 8 * hstride) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s[k] += p[k * hstride];
       }
+      for (; hb < hb1; ++hb, p += hstride) s[0] += p[0];
+      acc += ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
     }
+  }
   (tab ? a.dkp : a.dqp)[(long)th * N * a.R + n * a.R + r] = acc;
 }
 
