@@ -107,6 +107,82 @@ bwd_prep_staged_kernel(const T* __restrict__ dout, const T* __restrict__ o, cons
   }
 }
 
+// prep, bf16 maps with dh <= 32: the same staging with 16-byte copies (NT even, so a tile
+// starts 16-byte aligned whenever C is a multiple of 4), and the rows computed by 16 lanes
+// each (one DPP row): lane p takes channel pair p of its (token, head) row as one dword, D is
+// the row's DPP sum.  Lanes past dh/2 or past the tile's rows compute zeros and store nothing.
+__device__ __forceinline__ float prep_row16_sum(float v) {
+  auto dpp = [](float x, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  v += dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  v += dpp(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  v += dpp(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  v += dpp(v, std::integral_constant<int, 0x140>{});  // row_mirror
+  return v;
+}
+
+__global__ void __launch_bounds__(256)
+bwd_prep_pairs_kernel(const uint32_t* __restrict__ dout, const uint32_t* __restrict__ o,
+                      const uint32_t* __restrict__ g, uint32_t* __restrict__ da, uint32_t* __restrict__ dg,
+                      float* __restrict__ dsum, long ntok, int heads, int dh, int NT) {
+  extern __shared__ uint32_t sm[];
+  const int C2 = heads * dh / 2;  // dwords per token
+  const long tok0 = (long)blockIdx.x * NT;
+  const int nt = (int)min((long)NT, ntok - tok0);
+  const int ndw = nt * C2;
+  const int cap = NT * C2;
+  uint32_t* s_do = sm;
+  uint32_t* s_o = sm + cap;
+  uint32_t* s_g = sm + 2 * cap;
+  const long base = tok0 * C2;
+  // 16-byte copies: C2 and NT even keep the tile and the three LDS arrays 16-byte aligned
+  const bool vec = (C2 % 2 == 0) && (base & 3) == 0;
+  auto copy_in = [&](uint32_t* dst, const uint32_t* __restrict__ src) {
+    if (vec) {
+      for (int i = 4 * (int)threadIdx.x; i + 4 <= ndw; i += 1024)
+        *reinterpret_cast<u32x4_t*>(dst + i) = *reinterpret_cast<const u32x4_t*>(src + base + i);
+      for (int i = (ndw & ~3) + (int)threadIdx.x; i < ndw; i += 256) dst[i] = src[base + i];
+    } else {
+      for (int i = threadIdx.x; i < ndw; i += 256) dst[i] = src[base + i];
+    }
+  };
+  copy_in(s_do, dout);
+  copy_in(s_o, o);
+  copy_in(s_g, g);
+  __syncthreads();
+  const int pr = threadIdx.x & 15;
+  const int hp = dh / 2;
+  const int rows = nt * heads;
+  for (int r0 = 0; r0 < rows; r0 += 16) {
+    const int row = r0 + ((int)threadIdx.x >> 4);
+    const bool live = row < rows && pr < hp;
+    const int e = live ? (row / heads) * C2 + (row % heads) * hp + pr : 0;
+    const uint32_t wdo = live ? s_do[e] : 0u, wo = live ? s_o[e] : 0u, wg = live ? s_g[e] : 0u;
+    const float do0 = bf16_lo(wdo), do1 = bf16_hi(wdo), o0 = bf16_lo(wo), o1 = bf16_hi(wo);
+    const float s0 = 1.0f / (1.0f + expf(-bf16_lo(wg))), s1 = 1.0f / (1.0f + expf(-bf16_hi(wg)));
+    const float D = prep_row16_sum(fmaf(do1, o1, do0 * o0));
+    if (live) {
+      s_do[e] = pack_bf16(do0 * s0, do1 * s1);
+      s_o[e] = pack_bf16(do0 * o0 * (1.0f - s0), do1 * o1 * (1.0f - s1));
+      if (pr == 0) dsum[tok0 * heads + row] = D;
+    }
+  }
+  __syncthreads();
+  auto copy_out = [&](uint32_t* __restrict__ dst, const uint32_t* src) {
+    if (vec) {
+      for (int i = 4 * (int)threadIdx.x; i + 4 <= ndw; i += 1024)
+        *reinterpret_cast<u32x4_t*>(dst + base + i) = *reinterpret_cast<const u32x4_t*>(src + i);
+      for (int i = (ndw & ~3) + (int)threadIdx.x; i < ndw; i += 256) dst[base + i] = src[i];
+    } else {
+      for (int i = threadIdx.x; i < ndw; i += 256) dst[base + i] = src[i];
+    }
+  };
+  copy_out(da, s_do);
+  copy_out(dg, s_o);
+}
+
 // prep for rows too wide to stage (C * sizeof(T) > 16 KB): one thread per (token, head).
 template <typename T>
 __global__ void __launch_bounds__(256)
@@ -410,6 +486,15 @@ hipError_t launch_prep(const BwdArgs& a, hipStream_t stream) {
   const long ntok = (long)a.B * a.H * a.W;
   const int C = a.heads * a.dh;
   const int row_bytes = C * (int)sizeof(T);
+  if (sizeof(T) == 2 && a.dh % 2 == 0 && a.dh <= 32 && row_bytes % 4 == 0 && row_bytes <= 16384) {
+    const int NT = max(2, (6144 / row_bytes) & ~1);  // even; <= 18 KB of LDS: eight workgroups per CU
+    const int grid = (int)((ntok + NT - 1) / NT);
+    const size_t lds = 3 * (size_t)NT * row_bytes;
+    hipLaunchKernelGGL(bwd_prep_pairs_kernel, dim3(grid), dim3(256), lds, stream, (const uint32_t*)a.dout,
+                       (const uint32_t*)a.o, (const uint32_t*)a.g, (uint32_t*)a.da, (uint32_t*)a.dg, a.dsum, ntok,
+                       a.heads, a.dh, NT);
+    return hipGetLastError();
+  }
   if (row_bytes % 4 == 0 && row_bytes <= 16384) {
     const int NT = max(1, 16384 / row_bytes);  // <= 48 KB of LDS for the three maps
     const int grid = (int)((ntok + NT - 1) / NT);
