@@ -80,6 +80,8 @@ GATE = [
     (1, 3, 70, 62, "bf16"),
     (1, 4, 5, 256, "bf16"),
     (2, 17, 65, 96, "bf16"),
+    (2, 5, 9, 2, "bf16"),   # one channel pair: the smallest map the kernels take
+    (1, 4, 33, 2, "f32"),
 ]
 
 
