@@ -699,6 +699,25 @@ __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc,
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();
   }
+  // the gate values of the epilogue are loaded now, so that their latency hides behind the
+  // last tile's softmax and product instead of following them
+  int goff[2];
+  uint32_t gv[2][S::DT][4][2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int r = q0 + wave * QW + qb * 32 + l32;
+    int n;
+    locate<DH>(G, r < G.n_real ? r : G.n_real - 1, goff[qb], n);
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = dt * 32 + 8 * q4 + 4 * gh;
+        const int gw = (goff[qb] + d0) >> 1;
+        gv[qb][dt][q4][0] = active && d0 < DH ? g[gw] : 0u;
+        gv[qb][dt][q4][1] = active && d0 + 4 <= DH ? g[gw + 1] : 0u;
+      }
+  }
   softmax(ntiles - 1);
   __syncthreads();
   if (active) {
@@ -716,8 +735,7 @@ __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc,
     const float lsum = row_sum(rg, qb);
     if (r >= G.n_real) continue;
     const float inv = 1.0f / lsum;
-    int off, n;
-    locate<DH>(G, r, off, n);
+    const int off = goff[qb];
     if (lse) lse[(off - G.h * DH) / G.C * heads + G.h] = (rg.mhat[qb] + OFF + __log2f(lsum)) * LN2;
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
@@ -727,11 +745,11 @@ __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc,
         if (d0 >= DH) continue;
         const int e0 = 4 * q4;
         const int gw = (off + d0) >> 1;  // dword index of channels (d0, d0+1)
-        const uint32_t g01 = g[gw];
+        const uint32_t g01 = gv[qb][dt][q4][0];
         const uint32_t r01 = pack_bf16(rg.O[qb][dt][e0 + 0] * inv * sigmoidf(bf16_lo(g01)),
                                        rg.O[qb][dt][e0 + 1] * inv * sigmoidf(bf16_hi(g01)));
         if (d0 + 4 <= DH) {
-          const uint32_t g23 = g[gw + 1];
+          const uint32_t g23 = gv[qb][dt][q4][1];
           const uint32_t r23 = pack_bf16(rg.O[qb][dt][e0 + 2] * inv * sigmoidf(bf16_lo(g23)),
                                          rg.O[qb][dt][e0 + 3] * inv * sigmoidf(bf16_hi(g23)));
           o[gw] = r01;
