@@ -324,13 +324,22 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
     }
   };
   // the accumulator rounded into an output tile (NHWC order: token row t holds C/2 dwords)
+  // (with C % 4 == 0 the row stride C/2 and oc/2 are even: a pair of dwords is one aligned
+  // 8-byte write; otherwise two 4-byte writes)
   auto put = [&](const f32x16_t& acc, uint32_t* ot) {
     uint32_t* orow = ot + l32 * CP;
+    const bool pair8 = (CP & 1) == 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int oc = wave * 32 + 8 * q + 4 * gh;
-      if (oc < C) orow[oc >> 1] = pack_bf16(acc[4 * q], acc[4 * q + 1]);
-      if (oc + 2 < C) orow[(oc >> 1) + 1] = pack_bf16(acc[4 * q + 2], acc[4 * q + 3]);
+      const uint32_t lo = pack_bf16(acc[4 * q], acc[4 * q + 1]);
+      const uint32_t hi = pack_bf16(acc[4 * q + 2], acc[4 * q + 3]);
+      if (pair8 && oc + 2 < C) {
+        *reinterpret_cast<u32x2_t*>(orow + (oc >> 1)) = (u32x2_t){lo, hi};
+      } else {
+        if (oc < C) orow[oc >> 1] = lo;
+        if (oc + 2 < C) orow[(oc >> 1) + 1] = hi;
+      }
     }
   };
   // an output tile's tokens are one contiguous span of G: 16-byte stores
