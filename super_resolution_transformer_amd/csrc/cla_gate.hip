@@ -141,12 +141,34 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
   const int l32 = lane & 31;
   const int gh = lane >> 5;
   const int CP = C >> 1;  // channel pairs
-  const bool has_block = wave < NB && wave * 32 < C;
+  // C in 162..192 (NB = 6): the product runs as 16x16x32 blocks, each of the 8 waves taking
+  // one 16-token half of the tile (th) and three 16-channel output blocks (3 g4 .. 3 g4 + 2),
+  // so every SIMD issues the same matrix-core work and a wave reads half of the D tile.
+  // Otherwise wave w owns the 32-channel output block w (32x32x16 blocks).
+  constexpr bool SPLIT = NB == 6;
+  constexpr int NWA = SPLIT ? 3 * NB : KCH;  // A operands held by a wave
+  const int th = wave >> 2, g4 = wave & 3, l16 = lane & 15, kg = lane >> 4;
+  const bool has_block = SPLIT ? true : (wave < NB && wave * 32 < C);
 
   // ---- point-wise weights as A operands of this wave's output block: row = output
   // channel, 8 input channels per lane
-  u32x4_t wa[KCH];
-  {
+  u32x4_t wa[NWA];
+  if constexpr (SPLIT) {
+    // operand m = j NB + ks: output channel 16 (3 g4 + j) + l16, input channels 32 ks + 8 kg ..
+#pragma unroll
+    for (int m = 0; m < NWA; ++m) {
+      const int o = 16 * (3 * g4 + m / NB) + l16;
+      uint32_t w4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 32 * (m % NB) + 8 * kg + 2 * i;
+        const float a = (o < C && c < C) ? pw_w[c * C + o] : 0.0f;
+        const float b2 = (o < C && c + 1 < C) ? pw_w[(c + 1) * C + o] : 0.0f;
+        w4[i] = pack_bf16(a, b2);
+      }
+      wa[m] = (u32x4_t){w4[0], w4[1], w4[2], w4[3]};
+    }
+  } else {
     const int o = wave * 32 + l32;
 #pragma unroll
     for (int kc = 0; kc < KCH; ++kc) {
@@ -161,6 +183,9 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
       wa[kc] = (u32x4_t){w4[0], w4[1], w4[2], w4[3]};
     }
   }
+  // the product's accumulator: one 32x32 block, or three 16x16 blocks
+  struct AccSplit { f32x4_t a[3]; };
+  using Acc = std::conditional_t<SPLIT, AccSplit, f32x16_t>;
 
   // ---- depth-wise taps of this thread's channel pair (channel 2cp + h); it computes tokens
   // t0 .. t0+NRUN-1.  The taps are bf16 operands of v_dot2_f32_bf16: w01[h][j] holds the
@@ -234,6 +259,35 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
   };
 
 
+  // the product's pieces: accumulators from the bias, and product m of the wave's NWA
+  auto acc_init = [&](Acc& acc) {
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        acc.a[j] = *reinterpret_cast<const f32x4_t*>(pbias + 16 * (3 * g4 + j) + 4 * kg);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4_t bq = *reinterpret_cast<const f32x4_t*>(pbias + wave * 32 + 8 * q + 4 * gh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * q + e] = bq[e];
+      }
+    }
+  };
+  auto mma_step = [&](const uint32_t* dt, int m, Acc& acc) {
+    if constexpr (SPLIT) {
+      // B operand: token 16 th + l16, input channels 32 ks + 8 kg .. +7
+      const int ks = m % NB;
+      const u32x4_t bo = *reinterpret_cast<const u32x4_t*>(dt + (16 * th + l16) * DSTR + 16 * ks + 4 * kg);
+      acc.a[m / NB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[m]),
+                                                             __builtin_bit_cast(bf16x8_t, bo), acc.a[m / NB], 0, 0, 0);
+    } else {
+      const u32x4_t bo = *reinterpret_cast<const u32x4_t*>(dt + l32 * DSTR + 8 * m + 4 * gh);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, wa[m]),
+                                                    __builtin_bit_cast(bf16x8_t, bo), acc, 0, 0, 0);
+    }
+  };
+
   // ---- one tile's stencil, with the point-wise product of the previous tile spread over it.
   // Phase 1: D = depth-wise 3x3 of the tile over this thread's run (bf16 products with fp32
   // accumulation, six v_dot2_f32_bf16 per channel and token), rounded to bf16 into a D tile;
@@ -243,7 +297,7 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
   // without a channel pair read pair 0 (one broadcast address) and store nothing.  The
   // token loop has no branches.
   auto work = [&](auto mma_c, const uint32_t* up, const uint32_t* mid, const uint32_t* dn, uint32_t* dtw,
-                  const uint32_t* dtr, f32x16_t& acc) {
+                  const uint32_t* dtr, Acc& acc) {
     constexpr bool MMA = decltype(mma_c)::value;
     // the run's NRUN + 2 input columns, all read up front so that no token waits for LDS
     const int cpr = has_pair ? cp : 0;
@@ -254,15 +308,7 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
       raw[p][1] = mid[(t0 + p) * TS + cpr];
       raw[p][2] = dn[(t0 + p) * TS + cpr];
     }
-    if constexpr (MMA) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4_t bq = *reinterpret_cast<const f32x4_t*>(pbias + wave * 32 + 8 * q + 4 * gh);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * q + e] = bq[e];
-      }
-    }
-    auto operand = [&](int kc) { return *reinterpret_cast<const u32x4_t*>(dtr + l32 * DSTR + 8 * kc + 4 * gh); };
+    if constexpr (MMA) acc_init(acc);
     // an input column as dot-product operands: lo = (row y-1, row y) of channel 2cp, hi = the
     // same of channel 2cp+1 (one byte permute each), r2 = the row y+1 word as read
     struct Col { uint32_t lo, hi, r2; };
@@ -280,9 +326,7 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
     for (int i = 0; i < NRUN; ++i) {
       if constexpr (MMA) {
 #pragma unroll
-        for (int kc = i; kc < KCH; kc += NRUN)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, wa[kc]),
-                                                        __builtin_bit_cast(bf16x8_t, operand(kc)), acc, 0, 0, 0);
+        for (int m = i; m < NWA; m += NRUN) mma_step(dtr, m, acc);
       }
       const Col c2 = column(i + 2);
       float a0 = tb[0], a1 = tb[1];
@@ -309,37 +353,37 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
     }
   };
   // phase 2 alone (the last tile of a column range): products from the bias start
-  auto pointwise = [&](const uint32_t* dt, f32x16_t& acc) {
+  auto pointwise = [&](const uint32_t* dt, Acc& acc) {
+    acc_init(acc);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4_t bq = *reinterpret_cast<const f32x4_t*>(pbias + wave * 32 + 8 * q + 4 * gh);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[4 * q + e] = bq[e];
-    }
-#pragma unroll
-    for (int kc = 0; kc < KCH; ++kc) {
-      const u32x4_t bo = *reinterpret_cast<const u32x4_t*>(dt + l32 * DSTR + 8 * kc + 4 * gh);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, wa[kc]),
-                                                    __builtin_bit_cast(bf16x8_t, bo), acc, 0, 0, 0);
-    }
+    for (int m = 0; m < NWA; ++m) mma_step(dt, m, acc);
   };
   // the accumulator rounded into an output tile (NHWC order: token row t holds C/2 dwords)
   // (with C % 4 == 0 the row stride C/2 and oc/2 are even: a pair of dwords is one aligned
   // 8-byte write; otherwise two 4-byte writes)
-  auto put = [&](const f32x16_t& acc, uint32_t* ot) {
-    uint32_t* orow = ot + l32 * CP;
+  auto put = [&](const Acc& acc, uint32_t* ot) {
     const bool pair8 = (CP & 1) == 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int oc = wave * 32 + 8 * q + 4 * gh;
-      const uint32_t lo = pack_bf16(acc[4 * q], acc[4 * q + 1]);
-      const uint32_t hi = pack_bf16(acc[4 * q + 2], acc[4 * q + 3]);
+    // four consecutive outputs oc .. oc+3 of one token
+    auto put4 = [&](uint32_t* orow, int oc, float v0, float v1, float v2, float v3) {
+      const uint32_t lo = pack_bf16(v0, v1);
+      const uint32_t hi = pack_bf16(v2, v3);
       if (pair8 && oc + 2 < C) {
         *reinterpret_cast<u32x2_t*>(orow + (oc >> 1)) = (u32x2_t){lo, hi};
       } else {
         if (oc < C) orow[oc >> 1] = lo;
         if (oc + 2 < C) orow[(oc >> 1) + 1] = hi;
       }
+    };
+    if constexpr (SPLIT) {
+      uint32_t* orow = ot + (16 * th + l16) * CP;
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        put4(orow, 16 * (3 * g4 + j) + 4 * kg, acc.a[j][0], acc.a[j][1], acc.a[j][2], acc.a[j][3]);
+    } else {
+      uint32_t* orow = ot + l32 * CP;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        put4(orow, wave * 32 + 8 * q + 4 * gh, acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
     }
   };
   // an output tile's tokens are one contiguous span of G: 16-byte stores
@@ -377,7 +421,7 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
     const uint32_t* up = GATE_RING((K + 3) & 3);
     const uint32_t* mid = GATE_RING(K);
     const uint32_t* dn = GATE_RING((K + 1) & 3);
-    f32x16_t acc;
+    Acc acc;
     if (prev && has_block) {  // wave-uniform
       work(std::true_type{}, up, mid, dn, dtw, dtr, acc);
       put(acc, otw);
@@ -432,7 +476,7 @@ cla_gate_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ d
     __syncthreads();
     if (n >= 2) store((n & 1) ? ot0 : ot1, b, yend - 2, x0);
     if (has_block) {
-      f32x16_t acc;
+      Acc acc;
       pointwise((n & 1) ? dt1 : dt0, acc);
       put(acc, (n & 1) ? ot1 : ot0);
     }
