@@ -4,19 +4,22 @@
 // encoding layer and implicit neural field; gist.science summaries, part A,
 // mechanism steps 1-2).
 //
-// One workgroup handles TOK in-window positions in three phases that meet in
-// LDS: Fourier features (2+4L per position), the ReLU hidden layer (hidden per
-// position), then the two rank heads.  The whole job is at most a few tens of
-// MFLOP per window size and runs once per size, so it is written for clarity
-// and exact fp32 semantics (correctly rounded coordinate division, precise
-// sinf/cosf), not for speed.
+// One workgroup handles ENC_TOK in-window positions in three phases that meet
+// in LDS: Fourier features (2+4L per position), the ReLU hidden layer (hidden
+// per position), then the two rank heads.  The whole job is at most a few tens
+// of MFLOP per window size and runs once per size.  It keeps exact fp32
+// semantics (correctly rounded coordinate division, precise sinf/cosf, one FMA
+// chain per output in input order).  Each thread's dense-layer work is a serial
+// chain of LDS reads and FMAs, so the time is latency: small workgroups (8
+// positions; 1152 of them for a 96x96 window) put several on each CU to hide
+// it, and the weights are staged in LDS once per workgroup when they fit.
 #include "rib_device.hpp"
 #include "rib_bwd.hpp"
 #include "rib_launch.hpp"
 
 namespace rib {
 
-constexpr int ENC_TOK = 32;
+constexpr int ENC_TOK = 8;
 constexpr int ENC_THREADS = 256;
 
 // Fourier features of TOK consecutive positions starting at n0 (clamped to N-1):
@@ -74,9 +77,14 @@ static __device__ void fourier_features3(int n0, int N, int wt, int ws, int L, i
   }
 }
 
-// wt = 0: image windows (2 coordinates); wt >= 1: space-time windows of wt frames
+// wt = 0: image windows (2 coordinates); wt >= 1: space-time windows of wt frames.
+// kLdsW: the weights are first copied to LDS, so the two dense layers read
+// their operands from LDS instead of waiting on a global load per FMA.  Every
+// output keeps the same FMA order either way, so both variants give the same
+// bits.
+template <bool kLdsW>
 __global__ void __launch_bounds__(ENC_THREADS)
-encode_kernel(int wt, int ws, int L, int hidden, int R, const float* __restrict__ w,
+encode_kernel(int wt, int ws, int L, int hidden, int R, const float* __restrict__ wg,
               float* __restrict__ qp, float* __restrict__ kp) {
   extern __shared__ float sm[];
   const int F = wt ? 3 + 6 * L : 2 + 4 * L;
@@ -84,6 +92,14 @@ encode_kernel(int wt, int ws, int L, int hidden, int R, const float* __restrict_
   float* hid = sm + ENC_TOK * F;        // [ENC_TOK][hidden]
   const int N = (wt ? wt : 1) * ws * ws;
   const int n0 = blockIdx.x * ENC_TOK;
+
+  const float* w = wg;
+  if constexpr (kLdsW) {
+    float* sw = hid + ENC_TOK * hidden;  // [F*hidden + hidden + 2*hidden*R]
+    const int nw = F * hidden + hidden + 2 * hidden * R;
+    for (int i = threadIdx.x; i < nw; i += ENC_THREADS) sw[i] = wg[i];
+    w = sw;
+  }
 
   if (wt) fourier_features3(n0, N, wt, ws, L, ENC_TOK, F, feat);
   else fourier_features(n0, N, ws, L, ENC_TOK, F, feat);
@@ -118,24 +134,34 @@ encode_kernel(int wt, int ws, int L, int hidden, int R, const float* __restrict_
   }
 }
 
+// Weights at most this many bytes go through LDS (the headline encoder, L = 10,
+// hidden 64, R = 16, holds 18.7 KB).
+constexpr size_t ENC_LDS_W_MAX = 48 * 1024;
+
+static hipError_t launch_encode_any(int wt, int ws, int L, int hidden, int R, const float* w, float* qp, float* kp,
+                                    hipStream_t stream) {
+  const int N = (wt ? wt : 1) * ws * ws;
+  const int F = wt ? 3 + 6 * L : 2 + 4 * L;
+  const int blocks = (N + ENC_TOK - 1) / ENC_TOK;
+  const size_t lds = sizeof(float) * ENC_TOK * (size_t)(F + hidden);
+  const size_t wbytes = sizeof(float) * ((size_t)F * hidden + hidden + 2 * (size_t)hidden * R);
+  if (wbytes <= ENC_LDS_W_MAX)
+    hipLaunchKernelGGL(encode_kernel<true>, dim3(blocks), dim3(ENC_THREADS), lds + wbytes, stream, wt, ws, L, hidden,
+                       R, w, qp, kp);
+  else
+    hipLaunchKernelGGL(encode_kernel<false>, dim3(blocks), dim3(ENC_THREADS), lds, stream, wt, ws, L, hidden, R, w,
+                       qp, kp);
+  return hipGetLastError();
+}
+
 hipError_t launch_encode(int ws, int L, int hidden, int R, const float* w, float* qp, float* kp,
                          hipStream_t stream) {
-  const int N = ws * ws;
-  const int blocks = (N + ENC_TOK - 1) / ENC_TOK;
-  const size_t lds = sizeof(float) * ENC_TOK * (size_t)(2 + 4 * L + hidden);
-  hipLaunchKernelGGL(encode_kernel, dim3(blocks), dim3(ENC_THREADS), lds, stream, 0, ws, L, hidden, R,
-                     w, qp, kp);
-  return hipGetLastError();
+  return launch_encode_any(0, ws, L, hidden, R, w, qp, kp, stream);
 }
 
 hipError_t launch_encode3d(int wt, int ws, int L, int hidden, int R, const float* w, float* qp, float* kp,
                            hipStream_t stream) {
-  const int N = wt * ws * ws;
-  const int blocks = (N + ENC_TOK - 1) / ENC_TOK;
-  const size_t lds = sizeof(float) * ENC_TOK * (size_t)(3 + 6 * L + hidden);
-  hipLaunchKernelGGL(encode_kernel, dim3(blocks), dim3(ENC_THREADS), lds, stream, wt, ws, L, hidden, R,
-                     w, qp, kp);
-  return hipGetLastError();
+  return launch_encode_any(wt, ws, L, hidden, R, w, qp, kp, stream);
 }
 
 // Backward of the encoder (explainer section 2.2, the same three layers): for
