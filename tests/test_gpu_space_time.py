@@ -63,6 +63,20 @@ def test_encode3d_matches_oracle(torch, wt, ws, L):
         assert err <= 1e-5
 
 
+
+@pytest.mark.parametrize("wt,ws,L,hidden,R", [(2, 5, 16, 256, 64), (3, 4, 0, 1, 1)])
+def test_encode3d_other_widths(torch, wt, ws, L, hidden, R):
+    """The widest layers (weights too large to stage in LDS) and the narrowest."""
+    note(f"encode3d wt={wt} ws={ws} L={L} hidden={hidden} R={R}")
+    w = weights3d(L, hidden, R, 7)
+    qp, kp = rib.encode3d(wt, ws, L, hidden, R, torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    oq, ok = oracle.encode3d(wt, ws, L, hidden, R, w)
+    for got, want in ((qp, oq), (kp, ok)):
+        err = float(np.abs(got.cpu().numpy() - want).max())
+        note(f"  max|err| {err:.3g}")
+        assert err <= 1e-5
+
 CASES = [
     # (B, T, H, W, heads, dh, wt, ws, dtype)
     (1, 5, 9, 7, 2, 30, 2, 4, "bf16"),      # small kernel (32 tokens), ragged on every axis
