@@ -351,6 +351,28 @@ def time_backward(torch, rib, synthetic, cfg_idx, ws, reps):
                          "kernel": "rib_window_attn_backward (prep, two packs, dq, dkv, table reduce)"}}
 
 
+def copy_calibration(torch):
+    """Three plain device copies of 2^28 float32 (1 GiB read, 1 GiB written): the reference that
+    scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    return {"read": x.numel() * 4, "write": y.numel() * 4}
+
+
+# forward workloads that --only times alone: (label, config index, window, rotating input sets)
+ONLY = {
+    "sst-train-96": ("96x96 window, 32x96x96, C=180", 4, 96, 1),
+    "sst-infer-64": ("64x64 window, 1x180x320, C=180", 3, 64, 1),
+    "large-96": ("96x96 window, 1x360x640 (640x360 input), C=180", 5, 96, 1),
+    "sst-lite-16": ("16x16 window, 1x180x320, C=48 (40 rotating input sets)", 2, 16, 40),
+    "sst-lite-32": ("32x32 window, 1x180x320, C=48", 2, 32, 1),
+    "sst-lite-64": ("64x64 window, 1x180x320, C=48", 2, 64, 1),
+}
+
+
 def cpu_baseline(synthetic, cfg_idx, ws, units_sample):
     """The fp64 oracle as it stands, on the host cores, over a bounded sample of
     (image, window, head) units of the same workload, scaled to tokens/s."""
@@ -388,6 +410,8 @@ def main():
     ap.add_argument("--backward-only", action="store_true",
                     help="time only the training iteration (train forward + backward) on the 96x96 workload")
     ap.add_argument("--backward-reps", type=int, default=10, help="timed repetitions per backward call")
+    ap.add_argument("--only", choices=sorted(ONLY), default=None,
+                    help="time one forward workload alone and print its line (for profiler passes)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -402,6 +426,20 @@ def main():
     from super_resolution_transformer_amd import synthetic
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rib.lib()
+
+    if args.only:
+        name, cfg_idx, ws, copies = ONLY[args.only]
+        wl = Workload(torch, rib, synthetic, cfg_idx, ws, copies=copies)
+        wl.encode()
+        ms = time_attn_only(torch, wl, reps=args.steps, warmup=args.warmup)
+        tf = wl.F / (ms * 1e-3) / 1e12
+        out = {"only": name, "ms_attn": ms, "tokens_per_s": wl.tokens / (ms * 1e-3), "tflops": tf,
+               "pct_bf16_peak": 100 * tf / PEAK_BF16_TFLOPS, "alg_bytes": wl.M,
+               "alg_gbs": wl.M / (ms * 1e-3) / 1e9, "pct_hbm": 100 * wl.M / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        if args.copy_calibration:
+            out["copy_calibration_bytes"] = copy_calibration(torch)
+        print(json.dumps(out), flush=True)
+        return
 
     if args.backward_only:
         print(json.dumps({"backward": {"96x96 window, 32x96x96": time_backward(torch, rib, synthetic, 4, 96,
@@ -448,6 +486,7 @@ def main():
         for name, cfg_idx, ws, copies in (("64x64 window, 1x180x320, C=180", 3, 64, 1),
                                           ("96x96 window, 1x360x640 (640x360 input), C=180", 5, 96, 1),
                                           ("32x32 window, 1x180x320, C=48", 2, 32, 1),
+                                          ("64x64 window, 1x180x320, C=48", 2, 64, 1),
                                           ("16x16 window, 1x180x320, C=48 (HBM-bound; 40 rotating input sets)",
                                            2, 16, 40)):
             w2 = Workload(torch, rib, synthetic, cfg_idx, ws, copies=copies)
@@ -473,13 +512,7 @@ def main():
         torch.cuda.empty_cache()
 
     if args.copy_calibration:
-        x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        y = torch.empty_like(x)
-        for _ in range(3):
-            y.copy_(x)
-        torch.cuda.synchronize()
-        out["copy_calibration_bytes"] = {"read": x.numel() * 4, "write": y.numel() * 4}
-        del x, y
+        out["copy_calibration_bytes"] = copy_calibration(torch)
 
     if not args.no_cpu:
         import oracle

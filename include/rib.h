@@ -13,7 +13,8 @@
  *   - All pointers are device pointers (memory from hipMalloc or a framework
  *     allocator on the current device) unless stated otherwise.  The caller
  *     owns every buffer; the library allocates no device or host memory and
- *     keeps no state apart from a thread-local error message.
+ *     keeps no state apart from a thread-local error message (the number of
+ *     compute units, which sizes some grids, is queried on every call).
  *   - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t
  *     passed as void*, NULL = the null stream) and the call returns.  RIB_OK
  *     means "validated and enqueued"; a fault inside a kernel surfaces at the
@@ -96,7 +97,8 @@ rib_status rib_encode(int window, int L, int hidden, int R, const float* weights
  *                RIB_F32: dh <= 64, R <= 64;
  *                RIB_BF16: (dh, R) in {(8,8), (16,16), (30,16), (32,16),
  *                (16,32), (30,32)} (others return RIB_ERR_UNSUPPORTED).
- *                Base pointers must be 16-byte aligned.
+ *                qc, kc, v, g, o 4-byte aligned (dword accesses); qp, kp
+ *                8-byte aligned (float pairs).
  */
 rib_status rib_window_attn(const void* qc, const void* kc, const void* v, const void* g,
                            const float* qp, const float* kp, void* o, int B, int H, int W,
@@ -184,9 +186,11 @@ rib_status rib_attn_supported(int dh, int R, int window, rib_dtype dtype);
  *          weights.
  * dw_w   : device, float32 [C][3][3]; dw_b: device, float32 [C].
  * pw_w   : device, float32 [C][C], row = input channel (y = x W); pw_b: [C].
- * dtype  : RIB_F32 -- fp32 throughout; RIB_BF16 -- bf16 maps, the depth-wise
- *          stencil in fp32 rounded to bf16, the point-wise product on bf16
- *          matrix cores (weights rounded to bf16) with fp32 accumulation.
+ * dtype  : RIB_F32 -- fp32 throughout; RIB_BF16 -- bf16 maps; the depth-wise
+ *          stencil on bf16 dot products (taps rounded to bf16, exact products,
+ *          fp32 sums starting from the fp32 bias), D rounded to bf16; the
+ *          point-wise product on bf16 matrix cores (weights rounded to bf16)
+ *          with fp32 accumulation from the bias; G rounded to bf16.
  * Limits : C even, 2 <= C <= 256; B*H*W*C < 2^31; pointers 4-byte aligned.
  */
 rib_status rib_cla_gate(const void* x, const float* dw_w, const float* dw_b, const float* pw_w,

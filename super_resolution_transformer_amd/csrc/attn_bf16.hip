@@ -67,6 +67,7 @@ constexpr int QW = 64;             // queries per wave (two 32-query MFMA blocks
 constexpr int QB = QW * NWAVE;     // queries per workgroup
 constexpr int NSTAGE = 3;          // LDS stages of the key-tile pipeline
 constexpr float OFF = 7.0f;        // p = exp2(s - m_hat - OFF) <= 2^-OFF normally
+constexpr float OFF_FAST = 64.0f;  // offset of the whole-window kernel's unchecked first pass
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
@@ -431,7 +432,7 @@ __device__ __forceinline__ uint32_t exp_tile_fast(const f32x16_t (&Sacc)[NQ][2],
 // (unless this is the first tile) and the new -m_hat in the Q~ operand.
 template <int DH, int R, int NQ>
 __device__ __forceinline__ void rescale_tile(Regs<DH, R, NQ>& rg, const f32x16_t (&Sacc)[NQ][2],
-                                             uint32_t (&P)[NQ][2][8], bool first, int gh) {
+                                             uint32_t (&P)[NQ][2][8], bool first, int gh, float off = OFF) {
   using S = Shape<DH, R>;
   float shift[NQ];
 #pragma unroll
@@ -443,8 +444,8 @@ __device__ __forceinline__ void rescale_tile(Regs<DH, R, NQ>& rg, const f32x16_t
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, Sacc[qb][kb][e]);
     const LanePair pr = lane_pair(mx);
     mx = fmaxf(pr.lo, pr.hi);
-    const bool grow = first || (mx + OFF > 0.0f);
-    const float mnew = grow ? round_bf16(rg.mhat[qb] + mx + OFF) : rg.mhat[qb];
+    const bool grow = first || (mx + off > 0.0f);
+    const float mnew = grow ? round_bf16(rg.mhat[qb] + mx + off) : rg.mhat[qb];
     shift[qb] = mnew - rg.mhat[qb];
     rg.mhat[qb] = mnew;
     if (!first) {
@@ -455,7 +456,7 @@ __device__ __forceinline__ void rescale_tile(Regs<DH, R, NQ>& rg, const f32x16_t
         for (int e = 0; e < 16; ++e) rg.O[qb][dt][e] *= sc;
       if constexpr (!S::ONES) rg.lpart[qb] *= sc;
     }
-    const uint32_t cd = pack_bf16(-mnew, -OFF);
+    const uint32_t cd = pack_bf16(-mnew, -off);
     if (gh == S::GM) rg.qt[qb][S::CM][S::DM] = cd;
   }
   exp_tile(Sacc, P, shift);
@@ -775,7 +776,7 @@ constexpr int SQ = 256;        // queries (and keys) per workgroup
 constexpr int SNT = SQ / KT;   // key tiles, all resident
 
 // dword w of a Q~ row: [Qp/sqrt(R), Qc/sqrt(dh)] (log2 e folded in), the
-// (-m_hat = 0, -OFF) pair, zeros
+// (-m_hat = 0, -OFF_FAST) pair, zeros
 template <int DH, int R>
 __device__ __forceinline__ uint32_t qrow_word(int w, int off, int n, bool real, const float* __restrict__ qp,
                                               const uint32_t* __restrict__ qc, float sp, float sc) {
@@ -788,7 +789,7 @@ __device__ __forceinline__ uint32_t qrow_word(int w, int off, int n, bool real, 
     const uint32_t x = qc[(off >> 1) + (w - R / 2)];
     val = pack_bf16(bf16_lo(x) * sc, bf16_hi(x) * sc);
   } else if (w == S::CONSTDW) {
-    val = 0xC0E00000u;  // (-m_hat = 0, -OFF = -7)
+    val = 0xC2800000u;  // (-m_hat = 0, -OFF_FAST = -64)
   }
   return (real || w == S::CONSTDW) ? val : 0u;
 }
@@ -898,14 +899,53 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
     PhaseOps<DH, R> ops;
     f32x16_t Sacc[1][2];
     uint32_t P[1][2][8];
+    // First pass: the exact row maximum of the first key tile, then the other tiles
+    // exponentiated against it without a check, with the offset OFF_FAST = 64: p =
+    // 2^(s - m_hat - 64).  That is exact (up to rounding) unless a score exceeds m_hat by
+    // more than 64 + 106 (below that, p and the fp32 sums over at most 256 keys with
+    // |V| < 2^14 stay finite); keys more than 62 below m_hat, itself at most the row
+    // maximum, may flush to zero, and each weighs less than 2^-62 of the row.  A block whose
+    // row sum or output ends
+    // non-finite repeats its tiles with the checked loop: offset OFF, an OR over the packed
+    // P of every tile, and a rescale whenever a score exceeds the reference by more than 8.
     for (int x = 0; x < ntiles; ++x) {
       read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
       read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
       qk_tile<DH, R>(ops, rg, Sacc);
-      const uint32_t orv = exp_tile_fast(Sacc, P);
-      const bool first = x == 0;
-      if (__builtin_amdgcn_ballot_w64(first || (orv & 0x40004000u))) rescale_tile<DH, R>(rg, Sacc, P, first, gh);
+      if (x == 0)
+        rescale_tile<DH, R>(rg, Sacc, P, true, gh, OFF_FAST);
+      else
+        (void)exp_tile_fast(Sacc, P);
       pv_tile<DH, R>(ops, rg, P);
+    }
+    float off_used = OFF_FAST;
+    {
+      float t = row_sum(rg, 0);
+      int bad = !(t > 0.0f);
+#pragma unroll
+      for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) t += rg.O[0][dt][e];
+      bad |= !__builtin_isfinite(t);
+      if (__builtin_amdgcn_ballot_w64(bad)) {
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) rg.O[0][dt][e] = 0.0f;
+        rg.mhat[0] = 0.0f;
+        rg.lpart[0] = 0.0f;
+        if (gh == S::GM) rg.qt[0][S::CM][S::DM] = 0xC0E00000u;  // (-m_hat = 0, -OFF = -7)
+        for (int x = 0; x < ntiles; ++x) {
+          read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
+          read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
+          qk_tile<DH, R>(ops, rg, Sacc);
+          const uint32_t orv = exp_tile_fast(Sacc, P);
+          const bool first = x == 0;
+          if (__builtin_amdgcn_ballot_w64(first || (orv & 0x40004000u))) rescale_tile<DH, R>(rg, Sacc, P, first, gh);
+          pv_tile<DH, R>(ops, rg, P);
+        }
+        off_used = OFF;
+      }
     }
 
     // ---- epilogue of the block: O / l * sigmoid(G), bf16, NHWC
@@ -913,7 +953,7 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
     const float lsum = row_sum(rg, 0);
     if (r < G.n_real) {
       const float inv = 1.0f / lsum;
-      if (lse) lse[(offq - G.h * DH) / G.C * heads + G.h] = (rg.mhat[0] + OFF + __log2f(lsum)) * LN2;
+      if (lse) lse[(offq - G.h * DH) / G.C * heads + G.h] = (rg.mhat[0] + off_used + __log2f(lsum)) * LN2;
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
@@ -947,6 +987,17 @@ __device__ __forceinline__ int interleave_logical(int bid, int qblocks) {
   return ((bid / per) * 8 + bid % 8) * qblocks + (bid % per) / 8;
 }
 
+// Workgroup -> window unit for the whole-window kernel, on a grid of 8 * ceil(windows / 8) *
+// heads workgroups.  The heads of a window take consecutive workgroups of one XCD (the
+// dispatcher sends workgroup i to XCD i % 8), so the token rows they share (a row holds every
+// head's slice) are fetched once into that XCD's L2; windows are dealt round-robin over the
+// XCDs, so the smaller edge windows spread evenly.  Units past the last are padding.
+__device__ __forceinline__ int window_unit(int bid, int heads) {
+  const int xcd = bid & 7, slot = bid >> 3;  // slot-th workgroup this XCD receives
+  const int k = slot / heads;
+  return (k * 8 + xcd) * heads + (slot - k * heads);
+}
+
 template <int DH, int R>
 __global__ void __launch_bounds__(QB, 1)
 attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
@@ -966,7 +1017,7 @@ attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
                        uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws,
                        int total, long tstride, float* __restrict__ lse) {
   attn_small_body<DH, R>(qc, kc, v, g, qp, kp, o, B, T, H, W, heads, wt, ws, total, tstride, lse,
-                         interleave_logical(blockIdx.x, 1));
+                         window_unit(blockIdx.x, heads));
 }
 
 // ---- several independent calls in one launch ---------------------------------
@@ -1023,7 +1074,7 @@ __global__ void __launch_bounds__(SQ, 3) attn_bf16_small_group_kernel(const Call
   CallDesc c;
   const int lb = group_call(grp, blockIdx.x, c);
   attn_small_body<DH, R>(c.qc, c.kc, c.v, c.g, c.qp, c.kp, c.o, c.B, c.T, c.H, c.W, c.heads, c.wt, c.ws,
-                         c.units, c.tstride, c.lse, interleave_logical(lb, 1));
+                         c.units, c.tstride, c.lse, window_unit(lb, c.heads));
 }
 
 template <int DH, int R>
@@ -1031,8 +1082,9 @@ hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
   const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws, nWt = (a.T + a.wt - 1) / a.wt;
   const int NW = a.wt * a.ws * a.ws;
   if (NW <= SQ) {
-    const int total = a.B * nWt * nWy * nWx * a.heads;
-    const int grid = 8 * ((total + 7) / 8);  // interleave_logical with one query block
+    const int windows = a.B * nWt * nWy * nWx;
+    const int total = windows * a.heads;
+    const int grid = 8 * ((windows + 7) / 8) * a.heads;  // see window_unit
     hipLaunchKernelGGL((attn_bf16_small_kernel<DH, R>), dim3(grid), dim3(SQ), 0, stream,
                        (const uint32_t*)a.qc, (const uint32_t*)a.kc, (const uint32_t*)a.v,
                        (const uint32_t*)a.g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt,
@@ -1079,7 +1131,8 @@ hipError_t launch_group(const AttnArgs* const* calls, int n, bool small, hipStre
     c.units = call_units(a);
     c.qblocks = small ? 1 : call_qblocks(a);
     grp.first[i] = first;
-    first += 8 * ((c.units + 7) / 8) * c.qblocks;
+    first += small ? 8 * ((c.units / c.heads + 7) / 8) * c.heads  // see window_unit
+                   : 8 * ((c.units + 7) / 8) * c.qblocks;         // see interleave_logical
   }
   grp.first[n] = first;
   if (small)

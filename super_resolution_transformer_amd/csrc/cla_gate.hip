@@ -502,15 +502,11 @@ hipError_t launch_gate_bf16(const GateArgs& a, int nseg, long ntiles, int grid, 
 }  // namespace
 
 int device_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
-  }
-  return cus;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      n > 0)
+    return n;
+  return 256;
 }
 
 hipError_t launch_cla_gate(const GateArgs& a, bool bf16, hipStream_t stream) {

@@ -108,9 +108,13 @@ rib_status check_attn(const char* fn, bool per_head, const void* qc, const void*
   const uint64_t elems = (uint64_t)B * T * H * W * (uint64_t)heads * dh;
   if (elems >= (1ull << 31))
     return fail(RIB_ERR_UNSUPPORTED, "%s: B*T*H*W*heads*dh must be < 2^31", fn);
-  if (!aligned(qc, 16) || !aligned(kc, 16) || !aligned(v, 16) || !aligned(g, 16) || !aligned(qp, 16) ||
-      !aligned(kp, 16) || !aligned(o, 16))
-    return fail(RIB_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+  // maps: the kernels read and write them in dwords (head slices of bf16 maps start on any
+  // dword: 60 bytes apart for 30-channel heads), and their buffer loads need only dword
+  // alignment; tables: the query side reads float pairs
+  if (!aligned(qc, 4) || !aligned(kc, 4) || !aligned(v, 4) || !aligned(g, 4) || !aligned(o, 4))
+    return fail(RIB_ERR_INVALID_ARG, "%s: map pointers must be 4-byte aligned", fn);
+  if (!aligned(qp, 8) || !aligned(kp, 8))
+    return fail(RIB_ERR_INVALID_ARG, "%s: qp and kp must be 8-byte aligned", fn);
   const size_t nb = (size_t)elems * (dtype == RIB_F32 ? 4 : 2);
   const size_t np = sizeof(float) * (size_t)wt * window * window * R * (per_head ? heads : 1);
   if (overlap(o, nb, qc, nb) || overlap(o, nb, kc, nb) || overlap(o, nb, v, nb) || overlap(o, nb, g, nb) ||

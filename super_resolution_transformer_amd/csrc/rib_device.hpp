@@ -47,18 +47,6 @@ __device__ __forceinline__ uint32_t lane_xor1(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
 }
 
-// Workgroup barrier that orders LDS only.  __syncthreads() also releases global memory,
-// which makes every wave wait for its buffer loads into LDS (and its stores) first; kernels
-// that keep the next tile's loads in flight across the barriers of the current tile use
-// this one.  (s_waitcnt lgkmcnt(0) with the other counters at their maximum is 0xC07F on
-// gfx9; the signal fences keep the compiler from moving memory accesses across it.)
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 __device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
 // Map workgroup i of a launch of 8*per workgroups so that consecutive logical

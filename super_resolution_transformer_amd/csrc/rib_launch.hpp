@@ -48,7 +48,7 @@ struct GateArgs {
 // CLA gate producer; bf16 = false: fp32 maps.  C even, C <= 256.
 hipError_t launch_cla_gate(const GateArgs& a, bool bf16, hipStream_t stream);
 
-// compute units of the device current at the first call (cached)
+// compute units of the current device (queried on every call)
 int device_cus();
 
 struct LnQkvArgs {

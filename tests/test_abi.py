@@ -87,9 +87,12 @@ def test_attn_validation(L):
     assert attn(L, window=200) == rib.RIB_ERR_UNSUPPORTED
     assert attn(L, B=1 << 12, H=1 << 10, W=1 << 10) == rib.RIB_ERR_UNSUPPORTED   # >= 2^31 elements
     assert "2^31" in L.rib_last_error().decode()
-    mis = [ctypes.c_void_p(P[0].value + 4)] + P[1:7]
+    mis = [ctypes.c_void_p(P[0].value + 2)] + P[1:7]                     # maps: dword alignment
     assert attn(L, mis) == rib.RIB_ERR_INVALID_ARG
     assert "aligned" in L.rib_last_error().decode()
+    mis_tab = P[:4] + [ctypes.c_void_p(P[4].value + 4)] + P[5:7]           # tables: float pairs
+    assert attn(L, mis_tab) == rib.RIB_ERR_INVALID_ARG
+    assert "8-byte" in L.rib_last_error().decode()
     alias = P[:6] + [ctypes.c_void_p(P[2].value + 256)]                     # o inside v
     assert attn(L, alias) == rib.RIB_ERR_INVALID_ARG
     assert "overlap" in L.rib_last_error().decode()
