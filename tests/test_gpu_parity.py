@@ -2,10 +2,9 @@
 
 Tolerances: max abs error <= 1e-5 for fp32 inputs, <= 2e-2 for bf16 inputs
 with fp32 accumulation; window/index mapping (locality, equivariance, one-hot
-index pins) bit-exact.  Small problems are compared element by element over the
-whole output; the full-size workloads (in the launch configuration the
-benchmark times) are compared at sampled query tokens, which the oracle
-computes row by row.
+index pins) bit-exact.  Every comparison is element by element over the whole
+output: small problems, and the full-size workloads in the launch configuration
+the benchmark times.
 """
 import math
 import sys
@@ -131,35 +130,21 @@ def test_sst_lite_cyclic_windows_whole_16(torch):
     compare(got, want, "bf16", "sst-lite ws16")
 
 
-# ---------------------------------------------------------------- full-size workloads, sampled rows
-def sample_tokens(B, H, W, ws, n, seed):
-    """Sampled query tokens: window corners and edges of every window type, plus random ones."""
-    rng = np.random.default_rng(seed)
-    toks = set()
-    nWy, nWx = -(-H // ws), -(-W // ws)
-    for wy in {0, nWy // 2, nWy - 1}:
-        for wx in {0, nWx // 2, nWx - 1}:
-            y0, x0 = wy * ws, wx * ws
-            y1, x1 = min(H, y0 + ws) - 1, min(W, x0 + ws) - 1
-            for (y, x) in [(y0, x0), (y0, x1), (y1, x0), (y1, x1), ((y0 + y1) // 2, (x0 + x1) // 2)]:
-                toks.add((int(rng.integers(B)), y, x))
-    while len(toks) < n:
-        toks.add((int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(W))))
-    t = np.array(sorted(toks))
-    return t[:, 0], t[:, 1], t[:, 2]
-
-
-@pytest.mark.parametrize("cfg,ws", [(2, 32), (2, 64), (3, 64), (4, 96), (5, 96)])
-def test_full_size_workload_sampled(torch, cfg, ws):
+# ---------------------------------------------------------------- full-size workloads, whole outputs
+@pytest.mark.parametrize("cfg,ws", [(2, 32), (2, 64), (3, 64), (5, 96), (4, 96)])
+def test_full_size_workload_whole(torch, cfg, ws):
+    """Every output of the full-size workloads, in the launch configuration the benchmark times
+    (the 180x320 maps at 32x32 and 64x64 windows, C = 48 and 180; the 640x360 input and the
+    32 x 96x96 training batch at 96x96 windows), against the threaded fp64 oracle: every image,
+    window, head and query block, edge windows included.  The oracle takes about a minute for
+    the 32 x 96x96 batch on 16 cores."""
     p = synthetic.config_problem(cfg)
-    note(f"workload {synthetic.CONFIGS[cfg].name} ws={ws}: B={p.B} H={p.H} W={p.W} C={p.C}")
+    note(f"workload {synthetic.CONFIGS[cfg].name} ws={ws}: B={p.B} H={p.H} W={p.W} C={p.C} (whole output)")
     got, _, _ = gpu_run(torch, p, ws)
-    tb, ty, tx = sample_tokens(p.B, p.H, p.W, ws, 384, seed=cfg)
-    oq, ok = oracle.encode(ws, p.L, p.hidden, p.R, p.weights)
-    want = oracle.window_attn_rows(p.qc, p.kc, p.v, p.g, oq, ok, p.heads, ws, tb, ty, tx)
-    compare(got[tb, ty, tx], want, p.dtype, f"{len(tb)} sampled rows")
-    # property at every position: |O| <= max|V| * sigmoid(G) elementwise (convex combination)
     assert np.all(np.isfinite(got))
+    oq, ok = oracle.encode(ws, p.L, p.hidden, p.R, p.weights)
+    want = oracle.window_attn(p.qc, p.kc, p.v, p.g, oq, ok, p.heads, ws)
+    compare(got, want, p.dtype, f"{got.size} outputs")
 
 
 # ---------------------------------------------------------------- bit-exact index pins
