@@ -13,8 +13,10 @@
  *   - All pointers are device pointers (memory from hipMalloc or a framework
  *     allocator on the current device) unless stated otherwise.  The caller
  *     owns every buffer; the library allocates no device or host memory and
- *     keeps no state apart from a thread-local error message (the number of
- *     compute units, which sizes some grids, is queried on every call).
+ *     keeps no state apart from a thread-local error message and the fixed
+ *     per-device array of rib_encode_backward_noalloc (with its looked-up
+ *     address per device); the number of compute units, which sizes some
+ *     grids, is queried on every call.
  *   - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t
  *     passed as void*, NULL = the null stream) and the call returns.  RIB_OK
  *     means "validated and enqueued"; a fault inside a kernel surfaces at the
@@ -274,6 +276,28 @@ rib_status rib_encode_backward(int window, int L, int hidden, int R, const float
                                void* stream);
 
 /*
+ * rib_encode_backward_noalloc -- rib_encode_backward for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving or
+ * training loops, harnesses that forbid hipMalloc.  Same arguments, layouts,
+ * limits and errors as rib_encode_backward, without the workspace: the
+ * partial gradients go to a fixed 4 MiB array that the library holds on each
+ * device it runs on until the process ends.  It calls no hipMalloc, hipFree
+ * or allocating library routine; the first call on a device looks up that
+ * device's array once.  The workspace holds min(ceil(window^2 / 16),
+ * 2^20 / weights) partial rows, so every size rib_encode_backward takes fits
+ * (at most 49,920 weights); a weight count beyond 2^20 floats would be
+ * refused with RIB_ERR_UNSUPPORTED.  When the row count equals
+ * ceil(window^2 / 16) (window <= 59 for the 4,800-weight encoder) the result
+ * is bit-identical to rib_encode_backward's; otherwise a workgroup sums
+ * several 16-position chunks and the summation order differs.  Calls on one
+ * device share the array: two calls whose executions overlap on one device
+ * (different streams, or host threads without ordering) race and give wrong
+ * gradients; calls ordered on one stream are safe.
+ */
+rib_status rib_encode_backward_noalloc(int window, int L, int hidden, int R, const float* weights,
+                                       const float* dqp, const float* dkp, float* dweights, void* stream);
+
+/*
  * rib_ln_qkv -- the attention's input projection in an SST block (explainer
  * section 3.1: each block runs LayerNorm, then the RIB attention), per token:
  *   mu = mean_c x_c,  var = mean_c (x_c - mu)^2         (biased variance)
@@ -328,7 +352,7 @@ const char* rib_last_error(void);
 /* ABI version of this header (incremented on any incompatible change). */
 int rib_abi_version(void);
 
-#define RIB_ABI_VERSION 9
+#define RIB_ABI_VERSION 10
 
 #ifdef __cplusplus
 }

@@ -81,6 +81,8 @@ def lib(path: str | None = None):
     L.rib_encode_backward_workspace.restype = sz
     L.rib_encode_backward.argtypes = [i] * 4 + [vp] * 5 + [sz, vp]
     L.rib_encode_backward.restype = i
+    L.rib_encode_backward_noalloc.argtypes = [i] * 4 + [vp] * 5
+    L.rib_encode_backward_noalloc.restype = i
     L.rib_ln_qkv.argtypes = [vp] * 9 + [i] * 4 + [ctypes.c_float, i, vp]
     L.rib_ln_qkv.restype = i
     L.rib_encode3d.argtypes = [i] * 5 + [vp] * 4
@@ -355,6 +357,21 @@ def encode_backward_into(window: int, L: int, hidden: int, R: int, weights, dqp,
         raise ValueError("work must be a contiguous GPU buffer")
     _check(lib().rib_encode_backward(window, L, hidden, R, _ptr(weights), _ptr(dqp), _ptr(dkp), _ptr(dw),
                                      _ptr(work), work.numel() * work.element_size(), _stream(weights)))
+
+
+def encode_backward_noalloc_into(window: int, L: int, hidden: int, R: int, weights, dqp, dkp, dw) -> None:
+    """encode_backward_into without a workspace argument: the library's fixed per-device array
+    takes the partial gradients (no device allocation; calls that overlap on one device race)."""
+    import torch
+    ts = (weights, dqp, dkp, dw)
+    if not all(t.is_cuda and t.is_contiguous() and t.dtype == torch.float32 for t in ts):
+        raise ValueError("weights, dqp, dkp, dw must be contiguous float32 GPU tensors")
+    if weights.numel() != weight_count(L, hidden, R) or dw.numel() != weights.numel():
+        raise ValueError("packed weight vector has the wrong length")
+    if dqp.shape != (window * window, R) or dkp.shape != (window * window, R):
+        raise ValueError("dqp, dkp must be [window*window, R]")
+    _check(lib().rib_encode_backward_noalloc(window, L, hidden, R, _ptr(weights), _ptr(dqp), _ptr(dkp), _ptr(dw),
+                                             _stream(weights)))
 
 
 def ln_qkv(x, gamma, beta, w, bias, eps: float = 1e-5, with_xn: bool = False):

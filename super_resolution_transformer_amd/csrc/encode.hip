@@ -17,6 +17,8 @@
 #include "rib_bwd.hpp"
 #include "rib_launch.hpp"
 
+#include <mutex>
+
 namespace rib {
 
 constexpr int ENC_TOK = 8;
@@ -169,9 +171,12 @@ hipError_t launch_encode3d(int wt, int ws, int L, int hidden, int R, const float
 //   dWp_q = sum_n h_n (x) dQp_n,   dWp_k = sum_n h_n (x) dKp_n
 //   dpre_n = (dQp_n Wp_q^T + dKp_n Wp_k^T) * [pre_n > 0]
 //   dW_h = sum_n r_n (x) dpre_n,   db_h = sum_n dpre_n
-// Workgroup g handles the EB_TOK positions of chunk g and writes its partial
-// gradient of the whole packed weight vector to its own row of the workspace;
-// a second kernel sums the rows in a fixed order (deterministic, no atomics).
+// The window's positions fall into chunks of EB_TOK; workgroup g of a grid of
+// `rows` handles chunks g, g + rows, ... in that order and accumulates its
+// partial gradient of the whole packed weight vector in its own row of the
+// workspace (each thread owns the same weights in every chunk, so the row needs
+// no clearing and no atomics); a second kernel sums the rows in a fixed order.
+// With one chunk per workgroup (rows = chunk count) a row is one chunk's sum.
 // pre_n is recomputed with the forward's exact arithmetic so the ReLU mask
 // matches the forward's.
 constexpr int EB_TOK = 16;
@@ -180,7 +185,7 @@ int encode_bwd_blocks(int ws) { return (ws * ws + EB_TOK - 1) / EB_TOK; }
 
 __global__ void __launch_bounds__(ENC_THREADS)
 encode_bwd_kernel(int ws, int L, int hidden, int R, const float* __restrict__ w, const float* __restrict__ dqp,
-                  const float* __restrict__ dkp, float* __restrict__ work) {
+                  const float* __restrict__ dkp, float* __restrict__ work, int chunks) {
   extern __shared__ float sm[];
   const int F = 2 + 4 * L;
   float* feat = sm;                        // [EB_TOK][F]
@@ -195,8 +200,9 @@ encode_bwd_kernel(int ws, int L, int hidden, int R, const float* __restrict__ w,
   const float* Wk = Wq + hidden * R;
   const int nw = F * hidden + hidden + 2 * hidden * R;
   float* out = work + (long)blockIdx.x * nw;
-  {
-    const int chunk = blockIdx.x;
+  for (int chunk = blockIdx.x; chunk < chunks; chunk += gridDim.x) {
+    const bool first = chunk == (int)blockIdx.x;
+    if (!first) __syncthreads();  // the previous chunk's last phase still reads the LDS arrays
     const int n0 = chunk * EB_TOK;
     fourier_features(n0, N, ws, L, EB_TOK, F, feat);
     for (int item = threadIdx.x; item < EB_TOK * R; item += ENC_THREADS) {
@@ -233,7 +239,7 @@ encode_bwd_kernel(int ws, int L, int hidden, int R, const float* __restrict__ w,
         const float* gg = is_k ? gk : gq;
         for (int t = 0; t < EB_TOK; ++t) acc = fmaf(hid[t * hidden + j], gg[t * R + r], acc);
       }
-      out[item] = acc;
+      out[item] = first ? acc : out[item] + acc;
     }
   }
 }
@@ -258,15 +264,52 @@ encode_bwd_reduce_kernel(int nw, int blocks, const float* __restrict__ work, flo
 }
 
 hipError_t launch_encode_backward(int ws, int L, int hidden, int R, const float* w, const float* dqp,
-                                  const float* dkp, float* dw, float* work, hipStream_t stream) {
-  const int blocks = encode_bwd_blocks(ws);
+                                  const float* dkp, float* dw, float* work, int rows, hipStream_t stream) {
+  const int chunks = encode_bwd_blocks(ws);
+  rows = rows < chunks ? rows : chunks;
   const int F = 2 + 4 * L;
   const int nw = F * hidden + hidden + 2 * hidden * R;
   const size_t lds = sizeof(float) * EB_TOK * (size_t)(F + 2 * hidden + 2 * R);
-  hipLaunchKernelGGL(encode_bwd_kernel, dim3(blocks), dim3(ENC_THREADS), lds, stream, ws, L, hidden, R, w,
-                     dqp, dkp, work);
-  hipLaunchKernelGGL(encode_bwd_reduce_kernel, dim3((nw + 15) / 16), dim3(256), 0, stream, nw, blocks, work, dw);
+  hipLaunchKernelGGL(encode_bwd_kernel, dim3(rows), dim3(ENC_THREADS), lds, stream, ws, L, hidden, R, w,
+                     dqp, dkp, work, chunks);
+  hipLaunchKernelGGL(encode_bwd_reduce_kernel, dim3((nw + 15) / 16), dim3(256), 0, stream, nw, rows, work, dw);
   return hipGetLastError();
+}
+
+// Fixed workspace for callers that cannot allocate: one array per device,
+// resident from the code object's load until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it is only a handle);
+// it passes the device address that hipGetSymbolAddress returns, looked up
+// once per device and kept.
+static __device__ __align__(256) float scratch[ENC_SCRATCH_FLOATS];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mutex;
+float* scratch_ptr[MAX_DEVICES] = {};
+}  // namespace
+
+hipError_t encode_scratch(float** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *ptr = scratch_ptr[dev];
+  return hipSuccess;
+}
+
+int encode_scratch_rows(int ws, int L, int hidden, int R) {
+  const long nw = (long)(2 + 4 * L) * hidden + hidden + 2L * hidden * R;
+  const long fit = (long)ENC_SCRATCH_FLOATS / nw;
+  const long chunks = encode_bwd_blocks(ws);
+  return (int)(fit < chunks ? fit : chunks);
 }
 
 }  // namespace rib

@@ -397,8 +397,39 @@ rib_status rib_encode_backward(int window, int L, int hidden, int R, const float
       if (j != i && overlap(all[i], sizes[i], all[j], sizes[j]))
         return fail(RIB_ERR_INVALID_ARG, "%s: dweights or the workspace overlaps another buffer", fn);
   return hip_status(rib::launch_encode_backward(window, L, hidden, R, weights, dqp, dkp, dweights,
-                                                (float*)workspace, (hipStream_t)stream),
+                                                (float*)workspace, rib::encode_bwd_blocks(window),
+                                                (hipStream_t)stream),
                     "rib_encode_backward launch");
+}
+
+rib_status rib_encode_backward_noalloc(int window, int L, int hidden, int R, const float* weights,
+                                       const float* dqp, const float* dkp, float* dweights, void* stream) {
+  const char* fn = "rib_encode_backward_noalloc";
+  if (!weights || !dqp || !dkp || !dweights) return fail(RIB_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (window < 2) return fail(RIB_ERR_INVALID_ARG, "%s: window must be >= 2 (got %d)", fn, window);
+  if (L < 0 || hidden < 1 || R < 1)
+    return fail(RIB_ERR_INVALID_ARG, "%s: need L >= 0, hidden >= 1, R >= 1 (got %d, %d, %d)", fn, L, hidden, R);
+  if (window > 128 || L > 16 || hidden > 256 || R > 64)
+    return fail(RIB_ERR_UNSUPPORTED, "%s: limits are window <= 128, L <= 16, hidden <= 256, R <= 64", fn);
+  const size_t nw = (size_t)(2 + 4 * L) * hidden + hidden + 2 * (size_t)hidden * R;
+  const int rows = rib::encode_scratch_rows(window, L, hidden, R);
+  if (rows < 1)
+    return fail(RIB_ERR_UNSUPPORTED, "%s: %zu weights exceed the fixed workspace of %ld floats", fn, nw,
+                rib::ENC_SCRATCH_FLOATS);
+  const void* all[] = {weights, dqp, dkp, dweights};
+  for (const void* p : all)
+    if (!aligned(p, 4)) return fail(RIB_ERR_INVALID_ARG, "%s: pointers must be 4-byte aligned", fn);
+  const size_t no = sizeof(float) * (size_t)window * window * R;
+  const size_t sizes[] = {sizeof(float) * nw, no, no, sizeof(float) * nw};
+  for (int j = 0; j < 3; ++j)
+    if (overlap(all[3], sizes[3], all[j], sizes[j]))
+      return fail(RIB_ERR_INVALID_ARG, "%s: dweights overlaps another buffer", fn);
+  float* work = nullptr;
+  const hipError_t e = rib::encode_scratch(&work);
+  if (e != hipSuccess) return hip_status(e, "rib_encode_backward_noalloc workspace lookup");
+  return hip_status(rib::launch_encode_backward(window, L, hidden, R, weights, dqp, dkp, dweights, work, rows,
+                                                (hipStream_t)stream),
+                    "rib_encode_backward_noalloc launch");
 }
 
 }  // extern "C"

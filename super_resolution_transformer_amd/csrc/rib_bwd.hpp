@@ -81,9 +81,15 @@ bool attn_bwd_bf16_supported(int dh, int R);
 size_t attn_bwd_bf16_image_bytes(int B, int H, int W, int heads, int ws);
 hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 
-// encoder backward: workspace of encode_bwd_blocks(ws) * weight count floats
+// encoder backward: `rows` workgroups (at most encode_bwd_blocks(ws), one per
+// position chunk when equal) each fill one row of weight-count floats of `work`
 int encode_bwd_blocks(int ws);
 hipError_t launch_encode_backward(int ws, int L, int hidden, int R, const float* w, const float* dqp,
-                                  const float* dkp, float* dw, float* work, hipStream_t stream);
+                                  const float* dkp, float* dw, float* work, int rows, hipStream_t stream);
+// the per-device fixed workspace (4 MiB) and the rows of it one problem uses
+// (0 when one row does not fit)
+constexpr long ENC_SCRATCH_FLOATS = 1L << 20;
+hipError_t encode_scratch(float** ptr);
+int encode_scratch_rows(int ws, int L, int hidden, int R);
 
 }  // namespace rib

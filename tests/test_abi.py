@@ -21,7 +21,7 @@ def test_header_declares_the_boundary():
     assert set(rib.header_functions()) == {
         "rib_encode", "rib_window_attn", "rib_attn_supported", "rib_last_error", "rib_abi_version",
         "rib_cla_gate", "rib_window_attn_heads", "rib_window_attn_train", "rib_window_attn_backward", "rib_window_attn_backward_workspace",
-        "rib_encode_backward", "rib_encode_backward_workspace", "rib_ln_qkv", "rib_encode3d",
+        "rib_encode_backward", "rib_encode_backward_workspace", "rib_encode_backward_noalloc", "rib_ln_qkv", "rib_encode3d",
         "rib_window_attn3d", "rib_window_attn_multi", "rib_window_attn_heads_train",
         "rib_window_attn_heads_backward"}
 
@@ -258,6 +258,24 @@ def test_encode_backward_validation(L):
     assert L.rib_encode_backward(16, 10, 64, 16, w, q, k, d, ws, need - 4, None) == rib.RIB_ERR_INVALID_ARG
     assert L.rib_encode_backward(16, 10, 64, 16, w, q, k, w, ws, need, None) == rib.RIB_ERR_INVALID_ARG
     assert L.rib_encode_backward(16, 10, 64, 16, w, q, k, d, d, need, None) == rib.RIB_ERR_INVALID_ARG
+    assert "overlap" in L.rib_last_error().decode()
+
+
+@fake
+def test_encode_backward_noalloc_validation(L):
+    """The fixed-workspace variant refuses what rib_encode_backward refuses, before any HIP call."""
+    w, q, k, d = PB[:4]
+    f = L.rib_encode_backward_noalloc
+    assert f(16, 10, 64, 16, None, q, k, d, None) == rib.RIB_ERR_INVALID_ARG
+    assert "rib_encode_backward_noalloc" in L.rib_last_error().decode()
+    assert f(1, 10, 64, 16, w, q, k, d, None) == rib.RIB_ERR_INVALID_ARG
+    assert f(129, 10, 64, 16, w, q, k, d, None) == rib.RIB_ERR_UNSUPPORTED
+    assert f(16, 17, 64, 16, w, q, k, d, None) == rib.RIB_ERR_UNSUPPORTED
+    assert f(16, 10, 257, 16, w, q, k, d, None) == rib.RIB_ERR_UNSUPPORTED
+    assert f(16, 10, 64, 65, w, q, k, d, None) == rib.RIB_ERR_UNSUPPORTED
+    assert f(16, 10, 64, 16, w, q, k, ctypes.c_void_p(d.value + 2), None) == rib.RIB_ERR_INVALID_ARG
+    assert "aligned" in L.rib_last_error().decode()
+    assert f(16, 10, 64, 16, w, q, k, w, None) == rib.RIB_ERR_INVALID_ARG
     assert "overlap" in L.rib_last_error().decode()
 
 
