@@ -126,8 +126,11 @@ rib_status rib_window_attn_heads(const void* qc, const void* kc, const void* v, 
  * caller holding independent work at several points of that cycle (other
  * images, other streams of a batch, or the three window sizes of one shape)
  * passes the calls together, and the library runs them side by side:
- * RIB_BF16 calls that share (dh, R) take one launch per kernel kind (windows
- * of <= 256 tokens, larger windows) and per 8 calls, largest windows first;
+ * RIB_BF16 calls that share (dh, R) take one launch per workgroup size and
+ * per 8 calls, largest windows first: windows of at most 2,048 tokens (and of
+ * at most 4,096 when the call's 256-query workgroups number at most three per
+ * compute unit) share the 256-thread launch, larger windows the 512-thread
+ * tiled launch; the 16/32/64 cycle at C = 48 on a 180x320 map is one launch.
  * RIB_F32 calls run one after another.  Each call's output is bit-identical to
  * that of rib_window_attn with the same arguments.
  *

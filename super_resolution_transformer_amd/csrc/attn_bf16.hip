@@ -776,10 +776,11 @@ constexpr int SQ = 256;        // queries (and keys) per workgroup
 constexpr int SNT = SQ / KT;   // key tiles, all resident
 
 // dword w of a Q~ row: [Qp/sqrt(R), Qc/sqrt(dh)] (log2 e folded in), the
-// (-m_hat = 0, -OFF_FAST) pair, zeros
+// (-m_hat = 0, -offset) pair `cw`, zeros
 template <int DH, int R>
 __device__ __forceinline__ uint32_t qrow_word(int w, int off, int n, bool real, const float* __restrict__ qp,
-                                              const uint32_t* __restrict__ qc, float sp, float sc) {
+                                              const uint32_t* __restrict__ qc, float sp, float sc,
+                                              uint32_t cw) {
   using S = Shape<DH, R>;
   uint32_t val = 0u;
   if (w < R / 2) {
@@ -789,9 +790,52 @@ __device__ __forceinline__ uint32_t qrow_word(int w, int off, int n, bool real, 
     const uint32_t x = qc[(off >> 1) + (w - R / 2)];
     val = pack_bf16(bf16_lo(x) * sc, bf16_hi(x) * sc);
   } else if (w == S::CONSTDW) {
-    val = 0xC2800000u;  // (-m_hat = 0, -OFF_FAST = -64)
+    val = cw;
   }
   return (real || w == S::CONSTDW) ? val : 0u;
+}
+
+// Stages key r of window G (every role of the staging scheme: Kp, Kc and V
+// parts, padded keys masked) into row r % 64 of tile (r / 64) % 4 of `lds`;
+// the calling thread is thread r % 256 of a 256-thread workgroup.
+template <int DH, int R>
+__device__ __forceinline__ void stage_key(const Geo& G, uint32_t* lds, int r, const uint32_t* __restrict__ kc,
+                                          const uint32_t* __restrict__ v, const float* __restrict__ kp,
+                                          int map_elems, int window_tokens) {
+  using S = Shape<DH, R>;
+  using RL = Roles<DH, R>;
+  const bool real = r < G.n_real;
+  int off, n;
+  locate<DH>(G, real ? r : G.n_real - 1, off, n);
+  const unsigned map_bytes = (unsigned)map_elems * 2u;
+  const unsigned pos_bytes = (unsigned)(window_tokens * R) * 4u;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(kc), (short)0,
+                                                                      (int)map_bytes, (int)RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(v), (short)0,
+                                                                      (int)map_bytes, (int)RSRC_WORD3);
+  const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(kp), (short)0,
+                                                                      (int)pos_bytes, (int)RSRC_WORD3);
+  uint32_t* stage = lds + ((r >> 6) & (SNT - 1)) * S::STAGE_DW;
+  const int lane = r & 63;
+  Stage st[8];
+#pragma unroll
+  for (int role = 0; role < 8; ++role) {
+    const bool loads = role == 0 || (role == 1 && RL::KP1) || role == 2 || (role == 3 && RL::KC1) ||
+                       role == 4 || (role == 5 && RL::V1) || (role >= 6 && RL::KP67);
+    if (loads) {
+      const bool pos = role == 0 || role == 1 || role >= 6;
+      const unsigned sub = role >= 6 ? (unsigned)(role - 4) : (unsigned)(role & 1);
+      const unsigned voff = (pos ? (unsigned)(n * (R * 4)) : 2u * (unsigned)off) + 32u * sub;
+      const __amdgpu_buffer_rsrc_t rs = (role == 2 || role == 3) ? rk : (role == 4 || role == 5) ? rv : rp;
+      st[role].raw[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+      st[role].raw[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16u, 0, 0));
+    } else {
+      st[role].raw[0] = (u32x4_t){0u, 0u, 0u, 0u};
+      st[role].raw[1] = (u32x4_t){0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int role = 0; role < 8; ++role) store_tile<DH, R, true>(stage, role, lane, real, st[role]);
 }
 
 // One workgroup of the whole-window kernel: logical = window unit.
@@ -800,10 +844,9 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
                        const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                        const float* __restrict__ qp, const float* __restrict__ kp,
                        uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws,
-                       int total, long tstride, float* __restrict__ lse, int logical) {
+                       int total, long tstride, float* __restrict__ lse, int logical,
+                       uint32_t* lds) {
   using S = Shape<DH, R>;
-  using RL = Roles<DH, R>;
-  __shared__ __attribute__((aligned(16))) uint32_t lds[SNT * S::STAGE_DW];
 
   if (logical >= total) return;
   Geo G;
@@ -817,39 +860,7 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
   const int gh = lane >> 5;
 
   // ---- key r = tid: every staging role of the key, into tile r / 64 = wave
-  {
-    const bool real = tid < G.n_real;
-    int off, n;
-    locate<DH>(G, real ? tid : G.n_real - 1, off, n);
-    const unsigned map_bytes = (unsigned)(B * T * H * W * heads * DH) * 2u;
-    const unsigned pos_bytes = (unsigned)(wt * ws * ws * R) * 4u;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(kc), (short)0,
-                                                                        (int)map_bytes, (int)RSRC_WORD3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(v), (short)0,
-                                                                        (int)map_bytes, (int)RSRC_WORD3);
-    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(kp), (short)0,
-                                                                        (int)pos_bytes, (int)RSRC_WORD3);
-    uint32_t* stage = lds + wave * S::STAGE_DW;
-    Stage st[8];
-#pragma unroll
-    for (int role = 0; role < 8; ++role) {
-      const bool loads = role == 0 || (role == 1 && RL::KP1) || role == 2 || (role == 3 && RL::KC1) ||
-                         role == 4 || (role == 5 && RL::V1) || (role >= 6 && RL::KP67);
-      if (loads) {
-        const bool pos = role == 0 || role == 1 || role >= 6;
-        const unsigned sub = role >= 6 ? (unsigned)(role - 4) : (unsigned)(role & 1);
-        const unsigned voff = (pos ? (unsigned)(n * (R * 4)) : 2u * (unsigned)off) + 32u * sub;
-        const __amdgpu_buffer_rsrc_t rs = (role == 2 || role == 3) ? rk : (role == 4 || role == 5) ? rv : rp;
-        st[role].raw[0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
-        st[role].raw[1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16u, 0, 0));
-      } else {
-        st[role].raw[0] = (u32x4_t){0u, 0u, 0u, 0u};
-        st[role].raw[1] = (u32x4_t){0u, 0u, 0u, 0u};
-      }
-    }
-#pragma unroll
-    for (int role = 0; role < 8; ++role) store_tile<DH, R, true>(stage, role, lane, real, st[role]);
-  }
+  stage_key<DH, R>(G, lds, tid, kc, v, kp, B * T * H * W * heads * DH, wt * ws * ws);
 
   // ---- the wave's 64 queries run as two passes of 32 (NQ = 1): fewer live
   // registers, so three workgroups fit on a CU.  A pass picks up its Q~
@@ -870,7 +881,8 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
     for (int c = 0; c < S::KC; ++c) {
       u32x4_t q;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) q[i] = qrow_word<DH, R>(8 * c + 4 * gh + i, off, n, real, qp, qc, sp, sc);
+      for (int i = 0; i < 4; ++i)
+        q[i] = qrow_word<DH, R>(8 * c + 4 * gh + i, off, n, real, qp, qc, sp, sc, 0xC2800000u);  // (0, -OFF_FAST)
       rg.qt[0][c] = q;
     }
 #pragma unroll
@@ -975,6 +987,136 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
   }
 }
 
+// ---- windows of a few tiles per query block -----------------------------------
+// One workgroup of four waves takes SQ = 256 queries of one (window, head); the
+// window's keys pass through LDS in chunks of 256 (four 64-key tiles), every
+// thread staging one key of a chunk as in the whole-window kernel.  Each wave
+// keeps both of its 32-query blocks (Q~ operands, O, reference) in registers
+// across the chunks and runs a chunk's tiles for one block, then for the other.
+// The softmax is the tiled kernel's checked loop: exact maximum on the first
+// tile, offset OFF, an OR over the packed P of every later tile and a rescale
+// when the maximum grew by more than 8.  There is no hand-off between waves:
+// three workgroups share a CU, and while one stages a chunk the others compute.
+template <int DH, int R>
+__device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
+                       const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
+                       const float* __restrict__ qp, const float* __restrict__ kp,
+                       uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws,
+                       int total, long tstride, float* __restrict__ lse, int logical,
+                       uint32_t* lds) {
+  using S = Shape<DH, R>;
+
+  if (logical >= total) return;
+  const int qblocks = (wt * ws * ws + SQ - 1) / SQ;
+  Geo G;
+  decode_window<DH>(G, logical / qblocks, T, H, W, heads, wt, ws);
+  const int q0 = (logical % qblocks) * SQ;
+  if (q0 >= G.n_real) return;
+  qp += (long)G.h * tstride;  // per-head positional tables (tstride 0: one shared pair)
+  kp += (long)G.h * tstride;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int gh = lane >> 5;
+
+  // Q~ operands of the wave's two query blocks, straight from global memory
+  const float sp = LOG2E / sqrtf((float)R);
+  const float sc = LOG2E / sqrtf((float)DH);
+  Regs<DH, R, 1> rg0, rg1;
+  auto init_block = [&](Regs<DH, R, 1>& rg, int qb) {
+    const int r = q0 + wave * QW + qb * 32 + l32;
+    const bool real = r < G.n_real;
+    int off, n;
+    locate<DH>(G, real ? r : G.n_real - 1, off, n);
+#pragma unroll
+    for (int c = 0; c < S::KC; ++c) {
+      u32x4_t q;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        q[i] = qrow_word<DH, R>(8 * c + 4 * gh + i, off, n, real, qp, qc, sp, sc, 0xC0E00000u);  // (0, -OFF)
+      rg.qt[0][c] = q;
+    }
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) rg.O[0][dt][e] = 0.0f;
+    rg.mhat[0] = 0.0f;
+    rg.lpart[0] = 0.0f;
+  };
+  init_block(rg0, 0);
+  init_block(rg1, 1);
+  const bool act0 = q0 + wave * QW < G.n_real;  // wave-uniform
+  const bool act1 = q0 + wave * QW + 32 < G.n_real;
+  const int map_elems = B * T * H * W * heads * DH;
+
+  PhaseOps<DH, R> ops;
+  f32x16_t Sacc[1][2];
+  uint32_t P[1][2][8];
+  auto run_tiles = [&](Regs<DH, R, 1>& rg, int nt, bool first_chunk) {
+    for (int x = 0; x < nt; ++x) {
+      read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
+      read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
+      qk_tile<DH, R>(ops, rg, Sacc);
+      const uint32_t orv = exp_tile_fast(Sacc, P);
+      const bool first = first_chunk && x == 0;
+      if (__builtin_amdgcn_ballot_w64(first || (orv & 0x40004000u))) rescale_tile<DH, R>(rg, Sacc, P, first, gh);
+      pv_tile<DH, R>(ops, rg, P);
+    }
+  };
+  const int nchunks = (G.n_real + SQ - 1) / SQ;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    if (ch > 0) __syncthreads();  // every wave is done with the previous chunk's tiles
+    stage_key<DH, R>(G, lds, ch * SQ + tid, kc, v, kp, map_elems, wt * ws * ws);
+    __syncthreads();
+    const int left = G.n_real - ch * SQ;
+    const int nt = left >= SQ ? SNT : (left + KT - 1) / KT;
+    if (act0) run_tiles(rg0, nt, ch == 0);
+    if (act1) run_tiles(rg1, nt, ch == 0);
+  }
+
+  // ---- epilogue: O / l * sigmoid(G), bf16, NHWC
+  auto finish = [&](const Regs<DH, R, 1>& rg, int qb) {
+    const int r = q0 + wave * QW + qb * 32 + l32;
+    const float lsum = row_sum(rg, 0);
+    if (r >= G.n_real) return;
+    int off, n;
+    locate<DH>(G, r, off, n);
+    const float inv = 1.0f / lsum;
+    if (lse) lse[(off - G.h * DH) / G.C * heads + G.h] = (rg.mhat[0] + OFF + __log2f(lsum)) * LN2;
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = dt * 32 + 8 * q4 + 4 * gh;
+        if (d0 >= DH) continue;
+        const int e0 = 4 * q4;
+        const int gw = (off + d0) >> 1;
+        const uint32_t g01 = g[gw];
+        const uint32_t g23 = d0 + 4 <= DH ? g[gw + 1] : 0u;
+        o[gw] = pack_bf16(rg.O[0][dt][e0 + 0] * inv * sigmoidf(bf16_lo(g01)),
+                          rg.O[0][dt][e0 + 1] * inv * sigmoidf(bf16_hi(g01)));
+        if (d0 + 4 <= DH)
+          o[gw + 1] = pack_bf16(rg.O[0][dt][e0 + 2] * inv * sigmoidf(bf16_lo(g23)),
+                                rg.O[0][dt][e0 + 3] * inv * sigmoidf(bf16_hi(g23)));
+      }
+  };
+  if (act0) finish(rg0, 0);
+  if (act1) finish(rg1, 1);
+}
+
+// Workgroup -> logical index (window * heads + head) * qblocks + query block
+// for the chunked kernel, on a grid of 8 * ceil(windows / 8) * heads * qblocks
+// workgroups: all workgroups of a window (every head and query block) go to
+// one XCD, whose L2 then holds the window's token rows once for all of them,
+// and windows are dealt round-robin over the XCDs.  Indices past the last
+// window are padding.
+__device__ __forceinline__ int window_block(int bid, int per_window) {
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int k = slot / per_window;
+  return (k * 8 + xcd) * per_window + (slot - k * per_window);
+}
+
 // Workgroup -> logical index (window unit * qblocks + query block) for a grid
 // of 8 * ceil(units / 8) * qblocks workgroups.  Window unit 8k + x takes the
 // workgroups whose index is x mod 8, which the dispatcher's round-robin sends
@@ -1016,17 +1158,44 @@ attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
                        const float* __restrict__ qp, const float* __restrict__ kp,
                        uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws,
                        int total, long tstride, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[SNT * Shape<DH, R>::STAGE_DW];
   attn_small_body<DH, R>(qc, kc, v, g, qp, kp, o, B, T, H, W, heads, wt, ws, total, tstride, lse,
-                         window_unit(blockIdx.x, heads));
+                         window_unit(blockIdx.x, heads), lds);
 }
 
+template <int DH, int R>
+__global__ void __launch_bounds__(SQ, 3)
+attn_bf16_chunk_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
+                       const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
+                       const float* __restrict__ qp, const float* __restrict__ kp,
+                       uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws,
+                       int total, long tstride, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[SNT * Shape<DH, R>::STAGE_DW];
+  attn_chunk_body<DH, R>(qc, kc, v, g, qp, kp, o, B, T, H, W, heads, wt, ws, total, tstride, lse,
+                         window_block(blockIdx.x, heads * ((wt * ws * ws + SQ - 1) / SQ)), lds);
+}
+
+// Which kernel a call takes: the whole-window kernel up to SQ tokens per
+// window; the chunked kernel up to CHUNK_MAX tokens, and up to CHUNK_FIT when
+// its whole grid is resident at once (three workgroups per CU); the tiled
+// kernel otherwise.  Measured on 180x320 maps: the chunked kernel is 23% faster
+// on 32x32 windows at C = 48, 8% at C = 180, 16% on 4x16x16 and 2% on 2x32x32
+// video windows; on 64x64 windows it is 5% faster at C = 48 (720 workgroups,
+// one resident round) and 10% slower at C = 180 (1,440), where the tiled
+// kernel's two-group pipeline does more per key tile than the extra rounds cost.
+constexpr int CHUNK_MAX = 2048;
+constexpr int CHUNK_FIT = 4096;
+enum Kind { WHOLE = 0, CHUNKED = 1, TILED = 2 };
+
 // ---- several independent calls in one launch ---------------------------------
-// The calls of a group share the kernel variant (dh, R, whole-window or tiled)
-// and otherwise differ freely (maps, window sizes, tables).  Each call owns a
-// contiguous range of the grid, a multiple of 8 workgroups long, so that the
-// dispatcher's round-robin over the 8 XCDs gives every XCD the same share of
-// every call; inside a call, workgroups map to (window unit, query block) as in
-// a single call (interleave_logical).  The host orders the calls longest first.
+// The calls of a group share (dh, R) and the workgroup size, and otherwise
+// differ freely (maps, window sizes, tables): one group takes whole-window and
+// chunked calls together (256 threads), another tiled calls (512).  Each call
+// owns a contiguous range of the grid, a multiple of 8 workgroups long, so that
+// the dispatcher's round-robin over the 8 XCDs gives every XCD the same share
+// of every call; inside a call, workgroups map to their work as in a single
+// call (window_unit, window_block, interleave_logical), so every output is
+// bit-identical to the single call's.  The host orders the calls longest first.
 constexpr int GROUP_MAX = 8;
 
 struct CallDesc {
@@ -1039,7 +1208,7 @@ struct CallDesc {
   uint32_t* o;
   float* lse;
   long tstride;
-  int B, T, H, W, heads, wt, ws, units, qblocks;
+  int B, T, H, W, heads, wt, ws, units, qblocks, kind;
 };
 
 struct CallGroup {
@@ -1069,49 +1238,67 @@ __global__ void __launch_bounds__(QB, 1) attn_bf16_group_kernel(const CallGroup 
                          c.units * c.qblocks, c.tstride, c.lse, interleave_logical(lb, c.qblocks));
 }
 
+// whole-window and chunked calls: a uniform branch per workgroup on its call's kind
 template <int DH, int R>
-__global__ void __launch_bounds__(SQ, 3) attn_bf16_small_group_kernel(const CallGroup grp) {
+__global__ void __launch_bounds__(SQ, 3) attn_bf16_window_group_kernel(const CallGroup grp) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds[SNT * Shape<DH, R>::STAGE_DW];
   CallDesc c;
   const int lb = group_call(grp, blockIdx.x, c);
-  attn_small_body<DH, R>(c.qc, c.kc, c.v, c.g, c.qp, c.kp, c.o, c.B, c.T, c.H, c.W, c.heads, c.wt, c.ws,
-                         c.units, c.tstride, c.lse, window_unit(lb, c.heads));
+  if (c.kind == WHOLE)
+    attn_small_body<DH, R>(c.qc, c.kc, c.v, c.g, c.qp, c.kp, c.o, c.B, c.T, c.H, c.W, c.heads, c.wt, c.ws,
+                           c.units, c.tstride, c.lse, window_unit(lb, c.heads), lds);
+  else
+    attn_chunk_body<DH, R>(c.qc, c.kc, c.v, c.g, c.qp, c.kp, c.o, c.B, c.T, c.H, c.W, c.heads, c.wt, c.ws,
+                           c.units * c.qblocks, c.tstride, c.lse, window_block(lb, c.heads * c.qblocks), lds);
 }
 
-template <int DH, int R>
-hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
-  const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws, nWt = (a.T + a.wt - 1) / a.wt;
-  const int NW = a.wt * a.ws * a.ws;
-  if (NW <= SQ) {
-    const int windows = a.B * nWt * nWy * nWx;
-    const int total = windows * a.heads;
-    const int grid = 8 * ((windows + 7) / 8) * a.heads;  // see window_unit
-    hipLaunchKernelGGL((attn_bf16_small_kernel<DH, R>), dim3(grid), dim3(SQ), 0, stream,
-                       (const uint32_t*)a.qc, (const uint32_t*)a.kc, (const uint32_t*)a.v,
-                       (const uint32_t*)a.g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt,
-                       a.ws, total, a.tstride, a.lse);
-    return hipGetLastError();
-  }
-  const int qblocks = (NW + QB - 1) / QB;
-  const int units = a.B * nWt * nWy * nWx * a.heads;
-  const int total = units * qblocks;
-  const int grid = 8 * ((units + 7) / 8) * qblocks;  // see interleave_logical
-  hipLaunchKernelGGL((attn_bf16_kernel<DH, R>), dim3(grid), dim3(QB), 0, stream,
-                     (const uint32_t*)a.qc, (const uint32_t*)a.kc, (const uint32_t*)a.v,
-                     (const uint32_t*)a.g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt,
-                     a.ws, total, a.tstride, a.lse);
-  return hipGetLastError();
-}
-
-// window units of a call and whether it takes the whole-window kernel
+// window units of a call
 inline int call_units(const AttnArgs& a) {
   const int nWy = (a.H + a.ws - 1) / a.ws, nWx = (a.W + a.ws - 1) / a.ws, nWt = (a.T + a.wt - 1) / a.wt;
   return a.B * nWt * nWy * nWx * a.heads;
 }
-inline bool call_small(const AttnArgs& a) { return a.wt * a.ws * a.ws <= SQ; }
-inline int call_qblocks(const AttnArgs& a) { return (a.wt * a.ws * a.ws + QB - 1) / QB; }
+// cus: compute units of the device
+inline Kind call_kind(const AttnArgs& a, int cus) {
+  const int NW = a.wt * a.ws * a.ws;
+  if (NW <= SQ) return WHOLE;
+  if (NW <= CHUNK_MAX) return CHUNKED;
+  const long wgs = (long)call_units(a) * ((NW + SQ - 1) / SQ);
+  return NW <= CHUNK_FIT && wgs <= 3L * cus ? CHUNKED : TILED;
+}
+// query blocks per window unit for a kernel kind
+inline int kind_qblocks(const AttnArgs& a, Kind k) {
+  const int NW = a.wt * a.ws * a.ws;
+  return k == WHOLE ? 1 : k == CHUNKED ? (NW + SQ - 1) / SQ : (NW + QB - 1) / QB;
+}
+// workgroups of a call's grid range
+inline int kind_grid(const AttnArgs& a, Kind k) {
+  const int units = call_units(a), windows = units / a.heads, qb = kind_qblocks(a, k);
+  return k == TILED ? 8 * ((units + 7) / 8) * qb                  // see interleave_logical
+                    : 8 * ((windows + 7) / 8) * a.heads * qb;     // see window_unit, window_block
+}
 
 template <int DH, int R>
-hipError_t launch_group(const AttnArgs* const* calls, int n, bool small, hipStream_t stream) {
+hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
+  const Kind kind = call_kind(a, device_cus());
+  const int units = call_units(a), qb = kind_qblocks(a, kind), grid = kind_grid(a, kind);
+  const uint32_t* qc = (const uint32_t*)a.qc;
+  const uint32_t* kc = (const uint32_t*)a.kc;
+  const uint32_t* v = (const uint32_t*)a.v;
+  const uint32_t* g = (const uint32_t*)a.g;
+  if (kind == WHOLE)
+    hipLaunchKernelGGL((attn_bf16_small_kernel<DH, R>), dim3(grid), dim3(SQ), 0, stream, qc, kc, v, g, a.qp, a.kp,
+                       (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units, a.tstride, a.lse);
+  else if (kind == CHUNKED)
+    hipLaunchKernelGGL((attn_bf16_chunk_kernel<DH, R>), dim3(grid), dim3(SQ), 0, stream, qc, kc, v, g, a.qp, a.kp,
+                       (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units * qb, a.tstride, a.lse);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<DH, R>), dim3(grid), dim3(QB), 0, stream, qc, kc, v, g, a.qp, a.kp,
+                       (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units * qb, a.tstride, a.lse);
+  return hipGetLastError();
+}
+
+template <int DH, int R>
+hipError_t launch_group(const AttnArgs* const* calls, const Kind* kinds, int n, bool tiled, hipStream_t stream) {
   CallGroup grp{};
   grp.n = n;
   int first = 0;
@@ -1129,41 +1316,53 @@ hipError_t launch_group(const AttnArgs* const* calls, int n, bool small, hipStre
     c.tstride = a.tstride;
     c.B = a.B; c.T = a.T; c.H = a.H; c.W = a.W; c.heads = a.heads; c.wt = a.wt; c.ws = a.ws;
     c.units = call_units(a);
-    c.qblocks = small ? 1 : call_qblocks(a);
+    c.qblocks = kind_qblocks(a, kinds[i]);
+    c.kind = kinds[i];
     grp.first[i] = first;
-    first += small ? 8 * ((c.units / c.heads + 7) / 8) * c.heads  // see window_unit
-                   : 8 * ((c.units + 7) / 8) * c.qblocks;         // see interleave_logical
+    first += kind_grid(a, kinds[i]);
   }
   grp.first[n] = first;
-  if (small)
-    hipLaunchKernelGGL((attn_bf16_small_group_kernel<DH, R>), dim3(first), dim3(SQ), 0, stream, grp);
-  else
+  if (tiled)
     hipLaunchKernelGGL((attn_bf16_group_kernel<DH, R>), dim3(first), dim3(QB), 0, stream, grp);
+  else
+    hipLaunchKernelGGL((attn_bf16_window_group_kernel<DH, R>), dim3(first), dim3(SQ), 0, stream, grp);
   return hipGetLastError();
 }
 
-// all calls share (dh, R): whole-window calls in groups of the whole-window
-// kernel, the others in groups of the tiled kernel, longest windows first
+// all calls share (dh, R): whole-window and chunked calls in groups of the
+// 256-thread kernel, tiled calls in groups of the tiled kernel, each group's
+// longest windows first
 template <int DH, int R>
 hipError_t launch_multi_variant(const AttnArgs* calls, int n, hipStream_t stream) {
-  for (int small = 1; small >= 0; --small) {
+  const int cus = device_cus();
+  for (int tiled = 0; tiled <= 1; ++tiled) {
     const AttnArgs* sel[64];
+    Kind kinds[64];
     int m = 0;
-    for (int i = 0; i < n && m < 64; ++i)
-      if (call_small(calls[i]) == (small != 0)) sel[m++] = &calls[i];
+    for (int i = 0; i < n && m < 64; ++i) {
+      const Kind k = call_kind(calls[i], cus);  // the kernel the single call takes
+      if ((k == TILED) == (tiled != 0)) {
+        sel[m] = &calls[i];
+        kinds[m++] = k;
+      }
+    }
     // longest first: key tiles per window (stable insertion sort)
     for (int i = 1; i < m; ++i) {
       const AttnArgs* x = sel[i];
+      const Kind kxk = kinds[i];
       const int kx = x->wt * x->ws * x->ws;
       int j = i - 1;
       while (j >= 0 && sel[j]->wt * sel[j]->ws * sel[j]->ws < kx) {
         sel[j + 1] = sel[j];
+        kinds[j + 1] = kinds[j];
         --j;
       }
       sel[j + 1] = x;
+      kinds[j + 1] = kxk;
     }
     for (int i = 0; i < m; i += GROUP_MAX) {
-      const hipError_t e = launch_group<DH, R>(sel + i, m - i < GROUP_MAX ? m - i : GROUP_MAX, small != 0, stream);
+      const hipError_t e = launch_group<DH, R>(sel + i, kinds + i, m - i < GROUP_MAX ? m - i : GROUP_MAX,
+                                               tiled != 0, stream);
       if (e != hipSuccess) return e;
     }
   }

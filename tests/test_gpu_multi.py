@@ -1,9 +1,12 @@
 """GPU: rib_window_attn_multi runs several independent calls in few launches.
 
-Each call's output must be bit-identical to rib_window_attn on the same
-arguments (the batched kernels run the same per-workgroup code), which makes
-the index mapping of the grouped grid (call ranges, XCD interleave, padding
-workgroups) checkable exactly; one batch is also compared with the oracle.
+Calls whose windows take the 256-thread kernels (whole-window up to 256 tokens,
+chunked above) share one launch per 8 calls; calls of the tiled kernel share
+another.  Each call's output must be bit-identical to rib_window_attn on the
+same arguments (the batched kernels run the same per-workgroup code), which
+makes the index mapping of the grouped grid (call ranges, XCD dealing, padding
+workgroups, the per-call kernel branch) checkable exactly; one batch is also
+compared with the oracle.
 """
 import sys
 
@@ -56,13 +59,37 @@ def check_batch(torch, specs, dtype):
 
 
 def test_cyclic_schedule_sst_lite(torch):
-    """The three window sizes of the cyclic schedule on the SST-lite shape (180x320, C=48)."""
+    """The three window sizes of the cyclic schedule on the SST-lite shape (180x320, C=48): whole-window
+    (16), chunked (32, and 64 whose 720 workgroups are resident at once), one launch."""
     note("multi: cyclic 16/32/64 on 1x180x320, 3 heads x 16")
     check_batch(torch, [(1, 180, 320, 3, 16, 16, ws) for ws in (16, 32, 64)], "bf16")
 
 
+def test_cyclic_schedule_inference_shape(torch):
+    """The cyclic schedule at C = 180 (6 heads x 30): 16 and 32 in one launch, 64 in the tiled kernel."""
+    note("multi: cyclic 16/32/64 on 1x180x320, 6 heads x 30")
+    check_batch(torch, [(1, 180, 320, 6, 30, 16, ws) for ws in (16, 32, 64)], "bf16")
+
+
+@pytest.mark.parametrize("ws,n", [(32, 10), (16, 12), (96, 9)])
+def test_more_calls_than_one_group(torch, ws, n):
+    """More than 8 calls of one kernel kind and one (dh, R) variant: the batch is split over two launches
+    of the same grouped kernel (chunked, whole-window, tiled); ragged maps of different sizes."""
+    specs = [(1 + k % 2, 37 + 3 * k, 41 + 5 * k, 1 + k % 3, 30, 16, ws) for k in range(n)]
+    note(f"multi: {n} calls at window {ws}")
+    check_batch(torch, specs, "bf16")
+
+
+def test_sixteen_mixed_window_calls(torch):
+    """Sixteen whole-window and chunked calls (windows 8 to 45), the most one multi call takes."""
+    specs = [(1, 29 + 2 * k, 33 + k, 2, 16, 16, (8, 16, 17, 24, 32, 45)[k % 6]) for k in range(16)]
+    note("multi: 16 mixed whole-window and chunked calls")
+    check_batch(torch, specs, "bf16")
+
+
 def test_many_mixed_calls(torch):
-    """Ten calls: two groups of the tiled kernel, one of the whole-window kernel, ragged maps."""
+    """Ten calls: three take the tiled kernel (windows 96, 96, 128), seven the 256-thread kernels (windows 2,
+    4, 16, 16, 17, 32 and a 64 whose grid is resident at once) in one launch; ragged maps."""
     specs = [(1, 70, 61, 2, 30, 16, 96), (2, 37, 53, 3, 30, 16, 32), (1, 100, 61, 1, 30, 16, 64),
              (1, 40, 41, 1, 30, 16, 17), (3, 37, 53, 3, 30, 16, 16), (1, 5, 7, 2, 30, 16, 4),
              (1, 96, 96, 6, 30, 16, 96), (2, 21, 19, 2, 30, 16, 16), (1, 33, 130, 1, 30, 16, 128),

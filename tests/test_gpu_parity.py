@@ -107,7 +107,11 @@ SMALL = [
     (2, 21, 19, 2, 32, 16, 16, "bf16"),        # whole-window kernel, (32, 16) variant
     (1, 16, 16, 1, 30, 16, 16, "bf16"),        # exactly one full 16x16 window
     (2, 17, 33, 3, 16, 16, 16, "bf16"),        # one-row bottom windows
-    (1, 40, 41, 1, 16, 16, 17, "bf16"),        # 289 tokens: the tiled kernel just above 256
+    (1, 40, 41, 1, 16, 16, 17, "bf16"),        # 289 tokens: chunked kernel, two key chunks, one real query in a wave
+    (1, 50, 47, 2, 30, 16, 45, "bf16"),        # 2,025 tokens: eight chunks, the last one ragged
+    (1, 45, 50, 2, 8, 8, 24, "bf16"),          # chunked kernel, (8, 8) variant
+    (1, 30, 31, 2, 16, 32, 32, "bf16"),        # chunked kernel, (16, 32) variant
+    (1, 50, 47, 1, 30, 16, 46, "bf16"),        # 2,116 tokens: the tiled kernel just above the chunked range
 ]
 
 

@@ -1,15 +1,16 @@
 """GPU parity for scores far above the first key tile's maximum.
 
-Both bf16 kernels take the exact row maximum on the first key tile.  The tiled kernel (windows
-of more than 256 tokens) then checks every later tile: the packed bf16 P words are OR-reduced,
-and a value of 2 or more (the maximum grew by more than 8 base-2 units) sends the wave through
-an exact re-maximum and rescale before P is used.  The whole-window kernel (at most 256 tokens)
-exponentiates the later tiles against the first tile's maximum without a check, with an offset
-of 64 base-2 units; a block whose row sum or output ends non-finite repeats its tiles with the
-checked loop.  These inputs place two keys in later tiles whose score, for half of the queries,
-exceeds everything else by about 84 base-2 units (the checked rescale in the tiled kernel; the
-unchecked pass holds it in the whole-window kernel, with p up to ~2^20) or by about 250 (p
-overflows: the tiled kernel rescales, the whole-window kernel's checked re-run takes over).
+Every bf16 kernel takes the exact row maximum on the first key tile.  The chunked and tiled
+kernels (windows of more than 256 tokens) then check every later tile: the packed bf16 P words
+are OR-reduced, and a value of 2 or more (the maximum grew by more than 8 base-2 units) sends the
+wave through an exact re-maximum and rescale before P is used.  The whole-window kernel (at most
+256 tokens) exponentiates the later tiles against the first tile's maximum without a check, with
+an offset of 64 base-2 units; a block whose row sum or output ends non-finite repeats its tiles
+with the checked loop.  These inputs place two keys in later tiles whose score, for half of the queries,
+exceeds everything else by about 84 base-2 units (the checked rescale in the chunked and tiled
+kernels; the unchecked pass holds it in the whole-window kernel, with p up to ~2^20) or by about
+250 (p overflows: the chunked and tiled kernels rescale, the whole-window kernel's checked re-run
+takes over).
 Outputs are compared with the oracle over the whole map at the forward's bars (max abs error
 2e-2 for bf16; 1e-5 for fp32 plus the rounding of two spike scores of ~175, derived in the
 test); the row log-sum-exp at a bound derived from the rounding of the score operands.
@@ -49,10 +50,11 @@ def dev(torch, p, nm):
 
 CASES = [
     # B, H, W, heads, dh, R, ws, b (key spike), dtype
-    (1, 70, 64, 2, 30, 16, 64, 10.0, "bf16"),   # tiled kernel, +84 base-2 units: checked rescale
-    (1, 70, 64, 2, 30, 16, 64, 30.0, "bf16"),   # tiled kernel, +250
-    (1, 96, 100, 1, 30, 16, 96, 30.0, "bf16"),  # 96x96 windows, ragged right column
-    (1, 40, 33, 2, 16, 16, 32, 30.0, "bf16"),   # dh = 16 variant, ragged windows
+    (1, 70, 64, 2, 30, 16, 64, 10.0, "bf16"),   # chunked kernel (4,096 tokens, few workgroups), +84 base-2 units
+    (1, 70, 64, 2, 30, 16, 64, 30.0, "bf16"),   # chunked kernel, +250
+    (1, 96, 100, 1, 30, 16, 96, 30.0, "bf16"),  # tiled kernel, 96x96 windows, ragged right column
+    (1, 96, 100, 1, 30, 16, 96, 10.0, "bf16"),  # tiled kernel, +84
+    (1, 40, 33, 2, 16, 16, 32, 30.0, "bf16"),   # chunked kernel, dh = 16 variant, ragged windows
     (2, 37, 40, 2, 30, 16, 16, 10.0, "bf16"),   # whole-window kernel, +84: the unchecked pass
     (2, 37, 40, 2, 30, 16, 16, 30.0, "bf16"),   # whole-window kernel, +250: the checked re-run
     (1, 70, 64, 1, 30, 16, 64, 30.0, "f32"),
