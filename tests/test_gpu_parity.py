@@ -202,9 +202,10 @@ def test_positional_one_hot_is_bit_exact(torch, dtype, ws, H, W, R, dh):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("ws", [16, 32])
+@pytest.mark.parametrize("ws", [16, 32, 48])
 def test_locality_and_equivariance_bit_exact(torch, dtype, ws):
-    """Window 16 runs the whole-window bf16 kernel, window 32 the tiled one."""
+    """Window 16 runs the whole-window bf16 kernel, window 32 the chunked one, window 48 (2,304
+    tokens) the tiled one."""
     note(f"locality ws={ws} {dtype}")
     H, W, B, heads, dh, R = 3 * ws, 3 * ws, 2, 3, 30 if dtype == "bf16" else 16, 16
     p = synthetic.make_problem(B, H, W, heads, dh, R, dtype=dtype, seed=7)
