@@ -230,8 +230,10 @@ rib_status rib_cla_gate(const void* x, const float* dw_w, const float* dw_b, con
  *                         between calls.
  * dtype                 : RIB_F32 or RIB_BF16 (bf16 storage, fp32 arithmetic).
  * Every output and the workspace must be disjoint from every other buffer.
- * Limits : window <= 128, dh <= 64, R <= 64; B*H*W*heads*max(dh, R) < 2^31;
- *          pointers 16-byte aligned.
+ * Limits : window <= 128, dh <= 64, R <= 64; B*H*W*heads*max(dh, R) < 2^31.
+ * Alignment: maps, lse, dqp, dkp 4 bytes (dword accesses); qp, kp 8 bytes
+ *          (float pairs); the workspace 16 bytes (its packed operand images
+ *          are copied into LDS and read in 16-byte pieces).
  */
 size_t rib_window_attn_backward_workspace(int B, int H, int W, int heads, int dh, int R, int window,
                                           rib_dtype dtype);

@@ -137,8 +137,10 @@ bwd_prep_pairs_kernel(const uint32_t* __restrict__ dout, const uint32_t* __restr
   uint32_t* s_o = sm + cap;
   uint32_t* s_g = sm + 2 * cap;
   const long base = tok0 * C2;
-  // 16-byte copies: C2 and NT even keep the tile and the three LDS arrays 16-byte aligned
-  const bool vec = (C2 % 2 == 0) && (base & 3) == 0;
+  // 16-byte copies when every map is 16-byte aligned: C2 and NT even keep the tile and the three
+  // LDS arrays 16-byte aligned; otherwise dword copies (the maps need only 4-byte alignment)
+  const uintptr_t ptrs = (uintptr_t)dout | (uintptr_t)o | (uintptr_t)g | (uintptr_t)da | (uintptr_t)dg;
+  const bool vec = (C2 % 2 == 0) && (base & 3) == 0 && (ptrs & 15) == 0;
   auto copy_in = [&](uint32_t* dst, const uint32_t* __restrict__ src) {
     if (vec) {
       for (int i = 4 * (int)threadIdx.x; i + 4 <= ndw; i += 1024)

@@ -313,7 +313,11 @@ rib_status window_attn_backward(const char* fn, bool per_head, const void* qc, c
     return fail(RIB_ERR_UNSUPPORTED, "%s: B*H*W*heads*max(dh, R) must be < 2^31", fn);
   const void* all[] = {qc, kc, v, g, qp, kp, o, lse, dout, dqc, dkc, dv, dg, dqp, dkp, workspace};
   for (const void* p : all)
-    if (!aligned(p, 16)) return fail(RIB_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+    if (!aligned(p, 4)) return fail(RIB_ERR_INVALID_ARG, "%s: pointers must be 4-byte aligned", fn);
+  if (!aligned(qp, 8) || !aligned(kp, 8))
+    return fail(RIB_ERR_INVALID_ARG, "%s: qp and kp must be 8-byte aligned", fn);
+  if (!aligned(workspace, 16))
+    return fail(RIB_ERR_INVALID_ARG, "%s: the workspace must be 16-byte aligned", fn);
   const BwdLayout lay = bwd_layout(B, H, W, heads, dh, R, window, dtype);
   if (workspace_bytes < lay.total)
     return fail(RIB_ERR_INVALID_ARG, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, lay.total);

@@ -201,8 +201,12 @@ def test_backward_validation(L):
     assert bwd(L, window=129) == rib.RIB_ERR_UNSUPPORTED
     assert bwd(L, nbytes=need - 1) == rib.RIB_ERR_INVALID_ARG
     assert "workspace" in L.rib_last_error().decode()
-    assert bwd(L, [ctypes.c_void_p(PB[0].value + 4)] + PB[1:]) == rib.RIB_ERR_INVALID_ARG
-    assert "aligned" in L.rib_last_error().decode()
+    assert bwd(L, [ctypes.c_void_p(PB[0].value + 2)] + PB[1:]) == rib.RIB_ERR_INVALID_ARG   # maps: dwords
+    assert "4-byte" in L.rib_last_error().decode()
+    assert bwd(L, PB[:4] + [ctypes.c_void_p(PB[4].value + 4)] + PB[5:]) == rib.RIB_ERR_INVALID_ARG  # qp: pairs
+    assert "8-byte" in L.rib_last_error().decode()
+    assert bwd(L, PB[:15] + [ctypes.c_void_p(PB[15].value + 8)]) == rib.RIB_ERR_INVALID_ARG  # workspace
+    assert "16-byte" in L.rib_last_error().decode()
     alias = PB[:10] + [PB[2]] + PB[11:]                                   # dkc == v
     assert bwd(L, alias) == rib.RIB_ERR_INVALID_ARG
     assert "overlap" in L.rib_last_error().decode()
