@@ -992,7 +992,10 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
 // window's keys pass through LDS in chunks of 256 (four 64-key tiles), every
 // thread staging one key of a chunk as in the whole-window kernel.  Each wave
 // keeps both of its 32-query blocks (Q~ operands, O, reference) in registers
-// across the chunks and runs a chunk's tiles for one block, then for the other.
+// across the chunks; per tile it reads the K~ and V operands once, issues both
+// blocks' score products, and runs block 0's exponentials while block 1's
+// scores are still on the matrix core.  (Two values the epilogue needs spill
+// to scratch, once per wave, outside the loop.)
 // The softmax is the tiled kernel's checked loop: exact maximum on the first
 // tile, offset OFF, an OR over the packed P of every later tile and a rescale
 // when the maximum grew by more than 8.  There is no hand-off between waves:
@@ -1071,8 +1074,27 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
     __syncthreads();
     const int left = G.n_real - ch * SQ;
     const int nt = left >= SQ ? SNT : (left + KT - 1) / KT;
-    if (act0) run_tiles(rg0, nt, ch == 0);
-    if (act1) run_tiles(rg1, nt, ch == 0);
+    if (act1) {
+      // both blocks: one operand read per tile; block 1's scores issue on the matrix core
+      // while block 0's exponentials run
+      f32x16_t Sb[1][2];
+      uint32_t Pb[1][2][8];
+      for (int x = 0; x < nt; ++x) {
+        read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
+        read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
+        const bool first = ch == 0 && x == 0;
+        qk_tile<DH, R>(ops, rg0, Sacc);
+        qk_tile<DH, R>(ops, rg1, Sb);
+        const uint32_t or0 = exp_tile_fast(Sacc, P);
+        if (__builtin_amdgcn_ballot_w64(first || (or0 & 0x40004000u))) rescale_tile<DH, R>(rg0, Sacc, P, first, gh);
+        pv_tile<DH, R>(ops, rg0, P);
+        const uint32_t or1 = exp_tile_fast(Sb, Pb);
+        if (__builtin_amdgcn_ballot_w64(first || (or1 & 0x40004000u))) rescale_tile<DH, R>(rg1, Sb, Pb, first, gh);
+        pv_tile<DH, R>(ops, rg1, Pb);
+      }
+    } else if (act0) {
+      run_tiles(rg0, nt, ch == 0);
+    }
   }
 
   // ---- epilogue: O / l * sigmoid(G), bf16, NHWC
