@@ -216,14 +216,17 @@ encode_bwd_kernel(int ws, int L, int hidden, int R, const float* __restrict__ w,
       const int t = item / hidden, j = item % hidden;
       const float* f = feat + t * F;
       float acc = bh[j];
-      for (int k = 0; k < F; ++k) acc = fmaf(f[k], Wh[k * hidden + j], acc);
+#pragma unroll 8
+      for (int k = 0; k < F; ++k) acc = fmaf(f[k], Wh[k * hidden + j], acc);  // 8 weight loads in flight
       float dh = 0.0f;
+#pragma unroll 8
       for (int r = 0; r < R; ++r) dh = fmaf(gq[t * R + r], Wq[j * R + r], fmaf(gk[t * R + r], Wk[j * R + r], dh));
       hid[item] = fmaxf(acc, 0.0f);
       dpre[item] = acc > 0.0f ? dh : 0.0f;
     }
     __syncthreads();
-    for (int item = threadIdx.x; item < nw; item += ENC_THREADS) {
+    // this chunk's sum for one weight
+    auto partial = [&](int item) {
       float acc = 0.0f;
       if (item < F * hidden) {
         const int f = item / hidden, j = item % hidden;
@@ -239,7 +242,13 @@ encode_bwd_kernel(int ws, int L, int hidden, int R, const float* __restrict__ w,
         const float* gg = is_k ? gk : gq;
         for (int t = 0; t < EB_TOK; ++t) acc = fmaf(hid[t * hidden + j], gg[t * R + r], acc);
       }
-      out[item] = first ? acc : out[item] + acc;
+      return acc;
+    };
+    // two loops, so that the first chunk's stores come with no read of the row
+    if (first) {
+      for (int item = threadIdx.x; item < nw; item += ENC_THREADS) out[item] = partial(item);
+    } else {
+      for (int item = threadIdx.x; item < nw; item += ENC_THREADS) out[item] += partial(item);
     }
   }
 }
