@@ -386,10 +386,19 @@ def cpu_baseline(synthetic, cfg_idx, ws, units_sample):
     oracle.window_attn(p.qc, p.kc, p.v, p.g, qp, kp, c.heads, ws, unit_range=(0, units_sample))
     dt = time.perf_counter() - t0
     full = dt * total_units / units_sample           # all units are full 96x96 windows here
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {
         "value": c.B * c.H * c.W / full,
         "unit": "tokens/s",
         "cores": oracle.threads(),
+        "cpu_model": model,
         "kind": "oracle",
         "sample": f"{units_sample} of {total_units} (image, window, head) units of the same workload "
                   f"(each a full {ws}x{ws} window, 1 head), {dt:.1f} s, scaled by unit count",
