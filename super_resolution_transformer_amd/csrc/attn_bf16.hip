@@ -545,6 +545,7 @@ __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc,
   const int gh = lane >> 5;  // lane half
 
   // ---- prologue: build the workgroup's Q~ rows in LDS, then pick up the B operands
+  const unsigned map_bytes = (unsigned)(B * T * H * W * heads * DH) * 2u;
   {
     const int r = q0 + tid;
     const bool real = r < G.n_real;
@@ -552,15 +553,30 @@ __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc,
     locate<DH>(G, real ? r : G.n_real - 1, off, n);
     const float sp = LOG2E / sqrtf((float)R);
     const float sc = LOG2E / sqrtf((float)DH);
+    // the row's R Qp floats and DH/2 Qc dwords in 16-byte buffer loads (bounds-checked: the
+    // last load of a head slice may read into the next slice, whose dwords are not used)
+    constexpr int NQP = R / 4, NQC = (DH / 2 + 3) / 4;
+    const __amdgpu_buffer_rsrc_t rqp = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(qp), (short)0, (int)((unsigned)(wt * ws * ws * R) * 4u), (int)RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t rqc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qc), (short)0, (int)map_bytes, (int)RSRC_WORD3);
+    u32x4_t xp[NQP], xc[NQC];
+#pragma unroll
+    for (int k = 0; k < NQP; ++k)
+      xp[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rqp, (unsigned)(n * R + 4 * k) * 4u, 0, 0));
+#pragma unroll
+    for (int k = 0; k < NQC; ++k)
+      xc[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rqc, 2u * (unsigned)off + 16u * k, 0, 0));
     uint32_t row[S::ROWDW];
 #pragma unroll
     for (int w = 0; w < S::ROWDW; ++w) {
       uint32_t val;
       if (w < R / 2) {
-        const float2 pq = *reinterpret_cast<const float2*>(qp + n * R + 2 * w);
-        val = pack_bf16(pq.x * sp, pq.y * sp);
+        const uint32_t a = xp[w / 2][2 * (w % 2)], b = xp[w / 2][2 * (w % 2) + 1];
+        val = pack_bf16(__builtin_bit_cast(float, a) * sp, __builtin_bit_cast(float, b) * sp);
       } else if (w < R / 2 + DH / 2) {
-        const uint32_t x = qc[(off >> 1) + (w - R / 2)];
+        const int q = w - R / 2;
+        const uint32_t x = xc[q / 4][q % 4];
         val = pack_bf16(bf16_lo(x) * sc, bf16_hi(x) * sc);
       } else if (w == S::CONSTDW) {
         val = 0xC0E00000u;  // (-m_hat = 0, -OFF = -7)
@@ -595,7 +611,6 @@ __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc,
   const int grp = wave >> 2;  // 0: waves 0-3 lead, 1: waves 4-7 follow half a step behind
   // this wave's load source (wave-uniform): see the staging notes above
   using RL = Roles<DH, R>;
-  const unsigned map_bytes = (unsigned)(B * T * H * W * heads * DH) * 2u;
   const unsigned pos_bytes = (unsigned)(NW * R) * 4u;
   const void* src = (wave == 2 || wave == 3) ? (const void*)kc
                   : (wave == 4 || wave == 5) ? (const void*)v : (const void*)kp;
@@ -702,8 +717,12 @@ __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc,
   }
   // the gate values of the epilogue are loaded now, so that their latency hides behind the
   // last tile's softmax and product instead of following them
+  // (channels d0 .. d0+3 of the lane's token: one 8-byte buffer load; where the head slice ends
+  // inside the 4 channels the second dword belongs to the next slice and is not used)
   int goff[2];
   uint32_t gv[2][S::DT][4][2];
+  const __amdgpu_buffer_rsrc_t rgt =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(g), (short)0, (int)map_bytes, (int)RSRC_WORD3);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int r = q0 + wave * QW + qb * 32 + l32;
@@ -714,9 +733,12 @@ __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc,
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = dt * 32 + 8 * q4 + 4 * gh;
-        const int gw = (goff[qb] + d0) >> 1;
-        gv[qb][dt][q4][0] = active && d0 < DH ? g[gw] : 0u;
-        gv[qb][dt][q4][1] = active && d0 + 4 <= DH ? g[gw + 1] : 0u;
+        u32x2_t w2 = {0u, 0u};
+        if (active && d0 < DH)
+          w2 = __builtin_bit_cast(u32x2_t,
+                                  __builtin_amdgcn_raw_buffer_load_b64(rgt, 2u * (unsigned)(goff[qb] + d0), 0, 0));
+        gv[qb][dt][q4][0] = w2[0];
+        gv[qb][dt][q4][1] = w2[1];
       }
   }
   softmax(ntiles - 1);
@@ -729,7 +751,8 @@ __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc,
   if (grp == 0) __syncthreads();
 
   if (!active) return;
-  // ---- epilogue: O / l * sigmoid(G), bf16, NHWC
+  // ---- epilogue: O / l * sigmoid(G), bf16, NHWC; 4 channels per 8-byte buffer store
+  const __amdgpu_buffer_rsrc_t rot = __builtin_amdgcn_make_buffer_rsrc(o, (short)0, (int)map_bytes, (int)RSRC_WORD3);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int r = q0 + wave * QW + qb * 32 + l32;
@@ -753,10 +776,11 @@ __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc,
           const uint32_t g23 = gv[qb][dt][q4][1];
           const uint32_t r23 = pack_bf16(rg.O[qb][dt][e0 + 2] * inv * sigmoidf(bf16_lo(g23)),
                                          rg.O[qb][dt][e0 + 3] * inv * sigmoidf(bf16_hi(g23)));
-          o[gw] = r01;
-          o[gw + 1] = r23;
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) int,
+                                                                   (u32x2_t){r01, r23}),
+                                                rot, 4u * (unsigned)gw, 0, 0);
         } else {
-          o[gw] = r01;
+          __builtin_amdgcn_raw_buffer_store_b32((int)r01, rot, 4u * (unsigned)gw, 0, 0);
         }
       }
   }
