@@ -799,24 +799,74 @@ __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc,
 constexpr int SQ = 256;        // queries (and keys) per workgroup
 constexpr int SNT = SQ / KT;   // key tiles, all resident
 
-// dword w of a Q~ row: [Qp/sqrt(R), Qc/sqrt(dh)] (log2 e folded in), the
-// (-m_hat = 0, -offset) pair `cw`, zeros
+// Dwords w0 .. w0+3 (w0 = 8c + 4gh, the lane's half of chunk c) of a Q~ row:
+// [Qp/sqrt(R), Qc/sqrt(dh)] (log2 e folded in), the (-m_hat = 0, -offset) pair
+// `cw`, zeros; a padded query row keeps only the constant pair.  R/2 and w0 are
+// multiples of 4, so a group is all Qp, or Qc up to the end of the slice, or
+// neither: one pair of 16-byte Qp loads or one 16-byte Qc load (bounds-checked
+// buffer loads; past the end of the head slice the dwords are not used).
 template <int DH, int R>
-__device__ __forceinline__ uint32_t qrow_word(int w, int off, int n, bool real, const float* __restrict__ qp,
-                                              const uint32_t* __restrict__ qc, float sp, float sc,
-                                              uint32_t cw) {
+__device__ __forceinline__ u32x4_t qrow_group(int w0, int off, int n, bool real, __amdgpu_buffer_rsrc_t rqp,
+                                              __amdgpu_buffer_rsrc_t rqc, float sp, float sc, uint32_t cw) {
   using S = Shape<DH, R>;
-  uint32_t val = 0u;
-  if (w < R / 2) {
-    const float2 pq = *reinterpret_cast<const float2*>(qp + n * R + 2 * w);
-    val = pack_bf16(pq.x * sp, pq.y * sp);
-  } else if (w < R / 2 + DH / 2) {
-    const uint32_t x = qc[(off >> 1) + (w - R / 2)];
-    val = pack_bf16(bf16_lo(x) * sc, bf16_hi(x) * sc);
-  } else if (w == S::CONSTDW) {
-    val = cw;
+  static_assert(R % 8 == 0, "Qp groups of 4 dwords");
+  u32x4_t q;
+  if (w0 < R / 2) {
+    const f32x4_t a =
+        __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rqp, (unsigned)(n * R + 2 * w0) * 4u, 0, 0));
+    const f32x4_t b = __builtin_bit_cast(
+        f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rqp, (unsigned)(n * R + 2 * w0) * 4u + 16u, 0, 0));
+    q = (u32x4_t){pack_bf16(a[0] * sp, a[1] * sp), pack_bf16(a[2] * sp, a[3] * sp), pack_bf16(b[0] * sp, b[1] * sp),
+                  pack_bf16(b[2] * sp, b[3] * sp)};
+  } else if (w0 < R / 2 + DH / 2) {
+    const u32x4_t x = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rqc, 2u * (unsigned)off + 4u * (unsigned)(w0 - R / 2), 0, 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int w = w0 + i;
+      q[i] = w < R / 2 + DH / 2 ? pack_bf16(bf16_lo(x[i]) * sc, bf16_hi(x[i]) * sc) : (w == S::CONSTDW ? cw : 0u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = w0 + i == S::CONSTDW ? cw : 0u;
   }
-  return (real || w == S::CONSTDW) ? val : 0u;
+  if (!real) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = w0 + i == S::CONSTDW ? cw : 0u;
+  }
+  return q;
+}
+
+// gate channels d0 .. d0+3 of the head slice at element offset `off` (one 8-byte
+// buffer load; where the slice ends inside the 4 channels the second dword is
+// not used)
+__device__ __forceinline__ u32x2_t gate4(__amdgpu_buffer_rsrc_t rg, int off, int d0) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rg, 2u * (unsigned)(off + d0), 0, 0));
+}
+
+// output channels d0 .. d0+3 (both dwords) or d0 .. d0+1 (the slice ends there)
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t ro, int off, int d0, uint32_t r01, uint32_t r23,
+                                       bool both) {
+  if (both)
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) int,
+                                                             (u32x2_t){r01, r23}),
+                                          ro, 2u * (unsigned)(off + d0), 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32((int)r01, ro, 2u * (unsigned)(off + d0), 0, 0);
+}
+
+// buffer descriptors of a call's maps and positional table (num_records bounds every access)
+struct MapRsrc {
+  __amdgpu_buffer_rsrc_t qp, qc, g, o;
+};
+__device__ __forceinline__ MapRsrc map_rsrc(const float* qp, const uint32_t* qc, const uint32_t* g, uint32_t* o,
+                                            unsigned map_bytes, unsigned pos_bytes) {
+  MapRsrc m;
+  m.qp = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(qp), (short)0, (int)pos_bytes, (int)RSRC_WORD3);
+  m.qc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qc), (short)0, (int)map_bytes, (int)RSRC_WORD3);
+  m.g = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(g), (short)0, (int)map_bytes, (int)RSRC_WORD3);
+  m.o = __builtin_amdgcn_make_buffer_rsrc(o, (short)0, (int)map_bytes, (int)RSRC_WORD3);
+  return m;
 }
 
 // Stages key r of window G (every role of the staging scheme: Kp, Kc and V
@@ -895,6 +945,8 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
   Regs<DH, R, 1> rg;
   uint32_t gv[S::DT][4][2];
   int offq = 0;
+  const MapRsrc mr = map_rsrc(qp, qc, g, o, (unsigned)(B * T * H * W * heads * DH) * 2u,
+                              (unsigned)(wt * ws * ws * R) * 4u);
   auto load_block = [&](int qb) {
     const int r = wave * QW + qb * 32 + l32;
     const bool real = r < G.n_real;
@@ -902,21 +954,17 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
     locate<DH>(G, real ? r : G.n_real - 1, off, n);
     offq = off;
 #pragma unroll
-    for (int c = 0; c < S::KC; ++c) {
-      u32x4_t q;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        q[i] = qrow_word<DH, R>(8 * c + 4 * gh + i, off, n, real, qp, qc, sp, sc, 0xC2800000u);  // (0, -OFF_FAST)
-      rg.qt[0][c] = q;
-    }
+    for (int c = 0; c < S::KC; ++c)
+      rg.qt[0][c] = qrow_group<DH, R>(8 * c + 4 * gh, off, n, real, mr.qp, mr.qc, sp, sc, 0xC2800000u);  // (0, -OFF_FAST)
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d0 = dt * 32 + 8 * q4 + 4 * gh;
-        const int gw = (off + d0) >> 1;
-        gv[dt][q4][0] = d0 < DH ? g[gw] : 0u;
-        gv[dt][q4][1] = d0 + 4 <= DH ? g[gw + 1] : 0u;
+        u32x2_t w2 = {0u, 0u};
+        if (d0 < DH) w2 = gate4(mr.g, off, d0);
+        gv[dt][q4][0] = w2[0];
+        gv[dt][q4][1] = w2[1];
       }
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
@@ -997,15 +1045,12 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
           const int d0 = dt * 32 + 8 * q4 + 4 * gh;
           if (d0 >= DH) continue;
           const int e0 = 4 * q4;
-          const int gw = (offq + d0) >> 1;
-          const uint32_t g01 = gv[dt][q4][0];
-          o[gw] = pack_bf16(rg.O[0][dt][e0 + 0] * inv * sigmoidf(bf16_lo(g01)),
-                            rg.O[0][dt][e0 + 1] * inv * sigmoidf(bf16_hi(g01)));
-          if (d0 + 4 <= DH) {
-            const uint32_t g23 = gv[dt][q4][1];
-            o[gw + 1] = pack_bf16(rg.O[0][dt][e0 + 2] * inv * sigmoidf(bf16_lo(g23)),
-                                  rg.O[0][dt][e0 + 3] * inv * sigmoidf(bf16_hi(g23)));
-          }
+          const uint32_t g01 = gv[dt][q4][0], g23 = gv[dt][q4][1];
+          const uint32_t r01 = pack_bf16(rg.O[0][dt][e0 + 0] * inv * sigmoidf(bf16_lo(g01)),
+                                         rg.O[0][dt][e0 + 1] * inv * sigmoidf(bf16_hi(g01)));
+          const uint32_t r23 = pack_bf16(rg.O[0][dt][e0 + 2] * inv * sigmoidf(bf16_lo(g23)),
+                                         rg.O[0][dt][e0 + 3] * inv * sigmoidf(bf16_hi(g23)));
+          store4(mr.o, offq, d0, r01, r23, d0 + 4 <= DH);
         }
     }
   }
@@ -1051,19 +1096,16 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
   const float sp = LOG2E / sqrtf((float)R);
   const float sc = LOG2E / sqrtf((float)DH);
   Regs<DH, R, 1> rg0, rg1;
+  const MapRsrc mr = map_rsrc(qp, qc, g, o, (unsigned)(B * T * H * W * heads * DH) * 2u,
+                              (unsigned)(wt * ws * ws * R) * 4u);
   auto init_block = [&](Regs<DH, R, 1>& rg, int qb) {
     const int r = q0 + wave * QW + qb * 32 + l32;
     const bool real = r < G.n_real;
     int off, n;
     locate<DH>(G, real ? r : G.n_real - 1, off, n);
 #pragma unroll
-    for (int c = 0; c < S::KC; ++c) {
-      u32x4_t q;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        q[i] = qrow_word<DH, R>(8 * c + 4 * gh + i, off, n, real, qp, qc, sp, sc, 0xC0E00000u);  // (0, -OFF)
-      rg.qt[0][c] = q;
-    }
+    for (int c = 0; c < S::KC; ++c)
+      rg.qt[0][c] = qrow_group<DH, R>(8 * c + 4 * gh, off, n, real, mr.qp, mr.qc, sp, sc, 0xC0E00000u);  // (0, -OFF)
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
@@ -1137,14 +1179,12 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
         const int d0 = dt * 32 + 8 * q4 + 4 * gh;
         if (d0 >= DH) continue;
         const int e0 = 4 * q4;
-        const int gw = (off + d0) >> 1;
-        const uint32_t g01 = g[gw];
-        const uint32_t g23 = d0 + 4 <= DH ? g[gw + 1] : 0u;
-        o[gw] = pack_bf16(rg.O[0][dt][e0 + 0] * inv * sigmoidf(bf16_lo(g01)),
-                          rg.O[0][dt][e0 + 1] * inv * sigmoidf(bf16_hi(g01)));
-        if (d0 + 4 <= DH)
-          o[gw + 1] = pack_bf16(rg.O[0][dt][e0 + 2] * inv * sigmoidf(bf16_lo(g23)),
-                                rg.O[0][dt][e0 + 3] * inv * sigmoidf(bf16_hi(g23)));
+        const u32x2_t g4 = gate4(mr.g, off, d0);
+        const uint32_t r01 = pack_bf16(rg.O[0][dt][e0 + 0] * inv * sigmoidf(bf16_lo(g4[0])),
+                                       rg.O[0][dt][e0 + 1] * inv * sigmoidf(bf16_hi(g4[0])));
+        const uint32_t r23 = pack_bf16(rg.O[0][dt][e0 + 2] * inv * sigmoidf(bf16_lo(g4[1])),
+                                       rg.O[0][dt][e0 + 3] * inv * sigmoidf(bf16_hi(g4[1])));
+        store4(mr.o, off, d0, r01, r23, d0 + 4 <= DH);
       }
   };
   if (act0) finish(rg0, 0);
