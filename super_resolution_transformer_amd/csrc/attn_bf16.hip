@@ -1226,15 +1226,19 @@ __device__ __forceinline__ int window_unit(int bid, int heads) {
   return (k * 8 + xcd) * heads + (slot - k * heads);
 }
 
+// whole_windows: the window count is a multiple of 8, so whole windows (every head and query
+// block) can be dealt to the XCDs evenly (window_block); else window units are (interleave_logical)
 template <int DH, int R>
 __global__ void __launch_bounds__(QB, 1)
 attn_bf16_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
                  const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                  const float* __restrict__ qp, const float* __restrict__ kp,
                  uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws, int total,
-                 long tstride, float* __restrict__ lse) {
+                 long tstride, float* __restrict__ lse, int whole_windows) {
+  const int qblocks = (wt * ws * ws + QB - 1) / QB;
   attn_tiled_body<DH, R>(qc, kc, v, g, qp, kp, o, B, T, H, W, heads, wt, ws, total, tstride, lse,
-                         interleave_logical(blockIdx.x, (wt * ws * ws + QB - 1) / QB));
+                         whole_windows ? window_block(blockIdx.x, heads * qblocks)
+                                       : interleave_logical(blockIdx.x, qblocks));
 }
 
 template <int DH, int R>
@@ -1379,7 +1383,8 @@ hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
                        (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units * qb, a.tstride, a.lse);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<DH, R>), dim3(grid), dim3(QB), 0, stream, qc, kc, v, g, a.qp, a.kp,
-                       (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units * qb, a.tstride, a.lse);
+                       (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units * qb, a.tstride, a.lse,
+                       (units / a.heads) % 8 == 0 ? 1 : 0);
   return hipGetLastError();
 }
 
