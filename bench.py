@@ -9,8 +9,9 @@ R = 16, one 96x96 window per image.  Secondary figures for the 64x64 window
 (1x180x320, C = 180), the 640x360 input with 96x96 windows, and the 16x16
 window of the SST-lite map (HBM-bound) are reported in the same JSON line, and so is the
 CLA gate producer (rib_cla_gate, HBM-bound) and the LayerNorm + Q/K/V projection
-(rib_ln_qkv, HBM-bound) on the same maps, space-time windows on an 8-frame video map
-(rib_window_attn3d), and the
+(rib_ln_qkv, HBM-bound) on the same maps, that projection with its Q side moved into the
+attention (rib_window_attn_lnq) against the unfused pair, space-time windows on an 8-frame
+video map (rib_window_attn3d), and the
 training iteration of the attention (rib_window_attn_train + rib_window_attn_backward +
 rib_encode_backward) on the 96x96 and 64x64 workloads.
 
@@ -405,6 +406,46 @@ def cpu_baseline(synthetic, cfg_idx, ws, units_sample):
     }
 
 
+def time_fused_q(torch, rib, synthetic):
+    """The block's input projection plus the attention, two ways, on the 96x96-window maps:
+    unfused = rib_ln_qkv (Q, K, V, LN(X)) then rib_window_attn; fused = rib_ln_qkv without Q then
+    rib_window_attn_lnq (LayerNorm and the Q projection inside the attention's query prologue)."""
+    res = {}
+    for name, (B, H, W, heads, dh, ws, cfg_idx) in (("96x96 window, 32x96x96, C=180", (32, 96, 96, 6, 30, 96, 4)),
+                                                   ("96x96 window, 1x360x640, C=180", (1, 360, 640, 6, 30, 96, 5))):
+        C = heads * dh
+        c = synthetic.CONFIGS[cfg_idx]
+        lp = synthetic.make_ln_qkv_problem(B, H, W, C, "bf16", seed=3)
+        x = torch.from_numpy(lp.x_bits.view("int16")).view(torch.bfloat16).cuda()
+        prm = [torch.from_numpy(a).cuda() for a in (lp.gamma, lp.beta, lp.w, lp.bias)]
+        weights = synthetic.make_problem(1, 8, 8, heads, dh, c.R, c.L, c.hidden, "bf16", c.seed).weights
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(c.seed)
+        g = torch.empty_like(x).normal_(generator=gen)   # gate pre-activation ~ N(0, 1)
+        qp, kp = rib.encode(ws, c.L, c.hidden, c.R, torch.from_numpy(weights).cuda())
+        q, k, v, xn, o = (torch.empty_like(x) for _ in range(5))
+        unfused = lambda: (rib.ln_qkv_into(x, *prm, q, k, v, xn), rib.window_attn_into(q, k, v, g, qp, kp, heads, ws, o))
+        fused = lambda: (rib.ln_qkv_into(x, *prm, None, k, v, xn),
+                         rib.window_attn_lnq_into(x, *prm, k, v, g, qp, kp, heads, ws, o))
+        r = {}
+        for tag, fn in (("unfused", unfused), ("fused", fused)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(20):
+                fn()
+            e.record()
+            torch.cuda.synchronize()
+            r["ms_" + tag] = s.elapsed_time(e) / 20
+        r["fused_over_unfused"] = r["ms_fused"] / r["ms_unfused"]
+        res[name] = r
+        del x, q, k, v, xn, o, g
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -513,6 +554,7 @@ def main():
     if not args.no_extra:
         out["cla_gate"] = time_gate(torch, rib, synthetic)
         out["ln_qkv"] = time_ln_qkv(torch, rib, synthetic)
+        out["fused_q_projection"] = time_fused_q(torch, rib, synthetic)
         out["space_time"] = time_space_time(torch, rib, synthetic)
         out["cyclic_schedule"] = time_cyclic(torch, rib, synthetic)
         out["backward"] = {"96x96 window, 32x96x96": time_backward(torch, rib, synthetic, 4, 96, args.backward_reps),

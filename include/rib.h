@@ -317,6 +317,8 @@ rib_status rib_encode_backward_noalloc(int window, int L, int hidden, int R, con
  * dtype      : RIB_F32 -- fp32 throughout.  RIB_BF16 -- LayerNorm in fp32,
  *              xn and W rounded to bf16, the product on bf16 matrix cores
  *              with fp32 accumulation, outputs rounded to bf16.
+ * q may be NULL: Q is then not written (for rib_window_attn_lnq, which
+ * computes it inside the attention).
  * Outputs must not overlap each other or any input.
  * Limits : C <= 256 (even for bf16); B*H*W*C < 2^30; pointers 16-byte
  *          aligned; 0 <= eps <= 1.
@@ -324,6 +326,34 @@ rib_status rib_encode_backward_noalloc(int window, int L, int hidden, int R, con
 rib_status rib_ln_qkv(const void* x, const float* gamma, const float* beta, const float* w, const float* bias,
                       void* q, void* k, void* v, void* xn, int B, int H, int W, int C, float eps, rib_dtype dtype,
                       void* stream);
+
+/*
+ * rib_window_attn_lnq -- rib_window_attn with the Q side of the block's input
+ * projection fused into the attention (explainer section 3.1: LayerNorm, then
+ * the RIB attention): Qc = LN(x) W_q + b_q is computed inside the kernel for
+ * each query block and never stored; K and V come from rib_ln_qkv (whose q
+ * may then be NULL).  The LayerNorm and the Q columns of w and bias are those
+ * of rib_ln_qkv; the arithmetic folds the affine part into the weights:
+ *   q_d = bf16( inv (sum_c x_c W'_cd - mu sum_c W'_cd) + b'_d ),
+ *   W'_cd = bf16(gamma_c W_cd),  b'_d = bias_d + sum_c beta_c W_cd,
+ * inv = 1/sqrt(var + eps); the statistics are fp32 sums of x and x^2 (the
+ * bf16 products are exact), var = E[x^2] - mu^2; the product runs on bf16
+ * matrix cores with fp32 accumulation.  q can therefore differ from rib_ln_qkv's
+ * (which rounds LN(x) to bf16 before its product) by about one bf16 unit.
+ * The attention is rib_window_attn's.
+ * x          : device bf16 [B][H][W][heads*dh], the block input (read).
+ * gamma, beta: device float32 [C]; w: device float32 [C][3C], columns
+ *              Q | K | V; bias: device float32 [3C] (only Q's are read).
+ * kc, v, g, qp, kp, o, B, H, W, heads, dh, R, window: as rib_window_attn.
+ * Limits : RIB_BF16 only; (dh, R) in {(30, 16), (16, 16)}; heads*dh <= 192;
+ *          0 <= eps <= 1; alignment and aliasing as rib_window_attn (x in
+ *          place of qc), parameters 4-byte aligned and not overlapping o.
+ * Always runs the 512-query tiled kernel, whatever the window size.
+ */
+rib_status rib_window_attn_lnq(const void* x, const float* gamma, const float* beta, const float* w,
+                               const float* bias, const void* kc, const void* v, const void* g, const float* qp,
+                               const float* kp, void* o, int B, int H, int W, int heads, int dh, int R, int window,
+                               float eps, rib_dtype dtype, void* stream);
 
 /*
  * Space-time windows for video (explainer section 6: the coordinate MLP takes
@@ -357,7 +387,7 @@ const char* rib_last_error(void);
 /* ABI version of this header (incremented on any incompatible change). */
 int rib_abi_version(void);
 
-#define RIB_ABI_VERSION 10
+#define RIB_ABI_VERSION 11
 
 #ifdef __cplusplus
 }

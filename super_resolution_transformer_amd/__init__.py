@@ -85,6 +85,8 @@ def lib(path: str | None = None):
     L.rib_encode_backward_noalloc.restype = i
     L.rib_ln_qkv.argtypes = [vp] * 9 + [i] * 4 + [ctypes.c_float, i, vp]
     L.rib_ln_qkv.restype = i
+    L.rib_window_attn_lnq.argtypes = [vp] * 11 + [i] * 7 + [ctypes.c_float, i, vp]
+    L.rib_window_attn_lnq.restype = i
     L.rib_encode3d.argtypes = [i] * 5 + [vp] * 4
     L.rib_encode3d.restype = i
     L.rib_window_attn3d.argtypes = [vp] * 7 + [i] * 10 + [vp]
@@ -398,8 +400,43 @@ def ln_qkv_into(x, gamma, beta, w, bias, q, k, v, xn=None, eps: float = 1e-5) ->
         raise ValueError("gamma, beta [C], w [C, 3C], bias [3C] expected")
     if not all(t.is_cuda and t.is_contiguous() for t in ws + (x, *maps)):
         raise ValueError("all tensors must be contiguous GPU tensors")
-    _check(lib().rib_ln_qkv(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(w), _ptr(bias), _ptr(q), _ptr(k), _ptr(v),
+    _check(lib().rib_ln_qkv(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(w), _ptr(bias),
+                            _ptr(q) if q is not None else None, _ptr(k), _ptr(v),
                             _ptr(xn) if xn is not None else None, B, H, W, C, float(eps), _dtype_code(x), _stream(x)))
+
+
+def window_attn_lnq(x, gamma, beta, w, bias, kc, v, g, qp, kp, heads: int, window: int, eps: float = 1e-5):
+    """window_attn with Qc = LayerNorm(x) W_q + b_q computed inside the attention (the Q columns of
+    rib_ln_qkv's w and bias); kc, v from ln_qkv_into(..., q=None, ...).  bf16 only."""
+    import torch
+    o = torch.empty_like(kc)
+    window_attn_lnq_into(x, gamma, beta, w, bias, kc, v, g, qp, kp, heads, window, o, eps)
+    return o
+
+
+def window_attn_lnq_into(x, gamma, beta, w, bias, kc, v, g, qp, kp, heads: int, window: int, o,
+                         eps: float = 1e-5) -> None:
+    import torch
+    ts = (x, kc, v, g, o)
+    if any(t.dim() != 4 for t in ts) or any(t.shape != x.shape for t in ts):
+        raise ValueError("x, kc, v, g, o must all be [B, H, W, C]")
+    if any(t.dtype != torch.bfloat16 for t in ts):
+        raise ValueError("x, kc, v, g, o must be bfloat16")
+    B, H, W, C = x.shape
+    ps = (gamma, beta, w, bias)
+    if any(t.dtype != torch.float32 for t in ps) or gamma.shape != (C,) or beta.shape != (C,) \
+            or w.shape != (C, 3 * C) or bias.shape != (3 * C,):
+        raise ValueError("gamma, beta float32 [C], w [C, 3C], bias [3C] expected")
+    if not all(t.is_cuda and t.is_contiguous() for t in ts + ps + (qp, kp)):
+        raise ValueError("all tensors must be contiguous GPU tensors")
+    if qp.dtype != torch.float32 or kp.dtype != torch.float32 or qp.shape != kp.shape or qp.dim() != 2 \
+            or qp.shape[0] != window * window:
+        raise ValueError("qp, kp must be float32 [window*window, R]")
+    if heads < 1 or C % heads:
+        raise ValueError("channel count must be a multiple of heads")
+    _check(lib().rib_window_attn_lnq(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(w), _ptr(bias), _ptr(kc), _ptr(v),
+                                     _ptr(g), _ptr(qp), _ptr(kp), _ptr(o), B, H, W, heads, C // heads, qp.shape[1],
+                                     window, float(eps), _dtype_code(x), _stream(x)))
 
 
 def weight_count3d(L: int, hidden: int, R: int) -> int:

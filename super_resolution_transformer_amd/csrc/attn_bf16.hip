@@ -516,15 +516,176 @@ __device__ __forceinline__ void pv_tile(const PhaseOps<DH, R>& ops, Regs<DH, R, 
       }
 }
 
-// One workgroup of the tiled kernel: logical = (window unit) * qblocks + query block.
+// ---- LayerNorm and the Q projection inside the tiled kernel's Q~ build ---------
+// (omica.com.cn explainer section 3.1: LayerNorm, then the attention's Q/K/V
+// projection).  For its 512 queries and head h a workgroup computes, per query token,
+//   xn = (x - mu) / sqrt(var + eps) * gamma + beta   (biased variance, fp32)
+//   q  = bf16(xn W_q[:, h dh .. h dh + dh) + bias_q)
+// with the affine part folded into the weights, so that the raw bf16 x goes into
+// the matrix core as it is:
+//   q_d = inv * (sum_c x_c W'_cd - mu * sum_c W'_cd) + b'_d,
+//   W'_cd = bf16(gamma_c W_cd),  b'_d = bias_d + sum_c beta_c W_cd,  inv = 1/sqrt(var + eps).
+// W'^T (dh rows, padded to 32), its row sums and b' are built in LDS once per
+// workgroup from coalesced reads of W; the product x W' runs as q^T = W'^T x^T on
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  mu and var come from fp32 sums
+// of x and x^2 (v_dot2_f32_bf16: the products of bf16 values are exact), with
+// var = E[x^2] - mu^2 -- a quarter of the vector work of a second pass over
+// (x - mu), which a 16-lane SIMD pays four cycles per wave64 instruction for.  Rounding: W' is rounded once,
+// x is exact, and the subtraction of mu * sum_c W'_cd cancels the token offset in
+// fp32; rib_ln_qkv instead rounds xn before its product, so the two paths' q may
+// differ by about one bf16 unit.
+struct LnqArgs {
+  const uint32_t* x;   // block input, [B][T][H][W][C] bf16
+  const float* gamma;  // [C]
+  const float* beta;   // [C]
+  const float* w;      // [C][3C], columns Q | K | V (only Q is read)
+  const float* bias;   // [3C]
+  float eps;
+};
+constexpr int LNQ_CP = 192;              // channels of the contraction (C <= 192, zero padded)
+constexpr int LNQ_WST = LNQ_CP / 2 + 4;  // dwords per staged W'^T row (16-byte pad)
+constexpr int LNQ_NG = 16;               // channel groups of the staging (512 threads = 16 x 32)
+// LDS of the fused prologue after the Q~ rows: W'^T rows, then per-group partial
+// sums (row sum of W', beta W) and the final (sum_c W'_cd, b'_d) pairs
+constexpr int LNQ_DW = 32 * LNQ_WST + LNQ_NG * 64 + 64;
+
+// thread (d = tid & 31, group tid >> 5) handles channel pairs c = 2 (group + 16 i)
+template <int DH>
+__device__ __forceinline__ void lnq_stage_w(uint32_t* wt, const LnqArgs& L, int C, int h) {
+  const int d = threadIdx.x & 31, grp = threadIdx.x >> 5;
+  const int oc = h * DH + d;
+  const long C3 = 3L * C;
+  float cs = 0.0f, bb = 0.0f;
+#pragma unroll
+  for (int cp = grp; cp < LNQ_CP / 2; cp += LNQ_NG) {
+    const int c = 2 * cp;
+    float a = 0.0f, b = 0.0f;
+    if (d < DH && c < C) {
+      const float w0 = L.w[c * C3 + oc];
+      a = round_bf16(w0 * L.gamma[c]);
+      bb = fmaf(L.beta[c], w0, bb);
+      if (c + 1 < C) {
+        const float w1 = L.w[(c + 1) * C3 + oc];
+        b = round_bf16(w1 * L.gamma[c + 1]);
+        bb = fmaf(L.beta[c + 1], w1, bb);
+      }
+    }
+    cs += a + b;
+    wt[d * LNQ_WST + cp] = pack_bf16(a, b);
+  }
+  float* part = reinterpret_cast<float*>(wt + 32 * LNQ_WST);
+  part[grp * 64 + d] = cs;
+  part[grp * 64 + 32 + d] = bb;
+}
+
+// after a barrier: threads 0..31 sum the groups' partials into (sum_c W'_cd, b'_d)
+template <int DH>
+__device__ __forceinline__ void lnq_reduce(uint32_t* wt, const LnqArgs& L, int h) {
+  const int d = threadIdx.x;
+  if (d >= 32) return;
+  const float* part = reinterpret_cast<const float*>(wt + 32 * LNQ_WST);
+  float cs = 0.0f, bb = 0.0f;
+#pragma unroll
+  for (int g = 0; g < LNQ_NG; ++g) {
+    cs += part[g * 64 + d];
+    bb += part[g * 64 + 32 + d];
+  }
+  float* fin = reinterpret_cast<float*>(wt + 32 * LNQ_WST + LNQ_NG * 64);
+  fin[2 * d] = cs;
+  fin[2 * d + 1] = d < DH ? bb + L.bias[h * DH + d] : 0.0f;
+}
+
+// Qc of the lane's query (block qb of this wave) into its Q~ row in LDS: dwords
+// R/2 + 4i + 2gh (+1) hold channels 8i + 4gh .. +3 (those below DH)
+constexpr int LNQ_KS = LNQ_CP / 16;  // 16-channel steps of the contraction
+
+// the lane's channels 16s + 8gh .. +7 of its token (s < ceil(C / 16); the words
+// past C are cleared by lnq_block)
+__device__ __forceinline__ void lnq_load(u32x4_t (&xw)[LNQ_KS], __amdgpu_buffer_rsrc_t rx, int tok_off, int C, int gh) {
+#pragma unroll
+  for (int s = 0; s < LNQ_KS; ++s) {
+    const int c0 = 16 * s + 8 * gh;
+    xw[s] = (u32x4_t){0u, 0u, 0u, 0u};
+    if (c0 < C) xw[s] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rx, 2u * (unsigned)(tok_off + c0), 0, 0));
+  }
+}
+
 template <int DH, int R>
+__device__ __forceinline__ void lnq_block(uint32_t* rows, const uint32_t* wt, const LnqArgs& L, u32x4_t (&xw)[LNQ_KS],
+                                          bool real, int row, int C, int l32, int gh, float sc) {
+  using S = Shape<DH, R>;
+  constexpr int KS = LNQ_KS;
+  const int ks = (C + 15) >> 4;  // 16-channel steps that hold channels
+  // clear the words past C (C is even, so words are whole; only the last step holds any)
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    if (16 * s + 16 > C) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (16 * s + 8 * gh + 2 * e >= C) xw[s][e] = 0u;
+    }
+  f32x16_t acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    if (s < ks) {
+      const u32x4_t wa = *reinterpret_cast<const u32x4_t*>(wt + l32 * LNQ_WST + 8 * s + 4 * gh);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, wa), __builtin_bit_cast(bf16x8_t, xw[s]),
+                                                    acc, 0, 0, 0);
+    }
+  // token statistics: sum x and sum x^2 as bf16 pair dot products (the products are
+  // exact in fp32), over the lane pair's channels; var = E[x^2] - mu^2
+  float sum = 0.0f, sq = 0.0f;
+  const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+    if (s < ks) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // through a scalar: hipcc lowers a bit_cast of an ext_vector element
+        // (xw[s][e] directly) to element 0 for every e
+        const uint32_t word = xw[s][e];
+        const bf16x2_t xv = __builtin_bit_cast(bf16x2_t, word);
+        sum = __builtin_amdgcn_fdot2_f32_bf16(xv, one, sum, false);
+        sq = __builtin_amdgcn_fdot2_f32_bf16(xv, xv, sq, false);
+      }
+    }
+  {
+    const LanePair ps = lane_pair(sum), pq = lane_pair(sq);
+    sum = ps.lo + ps.hi;
+    sq = pq.lo + pq.hi;
+  }
+  const float mu = sum / (float)C;
+  sq = fmaxf(sq / (float)C - mu * mu, 0.0f);
+  const float inv = 1.0f / sqrtf(sq + L.eps);
+  if (!real) return;  // padded query rows keep their zeros
+  const float* fin = reinterpret_cast<const float*>(wt + 32 * LNQ_WST + LNQ_NG * 64);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      const int d = 8 * i + 4 * gh + 2 * jp;
+      if (d < DH) {
+        const float4 f = *reinterpret_cast<const float4*>(fin + 2 * d);  // (sum W', b') of d, d + 1
+        const float q0 = round_bf16(fmaf(inv, acc[4 * i + 2 * jp] - mu * f.x, f.y));
+        const float q1 = round_bf16(fmaf(inv, acc[4 * i + 2 * jp + 1] - mu * f.z, f.w));
+        rows[row * S::KSTR + R / 2 + d / 2] = pack_bf16(q0 * sc, q1 * sc);
+      }
+    }
+}
+
+// One workgroup of the tiled kernel: logical = (window unit) * qblocks + query block.
+// FUSEQ: Qc is computed from the block input (LnqArgs) instead of read from qc.
+template <int DH, int R, bool FUSEQ = false>
 __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
                  const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                  const float* __restrict__ qp, const float* __restrict__ kp,
                  uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws, int total,
-                 long tstride, float* __restrict__ lse, int logical) {
+                 long tstride, float* __restrict__ lse, int logical, const LnqArgs* lnq = nullptr) {
   using S = Shape<DH, R>;
-  __shared__ __attribute__((aligned(16))) uint32_t lds[S::LDS_DW];
+  constexpr int LDS_N = FUSEQ && S::QS_DW + LNQ_DW > S::LDS_DW ? S::QS_DW + LNQ_DW : S::LDS_DW;
+  __shared__ __attribute__((aligned(16))) uint32_t lds[LDS_N];
 
   if (logical >= total) return;
   const int NW = wt * ws * ws;  // tokens of a full window
@@ -566,7 +727,8 @@ __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc,
       xp[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rqp, (unsigned)(n * R + 4 * k) * 4u, 0, 0));
 #pragma unroll
     for (int k = 0; k < NQC; ++k)
-      xc[k] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rqc, 2u * (unsigned)off + 16u * k, 0, 0));
+      xc[k] = FUSEQ ? (u32x4_t){0u, 0u, 0u, 0u}
+                    : __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rqc, 2u * (unsigned)off + 16u * k, 0, 0));
     uint32_t row[S::ROWDW];
 #pragma unroll
     for (int w = 0; w < S::ROWDW; ++w) {
@@ -577,7 +739,7 @@ __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc,
       } else if (w < R / 2 + DH / 2) {
         const int q = w - R / 2;
         const uint32_t x = xc[q / 4][q % 4];
-        val = pack_bf16(bf16_lo(x) * sc, bf16_hi(x) * sc);
+        val = FUSEQ ? 0u : pack_bf16(bf16_lo(x) * sc, bf16_hi(x) * sc);  // fused: written below
       } else if (w == S::CONSTDW) {
         val = 0xC0E00000u;  // (-m_hat = 0, -OFF = -7)
       } else {
@@ -589,6 +751,31 @@ __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc,
 #pragma unroll
     for (int w = 0; w < S::ROWDW; w += 4)
       *reinterpret_cast<u32x4_t*>(dst + w) = (u32x4_t){row[w], row[w + 1], row[w + 2], row[w + 3]};
+  }
+  if constexpr (FUSEQ) {
+    // Qc = bf16(LN(x) W_q + b_q) of the wave's own rows (same wave as the row writes above)
+    uint32_t* wtl = lds + S::QS_DW;
+    lnq_stage_w<DH>(wtl, *lnq, G.C, G.h);
+    __syncthreads();
+    lnq_reduce<DH>(wtl, *lnq, G.h);
+    // both query blocks' x rows are requested before either is used
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(lnq->x), (short)0, (int)map_bytes, (int)RSRC_WORD3);
+    u32x4_t xw[2][LNQ_KS];
+    bool real[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int r = q0 + wave * QW + qb * 32 + l32;
+      real[qb] = r < G.n_real;
+      int off, n;
+      locate<DH>(G, real[qb] ? r : G.n_real - 1, off, n);
+      lnq_load(xw[qb], rx, off - G.h * DH, G.C, gh);
+    }
+    __syncthreads();
+    const float scq = LOG2E / sqrtf((float)DH);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+      lnq_block<DH, R>(lds, wtl, *lnq, xw[qb], real[qb], wave * QW + qb * 32 + l32, G.C, l32, gh, scq);
   }
   __syncthreads();
   Regs<DH, R> rg;
@@ -1226,6 +1413,20 @@ __device__ __forceinline__ int window_unit(int bid, int heads) {
   return (k * 8 + xcd) * heads + (slot - k * heads);
 }
 
+// the tiled kernel with LayerNorm and the Q projection in its Q~ build (qc unused)
+template <int DH, int R>
+__global__ void __launch_bounds__(QB, 1)
+attn_bf16_lnq_kernel(const uint32_t* __restrict__ kc, const uint32_t* __restrict__ v,
+                     const uint32_t* __restrict__ g, const float* __restrict__ qp, const float* __restrict__ kp,
+                     uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws, int total,
+                     long tstride, float* __restrict__ lse, int whole_windows, const LnqArgs L) {
+  const int qblocks = (wt * ws * ws + QB - 1) / QB;
+  attn_tiled_body<DH, R, true>(nullptr, kc, v, g, qp, kp, o, B, T, H, W, heads, wt, ws, total, tstride, lse,
+                               whole_windows ? window_block(blockIdx.x, heads * qblocks)
+                                             : interleave_logical(blockIdx.x, qblocks),
+                               &L);
+}
+
 // whole_windows: the window count is a multiple of 8, so whole windows (every head and query
 // block) can be dealt to the XCDs evenly (window_block); else window units are (interleave_logical)
 template <int DH, int R>
@@ -1478,6 +1679,23 @@ hipError_t launch_attn_bf16_multi(const AttnArgs* calls, int n, hipStream_t stre
   if (dh == 32 && R == 16) return launch_multi_variant<32, 16>(calls, n, stream);
   if (dh == 16 && R == 32) return launch_multi_variant<16, 32>(calls, n, stream);
   if (dh == 30 && R == 32) return launch_multi_variant<30, 32>(calls, n, stream);
+  return hipErrorInvalidValue;
+}
+
+template <int DH, int R>
+hipError_t launch_lnq_variant(const AttnArgs& a, const LnqArgs& L, hipStream_t stream) {
+  const int units = call_units(a), qb = kind_qblocks(a, TILED), grid = kind_grid(a, TILED);
+  hipLaunchKernelGGL((attn_bf16_lnq_kernel<DH, R>), dim3(grid), dim3(QB), 0, stream, (const uint32_t*)a.kc,
+                     (const uint32_t*)a.v, (const uint32_t*)a.g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.T, a.H, a.W,
+                     a.heads, a.wt, a.ws, units * qb, a.tstride, a.lse, (units / a.heads) % 8 == 0 ? 1 : 0, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16_lnq(const AttnArgs& a, const void* x, const float* gamma, const float* beta,
+                                const float* w, const float* bias, float eps, hipStream_t stream) {
+  const LnqArgs L{(const uint32_t*)x, gamma, beta, w, bias, eps};
+  if (a.dh == 30 && a.R == 16) return launch_lnq_variant<30, 16>(a, L, stream);
+  if (a.dh == 16 && a.R == 16) return launch_lnq_variant<16, 16>(a, L, stream);
   return hipErrorInvalidValue;
 }
 

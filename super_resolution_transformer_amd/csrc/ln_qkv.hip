@@ -268,7 +268,7 @@ ln_qkv_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ gam
       for (int j = tid; j < ndw; j += LQ_NT) dst[gdw + j] = src[j];
       return trips(ndw);
     };
-    pending_stores = copy_part(q, s_o);
+    pending_stores = q ? copy_part(q, s_o) : 0;  // q is null when the caller fuses Q into the attention
     pending_stores += copy_part(k, s_o + LQ_TT * C / 2);
     pending_stores += copy_part(v, s_o + LQ_TT * C);
     if (xn) pending_stores += copy_part(xn, xcur);
@@ -336,7 +336,7 @@ ln_qkv_plain_kernel(const T* __restrict__ x, const float* __restrict__ gamma, co
     float acc = bias[o];
     for (int c = 0; c < C; ++c) acc = fmaf(s_xn[tt][c], w[(long)c * C3 + o], acc);
     T* dst = o < C ? q : (o < 2 * C ? k : v);
-    lq_st(dst, (t0 + tt) * C + o % C, acc);
+    if (dst) lq_st(dst, (t0 + tt) * C + o % C, acc);  // q may be null
   }
 }
 

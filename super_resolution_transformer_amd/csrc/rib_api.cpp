@@ -155,6 +155,32 @@ rib_status rib_window_attn(const void* qc, const void* kc, const void* v, const 
                      window, dtype, stream);
 }
 
+rib_status rib_window_attn_lnq(const void* x, const float* gamma, const float* beta, const float* w,
+                               const float* bias, const void* kc, const void* v, const void* g, const float* qp,
+                               const float* kp, void* o, int B, int H, int W, int heads, int dh, int R, int window,
+                               float eps, rib_dtype dtype, void* stream) {
+  const char* fn = "rib_window_attn_lnq";
+  if (!gamma || !beta || !w || !bias) return fail(RIB_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (dtype != RIB_BF16) return fail(RIB_ERR_UNSUPPORTED, "%s: bf16 maps only", fn);
+  if (!(eps >= 0.0f) || eps > 1.0f) return fail(RIB_ERR_INVALID_ARG, "%s: eps must be in [0, 1]", fn);
+  if (!((dh == 30 && R == 16) || (dh == 16 && R == 16)))
+    return fail(RIB_ERR_UNSUPPORTED, "%s: (dh, R) must be (30, 16) or (16, 16) (got %d, %d)", fn, dh, R);
+  if ((long)heads * dh > 192) return fail(RIB_ERR_UNSUPPORTED, "%s: heads * dh must be <= 192", fn);
+  rib::AttnArgs a{};
+  const rib_status st = check_attn(fn, false, x, kc, v, g, qp, kp, o, nullptr, B, 1, H, W, heads, dh, R, 1,
+                                   window, dtype, a);
+  if (st != RIB_OK) return st;
+  const void* par[] = {gamma, beta, w, bias};
+  for (const void* p : par)
+    if (!aligned(p, 4)) return fail(RIB_ERR_INVALID_ARG, "%s: parameter pointers must be 4-byte aligned", fn);
+  const size_t C = (size_t)heads * dh;
+  const size_t nb = (size_t)B * H * W * C * 2;
+  const size_t psz[] = {4 * C, 4 * C, 12 * C * C, 12 * C};
+  for (int i = 0; i < 4; ++i)
+    if (overlap(o, nb, par[i], psz[i])) return fail(RIB_ERR_INVALID_ARG, "%s: output overlaps a parameter", fn);
+  return hip_status(rib::launch_attn_bf16_lnq(a, x, gamma, beta, w, bias, eps, (hipStream_t)stream), fn);
+}
+
 rib_status rib_window_attn_train(const void* qc, const void* kc, const void* v, const void* g,
                                  const float* qp, const float* kp, void* o, float* lse, int B, int H, int W,
                                  int heads, int dh, int R, int window, rib_dtype dtype, void* stream) {
@@ -444,7 +470,7 @@ rib_status rib_ln_qkv(const void* x, const float* gamma, const float* beta, cons
                       void* q, void* k, void* v, void* xn, int B, int H, int W, int C, float eps, rib_dtype dtype,
                       void* stream) {
   const char* fn = "rib_ln_qkv";
-  if (!x || !gamma || !beta || !w || !bias || !q || !k || !v) return fail(RIB_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (!x || !gamma || !beta || !w || !bias || !k || !v) return fail(RIB_ERR_INVALID_ARG, "%s: null pointer", fn);
   if (B < 1 || H < 1 || W < 1 || C < 1)
     return fail(RIB_ERR_INVALID_ARG, "%s: B, H, W, C must be >= 1 (got %d, %d, %d, %d)", fn, B, H, W, C);
   if (dtype != RIB_F32 && dtype != RIB_BF16) return fail(RIB_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);

@@ -25,6 +25,11 @@ hipError_t launch_encode(int ws, int L, int hidden, int R, const float* w, float
 hipError_t launch_encode3d(int wt, int ws, int L, int hidden, int R, const float* w, float* qp, float* kp,
                            hipStream_t stream);
 
+// tiled bf16 kernel with LayerNorm + the Q projection of x fused into its Q~ build
+// ((dh, R) in {(30, 16), (16, 16)}, C = heads * dh <= 192); a.qc is not read
+hipError_t launch_attn_bf16_lnq(const AttnArgs& a, const void* x, const float* gamma, const float* beta,
+                                const float* w, const float* bias, float eps, hipStream_t stream);
+
 // fp32 path: any dh <= 64, R <= 64.
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 

@@ -22,7 +22,7 @@ def test_header_declares_the_boundary():
         "rib_encode", "rib_window_attn", "rib_attn_supported", "rib_last_error", "rib_abi_version",
         "rib_cla_gate", "rib_window_attn_heads", "rib_window_attn_train", "rib_window_attn_backward", "rib_window_attn_backward_workspace",
         "rib_encode_backward", "rib_encode_backward_workspace", "rib_encode_backward_noalloc", "rib_ln_qkv", "rib_encode3d",
-        "rib_window_attn3d", "rib_window_attn_multi", "rib_window_attn_heads_train",
+        "rib_window_attn3d", "rib_window_attn_multi", "rib_window_attn_heads_train", "rib_window_attn_lnq",
         "rib_window_attn_heads_backward"}
 
 
@@ -304,6 +304,32 @@ def test_ln_qkv_validation(L):
     assert "overlap" in L.rib_last_error().decode()
     assert lnq(L, P[:5] + [P[5], P[5], P[7], None]) == rib.RIB_ERR_INVALID_ARG  # q == k
     assert lnq(L, P[:8] + [P[3]]) == rib.RIB_ERR_INVALID_ARG                     # xn == w
+
+
+@fake
+def test_window_attn_lnq_validation(L):
+    X = [ctypes.c_void_p(0x10000000 + i * 64 * MB) for i in range(11)]   # x gamma beta w bias kc v g qp kp o
+
+    def call(ptrs=None, B=1, H=8, W=8, heads=6, dh=30, R=16, window=8, eps=1e-5, dtype=rib.RIB_BF16):
+        return L.rib_window_attn_lnq(*(ptrs or X), B, H, W, heads, dh, R, window, ctypes.c_float(eps), dtype, None)
+    assert call(X[:1] + [None] + X[2:]) == rib.RIB_ERR_INVALID_ARG                  # gamma missing
+    assert "rib_window_attn_lnq" in L.rib_last_error().decode()
+    assert call([None] + X[1:]) == rib.RIB_ERR_INVALID_ARG                          # x missing
+    assert call(X[:10] + [None]) == rib.RIB_ERR_INVALID_ARG                         # o missing
+    assert call(dtype=rib.RIB_F32) == rib.RIB_ERR_UNSUPPORTED
+    assert call(dh=8, R=8) == rib.RIB_ERR_UNSUPPORTED
+    assert call(heads=7) == rib.RIB_ERR_UNSUPPORTED                                 # C = 210 > 192
+    assert call(eps=-1.0) == rib.RIB_ERR_INVALID_ARG
+    assert call(eps=float("nan")) == rib.RIB_ERR_INVALID_ARG
+    assert call(window=1) == rib.RIB_ERR_INVALID_ARG
+    assert call(X[:1] + [ctypes.c_void_p(X[1].value + 2)] + X[2:]) == rib.RIB_ERR_INVALID_ARG
+    assert "aligned" in L.rib_last_error().decode()
+    assert call(X[:10] + [X[3]]) == rib.RIB_ERR_INVALID_ARG                         # o == w
+    assert "overlap" in L.rib_last_error().decode()
+    assert call(X[:10] + [ctypes.c_void_p(X[3].value + 12 * 180 * 180 - 64)]) == rib.RIB_ERR_INVALID_ARG  # o in w's tail
+    assert call(X[:10] + [X[0]]) == rib.RIB_ERR_INVALID_ARG                         # o == x
+    # rib_ln_qkv without q still needs k and v
+    assert lnq(L, P[:5] + [None, None, P[7], None]) == rib.RIB_ERR_INVALID_ARG
 
 
 @fake
