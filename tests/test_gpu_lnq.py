@@ -101,3 +101,51 @@ def test_fused_q_locality(torch):
     out = rib.window_attn_lnq(x2, *prm, k, v, g, qp, kp, heads, ws)
     changed = (out.view(torch.int16) != base.view(torch.int16)).any(dim=-1).cpu().numpy()
     assert changed[0, 20, 37] and changed.sum() == 1   # only that query's own row: Q is per token
+
+
+@pytest.mark.parametrize("B,H,W", [(32, 96, 96), (1, 360, 640)], ids=["32x96x96", "1x360x640"])
+def test_fused_q_full_size(torch, B, H, W):
+    """The 96x96-window workloads at full size, in the launch bench.py times (C = 180, 6 heads):
+    - the whole output against the unfused GPU path (rib_ln_qkv + rib_window_attn, itself compared
+      with the oracle over whole outputs at these sizes) at 2e-2;
+    - sampled rows of two windows (the first window of the first image, the bottom-right window
+      of the last image: full, or ragged at 72x64) against the oracle chain, run on the window's
+      own region of x (LayerNorm and the projection act per token, so the region is exact)."""
+    heads, dh, ws = 6, 30, 96
+    C = heads * dh
+    note(f"lnq full size B={B} H={H} W={W}")
+    lp = synthetic.make_ln_qkv_problem(B, H, W, C, "bf16", seed=11)
+    gp = synthetic.make_gate_problem(B, H, W, C, "bf16", seed=12)     # its X serves as the gate map G
+    ap = synthetic.make_problem(1, 8, 8, heads, dh, 16, dtype="bf16", seed=13)
+    x = torch.from_numpy(lp.x_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    g = torch.from_numpy(gp.x_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    prm = [torch.from_numpy(np.ascontiguousarray(a)).cuda() for a in (lp.gamma, lp.beta, lp.w, lp.bias)]
+    qp, kp = rib.encode(ws, ap.L, ap.hidden, ap.R, torch.from_numpy(ap.weights).cuda())
+    k, v = torch.empty_like(x), torch.empty_like(x)
+    rib.ln_qkv_into(x, *prm, None, k, v)
+    got = rib.window_attn_lnq(x, *prm, k, v, g, qp, kp, heads, ws)
+    q2 = torch.empty_like(x)
+    rib.ln_qkv_into(x, *prm, q2, k, v)
+    ref = rib.window_attn(q2, k, v, g, qp, kp, heads, ws)
+    torch.cuda.synchronize()
+    err_gpu = float((got.float() - ref.float()).abs().max())
+    note(f"  whole output vs unfused GPU path: max|err| {err_gpu:.3g}")
+    assert err_gpu <= 2e-2
+    got = got.float().cpu().numpy().astype(np.float64)
+    del x, g, k, v, q2, ref
+    torch.cuda.empty_cache()
+    oq, ok = oracle.encode(ws, ap.L, ap.hidden, ap.R, ap.weights)
+    rng = np.random.default_rng(B + H)
+    for b, wy, wx in ((0, 0, 0), (B - 1, (H - 1) // ws, (W - 1) // ws)):
+        y0, x0 = wy * ws, wx * ws
+        y1, x1 = min(H, y0 + ws), min(W, x0 + ws)
+        reg = lambda a: np.ascontiguousarray(a[b:b + 1, y0:y1, x0:x1])
+        q, kk, vv = (synthetic.round_bf16(a.astype(np.float32))[1]
+                     for a in oracle.ln_qkv(reg(lp.x), lp.gamma, lp.beta, lp.w, lp.bias))
+        hh, ww = y1 - y0, x1 - x0
+        ty = np.concatenate([[0, 0, hh - 1, hh - 1], rng.integers(0, hh, 60)])
+        tx = np.concatenate([[0, ww - 1, 0, ww - 1], rng.integers(0, ww, 60)])
+        want = oracle.window_attn_rows(q, kk, vv, reg(gp.x), oq, ok, heads, ws, np.zeros_like(ty), ty, tx)
+        err = float(np.abs(got[b, y0 + ty, x0 + tx] - want).max())
+        note(f"  image {b} window ({wy},{wx}) {hh}x{ww}: 64 rows, max|err| vs oracle {err:.3g}")
+        assert err <= 2e-2
