@@ -1170,29 +1170,28 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
     PhaseOps<DH, R> ops;
     f32x16_t Sacc[1][2];
     uint32_t P[1][2][8];
-    // First pass: the exact row maximum of the first key tile, then the other tiles
-    // exponentiated against it without a check, with the offset OFF_FAST = 64: p =
-    // 2^(s - m_hat - 64).  That is exact (up to rounding) unless a score exceeds m_hat by
-    // more than 64 + 106 (below that, p and the fp32 sums over at most 256 keys with
-    // |V| < 2^14 stay finite); keys more than 62 below m_hat, itself at most the row
-    // maximum, may flush to zero, and each weighs less than 2^-62 of the row.  A block whose
-    // row sum or output ends
-    // non-finite repeats its tiles with the checked loop: offset OFF, an OR over the packed
-    // P of every tile, and a rescale whenever a score exceeds the reference by more than 8.
+    // First pass: every tile exponentiated against the fixed reference m_hat = 0 with the
+    // offset OFF_FAST = 64, p = 2^(s - 64), without a check (s: score in base-2 units; no
+    // row maximum is taken).  bf16 P keeps fp32's exponent range, so the pass is exact up
+    // to rounding while p and the fp32 sums stay finite and the row's largest p is a
+    // normal number.  Its result is kept when the row sum l and the output are finite and
+    // l >= 2^-86; since l <= 256 * 2^(s_max - 64), that means s_max >= -30, so keys that
+    // flush to zero (more than 62 below 0) weigh less than 2^-32 of the row's largest.
+    // Rows with s_max >= -22 always pass the test; finite sums hold for s_max up to about
+    // 170 with |V| < 2^14.  A block that fails repeats its tiles with the checked loop:
+    // exact maximum on the first tile, offset OFF, an OR over the packed P of every tile,
+    // and a rescale whenever a score exceeds the reference by more than 8.
     for (int x = 0; x < ntiles; ++x) {
       read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
       read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
       qk_tile<DH, R>(ops, rg, Sacc);
-      if (x == 0)
-        rescale_tile<DH, R>(rg, Sacc, P, true, gh, OFF_FAST);
-      else
-        (void)exp_tile_fast(Sacc, P);
+      (void)exp_tile_fast(Sacc, P);
       pv_tile<DH, R>(ops, rg, P);
     }
     float off_used = OFF_FAST;
     {
       float t = row_sum(rg, 0);
-      int bad = !(t > 0.0f);
+      int bad = !(t >= 0x1p-86f);
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll

@@ -152,6 +152,30 @@ def make_spike_problem(B: int, H: int, W: int, heads: int, dh: int, R: int, ws: 
     return p
 
 
+def make_low_score_problem(B: int, H: int, W: int, heads: int, dh: int, R: int, a: float,
+                           dtype: str = "bf16", seed: int = 0) -> Problem:
+    """A problem whose scores all lie far below zero.
+
+    Per head, with u a random unit vector: keys kc = u + 0.05 z and queries qc = -a u + 0.25 z'
+    (z, z' ~ N(0, 1) per element), so every query-key score is about -a / sqrt(dh) (natural
+    units; times log2(e) in base 2), spread by a few percent of that, plus the positional bias."""
+    p = make_problem(B, H, W, heads, dh, R, dtype=dtype, seed=seed)
+    rng = np.random.default_rng(seed + 7)
+    qc = np.empty((B, H, W, heads * dh), np.float32)
+    kc = np.empty_like(qc)
+    for h in range(heads):
+        u = rng.standard_normal(dh)
+        u /= np.linalg.norm(u)
+        sl = slice(h * dh, (h + 1) * dh)
+        kc[..., sl] = u + 0.05 * rng.standard_normal((B, H, W, dh))
+        qc[..., sl] = -a * u + 0.25 * rng.standard_normal((B, H, W, dh))
+    p.qc, p.kc = qc, kc
+    if dtype == "bf16":
+        p.bits["qc"], p.qc = round_bf16(qc)
+        p.bits["kc"], p.kc = round_bf16(kc)
+    return p
+
+
 def config_problem(idx: int, batch: int | None = None) -> Problem:
     """Inputs of one of the five workloads (``batch`` overrides B, e.g. for a CPU sample)."""
     c = CONFIGS[idx]

@@ -1,16 +1,20 @@
-"""GPU parity for scores far above the first key tile's maximum.
+"""GPU parity for scores far above, or all far below, the reference of the softmax.
 
-Every bf16 kernel takes the exact row maximum on the first key tile.  The chunked and tiled
-kernels (windows of more than 256 tokens) then check every later tile: the packed bf16 P words
-are OR-reduced, and a value of 2 or more (the maximum grew by more than 8 base-2 units) sends the
-wave through an exact re-maximum and rescale before P is used.  The whole-window kernel (at most
-256 tokens) exponentiates the later tiles against the first tile's maximum without a check, with
-an offset of 64 base-2 units; a block whose row sum or output ends non-finite repeats its tiles
-with the checked loop.  These inputs place two keys in later tiles whose score, for half of the queries,
-exceeds everything else by about 84 base-2 units (the checked rescale in the chunked and tiled
-kernels; the unchecked pass holds it in the whole-window kernel, with p up to ~2^20) or by about
-250 (p overflows: the chunked and tiled kernels rescale, the whole-window kernel's checked re-run
-takes over).
+The chunked and tiled kernels (windows of more than 256 tokens) take the exact row maximum on the
+first key tile and then check every later tile: the packed bf16 P words are OR-reduced, and a
+value of 2 or more (the maximum grew by more than 8 base-2 units) sends the wave through an exact
+re-maximum and rescale before P is used.  The whole-window kernel (at most 256 tokens) takes no
+maximum in its first pass: every tile is exponentiated against the fixed reference 0 with an
+offset of 64 base-2 units; a block whose row sum or output ends non-finite, or whose row sum is
+below 2^-86, repeats its tiles with the checked loop.  The first set of inputs places two keys in
+later tiles whose score, for half of the queries, exceeds everything else by about 84 base-2 units
+(the checked rescale in the chunked and tiled kernels; the first pass holds it in the whole-window
+kernel, with p up to ~2^20) or by about 250 (p overflows: the chunked and tiled kernels rescale,
+the whole-window kernel's checked re-run takes over).
+A second set places every score far below zero (about -60 and -20 base-2 units): at -60 the
+whole-window kernel's row sums fall below 2^-86 and the checked re-run takes over, at -20 the
+first pass is kept; the chunked and tiled kernels take the exact maximum of their first tile
+either way.
 Outputs are compared with the oracle over the whole map at the forward's bars (max abs error
 2e-2 for bf16; 1e-5 for fp32 plus the rounding of two spike scores of ~175, derived in the
 test); the row log-sum-exp at a bound derived from the rounding of the score operands.
@@ -95,4 +99,48 @@ def test_score_jump_matches_oracle(torch, case):
     bound = TOL[dtype] + (2.0 ** -7 if dtype == "bf16" else (dh + R) * 2.0 ** -24) * S
     lerr = float(np.abs(lse.cpu().numpy() - ref).max())
     note(f"  lse max|err| {lerr:.3g}  max|lse| {float(np.abs(ref).max()):.3g}  bound {bound:.3g}")
+    assert lerr <= bound
+
+
+LOW = [
+    # B, H, W, heads, dh, R, ws, target base-2 score, dtype
+    (2, 37, 40, 2, 30, 16, 16, -60.0, "bf16"),   # whole-window kernel: the checked re-run
+    (2, 37, 40, 2, 30, 16, 16, -20.0, "bf16"),   # whole-window kernel: the first pass is kept
+    (1, 40, 41, 3, 16, 16, 16, -60.0, "bf16"),   # whole-window kernel, dh = 16
+    (1, 40, 33, 2, 16, 16, 32, -60.0, "bf16"),   # chunked kernel
+    (1, 96, 100, 1, 30, 16, 96, -60.0, "bf16"),  # tiled kernel
+    (1, 37, 40, 2, 30, 16, 16, -60.0, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", LOW, ids=lambda c: "H{1}W{2}h{3}d{4}ws{6}s{7:g}-{8}".format(*c))
+def test_scores_far_below_zero_match_oracle(torch, case):
+    B, H, W, heads, dh, R, ws, target, dtype = case
+    note(f"low scores {case}")
+    a = -target * np.sqrt(dh) / np.log2(np.e)
+    p = synthetic.make_low_score_problem(B, H, W, heads, dh, R, a, dtype=dtype, seed=H + W + ws)
+    maps = [dev(torch, p, nm) for nm in ("qc", "kc", "v", "g")]
+    w = torch.from_numpy(p.weights).cuda()
+    qp, kp = rib.encode(ws, p.L, p.hidden, p.R, w)
+    o_plain = rib.window_attn(*maps, qp, kp, heads, ws)
+    o, lse = rib.window_attn_train(*maps, qp, kp, heads, ws)
+    torch.cuda.synchronize()
+    oq, ok = oracle.encode(ws, p.L, p.hidden, p.R, p.weights)
+    want = oracle.window_attn(p.qc, p.kc, p.v, p.g, oq, ok, heads, ws)
+    got = o.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    ref = oracle.window_lse(p.qc, p.kc, oq, ok, heads, ws)
+    note(f"  lse range [{float(ref.min()):.3g}, {float(ref.max()):.3g}] (natural units)")
+    err = float(np.abs(got - want).max())
+    note(f"  O max|err| {err:.3g}  max|O| {float(np.abs(want).max()):.3g}")
+    assert err <= TOL[dtype]
+    same = torch.equal(o.view(torch.int16), o_plain.view(torch.int16)) if dtype == "bf16" else torch.equal(o, o_plain)
+    assert same, "train forward and plain forward differ"
+    # lse: S bounds the sum of |products| of a score (Cauchy-Schwarz per part)
+    qn = np.linalg.norm(p.qc.reshape(-1, heads, dh), axis=-1).max()
+    kn = np.linalg.norm(p.kc.reshape(-1, heads, dh), axis=-1).max()
+    S = float(qn * kn) / np.sqrt(dh) + float(np.linalg.norm(oq, axis=1).max() * np.linalg.norm(ok, axis=1).max()) / np.sqrt(R)
+    bound = TOL[dtype] + (2.0 ** -7 if dtype == "bf16" else (dh + R) * 2.0 ** -24) * S
+    lerr = float(np.abs(lse.cpu().numpy() - ref).max())
+    note(f"  lse max|err| {lerr:.3g}  bound {bound:.3g}")
     assert lerr <= bound
