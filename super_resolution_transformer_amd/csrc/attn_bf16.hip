@@ -945,7 +945,7 @@ __device__ __forceinline__ void attn_tiled_body(const uint32_t* __restrict__ qc,
     const int r = q0 + wave * QW + qb * 32 + l32;
     const float lsum = row_sum(rg, qb);
     if (r >= G.n_real) continue;
-    const float inv = 1.0f / lsum;
+    const float inv = rcp_approx(lsum);
     const int off = goff[qb];
     if (lse) lse[(off - G.h * DH) / G.C * heads + G.h] = (rg.mhat[qb] + OFF + __log2f(lsum)) * LN2;
 #pragma unroll
@@ -1222,7 +1222,7 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
     const int r = wave * QW + qb * 32 + l32;
     const float lsum = row_sum(rg, 0);
     if (r < G.n_real) {
-      const float inv = 1.0f / lsum;
+      const float inv = rcp_approx(lsum);
       if (lse) lse[(offq - G.h * DH) / G.C * heads + G.h] = (rg.mhat[0] + off_used + __log2f(lsum)) * LN2;
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt)
@@ -1356,7 +1356,7 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
     if (r >= G.n_real) return;
     int off, n;
     locate<DH>(G, r, off, n);
-    const float inv = 1.0f / lsum;
+    const float inv = rcp_approx(lsum);
     if (lse) lse[(off - G.h * DH) / G.C * heads + G.h] = (rg.mhat[0] + OFF + __log2f(lsum)) * LN2;
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)

@@ -47,7 +47,13 @@ __device__ __forceinline__ uint32_t lane_xor1(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
 }
 
-__device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// 1/x on the reciprocal unit (v_rcp_f32, about 1 ulp) instead of the correctly rounded
+// division this library is built with (about ten instructions): for the bf16 epilogues,
+// which round their results to 8 significant bits.  x must be a normal number.
+__device__ __forceinline__ float rcp_approx(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// logistic sigmoid for the bf16 epilogues: 1 + e^-z >= 1, so the reciprocal is in (0, 1]
+__device__ __forceinline__ float sigmoidf(float z) { return rcp_approx(1.0f + __expf(-z)); }
 
 // Map workgroup i of a launch of 8*per workgroups so that consecutive logical
 // blocks run on the same XCD (the dispatcher sends block i to XCD i % 8).
