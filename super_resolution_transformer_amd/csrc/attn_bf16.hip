@@ -1251,10 +1251,17 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
 // blocks' score products, and runs block 0's exponentials while block 1's
 // scores are still on the matrix core.  (Two values the epilogue needs spill
 // to scratch, once per wave, outside the loop.)
-// The softmax is the tiled kernel's checked loop: exact maximum on the first
-// tile, offset OFF, an OR over the packed P of every later tile and a rescale
-// when the maximum grew by more than 8.  There is no hand-off between waves:
-// three workgroups share a CU, and while one stages a chunk the others compute.
+// The softmax first runs unchecked, as the whole-window kernel's first pass
+// does: every tile against the fixed reference 0 with the offset OFF_FAST.  A
+// 32-query block whose row sum ends below 2^-80 (so its maximum is below -28
+// base-2 units: l <= 4096 * 2^(s_max - 64)) or whose row sum or output is not
+// finite is computed again, all chunks staged again for the whole workgroup,
+// with the tiled kernel's checked loop: exact maximum on the first tile, offset
+// OFF, an OR over the packed P of every later tile and a rescale when the
+// maximum grew by more than 8.  Kept results lose only keys more than 62 below
+// 0, each under 2^-34 of the row's largest.  There is no hand-off between
+// waves: three workgroups share a CU, and while one stages a chunk the others
+// compute.
 template <int DH, int R>
 __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
                        const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
@@ -1291,7 +1298,7 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
     locate<DH>(G, real ? r : G.n_real - 1, off, n);
 #pragma unroll
     for (int c = 0; c < S::KC; ++c)
-      rg.qt[0][c] = qrow_group<DH, R>(8 * c + 4 * gh, off, n, real, mr.qp, mr.qc, sp, sc, 0xC0E00000u);  // (0, -OFF)
+      rg.qt[0][c] = qrow_group<DH, R>(8 * c + 4 * gh, off, n, real, mr.qp, mr.qc, sp, sc, 0xC2800000u);  // (0, -OFF_FAST)
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
@@ -1320,44 +1327,102 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
     }
   };
   const int nchunks = (G.n_real + SQ - 1) / SQ;
-  for (int ch = 0; ch < nchunks; ++ch) {
-    if (ch > 0) __syncthreads();  // every wave is done with the previous chunk's tiles
-    stage_key<DH, R>(G, lds, ch * SQ + tid, kc, v, kp, map_elems, wt * ws * ws);
-    __syncthreads();
-    const int left = G.n_real - ch * SQ;
-    const int nt = left >= SQ ? SNT : (left + KT - 1) / KT;
+  // stage each chunk of the window's keys (the whole workgroup), then run `tiles` on it
+  auto over_chunks = [&](auto&& tiles) {
+    for (int ch = 0; ch < nchunks; ++ch) {
+      if (ch > 0) __syncthreads();  // every wave is done with the previous chunk's tiles
+      stage_key<DH, R>(G, lds, ch * SQ + tid, kc, v, kp, map_elems, wt * ws * ws);
+      __syncthreads();
+      const int left = G.n_real - ch * SQ;
+      tiles(ch, left >= SQ ? SNT : (left + KT - 1) / KT);
+    }
+  };
+  // unchecked pass; both blocks: one operand read per tile, block 1's scores issue on
+  // the matrix core while block 0's exponentials run
+  over_chunks([&](int, int nt) {
     if (act1) {
-      // both blocks: one operand read per tile; block 1's scores issue on the matrix core
-      // while block 0's exponentials run
       f32x16_t Sb[1][2];
       uint32_t Pb[1][2][8];
       for (int x = 0; x < nt; ++x) {
         read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
         read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
-        const bool first = ch == 0 && x == 0;
         qk_tile<DH, R>(ops, rg0, Sacc);
         qk_tile<DH, R>(ops, rg1, Sb);
-        const uint32_t or0 = exp_tile_fast(Sacc, P);
-        if (__builtin_amdgcn_ballot_w64(first || (or0 & 0x40004000u))) rescale_tile<DH, R>(rg0, Sacc, P, first, gh);
+        (void)exp_tile_fast(Sacc, P);
         pv_tile<DH, R>(ops, rg0, P);
-        const uint32_t or1 = exp_tile_fast(Sb, Pb);
-        if (__builtin_amdgcn_ballot_w64(first || (or1 & 0x40004000u))) rescale_tile<DH, R>(rg1, Sb, Pb, first, gh);
+        (void)exp_tile_fast(Sb, Pb);
         pv_tile<DH, R>(ops, rg1, Pb);
       }
     } else if (act0) {
-      run_tiles(rg0, nt, ch == 0);
+      for (int x = 0; x < nt; ++x) {
+        read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
+        read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
+        qk_tile<DH, R>(ops, rg0, Sacc);
+        (void)exp_tile_fast(Sacc, P);
+        pv_tile<DH, R>(ops, rg0, P);
+      }
     }
+  });
+  // a block fails if its row sum is below 2^-80 or its row sum or output is not finite
+  // (wave-uniform)
+  auto failed = [&](Regs<DH, R, 1>& rg) -> bool {
+    float t = row_sum(rg, 0);
+    int bad = !(t >= 0x1p-80f);
+#pragma unroll
+    for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) t += rg.O[0][dt][e];
+    bad |= !__builtin_isfinite(t);
+    return __builtin_amdgcn_ballot_w64(bad) != 0;
+  };
+  const bool redo0 = act0 && failed(rg0), redo1 = act1 && failed(rg1);
+  // every wave is past its tiles here, so the re-run may stage over the last chunk
+  if (__syncthreads_or(redo0 || redo1)) {
+    auto reset = [&](Regs<DH, R, 1>& rg) {
+#pragma unroll
+      for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) rg.O[0][dt][e] = 0.0f;
+      rg.mhat[0] = 0.0f;
+      rg.lpart[0] = 0.0f;
+      if (gh == S::GM) rg.qt[0][S::CM][S::DM] = 0xC0E00000u;  // (-m_hat = 0, -OFF = -7)
+    };
+    if (redo0) reset(rg0);
+    if (redo1) reset(rg1);
+    over_chunks([&](int ch, int nt) {
+      if (redo0 && redo1) {
+        f32x16_t Sb[1][2];
+        uint32_t Pb[1][2][8];
+        for (int x = 0; x < nt; ++x) {
+          read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
+          read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
+          const bool first = ch == 0 && x == 0;
+          qk_tile<DH, R>(ops, rg0, Sacc);
+          qk_tile<DH, R>(ops, rg1, Sb);
+          const uint32_t or0 = exp_tile_fast(Sacc, P);
+          if (__builtin_amdgcn_ballot_w64(first || (or0 & 0x40004000u))) rescale_tile<DH, R>(rg0, Sacc, P, first, gh);
+          pv_tile<DH, R>(ops, rg0, P);
+          const uint32_t or1 = exp_tile_fast(Sb, Pb);
+          if (__builtin_amdgcn_ballot_w64(first || (or1 & 0x40004000u))) rescale_tile<DH, R>(rg1, Sb, Pb, first, gh);
+          pv_tile<DH, R>(ops, rg1, Pb);
+        }
+      } else if (redo0) {
+        run_tiles(rg0, nt, ch == 0);
+      } else if (redo1) {
+        run_tiles(rg1, nt, ch == 0);
+      }
+    });
   }
 
   // ---- epilogue: O / l * sigmoid(G), bf16, NHWC
-  auto finish = [&](const Regs<DH, R, 1>& rg, int qb) {
+  auto finish = [&](const Regs<DH, R, 1>& rg, int qb, bool redone) {
     const int r = q0 + wave * QW + qb * 32 + l32;
     const float lsum = row_sum(rg, 0);
     if (r >= G.n_real) return;
     int off, n;
     locate<DH>(G, r, off, n);
     const float inv = rcp_approx(lsum);
-    if (lse) lse[(off - G.h * DH) / G.C * heads + G.h] = (rg.mhat[0] + OFF + __log2f(lsum)) * LN2;
+    if (lse) lse[(off - G.h * DH) / G.C * heads + G.h] = (rg.mhat[0] + (redone ? OFF : OFF_FAST) + __log2f(lsum)) * LN2;
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
@@ -1373,8 +1438,8 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
         store4(mr.o, off, d0, r01, r23, d0 + 4 <= DH);
       }
   };
-  if (act0) finish(rg0, 0);
-  if (act1) finish(rg1, 1);
+  if (act0) finish(rg0, 0, redo0);
+  if (act1) finish(rg1, 1, redo1);
 }
 
 // Workgroup -> logical index (window * heads + head) * qblocks + query block

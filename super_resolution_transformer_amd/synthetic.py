@@ -153,22 +153,26 @@ def make_spike_problem(B: int, H: int, W: int, heads: int, dh: int, R: int, ws: 
 
 
 def make_low_score_problem(B: int, H: int, W: int, heads: int, dh: int, R: int, a: float,
-                           dtype: str = "bf16", seed: int = 0) -> Problem:
-    """A problem whose scores all lie far below zero.
+                           dtype: str = "bf16", seed: int = 0, rows: str = "all") -> Problem:
+    """A problem whose scores lie far below zero for the queries of the chosen map rows.
 
-    Per head, with u a random unit vector: keys kc = u + 0.05 z and queries qc = -a u + 0.25 z'
-    (z, z' ~ N(0, 1) per element), so every query-key score is about -a / sqrt(dh) (natural
-    units; times log2(e) in base 2), spread by a few percent of that, plus the positional bias."""
+    Per head, with u a random unit vector: keys kc = u + 0.05 z and, on the rows chosen by
+    ``rows`` ("all", "even" or "odd" y), queries qc = -a u + 0.25 z' (z, z' ~ N(0, 1) per
+    element), so each of their scores is about -a / sqrt(dh) (natural units; times log2(e) in
+    base 2), spread by a few percent of that, plus the positional bias.  Queries on the other
+    rows keep make_problem's N(0, 1) values (scores near 0)."""
     p = make_problem(B, H, W, heads, dh, R, dtype=dtype, seed=seed)
     rng = np.random.default_rng(seed + 7)
-    qc = np.empty((B, H, W, heads * dh), np.float32)
+    qc = p.qc.copy()
     kc = np.empty_like(qc)
+    sel = {"all": np.ones(H, bool), "even": np.arange(H) % 2 == 0, "odd": np.arange(H) % 2 == 1}[rows]
     for h in range(heads):
         u = rng.standard_normal(dh)
         u /= np.linalg.norm(u)
         sl = slice(h * dh, (h + 1) * dh)
         kc[..., sl] = u + 0.05 * rng.standard_normal((B, H, W, dh))
-        qc[..., sl] = -a * u + 0.25 * rng.standard_normal((B, H, W, dh))
+        low = -a * u + 0.25 * rng.standard_normal((B, H, W, dh))
+        qc[:, sel, :, sl] = low[:, sel]
     p.qc, p.kc = qc, kc
     if dtype == "bf16":
         p.bits["qc"], p.qc = round_bf16(qc)

@@ -1,20 +1,20 @@
 """GPU parity for scores far above, or all far below, the reference of the softmax.
 
-The chunked and tiled kernels (windows of more than 256 tokens) take the exact row maximum on the
-first key tile and then check every later tile: the packed bf16 P words are OR-reduced, and a
-value of 2 or more (the maximum grew by more than 8 base-2 units) sends the wave through an exact
-re-maximum and rescale before P is used.  The whole-window kernel (at most 256 tokens) takes no
-maximum in its first pass: every tile is exponentiated against the fixed reference 0 with an
-offset of 64 base-2 units; a block whose row sum or output ends non-finite, or whose row sum is
-below 2^-86, repeats its tiles with the checked loop.  The first set of inputs places two keys in
+The tiled kernel (windows of more than 2,048 tokens, or 4,096 when not resident at once) takes
+the exact row maximum on the first key tile and then checks every later tile: the packed bf16 P
+words are OR-reduced, and a value of 2 or more (the maximum grew by more than 8 base-2 units) sends
+the wave through an exact re-maximum and rescale before P is used.  The whole-window kernel (at
+most 256 tokens) and the chunked kernel take no maximum in a first pass: every tile is
+exponentiated against the fixed reference 0 with an offset of 64 base-2 units, unchecked; a block
+whose row sum or output ends non-finite, or whose row sum is below 2^-86 (whole-window) or 2^-80
+(chunked), is computed again with the checked loop.  The first set of inputs places two keys in
 later tiles whose score, for half of the queries, exceeds everything else by about 84 base-2 units
-(the checked rescale in the chunked and tiled kernels; the first pass holds it in the whole-window
-kernel, with p up to ~2^20) or by about 250 (p overflows: the chunked and tiled kernels rescale,
-the whole-window kernel's checked re-run takes over).
-A second set places every score far below zero (about -60 and -20 base-2 units): at -60 the
-whole-window kernel's row sums fall below 2^-86 and the checked re-run takes over, at -20 the
-first pass is kept; the chunked and tiled kernels take the exact maximum of their first tile
-either way.
+(the checked rescale in the tiled kernel; the first pass holds it in the others, with p up to
+~2^20) or by about 250 (p overflows: the tiled kernel rescales, the others' checked re-run takes
+over).  A second set places every score far below zero (about -60 and -20 base-2 units): at -60
+the whole-window and chunked kernels' row sums fall below their thresholds and the checked re-run
+takes over, at -20 the first pass is kept; the tiled kernel takes the exact maximum of its first
+tile either way.
 Outputs are compared with the oracle over the whole map at the forward's bars (max abs error
 2e-2 for bf16; 1e-5 for fp32 plus the rounding of two spike scores of ~175, derived in the
 test); the row log-sum-exp at a bound derived from the rounding of the score operands.
@@ -54,8 +54,8 @@ def dev(torch, p, nm):
 
 CASES = [
     # B, H, W, heads, dh, R, ws, b (key spike), dtype
-    (1, 70, 64, 2, 30, 16, 64, 10.0, "bf16"),   # chunked kernel (4,096 tokens, few workgroups), +84 base-2 units
-    (1, 70, 64, 2, 30, 16, 64, 30.0, "bf16"),   # chunked kernel, +250
+    (1, 70, 64, 2, 30, 16, 64, 10.0, "bf16"),   # chunked kernel (4,096 tokens, few workgroups), +84: the first pass
+    (1, 70, 64, 2, 30, 16, 64, 30.0, "bf16"),   # chunked kernel, +250: the checked re-run
     (1, 96, 100, 1, 30, 16, 96, 30.0, "bf16"),  # tiled kernel, 96x96 windows, ragged right column
     (1, 96, 100, 1, 30, 16, 96, 10.0, "bf16"),  # tiled kernel, +84
     (1, 40, 33, 2, 16, 16, 32, 30.0, "bf16"),   # chunked kernel, dh = 16 variant, ragged windows
@@ -103,22 +103,27 @@ def test_score_jump_matches_oracle(torch, case):
 
 
 LOW = [
-    # B, H, W, heads, dh, R, ws, target base-2 score, dtype
-    (2, 37, 40, 2, 30, 16, 16, -60.0, "bf16"),   # whole-window kernel: the checked re-run
-    (2, 37, 40, 2, 30, 16, 16, -20.0, "bf16"),   # whole-window kernel: the first pass is kept
-    (1, 40, 41, 3, 16, 16, 16, -60.0, "bf16"),   # whole-window kernel, dh = 16
-    (1, 40, 33, 2, 16, 16, 32, -60.0, "bf16"),   # chunked kernel
-    (1, 96, 100, 1, 30, 16, 96, -60.0, "bf16"),  # tiled kernel
-    (1, 37, 40, 2, 30, 16, 16, -60.0, "f32"),
+    # B, H, W, heads, dh, R, ws, target base-2 score, rows of low queries, dtype
+    (2, 37, 40, 2, 30, 16, 16, -60.0, "all", "bf16"),   # whole-window kernel: the checked re-run
+    (2, 37, 40, 2, 30, 16, 16, -20.0, "all", "bf16"),   # whole-window kernel: the first pass is kept
+    (1, 40, 41, 3, 16, 16, 16, -60.0, "all", "bf16"),   # whole-window kernel, dh = 16
+    (1, 40, 33, 2, 16, 16, 32, -60.0, "all", "bf16"),   # chunked kernel: every block re-runs
+    (1, 40, 33, 2, 16, 16, 32, -20.0, "all", "bf16"),   # chunked kernel: the first pass is kept
+    # 32x32 windows: a wave's block 0 holds an even window row, block 1 an odd one, so one block
+    # of each wave re-runs while the other keeps its first pass
+    (1, 64, 70, 2, 30, 16, 32, -60.0, "even", "bf16"),
+    (1, 64, 70, 2, 30, 16, 32, -60.0, "odd", "bf16"),
+    (1, 96, 100, 1, 30, 16, 96, -60.0, "all", "bf16"),  # tiled kernel
+    (1, 37, 40, 2, 30, 16, 16, -60.0, "all", "f32"),
 ]
 
 
-@pytest.mark.parametrize("case", LOW, ids=lambda c: "H{1}W{2}h{3}d{4}ws{6}s{7:g}-{8}".format(*c))
+@pytest.mark.parametrize("case", LOW, ids=lambda c: "H{1}W{2}h{3}d{4}ws{6}s{7:g}{8}-{9}".format(*c))
 def test_scores_far_below_zero_match_oracle(torch, case):
-    B, H, W, heads, dh, R, ws, target, dtype = case
+    B, H, W, heads, dh, R, ws, target, rows, dtype = case
     note(f"low scores {case}")
     a = -target * np.sqrt(dh) / np.log2(np.e)
-    p = synthetic.make_low_score_problem(B, H, W, heads, dh, R, a, dtype=dtype, seed=H + W + ws)
+    p = synthetic.make_low_score_problem(B, H, W, heads, dh, R, a, dtype=dtype, seed=H + W + ws, rows=rows)
     maps = [dev(torch, p, nm) for nm in ("qc", "kc", "v", "g")]
     w = torch.from_numpy(p.weights).cuda()
     qp, kp = rib.encode(ws, p.L, p.hidden, p.R, w)
