@@ -127,10 +127,12 @@ rib_status rib_window_attn_heads(const void* qc, const void* kc, const void* v, 
  * images, other streams of a batch, or the three window sizes of one shape)
  * passes the calls together, and the library runs them side by side:
  * RIB_BF16 calls that share (dh, R) take one launch per workgroup size and
- * per 8 calls, largest windows first: windows of at most 2,048 tokens (and of
- * at most 4,096 when the call's 256-query workgroups number at most three per
- * compute unit) share the 256-thread launch, larger windows the 512-thread
- * tiled launch; the 16/32/64 cycle at C = 48 on a 180x320 map is one launch.
+ * per 8 calls, largest windows first: calls on the 256-thread kernels share
+ * one launch; only the (dh, R) shapes (32, 16), (16, 32) and (30, 32) run
+ * windows of more than 2,048 tokens (4,096 when the call's 256-query
+ * workgroups number more than three per compute unit) on the 512-thread
+ * tiled kernel, in a launch of their own.  The 16/32/64 cycle is one launch
+ * for (dh, R) = (16, 16) and (30, 16).
  * RIB_F32 calls run one after another.  Each call's output is bit-identical to
  * that of rib_window_attn with the same arguments.
  *

@@ -1242,7 +1242,7 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
   }
 }
 
-// ---- windows of a few tiles per query block -----------------------------------
+// ---- windows of more than 256 tokens: the chunked kernel ----------------------
 // One workgroup of four waves takes SQ = 256 queries of one (window, head); the
 // window's keys pass through LDS in chunks of 256 (four 64-key tiles), every
 // thread staging one key of a chunk as in the whole-window kernel.  Each wave
@@ -1253,13 +1253,14 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
 // to scratch, once per wave, outside the loop.)
 // The softmax first runs unchecked, as the whole-window kernel's first pass
 // does: every tile against the fixed reference 0 with the offset OFF_FAST.  A
-// 32-query block whose row sum ends below 2^-80 (so its maximum is below -28
-// base-2 units: l <= 4096 * 2^(s_max - 64)) or whose row sum or output is not
-// finite is computed again, all chunks staged again for the whole workgroup,
-// with the tiled kernel's checked loop: exact maximum on the first tile, offset
-// OFF, an OR over the packed P of every later tile and a rescale when the
-// maximum grew by more than 8.  Kept results lose only keys more than 62 below
-// 0, each under 2^-34 of the row's largest.  There is no hand-off between
+// 32-query block whose row sum ends below 2^-80 or whose row sum or output is
+// not finite is computed again, all chunks staged again for the whole
+// workgroup, with the tiled kernel's checked loop: exact maximum on the first
+// tile, offset OFF, an OR over the packed P of every later tile and a rescale
+// when the maximum grew by more than 8.  A kept row has l >= 2^-80 and
+// l <= n 2^(s_max - 64) over its n <= 16,384 keys, so s_max >= -30 base-2
+// units: keys that flush to zero (more than 62 below 0) each weigh under 2^-32
+// of the row's largest.  There is no hand-off between
 // waves: three workgroups share a CU, and while one stages a chunk the others
 // compute.
 template <int DH, int R>
@@ -1524,20 +1525,32 @@ attn_bf16_chunk_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
                        const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                        const float* __restrict__ qp, const float* __restrict__ kp,
                        uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws,
-                       int total, long tstride, float* __restrict__ lse) {
+                       int total, long tstride, float* __restrict__ lse, int whole_windows) {
   __shared__ __attribute__((aligned(16))) uint32_t lds[SNT * Shape<DH, R>::STAGE_DW];
+  const int qblocks = (wt * ws * ws + SQ - 1) / SQ;
   attn_chunk_body<DH, R>(qc, kc, v, g, qp, kp, o, B, T, H, W, heads, wt, ws, total, tstride, lse,
-                         window_block(blockIdx.x, heads * ((wt * ws * ws + SQ - 1) / SQ)), lds);
+                         whole_windows ? window_block(blockIdx.x, heads * qblocks)
+                                       : interleave_logical(blockIdx.x, qblocks), lds);
 }
 
 // Which kernel a call takes: the whole-window kernel up to SQ tokens per
-// window; the chunked kernel up to CHUNK_MAX tokens, and up to CHUNK_FIT when
-// its whole grid is resident at once (three workgroups per CU); the tiled
-// kernel otherwise.  Measured on 180x320 maps: the chunked kernel is 23% faster
-// on 32x32 windows at C = 48, 8% at C = 180, 16% on 4x16x16 and 2% on 2x32x32
-// video windows; on 64x64 windows it is 5% faster at C = 48 (720 workgroups,
-// one resident round) and 10% slower at C = 180 (1,440), where the tiled
-// kernel's two-group pipeline does more per key tile than the extra rounds cost.
+// window, the chunked kernel above that.  The (dh, R) shapes whose chunked
+// kernel spills more registers ((32, 16), (16, 32), (30, 32): 56-116 bytes per
+// lane against 16-32 for the others; not timed on the chunked kernel) keep the
+// tiled kernel for windows of more than CHUNK_MAX tokens, unless the chunked
+// grid is resident at once (three workgroups per CU, up to CHUNK_FIT tokens).  Measured on the (30, 16) and (16, 16) shapes (same process,
+// interleaved rounds): against the tiled kernel the chunked kernel takes 4% less
+// time on 32 x 96x96 windows at C = 180, 1% less on 1x360x640 with 96x96
+// windows, 0.4% less on 64x64 windows at C = 180 and 5% less at C = 48; on
+// 32x32 windows 8-23% less.
+// XCD dealing of chunked calls: whole windows (every head and query block of a
+// window on one XCD, window_block) when the windows have at most CHUNK_MAX
+// tokens or their number is a multiple of 8; otherwise window units one by one
+// (interleave_logical), as the tiled kernel deals them.  Whole windows of 4,096
+// or 9,216 tokens are too coarse to spread 15 or 28 windows evenly over 8 XCDs:
+// 64x64 windows at C = 48 took 0.133 ms dealt whole and 0.126 ms by unit,
+// 1x360x640 with 96x96 windows 2.18 against 1.80 ms; 32x32 windows (60 on a
+// 180x320 map) are faster dealt whole (0.037 against 0.040 ms at C = 48).
 constexpr int CHUNK_MAX = 2048;
 constexpr int CHUNK_FIT = 4096;
 enum Kind { WHOLE = 0, CHUNKED = 1, TILED = 2 };
@@ -1564,6 +1577,7 @@ struct CallDesc {
   float* lse;
   long tstride;
   int B, T, H, W, heads, wt, ws, units, qblocks, kind;
+  int whole;  // chunked calls: 1 = whole windows per XCD (window_block), 0 = by unit
 };
 
 struct CallGroup {
@@ -1604,7 +1618,8 @@ __global__ void __launch_bounds__(SQ, 3) attn_bf16_window_group_kernel(const Cal
                            c.units, c.tstride, c.lse, window_unit(lb, c.heads), lds);
   else
     attn_chunk_body<DH, R>(c.qc, c.kc, c.v, c.g, c.qp, c.kp, c.o, c.B, c.T, c.H, c.W, c.heads, c.wt, c.ws,
-                           c.units * c.qblocks, c.tstride, c.lse, window_block(lb, c.heads * c.qblocks), lds);
+                           c.units * c.qblocks, c.tstride, c.lse,
+                           c.whole ? window_block(lb, c.heads * c.qblocks) : interleave_logical(lb, c.qblocks), lds);
 }
 
 // window units of a call
@@ -1617,8 +1632,14 @@ inline Kind call_kind(const AttnArgs& a, int cus) {
   const int NW = a.wt * a.ws * a.ws;
   if (NW <= SQ) return WHOLE;
   if (NW <= CHUNK_MAX) return CHUNKED;
+  const bool spills = (a.dh == 32 && a.R == 16) || (a.dh == 16 && a.R == 32) || (a.dh == 30 && a.R == 32);
+  if (!spills) return CHUNKED;
   const long wgs = (long)call_units(a) * ((NW + SQ - 1) / SQ);
   return NW <= CHUNK_FIT && wgs <= 3L * cus ? CHUNKED : TILED;
+}
+// chunked calls: whole windows to an XCD (see above)
+inline bool chunk_whole(const AttnArgs& a) {
+  return a.wt * a.ws * a.ws <= CHUNK_MAX || (call_units(a) / a.heads) % 8 == 0;
 }
 // query blocks per window unit for a kernel kind
 inline int kind_qblocks(const AttnArgs& a, Kind k) {
@@ -1628,8 +1649,9 @@ inline int kind_qblocks(const AttnArgs& a, Kind k) {
 // workgroups of a call's grid range
 inline int kind_grid(const AttnArgs& a, Kind k) {
   const int units = call_units(a), windows = units / a.heads, qb = kind_qblocks(a, k);
-  return k == TILED ? 8 * ((units + 7) / 8) * qb                  // see interleave_logical
-                    : 8 * ((windows + 7) / 8) * a.heads * qb;     // see window_unit, window_block
+  const bool by_unit = k == TILED || (k == CHUNKED && !chunk_whole(a));
+  return by_unit ? 8 * ((units + 7) / 8) * qb                // see interleave_logical
+                 : 8 * ((windows + 7) / 8) * a.heads * qb;   // see window_unit, window_block
 }
 
 template <int DH, int R>
@@ -1645,7 +1667,8 @@ hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
                        (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units, a.tstride, a.lse);
   else if (kind == CHUNKED)
     hipLaunchKernelGGL((attn_bf16_chunk_kernel<DH, R>), dim3(grid), dim3(SQ), 0, stream, qc, kc, v, g, a.qp, a.kp,
-                       (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units * qb, a.tstride, a.lse);
+                       (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units * qb, a.tstride, a.lse,
+                       chunk_whole(a) ? 1 : 0);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<DH, R>), dim3(grid), dim3(QB), 0, stream, qc, kc, v, g, a.qp, a.kp,
                        (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units * qb, a.tstride, a.lse,
@@ -1674,6 +1697,7 @@ hipError_t launch_group(const AttnArgs* const* calls, const Kind* kinds, int n, 
     c.units = call_units(a);
     c.qblocks = kind_qblocks(a, kinds[i]);
     c.kind = kinds[i];
+    c.whole = chunk_whole(a) ? 1 : 0;
     grp.first[i] = first;
     first += kind_grid(a, kinds[i]);
   }

@@ -49,11 +49,12 @@ def maps_of(torch, p):
     return [torch.from_numpy(p.bits[n].view(np.int16)).view(torch.bfloat16).cuda() for n in ("qc", "kc", "v", "g")]
 
 
-@pytest.mark.parametrize("ws", [16, 32, 96])
-def test_forward_on_dword_aligned_maps(torch, ws):
-    """An image of 37x53 tokens at C = 90 (odd H*W*C): whole-window, chunked and tiled kernels."""
-    note(f"alignment forward ws={ws}")
-    p = synthetic.make_problem(1, 37, 53, 3, 30, 16, dtype="bf16", seed=ws)
+@pytest.mark.parametrize("ws,R", [(16, 16), (32, 16), (96, 16), (96, 32)])
+def test_forward_on_dword_aligned_maps(torch, ws, R):
+    """An image of 37x53 tokens at C = 90 (odd H*W*C): whole-window (16), chunked (32; 96 at R = 16)
+    and tiled (96 at R = 32) kernels."""
+    note(f"alignment forward ws={ws} R={R}")
+    p = synthetic.make_problem(1, 37, 53, 3, 30, R, dtype="bf16", seed=ws)
     maps = maps_of(torch, p)
     qp, kp = rib.encode(ws, p.L, p.hidden, p.R, torch.from_numpy(p.weights).cuda())
     want = rib.window_attn(*maps, qp, kp, 3, ws)

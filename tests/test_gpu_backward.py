@@ -143,7 +143,7 @@ LSE_CASES = [
     (1, 64, 64, 3, 16, 16, 16, "f32"),
     (1, 21, 13, 2, 30, 16, 8, "f32"),
     (1, 40, 24, 6, 30, 16, 16, "bf16"),     # small-window kernel
-    (1, 70, 33, 6, 30, 16, 32, "bf16"),     # tiled kernel, ragged windows
+    (1, 70, 33, 6, 30, 16, 32, "bf16"),     # chunked forward, ragged windows
     (1, 64, 64, 3, 16, 16, 64, "bf16"),
     (1, 100, 96, 2, 30, 16, 96, "bf16"),    # 96x96 windows, one 4-row window below
 ]

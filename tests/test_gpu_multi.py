@@ -1,7 +1,8 @@
 """GPU: rib_window_attn_multi runs several independent calls in few launches.
 
 Calls whose windows take the 256-thread kernels (whole-window up to 256 tokens,
-chunked above) share one launch per 8 calls; calls of the tiled kernel share
+chunked above) share one launch per 8 calls; calls of the tiled kernel (the
+(dh, R) shapes (32, 16), (16, 32) and (30, 32) above 2,048 tokens) share
 another.  Each call's output must be bit-identical to rib_window_attn on the
 same arguments (the batched kernels run the same per-workgroup code), which
 makes the index mapping of the grouped grid (call ranges, XCD dealing, padding
@@ -66,17 +67,19 @@ def test_cyclic_schedule_sst_lite(torch):
 
 
 def test_cyclic_schedule_inference_shape(torch):
-    """The cyclic schedule at C = 180 (6 heads x 30): 16 and 32 in one launch, 64 in the tiled kernel."""
+    """The cyclic schedule at C = 180 (6 heads x 30): 16, 32 and 64 in one launch (64 dealt to the XCDs
+    by window unit: 15 windows)."""
     note("multi: cyclic 16/32/64 on 1x180x320, 6 heads x 30")
     check_batch(torch, [(1, 180, 320, 6, 30, 16, ws) for ws in (16, 32, 64)], "bf16")
 
 
-@pytest.mark.parametrize("ws,n", [(32, 10), (16, 12), (96, 9)])
-def test_more_calls_than_one_group(torch, ws, n):
+@pytest.mark.parametrize("ws,n,R", [(32, 10, 16), (16, 12, 16), (96, 9, 16), (96, 9, 32)])
+def test_more_calls_than_one_group(torch, ws, n, R):
     """More than 8 calls of one kernel kind and one (dh, R) variant: the batch is split over two launches
-    of the same grouped kernel (chunked, whole-window, tiled); ragged maps of different sizes."""
-    specs = [(1 + k % 2, 37 + 3 * k, 41 + 5 * k, 1 + k % 3, 30, 16, ws) for k in range(n)]
-    note(f"multi: {n} calls at window {ws}")
+    of the same grouped kernel (chunked, whole-window, chunked dealt by unit, tiled at R = 32); ragged
+    maps of different sizes."""
+    specs = [(1 + k % 2, 37 + 3 * k, 41 + 5 * k, 1 + k % 3, 30, R, ws) for k in range(n)]
+    note(f"multi: {n} calls at window {ws}, R = {R}")
     check_batch(torch, specs, "bf16")
 
 
@@ -88,13 +91,23 @@ def test_sixteen_mixed_window_calls(torch):
 
 
 def test_many_mixed_calls(torch):
-    """Ten calls: three take the tiled kernel (windows 96, 96, 128), seven the 256-thread kernels (windows 2,
-    4, 16, 16, 17, 32 and a 64 whose grid is resident at once) in one launch; ragged maps."""
+    """Ten calls of the 256-thread kernels in two launches (8 + 2): windows 2, 4, 16, 16 and 17 (whole
+    window), 32 and 64 (whole windows per XCD), 96, 96 and 128 (chunked, some dealt by unit); ragged
+    maps."""
     specs = [(1, 70, 61, 2, 30, 16, 96), (2, 37, 53, 3, 30, 16, 32), (1, 100, 61, 1, 30, 16, 64),
              (1, 40, 41, 1, 30, 16, 17), (3, 37, 53, 3, 30, 16, 16), (1, 5, 7, 2, 30, 16, 4),
              (1, 96, 96, 6, 30, 16, 96), (2, 21, 19, 2, 30, 16, 16), (1, 33, 130, 1, 30, 16, 128),
              (1, 1, 1, 2, 30, 16, 2)]
     note(f"multi: {len(specs)} mixed calls")
+    check_batch(torch, specs, "bf16")
+
+
+def test_tiled_and_chunked_calls_of_one_variant(torch):
+    """(dh, R) = (30, 32): windows 96 and 128 take the tiled kernel (one launch), 16, 32 and a
+    resident 64 the 256-thread kernels (another); ragged maps."""
+    specs = [(1, 70, 61, 2, 30, 32, 96), (1, 33, 130, 1, 30, 32, 128), (2, 37, 53, 2, 30, 32, 16),
+             (1, 37, 53, 3, 30, 32, 32), (1, 100, 61, 1, 30, 32, 64)]
+    note("multi: tiled and chunked calls at (30, 32)")
     check_batch(torch, specs, "bf16")
 
 

@@ -111,7 +111,10 @@ SMALL = [
     (1, 50, 47, 2, 30, 16, 45, "bf16"),        # 2,025 tokens: eight chunks, the last one ragged
     (1, 45, 50, 2, 8, 8, 24, "bf16"),          # chunked kernel, (8, 8) variant
     (1, 30, 31, 2, 16, 32, 32, "bf16"),        # chunked kernel, (16, 32) variant
-    (1, 50, 47, 1, 30, 16, 46, "bf16"),        # 2,116 tokens: the tiled kernel just above the chunked range
+    (1, 50, 47, 1, 30, 16, 46, "bf16"),        # 2,116 tokens: chunked, 4 windows dealt to the XCDs by unit
+    (1, 50, 47, 1, 30, 32, 46, "bf16"),        # 2,116 tokens, (30, 32): the tiled kernel
+    (1, 70, 61, 1, 32, 16, 96, "bf16"),        # (32, 16) at 96x96: the tiled kernel
+    (1, 100, 61, 2, 16, 32, 64, "bf16"),       # (16, 32) at 64x64, grid resident at once: chunked
 ]
 
 
@@ -204,8 +207,8 @@ def test_positional_one_hot_is_bit_exact(torch, dtype, ws, H, W, R, dh):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("ws", [16, 32, 48])
 def test_locality_and_equivariance_bit_exact(torch, dtype, ws):
-    """Window 16 runs the whole-window bf16 kernel, window 32 the chunked one, window 48 (2,304
-    tokens) the tiled one."""
+    """Window 16 runs the whole-window bf16 kernel, window 32 the chunked one with whole windows dealt
+    to the XCDs, window 48 (2,304 tokens, 18 windows) the chunked one dealt by window unit."""
     note(f"locality ws={ws} {dtype}")
     H, W, B, heads, dh, R = 3 * ws, 3 * ws, 2, 3, 30 if dtype == "bf16" else 16, 16
     p = synthetic.make_problem(B, H, W, heads, dh, R, dtype=dtype, seed=7)
@@ -256,7 +259,7 @@ def test_unsupported_shape_raises(torch):
 @pytest.mark.parametrize("B,H,W,heads,dh,R,ws,dtype", [
     (1, 20, 30, 3, 16, 16, 8, "f32"),
     (2, 37, 53, 3, 30, 16, 16, "bf16"),     # whole-window kernel
-    (1, 37, 53, 2, 30, 16, 32, "bf16"),     # tiled kernel
+    (1, 37, 53, 2, 30, 16, 32, "bf16"),     # chunked kernel
     (1, 30, 31, 2, 16, 32, 16, "bf16"),
     (1, 70, 61, 2, 30, 32, 64, "bf16"),
 ])

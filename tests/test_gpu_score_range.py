@@ -1,9 +1,9 @@
 """GPU parity for scores far above, or all far below, the reference of the softmax.
 
-The tiled kernel (windows of more than 2,048 tokens, or 4,096 when not resident at once) takes
-the exact row maximum on the first key tile and then checks every later tile: the packed bf16 P
-words are OR-reduced, and a value of 2 or more (the maximum grew by more than 8 base-2 units) sends
-the wave through an exact re-maximum and rescale before P is used.  The whole-window kernel (at
+The tiled kernel (windows of more than 2,048 tokens for the (dh, R) shapes (32, 16), (16, 32) and
+(30, 32)) takes the exact row maximum on the first key tile and then checks every later tile: the
+packed bf16 P words are OR-reduced, and a value of 2 or more (the maximum grew by more than 8 base-2
+units) sends the wave through an exact re-maximum and rescale before P is used.  The whole-window kernel (at
 most 256 tokens) and the chunked kernel take no maximum in a first pass: every tile is
 exponentiated against the fixed reference 0 with an offset of 64 base-2 units, unchecked; a block
 whose row sum or output ends non-finite, or whose row sum is below 2^-86 (whole-window) or 2^-80
@@ -56,8 +56,10 @@ CASES = [
     # B, H, W, heads, dh, R, ws, b (key spike), dtype
     (1, 70, 64, 2, 30, 16, 64, 10.0, "bf16"),   # chunked kernel (4,096 tokens, few workgroups), +84: the first pass
     (1, 70, 64, 2, 30, 16, 64, 30.0, "bf16"),   # chunked kernel, +250: the checked re-run
-    (1, 96, 100, 1, 30, 16, 96, 30.0, "bf16"),  # tiled kernel, 96x96 windows, ragged right column
-    (1, 96, 100, 1, 30, 16, 96, 10.0, "bf16"),  # tiled kernel, +84
+    (1, 96, 100, 1, 30, 16, 96, 30.0, "bf16"),  # chunked kernel, 96x96 windows, ragged right column
+    (1, 96, 100, 1, 30, 16, 96, 10.0, "bf16"),  # chunked kernel, 96x96 windows, +84
+    (1, 96, 100, 1, 30, 32, 96, 30.0, "bf16"),  # tiled kernel ((30, 32) at 96x96), +250
+    (1, 96, 100, 1, 30, 32, 96, 10.0, "bf16"),  # tiled kernel, +84
     (1, 40, 33, 2, 16, 16, 32, 30.0, "bf16"),   # chunked kernel, dh = 16 variant, ragged windows
     (2, 37, 40, 2, 30, 16, 16, 10.0, "bf16"),   # whole-window kernel, +84: the unchecked pass
     (2, 37, 40, 2, 30, 16, 16, 30.0, "bf16"),   # whole-window kernel, +250: the checked re-run
@@ -113,7 +115,8 @@ LOW = [
     # of each wave re-runs while the other keeps its first pass
     (1, 64, 70, 2, 30, 16, 32, -60.0, "even", "bf16"),
     (1, 64, 70, 2, 30, 16, 32, -60.0, "odd", "bf16"),
-    (1, 96, 100, 1, 30, 16, 96, -60.0, "all", "bf16"),  # tiled kernel
+    (1, 96, 100, 1, 30, 16, 96, -60.0, "all", "bf16"),  # chunked kernel, 96x96 windows
+    (1, 96, 100, 1, 30, 32, 96, -60.0, "all", "bf16"),  # tiled kernel
     (1, 37, 40, 2, 30, 16, 16, -60.0, "all", "f32"),
 ]
 

@@ -80,7 +80,7 @@ def test_encode3d_other_widths(torch, wt, ws, L, hidden, R):
 CASES = [
     # (B, T, H, W, heads, dh, wt, ws, dtype)
     (1, 5, 9, 7, 2, 30, 2, 4, "bf16"),      # small kernel (32 tokens), ragged on every axis
-    (1, 3, 20, 18, 2, 30, 2, 16, "bf16"),   # tiled kernel, 512-token windows, ragged
+    (1, 3, 20, 18, 2, 30, 2, 16, "bf16"),   # chunked kernel, 512-token windows, ragged
     (1, 4, 16, 16, 3, 16, 4, 8, "bf16"),    # 256 tokens: small kernel, dh 16
     (2, 3, 17, 20, 1, 30, 3, 17, "bf16"),   # 867 tokens: two query blocks, 14 key tiles with frame crossings
     (1, 7, 12, 12, 2, 16, 4, 16, "bf16"),   # 1024-token windows, a one-frame window at the end
@@ -127,7 +127,7 @@ def test_one_frame_video_is_the_image_path(torch, dtype, ws):
 
 
 def test_attn3d_locality(torch):
-    """Changing one token's key and value changes outputs in its space-time window only (bf16, tiled kernel)."""
+    """Changing one token's key and value changes outputs in its space-time window only (bf16, chunked kernel)."""
     B, T, H, W, heads, dh, wt, ws = 1, 4, 20, 20, 1, 30, 2, 16
     maps, bits = video_problem(B, T, H, W, heads, dh, "bf16", seed=3)
     dev = to_dev(torch, maps, bits, "bf16")
