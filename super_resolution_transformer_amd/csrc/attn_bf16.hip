@@ -1455,6 +1455,19 @@ __device__ __forceinline__ int window_block(int bid, int per_window) {
   return (k * 8 + xcd) * per_window + (slot - k * per_window);
 }
 
+// As window_block, with the workgroups of a window numbered query block first:
+// the heads of one query block take consecutive workgroups, so the resident
+// workgroups of an XCD cover every head of the window at once and read each
+// cache line of the window's token rows (which hold every head's slice)
+// together.  Returns the logical index (window * heads + head) * qblocks + qb.
+__device__ __forceinline__ int window_block_qb(int bid, int heads, int qblocks) {
+  const int per = heads * qblocks;
+  const int L = window_block(bid, per);
+  const int win = L / per, j = L - win * per;
+  const int qb = j / heads, h = j - qb * heads;
+  return (win * heads + h) * qblocks + qb;
+}
+
 // Workgroup -> logical index (window unit * qblocks + query block) for a grid
 // of 8 * ceil(units / 8) * qblocks workgroups.  Window unit 8k + x takes the
 // workgroups whose index is x mod 8, which the dispatcher's round-robin sends
@@ -1487,7 +1500,7 @@ attn_bf16_lnq_kernel(const uint32_t* __restrict__ kc, const uint32_t* __restrict
                      long tstride, float* __restrict__ lse, int whole_windows, const LnqArgs L) {
   const int qblocks = (wt * ws * ws + QB - 1) / QB;
   attn_tiled_body<DH, R, true>(nullptr, kc, v, g, qp, kp, o, B, T, H, W, heads, wt, ws, total, tstride, lse,
-                               whole_windows ? window_block(blockIdx.x, heads * qblocks)
+                               whole_windows ? window_block_qb(blockIdx.x, heads, qblocks)
                                              : interleave_logical(blockIdx.x, qblocks),
                                &L);
 }
@@ -1529,7 +1542,7 @@ attn_bf16_chunk_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
   __shared__ __attribute__((aligned(16))) uint32_t lds[SNT * Shape<DH, R>::STAGE_DW];
   const int qblocks = (wt * ws * ws + SQ - 1) / SQ;
   attn_chunk_body<DH, R>(qc, kc, v, g, qp, kp, o, B, T, H, W, heads, wt, ws, total, tstride, lse,
-                         whole_windows ? window_block(blockIdx.x, heads * qblocks)
+                         whole_windows ? window_block_qb(blockIdx.x, heads, qblocks)
                                        : interleave_logical(blockIdx.x, qblocks), lds);
 }
 
@@ -1619,7 +1632,7 @@ __global__ void __launch_bounds__(SQ, 3) attn_bf16_window_group_kernel(const Cal
   else
     attn_chunk_body<DH, R>(c.qc, c.kc, c.v, c.g, c.qp, c.kp, c.o, c.B, c.T, c.H, c.W, c.heads, c.wt, c.ws,
                            c.units * c.qblocks, c.tstride, c.lse,
-                           c.whole ? window_block(lb, c.heads * c.qblocks) : interleave_logical(lb, c.qblocks), lds);
+                           c.whole ? window_block_qb(lb, c.heads, c.qblocks) : interleave_logical(lb, c.qblocks), lds);
 }
 
 // window units of a call
