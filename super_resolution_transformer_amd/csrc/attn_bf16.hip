@@ -67,7 +67,7 @@ constexpr int QW = 64;             // queries per wave (two 32-query MFMA blocks
 constexpr int QB = QW * NWAVE;     // queries per workgroup
 constexpr int NSTAGE = 3;          // LDS stages of the key-tile pipeline
 constexpr float OFF = 7.0f;        // p = exp2(s - m_hat - OFF) <= 2^-OFF normally
-constexpr float OFF_FAST = 64.0f;  // offset of the whole-window kernel's unchecked first pass
+constexpr float OFF_FAST = 64.0f;  // offset of the unchecked first pass (whole-window and chunked kernels)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // gfx9 raw buffer: 32-bit data format
@@ -1551,13 +1551,14 @@ attn_bf16_chunk_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
 // kernel spills more registers ((32, 16), (16, 32), (30, 32): 56-116 bytes per
 // lane against 16-32 for the others; not timed on the chunked kernel) keep the
 // tiled kernel for windows of more than CHUNK_MAX tokens, unless the chunked
-// grid is resident at once (three workgroups per CU, up to CHUNK_FIT tokens).  Measured on the (30, 16) and (16, 16) shapes (same process,
-// interleaved rounds): against the tiled kernel the chunked kernel takes 4% less
-// time on 32 x 96x96 windows at C = 180, 1% less on 1x360x640 with 96x96
-// windows, 0.4% less on 64x64 windows at C = 180 and 5% less at C = 48; on
-// 32x32 windows 8-23% less.
+// grid is resident at once (three workgroups per CU, up to CHUNK_FIT tokens).
+// Measured on the (30, 16) and (16, 16) shapes (same process, interleaved
+// rounds): against the tiled kernel the chunked kernel takes 4% less time on
+// 32 x 96x96 windows at C = 180, 1% less on 1x360x640 with 96x96 windows, 0.4%
+// less on 64x64 windows at C = 180 and 5% less at C = 48; on 32x32 windows
+// 8-23% less.
 // XCD dealing of chunked calls: whole windows (every head and query block of a
-// window on one XCD, window_block) when the windows have at most CHUNK_MAX
+// window on one XCD, window_block_qb) when the windows have at most CHUNK_MAX
 // tokens or their number is a multiple of 8; otherwise window units one by one
 // (interleave_logical), as the tiled kernel deals them.  Whole windows of 4,096
 // or 9,216 tokens are too coarse to spread 15 or 28 windows evenly over 8 XCDs:
