@@ -191,7 +191,9 @@ ln_qkv_bf16_kernel(const uint32_t* __restrict__ x, const float* __restrict__ gam
         sq = fmaf(d, d, sq);
       }
       sq = row16_sum(sq);
-      const float inv = 1.0f / sqrtf(sq / (float)C + eps);
+      // v_rsq_f32 (about 1 ulp): LN(x) is rounded to bf16 next, and the correctly rounded
+      // sqrt and divide this library is built with would cost some 25 instructions here
+      const float inv = __builtin_amdgcn_rsqf(sq * (1.0f / (float)C) + eps);
       uint32_t* xo = xcur + t * (C / 2);
 #pragma unroll
       for (int g4 = 0; g4 < CPT / 4; ++g4) {
