@@ -24,7 +24,7 @@
 //    their dA' row is 0 (padded queries, dkv pass), so they add nothing; no
 //    masking instructions are needed.
 //
-// dq pass (query-major): a workgroup of 8 waves owns 512 queries of one
+// dq pass (query-major): a workgroup of 4 waves owns 256 queries of one
 // (image, window, head); each wave keeps the B operands of its 64 queries
 // (augmented query rows and dA' rows) in VGPRs and streams the window's keys
 // through LDS in tiles of 64.  S^T = Kt Qt^T and (dP - D)^T = V' dA'^T come
@@ -33,6 +33,9 @@
 // rows with the transposing ds_read_b64_tr_b16 (the forward kernel's PV
 // trick).  dkv pass (key-major): the mirror image, lane = key: S = Qt Kt^T,
 // dP - D = dA' V'^T, then dV'^T += dA'^T P and dKt^T += Qt^T dS.
+// Two workgroups share a CU (208-240 registers per lane), each waiting only at
+// its own per-tile barrier; one workgroup of 8 waves and 512 rows per CU took
+// 4% longer on the 32 x 96x96 workload (bit-identical gradients).
 //
 // LDS layout (both passes): a tile of TT rows is stored chunk-major, one
 // 16-byte chunk = 8 consecutive bf16 columns of a row, chunk c of row j at
@@ -48,7 +51,7 @@ namespace rib {
 
 namespace {
 
-constexpr int NWV = 8;         // waves per workgroup
+constexpr int NWV = 4;         // waves per workgroup (two workgroups per CU, each with its own barriers)
 constexpr int RW = 64;         // own rows per wave (two 32-row MFMA blocks)
 constexpr int RB = NWV * RW;   // own rows per workgroup
 constexpr int TT = 64;         // streamed rows per LDS tile
@@ -70,7 +73,7 @@ struct BS {
   static constexpr int ST_DW = A_DW + V_DW;
   static_assert(DC == 2, "value rows are one 32-column tile");
   static_assert(NP == 10, "packed rows of 160 bytes");
-  static_assert(NP <= 2 * NWV, "at most two staging pieces per thread");
+  static_assert(NP <= 3 * NWV, "at most three staging pieces per thread");
 };
 
 // dword of chunk c (columns 8c .. 8c+7) of row j of a tile
@@ -319,10 +322,10 @@ struct Frame {
   }
 
   // LDS-direct copy of streamed tile t into the stage `dst`: wave w copies
-  // chunks w and w + 8; lane l writes row l of the chunk.
+  // chunks w, w + 4 and w + 8; lane l writes row l of the chunk.
   __device__ __forceinline__ void issue(uint32_t* dst, int t) const {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < (S::NP + NWV - 1) / NWV; ++k) {
       const int cc = wave + NWV * k;
       if (cc < S::NP) {
         const unsigned off = (unsigned)(((t * S::NP + cc) * 256 + lane * 4) * 4);
@@ -335,7 +338,7 @@ struct Frame {
 
 // ---- dq pass -------------------------------------------------------------------
 template <int DH, int R>
-__global__ void __launch_bounds__(RB, 1)
+__global__ void __launch_bounds__(RB, 2)
 bwd_dq_bf16_kernel(BwdArgs a, int total) {
   using S = BS<DH, R>;
   // two stages as two arrays (not one double buffer): the compiler then sees
@@ -441,7 +444,7 @@ bwd_dq_bf16_kernel(BwdArgs a, int total) {
 
 // ---- dkv pass ------------------------------------------------------------------
 template <int DH, int R>
-__global__ void __launch_bounds__(RB, 1)
+__global__ void __launch_bounds__(RB, 2)
 bwd_dkv_bf16_kernel(BwdArgs a, int total) {
   using S = BS<DH, R>;
   // two stages as two arrays, as in the dq pass
