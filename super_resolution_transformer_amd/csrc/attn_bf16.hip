@@ -360,7 +360,7 @@ __device__ __forceinline__ int opaque(int x) {
 template <int DH, int R>
 __device__ __forceinline__ void read_k_ops(const uint32_t* lds, int kst, int l32, int gh, PhaseOps<DH, R>& ops) {
   using S = Shape<DH, R>;
-  const uint32_t* base = lds + opaque(kst + kchunk_dw(gh, l32));
+  const uint32_t* base = lds + opaque(kchunk_dw(gh, l32)) + kst;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -474,7 +474,7 @@ __device__ __forceinline__ void read_v_ops(const uint32_t* lds, int vst, int lan
   const int j = lane & 15, q = lane >> 4;
   const int key0 = 4 * (q >> 1) + (j >> 2);
   const int ch0 = 16 * (q & 1) + 4 * (j & 3);
-  const uint32_t* base = lds + opaque(vst + vpiece_dw<S::DT>(key0, ch0));
+  const uint32_t* base = lds + opaque(vpiece_dw<S::DT>(key0, ch0)) + vst;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -1058,8 +1058,9 @@ __device__ __forceinline__ MapRsrc map_rsrc(const float* qp, const uint32_t* qc,
 
 // Stages key r of window G (every role of the staging scheme: Kp, Kc and V
 // parts, padded keys masked) into row r % 64 of tile (r / 64) % 4 of `lds`;
-// the calling thread is thread r % 256 of a 256-thread workgroup.
-template <int DH, int R>
+// the calling thread is thread r % 256 of a 256-thread workgroup.  MASK =
+// false: the caller knows key r is real (no selects on the stored words).
+template <int DH, int R, bool MASK = true>
 __device__ __forceinline__ void stage_key(const Geo& G, uint32_t* lds, int r, const uint32_t* __restrict__ kc,
                                           const uint32_t* __restrict__ v, const float* __restrict__ kp,
                                           int map_elems, int window_tokens) {
@@ -1096,7 +1097,7 @@ __device__ __forceinline__ void stage_key(const Geo& G, uint32_t* lds, int r, co
     }
   }
 #pragma unroll
-  for (int role = 0; role < 8; ++role) store_tile<DH, R, true>(stage, role, lane, real, st[role]);
+  for (int role = 0; role < 8; ++role) store_tile<DH, R, MASK>(stage, role, lane, real, st[role]);
 }
 
 // One workgroup of the whole-window kernel: logical = window unit.
@@ -1332,9 +1333,12 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
   auto over_chunks = [&](auto&& tiles) {
     for (int ch = 0; ch < nchunks; ++ch) {
       if (ch > 0) __syncthreads();  // every wave is done with the previous chunk's tiles
-      stage_key<DH, R>(G, lds, ch * SQ + tid, kc, v, kp, map_elems, wt * ws * ws);
-      __syncthreads();
       const int left = G.n_real - ch * SQ;
+      if (left >= SQ)  // every key of the chunk is real: no masking selects
+        stage_key<DH, R, false>(G, lds, ch * SQ + tid, kc, v, kp, map_elems, wt * ws * ws);
+      else
+        stage_key<DH, R, true>(G, lds, ch * SQ + tid, kc, v, kp, map_elems, wt * ws * ws);
+      __syncthreads();
       tiles(ch, left >= SQ ? SNT : (left + KT - 1) / KT);
     }
   };
