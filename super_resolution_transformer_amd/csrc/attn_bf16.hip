@@ -488,6 +488,49 @@ __device__ __forceinline__ void read_v_ops(const uint32_t* lds, int vst, int lan
       }
 }
 
+// Byte offsets in a staging array of this lane's K~ and V operand reads,
+// carried from key tile to key tile of a run of consecutive tiles (stride
+// `tile` dwords): each read addresses the carried register plus an immediate
+// offset, and the next tile costs one add per array.  The carried values pass
+// through opaque() in place, so that the compiler keeps one register instead
+// of one hoisted address per read.
+template <int DH, int R>
+struct OpsWalk {
+  int kb, vb;
+  __device__ __forceinline__ OpsWalk(int l32, int gh, int lane, int kst, int vst) {
+    using S = Shape<DH, R>;
+    const int j = lane & 15, q = lane >> 4;
+    kb = 4 * (kst + kchunk_dw(gh, l32));
+    vb = 4 * (vst + vpiece_dw<S::DT>(4 * (q >> 1) + (j >> 2), 16 * (q & 1) + 4 * (j & 3)));
+  }
+  // operands of the current tile, then advance by `tile` dwords
+  __device__ __forceinline__ void read(const uint32_t* lds, int tile, PhaseOps<DH, R>& ops) {
+    using S = Shape<DH, R>;
+    kb = opaque(kb);
+    vb = opaque(vb);
+    const uint32_t* kbase = reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lds) + kb);
+    const uint32_t* vbase = reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lds) + vb);
+#pragma unroll
+    for (int kblk = 0; kblk < 2; ++kblk)
+#pragma unroll
+      for (int c = 0; c < S::KC; ++c)
+        ops.ka[kblk][c] = *reinterpret_cast<const u32x4_t*>(kbase + kchunk_dw(2 * c, kblk * 32));
+#pragma unroll
+    for (int kblk = 0; kblk < 2; ++kblk)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int dt = 0; dt < S::DT; ++dt) {
+          const int kofs = kblk * 32 + 16 * c2;
+          const u32x2_t lo = ds_read_tr16(vbase + vpiece_dw<S::DT>(kofs, dt * 32));
+          const u32x2_t hi = ds_read_tr16(vbase + vpiece_dw<S::DT>(kofs + 8, dt * 32));
+          ops.va[kblk][c2][dt] = (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
+        }
+    kb += 4 * tile;
+    vb += 4 * tile;
+  }
+};
+
 // O^T += V^T P^T (and, without a ones channel, l += the lane's p values)
 template <int DH, int R, int NQ>
 __device__ __forceinline__ void pv_tile(const PhaseOps<DH, R>& ops, Regs<DH, R, NQ>& rg, const uint32_t (&P)[NQ][2][8]) {
@@ -1182,9 +1225,9 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
     // 170 with |V| < 2^14.  A block that fails repeats its tiles with the checked loop:
     // exact maximum on the first tile, offset OFF, an OR over the packed P of every tile,
     // and a rescale whenever a score exceeds the reference by more than 8.
+    OpsWalk<DH, R> walk(l32, gh, lane, 0, S::KS_DW);
     for (int x = 0; x < ntiles; ++x) {
-      read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
-      read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
+      walk.read(lds, S::STAGE_DW, ops);
       qk_tile<DH, R>(ops, rg, Sacc);
       (void)exp_tile_fast(Sacc, P);
       pv_tile<DH, R>(ops, rg, P);
@@ -1206,9 +1249,9 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
         rg.mhat[0] = 0.0f;
         rg.lpart[0] = 0.0f;
         if (gh == S::GM) rg.qt[0][S::CM][S::DM] = 0xC0E00000u;  // (-m_hat = 0, -OFF = -7)
+        OpsWalk<DH, R> rwalk(l32, gh, lane, 0, S::KS_DW);
         for (int x = 0; x < ntiles; ++x) {
-          read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
-          read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
+          rwalk.read(lds, S::STAGE_DW, ops);
           qk_tile<DH, R>(ops, rg, Sacc);
           const uint32_t orv = exp_tile_fast(Sacc, P);
           const bool first = x == 0;
@@ -1318,9 +1361,9 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
   f32x16_t Sacc[1][2];
   uint32_t P[1][2][8];
   auto run_tiles = [&](Regs<DH, R, 1>& rg, int nt, bool first_chunk) {
+    OpsWalk<DH, R> walk(l32, gh, lane, 0, S::KS_DW);
     for (int x = 0; x < nt; ++x) {
-      read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
-      read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
+      walk.read(lds, S::STAGE_DW, ops);
       qk_tile<DH, R>(ops, rg, Sacc);
       const uint32_t orv = exp_tile_fast(Sacc, P);
       const bool first = first_chunk && x == 0;
@@ -1348,9 +1391,9 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
     if (act1) {
       f32x16_t Sb[1][2];
       uint32_t Pb[1][2][8];
+      OpsWalk<DH, R> walk(l32, gh, lane, 0, S::KS_DW);
       for (int x = 0; x < nt; ++x) {
-        read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
-        read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
+        walk.read(lds, S::STAGE_DW, ops);
         qk_tile<DH, R>(ops, rg0, Sacc);
         qk_tile<DH, R>(ops, rg1, Sb);
         (void)exp_tile_fast(Sacc, P);
@@ -1359,9 +1402,9 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
         pv_tile<DH, R>(ops, rg1, Pb);
       }
     } else if (act0) {
+      OpsWalk<DH, R> walk(l32, gh, lane, 0, S::KS_DW);
       for (int x = 0; x < nt; ++x) {
-        read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
-        read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
+        walk.read(lds, S::STAGE_DW, ops);
         qk_tile<DH, R>(ops, rg0, Sacc);
         (void)exp_tile_fast(Sacc, P);
         pv_tile<DH, R>(ops, rg0, P);
@@ -1398,9 +1441,9 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
       if (redo0 && redo1) {
         f32x16_t Sb[1][2];
         uint32_t Pb[1][2][8];
+        OpsWalk<DH, R> walk(l32, gh, lane, 0, S::KS_DW);
         for (int x = 0; x < nt; ++x) {
-          read_k_ops<DH, R>(lds, x * S::STAGE_DW, l32, gh, ops);
-          read_v_ops<DH, R>(lds, x * S::STAGE_DW + S::KS_DW, lane, ops);
+          walk.read(lds, S::STAGE_DW, ops);
           const bool first = ch == 0 && x == 0;
           qk_tile<DH, R>(ops, rg0, Sacc);
           qk_tile<DH, R>(ops, rg1, Sb);
