@@ -1307,7 +1307,11 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
 // of the row's largest.  There is no hand-off between
 // waves: three workgroups share a CU, and while one stages a chunk the others
 // compute.
-template <int DH, int R>
+// NP pairs of 32-query blocks per wave: NP = 1 (64 queries per wave, 256 per
+// workgroup, three workgroups per CU) or NP = 2 (128 per wave, 512 per
+// workgroup, two workgroups per CU: each staged chunk and each tile's operand
+// reads then serve twice the queries).
+template <int DH, int R, int NP = 1>
 __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
                        const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                        const float* __restrict__ qp, const float* __restrict__ kp,
@@ -1315,12 +1319,15 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
                        int total, long tstride, float* __restrict__ lse, int logical,
                        uint32_t* lds) {
   using S = Shape<DH, R>;
+  constexpr int NB = 2 * NP;       // 32-query blocks per wave
+  constexpr int WQ = 32 * NB;      // queries per wave
+  constexpr int CQ = 4 * WQ;       // queries per workgroup
 
   if (logical >= total) return;
-  const int qblocks = (wt * ws * ws + SQ - 1) / SQ;
+  const int qblocks = (wt * ws * ws + CQ - 1) / CQ;
   Geo G;
   decode_window<DH>(G, logical / qblocks, T, H, W, heads, wt, ws);
-  const int q0 = (logical % qblocks) * SQ;
+  const int q0 = (logical % qblocks) * CQ;
   if (q0 >= G.n_real) return;
   qp += (long)G.h * tstride;  // per-head positional tables (tstride 0: one shared pair)
   kp += (long)G.h * tstride;
@@ -1330,45 +1337,46 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
   const int l32 = lane & 31;
   const int gh = lane >> 5;
 
-  // Q~ operands of the wave's two query blocks, straight from global memory
+  // Q~ operands of the wave's query blocks, straight from global memory
   const float sp = LOG2E / sqrtf((float)R);
   const float sc = LOG2E / sqrtf((float)DH);
-  Regs<DH, R, 1> rg0, rg1;
+  Regs<DH, R, 1> rg[NB];
   const MapRsrc mr = map_rsrc(qp, qc, g, o, (unsigned)(B * T * H * W * heads * DH) * 2u,
                               (unsigned)(wt * ws * ws * R) * 4u);
-  auto init_block = [&](Regs<DH, R, 1>& rg, int qb) {
-    const int r = q0 + wave * QW + qb * 32 + l32;
+  const int wq0 = q0 + wave * WQ;  // first query of the wave
+  auto init_block = [&](Regs<DH, R, 1>& r_, int qb) {
+    const int r = wq0 + qb * 32 + l32;
     const bool real = r < G.n_real;
     int off, n;
     locate<DH>(G, real ? r : G.n_real - 1, off, n);
 #pragma unroll
     for (int c = 0; c < S::KC; ++c)
-      rg.qt[0][c] = qrow_group<DH, R>(8 * c + 4 * gh, off, n, real, mr.qp, mr.qc, sp, sc, 0xC2800000u);  // (0, -OFF_FAST)
+      r_.qt[0][c] = qrow_group<DH, R>(8 * c + 4 * gh, off, n, real, mr.qp, mr.qc, sp, sc, 0xC2800000u);  // (0, -OFF_FAST)
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) rg.O[0][dt][e] = 0.0f;
-    rg.mhat[0] = 0.0f;
-    rg.lpart[0] = 0.0f;
+      for (int e = 0; e < 16; ++e) r_.O[0][dt][e] = 0.0f;
+    r_.mhat[0] = 0.0f;
+    r_.lpart[0] = 0.0f;
   };
-  init_block(rg0, 0);
-  init_block(rg1, 1);
-  const bool act0 = q0 + wave * QW < G.n_real;  // wave-uniform
-  const bool act1 = q0 + wave * QW + 32 < G.n_real;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) init_block(rg[b], b);
+  // blocks holding a real query: a prefix of the wave's blocks (wave-uniform)
+  const int nact = G.n_real <= wq0 ? 0 : min(NB, (G.n_real - wq0 + 31) / 32);
   const int map_elems = B * T * H * W * heads * DH;
 
   PhaseOps<DH, R> ops;
   f32x16_t Sacc[1][2];
   uint32_t P[1][2][8];
-  auto run_tiles = [&](Regs<DH, R, 1>& rg, int nt, bool first_chunk) {
+  auto run_tiles = [&](Regs<DH, R, 1>& r_, int nt, bool first_chunk) {
     OpsWalk<DH, R> walk(l32, gh, lane, 0, S::KS_DW);
     for (int x = 0; x < nt; ++x) {
       walk.read(lds, S::STAGE_DW, ops);
-      qk_tile<DH, R>(ops, rg, Sacc);
+      qk_tile<DH, R>(ops, r_, Sacc);
       const uint32_t orv = exp_tile_fast(Sacc, P);
       const bool first = first_chunk && x == 0;
-      if (__builtin_amdgcn_ballot_w64(first || (orv & 0x40004000u))) rescale_tile<DH, R>(rg, Sacc, P, first, gh);
-      pv_tile<DH, R>(ops, rg, P);
+      if (__builtin_amdgcn_ballot_w64(first || (orv & 0x40004000u))) rescale_tile<DH, R>(r_, Sacc, P, first, gh);
+      pv_tile<DH, R>(ops, r_, P);
     }
   };
   const int nchunks = (G.n_real + SQ - 1) / SQ;
@@ -1385,92 +1393,81 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
       tiles(ch, left >= SQ ? SNT : (left + KT - 1) / KT);
     }
   };
-  // unchecked pass; both blocks: one operand read per tile, block 1's scores issue on
-  // the matrix core while block 0's exponentials run
+  // unchecked pass; a pair of blocks at a time: one operand read per tile for all
+  // blocks, the second block's scores issue on the matrix core while the first
+  // block's exponentials run
   over_chunks([&](int, int nt) {
-    if (act1) {
-      f32x16_t Sb[1][2];
-      uint32_t Pb[1][2][8];
-      OpsWalk<DH, R> walk(l32, gh, lane, 0, S::KS_DW);
-      for (int x = 0; x < nt; ++x) {
-        walk.read(lds, S::STAGE_DW, ops);
-        qk_tile<DH, R>(ops, rg0, Sacc);
-        qk_tile<DH, R>(ops, rg1, Sb);
-        (void)exp_tile_fast(Sacc, P);
-        pv_tile<DH, R>(ops, rg0, P);
-        (void)exp_tile_fast(Sb, Pb);
-        pv_tile<DH, R>(ops, rg1, Pb);
-      }
-    } else if (act0) {
-      OpsWalk<DH, R> walk(l32, gh, lane, 0, S::KS_DW);
-      for (int x = 0; x < nt; ++x) {
-        walk.read(lds, S::STAGE_DW, ops);
-        qk_tile<DH, R>(ops, rg0, Sacc);
-        (void)exp_tile_fast(Sacc, P);
-        pv_tile<DH, R>(ops, rg0, P);
+    if (nact == 0) return;
+    f32x16_t Sb[1][2];
+    uint32_t Pb[1][2][8];
+    OpsWalk<DH, R> walk(l32, gh, lane, 0, S::KS_DW);
+    for (int x = 0; x < nt; ++x) {
+      walk.read(lds, S::STAGE_DW, ops);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        if (2 * p + 1 < nact) {
+          qk_tile<DH, R>(ops, rg[2 * p], Sacc);
+          qk_tile<DH, R>(ops, rg[2 * p + 1], Sb);
+          (void)exp_tile_fast(Sacc, P);
+          pv_tile<DH, R>(ops, rg[2 * p], P);
+          (void)exp_tile_fast(Sb, Pb);
+          pv_tile<DH, R>(ops, rg[2 * p + 1], Pb);
+        } else if (2 * p < nact) {
+          qk_tile<DH, R>(ops, rg[2 * p], Sacc);
+          (void)exp_tile_fast(Sacc, P);
+          pv_tile<DH, R>(ops, rg[2 * p], P);
+        }
       }
     }
   });
   // a block fails if its row sum is below 2^-80 or its row sum or output is not finite
   // (wave-uniform)
-  auto failed = [&](Regs<DH, R, 1>& rg) -> bool {
-    float t = row_sum(rg, 0);
+  auto failed = [&](Regs<DH, R, 1>& r_) -> bool {
+    float t = row_sum(r_, 0);
     int bad = !(t >= 0x1p-80f);
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) t += rg.O[0][dt][e];
+      for (int e = 0; e < 16; ++e) t += r_.O[0][dt][e];
     bad |= !__builtin_isfinite(t);
     return __builtin_amdgcn_ballot_w64(bad) != 0;
   };
-  const bool redo0 = act0 && failed(rg0), redo1 = act1 && failed(rg1);
+  bool redo[NB];
+  bool any = false;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    redo[b] = b < nact && failed(rg[b]);
+    any |= redo[b];
+  }
   // every wave is past its tiles here, so the re-run may stage over the last chunk
-  if (__syncthreads_or(redo0 || redo1)) {
-    auto reset = [&](Regs<DH, R, 1>& rg) {
+  if (__syncthreads_or(any)) {
 #pragma unroll
-      for (int dt = 0; dt < S::DT; ++dt)
+    for (int b = 0; b < NB; ++b)
+      if (redo[b]) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) rg.O[0][dt][e] = 0.0f;
-      rg.mhat[0] = 0.0f;
-      rg.lpart[0] = 0.0f;
-      if (gh == S::GM) rg.qt[0][S::CM][S::DM] = 0xC0E00000u;  // (-m_hat = 0, -OFF = -7)
-    };
-    if (redo0) reset(rg0);
-    if (redo1) reset(rg1);
-    over_chunks([&](int ch, int nt) {
-      if (redo0 && redo1) {
-        f32x16_t Sb[1][2];
-        uint32_t Pb[1][2][8];
-        OpsWalk<DH, R> walk(l32, gh, lane, 0, S::KS_DW);
-        for (int x = 0; x < nt; ++x) {
-          walk.read(lds, S::STAGE_DW, ops);
-          const bool first = ch == 0 && x == 0;
-          qk_tile<DH, R>(ops, rg0, Sacc);
-          qk_tile<DH, R>(ops, rg1, Sb);
-          const uint32_t or0 = exp_tile_fast(Sacc, P);
-          if (__builtin_amdgcn_ballot_w64(first || (or0 & 0x40004000u))) rescale_tile<DH, R>(rg0, Sacc, P, first, gh);
-          pv_tile<DH, R>(ops, rg0, P);
-          const uint32_t or1 = exp_tile_fast(Sb, Pb);
-          if (__builtin_amdgcn_ballot_w64(first || (or1 & 0x40004000u))) rescale_tile<DH, R>(rg1, Sb, Pb, first, gh);
-          pv_tile<DH, R>(ops, rg1, Pb);
-        }
-      } else if (redo0) {
-        run_tiles(rg0, nt, ch == 0);
-      } else if (redo1) {
-        run_tiles(rg1, nt, ch == 0);
+        for (int dt = 0; dt < S::DT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) rg[b].O[0][dt][e] = 0.0f;
+        rg[b].mhat[0] = 0.0f;
+        rg[b].lpart[0] = 0.0f;
+        if (gh == S::GM) rg[b].qt[0][S::CM][S::DM] = 0xC0E00000u;  // (-m_hat = 0, -OFF = -7)
       }
+    over_chunks([&](int ch, int nt) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        if (redo[b]) run_tiles(rg[b], nt, ch == 0);
     });
   }
 
   // ---- epilogue: O / l * sigmoid(G), bf16, NHWC
-  auto finish = [&](const Regs<DH, R, 1>& rg, int qb, bool redone) {
-    const int r = q0 + wave * QW + qb * 32 + l32;
-    const float lsum = row_sum(rg, 0);
+  auto finish = [&](const Regs<DH, R, 1>& r_, int qb, bool redone) {
+    const int r = wq0 + qb * 32 + l32;
+    const float lsum = row_sum(r_, 0);
     if (r >= G.n_real) return;
     int off, n;
     locate<DH>(G, r, off, n);
     const float inv = rcp_approx(lsum);
-    if (lse) lse[(off - G.h * DH) / G.C * heads + G.h] = (rg.mhat[0] + (redone ? OFF : OFF_FAST) + __log2f(lsum)) * LN2;
+    if (lse) lse[(off - G.h * DH) / G.C * heads + G.h] = (r_.mhat[0] + (redone ? OFF : OFF_FAST) + __log2f(lsum)) * LN2;
 #pragma unroll
     for (int dt = 0; dt < S::DT; ++dt)
 #pragma unroll
@@ -1479,15 +1476,16 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
         if (d0 >= DH) continue;
         const int e0 = 4 * q4;
         const u32x2_t g4 = gate4(mr.g, off, d0);
-        const uint32_t r01 = pack_bf16(rg.O[0][dt][e0 + 0] * inv * sigmoidf(bf16_lo(g4[0])),
-                                       rg.O[0][dt][e0 + 1] * inv * sigmoidf(bf16_hi(g4[0])));
-        const uint32_t r23 = pack_bf16(rg.O[0][dt][e0 + 2] * inv * sigmoidf(bf16_lo(g4[1])),
-                                       rg.O[0][dt][e0 + 3] * inv * sigmoidf(bf16_hi(g4[1])));
+        const uint32_t r01 = pack_bf16(r_.O[0][dt][e0 + 0] * inv * sigmoidf(bf16_lo(g4[0])),
+                                       r_.O[0][dt][e0 + 1] * inv * sigmoidf(bf16_hi(g4[0])));
+        const uint32_t r23 = pack_bf16(r_.O[0][dt][e0 + 2] * inv * sigmoidf(bf16_lo(g4[1])),
+                                       r_.O[0][dt][e0 + 3] * inv * sigmoidf(bf16_hi(g4[1])));
         store4(mr.o, off, d0, r01, r23, d0 + 4 <= DH);
       }
   };
-  if (act0) finish(rg0, 0, redo0);
-  if (act1) finish(rg1, 1, redo1);
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    if (b < nact) finish(rg[b], b, redo[b]);
 }
 
 // Workgroup -> logical index (window * heads + head) * qblocks + query block
@@ -1579,18 +1577,24 @@ attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
                          window_unit(blockIdx.x, heads), lds);
 }
 
-template <int DH, int R>
-__global__ void __launch_bounds__(SQ, 3)
+// NP = 2 (four blocks per wave, two workgroups per CU) only for the shapes
+// whose four blocks fit 256 registers.
+constexpr bool chunk_two_pairs(int dh, int R) {
+  return (dh == 30 && R == 16) || (dh == 16 && R == 16) || (dh == 8 && R == 8);
+}
+
+template <int DH, int R, int NP>
+__global__ void __launch_bounds__(SQ, NP == 2 ? 2 : 3)
 attn_bf16_chunk_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
                        const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                        const float* __restrict__ qp, const float* __restrict__ kp,
                        uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws,
                        int total, long tstride, float* __restrict__ lse, int whole_windows) {
   __shared__ __attribute__((aligned(16))) uint32_t lds[SNT * Shape<DH, R>::STAGE_DW];
-  const int qblocks = (wt * ws * ws + SQ - 1) / SQ;
-  attn_chunk_body<DH, R>(qc, kc, v, g, qp, kp, o, B, T, H, W, heads, wt, ws, total, tstride, lse,
-                         whole_windows ? window_block_qb(blockIdx.x, heads, qblocks)
-                                       : interleave_logical(blockIdx.x, qblocks), lds);
+  const int qblocks = (wt * ws * ws + 256 * NP - 1) / (256 * NP);
+  attn_chunk_body<DH, R, NP>(qc, kc, v, g, qp, kp, o, B, T, H, W, heads, wt, ws, total, tstride, lse,
+                             whole_windows ? window_block_qb(blockIdx.x, heads, qblocks)
+                                           : interleave_logical(blockIdx.x, qblocks), lds);
 }
 
 // Which kernel a call takes: the whole-window kernel up to SQ tokens per
@@ -1702,14 +1706,28 @@ inline Kind call_kind(const AttnArgs& a, int cus) {
 inline bool chunk_whole(const AttnArgs& a) {
   return a.wt * a.ws * a.ws <= CHUNK_MAX || (call_units(a) / a.heads) % 8 == 0;
 }
-// query blocks per window unit for a kernel kind
-inline int kind_qblocks(const AttnArgs& a, Kind k) {
-  const int NW = a.wt * a.ws * a.ws;
-  return k == WHOLE ? 1 : k == CHUNKED ? (NW + SQ - 1) / SQ : (NW + QB - 1) / QB;
+// Block pairs per wave of a chunked call's own launch (a grouped launch always
+// takes one).  Two pairs stage each key chunk for 512 queries instead of 256
+// and read each tile's operands for 128 queries per wave instead of 64, but
+// make half as many, larger workgroups; they pay only where the grid still
+// fills at least four rounds of two workgroups per CU.  Same box, interleaved
+// rounds: 32 x 96x96 at C = 180 2.412 -> 2.367 ms, 1x360x640 with 96x96
+// windows 1.775 -> 1.729 ms; with two pairs 64x64 windows at C = 180 took
+// 0.2422 against 0.2365 ms, and 32x32 and 64x64 windows at C = 48 17-18% longer.
+inline int chunk_pairs(const AttnArgs& a, int cus) {
+  if (!chunk_two_pairs(a.dh, a.R)) return 1;
+  const long wgs = (long)call_units(a) * ((a.wt * a.ws * a.ws + 511) / 512);
+  return wgs >= 8L * cus ? 2 : 1;
+}
+// query blocks per window unit for a kernel kind (np: block pairs per wave of a
+// chunked call)
+inline int kind_qblocks(const AttnArgs& a, Kind k, int np = 1) {
+  const int NW = a.wt * a.ws * a.ws, CQ = 256 * np;
+  return k == WHOLE ? 1 : k == CHUNKED ? (NW + CQ - 1) / CQ : (NW + QB - 1) / QB;
 }
 // workgroups of a call's grid range
-inline int kind_grid(const AttnArgs& a, Kind k) {
-  const int units = call_units(a), windows = units / a.heads, qb = kind_qblocks(a, k);
+inline int kind_grid(const AttnArgs& a, Kind k, int np = 1) {
+  const int units = call_units(a), windows = units / a.heads, qb = kind_qblocks(a, k, np);
   const bool by_unit = k == TILED || (k == CHUNKED && !chunk_whole(a));
   return by_unit ? 8 * ((units + 7) / 8) * qb                // see interleave_logical
                  : 8 * ((windows + 7) / 8) * a.heads * qb;   // see window_unit, window_block
@@ -1717,8 +1735,10 @@ inline int kind_grid(const AttnArgs& a, Kind k) {
 
 template <int DH, int R>
 hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
-  const Kind kind = call_kind(a, device_cus());
-  const int units = call_units(a), qb = kind_qblocks(a, kind), grid = kind_grid(a, kind);
+  const int cus = device_cus();
+  const Kind kind = call_kind(a, cus);
+  const int np = kind == CHUNKED ? chunk_pairs(a, cus) : 1;
+  const int units = call_units(a), qb = kind_qblocks(a, kind, np), grid = kind_grid(a, kind, np);
   const uint32_t* qc = (const uint32_t*)a.qc;
   const uint32_t* kc = (const uint32_t*)a.kc;
   const uint32_t* v = (const uint32_t*)a.v;
@@ -1726,10 +1746,20 @@ hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
   if (kind == WHOLE)
     hipLaunchKernelGGL((attn_bf16_small_kernel<DH, R>), dim3(grid), dim3(SQ), 0, stream, qc, kc, v, g, a.qp, a.kp,
                        (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units, a.tstride, a.lse);
-  else if (kind == CHUNKED)
-    hipLaunchKernelGGL((attn_bf16_chunk_kernel<DH, R>), dim3(grid), dim3(SQ), 0, stream, qc, kc, v, g, a.qp, a.kp,
-                       (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units * qb, a.tstride, a.lse,
-                       chunk_whole(a) ? 1 : 0);
+  else if (kind == CHUNKED) {
+    bool two = false;
+    if constexpr (chunk_two_pairs(DH, R)) {
+      two = np == 2;
+      if (two)
+        hipLaunchKernelGGL((attn_bf16_chunk_kernel<DH, R, 2>), dim3(grid), dim3(SQ), 0, stream, qc, kc, v, g, a.qp,
+                           a.kp, (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units * qb, a.tstride,
+                           a.lse, chunk_whole(a) ? 1 : 0);
+    }
+    if (!two)
+      hipLaunchKernelGGL((attn_bf16_chunk_kernel<DH, R, 1>), dim3(grid), dim3(SQ), 0, stream, qc, kc, v, g, a.qp,
+                         a.kp, (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units * qb, a.tstride,
+                         a.lse, chunk_whole(a) ? 1 : 0);
+  }
   else
     hipLaunchKernelGGL((attn_bf16_kernel<DH, R>), dim3(grid), dim3(QB), 0, stream, qc, kc, v, g, a.qp, a.kp,
                        (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units * qb, a.tstride, a.lse,
