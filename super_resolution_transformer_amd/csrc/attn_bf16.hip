@@ -1307,11 +1307,11 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
 // of the row's largest.  There is no hand-off between
 // waves: three workgroups share a CU, and while one stages a chunk the others
 // compute.
-// NP pairs of 32-query blocks per wave: NP = 1 (64 queries per wave, 256 per
-// workgroup, three workgroups per CU) or NP = 2 (128 per wave, 512 per
+// NB 32-query blocks per wave: NB = 2 (64 queries per wave, 256 per workgroup,
+// three workgroups per CU), 3 or 4 (96 or 128 per wave, 384 or 512 per
 // workgroup, two workgroups per CU: each staged chunk and each tile's operand
-// reads then serve twice the queries).
-template <int DH, int R, int NP = 1>
+// reads then serve 1.5 or 2 times the queries).
+template <int DH, int R, int NB = 2>
 __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
                        const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                        const float* __restrict__ qp, const float* __restrict__ kp,
@@ -1319,7 +1319,6 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
                        int total, long tstride, float* __restrict__ lse, int logical,
                        uint32_t* lds) {
   using S = Shape<DH, R>;
-  constexpr int NB = 2 * NP;       // 32-query blocks per wave
   constexpr int WQ = 32 * NB;      // queries per wave
   constexpr int CQ = 4 * WQ;       // queries per workgroup
 
@@ -1404,14 +1403,15 @@ __device__ __forceinline__ void attn_chunk_body(const uint32_t* __restrict__ qc,
     for (int x = 0; x < nt; ++x) {
       walk.read(lds, S::STAGE_DW, ops);
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        if (2 * p + 1 < nact) {
+      for (int p = 0; p < (NB + 1) / 2; ++p) {
+        const int q1 = 2 * p + 1 < NB ? 2 * p + 1 : 2 * p;  // the pair's second block, if any
+        if (2 * p + 1 < NB && q1 < nact) {
           qk_tile<DH, R>(ops, rg[2 * p], Sacc);
-          qk_tile<DH, R>(ops, rg[2 * p + 1], Sb);
+          qk_tile<DH, R>(ops, rg[q1], Sb);
           (void)exp_tile_fast(Sacc, P);
           pv_tile<DH, R>(ops, rg[2 * p], P);
           (void)exp_tile_fast(Sb, Pb);
-          pv_tile<DH, R>(ops, rg[2 * p + 1], Pb);
+          pv_tile<DH, R>(ops, rg[q1], Pb);
         } else if (2 * p < nact) {
           qk_tile<DH, R>(ops, rg[2 * p], Sacc);
           (void)exp_tile_fast(Sacc, P);
@@ -1577,22 +1577,22 @@ attn_bf16_small_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
                          window_unit(blockIdx.x, heads), lds);
 }
 
-// NP = 2 (four blocks per wave, two workgroups per CU) only for the shapes
-// whose four blocks fit 256 registers.
-constexpr bool chunk_two_pairs(int dh, int R) {
+// More than two blocks per wave (two workgroups per CU) only for the shapes
+// whose blocks then still fit 256 registers.
+constexpr bool chunk_more_blocks(int dh, int R) {
   return (dh == 30 && R == 16) || (dh == 16 && R == 16) || (dh == 8 && R == 8);
 }
 
-template <int DH, int R, int NP>
-__global__ void __launch_bounds__(SQ, NP == 2 ? 2 : 3)
+template <int DH, int R, int NB>
+__global__ void __launch_bounds__(SQ, NB == 2 ? 3 : 2)
 attn_bf16_chunk_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restrict__ kc,
                        const uint32_t* __restrict__ v, const uint32_t* __restrict__ g,
                        const float* __restrict__ qp, const float* __restrict__ kp,
                        uint32_t* __restrict__ o, int B, int T, int H, int W, int heads, int wt, int ws,
                        int total, long tstride, float* __restrict__ lse, int whole_windows) {
   __shared__ __attribute__((aligned(16))) uint32_t lds[SNT * Shape<DH, R>::STAGE_DW];
-  const int qblocks = (wt * ws * ws + 256 * NP - 1) / (256 * NP);
-  attn_chunk_body<DH, R, NP>(qc, kc, v, g, qp, kp, o, B, T, H, W, heads, wt, ws, total, tstride, lse,
+  const int qblocks = (wt * ws * ws + 128 * NB - 1) / (128 * NB);
+  attn_chunk_body<DH, R, NB>(qc, kc, v, g, qp, kp, o, B, T, H, W, heads, wt, ws, total, tstride, lse,
                              whole_windows ? window_block_qb(blockIdx.x, heads, qblocks)
                                            : interleave_logical(blockIdx.x, qblocks), lds);
 }
@@ -1682,7 +1682,7 @@ __global__ void __launch_bounds__(SQ, 3) attn_bf16_window_group_kernel(const Cal
     attn_small_body<DH, R>(c.qc, c.kc, c.v, c.g, c.qp, c.kp, c.o, c.B, c.T, c.H, c.W, c.heads, c.wt, c.ws,
                            c.units, c.tstride, c.lse, window_unit(lb, c.heads), lds);
   else
-    attn_chunk_body<DH, R>(c.qc, c.kc, c.v, c.g, c.qp, c.kp, c.o, c.B, c.T, c.H, c.W, c.heads, c.wt, c.ws,
+    attn_chunk_body<DH, R, 2>(c.qc, c.kc, c.v, c.g, c.qp, c.kp, c.o, c.B, c.T, c.H, c.W, c.heads, c.wt, c.ws,
                            c.units * c.qblocks, c.tstride, c.lse,
                            c.whole ? window_block_qb(lb, c.heads, c.qblocks) : interleave_logical(lb, c.qblocks), lds);
 }
@@ -1706,28 +1706,36 @@ inline Kind call_kind(const AttnArgs& a, int cus) {
 inline bool chunk_whole(const AttnArgs& a) {
   return a.wt * a.ws * a.ws <= CHUNK_MAX || (call_units(a) / a.heads) % 8 == 0;
 }
-// Block pairs per wave of a chunked call's own launch (a grouped launch always
-// takes one).  Two pairs stage each key chunk for 512 queries instead of 256
-// and read each tile's operands for 128 queries per wave instead of 64, but
-// make half as many, larger workgroups; they pay only where the grid still
-// fills at least four rounds of two workgroups per CU.  Same box, interleaved
-// rounds: 32 x 96x96 at C = 180 2.412 -> 2.367 ms, 1x360x640 with 96x96
-// windows 1.775 -> 1.729 ms; with two pairs 64x64 windows at C = 180 took
-// 0.2422 against 0.2365 ms, and 32x32 and 64x64 windows at C = 48 17-18% longer.
-inline int chunk_pairs(const AttnArgs& a, int cus) {
-  if (!chunk_two_pairs(a.dh, a.R)) return 1;
-  const long wgs = (long)call_units(a) * ((a.wt * a.ws * a.ws + 511) / 512);
-  return wgs >= 8L * cus ? 2 : 1;
+// 32-query blocks per wave of a chunked call's own launch (a grouped launch
+// always takes two).  More blocks stage each key chunk and read each tile's
+// operands for more queries, but make fewer, larger workgroups at two per CU.
+// Measured, same box, interleaved rounds, bit-identical outputs (ms with 2 / 3 /
+// 4 blocks): 32 x 96x96 at C = 180 2.426 / 2.408 / 2.355; 1x360x640 with 96x96
+// windows 1.784 / 1.796 / 1.718; 64x64 windows at C = 180 0.2321 / 0.2286 /
+// 0.2317; 32x32 windows at C = 180 0.0717 / 0.0783 / 0.0709; 8 frames with
+// 2x32x32 windows 0.945 / 1.009 / 0.921, with 4x16x16 windows 0.571 / 0.617 /
+// 0.572; 32x32 and 64x64 windows at C = 48 (SST-lite): 0.0349 / 0.0430 / 0.0408
+// and 0.108 / 0.115 / 0.122.  Four blocks pay once the grid fills four rounds of
+// two workgroups per CU; three only on windows of 4,096 tokens or more (a
+// 384-query block wastes up to a third of a workgroup on smaller ones) whose
+// grid still fills 1.75 rounds.
+inline int chunk_blocks(const AttnArgs& a, int cus) {
+  if (!chunk_more_blocks(a.dh, a.R)) return 2;
+  const int NW = a.wt * a.ws * a.ws;
+  const long units = call_units(a);
+  if (units * ((NW + 511) / 512) >= 8L * cus) return 4;
+  if (NW >= 4096 && 2 * units * ((NW + 383) / 384) >= 7L * cus) return 3;
+  return 2;
 }
-// query blocks per window unit for a kernel kind (np: block pairs per wave of a
-// chunked call)
-inline int kind_qblocks(const AttnArgs& a, Kind k, int np = 1) {
-  const int NW = a.wt * a.ws * a.ws, CQ = 256 * np;
+// query blocks per window unit for a kernel kind (nb: 32-query blocks per wave
+// of a chunked call)
+inline int kind_qblocks(const AttnArgs& a, Kind k, int nb = 2) {
+  const int NW = a.wt * a.ws * a.ws, CQ = 128 * nb;
   return k == WHOLE ? 1 : k == CHUNKED ? (NW + CQ - 1) / CQ : (NW + QB - 1) / QB;
 }
 // workgroups of a call's grid range
-inline int kind_grid(const AttnArgs& a, Kind k, int np = 1) {
-  const int units = call_units(a), windows = units / a.heads, qb = kind_qblocks(a, k, np);
+inline int kind_grid(const AttnArgs& a, Kind k, int nb = 2) {
+  const int units = call_units(a), windows = units / a.heads, qb = kind_qblocks(a, k, nb);
   const bool by_unit = k == TILED || (k == CHUNKED && !chunk_whole(a));
   return by_unit ? 8 * ((units + 7) / 8) * qb                // see interleave_logical
                  : 8 * ((windows + 7) / 8) * a.heads * qb;   // see window_unit, window_block
@@ -1737,8 +1745,8 @@ template <int DH, int R>
 hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
   const int cus = device_cus();
   const Kind kind = call_kind(a, cus);
-  const int np = kind == CHUNKED ? chunk_pairs(a, cus) : 1;
-  const int units = call_units(a), qb = kind_qblocks(a, kind, np), grid = kind_grid(a, kind, np);
+  const int nb = kind == CHUNKED ? chunk_blocks(a, cus) : 2;
+  const int units = call_units(a), qb = kind_qblocks(a, kind, nb), grid = kind_grid(a, kind, nb);
   const uint32_t* qc = (const uint32_t*)a.qc;
   const uint32_t* kc = (const uint32_t*)a.kc;
   const uint32_t* v = (const uint32_t*)a.v;
@@ -1747,18 +1755,16 @@ hipError_t launch_variant(const AttnArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((attn_bf16_small_kernel<DH, R>), dim3(grid), dim3(SQ), 0, stream, qc, kc, v, g, a.qp, a.kp,
                        (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units, a.tstride, a.lse);
   else if (kind == CHUNKED) {
-    bool two = false;
-    if constexpr (chunk_two_pairs(DH, R)) {
-      two = np == 2;
-      if (two)
-        hipLaunchKernelGGL((attn_bf16_chunk_kernel<DH, R, 2>), dim3(grid), dim3(SQ), 0, stream, qc, kc, v, g, a.qp,
-                           a.kp, (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units * qb, a.tstride,
-                           a.lse, chunk_whole(a) ? 1 : 0);
+    auto launch = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(SQ), 0, stream, qc, kc, v, g, a.qp, a.kp, (uint32_t*)a.o, a.B, a.T,
+                         a.H, a.W, a.heads, a.wt, a.ws, units * qb, a.tstride, a.lse, chunk_whole(a) ? 1 : 0);
+    };
+    bool done = false;
+    if constexpr (chunk_more_blocks(DH, R)) {
+      if (nb == 4) launch(attn_bf16_chunk_kernel<DH, R, 4>), done = true;
+      if (nb == 3) launch(attn_bf16_chunk_kernel<DH, R, 3>), done = true;
     }
-    if (!two)
-      hipLaunchKernelGGL((attn_bf16_chunk_kernel<DH, R, 1>), dim3(grid), dim3(SQ), 0, stream, qc, kc, v, g, a.qp,
-                         a.kp, (uint32_t*)a.o, a.B, a.T, a.H, a.W, a.heads, a.wt, a.ws, units * qb, a.tstride,
-                         a.lse, chunk_whole(a) ? 1 : 0);
+    if (!done) launch(attn_bf16_chunk_kernel<DH, R, 2>);
   }
   else
     hipLaunchKernelGGL((attn_bf16_kernel<DH, R>), dim3(grid), dim3(QB), 0, stream, qc, kc, v, g, a.qp, a.kp,
