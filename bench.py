@@ -524,7 +524,7 @@ def main():
         "ms_encode": ms_enc,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
-                     "kernel": "attn_bf16_chunk_kernel<30,16,2>", "algorithmic_flop_per_launch": wl.F,
+                     "kernel": "attn_bf16_chunk_kernel<30,16,4>", "algorithmic_flop_per_launch": wl.F,
                      "launch_ms_p10_p50_p90": [attn_list[len(attn_list) // 10], attn_list[len(attn_list) // 2],
                                                attn_list[(9 * len(attn_list)) // 10]]},
     }
