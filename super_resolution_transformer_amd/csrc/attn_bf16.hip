@@ -9,7 +9,13 @@
 // (The pages concatenate content first; the column order of a contraction does
 // not change its value, and positional-first keeps the LDS rows aligned.)
 //
-// Design (one workgroup = 8 waves = 512 queries of one (image, window, head)):
+// Three kernels: the whole-window kernel (windows of up to 256 tokens), the
+// chunked kernel (larger windows; both below) and the tiled kernel, whose
+// design follows (it takes the head shapes whose chunked kernel spills
+// registers, and the fused LayerNorm + Q projection).  Most points below hold
+// for all three; the ping-pong is the tiled kernel's own.
+//
+// Tiled kernel (one workgroup = 8 waves = 512 queries of one (image, window, head)):
 //
 //  * Scores are computed transposed, S^T = K~ Q~^T, with
 //    v_mfma_f32_32x32x16_bf16: K~ rows are the A operand (read from LDS), the
@@ -1287,14 +1293,14 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
 }
 
 // ---- windows of more than 256 tokens: the chunked kernel ----------------------
-// One workgroup of four waves takes SQ = 256 queries of one (window, head); the
-// window's keys pass through LDS in chunks of 256 (four 64-key tiles), every
-// thread staging one key of a chunk as in the whole-window kernel.  Each wave
-// keeps both of its 32-query blocks (Q~ operands, O, reference) in registers
-// across the chunks; per tile it reads the K~ and V operands once, issues both
-// blocks' score products, and runs block 0's exponentials while block 1's
-// scores are still on the matrix core.  (Two values the epilogue needs spill
-// to scratch, once per wave, outside the loop.)
+// One workgroup of four waves takes the queries of NB 32-query blocks per wave
+// (256, 384 or 512) of one (window, head); the window's keys pass through LDS
+// in chunks of 256 (four 64-key tiles), every thread staging one key of a
+// chunk as in the whole-window kernel.  Each wave keeps its blocks (Q~
+// operands, O, reference) in registers across the chunks; per tile it reads
+// the K~ and V operands once for all of them and takes the blocks in pairs:
+// both blocks' score products, then the first block's exponentials while the
+// second block's scores are still on the matrix core.
 // The softmax first runs unchecked, as the whole-window kernel's first pass
 // does: every tile against the fixed reference 0 with the offset OFF_FAST.  A
 // 32-query block whose row sum ends below 2^-80 or whose row sum or output is
@@ -1305,8 +1311,8 @@ __device__ __forceinline__ void attn_small_body(const uint32_t* __restrict__ qc,
 // l <= n 2^(s_max - 64) over its n <= 16,384 keys, so s_max >= -30 base-2
 // units: keys that flush to zero (more than 62 below 0) each weigh under 2^-32
 // of the row's largest.  There is no hand-off between
-// waves: three workgroups share a CU, and while one stages a chunk the others
-// compute.
+// waves: three workgroups (two with three or four blocks per wave) share a CU,
+// and while one stages a chunk the others compute.
 // NB 32-query blocks per wave: NB = 2 (64 queries per wave, 256 per workgroup,
 // three workgroups per CU), 3 or 4 (96 or 128 per wave, 384 or 512 per
 // workgroup, two workgroups per CU: each staged chunk and each tile's operand
