@@ -1605,8 +1605,8 @@ attn_bf16_chunk_kernel(const uint32_t* __restrict__ qc, const uint32_t* __restri
 
 // Which kernel a call takes: the whole-window kernel up to SQ tokens per
 // window, the chunked kernel above that.  The (dh, R) shapes whose chunked
-// kernel spills more registers ((32, 16), (16, 32), (30, 32): 56-116 bytes per
-// lane against 16-32 for the others; not timed on the chunked kernel) keep the
+// kernel spills registers ((32, 16), (16, 32), (30, 32): 52-124 bytes per lane
+// against at most 8 for the others; not timed on the chunked kernel) keep the
 // tiled kernel for windows of more than CHUNK_MAX tokens, unless the chunked
 // grid is resident at once (three workgroups per CU, up to CHUNK_FIT tokens).
 // Measured on the (30, 16) and (16, 16) shapes (same process, interleaved
