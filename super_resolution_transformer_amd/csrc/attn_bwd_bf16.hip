@@ -1,5 +1,5 @@
 // attn_bwd_bf16.hip -- backward of RIB window attention on bf16 matrix cores
-// (gfx950, v_mfma_f32_32x32x16_bf16).
+// (gfx950, v_mfma_f32_32x32x16_bf16 and v_mfma_f32_16x16x32_bf16).
 //
 // The gradients of O = (softmax(S) V) * sigmoid(G), S = Qt Kt^T with the
 // augmented rows Qt = [Qp/sqrt(R), Qc/sqrt(dh)], Kt = [Kp, Kc] ("Rank-
@@ -33,7 +33,12 @@
 // rows with the transposing ds_read_b64_tr_b16 (the forward kernel's PV
 // trick).  dkv pass (key-major): the mirror image, lane = key: S = Qt Kt^T,
 // dP - D = dA' V'^T, then dV'^T += dA'^T P and dKt^T += Qt^T dS.
-// Two workgroups share a CU (208-240 registers per lane), each waiting only at
+// Where the augmented gradient has 33-48 columns (dh = 30, R = 16: 46), its
+// columns 32-47 come from two 16x16x32 products per 32-row block instead of a
+// 32x32 tile whose upper half would be padding: both operands are regrouped
+// across 16-lane rows with v_permlane16_swap (4 per operand), half the matrix
+// core time of the padded tile (4.6% off the whole backward at 32 x 96x96).
+// Two workgroups share a CU (164 and 255 registers per lane), each waiting only at
 // its own per-tile barrier; one workgroup of 8 waves and 512 rows per CU took
 // 4% longer on the 32 x 96x96 workload (bit-identical gradients).
 //
@@ -66,6 +71,10 @@ struct BS {
   static constexpr int KC = (R + DH + 2 + 15) / 16;  // 16-column chunks of an augmented row
   static constexpr int DC = (DH + 2 + 15) / 16;      // 16-column chunks of a value / gradient row
   static constexpr int MT = (R + DH + 31) / 32;      // 32-column tiles of an augmented gradient
+  // the last tile holds at most 16 useful columns: computed as two 16x16x32
+  // products (columns 32-47 only) instead of a 32-column tile
+  static constexpr bool H16 = MT == 2 && R + DH <= 48;
+  static constexpr int MF = H16 ? 1 : MT;            // 32-column tiles computed as such
   static constexpr int AP = 2 * KC;                  // 8-column pieces of an augmented row
   static constexpr int NP = AP + 2 * DC;             // pieces staged per streamed row
   static constexpr int A_DW = 2 * KC * CS;           // dwords of the augmented tile
@@ -277,6 +286,36 @@ __device__ __forceinline__ f32x16_t zero16() {
   return z;
 }
 
+// A 16 x 16 product over 32 contraction rows: lane l holds row (A) or column
+// (B) l % 16 with contraction rows 8(l/16) .. +7, and the result rows
+// 4(l/16) .. +3 of column l % 16.
+__device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// Two 32x32x16 operands x (contraction rows 0-15) and y (rows 16-31) of one
+// 32-row block, regrouped for 16x16x32 products by swapping 16-lane rows
+// (v_permlane16_swap: the odd rows of x trade places with the even rows of
+// y).  Lane half h of x holds rows {4h..4h+3, 8+4h..8+4h+3} of the block's
+// first 16, of y the same rows of the second 16.  Afterwards lo holds rows
+// 0-15 of the block (columns or rows l % 16) and hi rows 16-31, and in both
+// the lane groups l/16 = 0..3 carry the contraction rows of (x, h = 0),
+// (y, h = 0), (x, h = 1), (y, h = 1): all 32, the same in lo and hi.
+struct Halves {
+  u32x4_t lo, hi;
+};
+__device__ __forceinline__ Halves regroup16(const u32x4_t& x, const u32x4_t& y) {
+  Halves r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x[i], y[i], false, false);
+    r.lo[i] = p[0];
+    r.hi[i] = p[1];
+  }
+  return r;
+}
+
 // Shared frame of both passes: the unit, this wave's own rows and the
 // streamed side's packed image.
 template <int DH, int R>
@@ -351,12 +390,14 @@ bwd_dq_bf16_kernel(BwdArgs a, int total) {
   const int l32 = f.l32, hh = f.hh;
 
   u32x4_t qt[2][S::KC], dat[2][2];
-  f32x16_t acc[2][S::MT];
+  f32x16_t acc[2][S::MF];
+  f32x4_t acc16[2][2];  // H16: columns 32-47 of rows 0-15 and 16-31 of each block
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     f.own_row(f.r0 + qb * 32 + l32, qt[qb], dat[qb]);
 #pragma unroll
-    for (int mt = 0; mt < S::MT; ++mt) acc[qb][mt] = zero16();
+    for (int mt = 0; mt < S::MF; ++mt) acc[qb][mt] = zero16();
+    acc16[qb][0] = acc16[qb][1] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
   }
 
   f.issue(lds0, 0);
@@ -380,6 +421,8 @@ bwd_dq_bf16_kernel(BwdArgs a, int total) {
         for (int mt = 0; mt < S::MT; ++mt)
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) kt[mt][c2] = tr_operand(cur, 0, lb, kb * 32 + 16 * c2, 32 * mt);
+        u32x4_t k16;  // H16: the last tile's operand for columns 32-47
+        if constexpr (S::H16) k16 = regroup16(kt[1][0], kt[1][1]).lo;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
           f32x16_t s = zero16(), d = zero16();
@@ -392,12 +435,16 @@ bwd_dq_bf16_kernel(BwdArgs a, int total) {
           for (int i = 0; i < 8; ++i)
             ds[i] = pack_bf16(__builtin_amdgcn_exp2f(s[2 * i]) * d[2 * i],
                               __builtin_amdgcn_exp2f(s[2 * i + 1]) * d[2 * i + 1]);
+          const u32x4_t db[2] = {{ds[0], ds[1], ds[2], ds[3]}, {ds[4], ds[5], ds[6], ds[7]}};
 #pragma unroll
-          for (int mt = 0; mt < S::MT; ++mt)
+          for (int mt = 0; mt < S::MF; ++mt)
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2)
-              acc[qb][mt] = mfma(kt[mt][c2], (u32x4_t){ds[4 * c2], ds[4 * c2 + 1], ds[4 * c2 + 2], ds[4 * c2 + 3]},
-                                 acc[qb][mt]);
+            for (int c2 = 0; c2 < 2; ++c2) acc[qb][mt] = mfma(kt[mt][c2], db[c2], acc[qb][mt]);
+          if constexpr (S::H16) {
+            const Halves b = regroup16(db[0], db[1]);
+            acc16[qb][0] = mfma16(k16, b.lo, acc16[qb][0]);
+            acc16[qb][1] = mfma16(k16, b.hi, acc16[qb][1]);
+          }
         }
       }
     }
@@ -411,34 +458,49 @@ bwd_dq_bf16_kernel(BwdArgs a, int total) {
   if (!f.active) return;
 
   // ---- epilogue: register e of acc[qb][mt] is column 32mt + 8(e/4) + 4hh + e%4
+  // of row l32; register i of acc16[qb][h] column 32 + 4(lane/16) + i of row
+  // 16h + lane%16
   const Unit& u = f.u;
   const int C = a.heads * DH;
   const float gq = 1.0f / sqrtf((float)R), gc = 1.0f / sqrtf((float)DH);
   uint32_t* dqc = (uint32_t*)a.dqc;
+  // columns c0 .. c0+3 of the own row at token tok
+  auto put4 = [&](long tok, int c0, float x0, float x1, float x2, float x3) {
+    if (c0 + 4 <= R) {
+      float* qrow = a.qrows + (((long)u.h * a.B + u.b) * a.H * a.W + (tok - (long)u.b * a.H * a.W)) * R;
+      *reinterpret_cast<float4*>(qrow + c0) = make_float4(x0 * gq, x1 * gq, x2 * gq, x3 * gq);
+    } else if (c0 >= R && c0 < R + DH) {
+      const long e = (tok * C + (long)u.h * DH + c0 - R) >> 1;
+      dqc[e] = pack_bf16(x0 * gc, x1 * gc);
+      if (c0 + 2 < R + DH) dqc[e + 1] = pack_bf16(x2 * gc, x3 * gc);
+    }
+  };
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int r = f.r0 + qb * 32 + l32;
-    if (r >= u.n_real) continue;
     long tok;
     int n;
-    locate(u, a, r, tok, n);
-    const long cofs = tok * C + (long)u.h * DH;
-    float* qrow = a.qrows + (((long)u.h * a.B + u.b) * a.H * a.W + (tok - (long)u.b * a.H * a.W)) * R;
+    if (r < u.n_real) {
+      locate(u, a, r, tok, n);
 #pragma unroll
-    for (int mt = 0; mt < S::MT; ++mt)
+      for (int mt = 0; mt < S::MF; ++mt)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int c0 = 32 * mt + 8 * g4 + 4 * hh;  // first of 4 consecutive columns
-        const f32x16_t& x = acc[qb][mt];
-        if (c0 + 4 <= R) {
-          *reinterpret_cast<float4*>(qrow + c0) =
-              make_float4(x[4 * g4] * gq, x[4 * g4 + 1] * gq, x[4 * g4 + 2] * gq, x[4 * g4 + 3] * gq);
-        } else if (c0 >= R && c0 < R + DH) {
-          const long e = (cofs + c0 - R) >> 1;
-          dqc[e] = pack_bf16(x[4 * g4] * gc, x[4 * g4 + 1] * gc);
-          if (c0 + 2 < R + DH) dqc[e + 1] = pack_bf16(x[4 * g4 + 2] * gc, x[4 * g4 + 3] * gc);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x16_t& x = acc[qb][mt];
+          put4(tok, 32 * mt + 8 * g4 + 4 * hh, x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]);
+        }
+    }
+    if constexpr (S::H16) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r16 = f.r0 + qb * 32 + 16 * h + (f.lane & 15);
+        const f32x4_t& x = acc16[qb][h];
+        if (r16 < u.n_real) {
+          locate(u, a, r16, tok, n);
+          put4(tok, 32 + 4 * (f.lane >> 4), x[0], x[1], x[2], x[3]);
         }
       }
+    }
   }
 }
 
@@ -455,13 +517,15 @@ bwd_dkv_bf16_kernel(BwdArgs a, int total) {
   const int l32 = f.l32, hh = f.hh;
 
   u32x4_t kt[2][S::KC], vt[2][2];
-  f32x16_t accv[2], acck[2][S::MT];
+  f32x16_t accv[2], acck[2][S::MF];
+  f32x4_t acck16[2][2];  // H16: columns 32-47 of rows 0-15 and 16-31 of each block
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     f.own_row(f.r0 + kb * 32 + l32, kt[kb], vt[kb]);
     accv[kb] = zero16();
 #pragma unroll
-    for (int mt = 0; mt < S::MT; ++mt) acck[kb][mt] = zero16();
+    for (int mt = 0; mt < S::MF; ++mt) acck[kb][mt] = zero16();
+    acck16[kb][0] = acck16[kb][1] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
   }
 
   f.issue(lds0, 0);
@@ -487,6 +551,8 @@ bwd_dkv_bf16_kernel(BwdArgs a, int total) {
         for (int mt = 0; mt < S::MT; ++mt)
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) qT[mt][c2] = tr_operand(cur, 0, lb, qb * 32 + 16 * c2, 32 * mt);
+        u32x4_t q16;  // H16: the last tile's operand for columns 32-47
+        if constexpr (S::H16) q16 = regroup16(qT[1][0], qT[1][1]).lo;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           f32x16_t s = zero16(), d = zero16();
@@ -501,13 +567,18 @@ bwd_dkv_bf16_kernel(BwdArgs a, int total) {
             pp[i] = pack_bf16(p0, p1);
             ds[i] = pack_bf16(p0 * d[2 * i], p1 * d[2 * i + 1]);
           }
+          const u32x4_t db[2] = {{ds[0], ds[1], ds[2], ds[3]}, {ds[4], ds[5], ds[6], ds[7]}};
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) {
             const u32x4_t pb = {pp[4 * c2], pp[4 * c2 + 1], pp[4 * c2 + 2], pp[4 * c2 + 3]};
-            const u32x4_t db = {ds[4 * c2], ds[4 * c2 + 1], ds[4 * c2 + 2], ds[4 * c2 + 3]};
             accv[kb] = mfma(gT[c2], pb, accv[kb]);
 #pragma unroll
-            for (int mt = 0; mt < S::MT; ++mt) acck[kb][mt] = mfma(qT[mt][c2], db, acck[kb][mt]);
+            for (int mt = 0; mt < S::MF; ++mt) acck[kb][mt] = mfma(qT[mt][c2], db[c2], acck[kb][mt]);
+          }
+          if constexpr (S::H16) {
+            const Halves b = regroup16(db[0], db[1]);
+            acck16[kb][0] = mfma16(q16, b.lo, acck16[kb][0]);
+            acck16[kb][1] = mfma16(q16, b.hi, acck16[kb][1]);
           }
         }
       }
@@ -526,6 +597,19 @@ bwd_dkv_bf16_kernel(BwdArgs a, int total) {
   const int C = a.heads * DH;
   uint32_t* dkc = (uint32_t*)a.dkc;
   uint32_t* dvo = (uint32_t*)a.dv;
+  auto krows_of = [&](long tok) {
+    return a.krows + (((long)u.h * a.B + u.b) * a.H * a.W + (tok - (long)u.b * a.H * a.W)) * R;
+  };
+  // columns c0 .. c0+3 of a key's gradient row (krow: its table row, cofs: its first channel)
+  auto put4 = [&](float* krow, long cofs, int c0, float x0, float x1, float x2, float x3) {
+    if (c0 + 4 <= R) {
+      *reinterpret_cast<float4*>(krow + c0) = make_float4(x0 * LN2, x1 * LN2, x2 * LN2, x3 * LN2);
+    } else if (c0 >= R && c0 < R + DH) {
+      const long e = (cofs + c0 - R) >> 1;
+      dkc[e] = pack_bf16(x0 * LN2, x1 * LN2);
+      if (c0 + 2 < R + DH) dkc[e + 1] = pack_bf16(x2 * LN2, x3 * LN2);
+    }
+  };
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int r = f.r0 + kb * 32 + l32;
@@ -534,7 +618,7 @@ bwd_dkv_bf16_kernel(BwdArgs a, int total) {
     int n;
     locate(u, a, r, tok, n);
     const long cofs = tok * C + (long)u.h * DH;
-    float* krow = a.krows + (((long)u.h * a.B + u.b) * a.H * a.W + (tok - (long)u.b * a.H * a.W)) * R;
+    float* krow = krows_of(tok);
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int c0 = 8 * g4 + 4 * hh;
@@ -546,19 +630,26 @@ bwd_dkv_bf16_kernel(BwdArgs a, int total) {
       }
     }
 #pragma unroll
-    for (int mt = 0; mt < S::MT; ++mt)
+    for (int mt = 0; mt < S::MF; ++mt)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int c0 = 32 * mt + 8 * g4 + 4 * hh;
         const f32x16_t& x = acck[kb][mt];
-        if (c0 + 4 <= R) {
-          *reinterpret_cast<float4*>(krow + c0) =
-              make_float4(x[4 * g4] * LN2, x[4 * g4 + 1] * LN2, x[4 * g4 + 2] * LN2, x[4 * g4 + 3] * LN2);
-        } else if (c0 >= R && c0 < R + DH) {
-          const long e = (cofs + c0 - R) >> 1;
-          dkc[e] = pack_bf16(x[4 * g4] * LN2, x[4 * g4 + 1] * LN2);
-          if (c0 + 2 < R + DH) dkc[e + 1] = pack_bf16(x[4 * g4 + 2] * LN2, x[4 * g4 + 3] * LN2);
-        }
+        put4(krow, cofs, 32 * mt + 8 * g4 + 4 * hh, x[4 * g4], x[4 * g4 + 1], x[4 * g4 + 2], x[4 * g4 + 3]);
+      }
+  }
+  if constexpr (S::H16) {
+    // register i of acck16[kb][h] is column 32 + 4(lane/16) + i of key row 16h + lane%16
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = f.r0 + kb * 32 + 16 * h + (f.lane & 15);
+        if (r >= u.n_real) continue;
+        long tok;
+        int n;
+        locate(u, a, r, tok, n);
+        const f32x4_t& x = acck16[kb][h];
+        put4(krows_of(tok), tok * C + (long)u.h * DH, 32 + 4 * (f.lane >> 4), x[0], x[1], x[2], x[3]);
       }
   }
 }
